@@ -1,0 +1,121 @@
+"""CPU oracle of the gated delta rule (token-serial, float64).
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import this package.  The HIP library never
+does, and this package imports nothing from it.
+
+``forward`` / ``backward`` call the C oracle in ``gdn_oracle.c`` (built with
+gcc into ``libgdn_oracle.so`` next to it).  Inputs are converted to their exact
+float64 values first (see ``gdn_inputs.as_f64``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "gdn_oracle.c")
+LIB = os.path.join(_HERE, "libgdn_oracle.so")
+CFLAGS = ["-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-std=c11"]
+
+_lib = None
+
+
+def build(force: bool = False, src: str = SRC, out: str = LIB, extra: tuple = ()) -> str:
+    """Compile the C oracle with gcc (host code only)."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, *extra, src, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def _bind(lib):
+    dp = ctypes.POINTER(ctypes.c_double)
+    i = ctypes.c_int
+    lib.oracle_forward.argtypes = [i, i, i, i, i, i, ctypes.c_double] + [dp] * 8 + [i]
+    lib.oracle_forward.restype = i
+    lib.oracle_backward.argtypes = [i, i, i, i, i, i, ctypes.c_double] + [dp] * 14 + [i]
+    lib.oracle_backward.restype = i
+    lib.oracle_max_threads.restype = i
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (building if needed) the oracle library.  A path loads a variant."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        _lib = _bind(ctypes.CDLL(build()))
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    assert x.dtype == np.float64 and x.flags.c_contiguous
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if x.dtype == np.uint16:  # bf16 bits
+        x = (x.astype(np.uint32) << 16).view(np.float32)
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _dims(q, v, g):
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    per_channel = int(g.ndim == 4)
+    return B, T, H, Dk, Dv, per_channel
+
+
+def forward(q, k, v, g, beta, scale, h0=None, nthreads: int = 0, lib=None):
+    """Returns (o [B,T,H,Dv], hT [B,H,Dk,Dv]) in float64."""
+    q, k, v, g, beta, h0 = map(_f64, (q, k, v, g, beta, h0))
+    B, T, H, Dk, Dv, pc = _dims(q, v, g)
+    o = np.zeros((B, T, H, Dv))
+    hT = np.zeros((B, H, Dk, Dv))
+    lib = lib or load()
+    rc = lib.oracle_forward(B, T, H, Dk, Dv, pc, float(scale), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_forward: bad dimensions")
+    return o, hT
+
+
+def backward(q, k, v, g, beta, scale, dO, h0=None, dhT=None, nthreads: int = 0, lib=None):
+    """Returns dict of float64 gradients dq, dk, dv, dg, dbeta, dh0."""
+    q, k, v, g, beta, h0, dO, dhT = map(_f64, (q, k, v, g, beta, h0, dO, dhT))
+    B, T, H, Dk, Dv, pc = _dims(q, v, g)
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+               dg=np.zeros_like(g), dbeta=np.zeros_like(beta), dh0=np.zeros((B, H, Dk, Dv)))
+    lib = lib or load()
+    rc = lib.oracle_backward(B, T, H, Dk, Dv, pc, float(scale), _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(g), _ptr(beta), _ptr(h0), _ptr(dO), _ptr(dhT),
+                             _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                             _ptr(out["dbeta"]), _ptr(out["dh0"]), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_backward: bad dimensions")
+    return out
+
+
+def forward_inputs(inp: dict, **kw):
+    """forward() on a workload dict from gdn_inputs."""
+    return forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["meta"]["scale"],
+                   h0=inp.get("h0"), **kw)
+
+
+def backward_inputs(inp: dict, **kw):
+    return backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["meta"]["scale"],
+                    inp["dO"], h0=inp.get("h0"), dhT=inp.get("dhT"), **kw)
+
+
+def max_threads() -> int:
+    return load().oracle_max_threads()
