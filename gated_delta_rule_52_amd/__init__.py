@@ -1,0 +1,197 @@
+"""Python binding of libgdn.so, the gated delta-rule layer for MI355X (gfx950).
+
+Argument marshalling only: torch tensors supply device memory and the current
+stream, every computation runs in the library's HIP kernels.  The functions
+carry the names of the C entry points in include/gdn.h:
+
+    gdn_new_state(B, H, Dk, Dv)                      -> zeroed fp32 state
+    gdn_workspace_bytes(shape, for_backward)
+    gdn_forward(q, k, v, g, beta, h0=None, ...)      -> (o, hT)
+    gdn_backward(q, k, v, g, beta, dO, h0=None, dhT=None, ...)
+                                                     -> (dq, dk, dv, dg, dbeta, dh0)
+    gdn_decode_step(q, k, v, g, beta, state, ...)    -> o   (state updated in place)
+
+plus ``new_state`` (the gated-deltanet card's name for gdn_new_state).
+Layouts: q, k [B,T,H,Dk]; v [B,T,H,Dv]; g [B,T,H,Dk] or [B,T,H] (fp32);
+beta [B,T,H] (fp32); states [B,H,Dk,Dv] fp32.  q, k, v share one dtype
+(float32 or bfloat16); outputs take that dtype.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+GDN_DECAY_PER_HEAD, GDN_DECAY_PER_CHANNEL = 0, 1
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_ALIGNMENT",
+          4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
+EXPORTS = ("gdn_new_state", "gdn_workspace_bytes", "gdn_forward", "gdn_backward",
+           "gdn_decode_step", "gdn_status_string")
+
+
+class GdnShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+                ("Dk", ctypes.c_int), ("Dv", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("decay", ctypes.c_int), ("scale", ctypes.c_float), ("chunk", ctypes.c_int)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {lib().gdn_status_string(code).decode()}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libgdn.so.  Raises if it has not been built: there is no
+    other implementation to fall back to."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libgdn.so is not built ({LIB_PATH}); run "
+                              "`python -m gated_delta_rule_52_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i, fp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p
+        sp = ctypes.POINTER(GdnShape)
+        L.gdn_new_state.argtypes = [fp, i, i, i, i, vp]
+        L.gdn_new_state.restype = i
+        L.gdn_workspace_bytes.argtypes = [sp, i]
+        L.gdn_workspace_bytes.restype = sz
+        L.gdn_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_forward.restype = i
+        L.gdn_backward.argtypes = [sp] + [vp] * 15 + [sz, vp]
+        L.gdn_backward.restype = i
+        L.gdn_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.gdn_decode_step.restype = i
+        L.gdn_status_string.argtypes = [i]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return GDN_F32
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def make_shape(q, v, g, scale=None, chunk=None) -> GdnShape:
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    decay = GDN_DECAY_PER_CHANNEL if g.dim() == 4 else GDN_DECAY_PER_HEAD
+    return GdnShape(B, T, H, Dk, Dv, _dtype_code(q), decay,
+                    0.0 if scale is None else float(scale), 0 if chunk is None else int(chunk))
+
+
+def _call(fn, where, *args):
+    rc = fn(*args)
+    if rc != 0:
+        raise GdnError(rc, where)
+
+
+def gdn_new_state(B: int, H: int, Dk: int, Dv: int, device="cuda") -> torch.Tensor:
+    s = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=device)
+    _call(lib().gdn_new_state, "gdn_new_state", _ptr(s), B, H, Dk, Dv, _stream())
+    return s
+
+
+new_state = gdn_new_state
+
+
+def gdn_workspace_bytes(shape: GdnShape, for_backward: bool = False) -> int:
+    return int(lib().gdn_workspace_bytes(ctypes.byref(shape), int(for_backward)))
+
+
+def workspace(shape: GdnShape, for_backward: bool, device) -> torch.Tensor:
+    n = gdn_workspace_bytes(shape, for_backward)
+    if n == 0 and shape.T > 0:
+        raise GdnError(2, "gdn_workspace_bytes")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _check_inputs(q, k, v, g, beta):
+    dt = q.dtype
+    _check(q, "q", dt); _check(k, "k", dt); _check(v, "v", dt)
+    _check(g, "g", torch.float32); _check(beta, "beta", torch.float32)
+
+
+def gdn_forward(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT=None,
+                want_state=True, ws=None):
+    """Chunked forward.  Returns (o, hT); hT is None when want_state is False.
+    Passing hT=h0 carries the state in place."""
+    _check_inputs(q, k, v, g, beta)
+    _check(h0, "h0", torch.float32)
+    sh = make_shape(q, v, g, scale, chunk)
+    B, T, H, _ = q.shape
+    if o is None:
+        o = torch.empty((B, T, H, sh.Dv), dtype=q.dtype, device=q.device)
+    if hT is None and want_state:
+        hT = torch.empty((B, H, sh.Dk, sh.Dv), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(sh, False, q.device)
+    _call(lib().gdn_forward, "gdn_forward", ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+          _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), _ptr(ws), ws.numel(), _stream())
+    return o, hT
+
+
+def gdn_backward(q, k, v, g, beta, dO, h0=None, dhT=None, *, scale=None, chunk=None,
+                 want_dh0=True, ws=None):
+    """Gradients (dq, dk, dv, dg, dbeta, dh0) of sum(o*dO) + sum(hT*dhT)."""
+    _check_inputs(q, k, v, g, beta)
+    _check(dO, "dO", q.dtype)
+    _check(h0, "h0", torch.float32); _check(dhT, "dhT", torch.float32)
+    sh = make_shape(q, v, g, scale, chunk)
+    dq = torch.empty_like(q); dk = torch.empty_like(k); dv = torch.empty_like(v)
+    dg = torch.empty_like(g); dbeta = torch.empty_like(beta)
+    dh0 = (torch.empty((sh.B, sh.H, sh.Dk, sh.Dv), dtype=torch.float32, device=q.device)
+           if want_dh0 else None)
+    if ws is None:
+        ws = workspace(sh, True, q.device)
+    _call(lib().gdn_backward, "gdn_backward", ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v),
+          _ptr(g), _ptr(beta), _ptr(h0), _ptr(dO), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv),
+          _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(ws), ws.numel(), _stream())
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+def gdn_decode_step(q, k, v, g, beta, state, *, scale=None, o=None):
+    """One token for every (b, h); q,k [B,1,H,Dk] (or [B,H,Dk]), state updated in place."""
+    if q.dim() == 3:
+        q, k, v = q.unsqueeze(1), k.unsqueeze(1), v.unsqueeze(1)
+        g = g.unsqueeze(1)
+        beta = beta.unsqueeze(1)
+    _check_inputs(q, k, v, g, beta)
+    _check(state, "state", torch.float32)
+    sh = make_shape(q, v, g, scale, None)
+    if o is None:
+        o = torch.empty((sh.B, 1, sh.H, sh.Dv), dtype=q.dtype, device=q.device)
+    _call(lib().gdn_decode_step, "gdn_decode_step", ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v),
+          _ptr(g), _ptr(beta), _ptr(state), _ptr(o), _stream())
+    return o

@@ -1,0 +1,74 @@
+// common.h -- device helpers shared by the gfx950 kernels of the gated
+// delta-rule library: element conversion, MFMA fragments, launch checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// ---------------------------------------------------------------------------
+// element types
+// ---------------------------------------------------------------------------
+struct bf16 {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(((uint32_t)x.bits) << 16); }
+
+// float -> bf16, round to nearest even (inputs here are finite)
+__device__ __forceinline__ bf16 f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    bf16 r;
+    r.bits = (uint16_t)(u >> 16);
+    return r;
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return f32_to_bf16(x); }
+
+// exp(x) as 2^(x*log2 e) on the hardware exp2 unit
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// MFMA (CDNA3/CDNA4 matrix cores), wave64
+//
+// v_mfma_f32_16x16x4_f32:  D[16x16] += A[16x4] * B[4x16]
+//   lane l supplies A[l%16][l/16] and B[l/16][l%16];
+//   lane l holds D[4*(l/16)+r][l%16] in acc[r], r = 0..3.
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16]
+//   lane l supplies A[l%16][8*(l/16)+e] and B[8*(l/16)+e][l%16], e = 0..7;
+//   same D layout.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+}  // namespace gdn
+
+#define GDN_HIP_CHECK_LAUNCH()                                   \
+    do {                                                         \
+        if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP; \
+    } while (0)

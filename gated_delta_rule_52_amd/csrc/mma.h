@@ -1,0 +1,76 @@
+// mma.h -- 16x16 output tiles on the gfx950 matrix cores, operands from LDS
+// (or any addressable float memory) with arbitrary row/column strides, so one
+// helper serves A*B, A^T*B, A*B^T and A^T*B^T.
+//
+// A 16x16 tile D(i, j) += sum_k A(i, k) B(k, j), i, j in [0, 16), k in [0, K):
+//   A(i, k) = A[i * ars + k * acs],   B(k, j) = B[k * brs + j * bcs].
+// Result layout (both MFMA kinds): lane l holds D(4*(l/16) + r, l%16) in acc[r].
+//
+// MT selects the matrix-core instruction: MT_F32 uses v_mfma_f32_16x16x4_f32
+// (fp32 operands, exact products), MT_BF16 v_mfma_f32_16x16x32_bf16 (operands
+// rounded to bf16 nearest-even, fp32 accumulation).
+#pragma once
+
+#include "common.h"
+
+namespace gdn {
+
+enum { MT_F32 = 0, MT_BF16 = 1 };
+
+__device__ __forceinline__ int acc_row(int r) { return 4 * (lane_id() >> 4) + r; }
+__device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+
+template <int MT>
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, const float* __restrict__ A, int ars, int acs,
+                                       const float* __restrict__ B, int brs, int bcs, int K)
+{
+    const int l = lane_id();
+    const int r = l & 15, kk = l >> 4;
+    if (MT == MT_F32) {
+        for (int k = 0; k < K; k += 4)
+            acc = mfma_f32_16x16x4(A[r * ars + (k + kk) * acs], B[(k + kk) * brs + r * bcs], acc);
+    } else {
+        for (int k = 0; k < K; k += 32) {
+            bf16x8 a, b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kx = k + 8 * kk + e;
+                const bool in = kx < K;
+                a[e] = (__bf16)(in ? A[r * ars + kx * acs] : 0.f);
+                b[e] = (__bf16)(in ? B[kx * brs + r * bcs] : 0.f);
+            }
+            acc = mfma_bf16_16x16x32(a, b, acc);
+        }
+    }
+    return acc;
+}
+
+// Compile-time K (fully unrolled).
+template <int MT, int K>
+__device__ __forceinline__ f32x4 mma16k(f32x4 acc, const float* __restrict__ A, int ars, int acs,
+                                        const float* __restrict__ B, int brs, int bcs)
+{
+    const int l = lane_id();
+    const int r = l & 15, kk = l >> 4;
+    if (MT == MT_F32) {
+#pragma unroll
+        for (int k = 0; k < K; k += 4)
+            acc = mfma_f32_16x16x4(A[r * ars + (k + kk) * acs], B[(k + kk) * brs + r * bcs], acc);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; k += 32) {
+            bf16x8 a, b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kx = k + 8 * kk + e;
+                const bool in = (K % 32 == 0) || kx < K;
+                a[e] = (__bf16)(in ? A[r * ars + kx * acs] : 0.f);
+                b[e] = (__bf16)(in ? B[kx * brs + r * bcs] : 0.f);
+            }
+            acc = mfma_bf16_16x16x32(a, b, acc);
+        }
+    }
+    return acc;
+}
+
+}  // namespace gdn

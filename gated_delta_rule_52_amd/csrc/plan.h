@@ -1,0 +1,72 @@
+// plan.h -- shape plan and workspace layout of the chunked path.
+//
+// The chunked form processes each (batch, head) sequence in chunks of C
+// tokens; NC = ceil(T / C).  A chunk-head is one chunk of one (b, h); its
+// index is ch = (b * H + h) * NC + n.  All workspace arrays are float32 and
+// indexed by chunk-head:
+//   W   [ch][C][Dk]   W  = T diag(beta) (K o Gamma)        (WY form of the solve)
+//   U   [ch][C][Dv]   U  = T diag(beta) V
+//   Qg  [ch][C][Dk]   Qg = scale * (Q o Gamma)             (query read of the carried state)
+//   Kh  [ch][C][Dk]   Kh = K o exp(G_{C-1} - G)            (key write into the next state)
+//   Ps  [ch][C][C]    Ps = scale * P  (decayed query-key scores, lower incl. diagonal)
+//   gam [ch][Dk]      gam = exp(G_{C-1})                   (whole-chunk decay)
+// backward only:
+//   Tm  [ch][C][C]    T = (I + A)^-1
+//   Sst [ch][Dk][Dv]  state at the start of chunk n
+//   dSt [ch][Dk][Dv]  gradient with respect to the state at the end of chunk n
+//   dDt [ch][C][Dv]   gradient with respect to the chunk's deltas D
+// G is the chunk-local inclusive cumulative log-decay and Gamma = exp(G).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+struct Plan {
+    int B, T, H, Dk, Dv, C, NC, dtype, decay;
+    float scale;
+    size_t n_ch;  // B * H * NC
+    // byte offsets into the workspace
+    size_t o_W, o_U, o_Qg, o_Kh, o_Ps, o_gam, o_Tm, o_Sst, o_dSt, o_dDt;
+    size_t ws_fwd_bytes, ws_bwd_bytes;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline bool plan_supported(int Dk, int Dv, int C)
+{
+    if (Dk != Dv) return false;
+    if (C == 64) return Dk == 16 || Dk == 32 || Dk == 64 || Dk == 128;
+    if (C == 16) return Dk == 16 || Dk == 32 || Dk == 64 || Dk == 128;
+    return false;
+}
+
+inline Plan make_plan(const gdn_shape& s, float scale)
+{
+    Plan p;
+    p.B = s.B; p.T = s.T; p.H = s.H; p.Dk = s.Dk; p.Dv = s.Dv;
+    p.C = s.chunk ? s.chunk : 64;
+    p.NC = (s.T + p.C - 1) / p.C;
+    p.dtype = s.dtype; p.decay = s.decay; p.scale = scale;
+    p.n_ch = (size_t)s.B * s.H * p.NC;
+    const size_t f = sizeof(float), n = p.n_ch, C = p.C, Dk = p.Dk, Dv = p.Dv;
+    size_t off = 0;
+    p.o_W = off;   off = align256(off + n * C * Dk * f);
+    p.o_U = off;   off = align256(off + n * C * Dv * f);
+    p.o_Qg = off;  off = align256(off + n * C * Dk * f);
+    p.o_Kh = off;  off = align256(off + n * C * Dk * f);
+    p.o_Ps = off;  off = align256(off + n * C * C * f);
+    p.o_gam = off; off = align256(off + n * Dk * f);
+    p.ws_fwd_bytes = off;
+    p.o_Tm = off;  off = align256(off + n * C * C * f);
+    p.o_Sst = off; off = align256(off + n * Dk * Dv * f);
+    p.o_dSt = off; off = align256(off + n * Dk * Dv * f);
+    p.o_dDt = off; off = align256(off + n * C * Dv * f);
+    p.ws_bwd_bytes = off;
+    return p;
+}
+
+}  // namespace gdn

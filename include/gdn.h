@@ -1,0 +1,144 @@
+/*
+ * gdn.h -- C ABI of the gated delta-rule layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (gated-deltanet card, "Method"; per-key-channel decay as in GDN-2,
+ * Marin note "Background") keeps a state S [Dk x Dv] per (batch, head) and,
+ * for each token t, applies
+ *     S <- diag(exp(g_t)) S;  m = S^T k_t;  d = beta_t (v_t - m);
+ *     S <- S + k_t d^T;       o_t = scale * S^T q_t.
+ * g_t is one log-decay per key channel (GDN_DECAY_PER_CHANNEL) or one scalar
+ * per head broadcast over the channels (GDN_DECAY_PER_HEAD).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers are DEVICE pointers (hipMalloc'd or from a torch tensor), dense,
+ * row-major, 16-byte aligned.  The caller owns every buffer; the library keeps
+ * no allocation between calls and allocates nothing itself.  All work is
+ * enqueued on `stream` (a hipStream_t; NULL = the null stream) with no host
+ * synchronisation, so asynchronous faults surface at the caller's next sync.
+ *
+ * Tensor layouts (element types in brackets):
+ *   q, k      [B, T, H, Dk]         (dtype: float32 or bf16)
+ *   v, o, dO  [B, T, H, Dv]         (dtype)
+ *   g         [B, T, H, Dk] per channel, or [B, T, H] per head   (float32)
+ *   beta      [B, T, H]                                          (float32)
+ *   states    h0, hT, dhT, dh0, decode state: [B, H, Dk, Dv]     (float32)
+ *   dq, dk    [B, T, H, Dk] (dtype);  dv [B, T, H, Dv] (dtype)
+ *   dg        like g (float32);  dbeta [B, T, H] (float32)
+ * Grouped-query repetition of q/k heads is the caller's (gated-deltanet card,
+ * "Requirements and limits").  q and k are used as given: callers that want
+ * L2-normalised keys normalise them first.
+ *
+ * Errors: every call returns a status.  Bad shapes, NULL required pointers,
+ * misaligned pointers and a too-small workspace are rejected before anything
+ * is launched.  An unsupported (chunk, Dk, Dv) combination returns
+ * GDN_ERR_UNSUPPORTED; there is no fallback path.  A failed launch returns
+ * GDN_ERR_HIP.  Results are deterministic: repeated calls with the same inputs
+ * are bitwise identical (gated-deltanet card, "Correctness").
+ *
+ * Supported sizes: Dk, Dv in {16, 32, 64, 128}; chunk 16 or 64 (0 = 64);
+ * any T >= 0 (a ragged last chunk is processed as if padded with tokens that
+ * have g = 0 and beta = 0, which leave the state exactly unchanged; their
+ * outputs are not written); B, H >= 1.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1,
+    GDN_ERR_UNSUPPORTED = 2,
+    GDN_ERR_ALIGNMENT = 3,
+    GDN_ERR_WORKSPACE = 4,
+    GDN_ERR_HIP = 5
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+typedef enum { GDN_DECAY_PER_HEAD = 0, GDN_DECAY_PER_CHANNEL = 1 } gdn_decay;
+
+typedef struct {
+    int B, T, H, Dk, Dv;
+    int dtype;   /* gdn_dtype of q, k, v, o, dO, dq, dk, dv */
+    int decay;   /* gdn_decay */
+    float scale; /* output scale; 0 means Dk^-0.5 (the atomic_ops card passes d^-0.5) */
+    int chunk;   /* chunk length C of the chunked form: 16 or 64; 0 means 64 */
+} gdn_shape;
+
+/*
+ * gdn_new_state -- zero-fill a caller-allocated state buffer [B,H,Dk,Dv] float32.
+ * The gated-deltanet card's new_state(batch, heads, key_dim, value_dim) gives a
+ * fresh state for a sequence ("Usage"); zero is the state before any token.
+ * Errors: GDN_ERR_INVALID_ARG for NULL state or non-positive sizes.
+ */
+gdn_status gdn_new_state(float *state, int B, int H, int Dk, int Dv, void *stream);
+
+/*
+ * gdn_workspace_bytes -- device scratch size that gdn_forward
+ * (for_backward = 0) or gdn_backward (for_backward = 1) needs for `shape`.
+ * Returns 0 for an invalid or unsupported shape.  The workspace is caller
+ * memory, 256-byte aligned, contents on entry irrelevant.
+ */
+size_t gdn_workspace_bytes(const gdn_shape *shape, int for_backward);
+
+/*
+ * gdn_forward -- the whole layer over T tokens in chunked form.
+ *
+ * Within each chunk of C tokens the per-channel cumulative log-decay is formed
+ * (Marin note, "Background"); query-key and key-key scores that span two
+ * halves of a block are computed with the decay split at the last token of
+ * the earlier half, so the spanning scores are one dense matrix product per
+ * block pair, while pairs inside the smallest blocks are scored pairwise
+ * (Marin note, "Approach"); the unit-lower-triangular delta system of the
+ * chunk is solved in WY form; and the state is carried across chunks
+ * (atomic_ops card, "Features": chunk scores, WY block solve, recompute,
+ * inter-chunk scan).  The result equals the token recurrence above up to
+ * floating-point rounding.
+ *
+ * h0 may be NULL (zero initial state).  hT may be NULL (not written) and may
+ * alias h0 (the state carries in place across calls, as in the gated-deltanet
+ * card's "Usage").  o must not alias any input.  ws must hold
+ * gdn_workspace_bytes(shape, 0) bytes (GDN_ERR_WORKSPACE otherwise).
+ */
+gdn_status gdn_forward(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, const float *h0, void *o, float *hT,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_backward -- gradients of the chunked forward with respect to q, k, v, g,
+ * beta and h0, given dO = dL/do and dhT = dL/dhT (NULL = zero).  The forward
+ * intermediates are recomputed from the inputs (nothing is kept between
+ * calls); the backward runs a reverse scan over chunks followed by a
+ * chunk-parallel gradient stage (atomic_ops card, "Features": fused backward).
+ * dh0 may be NULL (not written).  Every other output is required.
+ * ws must hold gdn_workspace_bytes(shape, 1) bytes.
+ */
+gdn_status gdn_backward(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, const float *h0, const void *dO,
+                        const float *dhT, void *dq, void *dk, void *dv, float *dg, float *dbeta,
+                        float *dh0, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_decode_step -- one token of the recurrence for every (batch, head), with
+ * the state updated in place: each state is read once and written once
+ * (gated-deltanet card, "Method": the state is the whole cost).  shape->T must
+ * be 1; q, k [B,1,H,Dk]; v, o [B,1,H,Dv]; g [B,1,H,Dk] or [B,1,H];
+ * beta [B,1,H]; state [B,H,Dk,Dv] float32 (read and overwritten).
+ * Decoding token by token equals the chunked forward up to rounding.
+ */
+gdn_status gdn_decode_step(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, float *state, void *o,
+                           void *stream);
+
+/* gdn_status_string -- static, human-readable name of a status code. */
+const char *gdn_status_string(gdn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

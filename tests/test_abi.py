@@ -1,0 +1,80 @@
+"""The C-ABI library loads and exports every entry point include/gdn.h declares
+(no GPU needed: nothing is computed), and the host-side argument checks reject
+bad calls before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_52_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_symbols() == sorted(gdn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = gdn.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = gdn.lib()
+    for code in range(6):
+        s = L.gdn_status_string(code).decode()
+        assert s.startswith(gdn.STATUS[code])
+
+
+def _shape(**kw):
+    d = dict(B=2, T=128, H=3, Dk=128, Dv=128, dtype=0, decay=1, scale=0.0, chunk=0)
+    d.update(kw)
+    return gdn.GdnShape(**d)
+
+
+def test_workspace_query():
+    L = gdn.lib()
+    sh = _shape()
+    fwd = L.gdn_workspace_bytes(ctypes.byref(sh), 0)
+    bwd = L.gdn_workspace_bytes(ctypes.byref(sh), 1)
+    assert 0 < fwd < bwd
+    assert fwd % 256 == 0 and bwd % 256 == 0
+    for bad in (dict(Dk=100, Dv=100), dict(chunk=32), dict(B=0), dict(dtype=7), dict(decay=3),
+                dict(Dk=64, Dv=128)):
+        assert L.gdn_workspace_bytes(ctypes.byref(_shape(**bad)), 0) == 0, bad
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(B=0), 1), (dict(T=-1), 1), (dict(dtype=5), 1), (dict(decay=9), 1),
+    (dict(scale=-1.0), 1), (dict(Dk=48, Dv=48), 2), (dict(chunk=32), 2),
+])
+def test_forward_rejects_bad_shapes_before_launch(bad, code):
+    L = gdn.lib()
+    sh = _shape(**bad)
+    p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    rc = L.gdn_forward(ctypes.byref(sh), p, p, p, p, p, None, p, None, p, 1 << 40, None)
+    assert rc == code
+
+
+def test_null_and_misaligned_pointers_rejected():
+    L = gdn.lib()
+    sh = _shape()
+    p = ctypes.c_void_p(256)
+    mis = ctypes.c_void_p(258)
+    assert L.gdn_forward(ctypes.byref(sh), None, p, p, p, p, None, p, None, p, 1 << 40, None) == 1
+    assert L.gdn_forward(ctypes.byref(sh), mis, p, p, p, p, None, p, None, p, 1 << 40, None) == 3
+    assert L.gdn_forward(ctypes.byref(sh), p, p, p, p, p, None, p, None, p, 16, None) == 4
+    d = _shape(T=1)
+    assert L.gdn_decode_step(ctypes.byref(_shape(T=2)), p, p, p, p, p, p, p, None) == 1
+    assert L.gdn_decode_step(ctypes.byref(d), p, p, p, p, p, None, p, None) == 1
+    assert L.gdn_new_state(None, 1, 1, 16, 16, None) == 1
+    assert L.gdn_new_state(mis, 1, 1, 16, 16, None) == 3
