@@ -39,8 +39,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline bool plan_supported(int Dk, int Dv, int C)
 {
     if (Dk != Dv) return false;
-    if (C == 64) return Dk == 16 || Dk == 32 || Dk == 64 || Dk == 128;
-    if (C == 16) return Dk == 16 || Dk == 32 || Dk == 64 || Dk == 128;
+    if (C == 64) return Dk == 64 || Dk == 128;
+    if (C == 16) return Dk == 16;
     return false;
 }
 
