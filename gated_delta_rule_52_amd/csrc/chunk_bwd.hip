@@ -1,0 +1,781 @@
+// chunk_bwd.hip -- backward of the chunked gated delta rule on gfx950.
+//
+// Gradients of L(o, hT) with respect to q, k, v, g, beta and h0, given dO and
+// dhT (atomic_ops card, "Features": the backward is a chain of stage kernels
+// after the forward).  Nothing is kept from the forward call: the forward
+// intermediates are recomputed (prep with T, then the state scan saving the
+// state at the start of every chunk), then
+//
+//  bscan    one workgroup per (b, h, Dv-slice), chunks in reverse, carrying
+//           dS = dL/dS (the state at the end of the chunk):
+//             dD = scale P^T dO + Kh dS'           (gradient of the deltas)
+//             dS <- Qg^T dO + gam o dS' - W^T dD
+//           and dh0 = dS after chunk 0.
+//  bchunk1  one workgroup per chunk-head; streams the Dv columns of S, dS',
+//           dO, dD and U in 32-wide tiles and accumulates the contractions
+//           over Dv:  dQg = dO S^T, dW = -dD S^T, dKh = D dS'^T,
+//           dPs = dO D^T, dT(U) = dD (beta V)^T, dgam = rowsum(dS' o S),
+//           plus dX_V = T^T dD -> dv = beta dX_V and <dX_V, v> (part of dbeta).
+//  bchunk2  one workgroup per chunk-head (8 waves); dX_K = T^T dW,
+//           dT = dT(U) + dW X_K^T, dA = -T^T dT T^T (strictly lower), then the
+//           score gradients through the same block-boundary split as the
+//           forward (every (i, j) pair belongs to exactly one level; at level h
+//           the decay factors of the query rows and key rows are separate, so
+//           sum_j dP_ij k_j o E_ij = F_i o (dP KF)_i is a matrix product), the
+//           gradients of the decay factors (Gamma, Kh, gam, the level
+//           factors) and finally dg = reverse cumulative sum of dG over the
+//           chunk, where G is the chunk-local cumulative log-decay.
+#include <type_traits>
+
+#include "chunk_common.h"
+#include "plan.h"
+
+namespace gdn {
+
+gdn_status recompute_dispatch(const Plan& p, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* h0, void* ws,
+                              hipStream_t st);
+
+template <int DV>
+struct BScanCfg {
+    static constexpr int BV = DV >= 32 ? 32 : DV;
+    static constexpr int NS = DV / BV;
+    static constexpr int PS = BV + 4;
+};
+
+// ---------------------------------------------------------------------------
+// bscan
+// ---------------------------------------------------------------------------
+template <typename TIn, int C, int DK, int DV, int MT>
+__global__ void __launch_bounds__(NTHR)
+bscan_kernel(const float* __restrict__ Qgi, const float* __restrict__ Khi,
+             const float* __restrict__ Wi, const float* __restrict__ Psi,
+             const float* __restrict__ gami, const TIn* __restrict__ dO,
+             const float* __restrict__ dhT, float* __restrict__ dSt, float* __restrict__ dDt,
+             float* __restrict__ dh0, int BH, int T, int H, int NC)
+{
+    using G = Geo<C, DK, DV>;
+    using SC = BScanCfg<DV>;
+    constexpr int PD = G::PD, PC = G::PC, BV = SC::BV, NS = SC::NS, PS = SC::PS;
+    __shared__ float sdS[DK][PS], sQ[C][PD], sK[C][PD], sW[C][PD], sP[C][PC], sdO[C][PS],
+        sdD[C][PS], sg[DK];
+
+    const int x = blockIdx.x;
+    const int grp = x / (8 * NS), rem = x % (8 * NS);
+    const int sl = rem / 8, bh = grp * 8 + rem % 8;
+    if (bh >= BH) return;
+    const int b = bh / H, h = bh % H;
+    const int v0 = sl * BV;
+    const int tid = threadIdx.x, w = tid >> 6;
+
+    for (int idx = tid; idx < DK * BV; idx += NTHR) {
+        const int i = idx / BV, j = idx % BV;
+        sdS[i][j] = dhT ? dhT[((size_t)bh * DK + i) * DV + v0 + j] : 0.f;
+    }
+    __syncthreads();
+
+    constexpr int TD = (C / 16) * (BV / 16);
+    constexpr int TS = (DK / 16) * (BV / 16);
+    constexpr int MD = (TD + 3) / 4, MS = (TS + 3) / 4;
+
+    for (int n = NC - 1; n >= 0; --n) {
+        const size_t ch = (size_t)bh * NC + n;
+        {
+            float* dp = dSt + ch * DK * DV;
+            for (int idx = tid; idx < DK * BV; idx += NTHR) {
+                const int i = idx / BV, j = idx % BV;
+                dp[i * DV + v0 + j] = sdS[i][j];
+            }
+            const float* Qp = Qgi + ch * C * DK;
+            const float* Kp = Khi + ch * C * DK;
+            const float* Wp = Wi + ch * C * DK;
+            for (int idx = tid; idx < C * DK / 4; idx += NTHR) {
+                const int r = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
+                st4(&sQ[r][c4], load4<float>(Qp + r * DK + c4));
+                st4(&sK[r][c4], load4<float>(Kp + r * DK + c4));
+                st4(&sW[r][c4], load4<float>(Wp + r * DK + c4));
+            }
+            const float* Pp = Psi + ch * C * C;
+            for (int idx = tid; idx < C * C / 4; idx += NTHR) {
+                const int r = idx / (C / 4), c4 = (idx % (C / 4)) * 4;
+                st4(&sP[r][c4], load4<float>(Pp + r * C + c4));
+            }
+            for (int i = tid; i < DK; i += NTHR) sg[i] = gami[ch * DK + i];
+            for (int idx = tid; idx < C * BV; idx += NTHR) {
+                const int r = idx / BV, j = idx % BV;
+                const int t = n * C + r;
+                sdO[r][j] = t < T ? to_f32(dO[(((size_t)b * T + t) * H + h) * DV + v0 + j]) : 0.f;
+            }
+        }
+        __syncthreads();
+        float* dDp = dDt + ch * C * DV;
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            const int idx = w + 4 * m;
+            if (idx < TD) {
+                const int ti = idx / (BV / 16), tj = idx % (BV / 16);
+                f32x4 acc = mma16k<MT, C>(zero4(), &sP[0][ti * 16], 1, PC, &sdO[0][tj * 16], PS, 1);
+                acc = mma16k<MT, DK>(acc, &sK[ti * 16][0], PD, 1, &sdS[0][tj * 16], PS, 1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
+                    sdD[i][j] = acc[r];
+                    dDp[i * DV + v0 + j] = acc[r];
+                }
+            }
+        }
+        __syncthreads();
+        f32x4 sn[MS];
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + 4 * m;
+            if (idx < TS) {
+                const int si = idx / (BV / 16), sj = idx % (BV / 16);
+                f32x4 acc;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = si * 16 + acc_row(r);
+                    acc[r] = sg[i] * sdS[i][sj * 16 + acc_col()];
+                }
+                acc = mma16k<MT, C>(acc, &sQ[0][si * 16], 1, PD, &sdO[0][sj * 16], PS, 1);
+                f32x4 wd = mma16k<MT, C>(zero4(), &sW[0][si * 16], 1, PD, &sdD[0][sj * 16], PS, 1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] -= wd[r];
+                sn[m] = acc;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + 4 * m;
+            if (idx < TS) {
+                const int si = idx / (BV / 16), sj = idx % (BV / 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sdS[si * 16 + acc_row(r)][sj * 16 + acc_col()] = sn[m][r];
+            }
+        }
+        __syncthreads();
+    }
+    if (dh0) {
+        for (int idx = tid; idx < DK * BV; idx += NTHR) {
+            const int i = idx / BV, j = idx % BV;
+            dh0[((size_t)bh * DK + i) * DV + v0 + j] = sdS[i][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bchunk1
+// ---------------------------------------------------------------------------
+template <typename TIn, int C, int DK, int DV, int MT>
+__global__ void __launch_bounds__(NTHR)
+bchunk1_kernel(const TIn* __restrict__ v, const float* __restrict__ beta,
+               const TIn* __restrict__ dO, const float* __restrict__ Wi,
+               const float* __restrict__ Ui, const float* __restrict__ Tmi,
+               const float* __restrict__ Sst, const float* __restrict__ dSt,
+               const float* __restrict__ dDt, TIn* __restrict__ dvo, float* __restrict__ dQgo,
+               float* __restrict__ dWgo, float* __restrict__ dKho, float* __restrict__ dPso,
+               float* __restrict__ dT1o, float* __restrict__ dgmo, float* __restrict__ dbpo, int T,
+               int H, int NC)
+{
+    using G = Geo<C, DK, DV>;
+    constexpr int PD = G::PD, PC = G::PC, NB = G::NB;
+    constexpr int BW = DV >= 32 ? 32 : DV, PW = BW + 4;
+    __shared__ float sW[C][PD], sT[C][PC], sS[DK][PW], sdS[DK][PW], sdO[C][PW], sdD[C][PW],
+        sD[C][PW], sv[C][PW], sxv[C][PW], sdx[C][PW], sbeta[C], sred[NTHR];
+
+    const int ch = blockIdx.x;
+    const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
+    const int t0 = n * C;
+    const int nvalid = min(C, T - t0);
+    const int tid = threadIdx.x, w = tid >> 6;
+    const size_t tok0 = ((size_t)b * T + t0) * H + h;
+    const size_t rsV = (size_t)H * DV;
+
+    {
+        const float* Wp = Wi + (size_t)ch * C * DK;
+        for (int idx = tid; idx < C * DK / 4; idx += NTHR) {
+            const int r = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
+            st4(&sW[r][c4], load4<float>(Wp + r * DK + c4));
+        }
+        const float* Tp = Tmi + (size_t)ch * C * C;
+        for (int idx = tid; idx < C * C / 4; idx += NTHR) {
+            const int r = idx / (C / 4), c4 = (idx % (C / 4)) * 4;
+            st4(&sT[r][c4], load4<float>(Tp + r * C + c4));
+        }
+        for (int r = tid; r < C; r += NTHR) sbeta[r] = r < nvalid ? beta[tok0 + (size_t)r * H] : 0.f;
+    }
+
+    constexpr int T3 = NB * (DK / 16), M3 = (T3 + 3) / 4;  // [C x DK] tiles per wave
+    constexpr int T2 = NB * NB, M2 = (T2 + 3) / 4;         // [C x C] tiles per wave
+    constexpr int TD = NB * (BW / 16), MD = (TD + 3) / 4;   // [C x BW] tiles per wave
+    f32x4 aQ[M3], aW[M3], aK[M3], aP[M2], aT[M2];
+#pragma unroll
+    for (int m = 0; m < M3; ++m) aQ[m] = aW[m] = aK[m] = zero4();
+#pragma unroll
+    for (int m = 0; m < M2; ++m) aP[m] = aT[m] = zero4();
+    constexpr int NG = (NTHR / DK) > 0 ? NTHR / DK : 1;  // threads per key channel
+    const int gc = tid % DK, gg = tid / DK;
+    float dgm_part = 0.f, dbp_part = 0.f;
+
+    const float* Sp = Sst + (size_t)ch * DK * DV;
+    const float* dSp = dSt + (size_t)ch * DK * DV;
+    const float* dDp = dDt + (size_t)ch * C * DV;
+    const float* Up = Ui + (size_t)ch * C * DV;
+
+    for (int v0 = 0; v0 < DV; v0 += BW) {
+        __syncthreads();
+        for (int idx = tid; idx < DK * BW; idx += NTHR) {
+            const int i = idx / BW, j = idx % BW;
+            sS[i][j] = Sp[i * DV + v0 + j];
+            sdS[i][j] = dSp[i * DV + v0 + j];
+        }
+        for (int idx = tid; idx < C * BW; idx += NTHR) {
+            const int r = idx / BW, j = idx % BW;
+            float dov = 0.f, vv = 0.f;
+            if (r < nvalid) {
+                dov = to_f32(dO[(tok0 + (size_t)r * H) * DV + v0 + j]);
+                vv = to_f32(v[tok0 * DV + r * rsV + v0 + j]);
+            }
+            sdO[r][j] = dov;
+            sv[r][j] = vv;
+            sxv[r][j] = sbeta[r] * vv;
+            sdD[r][j] = dDp[r * DV + v0 + j];
+            sD[r][j] = Up[r * DV + v0 + j];
+        }
+        __syncthreads();
+        // D = U - W S ; dX_V = T^T dD (dv = beta dX_V)
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            const int idx = w + 4 * m;
+            if (idx < TD) {
+                const int ti = idx / (BW / 16), tj = idx % (BW / 16);
+                f32x4 ws = mma16k<MT_F32, DK>(zero4(), &sW[ti * 16][0], PD, 1, &sS[0][tj * 16], PW, 1);
+                f32x4 dx = mma16k<MT, C>(zero4(), &sT[0][ti * 16], 1, PC, &sdD[0][tj * 16], PW, 1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
+                    sD[i][j] -= ws[r];
+                    sdx[i][j] = dx[r];
+                    if (i < nvalid) dvo[(tok0 + (size_t)i * H) * DV + v0 + j] = from_f32<TIn>(sbeta[i] * dx[r]);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < M3; ++m) {
+            const int idx = w + 4 * m;
+            if (idx < T3) {
+                const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+                aQ[m] = mma16k<MT, BW>(aQ[m], &sdO[ti * 16][0], PW, 1, &sS[tj * 16][0], 1, PW);
+                aW[m] = mma16k<MT, BW>(aW[m], &sdD[ti * 16][0], PW, 1, &sS[tj * 16][0], 1, PW);
+                aK[m] = mma16k<MT, BW>(aK[m], &sD[ti * 16][0], PW, 1, &sdS[tj * 16][0], 1, PW);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M2; ++m) {
+            const int idx = w + 4 * m;
+            if (idx < T2) {
+                const int ti = idx / NB, tj = idx % NB;
+                aP[m] = mma16k<MT, BW>(aP[m], &sdO[ti * 16][0], PW, 1, &sD[tj * 16][0], 1, PW);
+                aT[m] = mma16k<MT, BW>(aT[m], &sdD[ti * 16][0], PW, 1, &sxv[tj * 16][0], 1, PW);
+            }
+        }
+        if (gg < NG) {
+            for (int j = gg; j < BW; j += NG) dgm_part += sdS[gc][j] * sS[gc][j];
+        }
+        for (int r = tid; r < C; r += NTHR) {
+            float s = 0.f;
+            for (int j = 0; j < BW; ++j) s += sdx[r][j] * sv[r][j];
+            dbp_part += s;
+        }
+    }
+
+    // outputs
+    float* dQp = dQgo + (size_t)ch * C * DK;
+    float* dWp = dWgo + (size_t)ch * C * DK;
+    float* dKp = dKho + (size_t)ch * C * DK;
+#pragma unroll
+    for (int m = 0; m < M3; ++m) {
+        const int idx = w + 4 * m;
+        if (idx < T3) {
+            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
+                dQp[i * DK + j] = aQ[m][r];
+                dWp[i * DK + j] = -aW[m][r];
+                dKp[i * DK + j] = aK[m][r];
+            }
+        }
+    }
+    float* dPp = dPso + (size_t)ch * C * C;
+    float* dTp = dT1o + (size_t)ch * C * C;
+#pragma unroll
+    for (int m = 0; m < M2; ++m) {
+        const int idx = w + 4 * m;
+        if (idx < T2) {
+            const int ti = idx / NB, tj = idx % NB;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
+                dPp[i * C + j] = aP[m][r];
+                dTp[i * C + j] = aT[m][r];
+            }
+        }
+    }
+    sred[tid] = dgm_part;
+    __syncthreads();
+    if (tid < DK) {
+        float s = 0.f;
+        for (int gi = 0; gi < NG; ++gi) s += sred[gi * DK + tid];
+        dgmo[(size_t)ch * DK + tid] = s;
+    }
+    for (int r = tid; r < C; r += NTHR) dbpo[(size_t)ch * C + r] = dbp_part;
+}
+
+// ---------------------------------------------------------------------------
+// bchunk2
+// ---------------------------------------------------------------------------
+constexpr int NTHR2 = 512;  // 8 waves
+constexpr int NPART = 4;    // row parts of the column passes
+
+template <typename TIn, int C, int DK, int DV, bool PCH, int MT>
+__global__ void __launch_bounds__(NTHR2)
+bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
+               const float* __restrict__ beta, const float* __restrict__ Tmi,
+               const float* __restrict__ dQgi, const float* __restrict__ dWgi,
+               const float* __restrict__ dKhi, const float* __restrict__ dPsi,
+               const float* __restrict__ dT1i, const float* __restrict__ dgmi,
+               const float* __restrict__ dbpi, TIn* __restrict__ dqo, TIn* __restrict__ dko,
+               float* __restrict__ dgo, float* __restrict__ dbo, int T, int H, int NC, float scale)
+{
+    using G = Geo<C, DK, DV>;
+    constexpr int PD = G::PD, PC = G::PC, NB = G::NB;
+    constexpr int RPP = C / NPART;  // rows per part
+    constexpr int NW = NTHR2 / 64;
+    __shared__ float sT[C][PC], sdP[C][PC], sdA[C][PC], sX[C][PD], sY[C][PD], sZ[C][PD];
+    __shared__ float sbeta[C], stot[NPART][DK], sext[NPART][DK];
+
+    const int ch = blockIdx.x;
+    const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
+    const int t0 = n * C;
+    const int nvalid = min(C, T - t0);
+    const int tid = threadIdx.x, w = tid >> 6;
+    const size_t tok0 = ((size_t)b * T + t0) * H + h;
+    const size_t rsK = (size_t)H * DK;
+
+    // column threads: channel c, rows [p0, p0 + RPP)
+    const bool cp = tid < NPART * DK;
+    const int c = tid % DK, part = cp ? tid / DK : 0, p0 = part * RPP;
+
+    {
+        const float* Tp = Tmi + (size_t)ch * C * C;
+        for (int idx = tid; idx < C * C; idx += NTHR2) sT[idx / C][idx % C] = Tp[idx];
+        const float* dWp = dWgi + (size_t)ch * C * DK;
+        for (int idx = tid; idx < C * DK / 4; idx += NTHR2) {
+            const int r = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
+            st4(&sY[r][c4], load4<float>(dWp + r * DK + c4));
+        }
+        for (int r = tid; r < C; r += NTHR2) sbeta[r] = r < nvalid ? beta[tok0 + (size_t)r * H] : 0.f;
+    }
+    float a[RPP], qv[RPP], kv[RPP], Gm[RPP];
+    float dq[RPP], dk[RPP], dG[RPP], dbr[RPP];
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) {
+        const int r = p0 + i;
+        float gv = 0.f, qx = 0.f, kx = 0.f;
+        if (cp && r < nvalid) {
+            gv = PCH ? g[(tok0 + (size_t)r * H) * DK + c] : g[tok0 + (size_t)r * H];
+            qx = to_f32(q[tok0 * DK + r * rsK + c]);
+            kx = to_f32(k[tok0 * DK + r * rsK + c]);
+        }
+        a[i] = expf(gv);
+        qv[i] = qx;
+        kv[i] = kx;
+        dq[i] = dk[i] = dG[i] = dbr[i] = 0.f;
+    }
+    {
+        float pt = 1.f;
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) pt *= a[i];
+        if (cp) stot[part][c] = pt;
+    }
+    __syncthreads();
+
+    // ---- Gamma, Kh factor, X_K; contributions of dQg, dKh, dgam
+    if (cp) {
+        const float* dQp = dQgi + (size_t)ch * C * DK;
+        const float* dKp = dKhi + (size_t)ch * C * DK;
+        float pre = 1.f, suf = 1.f;
+        for (int pp = 0; pp < part; ++pp) pre *= stot[pp][c];
+        for (int pp = part + 1; pp < NPART; ++pp) suf *= stot[pp][c];
+        float Gr = pre;
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            Gr *= a[i];
+            Gm[i] = Gr;
+        }
+        float kap = suf, sumKh = 0.f;
+#pragma unroll
+        for (int i = RPP - 1; i >= 0; --i) {
+            const int r = p0 + i;
+            const float dqg = dQp[r * DK + c], dkh = dKp[r * DK + c];
+            dq[i] += scale * Gm[i] * dqg;
+            dG[i] += scale * qv[i] * Gm[i] * dqg;
+            const float khv = kv[i] * kap;
+            dk[i] += kap * dkh;
+            dG[i] -= khv * dkh;
+            sumKh += khv * dkh;
+            sX[r][c] = sbeta[r] * kv[i] * Gm[i];  // X_K
+            kap *= a[i];
+        }
+        sext[part][c] = sumKh;
+    }
+    __syncthreads();
+    if (cp && part == NPART - 1) {
+        float s = 0.f;
+        for (int pp = 0; pp < NPART; ++pp) s += sext[pp][c];
+        dG[RPP - 1] += s + Gm[RPP - 1] * dgmi[(size_t)ch * DK + c];
+    }
+
+    // ---- dX_K = T^T dW (-> sZ);  dT = dT(U) + dW X_K^T (-> sdA)
+    {
+        constexpr int T3 = NB * (DK / 16);
+        for (int idx = w; idx < T3; idx += NW) {
+            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+            f32x4 acc = mma16k<MT_F32, C>(zero4(), &sT[0][ti * 16], 1, PC, &sY[0][tj * 16], PD, 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sZ[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = acc[r];
+        }
+        const float* dT1p = dT1i + (size_t)ch * C * C;
+        for (int idx = w; idx < NB * NB; idx += NW) {
+            const int ti = idx / NB, tj = idx % NB;
+            f32x4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = dT1p[(ti * 16 + acc_row(r)) * C + tj * 16 + acc_col()];
+            acc = mma16k<MT_F32, DK>(acc, &sY[ti * 16][0], PD, 1, &sX[tj * 16][0], 1, PD);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sdA[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = acc[r];
+        }
+    }
+    __syncthreads();
+    // X_K contributions: dk += beta Gamma dX_K, dG += X_K o dX_K, dbeta += <k Gamma, dX_K>
+    if (cp) {
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            const int r = p0 + i;
+            const float dx = sZ[r][c];
+            const float kg = kv[i] * Gm[i];
+            dk[i] += sbeta[r] * Gm[i] * dx;
+            dG[i] += sbeta[r] * kg * dx;
+            dbr[i] += kg * dx;
+        }
+    }
+    // Y = dT T^T (-> sdP as scratch)
+    for (int idx = w; idx < NB * NB; idx += NW) {
+        const int ti = idx / NB, tj = idx % NB;
+        f32x4 acc = mma16k<MT_F32, C>(zero4(), &sdA[ti * 16][0], PC, 1, &sT[tj * 16][0], 1, PC);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sdP[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = acc[r];
+    }
+    __syncthreads();
+    // dA = -T^T Y, strictly lower
+    f32x4 dAt[(NB * NB + NW - 1) / NW];
+#pragma unroll
+    for (int m = 0; m < (NB * NB + NW - 1) / NW; ++m) {
+        const int idx = w + NW * m;
+        if (idx < NB * NB) {
+            const int ti = idx / NB, tj = idx % NB;
+            dAt[m] = mma16k<MT_F32, C>(zero4(), &sT[0][ti * 16], 1, PC, &sdP[0][tj * 16], PC, 1);
+        }
+    }
+    __syncthreads();
+    {
+        const float* dPp = dPsi + (size_t)ch * C * C;
+#pragma unroll
+        for (int m = 0; m < (NB * NB + NW - 1) / NW; ++m) {
+            const int idx = w + NW * m;
+            if (idx < NB * NB) {
+                const int ti = idx / NB, tj = idx % NB;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
+                    sdA[i][j] = i > j ? -dAt[m][r] : 0.f;
+                    sdP[i][j] = i >= j ? scale * dPp[i * C + j] : 0.f;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // diagonal scores (E = 1): P_ii = q_i . k_i
+    if (cp) {
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            const int r = p0 + i;
+            const float dp = sdP[r][r];
+            dq[i] += dp * kv[i];
+            dk[i] += dp * qv[i];
+        }
+    }
+
+    // ---- score gradients, level by level (h = C/2 .. 1)
+#pragma unroll
+    for (int lvl = 0; (C >> (lvl + 1)) >= 1; ++lvl) {
+        const int hl = C >> (lvl + 1);
+        float F[RPP];
+        bool qside[RPP];
+        // level-hl factor of each own row: query rows prod_{s=m+1..r} a_s,
+        // key rows prod_{s=r+1..m} a_s, m the last token of the earlier half
+        if (hl >= RPP) {
+            const int base = (p0 / (2 * hl)) * (2 * hl);
+            const bool qs = p0 >= base + hl;
+            if (qs) {
+                float pre = 1.f;
+                for (int pp = (base + hl) / RPP; pp < part; ++pp) pre *= stot[pp][c];
+                float Fr = pre;
+#pragma unroll
+                for (int i = 0; i < RPP; ++i) {
+                    Fr *= a[i];
+                    F[i] = Fr;
+                    qside[i] = true;
+                }
+            } else {
+                float suf = 1.f;
+                for (int pp = part + 1; pp < (base + hl) / RPP; ++pp) suf *= stot[pp][c];
+                float Fr = suf;
+#pragma unroll
+                for (int i = RPP - 1; i >= 0; --i) {
+                    F[i] = Fr;
+                    qside[i] = false;
+                    Fr *= a[i];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u0 = 0; u0 < RPP; u0 += (hl < RPP ? hl : RPP)) {
+                const bool qs = ((p0 + u0) / hl) & 1;
+                if (qs) {
+                    float Fr = 1.f;
+#pragma unroll
+                    for (int i = 0; i < hl; ++i) {
+                        Fr *= a[u0 + i];
+                        F[u0 + i] = Fr;
+                        qside[u0 + i] = true;
+                    }
+                } else {
+                    float Fr = 1.f;
+#pragma unroll
+                    for (int i = hl - 1; i >= 0; --i) {
+                        F[u0 + i] = Fr;
+                        qside[u0 + i] = false;
+                        Fr *= a[u0 + i];
+                    }
+                }
+            }
+        }
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                sX[p0 + i][c] = qv[i] * F[i];  // QK
+                sY[p0 + i][c] = kv[i] * F[i];  // KK
+            }
+        }
+        __syncthreads();
+        // R1 = dP_h KK (query rows) + dP_h^T QK (key rows);
+        // R2 = dA_h KK (query rows) + (diag(beta) dA_h)^T KK (key rows)
+        constexpr int T3 = NB * (DK / 16), M3 = (T3 + NW - 1) / NW;
+        f32x4 r2[M3];
+#pragma unroll
+        for (int m = 0; m < M3; ++m) {
+            const int idx = w + NW * m;
+            if (idx >= T3) continue;
+            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+            f32x4 r1 = zero4();
+            r2[m] = zero4();
+            if (hl >= 16) {
+                const int base = (ti * 16 / (2 * hl)) * (2 * hl);
+                const bool qs = ti * 16 >= base + hl;
+                if (qs) {
+                    r1 = mma16fd<MT>(r1, [&](int i, int kx) { return sdP[ti * 16 + i][base + kx]; },
+                                     [&](int kx, int j) { return sY[base + kx][tj * 16 + j]; }, hl);
+                    r2[m] = mma16fd<MT>(r2[m], [&](int i, int kx) { return sdA[ti * 16 + i][base + kx]; },
+                                        [&](int kx, int j) { return sY[base + kx][tj * 16 + j]; }, hl);
+                } else {
+                    const int qb = base + hl;
+                    r1 = mma16fd<MT>(r1, [&](int i, int kx) { return sdP[qb + kx][ti * 16 + i]; },
+                                     [&](int kx, int j) { return sX[qb + kx][tj * 16 + j]; }, hl);
+                    r2[m] = mma16fd<MT>(r2[m], [&](int i, int kx) { return sbeta[qb + kx] * sdA[qb + kx][ti * 16 + i]; },
+                                        [&](int kx, int j) { return sY[qb + kx][tj * 16 + j]; }, hl);
+                }
+            } else {
+                const int tb = ti * 16;
+                r1 = mma16f<MT, 16>(r1,
+                    [&](int i, int kx) { return in_level(i, kx, hl) ? sdP[tb + i][tb + kx] : 0.f; },
+                    [&](int kx, int j) { return sY[tb + kx][tj * 16 + j]; });
+                r1 = mma16f<MT, 16>(r1,
+                    [&](int i, int kx) { return in_level(kx, i, hl) ? sdP[tb + kx][tb + i] : 0.f; },
+                    [&](int kx, int j) { return sX[tb + kx][tj * 16 + j]; });
+                r2[m] = mma16f<MT, 16>(r2[m],
+                    [&](int i, int kx) {
+                        return in_level(i, kx, hl) ? sdA[tb + i][tb + kx]
+                             : (in_level(kx, i, hl) ? sbeta[tb + kx] * sdA[tb + kx][tb + i] : 0.f);
+                    },
+                    [&](int kx, int j) { return sY[tb + kx][tj * 16 + j]; });
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sZ[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = r1[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < M3; ++m) {
+            const int idx = w + NW * m;
+            if (idx >= T3) continue;
+            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sX[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = r2[m][r];
+        }
+        __syncthreads();
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                const int r = p0 + i;
+                const float R1 = sZ[r][c], R2 = sX[r][c];
+                if (qside[i]) {
+                    const float bt = sbeta[r];
+                    dq[i] += F[i] * R1;
+                    dk[i] += bt * F[i] * R2;
+                    dG[i] += qv[i] * F[i] * R1 + bt * kv[i] * F[i] * R2;
+                    dbr[i] += kv[i] * F[i] * R2;
+                } else {
+                    dk[i] += F[i] * (R1 + R2);
+                    dG[i] -= kv[i] * F[i] * (R1 + R2);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- dg = reverse cumulative sum of dG over the chunk; dbeta; dq, dk out
+    if (cp) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = RPP - 1; i >= 0; --i) {
+            s += dG[i];
+            dG[i] = s;
+        }
+        sext[part][c] = s;
+    }
+    __syncthreads();
+    if (cp) {
+        float add = 0.f;
+        for (int pp = part + 1; pp < NPART; ++pp) add += sext[pp][c];
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            const int r = p0 + i;
+            dG[i] += add;
+            sZ[r][c] = dG[i];
+            sX[r][c] = dbr[i];
+            if (r < nvalid) {
+                dqo[tok0 * DK + r * rsK + c] = from_f32<TIn>(dq[i]);
+                dko[tok0 * DK + r * rsK + c] = from_f32<TIn>(dk[i]);
+                if (PCH) dgo[(tok0 + (size_t)r * H) * DK + c] = dG[i];
+            }
+        }
+    }
+    __syncthreads();
+    for (int r = tid; r < nvalid; r += NTHR2) {
+        float sb = dbpi[(size_t)ch * C + r];
+        for (int cc = 0; cc < DK; ++cc) sb += sX[r][cc];
+        dbo[tok0 + (size_t)r * H] = sb;
+        if (!PCH) {
+            float sg = 0.f;
+            for (int cc = 0; cc < DK; ++cc) sg += sZ[r][cc];
+            dgo[tok0 + (size_t)r * H] = sg;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+template <typename TIn, int C, int DK, int DV>
+gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, const float* h0, const void* dO, const float* dhT,
+                      void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0, char* ws,
+                      hipStream_t st)
+{
+    constexpr int MT = std::is_same<TIn, bf16>::value ? MT_BF16 : MT_F32;
+    gdn_status s = recompute_dispatch(p, q, k, v, g, beta, h0, ws, st);
+    if (s != GDN_OK) return s;
+    const int BH = p.B * p.H;
+    {
+        using SC = BScanCfg<DV>;
+        dim3 grid((unsigned)(((BH + 7) / 8) * 8 * SC::NS)), block(NTHR);
+        hipLaunchKernelGGL((bscan_kernel<TIn, C, DK, DV, MT_F32>), grid, block, 0, st,
+                           (const float*)(ws + p.o_Qg), (const float*)(ws + p.o_Kh),
+                           (const float*)(ws + p.o_W), (const float*)(ws + p.o_Ps),
+                           (const float*)(ws + p.o_gam), (const TIn*)dO, dhT,
+                           (float*)(ws + p.o_dSt), (float*)(ws + p.o_dDt), dh0, BH, p.T, p.H, p.NC);
+        GDN_HIP_CHECK_LAUNCH();
+    }
+    dim3 gch((unsigned)p.n_ch);
+    hipLaunchKernelGGL((bchunk1_kernel<TIn, C, DK, DV, MT_F32>), gch, dim3(NTHR), 0, st,
+                       (const TIn*)v, beta, (const TIn*)dO, (const float*)(ws + p.o_W),
+                       (const float*)(ws + p.o_U), (const float*)(ws + p.o_Tm),
+                       (const float*)(ws + p.o_Sst), (const float*)(ws + p.o_dSt),
+                       (const float*)(ws + p.o_dDt), (TIn*)dv, (float*)(ws + p.o_dQg),
+                       (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh), (float*)(ws + p.o_dPs),
+                       (float*)(ws + p.o_dT1), (float*)(ws + p.o_dgm), (float*)(ws + p.o_dbp), p.T,
+                       p.H, p.NC);
+    GDN_HIP_CHECK_LAUNCH();
+    const void* args_dummy = nullptr;
+    (void)args_dummy;
+    if (p.decay == GDN_DECAY_PER_CHANNEL)
+        hipLaunchKernelGGL((bchunk2_kernel<TIn, C, DK, DV, true, MT>), gch, dim3(NTHR2), 0, st,
+                           (const TIn*)q, (const TIn*)k, g, beta, (const float*)(ws + p.o_Tm),
+                           (const float*)(ws + p.o_dQg), (const float*)(ws + p.o_dWg),
+                           (const float*)(ws + p.o_dKh), (const float*)(ws + p.o_dPs),
+                           (const float*)(ws + p.o_dT1), (const float*)(ws + p.o_dgm),
+                           (const float*)(ws + p.o_dbp), (TIn*)dq, (TIn*)dk, dg, dbeta, p.T, p.H,
+                           p.NC, p.scale);
+    else
+        hipLaunchKernelGGL((bchunk2_kernel<TIn, C, DK, DV, false, MT>), gch, dim3(NTHR2), 0, st,
+                           (const TIn*)q, (const TIn*)k, g, beta, (const float*)(ws + p.o_Tm),
+                           (const float*)(ws + p.o_dQg), (const float*)(ws + p.o_dWg),
+                           (const float*)(ws + p.o_dKh), (const float*)(ws + p.o_dPs),
+                           (const float*)(ws + p.o_dT1), (const float*)(ws + p.o_dgm),
+                           (const float*)(ws + p.o_dbp), (TIn*)dq, (TIn*)dk, dg, dbeta, p.T, p.H,
+                           p.NC, p.scale);
+    GDN_HIP_CHECK_LAUNCH();
+    return GDN_OK;
+}
+
+template <typename TIn>
+gdn_status backward_dt(const Plan& p, const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* h0, const void* dO, const float* dhT,
+                       void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0, char* ws,
+                       hipStream_t st)
+{
+#define GDN_BWD(C_, D_)                                                                           \
+    if (p.C == C_ && p.Dk == D_ && p.Dv == D_)                                                     \
+        return backward_t<TIn, C_, D_, D_>(p, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, \
+                                           dh0, ws, st);
+    GDN_BWD(64, 128) GDN_BWD(64, 64) GDN_BWD(16, 16)
+#undef GDN_BWD
+    return GDN_ERR_UNSUPPORTED;
+}
+
+gdn_status backward_dispatch(const Plan& p, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const float* h0, const void* dO,
+                             const float* dhT, void* dq, void* dk, void* dv, float* dg,
+                             float* dbeta, float* dh0, void* ws, hipStream_t st)
+{
+    if (p.dtype == GDN_BF16)
+        return backward_dt<bf16>(p, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
+                                 (char*)ws, st);
+    return backward_dt<float>(p, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
+                              (char*)ws, st);
+}
+
+}  // namespace gdn

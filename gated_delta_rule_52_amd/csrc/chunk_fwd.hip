@@ -513,11 +513,29 @@ gdn_status forward_dispatch(const Plan& p, const void* q, const void* k, const v
     return forward_dt<float>(p, q, k, v, g, beta, h0, o, hT, (char*)ws, st);
 }
 
-gdn_status backward_dispatch(const Plan& p, const void* q, const void* k, const void* v,
-                             const float* g, const float* beta, const float* h0, const void* dO,
-                             const float* dhT, void* dq, void* dk, void* dv, float* dg,
-                             float* dbeta, float* dh0, void* ws, hipStream_t st)
+// Forward recompute for the backward pass: the prep outputs (with T) and the
+// state at the start of every chunk; no outputs are written.
+template <typename TIn, int C, int DK, int DV>
+gdn_status recompute_t(const Plan& p, const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* h0, char* ws, hipStream_t st)
 {
+    constexpr int MT = std::is_same<TIn, bf16>::value ? MT_BF16 : MT_F32;
+    gdn_status s = run_prep<TIn, C, DK, DV, MT>(p, q, k, v, g, beta, ws, true, st);
+    if (s != GDN_OK) return s;
+    return run_scan<TIn, C, DK, DV, MT_F32, true, false>(p, h0, nullptr, nullptr, ws, st);
+}
+
+gdn_status recompute_dispatch(const Plan& p, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* h0, void* ws,
+                              hipStream_t st)
+{
+#define GDN_REC(C_, D_)                                                                        \
+    if (p.C == C_ && p.Dk == D_ && p.Dv == D_)                                                  \
+        return p.dtype == GDN_BF16                                                              \
+                   ? recompute_t<bf16, C_, D_, D_>(p, q, k, v, g, beta, h0, (char*)ws, st)      \
+                   : recompute_t<float, C_, D_, D_>(p, q, k, v, g, beta, h0, (char*)ws, st);
+    GDN_REC(64, 128) GDN_REC(64, 64) GDN_REC(16, 16)
+#undef GDN_REC
     return GDN_ERR_UNSUPPORTED;
 }
 

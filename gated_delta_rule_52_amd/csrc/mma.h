@@ -74,3 +74,59 @@ __device__ __forceinline__ f32x4 mma16k(f32x4 acc, const float* __restrict__ A, 
 }
 
 }  // namespace gdn
+
+namespace gdn {
+
+// Functor form: fa(i, k) and fb(k, j) return the operand elements (masks,
+// per-row scalings, transposes are expressed inside them).  K is the
+// contraction length; elements with k >= K are never requested.
+template <int MT, int K, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mma16f(f32x4 acc, FA fa, FB fb)
+{
+    const int l = lane_id();
+    const int r = l & 15, kk = l >> 4;
+    if (MT == MT_F32) {
+#pragma unroll
+        for (int k = 0; k < K; k += 4) acc = mfma_f32_16x16x4(fa(r, k + kk), fb(k + kk, r), acc);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; k += 32) {
+            bf16x8 a, b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kx = k + 8 * kk + e;
+                const bool in = (K % 32 == 0) || kx < K;
+                a[e] = (__bf16)(in ? fa(r, kx) : 0.f);
+                b[e] = (__bf16)(in ? fb(kx, r) : 0.f);
+            }
+            acc = mfma_bf16_16x16x32(a, b, acc);
+        }
+    }
+    return acc;
+}
+
+// Runtime contraction length (multiple of 4 for MT_F32).
+template <int MT, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mma16fd(f32x4 acc, FA fa, FB fb, int K)
+{
+    const int l = lane_id();
+    const int r = l & 15, kk = l >> 4;
+    if (MT == MT_F32) {
+        for (int k = 0; k < K; k += 4) acc = mfma_f32_16x16x4(fa(r, k + kk), fb(k + kk, r), acc);
+    } else {
+        for (int k = 0; k < K; k += 32) {
+            bf16x8 a, b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kx = k + 8 * kk + e;
+                const bool in = kx < K;
+                a[e] = (__bf16)(in ? fa(r, kx) : 0.f);
+                b[e] = (__bf16)(in ? fb(kx, r) : 0.f);
+            }
+            acc = mfma_bf16_16x16x32(a, b, acc);
+        }
+    }
+    return acc;
+}
+
+}  // namespace gdn

@@ -15,6 +15,9 @@
 //   Sst [ch][Dk][Dv]  state at the start of chunk n
 //   dSt [ch][Dk][Dv]  gradient with respect to the state at the end of chunk n
 //   dDt [ch][C][Dv]   gradient with respect to the chunk's deltas D
+//   dQg [ch][C][Dk]   dL/dQg,  dWg [ch][C][Dk] dL/dW,  dKh [ch][C][Dk] dL/dKh
+//   dPs [ch][C][C]    dL/dPs,  dT1 [ch][C][C]  dL/dT through U
+//   dgm [ch][Dk]      dL/dgam, dbp [ch][C]     part of dL/dbeta (through U)
 // G is the chunk-local inclusive cumulative log-decay and Gamma = exp(G).
 #pragma once
 
@@ -31,6 +34,7 @@ struct Plan {
     size_t n_ch;  // B * H * NC
     // byte offsets into the workspace
     size_t o_W, o_U, o_Qg, o_Kh, o_Ps, o_gam, o_Tm, o_Sst, o_dSt, o_dDt;
+    size_t o_dQg, o_dWg, o_dKh, o_dPs, o_dT1, o_dgm, o_dbp;
     size_t ws_fwd_bytes, ws_bwd_bytes;
 };
 
@@ -65,6 +69,13 @@ inline Plan make_plan(const gdn_shape& s, float scale)
     p.o_Sst = off; off = align256(off + n * Dk * Dv * f);
     p.o_dSt = off; off = align256(off + n * Dk * Dv * f);
     p.o_dDt = off; off = align256(off + n * C * Dv * f);
+    p.o_dQg = off; off = align256(off + n * C * Dk * f);
+    p.o_dWg = off; off = align256(off + n * C * Dk * f);
+    p.o_dKh = off; off = align256(off + n * C * Dk * f);
+    p.o_dPs = off; off = align256(off + n * C * C * f);
+    p.o_dT1 = off; off = align256(off + n * C * C * f);
+    p.o_dgm = off; off = align256(off + n * Dk * f);
+    p.o_dbp = off; off = align256(off + n * C * f);
     p.ws_bwd_bytes = off;
     return p;
 }
