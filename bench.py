@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Throughput of the gated delta-rule layer on one MI355X.
+
+A step is one forward plus one backward of the chunked per-channel-decay layer
+(gdn_forward then gdn_backward: every kernel of the hot path) over one batch of
+synthetic inputs shaped like the pages' training workload: B=8, T=4096, H=6,
+Dk=Dv=128, chunk 64, bf16 q/k/v with fp32 decay, gates and state (Marin note,
+"Single-device benchmark"; atomic_ops card, "Benchmarks").  Inputs are resident
+in HBM before timing starts.  The result is gated on correctness first: sampled
+heads are checked against the CPU oracle (atomic_ops card, "Reproduce": timings
+are correctness-gated).
+
+Printed: ONE JSON line.  value = tokens/s of the fwd+bwd step (tokens = B*T
+per call, each token carrying all H heads).  Also reported: forward-only
+tokens/s, the decode step (B=256, H=16, 128x128 state) in GB/s, per-kernel
+device times from HIP events recorded around each launch on its stream, the
+roofline of the dominant kernel, and the CPU oracle timed on this host.
+
+    python bench.py [--steps K] [--warmup W] [--dtype bf16|f32] [--batch B]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+# contraction dtype of each kernel's dominant matrix products
+KERNEL_MFMA = {"prep": "bf16", "prep_bwd": "bf16", "scan": "f32", "scan_save": "f32",
+               "bscan": "f32", "bchunk1": "f32", "bchunk2": "bf16"}
+# TPU v6e, Sept-2026 prototype, B=8 T=4096 H=6 d=128 BF16 fwd+bwd: 22.44 ms
+# (Marin note, "Single-device benchmark") -> B*T / 22.44 ms
+PAGES_FWDBWD_TOKENS_S = 8 * 4096 / 22.44e-3
+
+
+def kernel_work(name, B, T, H, C, DK, DV, in_bytes):
+    """Algorithmic (flops, bytes) of one launch: the contractions the kernel
+    must perform and the HBM bytes it must move in this design (each input
+    read once, each output written once)."""
+    NC = (T + C - 1) // C
+    n = B * H * NC
+    f4 = 4
+    tri = C * (C + 1) // 2
+    backward = name in ("prep_bwd", "scan_save")
+    if name in ("prep", "prep_bwd"):
+        fl = 2 * C * C * DK + 2 * tri * (DK + DV)
+        by = (2 * C * DK + C * DV) * in_bytes + C * DK * f4 + C * f4 \
+            + (3 * C * DK + C * DV + C * C + DK) * f4 + (C * C * f4 if backward else 0)
+    elif name in ("scan", "scan_save"):
+        if backward:  # state-saving pass: D and the state update only
+            fl = 4 * C * DK * DV
+            by = (2 * C * DK + C * DV + DK) * f4 + DK * DV * f4
+        else:
+            fl = 6 * C * DK * DV + 2 * tri * DV
+            by = (3 * C * DK + C * DV + C * C + DK) * f4 + C * DV * in_bytes
+    elif name == "bscan":
+        fl = 6 * C * DK * DV + 2 * tri * DV
+        by = (3 * C * DK + C * C + DK) * f4 + C * DV * in_bytes + (DK * DV + C * DV) * f4
+    elif name == "bchunk1":
+        fl = 2 * C * DK * DV + 2 * tri * DV + 6 * C * DK * DV + 4 * C * C * DV
+        by = (2 * C * DK + C * DV * 2 + C * C + 2 * DK * DV) * f4 + 3 * C * DV * in_bytes \
+            + (3 * C * DK + 2 * C * C + DK + C) * f4
+    elif name == "bchunk2":
+        fl = 2 * tri * DK + 2 * C * C * DK + 4 * C * C * C + 4 * (C * (C - 1) // 2) * 2 * DK
+        by = 2 * C * DK * in_bytes + C * DK * f4 + C * f4 + (C * C + 3 * C * DK + 2 * C * C + DK + C) * f4 \
+            + 2 * C * DK * in_bytes + C * DK * f4 + C * f4
+    else:
+        return None
+    return fl * n, by * n
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--batch", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the layer shards over (batch, head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_52_amd as gdn
+    import gdn_inputs as gi
+    from gated_delta_rule_52_amd.profile import LaunchRecorder
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    B, T, H, D, C = args.batch, 4096, 6, 128, 64
+    dt = args.dtype
+    in_bytes = 2 if dt == "bf16" else 4
+    log(f"[bench] workload B={B} T={T} H={H} D={D} dtype={dt}: generating inputs")
+    inp = gi.train(dtype=dt, B=B, grads=True)
+    to = {}
+    for k_, x in inp.items():
+        if isinstance(x, np.ndarray):
+            if x.dtype == np.uint16:
+                to[k_] = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+            else:
+                to[k_] = torch.from_numpy(x).cuda()
+    scale = inp["meta"]["scale"]
+    q, k, v, g, beta, dO, dhT = (to[n] for n in ("q", "k", "v", "g", "beta", "dO", "dhT"))
+    sh = gdn.make_shape(q, v, g, scale, C)
+    ws_f = gdn.workspace(sh, False, q.device)
+    ws_b = gdn.workspace(sh, True, q.device)
+    o = torch.empty_like(v)
+    hT = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+
+    def fwd():
+        gdn.gdn_forward(q, k, v, g, beta, None, scale=scale, chunk=C, o=o, hT=hT, ws=ws_f)
+
+    def step():
+        fwd()
+        return gdn.gdn_backward(q, k, v, g, beta, dO, None, dhT, scale=scale, chunk=C, ws=ws_b)
+
+    # ---- correctness gate on sampled heads (oracle = token-serial CPU reference)
+    import oracle
+    log("[bench] correctness gate")
+    grads = step()
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (B - 1, H - 1)]
+
+    def pick(x, b, h):
+        return x[b, :, h].float().cpu().numpy().astype(np.float64)
+
+    sub = {n: np.stack([inp[n][b, :, h] for b, h in pairs], axis=1)[None]
+           for n in ("q", "k", "v", "g", "beta", "dO")}
+    sub["dhT"] = np.stack([inp["dhT"][b, h] for b, h in pairs])[None]
+    o_ref, h_ref = oracle.forward(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], scale)
+    g_ref = oracle.backward(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], scale, sub["dO"],
+                            dhT=sub["dhT"])
+
+    def rel(x, y):
+        return float(np.max(np.abs(x - y)) / np.max(np.abs(y)))
+
+    par = {"o": rel(np.stack([pick(o, b, h) for b, h in pairs], 1)[None], o_ref),
+           "hT": rel(np.stack([hT[b, h].cpu().numpy() for b, h in pairs])[None], h_ref)}
+    gn = dict(zip(("dq", "dk", "dv", "dg", "dbeta"), grads[:5]))
+    for name, x in gn.items():
+        got = np.stack([pick(x, b, h) for b, h in pairs], 1)[None]
+        par[name] = rel(got, g_ref[name])
+    par["dh0"] = rel(np.stack([grads[5][b, h].cpu().numpy() for b, h in pairs])[None], g_ref["dh0"])
+    tol = 2e-2 if dt == "bf16" else 1e-5
+    parity_ok = all(e <= tol for e in par.values())
+    log(f"[bench] parity (max rel err, tol {tol}): " + ", ".join(f"{k_} {e:.2e}" for k_, e in par.items()))
+
+    # ---- fwd+bwd: warmup, then exactly K timed steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    launches_per_step = 7
+    rec = LaunchRecorder(args.steps * launches_per_step + 16)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    with rec:
+        for _ in range(args.steps):
+            step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    value = B * T / (ms_step * 1e-3)
+    per = {name: (float(np.mean(ms)), len(ms)) for name, ms in rec.by_kernel().items()}
+    rec.close()
+    log(f"[bench] fwd+bwd {ms_step:.3f} ms/step ({value / 1e6:.2f} M tokens/s); wall {wall:.3f} s")
+    for name, (ms, cnt) in sorted(per.items(), key=lambda x: -x[1][0] * x[1][1]):
+        log(f"[bench]   {name:8s} {ms * 1e3:9.1f} us x {cnt // args.steps}/step")
+
+    # dominant kernel by device time per step, and its roofline
+    dom = max(per, key=lambda n: per[n][0] * per[n][1])
+    fl, by = kernel_work(dom, B, T, H, C, D, D, in_bytes)
+    dur = per[dom][0] * 1e-3
+    mt = KERNEL_MFMA.get(dom) if dt == "bf16" else "f32"
+    ridge = PEAK_TFLOPS[mt] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if fl / by >= ridge:
+        roof = {"bound": "mfma", "achieved": fl / dur / 1e12, "peak": PEAK_TFLOPS[mt],
+                "unit": "TFLOP/s", "mfma_dtype": mt}
+    else:
+        roof = {"bound": "hbm", "achieved": by / dur / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["avg_launch_us"] = dur * 1e6
+    roof["algorithmic_flops_per_launch"] = fl
+    roof["algorithmic_bytes_per_launch"] = by
+
+    # ---- forward only
+    for _ in range(3):
+        fwd()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        fwd()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_fwd = ev0.elapsed_time(ev1) / args.steps
+    fwd_tps = B * T / (ms_fwd * 1e-3)
+    log(f"[bench] fwd {ms_fwd:.3f} ms ({fwd_tps / 1e6:.2f} M tokens/s)")
+
+    # ---- decode: B=256 H=16 128x128 fp32 state, one token per step
+    decode = None
+    if not args.no_decode:
+        dinp = gi.decode(steps=8)
+        Bd, Hd = 256, 16
+        state = torch.from_numpy(dinp["h0"]).cuda()
+        steps_in = []
+        for t in range(8):
+            steps_in.append(tuple(torch.from_numpy(np.ascontiguousarray(dinp[n][:, t])).cuda()
+                                  for n in ("q", "k", "v", "g", "beta")))
+        od = torch.empty((Bd, 1, Hd, D), dtype=torch.float32, device="cuda")
+        for t in range(8):
+            gdn.gdn_decode_step(*steps_in[t], state, o=od)
+        torch.cuda.synchronize()
+        nd = 64
+        drec = LaunchRecorder(nd)
+        ev0.record()
+        with drec:
+            for i in range(nd):
+                gdn.gdn_decode_step(*steps_in[i % 8], state, o=od)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_dec = ev0.elapsed_time(ev1) / nd
+        kdec = float(np.mean(drec.by_kernel()["decode"]))
+        drec.close()
+        dbytes = Bd * Hd * (2 * D * D * 4 + 4 * D * 4 + 4) + Bd * Hd * D * 4
+        decode = {"workload": "decode step B=256 H=16 Dk=Dv=128, fp32 state, per-channel g",
+                  "ms_per_step": ms_dec, "kernel_us": kdec * 1e3,
+                  "tokens_per_s": Bd / (ms_dec * 1e-3),
+                  "achieved_GBs": dbytes / (kdec * 1e-3) / 1e9,
+                  "frac_hbm_peak": dbytes / (kdec * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "algorithmic_bytes_per_step": dbytes}
+        log(f"[bench] decode {kdec * 1e3:.1f} us/step, {decode['achieved_GBs']:.0f} GB/s")
+
+    # ---- CPU oracle on this host: a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu:
+        nthr = oracle.max_threads()
+        nh = min(B * H, max(2, nthr))
+        pairs = [(i // H, i % H) for i in range(nh)]
+        s = {n: np.stack([inp[n][b, :, h] for b, h in pairs], axis=1)[None]
+             for n in ("q", "k", "v", "g", "beta", "dO")}
+        s = {n: (x if x.dtype != np.uint16 else gi.as_f64(x)) for n, x in s.items()}
+        s = {n: np.ascontiguousarray(x, dtype=np.float64) for n, x in s.items()}
+        s["dhT"] = np.stack([inp["dhT"][b, h] for b, h in pairs])[None].astype(np.float64)
+        log(f"[bench] cpu oracle: {nh} heads x {T} tokens fwd+bwd on {nthr} threads")
+        t0 = time.perf_counter()
+        oracle.forward(s["q"], s["k"], s["v"], s["g"], s["beta"], scale)
+        oracle.backward(s["q"], s["k"], s["v"], s["g"], s["beta"], scale, s["dO"], dhT=s["dhT"])
+        tc = time.perf_counter() - t0
+        cpu = {"value": (nh / H) * T / tc, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+               "sample": f"{nh} of {B * H} (batch, head) sequences, T={T}, fwd+bwd, float64 "
+                         f"token-serial; tokens counted as heads/H*T; {tc:.1f} s"}
+        log(f"[bench] cpu oracle {cpu['value']:.0f} tokens/s in {tc:.1f} s")
+
+    line = {
+        "metric": "tokens/s fwd and fwd+bwd at B=8 T=4096 H=6 d=128; % MFMA/HBM peak",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": value / PAGES_FWDBWD_TOKENS_S if (dt == "bf16" and B == 8) else None,
+        "baseline_note": "pages' figure for this workload is TPU v6e (22.44 ms, Sept-2026 "
+                         "prototype): context, not a like-for-like target",
+        "dtype": dt,
+        "data": "synthetic (seeded PCG64; L2-normalised q,k; beta=sigmoid, g=-softplus of N(0,1))",
+        "config": {"workload": f"chunked gated delta rule fwd+bwd, per-channel decay, B={B} "
+                               f"T={T} H={H} Dk=Dv={D}, chunk {C}, {dt} q/k/v, fp32 state",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": D,
+                   "parallelism": "single GPU"},
+        "fwd_tokens_per_s": fwd_tps,
+        "fwd_ms": ms_fwd,
+        "parity_ok": parity_ok,
+        "parity_max_rel_err": par,
+        "kernels_avg_us": {n: v_[0] * 1e3 for n, v_ in per.items()},
+        "roofline": roof,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,7 +31,9 @@ GDN_DECAY_PER_HEAD, GDN_DECAY_PER_CHANNEL = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_ALIGNMENT",
           4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
 EXPORTS = ("gdn_new_state", "gdn_workspace_bytes", "gdn_forward", "gdn_backward",
-           "gdn_decode_step", "gdn_status_string")
+           "gdn_decode_step", "gdn_status_string",
+           # include/gdn_profile.h
+           "gdn_profile_begin", "gdn_profile_end", "gdn_profile_launch_name")
 
 
 class GdnShape(ctypes.Structure):

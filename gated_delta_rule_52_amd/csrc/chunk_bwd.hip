@@ -712,7 +712,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
     {
         using SC = BScanCfg<DV>;
         dim3 grid((unsigned)(((BH + 7) / 8) * 8 * SC::NS)), block(NTHR);
-        hipLaunchKernelGGL((bscan_kernel<TIn, C, DK, DV, MT_F32>), grid, block, 0, st,
+        GDN_LAUNCH("bscan", (bscan_kernel<TIn, C, DK, DV, MT_F32>), grid, block, st,
                            (const float*)(ws + p.o_Qg), (const float*)(ws + p.o_Kh),
                            (const float*)(ws + p.o_W), (const float*)(ws + p.o_Ps),
                            (const float*)(ws + p.o_gam), (const TIn*)dO, dhT,
@@ -720,7 +720,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
         GDN_HIP_CHECK_LAUNCH();
     }
     dim3 gch((unsigned)p.n_ch);
-    hipLaunchKernelGGL((bchunk1_kernel<TIn, C, DK, DV, MT_F32>), gch, dim3(NTHR), 0, st,
+    GDN_LAUNCH("bchunk1", (bchunk1_kernel<TIn, C, DK, DV, MT_F32>), gch, dim3(NTHR), st,
                        (const TIn*)v, beta, (const TIn*)dO, (const float*)(ws + p.o_W),
                        (const float*)(ws + p.o_U), (const float*)(ws + p.o_Tm),
                        (const float*)(ws + p.o_Sst), (const float*)(ws + p.o_dSt),
@@ -732,7 +732,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
     const void* args_dummy = nullptr;
     (void)args_dummy;
     if (p.decay == GDN_DECAY_PER_CHANNEL)
-        hipLaunchKernelGGL((bchunk2_kernel<TIn, C, DK, DV, true, MT>), gch, dim3(NTHR2), 0, st,
+        GDN_LAUNCH("bchunk2", (bchunk2_kernel<TIn, C, DK, DV, true, MT>), gch, dim3(NTHR2), st,
                            (const TIn*)q, (const TIn*)k, g, beta, (const float*)(ws + p.o_Tm),
                            (const float*)(ws + p.o_dQg), (const float*)(ws + p.o_dWg),
                            (const float*)(ws + p.o_dKh), (const float*)(ws + p.o_dPs),
@@ -740,7 +740,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                            (const float*)(ws + p.o_dbp), (TIn*)dq, (TIn*)dk, dg, dbeta, p.T, p.H,
                            p.NC, p.scale);
     else
-        hipLaunchKernelGGL((bchunk2_kernel<TIn, C, DK, DV, false, MT>), gch, dim3(NTHR2), 0, st,
+        GDN_LAUNCH("bchunk2", (bchunk2_kernel<TIn, C, DK, DV, false, MT>), gch, dim3(NTHR2), st,
                            (const TIn*)q, (const TIn*)k, g, beta, (const float*)(ws + p.o_Tm),
                            (const float*)(ws + p.o_dQg), (const float*)(ws + p.o_dWg),
                            (const float*)(ws + p.o_dKh), (const float*)(ws + p.o_dPs),

@@ -453,11 +453,11 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
     float* Tm = want_T ? (float*)(ws + p.o_Tm) : nullptr;
     dim3 grid((unsigned)p.n_ch), block(NTHR);
     if (p.decay == GDN_DECAY_PER_CHANNEL)
-        hipLaunchKernelGGL((prep_kernel<TIn, C, DK, DV, true, MT>), grid, block, 0, st,
+        GDN_LAUNCH(want_T ? "prep_bwd" : "prep", (prep_kernel<TIn, C, DK, DV, true, MT>), grid, block, st,
                            (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
                            p.scale, W, U, Qg, Kh, Ps, gam, Tm);
     else
-        hipLaunchKernelGGL((prep_kernel<TIn, C, DK, DV, false, MT>), grid, block, 0, st,
+        GDN_LAUNCH(want_T ? "prep_bwd" : "prep", (prep_kernel<TIn, C, DK, DV, false, MT>), grid, block, st,
                            (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
                            p.scale, W, U, Qg, Kh, Ps, gam, Tm);
     GDN_HIP_CHECK_LAUNCH();
@@ -471,7 +471,7 @@ gdn_status run_scan(const Plan& p, const float* h0, void* o, float* hT, char* ws
     const int BH = p.B * p.H;
     const int ngrp = (BH + 7) / 8;
     dim3 grid((unsigned)(ngrp * 8 * SC::NS)), block(NTHR);
-    hipLaunchKernelGGL((scan_kernel<TIn, C, DK, DV, MT, SAVE, OUT>), grid, block, 0, st,
+    GDN_LAUNCH(SAVE ? "scan_save" : "scan", (scan_kernel<TIn, C, DK, DV, MT, SAVE, OUT>), grid, block, st,
                        (const float*)(ws + p.o_W), (const float*)(ws + p.o_U),
                        (const float*)(ws + p.o_Qg), (const float*)(ws + p.o_Kh),
                        (const float*)(ws + p.o_Ps), (const float*)(ws + p.o_gam), h0, (TIn*)o, hT,

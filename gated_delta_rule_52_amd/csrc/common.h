@@ -66,7 +66,20 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// launch recorder (include/gdn_profile.h); no-ops unless a tool enabled it
+void prof_begin(const char* name, hipStream_t st);
+void prof_end(hipStream_t st);
+
 }  // namespace gdn
+
+// Launch a kernel on `st` between the recorder's marks, then check the launch.
+#define GDN_LAUNCH(name, kernel, grid, block, st, ...)                   \
+    do {                                                                 \
+        ::gdn::prof_begin(name, st);                                     \
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, __VA_ARGS__);     \
+        ::gdn::prof_end(st);                                             \
+        if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;         \
+    } while (0)
 
 #define GDN_HIP_CHECK_LAUNCH()                                   \
     do {                                                         \

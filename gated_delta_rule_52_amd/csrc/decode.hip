@@ -131,10 +131,10 @@ static gdn_status launch_decode(const gdn_shape* sh, const void* q, const void* 
     using C = DecodeCfg<DK, DV>;
     dim3 grid(sh->B * sh->H), block(C::NT);
     if (sh->decay == GDN_DECAY_PER_CHANNEL)
-        hipLaunchKernelGGL((decode_kernel<TIn, DK, DV, true>), grid, block, 0, st, (const TIn*)q,
+        GDN_LAUNCH("decode", (decode_kernel<TIn, DK, DV, true>), grid, block, st, (const TIn*)q,
                            (const TIn*)k, (const TIn*)v, g, beta, state, (TIn*)o, sh->H, scale);
     else
-        hipLaunchKernelGGL((decode_kernel<TIn, DK, DV, false>), grid, block, 0, st, (const TIn*)q,
+        GDN_LAUNCH("decode", (decode_kernel<TIn, DK, DV, false>), grid, block, st, (const TIn*)q,
                            (const TIn*)k, (const TIn*)v, g, beta, state, (TIn*)o, sh->H, scale);
     GDN_HIP_CHECK_LAUNCH();
     return GDN_OK;

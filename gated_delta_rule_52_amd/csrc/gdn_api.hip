@@ -81,8 +81,7 @@ gdn_status gdn_new_state(float* state, int B, int H, int Dk, int Dv, void* strea
     const size_t n4 = n / 4;
     size_t blocks = (n4 + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                       (hipStream_t)stream, (float4*)state, n4);
+    GDN_LAUNCH("fill_zero", fill_zero_kernel, dim3((unsigned)blocks), dim3(256), (hipStream_t)stream, (float4*)state, n4);
     GDN_HIP_CHECK_LAUNCH();
     return GDN_OK;
 }

@@ -1,0 +1,85 @@
+"""Binding of include/gdn_profile.h: per-launch device timings of the
+library's kernels, taken with HIP events recorded on each launch's stream."""
+from __future__ import annotations
+
+import collections
+import ctypes
+
+import torch  # noqa: F401  (loads the HIP runtime the library shares)
+
+from . import lib
+
+_hip = None
+
+
+def hip():
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so.7")
+        vp = ctypes.c_void_p
+        h.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+        h.hipEventCreate.restype = ctypes.c_int
+        h.hipEventDestroy.argtypes = [vp]
+        h.hipEventDestroy.restype = ctypes.c_int
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        h.hipEventElapsedTime.restype = ctypes.c_int
+        _hip = h
+    return _hip
+
+
+def _bind():
+    L = lib()
+    L.gdn_profile_begin.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    L.gdn_profile_begin.restype = ctypes.c_int
+    L.gdn_profile_end.argtypes = []
+    L.gdn_profile_end.restype = ctypes.c_int
+    L.gdn_profile_launch_name.argtypes = [ctypes.c_int]
+    L.gdn_profile_launch_name.restype = ctypes.c_char_p
+    return L
+
+
+class LaunchRecorder:
+    """with LaunchRecorder(n) as rec: ...; torch.cuda.synchronize(); rec.by_kernel()"""
+
+    def __init__(self, n_pairs: int):
+        self.n = n_pairs
+        self.events = (ctypes.c_void_p * (2 * n_pairs))()
+        for i in range(2 * n_pairs):
+            ev = ctypes.c_void_p()
+            if hip().hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = ev
+        self.count = 0
+
+    def __enter__(self):
+        rc = _bind().gdn_profile_begin(self.events, self.n)
+        if rc != 0:
+            raise RuntimeError(f"gdn_profile_begin: status {rc}")
+        return self
+
+    def __exit__(self, *exc):
+        self.count = _bind().gdn_profile_end()
+        return False
+
+    def launches(self):
+        """[(kernel name, milliseconds)] in launch order; call after a sync."""
+        L = _bind()
+        out = []
+        ms = ctypes.c_float()
+        for j in range(self.count):
+            if hip().hipEventElapsedTime(ctypes.byref(ms), self.events[2 * j],
+                                         self.events[2 * j + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append((L.gdn_profile_launch_name(j).decode(), ms.value))
+        return out
+
+    def by_kernel(self):
+        """{name: [ms, ...]}"""
+        d = collections.defaultdict(list)
+        for name, ms in self.launches():
+            d[name].append(ms)
+        return dict(d)
+
+    def close(self):
+        for i in range(2 * self.n):
+            hip().hipEventDestroy(self.events[i])

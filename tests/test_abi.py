@@ -13,9 +13,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_symbols():
-    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -78,3 +82,13 @@ def test_null_and_misaligned_pointers_rejected():
     assert L.gdn_decode_step(ctypes.byref(d), p, p, p, p, p, None, p, None) == 1
     assert L.gdn_new_state(None, 1, 1, 16, 16, None) == 1
     assert L.gdn_new_state(mis, 1, 1, 16, 16, None) == 3
+
+
+def test_profile_recorder_arguments():
+    L = gdn.lib()
+    L.gdn_profile_begin.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    assert L.gdn_profile_begin(None, 4) == 1
+    ev = (ctypes.c_void_p * 2)()
+    assert L.gdn_profile_begin(ev, 0) == 1
+    assert L.gdn_profile_begin(ev, 1 << 20) == 1
+    assert L.gdn_profile_end() == 0
