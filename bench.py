@@ -2,7 +2,8 @@
 """Throughput of the gated delta-rule layer on one MI355X.
 
 A step is one forward plus one backward of the chunked per-channel-decay layer
-(gdn_forward then gdn_backward: every kernel of the hot path) over one batch of
+(gdn_forward_train then gdn_backward_train: every kernel of the hot path; the
+backward reuses the forward's residuals, as a training step does) over one batch of
 synthetic inputs shaped like the pages' training workload: B=8, T=4096, H=6,
 Dk=Dv=128, chunk 64, bf16 q/k/v with fp32 decay, gates and state (Marin note,
 "Single-device benchmark"; atomic_ops card, "Benchmarks").  Inputs are resident
@@ -35,8 +36,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 # contraction dtype of each kernel's dominant matrix products
-KERNEL_MFMA = {"prep": "bf16", "prep_bwd": "bf16", "scan": "f32", "scan_save": "f32",
-               "bscan": "f32", "bchunk1": "f32", "bchunk2": "bf16"}
+KERNEL_MFMA = {"prep": "bf16", "prep_T": "bf16", "scan": "f32", "scan_save": "f32",
+               "scan_train": "f32", "bscan": "f32", "bchunk1": "f32", "bchunk2": "bf16"}
 # TPU v6e, Sept-2026 prototype, B=8 T=4096 H=6 d=128 BF16 fwd+bwd: 22.44 ms
 # (Marin note, "Single-device benchmark") -> B*T / 22.44 ms
 PAGES_FWDBWD_TOKENS_S = 8 * 4096 / 22.44e-3
@@ -50,18 +51,20 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes):
     n = B * H * NC
     f4 = 4
     tri = C * (C + 1) // 2
-    backward = name in ("prep_bwd", "scan_save")
-    if name in ("prep", "prep_bwd"):
+    backward = name in ("prep_T", "scan_save")
+    if name in ("prep", "prep_T"):
         fl = 2 * C * C * DK + 2 * tri * (DK + DV)
         by = (2 * C * DK + C * DV) * in_bytes + C * DK * f4 + C * f4 \
             + (3 * C * DK + C * DV + C * C + DK) * f4 + (C * C * f4 if backward else 0)
-    elif name in ("scan", "scan_save"):
-        if backward:  # state-saving pass: D and the state update only
+    elif name in ("scan", "scan_save", "scan_train"):
+        if name == "scan_save":  # state-saving pass: D and the state update only
             fl = 4 * C * DK * DV
             by = (2 * C * DK + C * DV + DK) * f4 + DK * DV * f4
         else:
             fl = 6 * C * DK * DV + 2 * tri * DV
             by = (3 * C * DK + C * DV + C * C + DK) * f4 + C * DV * in_bytes
+            if name == "scan_train":  # also writes the chunk-start states
+                by += DK * DV * f4
     elif name == "bscan":
         fl = 6 * C * DK * DV + 2 * tri * DV
         by = (3 * C * DK + C * C + DK) * f4 + C * DV * in_bytes + (DK * DV + C * DV) * f4
@@ -122,13 +125,17 @@ def main():
     ws_b = gdn.workspace(sh, True, q.device)
     o = torch.empty_like(v)
     hT = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    gout = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g),
+            torch.empty_like(beta), torch.empty_like(hT))
 
     def fwd():
         gdn.gdn_forward(q, k, v, g, beta, None, scale=scale, chunk=C, o=o, hT=hT, ws=ws_f)
 
     def step():
-        fwd()
-        return gdn.gdn_backward(q, k, v, g, beta, dO, None, dhT, scale=scale, chunk=C, ws=ws_b)
+        # training step: the backward reuses the forward's residuals
+        gdn.gdn_forward_train(q, k, v, g, beta, None, scale=scale, chunk=C, o=o, hT=hT, ws=ws_b)
+        return gdn.gdn_backward_train(q, k, v, g, beta, dO, ws_b, dhT, scale=scale, chunk=C,
+                                      out=gout)
 
     # ---- correctness gate on sampled heads (oracle = token-serial CPU reference)
     import oracle
@@ -165,7 +172,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    launches_per_step = 7
+    launches_per_step = 5
     rec = LaunchRecorder(args.steps * launches_per_step + 16)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

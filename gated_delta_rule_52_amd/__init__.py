@@ -31,7 +31,7 @@ GDN_DECAY_PER_HEAD, GDN_DECAY_PER_CHANNEL = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_ALIGNMENT",
           4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
 EXPORTS = ("gdn_new_state", "gdn_workspace_bytes", "gdn_forward", "gdn_backward",
-           "gdn_decode_step", "gdn_status_string",
+           "gdn_forward_train", "gdn_backward_train", "gdn_decode_step", "gdn_status_string",
            # include/gdn_profile.h
            "gdn_profile_begin", "gdn_profile_end", "gdn_profile_launch_name")
 
@@ -70,6 +70,10 @@ def lib():
         L.gdn_forward.restype = i
         L.gdn_backward.argtypes = [sp] + [vp] * 15 + [sz, vp]
         L.gdn_backward.restype = i
+        L.gdn_forward_train.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_forward_train.restype = i
+        L.gdn_backward_train.argtypes = [sp] + [vp] * 14 + [sz, vp]
+        L.gdn_backward_train.restype = i
         L.gdn_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_decode_step.restype = i
         L.gdn_status_string.argtypes = [i]
@@ -179,6 +183,46 @@ def gdn_backward(q, k, v, g, beta, dO, h0=None, dhT=None, *, scale=None, chunk=N
         ws = workspace(sh, True, q.device)
     _call(lib().gdn_backward, "gdn_backward", ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v),
           _ptr(g), _ptr(beta), _ptr(h0), _ptr(dO), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv),
+          _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(ws), ws.numel(), _stream())
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+def gdn_forward_train(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT=None,
+                      ws=None):
+    """Training forward: as gdn_forward, and leaves residuals in `ws` (a
+    backward-sized workspace, returned) for gdn_backward_train.
+    Returns (o, hT, ws)."""
+    _check_inputs(q, k, v, g, beta)
+    _check(h0, "h0", torch.float32)
+    sh = make_shape(q, v, g, scale, chunk)
+    B, T, H, _ = q.shape
+    if o is None:
+        o = torch.empty((B, T, H, sh.Dv), dtype=q.dtype, device=q.device)
+    if hT is None:
+        hT = torch.empty((B, H, sh.Dk, sh.Dv), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(sh, True, q.device)
+    _call(lib().gdn_forward_train, "gdn_forward_train", ctypes.byref(sh), _ptr(q), _ptr(k),
+          _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), _ptr(ws), ws.numel(),
+          _stream())
+    return o, hT, ws
+
+
+def gdn_backward_train(q, k, v, g, beta, dO, ws, dhT=None, *, scale=None, chunk=None,
+                       want_dh0=True, out=None):
+    """Training backward from the residuals gdn_forward_train left in `ws`."""
+    _check_inputs(q, k, v, g, beta)
+    _check(dO, "dO", q.dtype)
+    _check(dhT, "dhT", torch.float32)
+    sh = make_shape(q, v, g, scale, chunk)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g),
+               torch.empty_like(beta),
+               torch.empty((sh.B, sh.H, sh.Dk, sh.Dv), dtype=torch.float32, device=q.device)
+               if want_dh0 else None)
+    dq, dk, dv, dg, dbeta, dh0 = out
+    _call(lib().gdn_backward_train, "gdn_backward_train", ctypes.byref(sh), _ptr(q), _ptr(k),
+          _ptr(v), _ptr(g), _ptr(beta), _ptr(dO), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv),
           _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(ws), ws.numel(), _stream())
     return dq, dk, dv, dg, dbeta, dh0
 

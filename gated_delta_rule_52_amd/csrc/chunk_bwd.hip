@@ -33,8 +33,8 @@
 namespace gdn {
 
 gdn_status recompute_dispatch(const Plan& p, const void* q, const void* k, const void* v,
-                              const float* g, const float* beta, const float* h0, void* ws,
-                              hipStream_t st);
+                              const float* g, const float* beta, const float* h0, void* o,
+                              float* hT, bool out, void* ws, hipStream_t st);
 
 template <int DV>
 struct BScanCfg {
@@ -703,11 +703,13 @@ template <typename TIn, int C, int DK, int DV>
 gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v, const float* g,
                       const float* beta, const float* h0, const void* dO, const float* dhT,
                       void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0, char* ws,
-                      hipStream_t st)
+                      bool recompute, hipStream_t st)
 {
     constexpr int MT = std::is_same<TIn, bf16>::value ? MT_BF16 : MT_F32;
-    gdn_status s = recompute_dispatch(p, q, k, v, g, beta, h0, ws, st);
-    if (s != GDN_OK) return s;
+    if (recompute) {
+        gdn_status s = recompute_dispatch(p, q, k, v, g, beta, h0, nullptr, nullptr, false, ws, st);
+        if (s != GDN_OK) return s;
+    }
     const int BH = p.B * p.H;
     {
         using SC = BScanCfg<DV>;
@@ -755,12 +757,12 @@ template <typename TIn>
 gdn_status backward_dt(const Plan& p, const void* q, const void* k, const void* v, const float* g,
                        const float* beta, const float* h0, const void* dO, const float* dhT,
                        void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0, char* ws,
-                       hipStream_t st)
+                       bool recompute, hipStream_t st)
 {
 #define GDN_BWD(C_, D_)                                                                           \
     if (p.C == C_ && p.Dk == D_ && p.Dv == D_)                                                     \
         return backward_t<TIn, C_, D_, D_>(p, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, \
-                                           dh0, ws, st);
+                                           dh0, ws, recompute, st);
     GDN_BWD(64, 128) GDN_BWD(64, 64) GDN_BWD(16, 16)
 #undef GDN_BWD
     return GDN_ERR_UNSUPPORTED;
@@ -769,13 +771,13 @@ gdn_status backward_dt(const Plan& p, const void* q, const void* k, const void* 
 gdn_status backward_dispatch(const Plan& p, const void* q, const void* k, const void* v,
                              const float* g, const float* beta, const float* h0, const void* dO,
                              const float* dhT, void* dq, void* dk, void* dv, float* dg,
-                             float* dbeta, float* dh0, void* ws, hipStream_t st)
+                             float* dbeta, float* dh0, void* ws, bool recompute, hipStream_t st)
 {
     if (p.dtype == GDN_BF16)
         return backward_dt<bf16>(p, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
-                                 (char*)ws, st);
+                                 (char*)ws, recompute, st);
     return backward_dt<float>(p, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
-                              (char*)ws, st);
+                              (char*)ws, recompute, st);
 }
 
 }  // namespace gdn

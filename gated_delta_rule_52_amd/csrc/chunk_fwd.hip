@@ -453,11 +453,11 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
     float* Tm = want_T ? (float*)(ws + p.o_Tm) : nullptr;
     dim3 grid((unsigned)p.n_ch), block(NTHR);
     if (p.decay == GDN_DECAY_PER_CHANNEL)
-        GDN_LAUNCH(want_T ? "prep_bwd" : "prep", (prep_kernel<TIn, C, DK, DV, true, MT>), grid, block, st,
+        GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep_kernel<TIn, C, DK, DV, true, MT>), grid, block, st,
                            (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
                            p.scale, W, U, Qg, Kh, Ps, gam, Tm);
     else
-        GDN_LAUNCH(want_T ? "prep_bwd" : "prep", (prep_kernel<TIn, C, DK, DV, false, MT>), grid, block, st,
+        GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep_kernel<TIn, C, DK, DV, false, MT>), grid, block, st,
                            (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
                            p.scale, W, U, Qg, Kh, Ps, gam, Tm);
     GDN_HIP_CHECK_LAUNCH();
@@ -471,7 +471,7 @@ gdn_status run_scan(const Plan& p, const float* h0, void* o, float* hT, char* ws
     const int BH = p.B * p.H;
     const int ngrp = (BH + 7) / 8;
     dim3 grid((unsigned)(ngrp * 8 * SC::NS)), block(NTHR);
-    GDN_LAUNCH(SAVE ? "scan_save" : "scan", (scan_kernel<TIn, C, DK, DV, MT, SAVE, OUT>), grid, block, st,
+    GDN_LAUNCH(SAVE ? (OUT ? "scan_train" : "scan_save") : "scan", (scan_kernel<TIn, C, DK, DV, MT, SAVE, OUT>), grid, block, st,
                        (const float*)(ws + p.o_W), (const float*)(ws + p.o_U),
                        (const float*)(ws + p.o_Qg), (const float*)(ws + p.o_Kh),
                        (const float*)(ws + p.o_Ps), (const float*)(ws + p.o_gam), h0, (TIn*)o, hT,
@@ -514,26 +514,32 @@ gdn_status forward_dispatch(const Plan& p, const void* q, const void* k, const v
 }
 
 // Forward recompute for the backward pass: the prep outputs (with T) and the
-// state at the start of every chunk; no outputs are written.
+// state at the start of every chunk; no outputs are written.  With `out`, the
+// same pass also writes o and hT (the training forward, which leaves these
+// residuals in the workspace for the backward).
 template <typename TIn, int C, int DK, int DV>
 gdn_status recompute_t(const Plan& p, const void* q, const void* k, const void* v, const float* g,
-                       const float* beta, const float* h0, char* ws, hipStream_t st)
+                       const float* beta, const float* h0, void* o, float* hT, bool out, char* ws,
+                       hipStream_t st)
 {
     constexpr int MT = std::is_same<TIn, bf16>::value ? MT_BF16 : MT_F32;
     gdn_status s = run_prep<TIn, C, DK, DV, MT>(p, q, k, v, g, beta, ws, true, st);
     if (s != GDN_OK) return s;
+    if (out) return run_scan<TIn, C, DK, DV, MT_F32, true, true>(p, h0, o, hT, ws, st);
     return run_scan<TIn, C, DK, DV, MT_F32, true, false>(p, h0, nullptr, nullptr, ws, st);
 }
 
 gdn_status recompute_dispatch(const Plan& p, const void* q, const void* k, const void* v,
-                              const float* g, const float* beta, const float* h0, void* ws,
-                              hipStream_t st)
+                              const float* g, const float* beta, const float* h0, void* o,
+                              float* hT, bool out, void* ws, hipStream_t st)
 {
 #define GDN_REC(C_, D_)                                                                        \
     if (p.C == C_ && p.Dk == D_ && p.Dv == D_)                                                  \
         return p.dtype == GDN_BF16                                                              \
-                   ? recompute_t<bf16, C_, D_, D_>(p, q, k, v, g, beta, h0, (char*)ws, st)      \
-                   : recompute_t<float, C_, D_, D_>(p, q, k, v, g, beta, h0, (char*)ws, st);
+                   ? recompute_t<bf16, C_, D_, D_>(p, q, k, v, g, beta, h0, o, hT, out,         \
+                                                   (char*)ws, st)                               \
+                   : recompute_t<float, C_, D_, D_>(p, q, k, v, g, beta, h0, o, hT, out,        \
+                                                    (char*)ws, st);
     GDN_REC(64, 128) GDN_REC(64, 64) GDN_REC(16, 16)
 #undef GDN_REC
     return GDN_ERR_UNSUPPORTED;

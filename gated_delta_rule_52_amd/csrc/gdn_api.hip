@@ -16,7 +16,10 @@ gdn_status forward_dispatch(const Plan& p, const void* q, const void* k, const v
 gdn_status backward_dispatch(const Plan& p, const void* q, const void* k, const void* v,
                              const float* g, const float* beta, const float* h0, const void* dO,
                              const float* dhT, void* dq, void* dk, void* dv, float* dg,
-                             float* dbeta, float* dh0, void* ws, hipStream_t st);
+                             float* dbeta, float* dh0, void* ws, bool recompute, hipStream_t st);
+gdn_status recompute_dispatch(const Plan& p, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* h0, void* o,
+                              float* hT, bool out, void* ws, hipStream_t st);
 
 __global__ void fill_zero_kernel(float4* __restrict__ p, size_t n4)
 {
@@ -122,10 +125,11 @@ gdn_status gdn_forward(const gdn_shape* sh, const void* q, const void* k, const 
     return forward_dispatch(p, q, k, v, g, beta, h0, o, hT, ws, (hipStream_t)stream);
 }
 
-gdn_status gdn_backward(const gdn_shape* sh, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, const float* h0, const void* dO,
-                        const float* dhT, void* dq, void* dk, void* dv, float* dg, float* dbeta,
-                        float* dh0, void* ws, size_t ws_bytes, void* stream)
+static gdn_status backward_common(const gdn_shape* sh, const void* q, const void* k,
+                                  const void* v, const float* g, const float* beta,
+                                  const float* h0, const void* dO, const float* dhT, void* dq,
+                                  void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                                  void* ws, size_t ws_bytes, void* stream, bool recompute)
 {
     gdn_status s = check_shape(sh, false);
     if (s != GDN_OK) return s;
@@ -147,7 +151,41 @@ gdn_status gdn_backward(const gdn_shape* sh, const void* q, const void* k, const
     Plan p = make_plan(*sh, eff_scale(sh));
     if (p.ws_bwd_bytes && (!ws || ws_bytes < p.ws_bwd_bytes)) return GDN_ERR_WORKSPACE;
     return backward_dispatch(p, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, dh0, ws,
-                             (hipStream_t)stream);
+                             recompute, (hipStream_t)stream);
+}
+
+gdn_status gdn_backward(const gdn_shape* sh, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* h0, const void* dO,
+                        const float* dhT, void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                        float* dh0, void* ws, size_t ws_bytes, void* stream)
+{
+    return backward_common(sh, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, dh0, ws,
+                           ws_bytes, stream, true);
+}
+
+gdn_status gdn_forward_train(const gdn_shape* sh, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const float* h0, void* o,
+                             float* hT, void* ws, size_t ws_bytes, void* stream)
+{
+    gdn_status s = check_shape(sh, false);
+    if (s != GDN_OK) return s;
+    if (sh->T == 0) return gdn_forward(sh, q, k, v, g, beta, h0, o, hT, ws, ws_bytes, stream);
+    if (!q || !k || !v || !g || !beta || !o) return GDN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, o, h0, hT, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGNMENT;
+    Plan p = make_plan(*sh, eff_scale(sh));
+    if (!ws || ws_bytes < p.ws_bwd_bytes) return GDN_ERR_WORKSPACE;
+    return recompute_dispatch(p, q, k, v, g, beta, h0, o, hT, true, ws, (hipStream_t)stream);
+}
+
+gdn_status gdn_backward_train(const gdn_shape* sh, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const void* dO, const float* dhT,
+                              void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                              void* ws, size_t ws_bytes, void* stream)
+{
+    return backward_common(sh, q, k, v, g, beta, nullptr, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
+                           ws, ws_bytes, stream, false);
 }
 
 gdn_status gdn_decode_step(const gdn_shape* sh, const void* q, const void* k, const void* v,

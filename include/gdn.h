@@ -36,10 +36,11 @@
  * GDN_ERR_HIP.  Results are deterministic: repeated calls with the same inputs
  * are bitwise identical (gated-deltanet card, "Correctness").
  *
- * Supported sizes: Dk, Dv in {16, 32, 64, 128}; chunk 16 or 64 (0 = 64);
+ * Supported sizes: chunked calls Dk = Dv in {64, 128} with chunk 64 (the
+ * default) and Dk = Dv = 16 with chunk 16; decode Dk = Dv in {16, 32, 64, 128};
  * any T >= 0 (a ragged last chunk is processed as if padded with tokens that
  * have g = 0 and beta = 0, which leave the state exactly unchanged; their
- * outputs are not written); B, H >= 1.
+ * outputs are not written); B, H >= 1.  Anything else: GDN_ERR_UNSUPPORTED.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -89,13 +90,14 @@ size_t gdn_workspace_bytes(const gdn_shape *shape, int for_backward);
 /*
  * gdn_forward -- the whole layer over T tokens in chunked form.
  *
- * Within each chunk of C tokens the per-channel cumulative log-decay is formed
- * (Marin note, "Background"); query-key and key-key scores that span two
+ * Within each chunk of C tokens the per-channel cumulative decay is formed
+ * (Marin note, "Background"); query-key and key-key scores that span the two
  * halves of a block are computed with the decay split at the last token of
  * the earlier half, so the spanning scores are one dense matrix product per
- * block pair, while pairs inside the smallest blocks are scored pairwise
- * (Marin note, "Approach"); the unit-lower-triangular delta system of the
- * chunk is solved in WY form; and the state is carried across chunks
+ * block pair (Marin note, "Approach"); the split is repeated inside every
+ * half down to single tokens, so every score comes from such a product; the
+ * unit-lower-triangular delta system of the chunk is solved in WY form; and
+ * the state is carried across chunks
  * (atomic_ops card, "Features": chunk scores, WY block solve, recompute,
  * inter-chunk scan).  The result equals the token recurrence above up to
  * floating-point rounding.
@@ -122,6 +124,27 @@ gdn_status gdn_backward(const gdn_shape *shape, const void *q, const void *k, co
                         const float *g, const float *beta, const float *h0, const void *dO,
                         const float *dhT, void *dq, void *dk, void *dv, float *dg, float *dbeta,
                         float *dh0, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_forward_train / gdn_backward_train -- the same forward and backward for
+ * training, where the backward reuses what the forward computed instead of
+ * recomputing it (atomic_ops card, "Features": the backward reuses forward
+ * residuals).  gdn_forward_train writes o and hT exactly as gdn_forward and
+ * also leaves its chunk intermediates and the state at the start of every
+ * chunk in `ws`, which must hold gdn_workspace_bytes(shape, 1) bytes.
+ * gdn_backward_train then reads them from the same `ws`: it must be called
+ * with the same shape, the same q, k, v, g, beta contents and the workspace
+ * untouched in between (the library cannot check this; a mismatch gives
+ * wrong gradients, not an error).  Results equal gdn_backward's bitwise.
+ * Errors as gdn_forward / gdn_backward.
+ */
+gdn_status gdn_forward_train(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const float *h0, void *o,
+                             float *hT, void *ws, size_t ws_bytes, void *stream);
+gdn_status gdn_backward_train(const gdn_shape *shape, const void *q, const void *k,
+                              const void *v, const float *g, const float *beta, const void *dO,
+                              const float *dhT, void *dq, void *dk, void *dv, float *dg,
+                              float *dbeta, float *dh0, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * gdn_decode_step -- one token of the recurrence for every (batch, head), with

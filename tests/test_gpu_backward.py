@@ -99,3 +99,25 @@ def test_backward_deterministic():
     b = gpu_backward(inp, h0=False)
     for k in NAMES:
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("decay", ["channel", "head"])
+def test_training_pair_equals_separate_calls(dtype, decay):
+    """gdn_forward_train + gdn_backward_train (residuals kept) give bitwise the
+    same outputs and gradients as gdn_forward + gdn_backward (recompute)."""
+    import gated_delta_rule_52_amd as gdn
+    inp = gi.make_inputs(2, 200, 3, 128, 128, decay=decay, dtype=dtype, seed=21, h0_std=0.1,
+                         grads=True)
+    d = to_dev_inputs(inp)
+    sc = inp["meta"]["scale"]
+    o1, h1 = gdn.gdn_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], scale=sc)
+    g1 = gdn.gdn_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["dO"], d["h0"], d["dhT"],
+                          scale=sc)
+    o2, h2, ws = gdn.gdn_forward_train(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], scale=sc)
+    g2 = gdn.gdn_backward_train(d["q"], d["k"], d["v"], d["g"], d["beta"], d["dO"], ws, d["dhT"],
+                                scale=sc)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
