@@ -90,6 +90,8 @@ def main():
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -277,6 +279,15 @@ def main():
                "sample": f"{nh} of {B * H} (batch, head) sequences, T={T}, fwd+bwd, float64 "
                          f"token-serial; tokens counted as heads/H*T; {tc:.1f} s"}
         log(f"[bench] cpu oracle {cpu['value']:.0f} tokens/s in {tc:.1f} s")
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 1 GiB read + 1 GiB written")
+        del src, dst
 
     line = {
         "metric": "tokens/s fwd and fwd+bwd at B=8 T=4096 H=6 d=128; % MFMA/HBM peak",

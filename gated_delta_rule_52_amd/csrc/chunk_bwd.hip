@@ -338,7 +338,6 @@ bchunk1_kernel(const TIn* __restrict__ v, const float* __restrict__ beta,
 // bchunk2
 // ---------------------------------------------------------------------------
 constexpr int NTHR2 = 512;  // 8 waves
-constexpr int NPART = 4;    // row parts of the column passes
 
 template <typename TIn, int C, int DK, int DV, bool PCH, int MT>
 __global__ void __launch_bounds__(NTHR2)
@@ -352,7 +351,8 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
 {
     using G = Geo<C, DK, DV>;
     constexpr int PD = G::PD, PC = G::PC, NB = G::NB;
-    constexpr int RPP = C / NPART;  // rows per part
+    constexpr int RPP = 16;         // rows per column-thread part: one 16-token tile
+    constexpr int NPART = C / RPP;  // parts per chunk
     constexpr int NW = NTHR2 / 64;
     __shared__ float sT[C][PC], sdP[C][PC], sdA[C][PC], sX[C][PD], sY[C][PD], sZ[C][PD];
     __shared__ float sbeta[C], stot[NPART][DK], sext[NPART][DK];
@@ -519,59 +519,35 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
         }
     }
 
-    // ---- score gradients, level by level (h = C/2 .. 1)
+    // ---- score gradients of pairs that span two 16-token tiles: the levels
+    // h = C/2 .. 16 of the block-boundary split, as MFMA products of the score
+    // gradients and factored rows (each own row is in the query half or the key
+    // half of its 2h-block at every such level)
 #pragma unroll
-    for (int lvl = 0; (C >> (lvl + 1)) >= 1; ++lvl) {
+    for (int lvl = 0; (C >> (lvl + 1)) >= 16; ++lvl) {
         const int hl = C >> (lvl + 1);
         float F[RPP];
-        bool qside[RPP];
         // level-hl factor of each own row: query rows prod_{s=m+1..r} a_s,
         // key rows prod_{s=r+1..m} a_s, m the last token of the earlier half
-        if (hl >= RPP) {
-            const int base = (p0 / (2 * hl)) * (2 * hl);
-            const bool qs = p0 >= base + hl;
-            if (qs) {
-                float pre = 1.f;
-                for (int pp = (base + hl) / RPP; pp < part; ++pp) pre *= stot[pp][c];
-                float Fr = pre;
+        const int base = (p0 / (2 * hl)) * (2 * hl);
+        const bool qs = p0 >= base + hl;
+        if (qs) {
+            float pre = 1.f;
+            for (int pp = (base + hl) / RPP; pp < part; ++pp) pre *= stot[pp][c];
+            float Fr = pre;
 #pragma unroll
-                for (int i = 0; i < RPP; ++i) {
-                    Fr *= a[i];
-                    F[i] = Fr;
-                    qside[i] = true;
-                }
-            } else {
-                float suf = 1.f;
-                for (int pp = part + 1; pp < (base + hl) / RPP; ++pp) suf *= stot[pp][c];
-                float Fr = suf;
-#pragma unroll
-                for (int i = RPP - 1; i >= 0; --i) {
-                    F[i] = Fr;
-                    qside[i] = false;
-                    Fr *= a[i];
-                }
+            for (int i = 0; i < RPP; ++i) {
+                Fr *= a[i];
+                F[i] = Fr;
             }
         } else {
+            float suf = 1.f;
+            for (int pp = part + 1; pp < (base + hl) / RPP; ++pp) suf *= stot[pp][c];
+            float Fr = suf;
 #pragma unroll
-            for (int u0 = 0; u0 < RPP; u0 += (hl < RPP ? hl : RPP)) {
-                const bool qs = ((p0 + u0) / hl) & 1;
-                if (qs) {
-                    float Fr = 1.f;
-#pragma unroll
-                    for (int i = 0; i < hl; ++i) {
-                        Fr *= a[u0 + i];
-                        F[u0 + i] = Fr;
-                        qside[u0 + i] = true;
-                    }
-                } else {
-                    float Fr = 1.f;
-#pragma unroll
-                    for (int i = hl - 1; i >= 0; --i) {
-                        F[u0 + i] = Fr;
-                        qside[u0 + i] = false;
-                        Fr *= a[u0 + i];
-                    }
-                }
+            for (int i = RPP - 1; i >= 0; --i) {
+                F[i] = Fr;
+                Fr *= a[i];
             }
         }
         if (cp) {
@@ -593,35 +569,18 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
             const int ti = idx / (DK / 16), tj = idx % (DK / 16);
             f32x4 r1 = zero4();
             r2[m] = zero4();
-            if (hl >= 16) {
-                const int base = (ti * 16 / (2 * hl)) * (2 * hl);
-                const bool qs = ti * 16 >= base + hl;
-                if (qs) {
-                    r1 = mma16fd<MT>(r1, [&](int i, int kx) { return sdP[ti * 16 + i][base + kx]; },
-                                     [&](int kx, int j) { return sY[base + kx][tj * 16 + j]; }, hl);
-                    r2[m] = mma16fd<MT>(r2[m], [&](int i, int kx) { return sdA[ti * 16 + i][base + kx]; },
-                                        [&](int kx, int j) { return sY[base + kx][tj * 16 + j]; }, hl);
-                } else {
-                    const int qb = base + hl;
-                    r1 = mma16fd<MT>(r1, [&](int i, int kx) { return sdP[qb + kx][ti * 16 + i]; },
-                                     [&](int kx, int j) { return sX[qb + kx][tj * 16 + j]; }, hl);
-                    r2[m] = mma16fd<MT>(r2[m], [&](int i, int kx) { return sbeta[qb + kx] * sdA[qb + kx][ti * 16 + i]; },
-                                        [&](int kx, int j) { return sY[qb + kx][tj * 16 + j]; }, hl);
-                }
+            const int tbase = (ti * 16 / (2 * hl)) * (2 * hl);
+            if (ti * 16 >= tbase + hl) {
+                r1 = mma16fd<MT>(r1, [&](int i, int kx) { return sdP[ti * 16 + i][tbase + kx]; },
+                                 [&](int kx, int j) { return sY[tbase + kx][tj * 16 + j]; }, hl);
+                r2[m] = mma16fd<MT>(r2[m], [&](int i, int kx) { return sdA[ti * 16 + i][tbase + kx]; },
+                                    [&](int kx, int j) { return sY[tbase + kx][tj * 16 + j]; }, hl);
             } else {
-                const int tb = ti * 16;
-                r1 = mma16f<MT, 16>(r1,
-                    [&](int i, int kx) { return in_level(i, kx, hl) ? sdP[tb + i][tb + kx] : 0.f; },
-                    [&](int kx, int j) { return sY[tb + kx][tj * 16 + j]; });
-                r1 = mma16f<MT, 16>(r1,
-                    [&](int i, int kx) { return in_level(kx, i, hl) ? sdP[tb + kx][tb + i] : 0.f; },
-                    [&](int kx, int j) { return sX[tb + kx][tj * 16 + j]; });
-                r2[m] = mma16f<MT, 16>(r2[m],
-                    [&](int i, int kx) {
-                        return in_level(i, kx, hl) ? sdA[tb + i][tb + kx]
-                             : (in_level(kx, i, hl) ? sbeta[tb + kx] * sdA[tb + kx][tb + i] : 0.f);
-                    },
-                    [&](int kx, int j) { return sY[tb + kx][tj * 16 + j]; });
+                const int qb = tbase + hl;
+                r1 = mma16fd<MT>(r1, [&](int i, int kx) { return sdP[qb + kx][ti * 16 + i]; },
+                                 [&](int kx, int j) { return sX[qb + kx][tj * 16 + j]; }, hl);
+                r2[m] = mma16fd<MT>(r2[m], [&](int i, int kx) { return sbeta[qb + kx] * sdA[qb + kx][ti * 16 + i]; },
+                                    [&](int kx, int j) { return sY[qb + kx][tj * 16 + j]; }, hl);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) sZ[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = r1[r];
@@ -641,7 +600,7 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
             for (int i = 0; i < RPP; ++i) {
                 const int r = p0 + i;
                 const float R1 = sZ[r][c], R2 = sX[r][c];
-                if (qside[i]) {
+                if (qs) {
                     const float bt = sbeta[r];
                     dq[i] += F[i] * R1;
                     dk[i] += bt * F[i] * R2;
@@ -654,6 +613,36 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
             }
         }
         __syncthreads();
+    }
+
+    // ---- score gradients of pairs inside one 16-token tile (j < i), on VALU:
+    // this thread owns channel c of all 16 rows of its tile, so every pair's
+    // contribution to its rows is local (no reduction across lanes); the decay
+    // between the two tokens is the running product E_ij = prod_{s=j+1..i} a_s.
+    if (cp) {
+        float bt[RPP];
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) bt[i] = sbeta[p0 + i];
+#pragma unroll
+        for (int i = 1; i < RPP; ++i) {
+            float E = 1.f;
+#pragma unroll
+            for (int j = i - 1; j >= 0; --j) {
+                E *= a[j + 1];
+                const float tP = sdP[p0 + i][p0 + j] * E;
+                const float tA = sdA[p0 + i][p0 + j] * E;
+                dq[i] += tP * kv[j];
+                dk[j] += tP * qv[i];
+                const float btA = bt[i] * tA;
+                dk[i] += btA * kv[j];
+                dk[j] += btA * kv[i];
+                const float y = tA * kv[i] * kv[j];
+                const float x = tP * qv[i] * kv[j] + bt[i] * y;
+                dG[i] += x;
+                dG[j] -= x;
+                dbr[i] += y;
+            }
+        }
     }
 
     // ---- dg = reverse cumulative sum of dG over the chunk; dbeta; dq, dk out
@@ -714,7 +703,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
     {
         using SC = BScanCfg<DV>;
         dim3 grid((unsigned)(((BH + 7) / 8) * 8 * SC::NS)), block(NTHR);
-        GDN_LAUNCH("bscan", (bscan_kernel<TIn, C, DK, DV, MT_F32>), grid, block, st,
+        GDN_LAUNCH("bscan", (bscan_kernel<TIn, C, DK, DV, MT>), grid, block, st,
                            (const float*)(ws + p.o_Qg), (const float*)(ws + p.o_Kh),
                            (const float*)(ws + p.o_W), (const float*)(ws + p.o_Ps),
                            (const float*)(ws + p.o_gam), (const TIn*)dO, dhT,
@@ -722,7 +711,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
         GDN_HIP_CHECK_LAUNCH();
     }
     dim3 gch((unsigned)p.n_ch);
-    GDN_LAUNCH("bchunk1", (bchunk1_kernel<TIn, C, DK, DV, MT_F32>), gch, dim3(NTHR), st,
+    GDN_LAUNCH("bchunk1", (bchunk1_kernel<TIn, C, DK, DV, MT>), gch, dim3(NTHR), st,
                        (const TIn*)v, beta, (const TIn*)dO, (const float*)(ws + p.o_W),
                        (const float*)(ws + p.o_U), (const float*)(ws + p.o_Tm),
                        (const float*)(ws + p.o_Sst), (const float*)(ws + p.o_dSt),

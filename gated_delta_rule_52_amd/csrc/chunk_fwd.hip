@@ -488,7 +488,7 @@ gdn_status forward_t(const Plan& p, const void* q, const void* k, const void* v,
     constexpr int MT = std::is_same<TIn, bf16>::value ? MT_BF16 : MT_F32;
     gdn_status s = run_prep<TIn, C, DK, DV, MT>(p, q, k, v, g, beta, ws, false, st);
     if (s != GDN_OK) return s;
-    return run_scan<TIn, C, DK, DV, MT_F32, false, true>(p, h0, o, hT, ws, st);
+    return run_scan<TIn, C, DK, DV, MT, false, true>(p, h0, o, hT, ws, st);
 }
 
 template <typename TIn>
@@ -525,8 +525,8 @@ gdn_status recompute_t(const Plan& p, const void* q, const void* k, const void* 
     constexpr int MT = std::is_same<TIn, bf16>::value ? MT_BF16 : MT_F32;
     gdn_status s = run_prep<TIn, C, DK, DV, MT>(p, q, k, v, g, beta, ws, true, st);
     if (s != GDN_OK) return s;
-    if (out) return run_scan<TIn, C, DK, DV, MT_F32, true, true>(p, h0, o, hT, ws, st);
-    return run_scan<TIn, C, DK, DV, MT_F32, true, false>(p, h0, nullptr, nullptr, ws, st);
+    if (out) return run_scan<TIn, C, DK, DV, MT, true, true>(p, h0, o, hT, ws, st);
+    return run_scan<TIn, C, DK, DV, MT, true, false>(p, h0, nullptr, nullptr, ws, st);
 }
 
 gdn_status recompute_dispatch(const Plan& p, const void* q, const void* k, const void* v,
