@@ -164,6 +164,196 @@ bscan_kernel(const float* __restrict__ Qgi, const float* __restrict__ Khi,
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// reverse scan over bf16 chunk tables (bf16 inputs): the structure of the
+// forward scan2 -- 8 waves, dS slice in accumulator registers, K-contiguous
+// bf16 operands (P^T, Kh, Qg^T, W^T, dO^T, dS'^T, dD^T), next chunk prefetched.
+// ---------------------------------------------------------------------------
+constexpr int NTHR_B = 512;
+
+template <int C, int DK, int DV>
+__global__ void __launch_bounds__(NTHR_B)
+bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
+              const bf16* __restrict__ QgTb, const bf16* __restrict__ WTb,
+              const float* __restrict__ gami, const bf16* __restrict__ dO,
+              const float* __restrict__ dhT, float* __restrict__ dSt, float* __restrict__ dDt,
+              float* __restrict__ dh0, int BH, int T, int H, int NC)
+{
+    constexpr int BV = 32, NS = DV / BV, NW = NTHR_B / 64;
+    constexpr int PA = DK + 8, PT = C + 8;
+    constexpr int TD = (C / 16) * (BV / 16), TS = (DK / 16) * (BV / 16);
+    constexpr int MD = (TD + NW - 1) / NW, MS = (TS + NW - 1) / NW;
+    constexpr int QP = C * C / 8, QW = C * DK / 8, QK = DK * C / 8, QO = C * BV / 8;
+    constexpr int QALL = QP + QW + 2 * QK + QO, QPT = (QALL + NTHR_B - 1) / NTHR_B;
+    __shared__ __align__(16) bf16 sPT[C][PT], sK[C][PA], sQT[DK][PT], sWT[DK][PT], sdSt[BV][PA],
+        sdOt[BV][PT], sdDt[BV][PT];
+
+    const int x = blockIdx.x;
+    const int grp = x / (8 * NS), rem = x % (8 * NS);
+    const int sl = rem / 8, bh = grp * 8 + rem % 8;
+    if (bh >= BH) return;
+    const int b = bh / H, h = bh % H;
+    const int v0 = sl * BV;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+
+    f32x4 dacc[MS];
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        const int idx = w + NW * m;
+        dacc[m] = zero4();
+        if (idx < TS) {
+            const int si = idx / (BV / 16), sj = idx % (BV / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dacc[m][r] = dhT ? dhT[((size_t)bh * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] : 0.f;
+            *reinterpret_cast<uint2*>(&sdSt[sj * 16 + lr][si * 16 + 4 * lq]) =
+                pack4_bf16(dacc[m][0], dacc[m][1], dacc[m][2], dacc[m][3]);
+        }
+    }
+
+    uint4 pf[QPT];
+    float gpf[MS][4];
+    auto fetch = [&](int n) {
+        const size_t ch = (size_t)bh * NC + n;
+#pragma unroll
+        for (int q = 0; q < QPT; ++q) {
+            const int idx = tid + NTHR_B * q;
+            uint4 val = uint4{0u, 0u, 0u, 0u};
+            if (idx < QP) {
+                val = reinterpret_cast<const uint4*>(PsTb + ch * C * C)[idx];
+            } else if (idx < QP + QW) {
+                val = reinterpret_cast<const uint4*>(Khb + ch * C * DK)[idx - QP];
+            } else if (idx < QP + QW + QK) {
+                val = reinterpret_cast<const uint4*>(QgTb + ch * C * DK)[idx - QP - QW];
+            } else if (idx < QP + QW + 2 * QK) {
+                val = reinterpret_cast<const uint4*>(WTb + ch * C * DK)[idx - QP - QW - QK];
+            } else if (idx < QALL) {
+                const int e = idx - QP - QW - 2 * QK;
+                const int r = e / (BV / 8), j0 = (e % (BV / 8)) * 8;
+                const int t = n * C + r;
+                if (t < T)
+                    val = *reinterpret_cast<const uint4*>(dO + (((size_t)b * T + t) * H + h) * DV + v0 + j0);
+            }
+            pf[q] = val;
+        }
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TS) {
+                const int si = idx / (BV / 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gpf[m][r] = gami[ch * DK + si * 16 + 4 * lq + r];
+            }
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int q = 0; q < QPT; ++q) {
+            const int idx = tid + NTHR_B * q;
+            if (idx < QP) {
+                *reinterpret_cast<uint4*>(&sPT[idx / (C / 8)][(idx % (C / 8)) * 8]) = pf[q];
+            } else if (idx < QP + QW) {
+                const int e = idx - QP;
+                *reinterpret_cast<uint4*>(&sK[e / (DK / 8)][(e % (DK / 8)) * 8]) = pf[q];
+            } else if (idx < QP + QW + QK) {
+                const int e = idx - QP - QW;
+                *reinterpret_cast<uint4*>(&sQT[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
+            } else if (idx < QP + QW + 2 * QK) {
+                const int e = idx - QP - QW - QK;
+                *reinterpret_cast<uint4*>(&sWT[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
+            } else if (idx < QALL) {  // dO row r, columns j0..j0+7 -> dO^T
+                const int e = idx - QP - QW - 2 * QK;
+                const int r = e / (BV / 8), j0 = (e % (BV / 8)) * 8;
+                const uint32_t u[4] = {pf[q].x, pf[q].y, pf[q].z, pf[q].w};
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    sdOt[j0 + 2 * z][r].bits = (uint16_t)(u[z] & 0xFFFFu);
+                    sdOt[j0 + 2 * z + 1][r].bits = (uint16_t)(u[z] >> 16);
+                }
+            }
+        }
+    };
+    float gc[MS][4];
+    fetch(NC - 1);
+    stash();
+#pragma unroll
+    for (int m = 0; m < MS; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
+    __syncthreads();
+
+    for (int n = NC - 1; n >= 0; --n) {
+        const size_t ch = (size_t)bh * NC + n;
+        if (n > 0) fetch(n - 1);
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TS) {
+                const int si = idx / (BV / 16), sj = idx % (BV / 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dSt[(ch * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = dacc[m][r];
+            }
+        }
+        // dD = scale P^T dO + Kh dS'
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TD) {
+                const int ti = idx / (BV / 16), tj = idx % (BV / 16);
+                f32x4 acc = mma_kc<C>(zero4(), &sPT[ti * 16][0], PT, &sdOt[tj * 16][0], PT);
+                acc = mma_kc<DK>(acc, &sK[ti * 16][0], PA, &sdSt[tj * 16][0], PA);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dDt[(ch * C + ti * 16 + 4 * lq + r) * DV + v0 + tj * 16 + lr] = acc[r];
+                *reinterpret_cast<uint2*>(&sdDt[tj * 16 + lr][ti * 16 + 4 * lq]) =
+                    pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+            }
+        }
+        __syncthreads();
+        // dS <- gam o dS' + Qg^T dO - W^T dD
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TS) {
+                const int si = idx / (BV / 16), sj = idx % (BV / 16);
+                f32x4 acc;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = gc[m][r] * dacc[m][r];
+                acc = mma_kc<C>(acc, &sQT[si * 16][0], PT, &sdOt[sj * 16][0], PT);
+                const f32x4 wd = mma_kc<C>(zero4(), &sWT[si * 16][0], PT, &sdDt[sj * 16][0], PT);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dacc[m][r] = acc[r] - wd[r];
+                *reinterpret_cast<uint2*>(&sdSt[sj * 16 + lr][si * 16 + 4 * lq]) =
+                    pack4_bf16(dacc[m][0], dacc[m][1], dacc[m][2], dacc[m][3]);
+            }
+        }
+        __syncthreads();
+        if (n > 0) {
+            stash();
+#pragma unroll
+            for (int m = 0; m < MS; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
+        }
+        __syncthreads();
+    }
+    if (dh0) {
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TS) {
+                const int si = idx / (BV / 16), sj = idx % (BV / 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dh0[((size_t)bh * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = dacc[m][r];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // bchunk1
 // ---------------------------------------------------------------------------
@@ -193,10 +383,12 @@ bchunk1_kernel(const TIn* __restrict__ v, const float* __restrict__ beta,
     const size_t rsV = (size_t)H * DV;
 
     {
-        const float* Wp = Wi + (size_t)ch * C * DK;
         for (int idx = tid; idx < C * DK / 4; idx += NTHR) {
             const int r = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
-            st4(&sW[r][c4], load4<float>(Wp + r * DK + c4));
+            if constexpr (bf16_tables<TIn, C, DK>())
+                st4(&sW[r][c4], load4<bf16>(reinterpret_cast<const bf16*>(Wi) + (size_t)ch * C * DK + r * DK + c4));
+            else
+                st4(&sW[r][c4], load4<float>(Wi + (size_t)ch * C * DK + r * DK + c4));
         }
         const float* Tp = Tmi + (size_t)ch * C * C;
         for (int idx = tid; idx < C * C / 4; idx += NTHR) {
@@ -700,7 +892,15 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
         if (s != GDN_OK) return s;
     }
     const int BH = p.B * p.H;
-    {
+    if constexpr (bf16_tables<TIn, C, DK>()) {
+        const size_t n = p.n_ch;
+        dim3 grid((unsigned)(((BH + 7) / 8) * 8 * (DV / 32))), block(NTHR_B);
+        GDN_LAUNCH("bscan", (bscan2_kernel<C, DK, DV>), grid, block, st,
+                   (const bf16*)(ws + p.o_Ps) + n * C * C, (const bf16*)(ws + p.o_Kh) + n * C * DK,
+                   (const bf16*)(ws + p.o_Qg) + n * C * DK, (const bf16*)(ws + p.o_W) + n * C * DK,
+                   (const float*)(ws + p.o_gam), (const bf16*)dO, dhT, (float*)(ws + p.o_dSt),
+                   (float*)(ws + p.o_dDt), dh0, BH, p.T, p.H, p.NC);
+    } else {
         using SC = BScanCfg<DV>;
         dim3 grid((unsigned)(((BH + 7) / 8) * 8 * SC::NS)), block(NTHR);
         GDN_LAUNCH("bscan", (bscan_kernel<TIn, C, DK, DV, MT>), grid, block, st,

@@ -45,6 +45,14 @@ __device__ __forceinline__ bool in_level(int i, int j, int h)
     return (i / (2 * h) == j / (2 * h)) && ((i / h) & 1) && !((j / h) & 1);
 }
 
+// bf16 inputs at chunk 64 keep the chunk tables (W, Qg, Kh, P) in bf16, laid
+// out for the K-contiguous MFMA operands of the scans; other shapes keep fp32.
+template <typename TIn, int C, int DK>
+constexpr bool bf16_tables()
+{
+    return sizeof(TIn) == 2 && C == 64 && DK >= 64;
+}
+
 template <typename TIn>
 __device__ __forceinline__ float4 load4(const TIn* p);
 template <>

@@ -160,36 +160,61 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
         __syncthreads();
     }
 
-    // ---- scores out: Ps = scale P (global, upper part zero), A (x beta) to LDS
+    // ---- scores out: Ps = scale P (global, upper part zero), A (x beta) to LDS.
+    // bf16 inputs: Ps as bf16, and in training also its transpose PsT.
+    constexpr bool BT = bf16_tables<TIn, C, DK>();
+    const size_t nch = gridDim.x;
+    const bool bwdt = Tmo != nullptr;
     float* Ps = Pso + (size_t)ch * C * C;
+    bf16* Psb = reinterpret_cast<bf16*>(Pso) + (size_t)ch * C * C;
+    bf16* PsTb = reinterpret_cast<bf16*>(Pso) + nch * C * C + (size_t)ch * C * C;
+    auto put_ps = [&](int i0, int j, const float (&pv)[4]) {  // rows i0..i0+3, column j
+        if (BT) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Psb[(i0 + r) * C + j] = f32_to_bf16(pv[r]);
+            if (bwdt)
+                *reinterpret_cast<uint2*>(&PsTb[j * C + i0]) = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ps[(i0 + r) * C + j] = pv[r];
+        }
+    };
 #pragma unroll
     for (int s = 0; s < G::MAXOFF; ++s) {
         const int idx = w + 4 * s;
         if (idx < G::NOFF) {
             int ti, tj;
             off_tile(idx, ti, tj);
+            float pv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
-                Ps[i * C + j] = scale * accP[s][r];
+                pv[r] = scale * accP[s][r];
                 sA[i][j] = sbeta[i] * accA[s][r];
             }
+            put_ps(ti * 16 + acc_row(0), tj * 16 + acc_col(), pv);
         }
     }
     if (w < NB) {
         const int t = w;
+        float pv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = t * 16 + acc_row(r), j = t * 16 + acc_col();
-            const float pv = i > j ? dP[r] : (i == j ? sdiag[i] : 0.f);
-            Ps[i * C + j] = scale * pv;
+            pv[r] = scale * (i > j ? dP[r] : (i == j ? sdiag[i] : 0.f));
             sA[i][j] = i > j ? sbeta[i] * dA[r] : 0.f;
         }
+        put_ps(t * 16 + acc_row(0), t * 16 + acc_col(), pv);
     }
     for (int idx = tid; idx < C * C; idx += NTHR) {
         const int i = idx / C, j = idx % C;
         if (i / 16 < j / 16) {
-            Ps[idx] = 0.f;
+            if (BT) {
+                Psb[idx] = f32_to_bf16(0.f);
+                if (bwdt) PsTb[j * C + i] = f32_to_bf16(0.f);
+            } else {
+                Ps[idx] = 0.f;
+            }
             sA[i][j] = 0.f;
         }
     }
@@ -204,13 +229,12 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
     __syncthreads();
     if (cp) {
         float Gm = part ? stot[0][c] : 1.f;
-        float* Qg = Qgo + (size_t)ch * C * DK;
-        float* Kh = Kho + (size_t)ch * C * DK;
+        float qgv[HALF], khv[HALF];
 #pragma unroll
         for (int i = 0; i < HALF; ++i) {
             const int r = part * HALF + i;
             Gm *= a[i];
-            Qg[r * DK + c] = scale * sq[r][c] * Gm;
+            qgv[i] = scale * sq[r][c] * Gm;
             sY[r][c] = sbeta[r] * sk[r][c] * Gm;
         }
         if (part == 1) gamo[(size_t)ch * DK + c] = Gm;
@@ -218,8 +242,37 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
 #pragma unroll
         for (int i = HALF - 1; i >= 0; --i) {
             const int r = part * HALF + i;
-            Kh[r * DK + c] = sk[r][c] * kap;
+            khv[i] = sk[r][c] * kap;
             kap *= a[i];
+        }
+        if (BT) {
+            // forward: Qg [C][DK], KhT [DK][C]; training also QgT [DK][C], Kh [C][DK]
+            bf16* Qgb = reinterpret_cast<bf16*>(Qgo) + (size_t)ch * C * DK;
+            bf16* QgTb = reinterpret_cast<bf16*>(Qgo) + nch * C * DK + (size_t)ch * C * DK;
+            bf16* KhTb = reinterpret_cast<bf16*>(Kho) + (size_t)ch * C * DK;
+            bf16* Khb = reinterpret_cast<bf16*>(Kho) + nch * C * DK + (size_t)ch * C * DK;
+#pragma unroll
+            for (int i = 0; i < HALF; ++i) Qgb[(part * HALF + i) * DK + c] = f32_to_bf16(qgv[i]);
+#pragma unroll
+            for (int i = 0; i < HALF; i += 4)
+                *reinterpret_cast<uint2*>(&KhTb[c * C + part * HALF + i]) =
+                    pack4_bf16(khv[i], khv[i + 1], khv[i + 2], khv[i + 3]);
+            if (bwdt) {
+#pragma unroll
+                for (int i = 0; i < HALF; i += 4)
+                    *reinterpret_cast<uint2*>(&QgTb[c * C + part * HALF + i]) =
+                        pack4_bf16(qgv[i], qgv[i + 1], qgv[i + 2], qgv[i + 3]);
+#pragma unroll
+                for (int i = 0; i < HALF; ++i) Khb[(part * HALF + i) * DK + c] = f32_to_bf16(khv[i]);
+            }
+        } else {
+            float* Qg = Qgo + (size_t)ch * C * DK;
+            float* Kh = Kho + (size_t)ch * C * DK;
+#pragma unroll
+            for (int i = 0; i < HALF; ++i) {
+                Qg[(part * HALF + i) * DK + c] = qgv[i];
+                Kh[(part * HALF + i) * DK + c] = khv[i];
+            }
         }
     }
 
@@ -282,11 +335,22 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
     }
     __syncthreads();
     float* Wp = Wo + (size_t)ch * C * DK;
+    bf16* Wb = reinterpret_cast<bf16*>(Wo) + (size_t)ch * C * DK;
+    bf16* WTb = reinterpret_cast<bf16*>(Wo) + nch * C * DK + (size_t)ch * C * DK;
     for (int idx = w; idx < NB * (DK / 16); idx += 4) {
         const int ti = idx / (DK / 16), tj = idx % (DK / 16);
         f32x4 acc = mma16<MT_F32>(zero4(), &sT[ti * 16 * PC], PC, 1, &sY[0][tj * 16], PD, 1, 16 * (ti + 1));
+        if (BT) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Wp[(ti * 16 + acc_row(r)) * DK + tj * 16 + acc_col()] = acc[r];
+            for (int r = 0; r < 4; ++r)
+                Wb[(ti * 16 + acc_row(r)) * DK + tj * 16 + acc_col()] = f32_to_bf16(acc[r]);
+            if (bwdt)
+                *reinterpret_cast<uint2*>(&WTb[(tj * 16 + acc_col()) * C + ti * 16 + acc_row(0)]) =
+                    pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Wp[(ti * 16 + acc_row(r)) * DK + tj * 16 + acc_col()] = acc[r];
+        }
     }
     float* Up = Uo + (size_t)ch * C * DV;
     for (int idx = w; idx < NB * (DV / 16); idx += 4) {
@@ -437,6 +501,214 @@ scan_kernel(const float* __restrict__ Wi, const float* __restrict__ Ui,
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// scan over bf16 chunk tables (bf16 inputs): 8 waves; the fp32 state slice
+// lives in the MFMA accumulators of its owner waves for the whole sequence,
+// its bf16 copy S^T [BV][DK] in LDS is the B operand of W S and Qg S; every
+// operand is K-contiguous (one 16-byte LDS read per lane per MFMA); the next
+// chunk's tables are fetched into registers while the current one computes.
+// ---------------------------------------------------------------------------
+constexpr int NTHR_S = 512;
+
+template <int C, int DK, int DV, bool SAVE, bool OUT>
+__global__ void __launch_bounds__(NTHR_S)
+scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
+             const bf16* __restrict__ KhTb, const bf16* __restrict__ Psb,
+             const float* __restrict__ Ui, const float* __restrict__ gami,
+             const float* __restrict__ h0, bf16* __restrict__ o, float* __restrict__ hT,
+             float* __restrict__ Sst, int BH, int T, int H, int NC)
+{
+    constexpr int BV = 32, NS = DV / BV, NW = NTHR_S / 64;
+    constexpr int PA = DK + 8, PT = C + 8;  // bf16 pitches: rows 16-byte aligned, banks spread
+    constexpr int TD = (C / 16) * (BV / 16), TS = (DK / 16) * (BV / 16);
+    constexpr int MD = (TD + NW - 1) / NW, MS = (TS + NW - 1) / NW;
+    // 16-byte words of one chunk's tables
+    constexpr int QW = C * DK / 8, QK = DK * C / 8, QP = C * C / 8;
+    constexpr int QALL = 2 * QW + QK + QP, QPT = (QALL + NTHR_S - 1) / NTHR_S;
+    __shared__ __align__(16) bf16 sW[C][PA], sQ[C][PA], sKT[DK][PT], sP[C][PT], sSt[BV][PA], sDt[BV][PT];
+
+    const int x = blockIdx.x;
+    const int grp = x / (8 * NS), rem = x % (8 * NS);
+    const int sl = rem / 8, bh = grp * 8 + rem % 8;
+    if (bh >= BH) return;
+    const int b = bh / H, h = bh % H;
+    const int v0 = sl * BV;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+
+    // state tiles owned by this wave: S[si*16 + 4lq + r][sj*16 + lr]
+    f32x4 sacc[MS];
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        const int idx = w + NW * m;
+        sacc[m] = zero4();
+        if (idx < TS) {
+            const int si = idx / (BV / 16), sj = idx % (BV / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sacc[m][r] = h0 ? h0[((size_t)bh * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] : 0.f;
+            *reinterpret_cast<uint2*>(&sSt[sj * 16 + lr][si * 16 + 4 * lq]) =
+                pack4_bf16(sacc[m][0], sacc[m][1], sacc[m][2], sacc[m][3]);
+        }
+    }
+
+    uint4 pf[QPT];
+    float upf[MD][4], gpf[MS][4];
+    auto fetch = [&](int n) {  // chunk n tables -> registers
+        const size_t ch = (size_t)bh * NC + n;
+#pragma unroll
+        for (int q = 0; q < QPT; ++q) {
+            const int idx = tid + NTHR_S * q;
+            uint4 val = uint4{0u, 0u, 0u, 0u};
+            if (idx < QW) val = reinterpret_cast<const uint4*>(Wb + ch * C * DK)[idx];
+            else if (idx < 2 * QW) val = reinterpret_cast<const uint4*>(Qgb + ch * C * DK)[idx - QW];
+            else if (idx < 2 * QW + QK) val = reinterpret_cast<const uint4*>(KhTb + ch * C * DK)[idx - 2 * QW];
+            else if (idx < QALL) val = reinterpret_cast<const uint4*>(Psb + ch * C * C)[idx - 2 * QW - QK];
+            pf[q] = val;
+        }
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TD) {
+                const int ti = idx / (BV / 16), tj = idx % (BV / 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    upf[m][r] = Ui[(ch * C + ti * 16 + 4 * lq + r) * DV + v0 + tj * 16 + lr];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TS) {
+                const int si = idx / (BV / 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gpf[m][r] = gami[ch * DK + si * 16 + 4 * lq + r];
+            }
+        }
+    };
+    auto stash = [&]() {  // registers -> LDS tables
+#pragma unroll
+        for (int q = 0; q < QPT; ++q) {
+            const int idx = tid + NTHR_S * q;
+            if (idx < QW) {
+                *reinterpret_cast<uint4*>(&sW[idx / (DK / 8)][(idx % (DK / 8)) * 8]) = pf[q];
+            } else if (idx < 2 * QW) {
+                const int e = idx - QW;
+                *reinterpret_cast<uint4*>(&sQ[e / (DK / 8)][(e % (DK / 8)) * 8]) = pf[q];
+            } else if (idx < 2 * QW + QK) {
+                const int e = idx - 2 * QW;
+                *reinterpret_cast<uint4*>(&sKT[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
+            } else if (idx < QALL) {
+                const int e = idx - 2 * QW - QK;
+                *reinterpret_cast<uint4*>(&sP[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
+            }
+        }
+    };
+    fetch(0);
+    stash();
+    float uc[MD][4], gc[MS][4];
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) uc[m][r] = upf[m][r];
+#pragma unroll
+    for (int m = 0; m < MS; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
+    __syncthreads();
+
+    for (int n = 0; n < NC; ++n) {
+        const size_t ch = (size_t)bh * NC + n;
+        if (n + 1 < NC) fetch(n + 1);
+        if (SAVE) {
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int idx = w + NW * m;
+                if (idx < TS) {
+                    const int si = idx / (BV / 16), sj = idx % (BV / 16);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Sst[(ch * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = sacc[m][r];
+                }
+            }
+        }
+        // D = U - W S  and  O1 = Qg S
+        f32x4 o1[MD];
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TD) {
+                const int ti = idx / (BV / 16), tj = idx % (BV / 16);
+                f32x4 ws = mma_kc<DK>(zero4(), &sW[ti * 16][0], PA, &sSt[tj * 16][0], PA);
+                float dv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dv[r] = uc[m][r] - ws[r];
+                *reinterpret_cast<uint2*>(&sDt[tj * 16 + lr][ti * 16 + 4 * lq]) =
+                    pack4_bf16(dv[0], dv[1], dv[2], dv[3]);
+                if (OUT) o1[m] = mma_kc<DK>(zero4(), &sQ[ti * 16][0], PA, &sSt[tj * 16][0], PA);
+            }
+        }
+        __syncthreads();
+        if (OUT) {
+#pragma unroll
+            for (int m = 0; m < MD; ++m) {
+                const int idx = w + NW * m;
+                if (idx < TD) {
+                    const int ti = idx / (BV / 16), tj = idx % (BV / 16);
+                    // P is lower triangular: columns past the tile row are zero
+                    const int K = ((16 * (ti + 1) + 31) / 32) * 32;
+                    f32x4 acc = mma_kc_dyn(o1[m], &sP[ti * 16][0], PT, &sDt[tj * 16][0], PT, K);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = n * C + ti * 16 + 4 * lq + r;
+                        if (t < T) o[(((size_t)b * T + t) * H + h) * DV + v0 + tj * 16 + lr] = f32_to_bf16(acc[r]);
+                    }
+                }
+            }
+        }
+        // S <- gam o S + Kh^T D
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TS) {
+                const int si = idx / (BV / 16), sj = idx % (BV / 16);
+                f32x4 acc;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = gc[m][r] * sacc[m][r];
+                sacc[m] = mma_kc<C>(acc, &sKT[si * 16][0], PT, &sDt[sj * 16][0], PT);
+                *reinterpret_cast<uint2*>(&sSt[sj * 16 + lr][si * 16 + 4 * lq]) =
+                    pack4_bf16(sacc[m][0], sacc[m][1], sacc[m][2], sacc[m][3]);
+            }
+        }
+        __syncthreads();
+        if (n + 1 < NC) {
+            stash();
+#pragma unroll
+            for (int m = 0; m < MD; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) uc[m][r] = upf[m][r];
+#pragma unroll
+            for (int m = 0; m < MS; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
+        }
+        __syncthreads();
+    }
+    if (hT) {
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TS) {
+                const int si = idx / (BV / 16), sj = idx % (BV / 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    hT[((size_t)bh * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = sacc[m][r];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
@@ -470,6 +742,18 @@ gdn_status run_scan(const Plan& p, const float* h0, void* o, float* hT, char* ws
     using SC = ScanCfg<DV>;
     const int BH = p.B * p.H;
     const int ngrp = (BH + 7) / 8;
+    if constexpr (bf16_tables<TIn, C, DK>()) {
+        const size_t n = p.n_ch;
+        dim3 grid((unsigned)(ngrp * 8 * (DV / 32))), block(NTHR_S);
+        GDN_LAUNCH(SAVE ? (OUT ? "scan_train" : "scan_save") : "scan",
+                   (scan2_kernel<C, DK, DV, SAVE, OUT>), grid, block, st,
+                   (const bf16*)(ws + p.o_W), (const bf16*)(ws + p.o_Qg),
+                   (const bf16*)(ws + p.o_Kh), (const bf16*)(ws + p.o_Ps),
+                   (const float*)(ws + p.o_U), (const float*)(ws + p.o_gam), h0, (bf16*)o, hT,
+                   SAVE ? (float*)(ws + p.o_Sst) : nullptr, BH, p.T, p.H, p.NC);
+        (void)n;
+        return GDN_OK;
+    }
     dim3 grid((unsigned)(ngrp * 8 * SC::NS)), block(NTHR);
     GDN_LAUNCH(SAVE ? (OUT ? "scan_train" : "scan_save") : "scan", (scan_kernel<TIn, C, DK, DV, MT, SAVE, OUT>), grid, block, st,
                        (const float*)(ws + p.o_W), (const float*)(ws + p.o_U),

@@ -130,3 +130,46 @@ __device__ __forceinline__ f32x4 mma16fd(f32x4 acc, FA fa, FB fb, int K)
 }
 
 }  // namespace gdn
+
+namespace gdn {
+
+// K-contiguous bf16 operands: A is [16 rows][K] and Bt is [16 columns][K]
+// (B transposed), both with K contiguous, so each lane fetches its eight
+// operand elements with one 16-byte LDS read.  Rows must be 16-byte aligned.
+//   D(i, j) += sum_k A[i*lda + k] * Bt[j*ldb + k]
+template <int K>
+__device__ __forceinline__ f32x4 mma_kc(f32x4 acc, const bf16* __restrict__ A, int lda,
+                                        const bf16* __restrict__ Bt, int ldb)
+{
+    const int l = lane_id();
+    const int r = l & 15, kk = l >> 4;
+#pragma unroll
+    for (int k = 0; k < K; k += 32) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + k + 8 * kk);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bt + r * ldb + k + 8 * kk);
+        acc = mfma_bf16_16x16x32(a, b, acc);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ f32x4 mma_kc_dyn(f32x4 acc, const bf16* __restrict__ A, int lda,
+                                            const bf16* __restrict__ Bt, int ldb, int K)
+{
+    const int l = lane_id();
+    const int r = l & 15, kk = l >> 4;
+    for (int k = 0; k < K; k += 32) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + k + 8 * kk);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bt + r * ldb + k + 8 * kk);
+        acc = mfma_bf16_16x16x32(a, b, acc);
+    }
+    return acc;
+}
+
+// four consecutive bf16 (8 bytes) from four floats, round to nearest even
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d)
+{
+    return uint2{(uint32_t)f32_to_bf16(a).bits | ((uint32_t)f32_to_bf16(b).bits << 16),
+                 (uint32_t)f32_to_bf16(c).bits | ((uint32_t)f32_to_bf16(d).bits << 16)};
+}
+
+}  // namespace gdn
