@@ -526,6 +526,254 @@ bchunk1_kernel(const TIn* __restrict__ v, const float* __restrict__ beta,
     for (int r = tid; r < C; r += NTHR) dbpo[(size_t)ch * C + r] = dbp_part;
 }
 
+
+// ---------------------------------------------------------------------------
+// bchunk1 over bf16 tables (bf16 inputs): 8 waves, Dv streamed in 32-column
+// tiles with the next tile prefetched into registers; D comes from the forward
+// (saved by the scan); the five contractions over Dv are single K = 32 bf16
+// MFMAs on K-contiguous LDS tiles; dgam is summed from the fp32 states as they
+// are loaded; dX_V = T^T dD stays in fp32.
+// ---------------------------------------------------------------------------
+constexpr int NTHR_C = 512;
+
+template <int C, int DK, int DV>
+__global__ void __launch_bounds__(NTHR_C)
+bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
+                const bf16* __restrict__ dO, const bf16* __restrict__ Dst,
+                const float* __restrict__ Tmi, const float* __restrict__ Sst,
+                const float* __restrict__ dSt, const float* __restrict__ dDt,
+                bf16* __restrict__ dvo, float* __restrict__ dQgo, float* __restrict__ dWgo,
+                float* __restrict__ dKho, float* __restrict__ dPso, float* __restrict__ dT1o,
+                float* __restrict__ dgmo, float* __restrict__ dbpo, int T, int H, int NC)
+{
+    constexpr int BW = 32, NW = NTHR_C / 64, NB = C / 16;
+    constexpr int PB = BW + 8, PF = BW + 4, PC = C + 4;
+    constexpr int T3 = NB * (DK / 16), M3 = (T3 + NW - 1) / NW;
+    constexpr int T2 = NB * NB, M2 = (T2 + NW - 1) / NW;
+    constexpr int TD = NB * (BW / 16), MD = (TD + NW - 1) / NW;
+    constexpr int NS4 = DK * BW / 4;                 // float4 words of an S tile
+    constexpr int QS = (NS4 + NTHR_C - 1) / NTHR_C;  // per thread
+    constexpr int NB8 = C * BW / 8;                  // uint4 words of a bf16 [C][BW] tile
+    constexpr int ND4 = C * BW / 4;                  // float4 words of dD
+    static_assert(NB8 <= NTHR_C / 2 && ND4 <= NTHR_C, "tile split assumes C*BW <= 2048");
+    __shared__ __align__(16) bf16 sS[DK][PB], sdS[DK][PB], sdO[C][PB], sD[C][PB], sdD[C][PB], sXV[C][PB];
+    __shared__ __align__(16) float sT[C][PC], sdDf[C][PF], sv[C][PF];
+    __shared__ float sbeta[C], sred[NW][C];
+
+    const int ch = blockIdx.x;
+    const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
+    const int t0 = n * C;
+    const int nvalid = min(C, T - t0);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+    const size_t tok0 = ((size_t)b * T + t0) * H + h;
+
+    {
+        const float* Tp = Tmi + (size_t)ch * C * C;
+        for (int idx = tid; idx < C * C / 4; idx += NTHR_C) {
+            const int r = idx / (C / 4), c4 = (idx % (C / 4)) * 4;
+            st4(&sT[r][c4], load4<float>(Tp + r * C + c4));
+        }
+        for (int r = tid; r < C; r += NTHR_C) sbeta[r] = r < nvalid ? beta[tok0 + (size_t)r * H] : 0.f;
+    }
+    const float* Sp = Sst + (size_t)ch * DK * DV;
+    const float* dSp = dSt + (size_t)ch * DK * DV;
+    const float* dDp = dDt + (size_t)ch * C * DV;
+    const bf16* Dp = Dst + (size_t)ch * C * DV;
+
+    float4 pS[QS], pdS[QS], pdD;
+    uint4 pa, pb;  // threads < 256: D and v; threads >= 256: dO
+    auto fetch = [&](int v0) {
+#pragma unroll
+        for (int q = 0; q < QS; ++q) {
+            const int idx = tid + NTHR_C * q;
+            if (idx < NS4) {
+                const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
+                pS[q] = load4<float>(Sp + i * DV + v0 + j4);
+                pdS[q] = load4<float>(dSp + i * DV + v0 + j4);
+            }
+        }
+        if (tid < ND4) {
+            const int r = tid / (BW / 4), j4 = (tid % (BW / 4)) * 4;
+            pdD = load4<float>(dDp + r * DV + v0 + j4);
+        }
+        pa = pb = uint4{0u, 0u, 0u, 0u};
+        if (tid < NB8) {
+            const int r = tid / (BW / 8), j0 = (tid % (BW / 8)) * 8;
+            pa = *reinterpret_cast<const uint4*>(Dp + r * DV + v0 + j0);
+            if (r < nvalid) pb = *reinterpret_cast<const uint4*>(v + (tok0 + (size_t)r * H) * DV + v0 + j0);
+        } else if (tid >= NTHR_C / 2 && tid - NTHR_C / 2 < NB8) {
+            const int e = tid - NTHR_C / 2;
+            const int r = e / (BW / 8), j0 = (e % (BW / 8)) * 8;
+            if (r < nvalid) pa = *reinterpret_cast<const uint4*>(dO + (tok0 + (size_t)r * H) * DV + v0 + j0);
+        }
+    };
+    float dgm_part[QS];
+#pragma unroll
+    for (int q = 0; q < QS; ++q) dgm_part[q] = 0.f;
+    auto stash = [&]() {
+#pragma unroll
+        for (int q = 0; q < QS; ++q) {
+            const int idx = tid + NTHR_C * q;
+            if (idx < NS4) {
+                const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
+                const float4 a4 = pS[q], d4 = pdS[q];
+                dgm_part[q] += a4.x * d4.x + a4.y * d4.y + a4.z * d4.z + a4.w * d4.w;
+                *reinterpret_cast<uint2*>(&sS[i][j4]) = pack4_bf16(a4.x, a4.y, a4.z, a4.w);
+                *reinterpret_cast<uint2*>(&sdS[i][j4]) = pack4_bf16(d4.x, d4.y, d4.z, d4.w);
+            }
+        }
+        if (tid < ND4) {
+            const int r = tid / (BW / 4), j4 = (tid % (BW / 4)) * 4;
+            st4(&sdDf[r][j4], pdD);
+            *reinterpret_cast<uint2*>(&sdD[r][j4]) = pack4_bf16(pdD.x, pdD.y, pdD.z, pdD.w);
+        }
+        if (tid < NB8) {
+            const int r = tid / (BW / 8), j0 = (tid % (BW / 8)) * 8;
+            *reinterpret_cast<uint4*>(&sD[r][j0]) = pa;
+            const uint32_t u[4] = {pb.x, pb.y, pb.z, pb.w};
+            float vv[8];
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                vv[2 * z] = __uint_as_float(u[z] << 16);
+                vv[2 * z + 1] = __uint_as_float(u[z] & 0xFFFF0000u);
+            }
+            st4(&sv[r][j0], float4{vv[0], vv[1], vv[2], vv[3]});
+            st4(&sv[r][j0 + 4], float4{vv[4], vv[5], vv[6], vv[7]});
+            const float bt = sbeta[r];
+            *reinterpret_cast<uint2*>(&sXV[r][j0]) = pack4_bf16(bt * vv[0], bt * vv[1], bt * vv[2], bt * vv[3]);
+            *reinterpret_cast<uint2*>(&sXV[r][j0 + 4]) = pack4_bf16(bt * vv[4], bt * vv[5], bt * vv[6], bt * vv[7]);
+        } else if (tid >= NTHR_C / 2 && tid - NTHR_C / 2 < NB8) {
+            const int e = tid - NTHR_C / 2;
+            const int r = e / (BW / 8), j0 = (e % (BW / 8)) * 8;
+            *reinterpret_cast<uint4*>(&sdO[r][j0]) = pa;
+        }
+    };
+
+    f32x4 aQ[M3], aW[M3], aK[M3], aP[M2], aT[M2];
+#pragma unroll
+    for (int m = 0; m < M3; ++m) aQ[m] = aW[m] = aK[m] = zero4();
+#pragma unroll
+    for (int m = 0; m < M2; ++m) aP[m] = aT[m] = zero4();
+    float dbr[MD][4];
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dbr[m][r] = 0.f;
+
+    __syncthreads();  // sbeta ready for the first stash
+    fetch(0);
+    stash();
+    __syncthreads();
+    for (int v0 = 0; v0 < DV; v0 += BW) {
+        if (v0 + BW < DV) fetch(v0 + BW);
+        // dX_V = T^T dD (fp32): dv = beta dX_V, and <dX_V, v> for dbeta
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TD) {
+                const int ti = idx / (BW / 16), tj = idx % (BW / 16);
+                const f32x4 dx = mma16k<MT_F32, C>(zero4(), &sT[0][ti * 16], 1, PC, &sdDf[0][tj * 16], PF, 1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                    if (i < nvalid) dvo[(tok0 + (size_t)i * H) * DV + v0 + j] = f32_to_bf16(sbeta[i] * dx[r]);
+                    dbr[m][r] += dx[r] * sv[i][j];
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M3; ++m) {
+            const int idx = w + NW * m;
+            if (idx < T3) {
+                const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+                aQ[m] = mma_kc<BW>(aQ[m], &sdO[ti * 16][0], PB, &sS[tj * 16][0], PB);
+                aW[m] = mma_kc<BW>(aW[m], &sdD[ti * 16][0], PB, &sS[tj * 16][0], PB);
+                aK[m] = mma_kc<BW>(aK[m], &sD[ti * 16][0], PB, &sdS[tj * 16][0], PB);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M2; ++m) {
+            const int idx = w + NW * m;
+            if (idx < T2) {
+                const int ti = idx / NB, tj = idx % NB;
+                aP[m] = mma_kc<BW>(aP[m], &sdO[ti * 16][0], PB, &sD[tj * 16][0], PB);
+                aT[m] = mma_kc<BW>(aT[m], &sdD[ti * 16][0], PB, &sXV[tj * 16][0], PB);
+            }
+        }
+        __syncthreads();
+        if (v0 + BW < DV) stash();
+        __syncthreads();
+    }
+
+    // outputs
+    float* dQp = dQgo + (size_t)ch * C * DK;
+    float* dWp = dWgo + (size_t)ch * C * DK;
+    float* dKp = dKho + (size_t)ch * C * DK;
+#pragma unroll
+    for (int m = 0; m < M3; ++m) {
+        const int idx = w + NW * m;
+        if (idx < T3) {
+            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                dQp[i * DK + j] = aQ[m][r];
+                dWp[i * DK + j] = -aW[m][r];
+                dKp[i * DK + j] = aK[m][r];
+            }
+        }
+    }
+    float* dPp = dPso + (size_t)ch * C * C;
+    float* dTp = dT1o + (size_t)ch * C * C;
+#pragma unroll
+    for (int m = 0; m < M2; ++m) {
+        const int idx = w + NW * m;
+        if (idx < T2) {
+            const int ti = idx / NB, tj = idx % NB;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                dPp[i * C + j] = aP[m][r];
+                dTp[i * C + j] = aT[m][r];
+            }
+        }
+    }
+    // dgam: the BW/4 threads of one state row hold its partial sums
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+        float sgm = dgm_part[q];
+#pragma unroll
+        for (int off = 1; off < BW / 4; off <<= 1) sgm += __shfl_xor(sgm, off);
+        const int idx = tid + NTHR_C * q;
+        if (idx < NS4 && (idx % (BW / 4)) == 0) dgmo[(size_t)ch * DK + idx / (BW / 4)] = sgm;
+    }
+    // dbeta part: row sums of dX_V o v over the 16 columns of each tile, then
+    // over the column tiles (fixed order)
+    for (int idx = tid; idx < NW * C; idx += NTHR_C) (&sred[0][0])[idx] = 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MD; ++m) {
+        const int idx = w + NW * m;
+        if (idx < TD) {
+            const int ti = idx / (BW / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float sb = dbr[m][r];
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) sb += __shfl_xor(sb, off);
+                if (lr == 0) sred[w][ti * 16 + 4 * lq + r] = sb;
+            }
+        }
+    }
+    __syncthreads();
+    for (int r = tid; r < C; r += NTHR_C) {
+        float sb = 0.f;
+        for (int ww = 0; ww < NW; ++ww) sb += sred[ww][r];
+        dbpo[(size_t)ch * C + r] = sb;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // bchunk2
 // ---------------------------------------------------------------------------
@@ -911,6 +1159,15 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
         GDN_HIP_CHECK_LAUNCH();
     }
     dim3 gch((unsigned)p.n_ch);
+    if constexpr (bf16_tables<TIn, C, DK>()) {
+        GDN_LAUNCH("bchunk1", (bchunk1b_kernel<C, DK, DV>), gch, dim3(NTHR_C), st, (const bf16*)v,
+                   beta, (const bf16*)dO, (const bf16*)(ws + p.o_Dst), (const float*)(ws + p.o_Tm),
+                   (const float*)(ws + p.o_Sst), (const float*)(ws + p.o_dSt),
+                   (const float*)(ws + p.o_dDt), (bf16*)dv, (float*)(ws + p.o_dQg),
+                   (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh), (float*)(ws + p.o_dPs),
+                   (float*)(ws + p.o_dT1), (float*)(ws + p.o_dgm), (float*)(ws + p.o_dbp), p.T, p.H,
+                   p.NC);
+    } else
     GDN_LAUNCH("bchunk1", (bchunk1_kernel<TIn, C, DK, DV, MT>), gch, dim3(NTHR), st,
                        (const TIn*)v, beta, (const TIn*)dO, (const float*)(ws + p.o_W),
                        (const float*)(ws + p.o_U), (const float*)(ws + p.o_Tm),

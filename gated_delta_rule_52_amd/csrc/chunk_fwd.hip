@@ -517,7 +517,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
              const bf16* __restrict__ KhTb, const bf16* __restrict__ Psb,
              const float* __restrict__ Ui, const float* __restrict__ gami,
              const float* __restrict__ h0, bf16* __restrict__ o, float* __restrict__ hT,
-             float* __restrict__ Sst, int BH, int T, int H, int NC)
+             float* __restrict__ Sst, bf16* __restrict__ Dst, int BH, int T, int H, int NC)
 {
     constexpr int BV = 32, NS = DV / BV, NW = NTHR_S / 64;
     constexpr int PA = DK + 8, PT = C + 8;  // bf16 pitches: rows 16-byte aligned, banks spread
@@ -644,6 +644,11 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 float dv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dv[r] = uc[m][r] - ws[r];
+                if (SAVE) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Dst[(ch * C + ti * 16 + 4 * lq + r) * DV + v0 + tj * 16 + lr] = f32_to_bf16(dv[r]);
+                }
                 *reinterpret_cast<uint2*>(&sDt[tj * 16 + lr][ti * 16 + 4 * lq]) =
                     pack4_bf16(dv[0], dv[1], dv[2], dv[3]);
                 if (OUT) o1[m] = mma_kc<DK>(zero4(), &sQ[ti * 16][0], PA, &sSt[tj * 16][0], PA);
@@ -750,7 +755,8 @@ gdn_status run_scan(const Plan& p, const float* h0, void* o, float* hT, char* ws
                    (const bf16*)(ws + p.o_W), (const bf16*)(ws + p.o_Qg),
                    (const bf16*)(ws + p.o_Kh), (const bf16*)(ws + p.o_Ps),
                    (const float*)(ws + p.o_U), (const float*)(ws + p.o_gam), h0, (bf16*)o, hT,
-                   SAVE ? (float*)(ws + p.o_Sst) : nullptr, BH, p.T, p.H, p.NC);
+                   SAVE ? (float*)(ws + p.o_Sst) : nullptr, SAVE ? (bf16*)(ws + p.o_Dst) : nullptr,
+                   BH, p.T, p.H, p.NC);
         (void)n;
         return GDN_OK;
     }

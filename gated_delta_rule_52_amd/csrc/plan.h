@@ -18,6 +18,7 @@
 //   dQg [ch][C][Dk]   dL/dQg,  dWg [ch][C][Dk] dL/dW,  dKh [ch][C][Dk] dL/dKh
 //   dPs [ch][C][C]    dL/dPs,  dT1 [ch][C][C]  dL/dT through U
 //   dgm [ch][Dk]      dL/dgam, dbp [ch][C]     part of dL/dbeta (through U)
+//   Dst [ch][C][Dv]   the chunk deltas D (bf16; bf16 inputs at chunk 64 only)
 // G is the chunk-local inclusive cumulative log-decay and Gamma = exp(G).
 #pragma once
 
@@ -34,7 +35,7 @@ struct Plan {
     size_t n_ch;  // B * H * NC
     // byte offsets into the workspace
     size_t o_W, o_U, o_Qg, o_Kh, o_Ps, o_gam, o_Tm, o_Sst, o_dSt, o_dDt;
-    size_t o_dQg, o_dWg, o_dKh, o_dPs, o_dT1, o_dgm, o_dbp;
+    size_t o_dQg, o_dWg, o_dKh, o_dPs, o_dT1, o_dgm, o_dbp, o_Dst;
     size_t ws_fwd_bytes, ws_bwd_bytes;
 };
 
@@ -76,6 +77,7 @@ inline Plan make_plan(const gdn_shape& s, float scale)
     p.o_dT1 = off; off = align256(off + n * C * C * f);
     p.o_dgm = off; off = align256(off + n * Dk * f);
     p.o_dbp = off; off = align256(off + n * C * f);
+    p.o_Dst = off; off = align256(off + n * C * Dv * 2);
     p.ws_bwd_bytes = off;
     return p;
 }
