@@ -361,6 +361,348 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// prep over bf16 tables (bf16 inputs, chunk 64): 8 waves.  A column thread
+// owns one key channel of one 16-token tile and keeps its q, k and exp(g) in
+// registers; the level tables are bf16 rows with the channel index contiguous
+// (one 16-byte LDS read per MFMA operand); the diagonal scores are a chain of
+// the unscaled rows kept on the diagonal; W = T X_K and U = T X_V are bf16
+// MFMA products with X_K^T, X_V^T written by the column threads.
+// ---------------------------------------------------------------------------
+constexpr int NTHR_P = 512;
+
+template <int C, int DK, int DV, bool PCH>
+__global__ void __launch_bounds__(NTHR_P)
+prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+             const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int NC,
+             float scale, bf16* __restrict__ Wb, bf16* __restrict__ WTb, float* __restrict__ Uo,
+             bf16* __restrict__ Qgb, bf16* __restrict__ QgTb, bf16* __restrict__ KhTb,
+             bf16* __restrict__ Khb, bf16* __restrict__ Psb, bf16* __restrict__ PsTb,
+             float* __restrict__ gamo, float* __restrict__ Tmo)
+{
+    static_assert(C == 64 && DK == DV, "prep2: chunk 64, Dk == Dv");
+    constexpr int NW = NTHR_P / 64, RPP = 16, NPART = C / RPP, NB = C / 16;
+    constexpr int PA = DK + 8, PT = C + 8, PC = C + 4;
+    constexpr int NOFF = NB * (NB - 1) / 2;
+    // level tables; after the level loop the same bytes hold T and the merge scratch (fp32)
+    constexpr int SBUF = cmax(2 * C * PA * 2, 2 * C * PC * 4);
+    __shared__ __align__(16) char sbuf[SBUF];
+    __shared__ __align__(16) float sA[C][PC];  // A (beta rows), strictly lower; later T in bf16
+    __shared__ __align__(16) bf16 sXT[DK][PT];  // X_K^T, then X_V^T
+    __shared__ float sbeta[C], stot[NPART][DK];
+    bf16 (*sX)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf);
+    bf16 (*sY)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf + C * PA * 2);
+    float (*sT)[PC] = reinterpret_cast<float (*)[PC]>(sbuf);
+    float (*sYt)[PC] = reinterpret_cast<float (*)[PC]>(sbuf + C * PC * 4);
+    bf16 (*sTb)[PT] = reinterpret_cast<bf16 (*)[PT]>(&sA[0][0]);
+
+    const int ch = blockIdx.x;
+    const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
+    const int t0 = n * C;
+    const int nvalid = min(C, T - t0);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+    const size_t tok0 = ((size_t)b * T + t0) * H + h;
+    const size_t rsK = (size_t)H * DK;
+    const bool bwdt = Tmo != nullptr;
+    const bool cp = tid < NPART * DK;
+    const int c = tid % DK, part = cp ? tid / DK : 0, p0 = part * RPP;
+
+    float a[RPP], qv[RPP], kv[RPP];
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) {
+        const int r = p0 + i;
+        float gv = 0.f, qx = 0.f, kx = 0.f;
+        if (cp && r < nvalid) {
+            gv = PCH ? g[(tok0 + (size_t)r * H) * DK + c] : g[tok0 + (size_t)r * H];
+            qx = to_f32(q[tok0 * DK + r * rsK + c]);
+            kx = to_f32(k[tok0 * DK + r * rsK + c]);
+        }
+        a[i] = expf(gv);
+        qv[i] = qx;
+        kv[i] = kx;
+    }
+    for (int r = tid; r < C; r += NTHR_P) sbeta[r] = r < nvalid ? beta[tok0 + (size_t)r * H] : 0.f;
+    {
+        float pt = 1.f;
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) pt *= a[i];
+        if (cp) stot[part][c] = pt;
+    }
+    // level 0: unscaled rows, the diagonal P_ii = q_i . k_i
+    if (cp) {
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            sX[p0 + i][c] = f32_to_bf16(qv[i]);
+            sY[p0 + i][c] = f32_to_bf16(kv[i]);
+        }
+    }
+    __syncthreads();
+    f32x4 dP = zero4(), dA = zero4();
+    if (w < NB) {
+        const f32x4 tp = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sY[w * 16][0], PA);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dP[r] = (4 * lq + r == lr) ? tp[r] : 0.f;
+    }
+    // off-diagonal 16-tiles: waves NB.. own tile idx with (idx % (NW - NB)) == w - NB
+    constexpr int OW = NW - NB, MOFF = (NOFF + OW - 1) / OW;
+    f32x4 accP[MOFF], accA[MOFF];
+#pragma unroll
+    for (int m = 0; m < MOFF; ++m) accP[m] = accA[m] = zero4();
+    __syncthreads();
+
+#pragma unroll
+    for (int lvl = 0; (C >> (lvl + 1)) >= 1; ++lvl) {
+        const int hl = C >> (lvl + 1);
+        float F[RPP];
+        if (hl >= RPP) {
+            const int base = (p0 / (2 * hl)) * (2 * hl);
+            if (p0 >= base + hl) {
+                float pre = 1.f;
+                for (int pp = (base + hl) / RPP; pp < part; ++pp) pre *= stot[pp][c];
+                float Fr = pre;
+#pragma unroll
+                for (int i = 0; i < RPP; ++i) {
+                    Fr *= a[i];
+                    F[i] = Fr;
+                }
+            } else {
+                float suf = 1.f;
+                for (int pp = part + 1; pp < (base + hl) / RPP; ++pp) suf *= stot[pp][c];
+                float Fr = suf;
+#pragma unroll
+                for (int i = RPP - 1; i >= 0; --i) {
+                    F[i] = Fr;
+                    Fr *= a[i];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u0 = 0; u0 < RPP; u0 += (hl < RPP ? hl : RPP)) {
+                if (((p0 + u0) / hl) & 1) {
+                    float Fr = 1.f;
+#pragma unroll
+                    for (int i = 0; i < hl; ++i) {
+                        Fr *= a[u0 + i];
+                        F[u0 + i] = Fr;
+                    }
+                } else {
+                    float Fr = 1.f;
+#pragma unroll
+                    for (int i = hl - 1; i >= 0; --i) {
+                        F[u0 + i] = Fr;
+                        Fr *= a[u0 + i];
+                    }
+                }
+            }
+        }
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                sX[p0 + i][c] = f32_to_bf16(qv[i] * F[i]);
+                sY[p0 + i][c] = f32_to_bf16(kv[i] * F[i]);
+            }
+        }
+        __syncthreads();
+        if (hl >= 16) {
+            if (w >= NB) {
+#pragma unroll
+                for (int m = 0; m < MOFF; ++m) {
+                    const int idx = (w - NB) + OW * m;
+                    if (idx < NOFF) {
+                        int ti, tj;
+                        off_tile(idx, ti, tj);
+                        if (off_tile_level(ti, tj) == hl) {
+                            accP[m] = mma_kc<DK>(accP[m], &sX[ti * 16][0], PA, &sY[tj * 16][0], PA);
+                            accA[m] = mma_kc<DK>(accA[m], &sY[ti * 16][0], PA, &sY[tj * 16][0], PA);
+                        }
+                    }
+                }
+            }
+        } else if (w < NB) {
+            const f32x4 tp = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sY[w * 16][0], PA);
+            const f32x4 ta = mma_kc<DK>(zero4(), &sY[w * 16][0], PA, &sY[w * 16][0], PA);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (in_level(4 * lq + r, lr, hl)) {
+                    dP[r] += tp[r];
+                    dA[r] += ta[r];
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- scores out: Ps (bf16) and, for training, Ps^T; A (x beta) to LDS
+    bf16* Psc = Psb + (size_t)ch * C * C;
+    bf16* PsTc = PsTb + (size_t)ch * C * C;
+    auto put_ps = [&](int i0, int j, const float (&pv)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Psc[(i0 + r) * C + j] = f32_to_bf16(pv[r]);
+        if (bwdt) *reinterpret_cast<uint2*>(&PsTc[j * C + i0]) = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+    };
+    if (w >= NB) {
+#pragma unroll
+        for (int m = 0; m < MOFF; ++m) {
+            const int idx = (w - NB) + OW * m;
+            if (idx < NOFF) {
+                int ti, tj;
+                off_tile(idx, ti, tj);
+                float pv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                    pv[r] = scale * accP[m][r];
+                    sA[i][j] = sbeta[i] * accA[m][r];
+                }
+                put_ps(ti * 16 + 4 * lq, tj * 16 + lr, pv);
+            }
+        }
+    } else {
+        const int t = w;
+        float pv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = t * 16 + 4 * lq + r, j = t * 16 + lr;
+            pv[r] = i >= j ? scale * dP[r] : 0.f;
+            sA[i][j] = i > j ? sbeta[i] * dA[r] : 0.f;
+        }
+        put_ps(t * 16 + 4 * lq, t * 16 + lr, pv);
+    }
+    for (int idx = tid; idx < C * C; idx += NTHR_P) {
+        const int i = idx / C, j = idx % C;
+        if (i / 16 < j / 16) {
+            Psc[idx] = f32_to_bf16(0.f);
+            if (bwdt) PsTc[j * C + i] = f32_to_bf16(0.f);
+            sA[i][j] = 0.f;
+        }
+    }
+
+    // ---- Gamma, Kh factor, gam: Qg, Kh outputs and X_K^T = (beta K o Gamma)^T
+    if (cp) {
+        float pre = 1.f, suf = 1.f;
+        for (int pp = 0; pp < part; ++pp) pre *= stot[pp][c];
+        for (int pp = part + 1; pp < NPART; ++pp) suf *= stot[pp][c];
+        float qg[RPP], kh[RPP], xk[RPP];
+        float Gm = pre;
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            Gm *= a[i];
+            qg[i] = scale * qv[i] * Gm;
+            xk[i] = sbeta[p0 + i] * kv[i] * Gm;
+        }
+        if (part == NPART - 1) gamo[(size_t)ch * DK + c] = Gm;
+        float kap = suf;
+#pragma unroll
+        for (int i = RPP - 1; i >= 0; --i) {
+            kh[i] = kv[i] * kap;
+            kap *= a[i];
+        }
+        bf16* Qgc = Qgb + (size_t)ch * C * DK;
+        bf16* QgTc = QgTb + (size_t)ch * C * DK;
+        bf16* KhTc = KhTb + (size_t)ch * C * DK;
+        bf16* Khc = Khb + (size_t)ch * C * DK;
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) Qgc[(p0 + i) * DK + c] = f32_to_bf16(qg[i]);
+#pragma unroll
+        for (int i = 0; i < RPP; i += 4) {
+            *reinterpret_cast<uint2*>(&KhTc[c * C + p0 + i]) = pack4_bf16(kh[i], kh[i + 1], kh[i + 2], kh[i + 3]);
+            *reinterpret_cast<uint2*>(&sXT[c][p0 + i]) = pack4_bf16(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
+        }
+        if (bwdt) {
+#pragma unroll
+            for (int i = 0; i < RPP; i += 4)
+                *reinterpret_cast<uint2*>(&QgTc[c * C + p0 + i]) = pack4_bf16(qg[i], qg[i + 1], qg[i + 2], qg[i + 3]);
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) Khc[(p0 + i) * DK + c] = f32_to_bf16(kh[i]);
+        }
+    }
+    for (int idx = tid; idx < C * PC; idx += NTHR_P) (&sT[0][0])[idx] = 0.f;
+    __syncthreads();
+
+    // ---- WY solve: 16x16 diagonal blocks of (I + A)^-1 by forward substitution
+    if (w == 0) {
+        const int bb = lq, j = lr;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float sacc = (i == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) sacc -= sA[bb * 16 + i][bb * 16 + m] * x[m];
+            x[i] = sacc;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sT[bb * 16 + i][bb * 16 + j] = x[i];
+    }
+    __syncthreads();
+    // merge neighbouring diagonal blocks: T21 = -T22 (A21 T11)
+#pragma unroll
+    for (int sz = 16; 2 * sz <= C; sz *= 2) {
+        const int tps = (sz / 16) * (sz / 16);
+        const int ntile = (C / (2 * sz)) * tps;
+        for (int idx = w; idx < ntile; idx += NW) {
+            const int pi = idx / tps, ti = (idx % tps) / (sz / 16), tj = idx % (sz / 16);
+            const int b0 = pi * 2 * sz;
+            f32x4 y = mma16<MT_F32>(zero4(), &sA[b0 + sz + 16 * ti][b0], PC, 1, &sT[b0][b0 + 16 * tj], PC, 1, sz);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sYt[b0 + sz + 16 * ti + 4 * lq + r][b0 + 16 * tj + lr] = y[r];
+        }
+        __syncthreads();
+        for (int idx = w; idx < ntile; idx += NW) {
+            const int pi = idx / tps, ti = (idx % tps) / (sz / 16), tj = idx % (sz / 16);
+            const int b0 = pi * 2 * sz;
+            f32x4 t21 = mma16<MT_F32>(zero4(), &sT[b0 + sz + 16 * ti][b0 + sz], PC, 1, &sYt[b0 + sz][b0 + 16 * tj], PC, 1, sz);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sT[b0 + sz + 16 * ti + 4 * lq + r][b0 + 16 * tj + lr] = -t21[r];
+        }
+        __syncthreads();
+    }
+    // T out (fp32, training) and its bf16 copy (over sA, no longer needed)
+    for (int idx = tid; idx < C * C; idx += NTHR_P) {
+        const int i = idx / C, j = idx % C;
+        const float tv = sT[i][j];
+        if (bwdt) Tmo[(size_t)ch * C * C + idx] = tv;
+        sTb[i][j] = f32_to_bf16(tv);
+    }
+    __syncthreads();
+    // ---- W = T X_K (bf16 out, and W^T for training)
+    constexpr int TW = NB * (DK / 16);
+    for (int idx = w; idx < TW; idx += NW) {
+        const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+        const int K = ((16 * (ti + 1) + 31) / 32) * 32;
+        const f32x4 acc = mma_kc_dyn(zero4(), &sTb[ti * 16][0], PT, &sXT[tj * 16][0], PT, K);
+        bf16* Wc = Wb + (size_t)ch * C * DK;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Wc[(ti * 16 + 4 * lq + r) * DK + tj * 16 + lr] = f32_to_bf16(acc[r]);
+        if (bwdt)
+            *reinterpret_cast<uint2*>(&WTb[(size_t)ch * C * DK + (tj * 16 + lr) * C + ti * 16 + 4 * lq]) =
+                pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();
+    // ---- X_V^T = (beta V)^T, then U = T X_V (fp32 out)
+    if (cp) {
+        float xv[RPP];
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            const int r = p0 + i;
+            xv[i] = r < nvalid ? sbeta[r] * to_f32(v[tok0 * DV + r * rsK + c]) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < RPP; i += 4)
+            *reinterpret_cast<uint2*>(&sXT[c][p0 + i]) = pack4_bf16(xv[i], xv[i + 1], xv[i + 2], xv[i + 3]);
+    }
+    __syncthreads();
+    for (int idx = w; idx < TW; idx += NW) {
+        const int ti = idx / (DV / 16), tj = idx % (DV / 16);
+        const int K = ((16 * (ti + 1) + 31) / 32) * 32;
+        const f32x4 acc = mma_kc_dyn(zero4(), &sTb[ti * 16][0], PT, &sXT[tj * 16][0], PT, K);
+        float* Uc = Uo + (size_t)ch * C * DV;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Uc[(ti * 16 + 4 * lq + r) * DV + tj * 16 + lr] = acc[r];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // scan
 // ---------------------------------------------------------------------------
@@ -729,6 +1071,24 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
     float* gam = (float*)(ws + p.o_gam);
     float* Tm = want_T ? (float*)(ws + p.o_Tm) : nullptr;
     dim3 grid((unsigned)p.n_ch), block(NTHR);
+    if constexpr (bf16_tables<TIn, C, DK>()) {
+        const size_t n = p.n_ch;
+        bf16* Wb = (bf16*)W;
+        bf16* Qb = (bf16*)Qg;
+        bf16* Kb = (bf16*)Kh;
+        bf16* Pb = (bf16*)Ps;
+        if (p.decay == GDN_DECAY_PER_CHANNEL)
+            GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep2_kernel<C, DK, DV, true>), grid,
+                       dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g, beta,
+                       p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, U, Qb, Qb + n * C * DK, Kb,
+                       Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm);
+        else
+            GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep2_kernel<C, DK, DV, false>), grid,
+                       dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g, beta,
+                       p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, U, Qb, Qb + n * C * DK, Kb,
+                       Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm);
+        return GDN_OK;
+    }
     if (p.decay == GDN_DECAY_PER_CHANNEL)
         GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep_kernel<TIn, C, DK, DV, true, MT>), grid, block, st,
                            (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
