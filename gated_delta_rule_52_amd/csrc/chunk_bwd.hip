@@ -706,10 +706,10 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         __syncthreads();
     }
 
-    // outputs
-    float* dQp = dQgo + (size_t)ch * C * DK;
-    float* dWp = dWgo + (size_t)ch * C * DK;
-    float* dKp = dKho + (size_t)ch * C * DK;
+    // outputs (bf16: the consumer reads them as gradients of bf16-rounded products)
+    bf16* dQp = reinterpret_cast<bf16*>(dQgo) + (size_t)ch * C * DK;
+    bf16* dWp = reinterpret_cast<bf16*>(dWgo) + (size_t)ch * C * DK;
+    bf16* dKp = reinterpret_cast<bf16*>(dKho) + (size_t)ch * C * DK;
 #pragma unroll
     for (int m = 0; m < M3; ++m) {
         const int idx = w + NW * m;
@@ -718,14 +718,14 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                dQp[i * DK + j] = aQ[m][r];
-                dWp[i * DK + j] = -aW[m][r];
-                dKp[i * DK + j] = aK[m][r];
+                dQp[i * DK + j] = f32_to_bf16(aQ[m][r]);
+                dWp[i * DK + j] = f32_to_bf16(-aW[m][r]);
+                dKp[i * DK + j] = f32_to_bf16(aK[m][r]);
             }
         }
     }
-    float* dPp = dPso + (size_t)ch * C * C;
-    float* dTp = dT1o + (size_t)ch * C * C;
+    bf16* dPp = reinterpret_cast<bf16*>(dPso) + (size_t)ch * C * C;
+    bf16* dTp = reinterpret_cast<bf16*>(dT1o) + (size_t)ch * C * C;
 #pragma unroll
     for (int m = 0; m < M2; ++m) {
         const int idx = w + NW * m;
@@ -734,8 +734,8 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                dPp[i * C + j] = aP[m][r];
-                dTp[i * C + j] = aT[m][r];
+                dPp[i * C + j] = f32_to_bf16(aP[m][r]);
+                dTp[i * C + j] = f32_to_bf16(aT[m][r]);
             }
         }
     }
@@ -805,6 +805,15 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
     const size_t tok0 = ((size_t)b * T + t0) * H + h;
     const size_t rsK = (size_t)H * DK;
 
+    // intermediate gradients from bchunk1: bf16 with bf16 tables, else fp32
+    constexpr bool BT = bf16_tables<TIn, C, DK>();
+    using IT = typename std::conditional<BT, bf16, float>::type;
+    const IT* dQgI = reinterpret_cast<const IT*>(dQgi);
+    const IT* dWgI = reinterpret_cast<const IT*>(dWgi);
+    const IT* dKhI = reinterpret_cast<const IT*>(dKhi);
+    const IT* dPsI = reinterpret_cast<const IT*>(dPsi);
+    const IT* dT1I = reinterpret_cast<const IT*>(dT1i);
+
     // column threads: channel c, rows [p0, p0 + RPP)
     const bool cp = tid < NPART * DK;
     const int c = tid % DK, part = cp ? tid / DK : 0, p0 = part * RPP;
@@ -812,10 +821,10 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
     {
         const float* Tp = Tmi + (size_t)ch * C * C;
         for (int idx = tid; idx < C * C; idx += NTHR2) sT[idx / C][idx % C] = Tp[idx];
-        const float* dWp = dWgi + (size_t)ch * C * DK;
+        const IT* dWp = dWgI + (size_t)ch * C * DK;
         for (int idx = tid; idx < C * DK / 4; idx += NTHR2) {
             const int r = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
-            st4(&sY[r][c4], load4<float>(dWp + r * DK + c4));
+            st4(&sY[r][c4], load4<IT>(dWp + r * DK + c4));
         }
         for (int r = tid; r < C; r += NTHR2) sbeta[r] = r < nvalid ? beta[tok0 + (size_t)r * H] : 0.f;
     }
@@ -845,8 +854,8 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
 
     // ---- Gamma, Kh factor, X_K; contributions of dQg, dKh, dgam
     if (cp) {
-        const float* dQp = dQgi + (size_t)ch * C * DK;
-        const float* dKp = dKhi + (size_t)ch * C * DK;
+        const IT* dQp = dQgI + (size_t)ch * C * DK;
+        const IT* dKp = dKhI + (size_t)ch * C * DK;
         float pre = 1.f, suf = 1.f;
         for (int pp = 0; pp < part; ++pp) pre *= stot[pp][c];
         for (int pp = part + 1; pp < NPART; ++pp) suf *= stot[pp][c];
@@ -860,7 +869,7 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
 #pragma unroll
         for (int i = RPP - 1; i >= 0; --i) {
             const int r = p0 + i;
-            const float dqg = dQp[r * DK + c], dkh = dKp[r * DK + c];
+            const float dqg = to_f32(dQp[r * DK + c]), dkh = to_f32(dKp[r * DK + c]);
             dq[i] += scale * Gm[i] * dqg;
             dG[i] += scale * qv[i] * Gm[i] * dqg;
             const float khv = kv[i] * kap;
@@ -888,12 +897,12 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
 #pragma unroll
             for (int r = 0; r < 4; ++r) sZ[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = acc[r];
         }
-        const float* dT1p = dT1i + (size_t)ch * C * C;
+        const IT* dT1p = dT1I + (size_t)ch * C * C;
         for (int idx = w; idx < NB * NB; idx += NW) {
             const int ti = idx / NB, tj = idx % NB;
             f32x4 acc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = dT1p[(ti * 16 + acc_row(r)) * C + tj * 16 + acc_col()];
+            for (int r = 0; r < 4; ++r) acc[r] = to_f32(dT1p[(ti * 16 + acc_row(r)) * C + tj * 16 + acc_col()]);
             acc = mma16k<MT_F32, DK>(acc, &sY[ti * 16][0], PD, 1, &sX[tj * 16][0], 1, PD);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sdA[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = acc[r];
@@ -932,7 +941,7 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
     }
     __syncthreads();
     {
-        const float* dPp = dPsi + (size_t)ch * C * C;
+        const IT* dPp = dPsI + (size_t)ch * C * C;
 #pragma unroll
         for (int m = 0; m < (NB * NB + NW - 1) / NW; ++m) {
             const int idx = w + NW * m;
@@ -942,7 +951,7 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
                 for (int r = 0; r < 4; ++r) {
                     const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
                     sdA[i][j] = i > j ? -dAt[m][r] : 0.f;
-                    sdP[i][j] = i >= j ? scale * dPp[i * C + j] : 0.f;
+                    sdP[i][j] = i >= j ? scale * to_f32(dPp[i * C + j]) : 0.f;
                 }
             }
         }
