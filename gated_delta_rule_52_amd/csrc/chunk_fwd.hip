@@ -373,7 +373,7 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
 constexpr int NTHR_P = 512;
 
 template <int C, int DK, int DV, bool PCH>
-__global__ void __launch_bounds__(NTHR_P)
+__global__ void __launch_bounds__(NTHR_P, 4)
 prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
              const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int NC,
              float scale, bf16* __restrict__ Wb, bf16* __restrict__ WTb, float* __restrict__ Uo,
