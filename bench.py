@@ -32,53 +32,129 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# MI355X published peaks
+# MI355X published peaks (dense)
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
-# contraction dtype of each kernel's dominant matrix products
-KERNEL_MFMA = {"prep": "bf16", "prep_T": "bf16", "scan": "f32", "scan_save": "f32",
-               "scan_train": "f32", "bscan": "f32", "bchunk1": "f32", "bchunk2": "bf16"}
 # TPU v6e, Sept-2026 prototype, B=8 T=4096 H=6 d=128 BF16 fwd+bwd: 22.44 ms
 # (Marin note, "Single-device benchmark") -> B*T / 22.44 ms
 PAGES_FWDBWD_TOKENS_S = 8 * 4096 / 22.44e-3
+# kernel launch name -> the source file that defines it (for the counter digest)
+KERNEL_SOURCE = {"prep": "chunk_fwd.hip", "prep_T": "chunk_fwd.hip", "scan": "chunk_fwd.hip",
+                 "scan_save": "chunk_fwd.hip", "scan_train": "chunk_fwd.hip",
+                 "bscan": "chunk_bwd.hip", "bchunk1": "chunk_bwd.hip", "bchunk2": "chunk_bwd.hip",
+                 "decode": "decode.hip"}
+CSRC = os.path.join(ROOT, "gated_delta_rule_52_amd", "csrc")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_traffic_fwdbwd_b8_t4096_h6_d128_bf16.md")
 
 
-def kernel_work(name, B, T, H, C, DK, DV, in_bytes):
-    """Algorithmic (flops, bytes) of one launch: the contractions the kernel
-    must perform and the HBM bytes it must move in this design (each input
-    read once, each output written once)."""
+def kernel_source_digest(name):
+    """sha256 over the file that defines a kernel and every shared header: HBM
+    counters taken on another digest describe different code."""
+    import hashlib
+    h = hashlib.sha256()
+    files = [KERNEL_SOURCE[name]] + sorted(f for f in os.listdir(CSRC) if f.endswith(".h"))
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per launch of `name` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's reading), or None
+    when there is none or the kernel's sources changed since it was taken."""
+    try:
+        with open(COUNTERS_MD) as fh:
+            text = fh.read()
+        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        ent = blob["kernels"][name]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+    if ent.get("source_sha256") != kernel_source_digest(name):
+        return None
+    return ent["traffic_bytes"]
+
+
+def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True):
+    """Algorithmic work of one launch of a chunked kernel: HBM bytes (each
+    input read once, each output written once, in this design's data layout)
+    and the matrix-product flops it must do, split by the operand type of its
+    matrix-core instructions.  Counts are per chunk-head, times the launch's
+    B*H*ceil(T/C) chunk-heads.  Returns (bytes, {"f32": flops, "bf16": flops})."""
     NC = (T + C - 1) // C
     n = B * H * NC
     f4 = 4
-    tri = C * (C + 1) // 2
-    backward = name in ("prep_T", "scan_save")
+    bt = in_bytes == 2 and C == 64 and DK >= 64  # bf16 chunk tables and intermediates
+    tb = 2 if bt else 4                          # bytes per table element
+    ib = in_bytes
+    cd, cv, cc, kv = C * DK, C * DV, C * C, DK * DV
+    tri = C * (C + 1) // 2                       # lower triangle incl. diagonal
+    gb = cd * f4 if per_channel else C * f4      # log-decay bytes per chunk
+    mt = "bf16" if in_bytes == 2 else "f32"      # operand type of the big products
+    fl = {"f32": 0.0, "bf16": 0.0}
     if name in ("prep", "prep_T"):
-        fl = 2 * C * C * DK + 2 * tri * (DK + DV)
-        by = (2 * C * DK + C * DV) * in_bytes + C * DK * f4 + C * f4 \
-            + (3 * C * DK + C * DV + C * C + DK) * f4 + (C * C * f4 if backward else 0)
+        by = (2 * cd + cv) * ib + gb + C * f4                      # q k v, g, beta
+        by += 3 * cd * tb + cc * tb + cv * f4 + DK * f4            # W Qg Kh^T Ps, U, gam
+        if name == "prep_T":
+            by += (3 * cd + cc) * (tb if bt else 0) + cc * f4      # transposed tables, T
+        fl[mt] += 2 * (2 * tri * DK) + 2 * tri * (DK + DV)         # P, A; W = T X_K, U = T X_V
+        fl["f32"] += 2 * C ** 3 / 3                                # (I + A)^-1
     elif name in ("scan", "scan_save", "scan_train"):
-        if name == "scan_save":  # state-saving pass: D and the state update only
-            fl = 4 * C * DK * DV
-            by = (2 * C * DK + C * DV + DK) * f4 + DK * DV * f4
+        by = 3 * cd * tb + cc * tb + cv * f4 + DK * f4             # W Qg Kh Ps, U, gam
+        if name == "scan_save":                                    # deltas and states only
+            by -= cd * tb + cc * tb
+            by += kv * f4
+            fl[mt] += 4 * C * DK * DV
         else:
-            fl = 6 * C * DK * DV + 2 * tri * DV
-            by = (3 * C * DK + C * DV + C * C + DK) * f4 + C * DV * in_bytes
-            if name == "scan_train":  # also writes the chunk-start states
-                by += DK * DV * f4
+            by += cv * ib                                          # o
+            if name == "scan_train":
+                by += kv * f4 + (cv * 2 if bt else 0)              # chunk-start states, D
+            fl[mt] += 6 * C * DK * DV + 2 * tri * DV
     elif name == "bscan":
-        fl = 6 * C * DK * DV + 2 * tri * DV
-        by = (3 * C * DK + C * C + DK) * f4 + C * DV * in_bytes + (DK * DV + C * DV) * f4
+        by = cc * tb + 3 * cd * tb + DK * f4 + cv * ib             # Ps^T Kh Qg^T W^T, gam, dO
+        by += kv * f4 + cv * f4                                    # dS (chunk ends), dD
+        fl[mt] += 6 * C * DK * DV + 2 * tri * DV
     elif name == "bchunk1":
-        fl = 2 * C * DK * DV + 2 * tri * DV + 6 * C * DK * DV + 4 * C * C * DV
-        by = (2 * C * DK + C * DV * 2 + C * C + 2 * DK * DV) * f4 + 3 * C * DV * in_bytes \
-            + (3 * C * DK + 2 * C * C + DK + C) * f4
+        it = 2 if bt else 4
+        by = 2 * cv * ib + C * f4 + cc * f4 + 2 * kv * f4 + cv * f4   # v dO, beta, T, S, dS, dD
+        by += cv * 2 if bt else (cd + cv) * f4                        # D saved | W, U to recompute it
+        by += cv * ib + 3 * cd * it + 2 * cc * it + DK * f4 + C * f4  # dv, dQg dW dKh, dPs dT1, dgam, dbeta
+        fl[mt] += 6 * C * DK * DV + 2 * tri * DV + 2 * tri * DV       # dQg dW dKh, dPs, dT (lower)
+        fl["f32"] += 2 * tri * DV                                      # dU = T^T dD
+        if not bt:
+            fl[mt] += 2 * C * DK * DV                                  # D = U - W S
     elif name == "bchunk2":
-        fl = 2 * tri * DK + 2 * C * C * DK + 4 * C * C * C + 4 * (C * (C - 1) // 2) * 2 * DK
-        by = 2 * C * DK * in_bytes + C * DK * f4 + C * f4 + (C * C + 3 * C * DK + 2 * C * C + DK + C) * f4 \
-            + 2 * C * DK * in_bytes + C * DK * f4 + C * f4
+        it = 2 if bt else 4
+        by = 2 * cd * ib + gb + C * f4 + cc * f4                      # q k, g, beta, T
+        by += 3 * cd * it + 2 * cc * it + DK * f4 + C * f4            # dQg dW dKh, dPs dT1, dgam, dbeta part
+        by += 2 * cd * ib + gb + C * f4                               # dq dk, dg, dbeta
+        fl["f32"] += 2 * (2 * tri * DK) + 2 * (2 * C ** 3 / 3)        # T^T dW, dT += dW X_K^T; dA
+        fl[mt] += 2 * (2 * tri * DK) + 2 * (2 * tri * DK)             # score gradients of P and A
     else:
         return None
-    return fl * n, by * n
+    return by * n, {k_: v_ * n for k_, v_ in fl.items()}
+
+
+def roofline(name, dur_s, B, T, H, C, D, in_bytes):
+    """Lower bound on one launch's duration from its algorithmic work at the
+    published peaks; the largest term names the bound."""
+    by, fl = kernel_work(name, B, T, H, C, D, D, in_bytes)
+    terms = {"hbm": by / (PEAK_HBM_GBS * 1e9)}
+    for mt, f in fl.items():
+        if f:
+            terms["mfma_" + mt] = f / (PEAK_TFLOPS[mt] * 1e12)
+    bound = max(terms, key=terms.get)
+    if bound == "hbm":
+        r = {"bound": "hbm", "achieved": by / dur_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        mt = bound[5:]
+        r = {"bound": "mfma", "achieved": fl[mt] / dur_s / 1e12, "peak": PEAK_TFLOPS[mt],
+             "unit": "TFLOP/s", "mfma_dtype": mt}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["floor_us"] = {k_: v_ * 1e6 for k_, v_ in terms.items()}
+    r["algorithmic_bytes_per_launch"] = by
+    r["algorithmic_flops_per_launch"] = fl
+    return r
 
 
 def main():
@@ -90,6 +166,8 @@ def main():
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-fwd", action="store_true",
+                    help="skip the forward-only measurement (profiling runs: one launch name per kernel)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -196,34 +274,31 @@ def main():
 
     # dominant kernel by device time per step, and its roofline
     dom = max(per, key=lambda n: per[n][0] * per[n][1])
-    fl, by = kernel_work(dom, B, T, H, C, D, D, in_bytes)
-    dur = per[dom][0] * 1e-3
-    mt = KERNEL_MFMA.get(dom) if dt == "bf16" else "f32"
-    ridge = PEAK_TFLOPS[mt] * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if fl / by >= ridge:
-        roof = {"bound": "mfma", "achieved": fl / dur / 1e12, "peak": PEAK_TFLOPS[mt],
-                "unit": "TFLOP/s", "mfma_dtype": mt}
-    else:
-        roof = {"bound": "hbm", "achieved": by / dur / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof = roofline(dom, per[dom][0] * 1e-3, B, T, H, C, D, in_bytes)
+    roof["traffic"] = measured_traffic(dom) if dt == "bf16" and B == 8 else None
     roof["kernel"] = dom
-    roof["avg_launch_us"] = dur * 1e6
-    roof["algorithmic_flops_per_launch"] = fl
-    roof["algorithmic_bytes_per_launch"] = by
+    roof["avg_launch_us"] = per[dom][0] * 1e3
+    roof["launches_timed"] = per[dom][1]
+    others = {n: {"us": ms * 1e3, "bound": r["bound"], "frac": r["frac"]}
+              for n, (ms, _) in per.items()
+              for r in [roofline(n, ms * 1e-3, B, T, H, C, D, in_bytes)]}
+    log(f"[bench] dominant {dom}: {roof['achieved']:.0f} {roof['unit']} of {roof['peak']:.0f} "
+        f"({100 * roof['frac']:.1f}%, {roof['bound']}-bound); traffic {roof['traffic']}")
 
     # ---- forward only
-    for _ in range(3):
-        fwd()
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(args.steps):
-        fwd()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms_fwd = ev0.elapsed_time(ev1) / args.steps
-    fwd_tps = B * T / (ms_fwd * 1e-3)
-    log(f"[bench] fwd {ms_fwd:.3f} ms ({fwd_tps / 1e6:.2f} M tokens/s)")
+    ms_fwd = fwd_tps = None
+    if not args.no_fwd:
+        for _ in range(3):
+            fwd()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            fwd()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_fwd = ev0.elapsed_time(ev1) / args.steps
+        fwd_tps = B * T / (ms_fwd * 1e-3)
+        log(f"[bench] fwd {ms_fwd:.3f} ms ({fwd_tps / 1e6:.2f} M tokens/s)")
 
     # ---- decode: B=256 H=16 128x128 fp32 state, one token per step
     decode = None
@@ -259,11 +334,12 @@ def main():
                   "algorithmic_bytes_per_step": dbytes}
         log(f"[bench] decode {kdec * 1e3:.1f} us/step, {decode['achieved_GBs']:.0f} GB/s")
 
-    # ---- CPU oracle on this host: a bounded sample of the same workload
+    # ---- CPU oracle on this host: the same workload (every (batch, head)
+    # sequence unless that would take much longer than ~30 s of wall time)
     cpu = None
     if not args.no_cpu:
         nthr = oracle.max_threads()
-        nh = min(B * H, max(2, nthr))
+        nh = min(B * H, 8 * nthr)
         pairs = [(i // H, i % H) for i in range(nh)]
         s = {n: np.stack([inp[n][b, :, h] for b, h in pairs], axis=1)[None]
              for n in ("q", "k", "v", "g", "beta", "dO")}
@@ -276,8 +352,8 @@ def main():
         oracle.backward(s["q"], s["k"], s["v"], s["g"], s["beta"], scale, s["dO"], dhT=s["dhT"])
         tc = time.perf_counter() - t0
         cpu = {"value": (nh / H) * T / tc, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
-               "sample": f"{nh} of {B * H} (batch, head) sequences, T={T}, fwd+bwd, float64 "
-                         f"token-serial; tokens counted as heads/H*T; {tc:.1f} s"}
+               "sample": f"{nh} of {B * H} (batch, head) sequences of T={T}, fwd+bwd, float64 "
+                         f"token-serial, inputs widened from {dt}; tokens = heads/H*T; {tc:.1f} s"}
         log(f"[bench] cpu oracle {cpu['value']:.0f} tokens/s in {tc:.1f} s")
 
     if args.calibrate_copy:
@@ -312,7 +388,7 @@ def main():
         "fwd_ms": ms_fwd,
         "parity_ok": parity_ok,
         "parity_max_rel_err": par,
-        "kernels_avg_us": {n: v_[0] * 1e3 for n, v_ in per.items()},
+        "kernels": others,
         "roofline": roof,
         "decode": decode,
         "cpu_baseline": cpu,
