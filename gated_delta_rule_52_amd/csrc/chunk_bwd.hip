@@ -818,32 +818,52 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
     const bool cp = tid < NPART * DK;
     const int c = tid % DK, part = cp ? tid / DK : 0, p0 = part * RPP;
 
-    {
-        const float* Tp = Tmi + (size_t)ch * C * C;
-        for (int idx = tid; idx < C * C; idx += NTHR2) sT[idx / C][idx % C] = Tp[idx];
-        const IT* dWp = dWgI + (size_t)ch * C * DK;
-        for (int idx = tid; idx < C * DK / 4; idx += NTHR2) {
-            const int r = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
-            st4(&sY[r][c4], load4<IT>(dWp + r * DK + c4));
-        }
-        for (int r = tid; r < C; r += NTHR2) sbeta[r] = r < nvalid ? beta[tok0 + (size_t)r * H] : 0.f;
-    }
     float a[RPP], qv[RPP], kv[RPP], Gm[RPP];
     float dq[RPP], dk[RPP], dG[RPP], dbr[RPP];
 #pragma unroll
     for (int i = 0; i < RPP; ++i) {
         const int r = p0 + i;
-        float gv = 0.f, qx = 0.f, kx = 0.f;
-        if (cp && r < nvalid) {
-            gv = PCH ? g[(tok0 + (size_t)r * H) * DK + c] : g[tok0 + (size_t)r * H];
-            qx = to_f32(q[tok0 * DK + r * rsK + c]);
-            kx = to_f32(k[tok0 * DK + r * rsK + c]);
-        }
-        a[i] = expf(gv);
-        qv[i] = qx;
-        kv[i] = kx;
+        // rows past the end read the last valid row (every load unconditional,
+        // so all rows are in flight at once) and are then replaced by g = q = k = 0
+        const int rr = min(r, nvalid - 1);
+        const float gx = PCH ? g[(tok0 + (size_t)rr * H) * DK + c] : g[tok0 + (size_t)rr * H];
+        const float qx = to_f32(q[tok0 * DK + rr * rsK + c]);
+        const float kx = to_f32(k[tok0 * DK + rr * rsK + c]);
+        const bool ok = cp && r < nvalid;
+        a[i] = ok ? gx : 0.f;  // log-decay for now; exponentiated once the other loads are out
+        qv[i] = ok ? qx : 0.f;
+        kv[i] = ok ? kx : 0.f;
         dq[i] = dk[i] = dG[i] = dbr[i] = 0.f;
     }
+    {
+        // T, dW and beta: every load issued before the first LDS write
+        constexpr int NT1 = (C * C + NTHR2 - 1) / NTHR2, NW4 = (C * DK / 4 + NTHR2 - 1) / NTHR2;
+        const float* Tp = Tmi + (size_t)ch * C * C;
+        const IT* dWp = dWgI + (size_t)ch * C * DK;
+        float tv[NT1];
+        float4 wv[NW4];
+#pragma unroll
+        for (int u = 0; u < NT1; ++u) tv[u] = Tp[min(tid + NTHR2 * u, C * C - 1)];
+#pragma unroll
+        for (int u = 0; u < NW4; ++u) {
+            const int idx = min(tid + NTHR2 * u, C * DK / 4 - 1);
+            wv[u] = load4<IT>(dWp + (idx / (DK / 4)) * DK + (idx % (DK / 4)) * 4);
+        }
+        const float bv = beta[tok0 + (size_t)min(tid % C, nvalid - 1) * H];
+#pragma unroll
+        for (int u = 0; u < NT1; ++u) {
+            const int idx = tid + NTHR2 * u;
+            if (idx < C * C) sT[idx / C][idx % C] = tv[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NW4; ++u) {
+            const int idx = tid + NTHR2 * u;
+            if (idx < C * DK / 4) st4(&sY[idx / (DK / 4)][(idx % (DK / 4)) * 4], wv[u]);
+        }
+        if (tid < C) sbeta[tid] = tid < nvalid ? bv : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) a[i] = expf(a[i]);
     {
         float pt = 1.f;
 #pragma unroll
@@ -888,6 +908,25 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
         dG[RPP - 1] += s + Gm[RPP - 1] * dgmi[(size_t)ch * DK + c];
     }
 
+    // this wave's 16x16 tiles of the C x C gradients dT(U) and dPs, fetched
+    // before the products below so that their latency overlaps them
+    constexpr int MA = (NB * NB + NW - 1) / NW;
+    float pT1[MA][4], pPs[MA][4];
+    {
+        const IT* dT1p = dT1I + (size_t)ch * C * C;
+        const IT* dPp = dPsI + (size_t)ch * C * C;
+#pragma unroll
+        for (int m = 0; m < MA; ++m) {
+            const int idx = w + NW * m;
+            const int ti = (idx % (NB * NB)) / NB, tj = idx % NB;  // in range for every wave
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = (ti * 16 + acc_row(r)) * C + tj * 16 + acc_col();
+                pT1[m][r] = to_f32(dT1p[e]);
+                pPs[m][r] = to_f32(dPp[e]);
+            }
+        }
+    }
     // ---- dX_K = T^T dW (-> sZ);  dT = dT(U) + dW X_K^T (-> sdA)
     {
         constexpr int T3 = NB * (DK / 16);
@@ -897,15 +936,18 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
 #pragma unroll
             for (int r = 0; r < 4; ++r) sZ[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = acc[r];
         }
-        const IT* dT1p = dT1I + (size_t)ch * C * C;
-        for (int idx = w; idx < NB * NB; idx += NW) {
-            const int ti = idx / NB, tj = idx % NB;
-            f32x4 acc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = to_f32(dT1p[(ti * 16 + acc_row(r)) * C + tj * 16 + acc_col()]);
-            acc = mma16k<MT_F32, DK>(acc, &sY[ti * 16][0], PD, 1, &sX[tj * 16][0], 1, PD);
+        for (int m = 0; m < MA; ++m) {
+            const int idx = w + NW * m;
+            if (idx < NB * NB) {
+                const int ti = idx / NB, tj = idx % NB;
+                f32x4 acc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sdA[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = acc[r];
+                for (int r = 0; r < 4; ++r) acc[r] = pT1[m][r];
+                acc = mma16k<MT_F32, DK>(acc, &sY[ti * 16][0], PD, 1, &sX[tj * 16][0], 1, PD);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sdA[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = acc[r];
+            }
         }
     }
     __syncthreads();
@@ -930,9 +972,9 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
     }
     __syncthreads();
     // dA = -T^T Y, strictly lower
-    f32x4 dAt[(NB * NB + NW - 1) / NW];
+    f32x4 dAt[MA];
 #pragma unroll
-    for (int m = 0; m < (NB * NB + NW - 1) / NW; ++m) {
+    for (int m = 0; m < MA; ++m) {
         const int idx = w + NW * m;
         if (idx < NB * NB) {
             const int ti = idx / NB, tj = idx % NB;
@@ -941,9 +983,8 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
     }
     __syncthreads();
     {
-        const IT* dPp = dPsI + (size_t)ch * C * C;
 #pragma unroll
-        for (int m = 0; m < (NB * NB + NW - 1) / NW; ++m) {
+        for (int m = 0; m < MA; ++m) {
             const int idx = w + NW * m;
             if (idx < NB * NB) {
                 const int ti = idx / NB, tj = idx % NB;
@@ -951,7 +992,7 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
                 for (int r = 0; r < 4; ++r) {
                     const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
                     sdA[i][j] = i > j ? -dAt[m][r] : 0.f;
-                    sdP[i][j] = i >= j ? scale * to_f32(dPp[i * C + j]) : 0.f;
+                    sdP[i][j] = i >= j ? scale * pPs[m][r] : 0.f;
                 }
             }
         }

@@ -413,15 +413,16 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
     for (int i = 0; i < RPP; ++i) {
         const int r = p0 + i;
-        float gv = 0.f, qx = 0.f, kx = 0.f;
-        if (cp && r < nvalid) {
-            gv = PCH ? g[(tok0 + (size_t)r * H) * DK + c] : g[tok0 + (size_t)r * H];
-            qx = to_f32(q[tok0 * DK + r * rsK + c]);
-            kx = to_f32(k[tok0 * DK + r * rsK + c]);
-        }
-        a[i] = expf(gv);
-        qv[i] = qx;
-        kv[i] = kx;
+        // rows past the end read the last valid row (every load unconditional,
+        // so all rows are in flight at once) and are then replaced by g = q = k = 0
+        const int rr = min(r, nvalid - 1);
+        const float gx = PCH ? g[(tok0 + (size_t)rr * H) * DK + c] : g[tok0 + (size_t)rr * H];
+        const float qx = to_f32(q[tok0 * DK + rr * rsK + c]);
+        const float kx = to_f32(k[tok0 * DK + rr * rsK + c]);
+        const bool ok = cp && r < nvalid;
+        a[i] = expf(ok ? gx : 0.f);
+        qv[i] = ok ? qx : 0.f;
+        kv[i] = ok ? kx : 0.f;
     }
     for (int r = tid; r < C; r += NTHR_P) sbeta[r] = r < nvalid ? beta[tok0 + (size_t)r * H] : 0.f;
     {
@@ -686,7 +687,8 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
         for (int i = 0; i < RPP; ++i) {
             const int r = p0 + i;
-            xv[i] = r < nvalid ? sbeta[r] * to_f32(v[tok0 * DV + r * rsK + c]) : 0.f;
+            const float vx = to_f32(v[tok0 * DV + min(r, nvalid - 1) * rsK + c]);
+            xv[i] = r < nvalid ? sbeta[r] * vx : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < RPP; i += 4)

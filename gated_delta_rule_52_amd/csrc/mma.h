@@ -36,8 +36,10 @@ __device__ __forceinline__ f32x4 mma16(f32x4 acc, const float* __restrict__ A, i
             for (int e = 0; e < 8; ++e) {
                 const int kx = k + 8 * kk + e;
                 const bool in = kx < K;
-                a[e] = (__bf16)(in ? A[r * ars + kx * acs] : 0.f);
-                b[e] = (__bf16)(in ? B[kx * brs + r * bcs] : 0.f);
+                const int kc = in ? kx : K - 1;  // in-range index: the loads stay unconditional
+                const float va = A[r * ars + kc * acs], vb = B[kc * brs + r * bcs];
+                a[e] = (__bf16)(in ? va : 0.f);
+                b[e] = (__bf16)(in ? vb : 0.f);
             }
             acc = mfma_bf16_16x16x32(a, b, acc);
         }
@@ -64,8 +66,10 @@ __device__ __forceinline__ f32x4 mma16k(f32x4 acc, const float* __restrict__ A, 
             for (int e = 0; e < 8; ++e) {
                 const int kx = k + 8 * kk + e;
                 const bool in = (K % 32 == 0) || kx < K;
-                a[e] = (__bf16)(in ? A[r * ars + kx * acs] : 0.f);
-                b[e] = (__bf16)(in ? B[kx * brs + r * bcs] : 0.f);
+                const int kc = in ? kx : K - 1;
+                const float va = A[r * ars + kc * acs], vb = B[kc * brs + r * bcs];
+                a[e] = (__bf16)(in ? va : 0.f);
+                b[e] = (__bf16)(in ? vb : 0.f);
             }
             acc = mfma_bf16_16x16x32(a, b, acc);
         }
@@ -79,7 +83,8 @@ namespace gdn {
 
 // Functor form: fa(i, k) and fb(k, j) return the operand elements (masks,
 // per-row scalings, transposes are expressed inside them).  K is the
-// contraction length; elements with k >= K are never requested.
+// contraction length; fa / fb are called with k < K only (the bf16 paths
+// clamp the index of the padding lanes to K - 1 and zero the value).
 template <int MT, int K, typename FA, typename FB>
 __device__ __forceinline__ f32x4 mma16f(f32x4 acc, FA fa, FB fb)
 {
@@ -96,8 +101,10 @@ __device__ __forceinline__ f32x4 mma16f(f32x4 acc, FA fa, FB fb)
             for (int e = 0; e < 8; ++e) {
                 const int kx = k + 8 * kk + e;
                 const bool in = (K % 32 == 0) || kx < K;
-                a[e] = (__bf16)(in ? fa(r, kx) : 0.f);
-                b[e] = (__bf16)(in ? fb(kx, r) : 0.f);
+                const int kc = in ? kx : K - 1;
+                const float va = fa(r, kc), vb = fb(kc, r);
+                a[e] = (__bf16)(in ? va : 0.f);
+                b[e] = (__bf16)(in ? vb : 0.f);
             }
             acc = mfma_bf16_16x16x32(a, b, acc);
         }
@@ -120,8 +127,10 @@ __device__ __forceinline__ f32x4 mma16fd(f32x4 acc, FA fa, FB fb, int K)
             for (int e = 0; e < 8; ++e) {
                 const int kx = k + 8 * kk + e;
                 const bool in = kx < K;
-                a[e] = (__bf16)(in ? fa(r, kx) : 0.f);
-                b[e] = (__bf16)(in ? fb(kx, r) : 0.f);
+                const int kc = in ? kx : K - 1;
+                const float va = fa(r, kc), vb = fb(kc, r);
+                a[e] = (__bf16)(in ? va : 0.f);
+                b[e] = (__bf16)(in ? vb : 0.f);
             }
             acc = mfma_bf16_16x16x32(a, b, acc);
         }
