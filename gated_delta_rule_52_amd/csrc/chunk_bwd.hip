@@ -1109,29 +1109,38 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
     // this thread owns channel c of all 16 rows of its tile, so every pair's
     // contribution to its rows is local (no reduction across lanes); the decay
     // between the two tokens is the running product E_ij = prod_{s=j+1..i} a_s.
+    // Per row i the sums over j are kept in two scalars and per column j one
+    // sum over i; the decay gradient follows from them, since d/dG_i of
+    // E_ij = +E_ij and d/dG_j = -E_ij: dG_i += q_i rq_i + beta_i k_i ra_i and
+    // dG_j -= k_j cs_j (rq, ra: row sums of dP E k and dA E k; cs: column sums
+    // of dP E q + dA E beta k).
     if (cp) {
-        float bt[RPP];
+        float cs[RPP];
 #pragma unroll
-        for (int i = 0; i < RPP; ++i) bt[i] = sbeta[p0 + i];
+        for (int j = 0; j < RPP; ++j) cs[j] = 0.f;
 #pragma unroll
         for (int i = 1; i < RPP; ++i) {
-            float E = 1.f;
+            const int r = p0 + i;
+            const float bi = sbeta[r], bki = bi * kv[i];
+            float rq = 0.f, ra = 0.f, E = 1.f;
 #pragma unroll
             for (int j = i - 1; j >= 0; --j) {
                 E *= a[j + 1];
-                const float tP = sdP[p0 + i][p0 + j] * E;
-                const float tA = sdA[p0 + i][p0 + j] * E;
-                dq[i] += tP * kv[j];
-                dk[j] += tP * qv[i];
-                const float btA = bt[i] * tA;
-                dk[i] += btA * kv[j];
-                dk[j] += btA * kv[i];
-                const float y = tA * kv[i] * kv[j];
-                const float x = tP * qv[i] * kv[j] + bt[i] * y;
-                dG[i] += x;
-                dG[j] -= x;
-                dbr[i] += y;
+                const float tP = sdP[r][p0 + j] * E;
+                const float tA = sdA[r][p0 + j] * E;
+                rq += tP * kv[j];
+                ra += tA * kv[j];
+                cs[j] += tP * qv[i] + tA * bki;
             }
+            dq[i] += rq;
+            dk[i] += bi * ra;
+            dG[i] += qv[i] * rq + bki * ra;
+            dbr[i] += kv[i] * ra;
+        }
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            dk[j] += cs[j];
+            dG[j] -= kv[j] * cs[j];
         }
     }
 
