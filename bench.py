@@ -117,18 +117,22 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True):
     elif name == "bchunk1":
         it = 2 if bt else 4
         by = 2 * cv * ib + C * f4 + cc * f4 + 2 * kv * f4 + cv * f4   # v dO, beta, T, S, dS, dD
-        by += cv * 2 if bt else (cd + cv) * f4                        # D saved | W, U to recompute it
-        by += cv * ib + 3 * cd * it + 2 * cc * it + DK * f4 + C * f4  # dv, dQg dW dKh, dPs dT1, dgam, dbeta
-        fl[mt] += 6 * C * DK * DV + 2 * tri * DV + 2 * tri * DV       # dQg dW dKh, dPs, dT (lower)
-        fl["f32"] += 2 * tri * DV                                      # dU = T^T dD
+        by += (cv * 2 + cv * f4) if bt else (cd + cv) * f4            # D and U | W, U (D = U - W S)
+        by += cv * ib + 3 * cd * it + 2 * cc * it + DK * f4 + C * f4  # dv, dQg dW dKh, dPs G1|dT1, dgam, dbeta
+        fl[mt] += 6 * C * DK * DV + 2 * tri * DV + 2 * C * C * DV     # dQg dW dKh, dPs, dX_V U^T | dD X_V^T
+        fl["f32"] += 2 * tri * DV                                      # dX_V = T^T dD
         if not bt:
             fl[mt] += 2 * C * DK * DV                                  # D = U - W S
     elif name == "bchunk2":
         it = 2 if bt else 4
         by = 2 * cd * ib + gb + C * f4 + cc * f4                      # q k, g, beta, T
-        by += 3 * cd * it + 2 * cc * it + DK * f4 + C * f4            # dQg dW dKh, dPs dT1, dgam, dbeta part
+        by += 3 * cd * it + 2 * cc * it + DK * f4 + C * f4            # dQg dW dKh, dPs G1|dT1, dgam, dbeta part
+        by += cd * tb if bt else 0                                    # W (bf16 table)
         by += 2 * cd * ib + gb + C * f4                               # dq dk, dg, dbeta
-        fl["f32"] += 2 * (2 * tri * DK) + 2 * (2 * C ** 3 / 3)        # T^T dW, dT += dW X_K^T; dA
+        if bt:  # dX_K = T^T dW, dA = -(G1 + dX_K W^T) strictly lower, on bf16 MFMA
+            fl["bf16"] += 2 * tri * DK + 2 * (C * (C - 1) // 2) * DK
+        else:   # dX_K = T^T dW, dT = dT1 + dW X_K^T, dA = -T^T dT T^T
+            fl["f32"] += 2 * (2 * tri * DK) + 2 * (2 * C ** 3 / 3)
         fl[mt] += 2 * (2 * tri * DK) + 2 * (2 * tri * DK)             # score gradients of P and A
     else:
         return None

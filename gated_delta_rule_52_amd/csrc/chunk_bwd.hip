@@ -540,7 +540,8 @@ template <int C, int DK, int DV>
 __global__ void __launch_bounds__(NTHR_C)
 bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const bf16* __restrict__ dO, const bf16* __restrict__ Dst,
-                const float* __restrict__ Tmi, const float* __restrict__ Sst,
+                const float* __restrict__ Ui, const float* __restrict__ Tmi,
+                const float* __restrict__ Sst,
                 const float* __restrict__ dSt, const float* __restrict__ dDt,
                 bf16* __restrict__ dvo, float* __restrict__ dQgo, float* __restrict__ dWgo,
                 float* __restrict__ dKho, float* __restrict__ dPso, float* __restrict__ dT1o,
@@ -556,7 +557,8 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     constexpr int NB8 = C * BW / 8;                  // uint4 words of a bf16 [C][BW] tile
     constexpr int ND4 = C * BW / 4;                  // float4 words of dD
     static_assert(NB8 <= NTHR_C / 2 && ND4 <= NTHR_C, "tile split assumes C*BW <= 2048");
-    __shared__ __align__(16) bf16 sS[DK][PB], sdS[DK][PB], sdO[C][PB], sD[C][PB], sdD[C][PB], sXV[C][PB];
+    __shared__ __align__(16) bf16 sS[DK][PB], sdS[DK][PB], sdO[C][PB], sD[C][PB], sdD[C][PB];
+    __shared__ __align__(16) bf16 sU[C][PB], sdX[C][PB];  // U and dX_V tiles, for G1 = dX_V U^T
     __shared__ __align__(16) float sT[C][PC], sdDf[C][PF], sv[C][PF];
     __shared__ float sbeta[C], sred[NW][C];
 
@@ -580,8 +582,9 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     const float* dSp = dSt + (size_t)ch * DK * DV;
     const float* dDp = dDt + (size_t)ch * C * DV;
     const bf16* Dp = Dst + (size_t)ch * C * DV;
+    const float* Up = Ui + (size_t)ch * C * DV;
 
-    float4 pS[QS], pdS[QS], pdD;
+    float4 pS[QS], pdS[QS], pdD, pU;
     uint4 pa, pb;  // threads < 256: D and v; threads >= 256: dO
     auto fetch = [&](int v0) {
 #pragma unroll
@@ -596,6 +599,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         if (tid < ND4) {
             const int r = tid / (BW / 4), j4 = (tid % (BW / 4)) * 4;
             pdD = load4<float>(dDp + r * DV + v0 + j4);
+            pU = load4<float>(Up + r * DV + v0 + j4);
         }
         pa = pb = uint4{0u, 0u, 0u, 0u};
         if (tid < NB8) {
@@ -627,6 +631,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             const int r = tid / (BW / 4), j4 = (tid % (BW / 4)) * 4;
             st4(&sdDf[r][j4], pdD);
             *reinterpret_cast<uint2*>(&sdD[r][j4]) = pack4_bf16(pdD.x, pdD.y, pdD.z, pdD.w);
+            *reinterpret_cast<uint2*>(&sU[r][j4]) = pack4_bf16(pU.x, pU.y, pU.z, pU.w);
         }
         if (tid < NB8) {
             const int r = tid / (BW / 8), j0 = (tid % (BW / 8)) * 8;
@@ -640,9 +645,6 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             }
             st4(&sv[r][j0], float4{vv[0], vv[1], vv[2], vv[3]});
             st4(&sv[r][j0 + 4], float4{vv[4], vv[5], vv[6], vv[7]});
-            const float bt = sbeta[r];
-            *reinterpret_cast<uint2*>(&sXV[r][j0]) = pack4_bf16(bt * vv[0], bt * vv[1], bt * vv[2], bt * vv[3]);
-            *reinterpret_cast<uint2*>(&sXV[r][j0 + 4]) = pack4_bf16(bt * vv[4], bt * vv[5], bt * vv[6], bt * vv[7]);
         } else if (tid >= NTHR_C / 2 && tid - NTHR_C / 2 < NB8) {
             const int e = tid - NTHR_C / 2;
             const int r = e / (BW / 8), j0 = (e % (BW / 8)) * 8;
@@ -679,6 +681,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                     const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
                     if (i < nvalid) dvo[(tok0 + (size_t)i * H) * DV + v0 + j] = f32_to_bf16(sbeta[i] * dx[r]);
                     dbr[m][r] += dx[r] * sv[i][j];
+                    sdX[i][j] = f32_to_bf16(dx[r]);
                 }
             }
         }
@@ -698,7 +701,15 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             if (idx < T2) {
                 const int ti = idx / NB, tj = idx % NB;
                 aP[m] = mma_kc<BW>(aP[m], &sdO[ti * 16][0], PB, &sD[tj * 16][0], PB);
-                aT[m] = mma_kc<BW>(aT[m], &sdD[ti * 16][0], PB, &sXV[tj * 16][0], PB);
+            }
+        }
+        __syncthreads();  // the dX_V tile is complete
+#pragma unroll
+        for (int m = 0; m < M2; ++m) {
+            const int idx = w + NW * m;
+            if (idx < T2) {
+                const int ti = idx / NB, tj = idx % NB;
+                aT[m] = mma_kc<BW>(aT[m], &sdX[ti * 16][0], PB, &sU[tj * 16][0], PB);
             }
         }
         __syncthreads();
@@ -771,6 +782,208 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         float sb = 0.f;
         for (int ww = 0; ww < NW; ++ww) sb += sred[ww][r];
         dbpo[(size_t)ch * C + r] = sb;
+    }
+}
+
+// Score gradients, decay chain rule and outputs, shared by both bchunk2
+// kernels: on entry sdP holds scale * dPs (lower incl. diagonal), sdA holds dA
+// (strictly lower), and each column thread (channel c, rows p0 .. p0+RPP-1)
+// holds a = exp(g), q, k and its partial dq, dk, dG (= dL/dG before the
+// reverse cumsum) and dbeta terms; sX, sY, sZ are free [C][PD] fp32 tables.
+template <typename TIn, int C, int DK, bool PCH, int MT, int NTH, int RPP, int PC, int PD>
+__device__ __forceinline__ void score_grad_tail(
+    float (&a)[RPP], float (&qv)[RPP], float (&kv)[RPP], float (&dq)[RPP], float (&dk)[RPP],
+    float (&dG)[RPP], float (&dbr)[RPP], float (*sdP)[PC], float (*sdA)[PC], float (*sX)[PD],
+    float (*sY)[PD], float (*sZ)[PD], const float* sbeta, float (*stot)[DK], float (*sext)[DK],
+    bool cp, int c, int part, int p0, int nvalid, int ch, size_t tok0, size_t rsK, int H,
+    const float* __restrict__ dbpi, TIn* __restrict__ dqo, TIn* __restrict__ dko,
+    float* __restrict__ dgo, float* __restrict__ dbo)
+{
+    constexpr int NB = C / 16, NW = NTH / 64, NPART = C / RPP;
+    const int tid = threadIdx.x, w = tid >> 6;
+    // diagonal scores (E = 1): P_ii = q_i . k_i
+    if (cp) {
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            const int r = p0 + i;
+            const float dp = sdP[r][r];
+            dq[i] += dp * kv[i];
+            dk[i] += dp * qv[i];
+        }
+    }
+
+    // ---- score gradients of pairs that span two 16-token tiles: the levels
+    // h = C/2 .. 16 of the block-boundary split, as MFMA products of the score
+    // gradients and factored rows (each own row is in the query half or the key
+    // half of its 2h-block at every such level)
+#pragma unroll
+    for (int lvl = 0; (C >> (lvl + 1)) >= 16; ++lvl) {
+        const int hl = C >> (lvl + 1);
+        float F[RPP];
+        // level-hl factor of each own row: query rows prod_{s=m+1..r} a_s,
+        // key rows prod_{s=r+1..m} a_s, m the last token of the earlier half
+        const int base = (p0 / (2 * hl)) * (2 * hl);
+        const bool qs = p0 >= base + hl;
+        if (qs) {
+            float pre = 1.f;
+            for (int pp = (base + hl) / RPP; pp < part; ++pp) pre *= stot[pp][c];
+            float Fr = pre;
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                Fr *= a[i];
+                F[i] = Fr;
+            }
+        } else {
+            float suf = 1.f;
+            for (int pp = part + 1; pp < (base + hl) / RPP; ++pp) suf *= stot[pp][c];
+            float Fr = suf;
+#pragma unroll
+            for (int i = RPP - 1; i >= 0; --i) {
+                F[i] = Fr;
+                Fr *= a[i];
+            }
+        }
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                sX[p0 + i][c] = qv[i] * F[i];  // QK
+                sY[p0 + i][c] = kv[i] * F[i];  // KK
+            }
+        }
+        __syncthreads();
+        // R1 = dP_h KK (query rows) + dP_h^T QK (key rows);
+        // R2 = dA_h KK (query rows) + (diag(beta) dA_h)^T KK (key rows)
+        constexpr int T3 = NB * (DK / 16), M3 = (T3 + NW - 1) / NW;
+        f32x4 r2[M3];
+#pragma unroll
+        for (int m = 0; m < M3; ++m) {
+            const int idx = w + NW * m;
+            if (idx >= T3) continue;
+            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+            f32x4 r1 = zero4();
+            r2[m] = zero4();
+            const int tbase = (ti * 16 / (2 * hl)) * (2 * hl);
+            if (ti * 16 >= tbase + hl) {
+                r1 = mma16fd<MT>(r1, [&](int i, int kx) { return sdP[ti * 16 + i][tbase + kx]; },
+                                 [&](int kx, int j) { return sY[tbase + kx][tj * 16 + j]; }, hl);
+                r2[m] = mma16fd<MT>(r2[m], [&](int i, int kx) { return sdA[ti * 16 + i][tbase + kx]; },
+                                    [&](int kx, int j) { return sY[tbase + kx][tj * 16 + j]; }, hl);
+            } else {
+                const int qb = tbase + hl;
+                r1 = mma16fd<MT>(r1, [&](int i, int kx) { return sdP[qb + kx][ti * 16 + i]; },
+                                 [&](int kx, int j) { return sX[qb + kx][tj * 16 + j]; }, hl);
+                r2[m] = mma16fd<MT>(r2[m], [&](int i, int kx) { return sbeta[qb + kx] * sdA[qb + kx][ti * 16 + i]; },
+                                    [&](int kx, int j) { return sY[qb + kx][tj * 16 + j]; }, hl);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sZ[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = r1[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < M3; ++m) {
+            const int idx = w + NW * m;
+            if (idx >= T3) continue;
+            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sX[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = r2[m][r];
+        }
+        __syncthreads();
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                const int r = p0 + i;
+                const float R1 = sZ[r][c], R2 = sX[r][c];
+                if (qs) {
+                    const float bt = sbeta[r];
+                    dq[i] += F[i] * R1;
+                    dk[i] += bt * F[i] * R2;
+                    dG[i] += qv[i] * F[i] * R1 + bt * kv[i] * F[i] * R2;
+                    dbr[i] += kv[i] * F[i] * R2;
+                } else {
+                    dk[i] += F[i] * (R1 + R2);
+                    dG[i] -= kv[i] * F[i] * (R1 + R2);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- score gradients of pairs inside one 16-token tile (j < i), on VALU:
+    // this thread owns channel c of all 16 rows of its tile, so every pair's
+    // contribution to its rows is local (no reduction across lanes); the decay
+    // between the two tokens is the running product E_ij = prod_{s=j+1..i} a_s.
+    // Per row i the sums over j are kept in two scalars and per column j one
+    // sum over i; the decay gradient follows from them, since d/dG_i of
+    // E_ij = +E_ij and d/dG_j = -E_ij: dG_i += q_i rq_i + beta_i k_i ra_i and
+    // dG_j -= k_j cs_j (rq, ra: row sums of dP E k and dA E k; cs: column sums
+    // of dP E q + dA E beta k).
+    if (cp) {
+        float cs[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) cs[j] = 0.f;
+#pragma unroll
+        for (int i = 1; i < RPP; ++i) {
+            const int r = p0 + i;
+            const float bi = sbeta[r], bki = bi * kv[i];
+            float rq = 0.f, ra = 0.f, E = 1.f;
+#pragma unroll
+            for (int j = i - 1; j >= 0; --j) {
+                E *= a[j + 1];
+                const float tP = sdP[r][p0 + j] * E;
+                const float tA = sdA[r][p0 + j] * E;
+                rq += tP * kv[j];
+                ra += tA * kv[j];
+                cs[j] += tP * qv[i] + tA * bki;
+            }
+            dq[i] += rq;
+            dk[i] += bi * ra;
+            dG[i] += qv[i] * rq + bki * ra;
+            dbr[i] += kv[i] * ra;
+        }
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            dk[j] += cs[j];
+            dG[j] -= kv[j] * cs[j];
+        }
+    }
+
+    // ---- dg = reverse cumulative sum of dG over the chunk; dbeta; dq, dk out
+    if (cp) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = RPP - 1; i >= 0; --i) {
+            s += dG[i];
+            dG[i] = s;
+        }
+        sext[part][c] = s;
+    }
+    __syncthreads();
+    if (cp) {
+        float add = 0.f;
+        for (int pp = part + 1; pp < NPART; ++pp) add += sext[pp][c];
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            const int r = p0 + i;
+            dG[i] += add;
+            sZ[r][c] = dG[i];
+            sX[r][c] = dbr[i];
+            if (r < nvalid) {
+                dqo[tok0 * DK + r * rsK + c] = from_f32<TIn>(dq[i]);
+                dko[tok0 * DK + r * rsK + c] = from_f32<TIn>(dk[i]);
+                if (PCH) dgo[(tok0 + (size_t)r * H) * DK + c] = dG[i];
+            }
+        }
+    }
+    __syncthreads();
+    for (int r = tid; r < nvalid; r += NTH) {
+        float sb = dbpi[(size_t)ch * C + r];
+        for (int cc = 0; cc < DK; ++cc) sb += sX[r][cc];
+        dbo[tok0 + (size_t)r * H] = sb;
+        if (!PCH) {
+            float sg = 0.f;
+            for (int cc = 0; cc < DK; ++cc) sg += sZ[r][cc];
+            dgo[tok0 + (size_t)r * H] = sg;
+        }
     }
 }
 
@@ -998,190 +1211,247 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
         }
     }
     __syncthreads();
-    // diagonal scores (E = 1): P_ii = q_i . k_i
-    if (cp) {
+    score_grad_tail<TIn, C, DK, PCH, MT, NTHR2, RPP, PC, PD>(
+        a, qv, kv, dq, dk, dG, dbr, sdP, sdA, sX, sY, sZ, sbeta, stot, sext, cp, c, part, p0, nvalid,
+        ch, tok0, rsK, H, dbpi, dqo, dko, dgo, dbo);
+}
+
+// ---------------------------------------------------------------------------
+// bchunk2b: bf16 inputs at chunk 64.  The WY adjoint uses
+//   -T^T (dU X_V^T + dW X_K^T) T^T = -(dX_V U^T + dX_K W^T),
+// with dX_V = T^T dU and U = T X_V (likewise for K), so with G1 = dX_V U^T
+// from bchunk1b only dX_K = T^T dW and dX_K W^T remain, both on bf16 MFMA:
+// T and dX_K enter as bf16 hi + lo pairs (16 significant bits), dW and W
+// are bf16 tables already.
+// ---------------------------------------------------------------------------
+constexpr int NTHR_E = 512;  // 8 waves
+
+template <int C, int DK, bool PCH>
+__global__ void __launch_bounds__(NTHR_E)
+bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+                const float* __restrict__ beta, const float* __restrict__ Tmi,
+                const bf16* __restrict__ Wbi, const bf16* __restrict__ dQgi,
+                const bf16* __restrict__ dWgi, const bf16* __restrict__ dKhi,
+                const bf16* __restrict__ dPsi, const bf16* __restrict__ G1i,
+                const float* __restrict__ dgmi, const float* __restrict__ dbpi,
+                bf16* __restrict__ dqo, bf16* __restrict__ dko, float* __restrict__ dgo,
+                float* __restrict__ dbo, int T, int H, int NC, float scale)
+{
+    static_assert(C == 64, "bchunk2b: chunk 64");
+    constexpr int NB = C / 16, NW = NTHR_E / 64;
+    constexpr int RPP = 16, NPART = C / RPP;
+    constexpr int PC = C + 4, PD = DK + 4;  // fp32 pitches
+    constexpr int PT = C + 8, PK = DK + 8;  // bf16 pitches: 16-byte rows, banks spread
+    // WY-adjoint tables (bf16) and, afterwards, the level tables (fp32) share sbuf
+    constexpr int OT_L = C * PT * 2, OT_DW = 2 * C * PT * 2, OT_W = OT_DW + DK * PT * 2;
+    constexpr int OT_XH = OT_W + C * PK * 2, OT_XL = OT_XH + C * PK * 2, PH1 = OT_XL + C * PK * 2;
+    constexpr int PH2 = 3 * C * PD * 4;
+    __shared__ __align__(16) char sbuf[cmax(PH1, PH2)];
+    __shared__ __align__(16) float sdP[C][PC], sdA[C][PC];
+    __shared__ float sbeta[C], stot[NPART][DK], sext[NPART][DK];
+    bf16 (*sTh)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);         // T^T, high part
+    bf16 (*sTl)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + OT_L);  // T^T, low part
+    bf16 (*sdWT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + OT_DW);
+    bf16 (*sW)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + OT_W);
+    bf16 (*sXh)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + OT_XH);  // dX_K, high part
+    bf16 (*sXl)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + OT_XL);  // dX_K, low part
+    float (*sX)[PD] = reinterpret_cast<float (*)[PD]>(sbuf);
+    float (*sY)[PD] = reinterpret_cast<float (*)[PD]>(sbuf + C * PD * 4);
+    float (*sZ)[PD] = reinterpret_cast<float (*)[PD]>(sbuf + 2 * C * PD * 4);
+
+    const int ch = blockIdx.x;
+    const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
+    const int t0 = n * C;
+    const int nvalid = min(C, T - t0);
+    const int tid = threadIdx.x, w = tid >> 6;
+    const size_t tok0 = ((size_t)b * T + t0) * H + h;
+    const size_t rsK = (size_t)H * DK;
+
+    // column threads: channel c, rows [p0, p0 + RPP)
+    const bool cp = tid < NPART * DK;
+    const int c = tid % DK, part = cp ? tid / DK : 0, p0 = part * RPP;
+
+    float a[RPP], qv[RPP], kv[RPP], Gm[RPP];
+    float dq[RPP], dk[RPP], dG[RPP], dbr[RPP];
 #pragma unroll
-        for (int i = 0; i < RPP; ++i) {
-            const int r = p0 + i;
-            const float dp = sdP[r][r];
-            dq[i] += dp * kv[i];
-            dk[i] += dp * qv[i];
+    for (int i = 0; i < RPP; ++i) {
+        const int r = p0 + i;
+        // rows past the end read the last valid row (all loads unconditional)
+        // and are then replaced by g = q = k = 0
+        const int rr = min(r, nvalid - 1);
+        const float gx = PCH ? g[(tok0 + (size_t)rr * H) * DK + c] : g[tok0 + (size_t)rr * H];
+        const float qx = to_f32(q[tok0 * DK + rr * rsK + c]);
+        const float kx = to_f32(k[tok0 * DK + rr * rsK + c]);
+        const bool ok = cp && r < nvalid;
+        a[i] = ok ? gx : 0.f;  // log-decay until the other loads are out
+        qv[i] = ok ? qx : 0.f;
+        kv[i] = ok ? kx : 0.f;
+        dq[i] = dk[i] = dG[i] = dbr[i] = 0.f;
+    }
+    // this wave's 16x16 tiles of G1 and dPs (C x C), kept in registers
+    constexpr int MA = (NB * NB + NW - 1) / NW;
+    float pG[MA][4], pP[MA][4];
+    {
+        const bf16* Gp = G1i + (size_t)ch * C * C;
+        const bf16* Pp = dPsi + (size_t)ch * C * C;
+#pragma unroll
+        for (int m = 0; m < MA; ++m) {
+            const int idx = (w + NW * m) % (NB * NB);
+            const int ti = idx / NB, tj = idx % NB;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = (ti * 16 + acc_row(r)) * C + tj * 16 + acc_col();
+                pG[m][r] = to_f32(Gp[e]);
+                pP[m][r] = to_f32(Pp[e]);
+            }
         }
     }
-
-    // ---- score gradients of pairs that span two 16-token tiles: the levels
-    // h = C/2 .. 16 of the block-boundary split, as MFMA products of the score
-    // gradients and factored rows (each own row is in the query half or the key
-    // half of its 2h-block at every such level)
+    {
+        // T (fp32), dW and W (bf16), beta: all loads issued before the LDS writes
+        constexpr int NT4 = (C * C / 4 + NTHR_E - 1) / NTHR_E;
+        constexpr int NK8 = (C * DK / 8 + NTHR_E - 1) / NTHR_E;
+        const float* Tp = Tmi + (size_t)ch * C * C;
+        const bf16* dWp = dWgi + (size_t)ch * C * DK;
+        const bf16* Wp = Wbi + (size_t)ch * C * DK;
+        float4 tv[NT4];
+        uint4 dwv[NK8], wv[NK8];
 #pragma unroll
-    for (int lvl = 0; (C >> (lvl + 1)) >= 16; ++lvl) {
-        const int hl = C >> (lvl + 1);
-        float F[RPP];
-        // level-hl factor of each own row: query rows prod_{s=m+1..r} a_s,
-        // key rows prod_{s=r+1..m} a_s, m the last token of the earlier half
-        const int base = (p0 / (2 * hl)) * (2 * hl);
-        const bool qs = p0 >= base + hl;
-        if (qs) {
-            float pre = 1.f;
-            for (int pp = (base + hl) / RPP; pp < part; ++pp) pre *= stot[pp][c];
-            float Fr = pre;
-#pragma unroll
-            for (int i = 0; i < RPP; ++i) {
-                Fr *= a[i];
-                F[i] = Fr;
-            }
-        } else {
-            float suf = 1.f;
-            for (int pp = part + 1; pp < (base + hl) / RPP; ++pp) suf *= stot[pp][c];
-            float Fr = suf;
-#pragma unroll
-            for (int i = RPP - 1; i >= 0; --i) {
-                F[i] = Fr;
-                Fr *= a[i];
-            }
+        for (int u = 0; u < NT4; ++u) {
+            const int idx = min(tid + NTHR_E * u, C * C / 4 - 1);
+            tv[u] = *reinterpret_cast<const float4*>(Tp + 4 * idx);
         }
-        if (cp) {
 #pragma unroll
-            for (int i = 0; i < RPP; ++i) {
-                sX[p0 + i][c] = qv[i] * F[i];  // QK
-                sY[p0 + i][c] = kv[i] * F[i];  // KK
-            }
+        for (int u = 0; u < NK8; ++u) {
+            const int idx = min(tid + NTHR_E * u, C * DK / 8 - 1);
+            dwv[u] = *reinterpret_cast<const uint4*>(dWp + 8 * idx);
+            wv[u] = *reinterpret_cast<const uint4*>(Wp + 8 * idx);
         }
-        __syncthreads();
-        // R1 = dP_h KK (query rows) + dP_h^T QK (key rows);
-        // R2 = dA_h KK (query rows) + (diag(beta) dA_h)^T KK (key rows)
-        constexpr int T3 = NB * (DK / 16), M3 = (T3 + NW - 1) / NW;
-        f32x4 r2[M3];
+        const float bv = beta[tok0 + (size_t)min(tid % C, nvalid - 1) * H];
+        // T^T as high and low bf16 parts: element T[r][j] goes to row j, column r
 #pragma unroll
-        for (int m = 0; m < M3; ++m) {
-            const int idx = w + NW * m;
-            if (idx >= T3) continue;
-            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
-            f32x4 r1 = zero4();
-            r2[m] = zero4();
-            const int tbase = (ti * 16 / (2 * hl)) * (2 * hl);
-            if (ti * 16 >= tbase + hl) {
-                r1 = mma16fd<MT>(r1, [&](int i, int kx) { return sdP[ti * 16 + i][tbase + kx]; },
-                                 [&](int kx, int j) { return sY[tbase + kx][tj * 16 + j]; }, hl);
-                r2[m] = mma16fd<MT>(r2[m], [&](int i, int kx) { return sdA[ti * 16 + i][tbase + kx]; },
-                                    [&](int kx, int j) { return sY[tbase + kx][tj * 16 + j]; }, hl);
-            } else {
-                const int qb = tbase + hl;
-                r1 = mma16fd<MT>(r1, [&](int i, int kx) { return sdP[qb + kx][ti * 16 + i]; },
-                                 [&](int kx, int j) { return sX[qb + kx][tj * 16 + j]; }, hl);
-                r2[m] = mma16fd<MT>(r2[m], [&](int i, int kx) { return sbeta[qb + kx] * sdA[qb + kx][ti * 16 + i]; },
-                                    [&](int kx, int j) { return sY[qb + kx][tj * 16 + j]; }, hl);
-            }
+        for (int u = 0; u < NT4; ++u) {
+            const int idx = tid + NTHR_E * u;
+            if (idx < C * C / 4) {
+                const int r = idx / (C / 4), j0 = (idx % (C / 4)) * 4;
+                const float tt[4] = {tv[u].x, tv[u].y, tv[u].z, tv[u].w};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sZ[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = r1[r];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < M3; ++m) {
-            const int idx = w + NW * m;
-            if (idx >= T3) continue;
-            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sX[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = r2[m][r];
-        }
-        __syncthreads();
-        if (cp) {
-#pragma unroll
-            for (int i = 0; i < RPP; ++i) {
-                const int r = p0 + i;
-                const float R1 = sZ[r][c], R2 = sX[r][c];
-                if (qs) {
-                    const float bt = sbeta[r];
-                    dq[i] += F[i] * R1;
-                    dk[i] += bt * F[i] * R2;
-                    dG[i] += qv[i] * F[i] * R1 + bt * kv[i] * F[i] * R2;
-                    dbr[i] += kv[i] * F[i] * R2;
-                } else {
-                    dk[i] += F[i] * (R1 + R2);
-                    dG[i] -= kv[i] * F[i] * (R1 + R2);
+                for (int e = 0; e < 4; ++e) {
+                    const bf16 hi = f32_to_bf16(tt[e]);
+                    sTh[j0 + e][r] = hi;
+                    sTl[j0 + e][r] = f32_to_bf16(tt[e] - to_f32(hi));
                 }
             }
         }
-        __syncthreads();
-    }
-
-    // ---- score gradients of pairs inside one 16-token tile (j < i), on VALU:
-    // this thread owns channel c of all 16 rows of its tile, so every pair's
-    // contribution to its rows is local (no reduction across lanes); the decay
-    // between the two tokens is the running product E_ij = prod_{s=j+1..i} a_s.
-    // Per row i the sums over j are kept in two scalars and per column j one
-    // sum over i; the decay gradient follows from them, since d/dG_i of
-    // E_ij = +E_ij and d/dG_j = -E_ij: dG_i += q_i rq_i + beta_i k_i ra_i and
-    // dG_j -= k_j cs_j (rq, ra: row sums of dP E k and dA E k; cs: column sums
-    // of dP E q + dA E beta k).
-    if (cp) {
-        float cs[RPP];
+        // dW^T (element dW[r][cc] to row cc, column r) and W as it is
 #pragma unroll
-        for (int j = 0; j < RPP; ++j) cs[j] = 0.f;
+        for (int u = 0; u < NK8; ++u) {
+            const int idx = tid + NTHR_E * u;
+            if (idx < C * DK / 8) {
+                const int r = idx / (DK / 8), c0 = (idx % (DK / 8)) * 8;
+                const uint32_t x[4] = {dwv[u].x, dwv[u].y, dwv[u].z, dwv[u].w};
 #pragma unroll
-        for (int i = 1; i < RPP; ++i) {
-            const int r = p0 + i;
-            const float bi = sbeta[r], bki = bi * kv[i];
-            float rq = 0.f, ra = 0.f, E = 1.f;
-#pragma unroll
-            for (int j = i - 1; j >= 0; --j) {
-                E *= a[j + 1];
-                const float tP = sdP[r][p0 + j] * E;
-                const float tA = sdA[r][p0 + j] * E;
-                rq += tP * kv[j];
-                ra += tA * kv[j];
-                cs[j] += tP * qv[i] + tA * bki;
+                for (int e = 0; e < 4; ++e) {
+                    sdWT[c0 + 2 * e][r].bits = (uint16_t)(x[e] & 0xFFFFu);
+                    sdWT[c0 + 2 * e + 1][r].bits = (uint16_t)(x[e] >> 16);
+                }
+                *reinterpret_cast<uint4*>(&sW[r][c0]) = wv[u];
             }
-            dq[i] += rq;
-            dk[i] += bi * ra;
-            dG[i] += qv[i] * rq + bki * ra;
-            dbr[i] += kv[i] * ra;
         }
-#pragma unroll
-        for (int j = 0; j < RPP; ++j) {
-            dk[j] += cs[j];
-            dG[j] -= kv[j] * cs[j];
-        }
+        if (tid < C) sbeta[tid] = tid < nvalid ? bv : 0.f;
     }
-
-    // ---- dg = reverse cumulative sum of dG over the chunk; dbeta; dq, dk out
-    if (cp) {
-        float s = 0.f;
 #pragma unroll
-        for (int i = RPP - 1; i >= 0; --i) {
-            s += dG[i];
-            dG[i] = s;
-        }
-        sext[part][c] = s;
+    for (int i = 0; i < RPP; ++i) a[i] = expf(a[i]);
+    {
+        float pt = 1.f;
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) pt *= a[i];
+        if (cp) stot[part][c] = pt;
     }
     __syncthreads();
+
+    // ---- Gamma, Kh factor; contributions of dQg, dKh, dgam
     if (cp) {
-        float add = 0.f;
-        for (int pp = part + 1; pp < NPART; ++pp) add += sext[pp][c];
+        const bf16* dQp = dQgi + (size_t)ch * C * DK;
+        const bf16* dKp = dKhi + (size_t)ch * C * DK;
+        float pre = 1.f, suf = 1.f;
+        for (int pp = 0; pp < part; ++pp) pre *= stot[pp][c];
+        for (int pp = part + 1; pp < NPART; ++pp) suf *= stot[pp][c];
+        float Gr = pre;
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            Gr *= a[i];
+            Gm[i] = Gr;
+        }
+        float kap = suf, sumKh = 0.f;
+#pragma unroll
+        for (int i = RPP - 1; i >= 0; --i) {
+            const int r = p0 + i;
+            const float dqg = to_f32(dQp[r * DK + c]), dkh = to_f32(dKp[r * DK + c]);
+            dq[i] += scale * Gm[i] * dqg;
+            dG[i] += scale * qv[i] * Gm[i] * dqg;
+            const float khv = kv[i] * kap;
+            dk[i] += kap * dkh;
+            dG[i] -= khv * dkh;
+            sumKh += khv * dkh;
+            kap *= a[i];
+        }
+        sext[part][c] = sumKh;
+    }
+    // ---- dX_K = T^T dW: (T_hi + T_lo)^T dW on bf16 MFMA; stored as hi + lo
+    {
+        constexpr int T3 = NB * (DK / 16);
+        for (int idx = w; idx < T3; idx += NW) {
+            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+            f32x4 acc = mma_kc<C>(zero4(), &sTh[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
+            acc = mma_kc<C>(acc, &sTl[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
+                const bf16 hi = f32_to_bf16(acc[r]);
+                sXh[i][j] = hi;
+                sXl[i][j] = f32_to_bf16(acc[r] - to_f32(hi));
+            }
+        }
+    }
+    __syncthreads();
+    if (cp && part == NPART - 1) {
+        float sacc = 0.f;
+        for (int pp = 0; pp < NPART; ++pp) sacc += sext[pp][c];
+        dG[RPP - 1] += sacc + Gm[RPP - 1] * dgmi[(size_t)ch * DK + c];
+    }
+    // X_K = diag(beta) K o Gamma: dk += beta Gamma dX_K, dG += X_K o dX_K,
+    // dbeta += <k Gamma, dX_K>
+    if (cp) {
 #pragma unroll
         for (int i = 0; i < RPP; ++i) {
             const int r = p0 + i;
-            dG[i] += add;
-            sZ[r][c] = dG[i];
-            sX[r][c] = dbr[i];
-            if (r < nvalid) {
-                dqo[tok0 * DK + r * rsK + c] = from_f32<TIn>(dq[i]);
-                dko[tok0 * DK + r * rsK + c] = from_f32<TIn>(dk[i]);
-                if (PCH) dgo[(tok0 + (size_t)r * H) * DK + c] = dG[i];
+            const float dx = to_f32(sXh[r][c]) + to_f32(sXl[r][c]);
+            const float kg = kv[i] * Gm[i];
+            dk[i] += sbeta[r] * Gm[i] * dx;
+            dG[i] += sbeta[r] * kg * dx;
+            dbr[i] += kg * dx;
+        }
+    }
+    // ---- dA = -(G1 + dX_K W^T), strictly lower;  dP = scale dPs, lower
+#pragma unroll
+    for (int m = 0; m < MA; ++m) {
+        const int idx = w + NW * m;
+        if (idx < NB * NB) {
+            const int ti = idx / NB, tj = idx % NB;
+            f32x4 acc = mma_kc<DK>(zero4(), &sXh[ti * 16][0], PK, &sW[tj * 16][0], PK);
+            acc = mma_kc<DK>(acc, &sXl[ti * 16][0], PK, &sW[tj * 16][0], PK);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
+                sdA[i][j] = i > j ? -(pG[m][r] + acc[r]) : 0.f;
+                sdP[i][j] = i >= j ? scale * pP[m][r] : 0.f;
             }
         }
     }
     __syncthreads();
-    for (int r = tid; r < nvalid; r += NTHR2) {
-        float sb = dbpi[(size_t)ch * C + r];
-        for (int cc = 0; cc < DK; ++cc) sb += sX[r][cc];
-        dbo[tok0 + (size_t)r * H] = sb;
-        if (!PCH) {
-            float sg = 0.f;
-            for (int cc = 0; cc < DK; ++cc) sg += sZ[r][cc];
-            dgo[tok0 + (size_t)r * H] = sg;
-        }
-    }
+    score_grad_tail<bf16, C, DK, PCH, MT_BF16, NTHR_E, RPP, PC, PD>(
+        a, qv, kv, dq, dk, dG, dbr, sdP, sdA, sX, sY, sZ, sbeta, stot, sext, cp, c, part, p0, nvalid,
+        ch, tok0, rsK, H, dbpi, dqo, dko, dgo, dbo);
 }
 
 // ---------------------------------------------------------------------------
@@ -1220,7 +1490,8 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
     dim3 gch((unsigned)p.n_ch);
     if constexpr (bf16_tables<TIn, C, DK>()) {
         GDN_LAUNCH("bchunk1", (bchunk1b_kernel<C, DK, DV>), gch, dim3(NTHR_C), st, (const bf16*)v,
-                   beta, (const bf16*)dO, (const bf16*)(ws + p.o_Dst), (const float*)(ws + p.o_Tm),
+                   beta, (const bf16*)dO, (const bf16*)(ws + p.o_Dst), (const float*)(ws + p.o_U),
+                   (const float*)(ws + p.o_Tm),
                    (const float*)(ws + p.o_Sst), (const float*)(ws + p.o_dSt),
                    (const float*)(ws + p.o_dDt), (bf16*)dv, (float*)(ws + p.o_dQg),
                    (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh), (float*)(ws + p.o_dPs),
@@ -1236,8 +1507,26 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                        (float*)(ws + p.o_dT1), (float*)(ws + p.o_dgm), (float*)(ws + p.o_dbp), p.T,
                        p.H, p.NC);
     GDN_HIP_CHECK_LAUNCH();
-    const void* args_dummy = nullptr;
-    (void)args_dummy;
+    if constexpr (bf16_tables<TIn, C, DK>()) {
+        // dT1 holds G1 = dX_V U^T here (bchunk1b)
+        if (p.decay == GDN_DECAY_PER_CHANNEL)
+            GDN_LAUNCH("bchunk2", (bchunk2b_kernel<C, DK, true>), gch, dim3(NTHR_E), st,
+                       (const bf16*)q, (const bf16*)k, g, beta, (const float*)(ws + p.o_Tm),
+                       (const bf16*)(ws + p.o_W), (const bf16*)(ws + p.o_dQg),
+                       (const bf16*)(ws + p.o_dWg), (const bf16*)(ws + p.o_dKh),
+                       (const bf16*)(ws + p.o_dPs), (const bf16*)(ws + p.o_dT1),
+                       (const float*)(ws + p.o_dgm), (const float*)(ws + p.o_dbp), (bf16*)dq,
+                       (bf16*)dk, dg, dbeta, p.T, p.H, p.NC, p.scale);
+        else
+            GDN_LAUNCH("bchunk2", (bchunk2b_kernel<C, DK, false>), gch, dim3(NTHR_E), st,
+                       (const bf16*)q, (const bf16*)k, g, beta, (const float*)(ws + p.o_Tm),
+                       (const bf16*)(ws + p.o_W), (const bf16*)(ws + p.o_dQg),
+                       (const bf16*)(ws + p.o_dWg), (const bf16*)(ws + p.o_dKh),
+                       (const bf16*)(ws + p.o_dPs), (const bf16*)(ws + p.o_dT1),
+                       (const float*)(ws + p.o_dgm), (const float*)(ws + p.o_dbp), (bf16*)dq,
+                       (bf16*)dk, dg, dbeta, p.T, p.H, p.NC, p.scale);
+        return GDN_OK;
+    }
     if (p.decay == GDN_DECAY_PER_CHANNEL)
         GDN_LAUNCH("bchunk2", (bchunk2_kernel<TIn, C, DK, DV, true, MT>), gch, dim3(NTHR2), st,
                            (const TIn*)q, (const TIn*)k, g, beta, (const float*)(ws + p.o_Tm),
