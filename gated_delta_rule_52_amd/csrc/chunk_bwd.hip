@@ -1222,7 +1222,9 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
 // with dX_V = T^T dU and U = T X_V (likewise for K), so with G1 = dX_V U^T
 // from bchunk1b only dX_K = T^T dW and dX_K W^T remain, both on bf16 MFMA:
 // T and dX_K enter as bf16 hi + lo pairs (16 significant bits), dW and W
-// are bf16 tables already.
+// are bf16 tables already.  The score gradients dPs (unscaled) and dA are
+// then kept as bf16 tables in both orientations, and the level tables are
+// channel-major, so every MFMA operand is one 16-byte LDS read.
 // ---------------------------------------------------------------------------
 constexpr int NTHR_E = 512;  // 8 waves
 
@@ -1240,14 +1242,17 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     static_assert(C == 64, "bchunk2b: chunk 64");
     constexpr int NB = C / 16, NW = NTHR_E / 64;
     constexpr int RPP = 16, NPART = C / RPP;
-    constexpr int PC = C + 4, PD = DK + 4;  // fp32 pitches
+    constexpr int PD = DK + 4;              // fp32 pitch
     constexpr int PT = C + 8, PK = DK + 8;  // bf16 pitches: 16-byte rows, banks spread
-    // WY-adjoint tables (bf16) and, afterwards, the level tables (fp32) share sbuf
+    // WY-adjoint tables (bf16), later the level tables and results, share sbuf
     constexpr int OT_L = C * PT * 2, OT_DW = 2 * C * PT * 2, OT_W = OT_DW + DK * PT * 2;
     constexpr int OT_XH = OT_W + C * PK * 2, OT_XL = OT_XH + C * PK * 2, PH1 = OT_XL + C * PK * 2;
-    constexpr int PH2 = 3 * C * PD * 4;
+    constexpr int OL_K = DK * PT * 2, OL_R1 = 2 * DK * PT * 2, OL_R2 = OL_R1 + C * PD * 4;
+    constexpr int PH2 = OL_R2 + C * PD * 4;
     __shared__ __align__(16) char sbuf[cmax(PH1, PH2)];
-    __shared__ __align__(16) float sdP[C][PC], sdA[C][PC];
+    // score gradients, bf16: dPs (unscaled, lower incl. diagonal) and dA (strictly
+    // lower) by rows, their transposes, the latter with the beta of the row folded in
+    __shared__ __align__(16) bf16 sP[C][PT], sPT[C][PT], sA[C][PT], sAT[C][PT];
     __shared__ float sbeta[C], stot[NPART][DK], sext[NPART][DK];
     bf16 (*sTh)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);         // T^T, high part
     bf16 (*sTl)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + OT_L);  // T^T, low part
@@ -1255,9 +1260,10 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     bf16 (*sW)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + OT_W);
     bf16 (*sXh)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + OT_XH);  // dX_K, high part
     bf16 (*sXl)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + OT_XL);  // dX_K, low part
-    float (*sX)[PD] = reinterpret_cast<float (*)[PD]>(sbuf);
-    float (*sY)[PD] = reinterpret_cast<float (*)[PD]>(sbuf + C * PD * 4);
-    float (*sZ)[PD] = reinterpret_cast<float (*)[PD]>(sbuf + 2 * C * PD * 4);
+    bf16 (*sQKT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);         // level tables, channel-major
+    bf16 (*sKKT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + OL_K);
+    float (*sR1)[PD] = reinterpret_cast<float (*)[PD]>(sbuf + OL_R1);
+    float (*sR2)[PD] = reinterpret_cast<float (*)[PD]>(sbuf + OL_R2);
 
     const int ch = blockIdx.x;
     const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
@@ -1399,17 +1405,21 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     }
     // ---- dX_K = T^T dW: (T_hi + T_lo)^T dW on bf16 MFMA; stored as hi + lo
     {
-        constexpr int T3 = NB * (DK / 16);
-        for (int idx = w; idx < T3; idx += NW) {
-            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
-            f32x4 acc = mma_kc<C>(zero4(), &sTh[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
-            acc = mma_kc<C>(acc, &sTl[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
+        constexpr int T3 = NB * (DK / 16), M3 = (T3 + NW - 1) / NW;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
-                const bf16 hi = f32_to_bf16(acc[r]);
-                sXh[i][j] = hi;
-                sXl[i][j] = f32_to_bf16(acc[r] - to_f32(hi));
+        for (int m = 0; m < M3; ++m) {
+            const int idx = w + NW * m;
+            if (idx < T3) {
+                const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+                f32x4 acc = mma_kc<C>(zero4(), &sTh[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
+                acc = mma_kc<C>(acc, &sTl[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
+                    const bf16 hi = f32_to_bf16(acc[r]);
+                    sXh[i][j] = hi;
+                    sXl[i][j] = f32_to_bf16(acc[r] - to_f32(hi));
+                }
             }
         }
     }
@@ -1432,7 +1442,8 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             dbr[i] += kg * dx;
         }
     }
-    // ---- dA = -(G1 + dX_K W^T), strictly lower;  dP = scale dPs, lower
+    // ---- dA = -(G1 + dX_K W^T), strictly lower; dPs lower; bf16 tables by
+    // rows and transposed (dA^T with beta_i folded into column i)
 #pragma unroll
     for (int m = 0; m < MA; ++m) {
         const int idx = w + NW * m;
@@ -1440,18 +1451,219 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             const int ti = idx / NB, tj = idx % NB;
             f32x4 acc = mma_kc<DK>(zero4(), &sXh[ti * 16][0], PK, &sW[tj * 16][0], PK);
             acc = mma_kc<DK>(acc, &sXl[ti * 16][0], PK, &sW[tj * 16][0], PK);
+            float av[4], bav[4], pv[4];
+            const int i0 = ti * 16 + acc_row(0), j = tj * 16 + acc_col();
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
-                sdA[i][j] = i > j ? -(pG[m][r] + acc[r]) : 0.f;
-                sdP[i][j] = i >= j ? scale * pP[m][r] : 0.f;
+                const int i = i0 + r;
+                av[r] = i > j ? -(pG[m][r] + acc[r]) : 0.f;
+                bav[r] = sbeta[i] * av[r];
+                pv[r] = i >= j ? pP[m][r] : 0.f;
+                sA[i][j] = f32_to_bf16(av[r]);
+                sP[i][j] = f32_to_bf16(pv[r]);
+            }
+            *reinterpret_cast<uint2*>(&sAT[j][i0]) = pack4_bf16(bav[0], bav[1], bav[2], bav[3]);
+            *reinterpret_cast<uint2*>(&sPT[j][i0]) = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+        }
+    }
+    __syncthreads();
+
+    // ---- diagonal scores (decay 1): P_ii = q_i . k_i
+    if (cp) {
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            const float dp = scale * to_f32(sP[p0 + i][p0 + i]);
+            dq[i] += dp * kv[i];
+            dk[i] += dp * qv[i];
+        }
+    }
+
+    // ---- score gradients of pairs that span two 16-token tiles: levels
+    // h = 32, 16 of the block-boundary split.  Each own row is in the query
+    // half or the key half of its 2h-block; with F its level factor
+    // (query rows prod_{s=m+1..r} a_s, key rows prod_{s=r+1..m} a_s, m the last
+    // token of the earlier half) the tables hold (q o F)^T and (k o F)^T and
+    //   query rows: R1 = dPs KK,      R2 = dA KK
+    //   key rows:   R1 = dPs^T QK,    R2 = (diag(beta) dA)^T KK
+#pragma unroll
+    for (int lvl = 0; lvl < 2; ++lvl) {
+        const int hl = C >> (lvl + 1);
+        float F[RPP];
+        const int base = (p0 / (2 * hl)) * (2 * hl);
+        const bool qs = p0 >= base + hl;
+        if (qs) {
+            float pre = 1.f;
+            for (int pp = (base + hl) / RPP; pp < part; ++pp) pre *= stot[pp][c];
+            float Fr = pre;
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                Fr *= a[i];
+                F[i] = Fr;
+            }
+        } else {
+            float suf = 1.f;
+            for (int pp = part + 1; pp < (base + hl) / RPP; ++pp) suf *= stot[pp][c];
+            float Fr = suf;
+#pragma unroll
+            for (int i = RPP - 1; i >= 0; --i) {
+                F[i] = Fr;
+                Fr *= a[i];
+            }
+        }
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < RPP; i += 8) {
+                uint4 uq, uk;
+                const uint2 q0 = pack4_bf16(qv[i] * F[i], qv[i + 1] * F[i + 1], qv[i + 2] * F[i + 2], qv[i + 3] * F[i + 3]);
+                const uint2 q1 = pack4_bf16(qv[i + 4] * F[i + 4], qv[i + 5] * F[i + 5], qv[i + 6] * F[i + 6], qv[i + 7] * F[i + 7]);
+                const uint2 k0 = pack4_bf16(kv[i] * F[i], kv[i + 1] * F[i + 1], kv[i + 2] * F[i + 2], kv[i + 3] * F[i + 3]);
+                const uint2 k1 = pack4_bf16(kv[i + 4] * F[i + 4], kv[i + 5] * F[i + 5], kv[i + 6] * F[i + 6], kv[i + 7] * F[i + 7]);
+                uq = uint4{q0.x, q0.y, q1.x, q1.y};
+                uk = uint4{k0.x, k0.y, k1.x, k1.y};
+                *reinterpret_cast<uint4*>(&sQKT[c][p0 + i]) = uq;
+                *reinterpret_cast<uint4*>(&sKKT[c][p0 + i]) = uk;
+            }
+        }
+        __syncthreads();
+        constexpr int T3 = NB * (DK / 16), M3 = (T3 + NW - 1) / NW;
+#pragma unroll
+        for (int m = 0; m < M3; ++m) {
+            const int idx = w + NW * m;
+            if (idx < T3) {
+                const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+                const int tbase = (ti * 16 / (2 * hl)) * (2 * hl);
+                const bool qt = ti * 16 >= tbase + hl;
+                const int kb = qt ? tbase : tbase + hl;  // first row of the summed half
+                const bf16* A1 = qt ? &sP[ti * 16][kb] : &sPT[ti * 16][kb];
+                const bf16* A2 = qt ? &sA[ti * 16][kb] : &sAT[ti * 16][kb];
+                const bf16* B1 = qt ? &sKKT[tj * 16][kb] : &sQKT[tj * 16][kb];
+                const bf16* B2 = &sKKT[tj * 16][kb];
+                f32x4 r1, r2;
+                if (hl == 32) {
+                    r1 = mma_kc<32>(zero4(), A1, PT, B1, PT);
+                    r2 = mma_kc<32>(zero4(), A2, PT, B2, PT);
+                } else {
+                    r1 = mma_kc16(zero4(), A1, PT, B1, PT);
+                    r2 = mma_kc16(zero4(), A2, PT, B2, PT);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sR1[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = r1[r];
+                    sR2[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = r2[r];
+                }
+            }
+        }
+        __syncthreads();
+        if (cp) {
+            float R1[RPP], R2[RPP];
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                R1[i] = scale * sR1[p0 + i][c];
+                R2[i] = sR2[p0 + i][c];
+            }
+            if (qs) {
+#pragma unroll
+                for (int i = 0; i < RPP; ++i) {
+                    const float bt = sbeta[p0 + i];
+                    dq[i] += F[i] * R1[i];
+                    dk[i] += bt * F[i] * R2[i];
+                    dG[i] += qv[i] * F[i] * R1[i] + bt * kv[i] * F[i] * R2[i];
+                    dbr[i] += kv[i] * F[i] * R2[i];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < RPP; ++i) {
+                    dk[i] += F[i] * (R1[i] + R2[i]);
+                    dG[i] -= kv[i] * F[i] * (R1[i] + R2[i]);
+                }
+            }
+        }
+    }
+
+    // ---- pairs inside one 16-token tile (j < i), on VALU: this thread owns
+    // channel c of all 16 rows of its tile; E_ij = prod_{s=j+1..i} a_s.  Row
+    // sums rq (of dP E k), ra (of dA E k) and column sums cs (of dP E q +
+    // dA E beta k) give the decay gradient too: d/dG_i E_ij = E_ij = -d/dG_j E_ij.
+    if (cp) {
+        float cs[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) cs[j] = 0.f;
+#pragma unroll
+        for (int i = 1; i < RPP; ++i) {
+            const int r = p0 + i;
+            const float bi = sbeta[r], bki = bi * kv[i], sqi = scale * qv[i];
+            float rq = 0.f, ra = 0.f, E = 1.f;
+#pragma unroll
+            for (int j = i - 1; j >= 0; --j) {
+                E *= a[j + 1];
+                const float tP = to_f32(sP[r][p0 + j]) * E;
+                const float tA = to_f32(sA[r][p0 + j]) * E;
+                rq += tP * kv[j];
+                ra += tA * kv[j];
+                cs[j] += tP * sqi + tA * bki;
+            }
+            rq *= scale;
+            dq[i] += rq;
+            dk[i] += bi * ra;
+            dG[i] += qv[i] * rq + bki * ra;
+            dbr[i] += kv[i] * ra;
+        }
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            dk[j] += cs[j];
+            dG[j] -= kv[j] * cs[j];
+        }
+    }
+
+    // ---- dg = reverse cumulative sum of dG over the chunk; dbeta; dq, dk out
+    if (cp) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = RPP - 1; i >= 0; --i) {
+            s += dG[i];
+            dG[i] = s;
+        }
+        sext[part][c] = s;
+    }
+    __syncthreads();
+    if (cp) {
+        float add = 0.f;
+        for (int pp = part + 1; pp < NPART; ++pp) add += sext[pp][c];
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            const int r = p0 + i;
+            dG[i] += add;
+            sR1[r][c] = dG[i];
+            sR2[r][c] = dbr[i];
+            if (r < nvalid) {
+                dqo[tok0 * DK + r * rsK + c] = f32_to_bf16(dq[i]);
+                dko[tok0 * DK + r * rsK + c] = f32_to_bf16(dk[i]);
+                if (PCH) dgo[(tok0 + (size_t)r * H) * DK + c] = dG[i];
             }
         }
     }
     __syncthreads();
-    score_grad_tail<bf16, C, DK, PCH, MT_BF16, NTHR_E, RPP, PC, PD>(
-        a, qv, kv, dq, dk, dG, dbr, sdP, sdA, sX, sY, sZ, sbeta, stot, sext, cp, c, part, p0, nvalid,
-        ch, tok0, rsK, H, dbpi, dqo, dko, dgo, dbo);
+    // dbeta (and dg per head): row sums over the channels, 8 threads per row
+    {
+        const int r = tid >> 3, sub = tid & 7;
+        float sb = 0.f, sg = 0.f;
+        if (r < C) {
+#pragma unroll
+            for (int cc = sub; cc < DK; cc += 8) {
+                sb += sR2[r][cc];
+                if (!PCH) sg += sR1[r][cc];
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) {
+            sb += __shfl_xor(sb, off);
+            if (!PCH) sg += __shfl_xor(sg, off);
+        }
+        if (r < nvalid && sub == 0) {
+            dbo[tok0 + (size_t)r * H] = sb + dbpi[(size_t)ch * C + r];
+            if (!PCH) dgo[tok0 + (size_t)r * H] = sg;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -174,6 +174,19 @@ __device__ __forceinline__ f32x4 mma_kc_dyn(f32x4 acc, const bf16* __restrict__ 
     return acc;
 }
 
+// K = 16 on the 16x16x32 instruction: the lanes of the upper K half read an
+// in-range copy of the lower half and supply a zero B operand.
+__device__ __forceinline__ f32x4 mma_kc16(f32x4 acc, const bf16* __restrict__ A, int lda,
+                                          const bf16* __restrict__ Bt, int ldb)
+{
+    const int l = lane_id();
+    const int r = l & 15, kk = l >> 4, ko = 8 * (kk & 1);
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + ko);
+    bf16x8 b = *reinterpret_cast<const bf16x8*>(Bt + r * ldb + ko);
+    if (kk >= 2) b = bf16x8{};
+    return mfma_bf16_16x16x32(a, b, acc);
+}
+
 // four consecutive bf16 (8 bytes) from four floats, round to nearest even
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d)
 {
