@@ -117,21 +117,25 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True):
     elif name == "bchunk1":
         it = 2 if bt else 4
         by = 2 * cv * ib + C * f4 + cc * f4 + 2 * kv * f4 + cv * f4   # v dO, beta, T, S, dS, dD
-        by += (cv * 2 + cv * f4) if bt else (cd + cv) * f4            # D and U | W, U (D = U - W S)
-        by += cv * ib + 3 * cd * it + 2 * cc * it + DK * f4 + C * f4  # dv, dQg dW dKh, dPs G1|dT1, dgam, dbeta
+        by += (cv * 2 + cv * f4 + cd * tb) if bt else (cd + cv) * f4  # D, U, W | W, U (D = U - W S)
+        by += cv * ib + 3 * cd * it + 2 * cc * it + DK * f4 + C * f4  # dv, dQg dX_K|dW dKh, dPs dA|dT1, dgam, dbeta
         fl[mt] += 6 * C * DK * DV + 2 * tri * DV + 2 * C * C * DV     # dQg dW dKh, dPs, dX_V U^T | dD X_V^T
         fl["f32"] += 2 * tri * DV                                      # dX_V = T^T dD
-        if not bt:
+        if bt:   # keys' WY adjoint: dX_K = T^T dW, dA = -(G1 + dX_K W^T) strictly lower
+            fl["bf16"] += 2 * tri * DK + 2 * (C * (C - 1) // 2) * DK
+        else:
             fl[mt] += 2 * C * DK * DV                                  # D = U - W S
+    elif name == "bchunk2_finish":  # dbeta (and per-head dg) from the channel-half partials
+        by = (3 * C * f4 + C * f4) + (0 if per_channel else 2 * C * f4 + C * f4)
     elif name == "bchunk2":
         it = 2 if bt else 4
-        by = 2 * cd * ib + gb + C * f4 + cc * f4                      # q k, g, beta, T
-        by += 3 * cd * it + 2 * cc * it + DK * f4 + C * f4            # dQg dW dKh, dPs G1|dT1, dgam, dbeta part
-        by += cd * tb if bt else 0                                    # W (bf16 table)
-        by += 2 * cd * ib + gb + C * f4                               # dq dk, dg, dbeta
-        if bt:  # dX_K = T^T dW, dA = -(G1 + dX_K W^T) strictly lower, on bf16 MFMA
-            fl["bf16"] += 2 * tri * DK + 2 * (C * (C - 1) // 2) * DK
-        else:   # dX_K = T^T dW, dT = dT1 + dW X_K^T, dA = -T^T dT T^T
+        by = 2 * cd * ib + gb + C * f4                                # q k, g, beta
+        by += 3 * cd * it + 2 * cc * it + DK * f4                     # dQg dX_K|dW dKh, dPs dA|dT1, dgam
+        by += 2 * cd * ib + (gb if per_channel else 0)                # dq dk, dg
+        if bt:   # two channel halves: partial dbeta (and per-head dg) sums
+            by += 2 * C * f4 + (0 if per_channel else 2 * C * f4)
+        else:    # T, dbeta part in; dX_K = T^T dW, dT = dT1 + dW X_K^T, dA = -T^T dT T^T
+            by += cc * f4 + C * f4 + C * f4 + (0 if per_channel else C * f4)
             fl["f32"] += 2 * (2 * tri * DK) + 2 * (2 * C ** 3 / 3)
         fl[mt] += 2 * (2 * tri * DK) + 2 * (2 * tri * DK)             # score gradients of P and A
     else:
@@ -256,8 +260,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    launches_per_step = 5
-    rec = LaunchRecorder(args.steps * launches_per_step + 16)
+    rec = LaunchRecorder(args.steps * 16 + 16)  # room for every launch of the timed steps
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -541,7 +541,7 @@ __global__ void __launch_bounds__(NTHR_C)
 bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const bf16* __restrict__ dO, const bf16* __restrict__ Dst,
                 const float* __restrict__ Ui, const float* __restrict__ Tmi,
-                const float* __restrict__ Sst,
+                const bf16* __restrict__ Wbi, const float* __restrict__ Sst,
                 const float* __restrict__ dSt, const float* __restrict__ dDt,
                 bf16* __restrict__ dvo, float* __restrict__ dQgo, float* __restrict__ dWgo,
                 float* __restrict__ dKho, float* __restrict__ dPso, float* __restrict__ dT1o,
@@ -557,10 +557,31 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     constexpr int NB8 = C * BW / 8;                  // uint4 words of a bf16 [C][BW] tile
     constexpr int ND4 = C * BW / 4;                  // float4 words of dD
     static_assert(NB8 <= NTHR_C / 2 && ND4 <= NTHR_C, "tile split assumes C*BW <= 2048");
-    __shared__ __align__(16) bf16 sS[DK][PB], sdS[DK][PB], sdO[C][PB], sD[C][PB], sdD[C][PB];
-    __shared__ __align__(16) bf16 sU[C][PB], sdX[C][PB];  // U and dX_V tiles, for G1 = dX_V U^T
-    __shared__ __align__(16) float sT[C][PC], sdDf[C][PF], sv[C][PF];
+    constexpr int PT = C + 8, PK = DK + 8;  // bf16 pitches of the key WY-adjoint tables
+    // Dv-streaming tiles, and after the Dv loop the key WY-adjoint tables, share sbuf
+    constexpr int O_dS = DK * PB * 2, O_dO = 2 * DK * PB * 2, O_D = O_dO + C * PB * 2;
+    constexpr int O_dD = O_D + C * PB * 2, O_U = O_dD + C * PB * 2, O_dX = O_U + C * PB * 2;
+    constexpr int O_dDf = O_dX + C * PB * 2, O_v = O_dDf + C * PF * 4, STREAM = O_v + C * PF * 4;
+    constexpr int O_TTh = DK * PT * 2, O_TTl = O_TTh + C * PT * 2, O_W = O_TTl + C * PT * 2;
+    constexpr int O_Xh = O_W + C * PK * 2, O_Xl = O_Xh + C * PK * 2, ENDP = O_Xl + C * PK * 2;
+    __shared__ __align__(16) char sbuf[cmax(STREAM, ENDP)];
+    __shared__ __align__(16) float sT[C][PC];
     __shared__ float sbeta[C], sred[NW][C];
+    bf16 (*sS)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf);
+    bf16 (*sdS)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_dS);
+    bf16 (*sdO)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_dO);
+    bf16 (*sD)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_D);
+    bf16 (*sdD)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_dD);
+    bf16 (*sU)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_U);    // U and dX_V tiles,
+    bf16 (*sdX)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_dX);  // for G1 = dX_V U^T
+    float (*sdDf)[PF] = reinterpret_cast<float (*)[PF]>(sbuf + O_dDf);
+    float (*sv)[PF] = reinterpret_cast<float (*)[PF]>(sbuf + O_v);
+    bf16 (*sdWT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);          // dW^T
+    bf16 (*sTTh)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + O_TTh);  // T^T, high part
+    bf16 (*sTTl)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + O_TTl);  // T^T, low part
+    bf16 (*sW)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + O_W);
+    bf16 (*sXh)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + O_Xh);    // dX_K, high part
+    bf16 (*sXl)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + O_Xl);    // dX_K, low part
 
     const int ch = blockIdx.x;
     const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
@@ -667,8 +688,17 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     fetch(0);
     stash();
     __syncthreads();
+    constexpr int NK8 = (C * DK / 8 + NTHR_C - 1) / NTHR_C;
+    uint4 wv[NK8];  // W rows (bf16), fetched while the last Dv tile is processed
     for (int v0 = 0; v0 < DV; v0 += BW) {
-        if (v0 + BW < DV) fetch(v0 + BW);
+        if (v0 + BW < DV) {
+            fetch(v0 + BW);
+        } else {
+            const bf16* Wp = Wbi + (size_t)ch * C * DK;
+#pragma unroll
+            for (int u = 0; u < NK8; ++u)
+                wv[u] = *reinterpret_cast<const uint4*>(Wp + 8 * min(tid + NTHR_C * u, C * DK / 8 - 1));
+        }
         // dX_V = T^T dD (fp32): dv = beta dX_V, and <dX_V, v> for dbeta
 #pragma unroll
         for (int m = 0; m < MD; ++m) {
@@ -719,7 +749,6 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 
     // outputs (bf16: the consumer reads them as gradients of bf16-rounded products)
     bf16* dQp = reinterpret_cast<bf16*>(dQgo) + (size_t)ch * C * DK;
-    bf16* dWp = reinterpret_cast<bf16*>(dWgo) + (size_t)ch * C * DK;
     bf16* dKp = reinterpret_cast<bf16*>(dKho) + (size_t)ch * C * DK;
 #pragma unroll
     for (int m = 0; m < M3; ++m) {
@@ -730,13 +759,14 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             for (int r = 0; r < 4; ++r) {
                 const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
                 dQp[i * DK + j] = f32_to_bf16(aQ[m][r]);
-                dWp[i * DK + j] = f32_to_bf16(-aW[m][r]);
                 dKp[i * DK + j] = f32_to_bf16(aK[m][r]);
             }
+            // dW = -aW, stored transposed for dX_K = T^T dW (4 consecutive rows per lane)
+            *reinterpret_cast<uint2*>(&sdWT[tj * 16 + lr][ti * 16 + 4 * lq]) =
+                pack4_bf16(-aW[m][0], -aW[m][1], -aW[m][2], -aW[m][3]);
         }
     }
     bf16* dPp = reinterpret_cast<bf16*>(dPso) + (size_t)ch * C * C;
-    bf16* dTp = reinterpret_cast<bf16*>(dT1o) + (size_t)ch * C * C;
 #pragma unroll
     for (int m = 0; m < M2; ++m) {
         const int idx = w + NW * m;
@@ -746,7 +776,71 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             for (int r = 0; r < 4; ++r) {
                 const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
                 dPp[i * C + j] = f32_to_bf16(aP[m][r]);
-                dTp[i * C + j] = f32_to_bf16(aT[m][r]);
+            }
+        }
+    }
+
+    // ---- WY adjoint of the keys (W = T X_K):  dX_K = T^T dW and
+    //   dA = -T^T (dU X_V^T + dW X_K^T) T^T = -(dX_V U^T + dX_K W^T) = -(G1 + dX_K W^T),
+    // on bf16 MFMA with T and dX_K as high + low bf16 parts (16 significant bits).
+    // T^T: thread -> 8 consecutive columns of one row
+    for (int idx = tid; idx < C * C / 8; idx += NTHR_C) {
+        const int i = idx / (C / 8), k0 = (idx % (C / 8)) * 8;
+        float hv[8], lv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float t = sT[k0 + e][i];
+            hv[e] = to_f32(f32_to_bf16(t));
+            lv[e] = t - hv[e];
+        }
+        const uint2 h0 = pack4_bf16(hv[0], hv[1], hv[2], hv[3]), h1 = pack4_bf16(hv[4], hv[5], hv[6], hv[7]);
+        const uint2 l0 = pack4_bf16(lv[0], lv[1], lv[2], lv[3]), l1 = pack4_bf16(lv[4], lv[5], lv[6], lv[7]);
+        *reinterpret_cast<uint4*>(&sTTh[i][k0]) = uint4{h0.x, h0.y, h1.x, h1.y};
+        *reinterpret_cast<uint4*>(&sTTl[i][k0]) = uint4{l0.x, l0.y, l1.x, l1.y};
+    }
+#pragma unroll
+    for (int u = 0; u < NK8; ++u) {
+        const int idx = tid + NTHR_C * u;
+        if (idx < C * DK / 8) *reinterpret_cast<uint4*>(&sW[idx / (DK / 8)][(idx % (DK / 8)) * 8]) = wv[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M3; ++m) {
+        const int idx = w + NW * m;
+        if (idx < T3) {
+            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+            f32x4 acc = mma_kc<C>(zero4(), &sTTh[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
+            acc = mma_kc<C>(acc, &sTTl[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                const bf16 hi = f32_to_bf16(acc[r]);
+                sXh[i][j] = hi;
+                sXl[i][j] = f32_to_bf16(acc[r] - to_f32(hi));
+            }
+        }
+    }
+    __syncthreads();
+    {
+        // dX_K out (bf16), in place of dW
+        bf16* dXp = reinterpret_cast<bf16*>(dWgo) + (size_t)ch * C * DK;
+        for (int idx = tid; idx < C * DK / 8; idx += NTHR_C) {
+            const int r = idx / (DK / 8), c0 = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<uint4*>(dXp + r * DK + c0) = *reinterpret_cast<const uint4*>(&sXh[r][c0]);
+        }
+    }
+    bf16* dAp = reinterpret_cast<bf16*>(dT1o) + (size_t)ch * C * C;
+#pragma unroll
+    for (int m = 0; m < M2; ++m) {
+        const int idx = w + NW * m;
+        if (idx < T2) {
+            const int ti = idx / NB, tj = idx % NB;
+            f32x4 acc = mma_kc<DK>(aT[m], &sXh[ti * 16][0], PK, &sW[tj * 16][0], PK);
+            acc = mma_kc<DK>(acc, &sXl[ti * 16][0], PK, &sW[tj * 16][0], PK);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                dAp[i * C + j] = f32_to_bf16(i > j ? -acc[r] : 0.f);
             }
         }
     }
@@ -1217,65 +1311,58 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
 }
 
 // ---------------------------------------------------------------------------
-// bchunk2b: bf16 inputs at chunk 64.  The WY adjoint uses
-//   -T^T (dU X_V^T + dW X_K^T) T^T = -(dX_V U^T + dX_K W^T),
-// with dX_V = T^T dU and U = T X_V (likewise for K), so with G1 = dX_V U^T
-// from bchunk1b only dX_K = T^T dW and dX_K W^T remain, both on bf16 MFMA:
-// T and dX_K enter as bf16 hi + lo pairs (16 significant bits), dW and W
-// are bf16 tables already.  The score gradients dPs (unscaled) and dA are
-// then kept as bf16 tables in both orientations, and the level tables are
-// channel-major, so every MFMA operand is one 16-byte LDS read.
+// bchunk2c: bf16 inputs at chunk 64, after bchunk1b has taken the WY adjoint
+// (dX_K and dA).  One workgroup takes one chunk-head and half of its key
+// channels: score gradients by the block-boundary split, the decay chain rule
+// and the outputs dq, dk, dg of those channels.  256 threads and < 80 KB of
+// LDS let two workgroups share a CU, so one loads while the other computes.
+// dbeta (and dg for per-head decay) are row sums over all channels: each half
+// writes its partial sums and bchunk2_finish adds them in a fixed order.
 // ---------------------------------------------------------------------------
-constexpr int NTHR_E = 512;  // 8 waves
+constexpr int NTHR_F = 256;  // 4 waves: one per 16-row part
 
 template <int C, int DK, bool PCH>
-__global__ void __launch_bounds__(NTHR_E)
-bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
-                const float* __restrict__ beta, const float* __restrict__ Tmi,
-                const bf16* __restrict__ Wbi, const bf16* __restrict__ dQgi,
-                const bf16* __restrict__ dWgi, const bf16* __restrict__ dKhi,
-                const bf16* __restrict__ dPsi, const bf16* __restrict__ G1i,
-                const float* __restrict__ dgmi, const float* __restrict__ dbpi,
-                bf16* __restrict__ dqo, bf16* __restrict__ dko, float* __restrict__ dgo,
-                float* __restrict__ dbo, int T, int H, int NC, float scale)
+__global__ void __launch_bounds__(NTHR_F)
+bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+                const float* __restrict__ beta, const bf16* __restrict__ dQgi,
+                const bf16* __restrict__ dXKi, const bf16* __restrict__ dKhi,
+                const bf16* __restrict__ dPsi, const bf16* __restrict__ dAi,
+                const float* __restrict__ dgmi, bf16* __restrict__ dqo, bf16* __restrict__ dko,
+                float* __restrict__ dgo, float* __restrict__ dbq, float* __restrict__ dgq, int T,
+                int H, int NC, int nch, float scale)
 {
-    static_assert(C == 64, "bchunk2b: chunk 64");
-    constexpr int NB = C / 16, NW = NTHR_E / 64;
+    static_assert(C == 64, "bchunk2c: chunk 64");
+    constexpr int HC = DK / 2;  // key channels per workgroup
+    constexpr int NB = C / 16, NW = NTHR_F / 64;
     constexpr int RPP = 16, NPART = C / RPP;
-    constexpr int PD = DK + 4;              // fp32 pitch
-    constexpr int PT = C + 8, PK = DK + 8;  // bf16 pitches: 16-byte rows, banks spread
-    // WY-adjoint tables (bf16), later the level tables and results, share sbuf
-    constexpr int OT_L = C * PT * 2, OT_DW = 2 * C * PT * 2, OT_W = OT_DW + DK * PT * 2;
-    constexpr int OT_XH = OT_W + C * PK * 2, OT_XL = OT_XH + C * PK * 2, PH1 = OT_XL + C * PK * 2;
-    constexpr int OL_K = DK * PT * 2, OL_R1 = 2 * DK * PT * 2, OL_R2 = OL_R1 + C * PD * 4;
-    constexpr int PH2 = OL_R2 + C * PD * 4;
-    __shared__ __align__(16) char sbuf[cmax(PH1, PH2)];
+    static_assert(NPART * HC <= NTHR_F, "one column thread per (part, channel)");
+    constexpr int PT = C + 8;  // bf16 pitch: 16-byte rows, banks spread
+    constexpr int PH = HC + 1; // fp32 pitch of the result tables
     // score gradients, bf16: dPs (unscaled, lower incl. diagonal) and dA (strictly
-    // lower) by rows, their transposes, the latter with the beta of the row folded in
+    // lower) by rows and transposed, the transposed dA with beta_i folded in
     __shared__ __align__(16) bf16 sP[C][PT], sPT[C][PT], sA[C][PT], sAT[C][PT];
-    __shared__ float sbeta[C], stot[NPART][DK], sext[NPART][DK];
-    bf16 (*sTh)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);         // T^T, high part
-    bf16 (*sTl)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + OT_L);  // T^T, low part
-    bf16 (*sdWT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + OT_DW);
-    bf16 (*sW)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + OT_W);
-    bf16 (*sXh)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + OT_XH);  // dX_K, high part
-    bf16 (*sXl)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + OT_XL);  // dX_K, low part
-    bf16 (*sQKT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);         // level tables, channel-major
-    bf16 (*sKKT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + OL_K);
-    float (*sR1)[PD] = reinterpret_cast<float (*)[PD]>(sbuf + OL_R1);
-    float (*sR2)[PD] = reinterpret_cast<float (*)[PD]>(sbuf + OL_R2);
+    __shared__ __align__(16) bf16 sQKT[HC][PT], sKKT[HC][PT];  // level tables, channel-major
+    // level results: query rows scale*R1, key rows scale*R1 + R2 (sR); query rows'
+    // R2 (sR2, C/2 rows); before the levels sR also holds the dKh row-sum partials
+    __shared__ float sR[C][PH], sR2[C / 2][PH];
+    __shared__ float sbeta[C], stot[NPART][HC];
+    float (*sext)[HC] = reinterpret_cast<float (*)[HC]>(&sR[0][0]);
 
-    const int ch = blockIdx.x;
+    // block -> (chunk-head, half): the two halves of a chunk-head are 8 ids
+    // apart, so they run on the same XCD and share its L2 for the C x C tables
+    const int bid = blockIdx.x;
+    const int half = (bid >> 3) & 1;
+    const int ch = (bid >> 4) * 8 + (bid & 7);
+    if (ch >= nch) return;  // whole workgroup: no barrier is skipped by part of it
     const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
     const int t0 = n * C;
     const int nvalid = min(C, T - t0);
     const int tid = threadIdx.x, w = tid >> 6;
     const size_t tok0 = ((size_t)b * T + t0) * H + h;
     const size_t rsK = (size_t)H * DK;
-
-    // column threads: channel c, rows [p0, p0 + RPP)
-    const bool cp = tid < NPART * DK;
-    const int c = tid % DK, part = cp ? tid / DK : 0, p0 = part * RPP;
+    const bool cp = tid < NPART * HC;
+    const int cl = tid % HC, part = cp ? tid / HC : 0, p0 = part * RPP;
+    const int c = half * HC + cl;  // key channel
 
     float a[RPP], qv[RPP], kv[RPP], Gm[RPP];
     float dq[RPP], dk[RPP], dG[RPP], dbr[RPP];
@@ -1289,78 +1376,43 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         const float qx = to_f32(q[tok0 * DK + rr * rsK + c]);
         const float kx = to_f32(k[tok0 * DK + rr * rsK + c]);
         const bool ok = cp && r < nvalid;
-        a[i] = ok ? gx : 0.f;  // log-decay until the other loads are out
+        a[i] = ok ? gx : 0.f;  // log-decay until the table loads are out
         qv[i] = ok ? qx : 0.f;
         kv[i] = ok ? kx : 0.f;
         dq[i] = dk[i] = dG[i] = dbr[i] = 0.f;
     }
-    // this wave's 16x16 tiles of G1 and dPs (C x C), kept in registers
-    constexpr int MA = (NB * NB + NW - 1) / NW;
-    float pG[MA][4], pP[MA][4];
     {
-        const bf16* Gp = G1i + (size_t)ch * C * C;
+        // dPs and dA (C x C bf16): rows as they are, and transposed
+        constexpr int NC8 = C * C / 8, NU = (NC8 + NTHR_F - 1) / NTHR_F;
         const bf16* Pp = dPsi + (size_t)ch * C * C;
+        const bf16* Ap = dAi + (size_t)ch * C * C;
+        uint4 pw[NU], aw[NU];
+        float bw[NU];
 #pragma unroll
-        for (int m = 0; m < MA; ++m) {
-            const int idx = (w + NW * m) % (NB * NB);
-            const int ti = idx / NB, tj = idx % NB;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int e = (ti * 16 + acc_row(r)) * C + tj * 16 + acc_col();
-                pG[m][r] = to_f32(Gp[e]);
-                pP[m][r] = to_f32(Pp[e]);
-            }
-        }
-    }
-    {
-        // T (fp32), dW and W (bf16), beta: all loads issued before the LDS writes
-        constexpr int NT4 = (C * C / 4 + NTHR_E - 1) / NTHR_E;
-        constexpr int NK8 = (C * DK / 8 + NTHR_E - 1) / NTHR_E;
-        const float* Tp = Tmi + (size_t)ch * C * C;
-        const bf16* dWp = dWgi + (size_t)ch * C * DK;
-        const bf16* Wp = Wbi + (size_t)ch * C * DK;
-        float4 tv[NT4];
-        uint4 dwv[NK8], wv[NK8];
-#pragma unroll
-        for (int u = 0; u < NT4; ++u) {
-            const int idx = min(tid + NTHR_E * u, C * C / 4 - 1);
-            tv[u] = *reinterpret_cast<const float4*>(Tp + 4 * idx);
-        }
-#pragma unroll
-        for (int u = 0; u < NK8; ++u) {
-            const int idx = min(tid + NTHR_E * u, C * DK / 8 - 1);
-            dwv[u] = *reinterpret_cast<const uint4*>(dWp + 8 * idx);
-            wv[u] = *reinterpret_cast<const uint4*>(Wp + 8 * idx);
+        for (int u = 0; u < NU; ++u) {
+            const int idx = min(tid + NTHR_F * u, NC8 - 1);
+            pw[u] = *reinterpret_cast<const uint4*>(Pp + 8 * idx);
+            aw[u] = *reinterpret_cast<const uint4*>(Ap + 8 * idx);
+            bw[u] = beta[tok0 + (size_t)min(idx / (C / 8), nvalid - 1) * H];
         }
         const float bv = beta[tok0 + (size_t)min(tid % C, nvalid - 1) * H];
-        // T^T as high and low bf16 parts: element T[r][j] goes to row j, column r
 #pragma unroll
-        for (int u = 0; u < NT4; ++u) {
-            const int idx = tid + NTHR_E * u;
-            if (idx < C * C / 4) {
-                const int r = idx / (C / 4), j0 = (idx % (C / 4)) * 4;
-                const float tt[4] = {tv[u].x, tv[u].y, tv[u].z, tv[u].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bf16 hi = f32_to_bf16(tt[e]);
-                    sTh[j0 + e][r] = hi;
-                    sTl[j0 + e][r] = f32_to_bf16(tt[e] - to_f32(hi));
-                }
-            }
-        }
-        // dW^T (element dW[r][cc] to row cc, column r) and W as it is
-#pragma unroll
-        for (int u = 0; u < NK8; ++u) {
-            const int idx = tid + NTHR_E * u;
-            if (idx < C * DK / 8) {
-                const int r = idx / (DK / 8), c0 = (idx % (DK / 8)) * 8;
-                const uint32_t x[4] = {dwv[u].x, dwv[u].y, dwv[u].z, dwv[u].w};
+        for (int u = 0; u < NU; ++u) {
+            const int idx = tid + NTHR_F * u;
+            if (idx < NC8) {
+                const int i = idx / (C / 8), j0 = (idx % (C / 8)) * 8;
+                *reinterpret_cast<uint4*>(&sP[i][j0]) = pw[u];
+                *reinterpret_cast<uint4*>(&sA[i][j0]) = aw[u];
+                const float bi = i < nvalid ? bw[u] : 0.f;
+                const uint32_t pu[4] = {pw[u].x, pw[u].y, pw[u].z, pw[u].w};
+                const uint32_t au[4] = {aw[u].x, aw[u].y, aw[u].z, aw[u].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    sdWT[c0 + 2 * e][r].bits = (uint16_t)(x[e] & 0xFFFFu);
-                    sdWT[c0 + 2 * e + 1][r].bits = (uint16_t)(x[e] >> 16);
+                    sPT[j0 + 2 * e][i].bits = (uint16_t)(pu[e] & 0xFFFFu);
+                    sPT[j0 + 2 * e + 1][i].bits = (uint16_t)(pu[e] >> 16);
+                    sAT[j0 + 2 * e][i] = f32_to_bf16(bi * __uint_as_float(au[e] << 16));
+                    sAT[j0 + 2 * e + 1][i] = f32_to_bf16(bi * __uint_as_float(au[e] & 0xFFFF0000u));
                 }
-                *reinterpret_cast<uint4*>(&sW[r][c0]) = wv[u];
             }
         }
         if (tid < C) sbeta[tid] = tid < nvalid ? bv : 0.f;
@@ -1371,17 +1423,16 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         float pt = 1.f;
 #pragma unroll
         for (int i = 0; i < RPP; ++i) pt *= a[i];
-        if (cp) stot[part][c] = pt;
+        if (cp) stot[part][cl] = pt;
     }
     __syncthreads();
 
-    // ---- Gamma, Kh factor; contributions of dQg, dKh, dgam
+    // ---- Gamma, Kh factor; contributions of dQg, dKh; X_K = diag(beta) K o Gamma
     if (cp) {
-        const bf16* dQp = dQgi + (size_t)ch * C * DK;
-        const bf16* dKp = dKhi + (size_t)ch * C * DK;
+        const size_t e0 = (size_t)ch * C * DK + c;
         float pre = 1.f, suf = 1.f;
-        for (int pp = 0; pp < part; ++pp) pre *= stot[pp][c];
-        for (int pp = part + 1; pp < NPART; ++pp) suf *= stot[pp][c];
+        for (int pp = 0; pp < part; ++pp) pre *= stot[pp][cl];
+        for (int pp = part + 1; pp < NPART; ++pp) suf *= stot[pp][cl];
         float Gr = pre;
 #pragma unroll
         for (int i = 0; i < RPP; ++i) {
@@ -1392,7 +1443,8 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
 #pragma unroll
         for (int i = RPP - 1; i >= 0; --i) {
             const int r = p0 + i;
-            const float dqg = to_f32(dQp[r * DK + c]), dkh = to_f32(dKp[r * DK + c]);
+            const float dqg = to_f32(dQgi[e0 + r * DK]), dkh = to_f32(dKhi[e0 + r * DK]);
+            const float dx = to_f32(dXKi[e0 + r * DK]);
             dq[i] += scale * Gm[i] * dqg;
             dG[i] += scale * qv[i] * Gm[i] * dqg;
             const float khv = kv[i] * kap;
@@ -1400,74 +1452,20 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             dG[i] -= khv * dkh;
             sumKh += khv * dkh;
             kap *= a[i];
+            // dk += beta Gamma dX_K, dG += X_K o dX_K, dbeta += <k Gamma, dX_K>
+            const float kg = kv[i] * Gm[i], bt = sbeta[r];
+            dk[i] += bt * Gm[i] * dx;
+            dG[i] += bt * kg * dx;
+            dbr[i] += kg * dx;
         }
-        sext[part][c] = sumKh;
-    }
-    // ---- dX_K = T^T dW: (T_hi + T_lo)^T dW on bf16 MFMA; stored as hi + lo
-    {
-        constexpr int T3 = NB * (DK / 16), M3 = (T3 + NW - 1) / NW;
-#pragma unroll
-        for (int m = 0; m < M3; ++m) {
-            const int idx = w + NW * m;
-            if (idx < T3) {
-                const int ti = idx / (DK / 16), tj = idx % (DK / 16);
-                f32x4 acc = mma_kc<C>(zero4(), &sTh[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
-                acc = mma_kc<C>(acc, &sTl[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
-                    const bf16 hi = f32_to_bf16(acc[r]);
-                    sXh[i][j] = hi;
-                    sXl[i][j] = f32_to_bf16(acc[r] - to_f32(hi));
-                }
-            }
-        }
+        sext[part][cl] = sumKh;
     }
     __syncthreads();
     if (cp && part == NPART - 1) {
         float sacc = 0.f;
-        for (int pp = 0; pp < NPART; ++pp) sacc += sext[pp][c];
+        for (int pp = 0; pp < NPART; ++pp) sacc += sext[pp][cl];
         dG[RPP - 1] += sacc + Gm[RPP - 1] * dgmi[(size_t)ch * DK + c];
     }
-    // X_K = diag(beta) K o Gamma: dk += beta Gamma dX_K, dG += X_K o dX_K,
-    // dbeta += <k Gamma, dX_K>
-    if (cp) {
-#pragma unroll
-        for (int i = 0; i < RPP; ++i) {
-            const int r = p0 + i;
-            const float dx = to_f32(sXh[r][c]) + to_f32(sXl[r][c]);
-            const float kg = kv[i] * Gm[i];
-            dk[i] += sbeta[r] * Gm[i] * dx;
-            dG[i] += sbeta[r] * kg * dx;
-            dbr[i] += kg * dx;
-        }
-    }
-    // ---- dA = -(G1 + dX_K W^T), strictly lower; dPs lower; bf16 tables by
-    // rows and transposed (dA^T with beta_i folded into column i)
-#pragma unroll
-    for (int m = 0; m < MA; ++m) {
-        const int idx = w + NW * m;
-        if (idx < NB * NB) {
-            const int ti = idx / NB, tj = idx % NB;
-            f32x4 acc = mma_kc<DK>(zero4(), &sXh[ti * 16][0], PK, &sW[tj * 16][0], PK);
-            acc = mma_kc<DK>(acc, &sXl[ti * 16][0], PK, &sW[tj * 16][0], PK);
-            float av[4], bav[4], pv[4];
-            const int i0 = ti * 16 + acc_row(0), j = tj * 16 + acc_col();
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = i0 + r;
-                av[r] = i > j ? -(pG[m][r] + acc[r]) : 0.f;
-                bav[r] = sbeta[i] * av[r];
-                pv[r] = i >= j ? pP[m][r] : 0.f;
-                sA[i][j] = f32_to_bf16(av[r]);
-                sP[i][j] = f32_to_bf16(pv[r]);
-            }
-            *reinterpret_cast<uint2*>(&sAT[j][i0]) = pack4_bf16(bav[0], bav[1], bav[2], bav[3]);
-            *reinterpret_cast<uint2*>(&sPT[j][i0]) = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
-        }
-    }
-    __syncthreads();
-
     // ---- diagonal scores (decay 1): P_ii = q_i . k_i
     if (cp) {
 #pragma unroll
@@ -1478,11 +1476,10 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         }
     }
 
-    // ---- score gradients of pairs that span two 16-token tiles: levels
-    // h = 32, 16 of the block-boundary split.  Each own row is in the query
-    // half or the key half of its 2h-block; with F its level factor
-    // (query rows prod_{s=m+1..r} a_s, key rows prod_{s=r+1..m} a_s, m the last
-    // token of the earlier half) the tables hold (q o F)^T and (k o F)^T and
+    // ---- pairs that span two 16-token tiles: levels h = 32, 16 of the
+    // block-boundary split.  With F the level factor of each own row (query
+    // rows prod_{s=m+1..r} a_s, key rows prod_{s=r+1..m} a_s, m the last token
+    // of the earlier half) the tables hold (q o F)^T and (k o F)^T, and
     //   query rows: R1 = dPs KK,      R2 = dA KK
     //   key rows:   R1 = dPs^T QK,    R2 = (diag(beta) dA)^T KK
 #pragma unroll
@@ -1493,7 +1490,7 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         const bool qs = p0 >= base + hl;
         if (qs) {
             float pre = 1.f;
-            for (int pp = (base + hl) / RPP; pp < part; ++pp) pre *= stot[pp][c];
+            for (int pp = (base + hl) / RPP; pp < part; ++pp) pre *= stot[pp][cl];
             float Fr = pre;
 #pragma unroll
             for (int i = 0; i < RPP; ++i) {
@@ -1502,7 +1499,7 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             }
         } else {
             float suf = 1.f;
-            for (int pp = part + 1; pp < (base + hl) / RPP; ++pp) suf *= stot[pp][c];
+            for (int pp = part + 1; pp < (base + hl) / RPP; ++pp) suf *= stot[pp][cl];
             float Fr = suf;
 #pragma unroll
             for (int i = RPP - 1; i >= 0; --i) {
@@ -1513,24 +1510,21 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         if (cp) {
 #pragma unroll
             for (int i = 0; i < RPP; i += 8) {
-                uint4 uq, uk;
                 const uint2 q0 = pack4_bf16(qv[i] * F[i], qv[i + 1] * F[i + 1], qv[i + 2] * F[i + 2], qv[i + 3] * F[i + 3]);
                 const uint2 q1 = pack4_bf16(qv[i + 4] * F[i + 4], qv[i + 5] * F[i + 5], qv[i + 6] * F[i + 6], qv[i + 7] * F[i + 7]);
                 const uint2 k0 = pack4_bf16(kv[i] * F[i], kv[i + 1] * F[i + 1], kv[i + 2] * F[i + 2], kv[i + 3] * F[i + 3]);
                 const uint2 k1 = pack4_bf16(kv[i + 4] * F[i + 4], kv[i + 5] * F[i + 5], kv[i + 6] * F[i + 6], kv[i + 7] * F[i + 7]);
-                uq = uint4{q0.x, q0.y, q1.x, q1.y};
-                uk = uint4{k0.x, k0.y, k1.x, k1.y};
-                *reinterpret_cast<uint4*>(&sQKT[c][p0 + i]) = uq;
-                *reinterpret_cast<uint4*>(&sKKT[c][p0 + i]) = uk;
+                *reinterpret_cast<uint4*>(&sQKT[cl][p0 + i]) = uint4{q0.x, q0.y, q1.x, q1.y};
+                *reinterpret_cast<uint4*>(&sKKT[cl][p0 + i]) = uint4{k0.x, k0.y, k1.x, k1.y};
             }
         }
         __syncthreads();
-        constexpr int T3 = NB * (DK / 16), M3 = (T3 + NW - 1) / NW;
+        constexpr int T3 = NB * (HC / 16), M3 = (T3 + NW - 1) / NW;
 #pragma unroll
         for (int m = 0; m < M3; ++m) {
             const int idx = w + NW * m;
             if (idx < T3) {
-                const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+                const int ti = idx / (HC / 16), tj = idx % (HC / 16);
                 const int tbase = (ti * 16 / (2 * hl)) * (2 * hl);
                 const bool qt = ti * 16 >= tbase + hl;
                 const int kb = qt ? tbase : tbase + hl;  // first row of the summed half
@@ -1548,33 +1542,35 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    sR1[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = r1[r];
-                    sR2[ti * 16 + acc_row(r)][tj * 16 + acc_col()] = r2[r];
+                    const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
+                    if (qt) {
+                        sR[i][j] = scale * r1[r];
+                        sR2[(i / (2 * hl)) * hl + (i % hl)][j] = r2[r];
+                    } else {
+                        sR[i][j] = scale * r1[r] + r2[r];
+                    }
                 }
             }
         }
         __syncthreads();
         if (cp) {
-            float R1[RPP], R2[RPP];
-#pragma unroll
-            for (int i = 0; i < RPP; ++i) {
-                R1[i] = scale * sR1[p0 + i][c];
-                R2[i] = sR2[p0 + i][c];
-            }
             if (qs) {
 #pragma unroll
                 for (int i = 0; i < RPP; ++i) {
-                    const float bt = sbeta[p0 + i];
-                    dq[i] += F[i] * R1[i];
-                    dk[i] += bt * F[i] * R2[i];
-                    dG[i] += qv[i] * F[i] * R1[i] + bt * kv[i] * F[i] * R2[i];
-                    dbr[i] += kv[i] * F[i] * R2[i];
+                    const int r = p0 + i;
+                    const float R1 = sR[r][cl], R2 = sR2[(r / (2 * hl)) * hl + (r % hl)][cl];
+                    const float bt = sbeta[r];
+                    dq[i] += F[i] * R1;
+                    dk[i] += bt * F[i] * R2;
+                    dG[i] += qv[i] * F[i] * R1 + bt * kv[i] * F[i] * R2;
+                    dbr[i] += kv[i] * F[i] * R2;
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < RPP; ++i) {
-                    dk[i] += F[i] * (R1[i] + R2[i]);
-                    dG[i] -= kv[i] * F[i] * (R1[i] + R2[i]);
+                    const float R = sR[p0 + i][cl];
+                    dk[i] += F[i] * R;
+                    dG[i] -= kv[i] * F[i] * R;
                 }
             }
         }
@@ -1615,7 +1611,9 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         }
     }
 
-    // ---- dg = reverse cumulative sum of dG over the chunk; dbeta; dq, dk out
+    // ---- dg = reverse cumulative sum of dG over the chunk (the part sums go
+    // through stot, no longer needed); dq, dk, dg out; dbeta partials
+    float (*spart)[HC] = stot;  // every level factor was formed before the last level's barriers
     if (cp) {
         float s = 0.f;
 #pragma unroll
@@ -1623,18 +1621,17 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             s += dG[i];
             dG[i] = s;
         }
-        sext[part][c] = s;
+        spart[part][cl] = s;
     }
     __syncthreads();
     if (cp) {
         float add = 0.f;
-        for (int pp = part + 1; pp < NPART; ++pp) add += sext[pp][c];
+        for (int pp = part + 1; pp < NPART; ++pp) add += spart[pp][cl];
 #pragma unroll
         for (int i = 0; i < RPP; ++i) {
             const int r = p0 + i;
             dG[i] += add;
-            sR1[r][c] = dG[i];
-            sR2[r][c] = dbr[i];
+            sR[r][cl] = dbr[i];
             if (r < nvalid) {
                 dqo[tok0 * DK + r * rsK + c] = f32_to_bf16(dq[i]);
                 dko[tok0 * DK + r * rsK + c] = f32_to_bf16(dk[i]);
@@ -1643,27 +1640,56 @@ bchunk2b_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         }
     }
     __syncthreads();
-    // dbeta (and dg per head): row sums over the channels, 8 threads per row
+    // dbeta partial: row sums of dbr over this half's channels, 4 threads per row
     {
-        const int r = tid >> 3, sub = tid & 7;
-        float sb = 0.f, sg = 0.f;
+        const int r = tid >> 2, sub = tid & 3;
+        float sb = 0.f;
         if (r < C) {
 #pragma unroll
-            for (int cc = sub; cc < DK; cc += 8) {
-                sb += sR2[r][cc];
-                if (!PCH) sg += sR1[r][cc];
-            }
+            for (int cc = sub; cc < HC; cc += 4) sb += sR[r][cc];
         }
-#pragma unroll
-        for (int off = 1; off < 8; off <<= 1) {
-            sb += __shfl_xor(sb, off);
-            if (!PCH) sg += __shfl_xor(sg, off);
-        }
-        if (r < nvalid && sub == 0) {
-            dbo[tok0 + (size_t)r * H] = sb + dbpi[(size_t)ch * C + r];
-            if (!PCH) dgo[tok0 + (size_t)r * H] = sg;
-        }
+        sb += __shfl_xor(sb, 1);
+        sb += __shfl_xor(sb, 2);
+        if (r < C && sub == 0) dbq[((size_t)ch * 2 + half) * C + r] = sb;
     }
+    if (!PCH) {
+        // per-head decay: dg of a row is the sum of dG over all channels
+        __syncthreads();
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) sR[p0 + i][cl] = dG[i];
+        }
+        __syncthreads();
+        const int r = tid >> 2, sub = tid & 3;
+        float sg = 0.f;
+        if (r < C) {
+#pragma unroll
+            for (int cc = sub; cc < HC; cc += 4) sg += sR[r][cc];
+        }
+        sg += __shfl_xor(sg, 1);
+        sg += __shfl_xor(sg, 2);
+        if (r < C && sub == 0) dgq[((size_t)ch * 2 + half) * C + r] = sg;
+    }
+}
+
+// dbeta = (part through U, from bchunk1b) + the two channel halves' partials;
+// for per-head decay also dg = sum of the two halves.  Fixed order: repeatable.
+template <bool PCH>
+__global__ void __launch_bounds__(256)
+bchunk2_finish_kernel(const float* __restrict__ dbpi, const float* __restrict__ dbq,
+                      const float* __restrict__ dgq, float* __restrict__ dbo,
+                      float* __restrict__ dgo, int T, int H, int NC, int C, long long total)
+{
+    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= total) return;
+    const int r = (int)(e % C);
+    const long long ch = e / C;
+    const int n = (int)(ch % NC), bh = (int)(ch / NC), h = bh % H, b = bh / H;
+    const int t = n * C + r;
+    if (t >= T) return;
+    const size_t tok = ((size_t)b * T + t) * H + h;
+    dbo[tok] = dbpi[ch * C + r] + dbq[(ch * 2) * C + r] + dbq[(ch * 2 + 1) * C + r];
+    if (!PCH) dgo[tok] = dgq[(ch * 2) * C + r] + dgq[(ch * 2 + 1) * C + r];
 }
 
 // ---------------------------------------------------------------------------
@@ -1703,7 +1729,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
     if constexpr (bf16_tables<TIn, C, DK>()) {
         GDN_LAUNCH("bchunk1", (bchunk1b_kernel<C, DK, DV>), gch, dim3(NTHR_C), st, (const bf16*)v,
                    beta, (const bf16*)dO, (const bf16*)(ws + p.o_Dst), (const float*)(ws + p.o_U),
-                   (const float*)(ws + p.o_Tm),
+                   (const float*)(ws + p.o_Tm), (const bf16*)(ws + p.o_W),
                    (const float*)(ws + p.o_Sst), (const float*)(ws + p.o_dSt),
                    (const float*)(ws + p.o_dDt), (bf16*)dv, (float*)(ws + p.o_dQg),
                    (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh), (float*)(ws + p.o_dPs),
@@ -1720,23 +1746,33 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                        p.H, p.NC);
     GDN_HIP_CHECK_LAUNCH();
     if constexpr (bf16_tables<TIn, C, DK>()) {
-        // dT1 holds G1 = dX_V U^T here (bchunk1b)
+        // here the dW region holds dX_K and the dT1 region dA (bchunk1b)
+        const int nch = (int)p.n_ch;
+        dim3 g2((unsigned)(((p.n_ch + 7) / 8) * 16));
         if (p.decay == GDN_DECAY_PER_CHANNEL)
-            GDN_LAUNCH("bchunk2", (bchunk2b_kernel<C, DK, true>), gch, dim3(NTHR_E), st,
-                       (const bf16*)q, (const bf16*)k, g, beta, (const float*)(ws + p.o_Tm),
-                       (const bf16*)(ws + p.o_W), (const bf16*)(ws + p.o_dQg),
+            GDN_LAUNCH("bchunk2", (bchunk2c_kernel<C, DK, true>), g2, dim3(NTHR_F), st,
+                       (const bf16*)q, (const bf16*)k, g, beta, (const bf16*)(ws + p.o_dQg),
                        (const bf16*)(ws + p.o_dWg), (const bf16*)(ws + p.o_dKh),
                        (const bf16*)(ws + p.o_dPs), (const bf16*)(ws + p.o_dT1),
-                       (const float*)(ws + p.o_dgm), (const float*)(ws + p.o_dbp), (bf16*)dq,
-                       (bf16*)dk, dg, dbeta, p.T, p.H, p.NC, p.scale);
+                       (const float*)(ws + p.o_dgm), (bf16*)dq, (bf16*)dk, dg,
+                       (float*)(ws + p.o_dbq), (float*)(ws + p.o_dgq), p.T, p.H, p.NC, nch, p.scale);
         else
-            GDN_LAUNCH("bchunk2", (bchunk2b_kernel<C, DK, false>), gch, dim3(NTHR_E), st,
-                       (const bf16*)q, (const bf16*)k, g, beta, (const float*)(ws + p.o_Tm),
-                       (const bf16*)(ws + p.o_W), (const bf16*)(ws + p.o_dQg),
+            GDN_LAUNCH("bchunk2", (bchunk2c_kernel<C, DK, false>), g2, dim3(NTHR_F), st,
+                       (const bf16*)q, (const bf16*)k, g, beta, (const bf16*)(ws + p.o_dQg),
                        (const bf16*)(ws + p.o_dWg), (const bf16*)(ws + p.o_dKh),
                        (const bf16*)(ws + p.o_dPs), (const bf16*)(ws + p.o_dT1),
-                       (const float*)(ws + p.o_dgm), (const float*)(ws + p.o_dbp), (bf16*)dq,
-                       (bf16*)dk, dg, dbeta, p.T, p.H, p.NC, p.scale);
+                       (const float*)(ws + p.o_dgm), (bf16*)dq, (bf16*)dk, dg,
+                       (float*)(ws + p.o_dbq), (float*)(ws + p.o_dgq), p.T, p.H, p.NC, nch, p.scale);
+        const long long tot = (long long)p.n_ch * C;
+        dim3 gf((unsigned)((tot + 255) / 256));
+        if (p.decay == GDN_DECAY_PER_CHANNEL)
+            GDN_LAUNCH("bchunk2_finish", (bchunk2_finish_kernel<true>), gf, dim3(256), st,
+                       (const float*)(ws + p.o_dbp), (const float*)(ws + p.o_dbq),
+                       (const float*)(ws + p.o_dgq), dbeta, dg, p.T, p.H, p.NC, C, tot);
+        else
+            GDN_LAUNCH("bchunk2_finish", (bchunk2_finish_kernel<false>), gf, dim3(256), st,
+                       (const float*)(ws + p.o_dbp), (const float*)(ws + p.o_dbq),
+                       (const float*)(ws + p.o_dgq), dbeta, dg, p.T, p.H, p.NC, C, tot);
         return GDN_OK;
     }
     if (p.decay == GDN_DECAY_PER_CHANNEL)

@@ -2,8 +2,8 @@
 //
 // The chunked form processes each (batch, head) sequence in chunks of C
 // tokens; NC = ceil(T / C).  A chunk-head is one chunk of one (b, h); its
-// index is ch = (b * H + h) * NC + n.  All workspace arrays are float32 and
-// indexed by chunk-head:
+// index is ch = (b * H + h) * NC + n.  Workspace arrays are float32 unless noted
+// below, indexed by chunk-head:
 //   W   [ch][C][Dk]   W  = T diag(beta) (K o Gamma)        (WY form of the solve)
 //   U   [ch][C][Dv]   U  = T diag(beta) V
 //   Qg  [ch][C][Dk]   Qg = scale * (Q o Gamma)             (query read of the carried state)
@@ -19,6 +19,13 @@
 //   dPs [ch][C][C]    dL/dPs,  dT1 [ch][C][C]  dL/dT through U
 //   dgm [ch][Dk]      dL/dgam, dbp [ch][C]     part of dL/dbeta (through U)
 //   Dst [ch][C][Dv]   the chunk deltas D (bf16; bf16 inputs at chunk 64 only)
+//   dbq [ch][2][C]    per channel-half partial dbeta, dgq [ch][2][C] partial
+//                     per-head dg (bf16 inputs at chunk 64)
+// With bf16 inputs at chunk 64 the tables W, Qg, Kh, Ps are bf16 and each
+// region holds two of them (the second, transposed or row-major, for the
+// backward scan), and the backward's hand-offs are bf16 too: dQg, dKh, dPs;
+// the dW region holds dX_K = T^T dW and the dT1 region the strictly lower
+// dA = -(dX_V U^T + dX_K W^T).
 // G is the chunk-local inclusive cumulative log-decay and Gamma = exp(G).
 #pragma once
 
@@ -35,7 +42,7 @@ struct Plan {
     size_t n_ch;  // B * H * NC
     // byte offsets into the workspace
     size_t o_W, o_U, o_Qg, o_Kh, o_Ps, o_gam, o_Tm, o_Sst, o_dSt, o_dDt;
-    size_t o_dQg, o_dWg, o_dKh, o_dPs, o_dT1, o_dgm, o_dbp, o_Dst;
+    size_t o_dQg, o_dWg, o_dKh, o_dPs, o_dT1, o_dgm, o_dbp, o_Dst, o_dbq, o_dgq;
     size_t ws_fwd_bytes, ws_bwd_bytes;
 };
 
@@ -78,6 +85,8 @@ inline Plan make_plan(const gdn_shape& s, float scale)
     p.o_dgm = off; off = align256(off + n * Dk * f);
     p.o_dbp = off; off = align256(off + n * C * f);
     p.o_Dst = off; off = align256(off + n * C * Dv * 2);
+    p.o_dbq = off; off = align256(off + n * 2 * C * f);
+    p.o_dgq = off; off = align256(off + n * 2 * C * f);
     p.ws_bwd_bytes = off;
     return p;
 }
