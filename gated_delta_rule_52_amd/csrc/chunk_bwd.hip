@@ -173,7 +173,7 @@ bscan_kernel(const float* __restrict__ Qgi, const float* __restrict__ Khi,
 constexpr int NTHR_B = 512;
 
 template <int C, int DK, int DV>
-__global__ void __launch_bounds__(NTHR_B)
+__global__ void __launch_bounds__(NTHR_B) __attribute__((amdgpu_waves_per_eu(1, 2)))
 bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
               const bf16* __restrict__ QgTb, const bf16* __restrict__ WTb,
               const float* __restrict__ gami, const bf16* __restrict__ dO,
@@ -184,8 +184,18 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
     constexpr int PA = DK + 8, PT = C + 8;
     constexpr int TD = (C / 16) * (BV / 16), TS = (DK / 16) * (BV / 16);
     constexpr int MD = (TD + NW - 1) / NW, MS = (TS + NW - 1) / NW;
+    // 16-byte words of one chunk's tables, whole multiples of the thread count
+    // (branch-free prefetch: the compiler waits exactly for it, not for the
+    // stores issued after it); the dO slice has QO <= NTHR_B words
     constexpr int QP = C * C / 8, QW = C * DK / 8, QK = DK * C / 8, QO = C * BV / 8;
     constexpr int QALL = QP + QW + 2 * QK + QO, QPT = (QALL + NTHR_B - 1) / NTHR_B;
+    // every table is a whole number of words per thread (the dO slice fills part
+    // of the last slot), so the table of word slot q is known at compile time and
+    // the prefetch has no branches: the compiler then waits exactly for it, not
+    // also for the stores issued after it
+    static_assert(QP % NTHR_B == 0 && QW % NTHR_B == 0 && QK % NTHR_B == 0 && QO <= NTHR_B, "");
+    static_assert(QP + QW + 2 * QK == (QPT - 1) * NTHR_B, "dO in the last slot");
+    static_assert(TD % NW == 0 && TS % NW == 0, "tile split");
     __shared__ __align__(16) bf16 sPT[C][PT], sK[C][PA], sQT[DK][PT], sWT[DK][PT], sdSt[BV][PA],
         sdOt[BV][PT], sdDt[BV][PT];
 
@@ -221,46 +231,43 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
         for (int q = 0; q < QPT; ++q) {
             const int idx = tid + NTHR_B * q;
             uint4 val = uint4{0u, 0u, 0u, 0u};
-            if (idx < QP) {
+            if (q * NTHR_B < QP) {
                 val = reinterpret_cast<const uint4*>(PsTb + ch * C * C)[idx];
-            } else if (idx < QP + QW) {
+            } else if (q * NTHR_B < QP + QW) {
                 val = reinterpret_cast<const uint4*>(Khb + ch * C * DK)[idx - QP];
-            } else if (idx < QP + QW + QK) {
+            } else if (q * NTHR_B < QP + QW + QK) {
                 val = reinterpret_cast<const uint4*>(QgTb + ch * C * DK)[idx - QP - QW];
-            } else if (idx < QP + QW + 2 * QK) {
+            } else if (q * NTHR_B < QP + QW + 2 * QK) {
                 val = reinterpret_cast<const uint4*>(WTb + ch * C * DK)[idx - QP - QW - QK];
-            } else if (idx < QALL) {
-                const int e = idx - QP - QW - 2 * QK;
+            } else {  // dO slice: rows past the end (or threads past the slice) repeat a valid word, then zero
+                const int e = min(idx - QP - QW - 2 * QK, QO - 1);
                 const int r = e / (BV / 8), j0 = (e % (BV / 8)) * 8;
                 const int t = n * C + r;
-                if (t < T)
-                    val = *reinterpret_cast<const uint4*>(dO + (((size_t)b * T + t) * H + h) * DV + v0 + j0);
+                const uint4 ov = *reinterpret_cast<const uint4*>(dO + (((size_t)b * T + min(t, T - 1)) * H + h) * DV + v0 + j0);
+                val = t < T ? ov : uint4{0u, 0u, 0u, 0u};
             }
             pf[q] = val;
         }
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
-            const int idx = w + NW * m;
-            if (idx < TS) {
-                const int si = idx / (BV / 16);
+            const int si = (w + NW * m) / (BV / 16);  // w + NW m < TS for every wave
 #pragma unroll
-                for (int r = 0; r < 4; ++r) gpf[m][r] = gami[ch * DK + si * 16 + 4 * lq + r];
-            }
+            for (int r = 0; r < 4; ++r) gpf[m][r] = gami[ch * DK + si * 16 + 4 * lq + r];
         }
     };
     auto stash = [&]() {
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
             const int idx = tid + NTHR_B * q;
-            if (idx < QP) {
+            if (q * NTHR_B < QP) {
                 *reinterpret_cast<uint4*>(&sPT[idx / (C / 8)][(idx % (C / 8)) * 8]) = pf[q];
-            } else if (idx < QP + QW) {
+            } else if (q * NTHR_B < QP + QW) {
                 const int e = idx - QP;
                 *reinterpret_cast<uint4*>(&sK[e / (DK / 8)][(e % (DK / 8)) * 8]) = pf[q];
-            } else if (idx < QP + QW + QK) {
+            } else if (q * NTHR_B < QP + QW + QK) {
                 const int e = idx - QP - QW;
                 *reinterpret_cast<uint4*>(&sQT[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
-            } else if (idx < QP + QW + 2 * QK) {
+            } else if (q * NTHR_B < QP + QW + 2 * QK) {
                 const int e = idx - QP - QW - QK;
                 *reinterpret_cast<uint4*>(&sWT[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
             } else if (idx < QALL) {  // dO row r, columns j0..j0+7 -> dO^T

@@ -867,9 +867,14 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
     constexpr int PA = DK + 8, PT = C + 8;  // bf16 pitches: rows 16-byte aligned, banks spread
     constexpr int TD = (C / 16) * (BV / 16), TS = (DK / 16) * (BV / 16);
     constexpr int MD = (TD + NW - 1) / NW, MS = (TS + NW - 1) / NW;
-    // 16-byte words of one chunk's tables
+    // 16-byte words of one chunk's tables.  Each table is a whole number of words
+    // per thread, so the table of word slot q is known at compile time and the
+    // prefetch has no branches: the compiler then waits exactly for it, not also
+    // for the state and output stores issued after it.
     constexpr int QW = C * DK / 8, QK = DK * C / 8, QP = C * C / 8;
     constexpr int QALL = 2 * QW + QK + QP, QPT = (QALL + NTHR_S - 1) / NTHR_S;
+    static_assert(QW % NTHR_S == 0 && QK % NTHR_S == 0 && QP % NTHR_S == 0, "table split");
+    static_assert(TD % NW == 0 && TS % NW == 0, "tile split");
     __shared__ __align__(16) bf16 sW[C][PA], sQ[C][PA], sKT[DK][PT], sP[C][PT], sSt[BV][PA], sDt[BV][PT];
 
     const int x = blockIdx.x;
@@ -905,16 +910,16 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         for (int q = 0; q < QPT; ++q) {
             const int idx = tid + NTHR_S * q;
             uint4 val = uint4{0u, 0u, 0u, 0u};
-            if (idx < QW) val = reinterpret_cast<const uint4*>(Wb + ch * C * DK)[idx];
-            else if (idx < 2 * QW) val = reinterpret_cast<const uint4*>(Qgb + ch * C * DK)[idx - QW];
-            else if (idx < 2 * QW + QK) val = reinterpret_cast<const uint4*>(KhTb + ch * C * DK)[idx - 2 * QW];
-            else if (idx < QALL) val = reinterpret_cast<const uint4*>(Psb + ch * C * C)[idx - 2 * QW - QK];
+            if (q * NTHR_S < QW) val = reinterpret_cast<const uint4*>(Wb + ch * C * DK)[idx];
+            else if (q * NTHR_S < 2 * QW) val = reinterpret_cast<const uint4*>(Qgb + ch * C * DK)[idx - QW];
+            else if (q * NTHR_S < 2 * QW + QK) val = reinterpret_cast<const uint4*>(KhTb + ch * C * DK)[idx - 2 * QW];
+            else val = reinterpret_cast<const uint4*>(Psb + ch * C * C)[idx - 2 * QW - QK];
             pf[q] = val;
         }
 #pragma unroll
         for (int m = 0; m < MD; ++m) {
-            const int idx = w + NW * m;
-            if (idx < TD) {
+            const int idx = w + NW * m;  // < TD for every wave
+            {
                 const int ti = idx / (BV / 16), tj = idx % (BV / 16);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -923,27 +928,24 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         }
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
-            const int idx = w + NW * m;
-            if (idx < TS) {
-                const int si = idx / (BV / 16);
+            const int si = (w + NW * m) / (BV / 16);  // w + NW m < TS for every wave
 #pragma unroll
-                for (int r = 0; r < 4; ++r) gpf[m][r] = gami[ch * DK + si * 16 + 4 * lq + r];
-            }
+            for (int r = 0; r < 4; ++r) gpf[m][r] = gami[ch * DK + si * 16 + 4 * lq + r];
         }
     };
     auto stash = [&]() {  // registers -> LDS tables
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
             const int idx = tid + NTHR_S * q;
-            if (idx < QW) {
+            if (q * NTHR_S < QW) {
                 *reinterpret_cast<uint4*>(&sW[idx / (DK / 8)][(idx % (DK / 8)) * 8]) = pf[q];
-            } else if (idx < 2 * QW) {
+            } else if (q * NTHR_S < 2 * QW) {
                 const int e = idx - QW;
                 *reinterpret_cast<uint4*>(&sQ[e / (DK / 8)][(e % (DK / 8)) * 8]) = pf[q];
-            } else if (idx < 2 * QW + QK) {
+            } else if (q * NTHR_S < 2 * QW + QK) {
                 const int e = idx - 2 * QW;
                 *reinterpret_cast<uint4*>(&sKT[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
-            } else if (idx < QALL) {
+            } else {
                 const int e = idx - 2 * QW - QK;
                 *reinterpret_cast<uint4*>(&sP[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
             }
@@ -962,73 +964,53 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
     __syncthreads();
 
+    // Each step's global stores (chunk-start state, deltas, outputs) are issued
+    // after the step's prefetch wait (measured fastest: issued before it, the
+    // wait also covers them, as loads and stores share one counter).
     for (int n = 0; n < NC; ++n) {
         const size_t ch = (size_t)bh * NC + n;
         if (n + 1 < NC) fetch(n + 1);
+        f32x4 s0[MS];  // state at the start of the chunk (saved for the backward)
         if (SAVE) {
 #pragma unroll
-            for (int m = 0; m < MS; ++m) {
-                const int idx = w + NW * m;
-                if (idx < TS) {
-                    const int si = idx / (BV / 16), sj = idx % (BV / 16);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        Sst[(ch * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = sacc[m][r];
-                }
-            }
+            for (int m = 0; m < MS; ++m) s0[m] = sacc[m];
         }
         // D = U - W S  and  O1 = Qg S
         f32x4 o1[MD];
+        uint2 dpk[MD];  // D as bf16 (table for the state update; saved for the backward)
 #pragma unroll
         for (int m = 0; m < MD; ++m) {
             const int idx = w + NW * m;
-            if (idx < TD) {
-                const int ti = idx / (BV / 16), tj = idx % (BV / 16);
-                f32x4 ws = mma_kc<DK>(zero4(), &sW[ti * 16][0], PA, &sSt[tj * 16][0], PA);
-                float dv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dv[r] = uc[m][r] - ws[r];
-                if (SAVE) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        Dst[(ch * C + ti * 16 + 4 * lq + r) * DV + v0 + tj * 16 + lr] = f32_to_bf16(dv[r]);
-                }
-                *reinterpret_cast<uint2*>(&sDt[tj * 16 + lr][ti * 16 + 4 * lq]) =
-                    pack4_bf16(dv[0], dv[1], dv[2], dv[3]);
-                if (OUT) o1[m] = mma_kc<DK>(zero4(), &sQ[ti * 16][0], PA, &sSt[tj * 16][0], PA);
-            }
+            const int ti = idx / (BV / 16), tj = idx % (BV / 16);
+            f32x4 ws = mma_kc<DK>(zero4(), &sW[ti * 16][0], PA, &sSt[tj * 16][0], PA);
+            dpk[m] = pack4_bf16(uc[m][0] - ws[0], uc[m][1] - ws[1], uc[m][2] - ws[2], uc[m][3] - ws[3]);
+            *reinterpret_cast<uint2*>(&sDt[tj * 16 + lr][ti * 16 + 4 * lq]) = dpk[m];
+            if (OUT) o1[m] = mma_kc<DK>(zero4(), &sQ[ti * 16][0], PA, &sSt[tj * 16][0], PA);
         }
         __syncthreads();
+        uint2 opk[MD];  // outputs as bf16
         if (OUT) {
 #pragma unroll
             for (int m = 0; m < MD; ++m) {
                 const int idx = w + NW * m;
-                if (idx < TD) {
-                    const int ti = idx / (BV / 16), tj = idx % (BV / 16);
-                    // P is lower triangular: columns past the tile row are zero
-                    const int K = ((16 * (ti + 1) + 31) / 32) * 32;
-                    f32x4 acc = mma_kc_dyn(o1[m], &sP[ti * 16][0], PT, &sDt[tj * 16][0], PT, K);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = n * C + ti * 16 + 4 * lq + r;
-                        if (t < T) o[(((size_t)b * T + t) * H + h) * DV + v0 + tj * 16 + lr] = f32_to_bf16(acc[r]);
-                    }
-                }
+                const int ti = idx / (BV / 16), tj = idx % (BV / 16);
+                // P is lower triangular: columns past the tile row are zero
+                const int K = ((16 * (ti + 1) + 31) / 32) * 32;
+                const f32x4 acc = mma_kc_dyn(o1[m], &sP[ti * 16][0], PT, &sDt[tj * 16][0], PT, K);
+                opk[m] = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
             }
         }
         // S <- gam o S + Kh^T D
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
             const int idx = w + NW * m;
-            if (idx < TS) {
-                const int si = idx / (BV / 16), sj = idx % (BV / 16);
-                f32x4 acc;
+            const int si = idx / (BV / 16), sj = idx % (BV / 16);
+            f32x4 acc;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = gc[m][r] * sacc[m][r];
-                sacc[m] = mma_kc<C>(acc, &sKT[si * 16][0], PT, &sDt[sj * 16][0], PT);
-                *reinterpret_cast<uint2*>(&sSt[sj * 16 + lr][si * 16 + 4 * lq]) =
-                    pack4_bf16(sacc[m][0], sacc[m][1], sacc[m][2], sacc[m][3]);
-            }
+            for (int r = 0; r < 4; ++r) acc[r] = gc[m][r] * sacc[m][r];
+            sacc[m] = mma_kc<C>(acc, &sKT[si * 16][0], PT, &sDt[sj * 16][0], PT);
+            *reinterpret_cast<uint2*>(&sSt[sj * 16 + lr][si * 16 + 4 * lq]) =
+                pack4_bf16(sacc[m][0], sacc[m][1], sacc[m][2], sacc[m][3]);
         }
         __syncthreads();
         if (n + 1 < NC) {
@@ -1043,6 +1025,34 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
         }
         __syncthreads();
+        // this step's stores
+        if (SAVE) {
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int idx = w + NW * m;
+                const int si = idx / (BV / 16), sj = idx % (BV / 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Sst[(ch * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = s0[m][r];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            const int idx = w + NW * m;
+            const int ti = idx / (BV / 16), tj = idx % (BV / 16);
+            const uint32_t dw[2] = {dpk[m].x, dpk[m].y}, ow[2] = {opk[m].x, opk[m].y};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + 4 * lq + r;
+                const uint16_t db = (uint16_t)((r & 1) ? (dw[r >> 1] >> 16) : (dw[r >> 1] & 0xFFFFu));
+                if (SAVE) Dst[(ch * C + i) * DV + v0 + tj * 16 + lr].bits = db;
+                if (OUT) {
+                    const int t = n * C + i;
+                    const uint16_t ob = (uint16_t)((r & 1) ? (ow[r >> 1] >> 16) : (ow[r >> 1] & 0xFFFFu));
+                    if (t < T) o[(((size_t)b * T + t) * H + h) * DV + v0 + tj * 16 + lr].bits = ob;
+                }
+            }
+        }
     }
     if (hT) {
 #pragma unroll
