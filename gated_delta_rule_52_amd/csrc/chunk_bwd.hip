@@ -256,6 +256,9 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
         }
     };
     auto stash = [&]() {
+        // keep the use of the prefetched words here: hoisted into the compute
+        // phase they would make it wait for the prefetch
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
             const int idx = tid + NTHR_B * q;
@@ -573,6 +576,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     constexpr int O_Xh = O_W + C * PK * 2, O_Xl = O_Xh + C * PK * 2, ENDP = O_Xl + C * PK * 2;
     __shared__ __align__(16) char sbuf[cmax(STREAM, ENDP)];
     __shared__ __align__(16) float sT[C][PC];
+    __shared__ __align__(16) bf16 sDV[C][DV + 8];  // dv, written out after the Dv loop
     __shared__ float sbeta[C], sred[NW][C];
     bf16 (*sS)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf);
     bf16 (*sdS)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_dS);
@@ -612,71 +616,66 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     const bf16* Dp = Dst + (size_t)ch * C * DV;
     const float* Up = Ui + (size_t)ch * C * DV;
 
+    // Prefetch of one Dv tile, branch-free (a load under a divergent branch makes
+    // the compiler wait for it where the branches join): every thread loads two
+    // S words, two dS words, one dD and one U word, one D-or-dO word and one v
+    // word; rows past the end are clamped on load and zeroed in stash().
+    static_assert(NS4 == QS * NTHR_C && ND4 == NTHR_C && NB8 == NTHR_C / 2, "tile split");
     float4 pS[QS], pdS[QS], pdD, pU;
-    uint4 pa, pb;  // threads < 256: D and v; threads >= 256: dO
+    uint4 pa, pb;  // threads < NB8: D and v words; threads >= NB8: dO word (and an unused v word)
+    const bool lowh = tid < NB8;
+    const int e8 = lowh ? tid : tid - NB8;
+    const int r8 = e8 / (BW / 8), j8 = (e8 % (BW / 8)) * 8;
+    const bool row8 = r8 < nvalid;
+    const size_t tokr = (tok0 + (size_t)min(r8, nvalid - 1) * H) * DV;
+    const int rd = tid / (BW / 4), jd = (tid % (BW / 4)) * 4;  // dD / U word of this thread
     auto fetch = [&](int v0) {
 #pragma unroll
         for (int q = 0; q < QS; ++q) {
             const int idx = tid + NTHR_C * q;
-            if (idx < NS4) {
-                const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
-                pS[q] = load4<float>(Sp + i * DV + v0 + j4);
-                pdS[q] = load4<float>(dSp + i * DV + v0 + j4);
-            }
+            const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
+            pS[q] = load4<float>(Sp + i * DV + v0 + j4);
+            pdS[q] = load4<float>(dSp + i * DV + v0 + j4);
         }
-        if (tid < ND4) {
-            const int r = tid / (BW / 4), j4 = (tid % (BW / 4)) * 4;
-            pdD = load4<float>(dDp + r * DV + v0 + j4);
-            pU = load4<float>(Up + r * DV + v0 + j4);
-        }
-        pa = pb = uint4{0u, 0u, 0u, 0u};
-        if (tid < NB8) {
-            const int r = tid / (BW / 8), j0 = (tid % (BW / 8)) * 8;
-            pa = *reinterpret_cast<const uint4*>(Dp + r * DV + v0 + j0);
-            if (r < nvalid) pb = *reinterpret_cast<const uint4*>(v + (tok0 + (size_t)r * H) * DV + v0 + j0);
-        } else if (tid >= NTHR_C / 2 && tid - NTHR_C / 2 < NB8) {
-            const int e = tid - NTHR_C / 2;
-            const int r = e / (BW / 8), j0 = (e % (BW / 8)) * 8;
-            if (r < nvalid) pa = *reinterpret_cast<const uint4*>(dO + (tok0 + (size_t)r * H) * DV + v0 + j0);
-        }
+        pdD = load4<float>(dDp + rd * DV + v0 + jd);
+        pU = load4<float>(Up + rd * DV + v0 + jd);
+        const bf16* src = lowh ? Dp + r8 * DV + v0 + j8 : dO + tokr + v0 + j8;
+        pa = *reinterpret_cast<const uint4*>(src);
+        pb = *reinterpret_cast<const uint4*>(v + tokr + v0 + j8);
     };
     float dgm_part[QS];
 #pragma unroll
     for (int q = 0; q < QS; ++q) dgm_part[q] = 0.f;
     auto stash = [&]() {
+        // keep the use of the prefetched words here: hoisted into the compute
+        // phase they would make it wait for the prefetch
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < QS; ++q) {
             const int idx = tid + NTHR_C * q;
-            if (idx < NS4) {
-                const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
-                const float4 a4 = pS[q], d4 = pdS[q];
-                dgm_part[q] += a4.x * d4.x + a4.y * d4.y + a4.z * d4.z + a4.w * d4.w;
-                *reinterpret_cast<uint2*>(&sS[i][j4]) = pack4_bf16(a4.x, a4.y, a4.z, a4.w);
-                *reinterpret_cast<uint2*>(&sdS[i][j4]) = pack4_bf16(d4.x, d4.y, d4.z, d4.w);
-            }
+            const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
+            const float4 a4 = pS[q], d4 = pdS[q];
+            dgm_part[q] += a4.x * d4.x + a4.y * d4.y + a4.z * d4.z + a4.w * d4.w;
+            *reinterpret_cast<uint2*>(&sS[i][j4]) = pack4_bf16(a4.x, a4.y, a4.z, a4.w);
+            *reinterpret_cast<uint2*>(&sdS[i][j4]) = pack4_bf16(d4.x, d4.y, d4.z, d4.w);
         }
-        if (tid < ND4) {
-            const int r = tid / (BW / 4), j4 = (tid % (BW / 4)) * 4;
-            st4(&sdDf[r][j4], pdD);
-            *reinterpret_cast<uint2*>(&sdD[r][j4]) = pack4_bf16(pdD.x, pdD.y, pdD.z, pdD.w);
-            *reinterpret_cast<uint2*>(&sU[r][j4]) = pack4_bf16(pU.x, pU.y, pU.z, pU.w);
-        }
-        if (tid < NB8) {
-            const int r = tid / (BW / 8), j0 = (tid % (BW / 8)) * 8;
-            *reinterpret_cast<uint4*>(&sD[r][j0]) = pa;
-            const uint32_t u[4] = {pb.x, pb.y, pb.z, pb.w};
+        st4(&sdDf[rd][jd], pdD);
+        *reinterpret_cast<uint2*>(&sdD[rd][jd]) = pack4_bf16(pdD.x, pdD.y, pdD.z, pdD.w);
+        *reinterpret_cast<uint2*>(&sU[rd][jd]) = pack4_bf16(pU.x, pU.y, pU.z, pU.w);
+        if (lowh) {
+            *reinterpret_cast<uint4*>(&sD[r8][j8]) = pa;
+            const uint4 vb = row8 ? pb : uint4{0u, 0u, 0u, 0u};
+            const uint32_t u[4] = {vb.x, vb.y, vb.z, vb.w};
             float vv[8];
 #pragma unroll
             for (int z = 0; z < 4; ++z) {
                 vv[2 * z] = __uint_as_float(u[z] << 16);
                 vv[2 * z + 1] = __uint_as_float(u[z] & 0xFFFF0000u);
             }
-            st4(&sv[r][j0], float4{vv[0], vv[1], vv[2], vv[3]});
-            st4(&sv[r][j0 + 4], float4{vv[4], vv[5], vv[6], vv[7]});
-        } else if (tid >= NTHR_C / 2 && tid - NTHR_C / 2 < NB8) {
-            const int e = tid - NTHR_C / 2;
-            const int r = e / (BW / 8), j0 = (e % (BW / 8)) * 8;
-            *reinterpret_cast<uint4*>(&sdO[r][j0]) = pa;
+            st4(&sv[r8][j8], float4{vv[0], vv[1], vv[2], vv[3]});
+            st4(&sv[r8][j8 + 4], float4{vv[4], vv[5], vv[6], vv[7]});
+        } else {
+            *reinterpret_cast<uint4*>(&sdO[r8][j8]) = row8 ? pa : uint4{0u, 0u, 0u, 0u};
         }
     };
 
@@ -691,21 +690,24 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 #pragma unroll
         for (int r = 0; r < 4; ++r) dbr[m][r] = 0.f;
 
+    constexpr int NK8 = (C * DK / 8 + NTHR_C - 1) / NTHR_C;
+    uint4 wv[NK8];  // W rows (bf16) for the keys' WY adjoint after the Dv loop
+    {
+        const bf16* Wp = Wbi + (size_t)ch * C * DK;
+#pragma unroll
+        for (int u = 0; u < NK8; ++u)
+            wv[u] = *reinterpret_cast<const uint4*>(Wp + 8 * min(tid + NTHR_C * u, C * DK / 8 - 1));
+    }
     __syncthreads();  // sbeta ready for the first stash
     fetch(0);
     stash();
     __syncthreads();
-    constexpr int NK8 = (C * DK / 8 + NTHR_C - 1) / NTHR_C;
-    uint4 wv[NK8];  // W rows (bf16), fetched while the last Dv tile is processed
-    for (int v0 = 0; v0 < DV; v0 += BW) {
-        if (v0 + BW < DV) {
-            fetch(v0 + BW);
-        } else {
-            const bf16* Wp = Wbi + (size_t)ch * C * DK;
-#pragma unroll
-            for (int u = 0; u < NK8; ++u)
-                wv[u] = *reinterpret_cast<const uint4*>(Wp + 8 * min(tid + NTHR_C * u, C * DK / 8 - 1));
-        }
+    // one Dv tile; the last one is peeled (MORE = false) so that the prefetch and
+    // its stash need no run-time guard: with one, the compiler cannot match the
+    // two and waits for every outstanding load and store at the top of the loop
+    auto tile = [&](int v0, auto more_c) {
+        constexpr bool MORE = decltype(more_c)::value;
+        if constexpr (MORE) fetch(v0 + BW);
         // dX_V = T^T dD (fp32): dv = beta dX_V, and <dX_V, v> for dbeta
 #pragma unroll
         for (int m = 0; m < MD; ++m) {
@@ -716,7 +718,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                    if (i < nvalid) dvo[(tok0 + (size_t)i * H) * DV + v0 + j] = f32_to_bf16(sbeta[i] * dx[r]);
+                    sDV[i][v0 + j] = f32_to_bf16(sbeta[i] * dx[r]);
                     dbr[m][r] += dx[r] * sv[i][j];
                     sdX[i][j] = f32_to_bf16(dx[r]);
                 }
@@ -750,10 +752,22 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             }
         }
         __syncthreads();
-        if (v0 + BW < DV) stash();
-        __syncthreads();
-    }
+        if constexpr (MORE) {
+            stash();
+            __syncthreads();
+        }
+    };
+    for (int v0 = 0; v0 + BW < DV; v0 += BW) tile(v0, std::true_type{});
+    tile(DV - BW, std::false_type{});
 
+    // dv out: the loop stores nothing to global memory (a store there would be
+    // waited for with the next prefetch)
+    for (int idx = tid; idx < C * DV / 8; idx += NTHR_C) {
+        const int r = idx / (DV / 8), c0 = (idx % (DV / 8)) * 8;
+        if (r < nvalid)
+            *reinterpret_cast<uint4*>(dvo + (tok0 + (size_t)r * H) * DV + c0) =
+                *reinterpret_cast<const uint4*>(&sDV[r][c0]);
+    }
     // outputs (bf16: the consumer reads them as gradients of bf16-rounded products)
     bf16* dQp = reinterpret_cast<bf16*>(dQgo) + (size_t)ch * C * DK;
     bf16* dKp = reinterpret_cast<bf16*>(dKho) + (size_t)ch * C * DK;

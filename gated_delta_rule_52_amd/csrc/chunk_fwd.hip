@@ -934,6 +934,9 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         }
     };
     auto stash = [&]() {  // registers -> LDS tables
+        // keep the use of the prefetched words here: hoisted into the compute
+        // phase they would make it wait for the prefetch
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
             const int idx = tid + NTHR_S * q;
