@@ -876,6 +876,11 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
     static_assert(QW % NTHR_S == 0 && QK % NTHR_S == 0 && QP % NTHR_S == 0, "table split");
     static_assert(TD % NW == 0 && TS % NW == 0, "tile split");
     __shared__ __align__(16) bf16 sW[C][PA], sQ[C][PA], sKT[DK][PT], sP[C][PT], sSt[BV][PA], sDt[BV][PT];
+    // staging of each step's outputs (double-buffered by step parity), written
+    // out with 16-byte stores: the next chunk's start state (fp32), D and o (bf16)
+    constexpr int PF = BV + 4, PO = BV + 8;
+    __shared__ __align__(16) float sSf[2][DK][PF];
+    __shared__ __align__(16) bf16 sDr[2][C][PO], sOr[2][C][PO];
 
     const int x = blockIdx.x;
     const int grp = x / (8 * NS), rem = x % (8 * NS);
@@ -967,31 +972,41 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
     __syncthreads();
 
-    // Each step's global stores (chunk-start state, deltas, outputs) are issued
-    // after the step's prefetch wait (measured fastest: issued before it, the
-    // wait also covers them, as loads and stores share one counter).
+    // Each step's outputs are staged in LDS and written with 16-byte stores after
+    // the step's prefetch wait (issued before it, the wait would also cover them:
+    // loads and stores share one counter).
+    if (SAVE) {  // chunk 0 starts from h0
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + NW * m;
+            const int si = idx / (BV / 16), sj = idx % (BV / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Sst[((size_t)bh * NC * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = sacc[m][r];
+        }
+    }
     for (int n = 0; n < NC; ++n) {
         const size_t ch = (size_t)bh * NC + n;
+        const int pb = n & 1;
         if (n + 1 < NC) fetch(n + 1);
-        f32x4 s0[MS];  // state at the start of the chunk (saved for the backward)
-        if (SAVE) {
-#pragma unroll
-            for (int m = 0; m < MS; ++m) s0[m] = sacc[m];
-        }
         // D = U - W S  and  O1 = Qg S
         f32x4 o1[MD];
-        uint2 dpk[MD];  // D as bf16 (table for the state update; saved for the backward)
 #pragma unroll
         for (int m = 0; m < MD; ++m) {
             const int idx = w + NW * m;
             const int ti = idx / (BV / 16), tj = idx % (BV / 16);
             f32x4 ws = mma_kc<DK>(zero4(), &sW[ti * 16][0], PA, &sSt[tj * 16][0], PA);
-            dpk[m] = pack4_bf16(uc[m][0] - ws[0], uc[m][1] - ws[1], uc[m][2] - ws[2], uc[m][3] - ws[3]);
-            *reinterpret_cast<uint2*>(&sDt[tj * 16 + lr][ti * 16 + 4 * lq]) = dpk[m];
+            float dv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dv[r] = uc[m][r] - ws[r];
+            *reinterpret_cast<uint2*>(&sDt[tj * 16 + lr][ti * 16 + 4 * lq]) = pack4_bf16(dv[0], dv[1], dv[2], dv[3]);
+            if (SAVE) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sDr[pb][ti * 16 + 4 * lq + r][tj * 16 + lr] = f32_to_bf16(dv[r]);
+            }
             if (OUT) o1[m] = mma_kc<DK>(zero4(), &sQ[ti * 16][0], PA, &sSt[tj * 16][0], PA);
         }
         __syncthreads();
-        uint2 opk[MD];  // outputs as bf16
         if (OUT) {
 #pragma unroll
             for (int m = 0; m < MD; ++m) {
@@ -1000,7 +1015,8 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 // P is lower triangular: columns past the tile row are zero
                 const int K = ((16 * (ti + 1) + 31) / 32) * 32;
                 const f32x4 acc = mma_kc_dyn(o1[m], &sP[ti * 16][0], PT, &sDt[tj * 16][0], PT, K);
-                opk[m] = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sOr[pb][ti * 16 + 4 * lq + r][tj * 16 + lr] = f32_to_bf16(acc[r]);
             }
         }
         // S <- gam o S + Kh^T D
@@ -1014,6 +1030,10 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             sacc[m] = mma_kc<C>(acc, &sKT[si * 16][0], PT, &sDt[sj * 16][0], PT);
             *reinterpret_cast<uint2*>(&sSt[sj * 16 + lr][si * 16 + 4 * lq]) =
                 pack4_bf16(sacc[m][0], sacc[m][1], sacc[m][2], sacc[m][3]);
+            if (SAVE) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sSf[pb][si * 16 + 4 * lq + r][sj * 16 + lr] = sacc[m][r];
+            }
         }
         __syncthreads();
         if (n + 1 < NC) {
@@ -1028,32 +1048,34 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
         }
         __syncthreads();
-        // this step's stores
-        if (SAVE) {
+        // this step's stores, from the staging: the start state of chunk n + 1,
+        // then D and o of chunk n (rows of BV contiguous elements)
+        if (SAVE && n + 1 < NC) {
+            constexpr int NF4 = DK * BV / 4;
 #pragma unroll
-            for (int m = 0; m < MS; ++m) {
-                const int idx = w + NW * m;
-                const int si = idx / (BV / 16), sj = idx % (BV / 16);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Sst[(ch * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = s0[m][r];
+            for (int u = 0; u < (NF4 + NTHR_S - 1) / NTHR_S; ++u) {
+                const int e = tid + NTHR_S * u;
+                if (e < NF4) {
+                    const int i = e / (BV / 4), j4 = (e % (BV / 4)) * 4;
+                    *reinterpret_cast<float4*>(&Sst[((ch + 1) * DK + i) * DV + v0 + j4]) =
+                        *reinterpret_cast<const float4*>(&sSf[pb][i][j4]);
+                }
             }
         }
-#pragma unroll
-        for (int m = 0; m < MD; ++m) {
-            const int idx = w + NW * m;
-            const int ti = idx / (BV / 16), tj = idx % (BV / 16);
-            const uint32_t dw[2] = {dpk[m].x, dpk[m].y}, ow[2] = {opk[m].x, opk[m].y};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = ti * 16 + 4 * lq + r;
-                const uint16_t db = (uint16_t)((r & 1) ? (dw[r >> 1] >> 16) : (dw[r >> 1] & 0xFFFFu));
-                if (SAVE) Dst[(ch * C + i) * DV + v0 + tj * 16 + lr].bits = db;
-                if (OUT) {
-                    const int t = n * C + i;
-                    const uint16_t ob = (uint16_t)((r & 1) ? (ow[r >> 1] >> 16) : (ow[r >> 1] & 0xFFFFu));
-                    if (t < T) o[(((size_t)b * T + t) * H + h) * DV + v0 + tj * 16 + lr].bits = ob;
-                }
+        {
+            constexpr int NB8 = C * BV / 8;  // 16-byte words of a [C][BV] bf16 tile
+            static_assert(2 * NB8 <= NTHR_S, "D and o words, one per thread");
+            if (tid < NB8) {
+                const int i = tid / (BV / 8), j8 = (tid % (BV / 8)) * 8;
+                if (SAVE)
+                    *reinterpret_cast<uint4*>(&Dst[(ch * C + i) * DV + v0 + j8]) =
+                        *reinterpret_cast<const uint4*>(&sDr[pb][i][j8]);
+            } else if (tid < 2 * NB8) {
+                const int e = tid - NB8, i = e / (BV / 8), j8 = (e % (BV / 8)) * 8;
+                const int t = n * C + i;
+                if (OUT && t < T)
+                    *reinterpret_cast<uint4*>(&o[(((size_t)b * T + t) * H + h) * DV + v0 + j8]) =
+                        *reinterpret_cast<const uint4*>(&sOr[pb][i][j8]);
             }
         }
     }
