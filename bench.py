@@ -174,6 +174,7 @@ def main():
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-head", action="store_true", help="skip the per-head decay measurement")
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward-only measurement (profiling runs: one launch name per kernel)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -199,13 +200,18 @@ def main():
     in_bytes = 2 if dt == "bf16" else 4
     log(f"[bench] workload B={B} T={T} H={H} D={D} dtype={dt}: generating inputs")
     inp = gi.train(dtype=dt, B=B, grads=True)
-    to = {}
-    for k_, x in inp.items():
-        if isinstance(x, np.ndarray):
-            if x.dtype == np.uint16:
-                to[k_] = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).cuda()
-            else:
-                to[k_] = torch.from_numpy(x).cuda()
+
+    def to_device(d):
+        out = {}
+        for k_, x in d.items():
+            if isinstance(x, np.ndarray):
+                if x.dtype == np.uint16:
+                    out[k_] = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+                else:
+                    out[k_] = torch.from_numpy(x).cuda()
+        return out
+
+    to = to_device(inp)
     scale = inp["meta"]["scale"]
     q, k, v, g, beta, dO, dhT = (to[n] for n in ("q", "k", "v", "g", "beta", "dO", "dhT"))
     sh = gdn.make_shape(q, v, g, scale, C)
@@ -307,6 +313,63 @@ def main():
         fwd_tps = B * T / (ms_fwd * 1e-3)
         log(f"[bench] fwd {ms_fwd:.3f} ms ({fwd_tps / 1e6:.2f} M tokens/s)")
 
+    # ---- per-head decay (one log-decay per token and head) at the same shape
+    head = None
+    if not args.no_head:
+        hinp = gi.train(dtype=dt, B=B, grads=True, decay="head")
+        hd = to_device(hinp)
+        hg = hd["g"]
+        hq, hk, hv, hbeta, hdO, hdhT = (hd[n] for n in ("q", "k", "v", "beta", "dO", "dhT"))
+
+        hgout = (torch.empty_like(hq), torch.empty_like(hk), torch.empty_like(hv),
+                 torch.empty_like(hg), torch.empty_like(hbeta), torch.empty_like(hT))
+
+        def hstep():
+            gdn.gdn_forward_train(hq, hk, hv, hg, hbeta, None, scale=scale, chunk=C, o=o, hT=hT, ws=ws_b)
+            return gdn.gdn_backward_train(hq, hk, hv, hg, hbeta, hdO, ws_b, hdhT, scale=scale,
+                                          chunk=C, out=hgout)
+
+        hgr = hstep()
+        torch.cuda.synchronize()
+        hp = [(0, 0), (B - 1, H - 1)]
+        hs = {n: np.stack([hinp[n][b, :, h] for b, h in hp], axis=1)[None]
+              for n in ("q", "k", "v", "g", "beta", "dO")}
+        hs["dhT"] = np.stack([hinp["dhT"][b, h] for b, h in hp])[None]
+        ho_ref, _ = oracle.forward(hs["q"], hs["k"], hs["v"], hs["g"], hs["beta"], scale)
+        hg_ref = oracle.backward(hs["q"], hs["k"], hs["v"], hs["g"], hs["beta"], scale, hs["dO"],
+                                 dhT=hs["dhT"])
+        hpar = {"o": rel(np.stack([pick(o, b, h) for b, h in hp], 1)[None], ho_ref)}
+        for name, x in zip(("dq", "dk", "dv", "dg", "dbeta"), hgr[:5]):
+            got = (np.stack([x[b, :, h].float().cpu().numpy().astype(np.float64) for b, h in hp], 1)[None])
+            hpar[name] = rel(got, hg_ref[name])
+        for _ in range(args.warmup):
+            hstep()
+        torch.cuda.synchronize()
+        hrec = LaunchRecorder(args.steps * 16 + 16)
+        ev0.record()
+        with hrec:
+            for _ in range(args.steps):
+                hstep()
+        ev1.record()
+        torch.cuda.synchronize()
+        hms = ev0.elapsed_time(ev1) / args.steps
+        hker = {n: float(np.mean(ms)) * 1e3 for n, ms in hrec.by_kernel().items()}
+        hrec.close()
+        ev0.record()
+        for _ in range(args.steps):
+            gdn.gdn_forward(hq, hk, hv, hg, hbeta, None, scale=scale, chunk=C, o=o, hT=hT, ws=ws_f)
+        ev1.record()
+        torch.cuda.synchronize()
+        hfwd = ev0.elapsed_time(ev1) / args.steps
+        head = {"workload": f"per-head decay (g [B,T,H]), otherwise as above",
+                "fwdbwd_tokens_per_s": B * T / (hms * 1e-3), "ms_per_step": hms,
+                "fwd_tokens_per_s": B * T / (hfwd * 1e-3), "fwd_ms": hfwd,
+                "kernels_avg_us": hker, "parity_max_rel_err": hpar,
+                "parity_ok": all(e <= tol for e in hpar.values())}
+        log(f"[bench] per-head: fwd+bwd {hms:.3f} ms ({head['fwdbwd_tokens_per_s'] / 1e6:.2f} M tokens/s), "
+            f"fwd {hfwd:.3f} ms; parity " + ", ".join(f"{k_} {e:.1e}" for k_, e in hpar.items()))
+        log("[bench] per-head kernels: " + ", ".join(f"{n} {u:.0f} us" for n, u in hker.items()))
+
     # ---- decode: B=256 H=16 128x128 fp32 state, one token per step
     decode = None
     if not args.no_decode:
@@ -397,6 +460,7 @@ def main():
         "parity_max_rel_err": par,
         "kernels": others,
         "roofline": roof,
+        "per_head": head,
         "decode": decode,
         "cpu_baseline": cpu,
     }

@@ -109,6 +109,16 @@ def _check(t, name, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _check_shape(t, name, shape, dtype):
+    """A caller-supplied tensor the library reads or writes: device, dense, and
+    exactly `shape` (the C ABI takes bare pointers and cannot check sizes)."""
+    if t is None:
+        return
+    _check(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def make_shape(q, v, g, scale=None, chunk=None) -> GdnShape:
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -145,8 +155,30 @@ def workspace(shape: GdnShape, for_backward: bool, device) -> torch.Tensor:
 
 def _check_inputs(q, k, v, g, beta):
     dt = q.dtype
-    _check(q, "q", dt); _check(k, "k", dt); _check(v, "v", dt)
-    _check(g, "g", torch.float32); _check(beta, "beta", torch.float32)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, T, H, Dk], got {tuple(q.shape)}")
+    B, T, H, Dk = q.shape
+    _check(q, "q", dt)
+    _check_shape(k, "k", q.shape, dt)
+    if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError(f"v must be [{B}, {T}, {H}, Dv], got {tuple(v.shape)}")
+    _check(v, "v", dt)
+    if tuple(g.shape) not in ((B, T, H, Dk), (B, T, H)):
+        raise ValueError(f"g must be [{B}, {T}, {H}, {Dk}] or [{B}, {T}, {H}], got {tuple(g.shape)}")
+    _check(g, "g", torch.float32)
+    _check_shape(beta, "beta", (B, T, H), torch.float32)
+    for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+
+
+def _state_shape(sh):
+    return (sh.B, sh.H, sh.Dk, sh.Dv)
+
+
+def _check_ws(ws):
+    if ws is not None:
+        _check(ws, "ws")
 
 
 def gdn_forward(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT=None,
@@ -154,8 +186,11 @@ def gdn_forward(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT
     """Chunked forward.  Returns (o, hT); hT is None when want_state is False.
     Passing hT=h0 carries the state in place."""
     _check_inputs(q, k, v, g, beta)
-    _check(h0, "h0", torch.float32)
     sh = make_shape(q, v, g, scale, chunk)
+    _check_shape(h0, "h0", _state_shape(sh), torch.float32)
+    _check_shape(o, "o", v.shape, q.dtype)
+    _check_shape(hT, "hT", _state_shape(sh), torch.float32)
+    _check_ws(ws)
     B, T, H, _ = q.shape
     if o is None:
         o = torch.empty((B, T, H, sh.Dv), dtype=q.dtype, device=q.device)
@@ -172,9 +207,11 @@ def gdn_backward(q, k, v, g, beta, dO, h0=None, dhT=None, *, scale=None, chunk=N
                  want_dh0=True, ws=None):
     """Gradients (dq, dk, dv, dg, dbeta, dh0) of sum(o*dO) + sum(hT*dhT)."""
     _check_inputs(q, k, v, g, beta)
-    _check(dO, "dO", q.dtype)
-    _check(h0, "h0", torch.float32); _check(dhT, "dhT", torch.float32)
     sh = make_shape(q, v, g, scale, chunk)
+    _check_shape(dO, "dO", v.shape, q.dtype)
+    _check_shape(h0, "h0", _state_shape(sh), torch.float32)
+    _check_shape(dhT, "dhT", _state_shape(sh), torch.float32)
+    _check_ws(ws)
     dq = torch.empty_like(q); dk = torch.empty_like(k); dv = torch.empty_like(v)
     dg = torch.empty_like(g); dbeta = torch.empty_like(beta)
     dh0 = (torch.empty((sh.B, sh.H, sh.Dk, sh.Dv), dtype=torch.float32, device=q.device)
@@ -193,8 +230,11 @@ def gdn_forward_train(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=No
     backward-sized workspace, returned) for gdn_backward_train.
     Returns (o, hT, ws)."""
     _check_inputs(q, k, v, g, beta)
-    _check(h0, "h0", torch.float32)
     sh = make_shape(q, v, g, scale, chunk)
+    _check_shape(h0, "h0", _state_shape(sh), torch.float32)
+    _check_shape(o, "o", v.shape, q.dtype)
+    _check_shape(hT, "hT", _state_shape(sh), torch.float32)
+    _check_ws(ws)
     B, T, H, _ = q.shape
     if o is None:
         o = torch.empty((B, T, H, sh.Dv), dtype=q.dtype, device=q.device)
@@ -212,9 +252,21 @@ def gdn_backward_train(q, k, v, g, beta, dO, ws, dhT=None, *, scale=None, chunk=
                        want_dh0=True, out=None):
     """Training backward from the residuals gdn_forward_train left in `ws`."""
     _check_inputs(q, k, v, g, beta)
-    _check(dO, "dO", q.dtype)
-    _check(dhT, "dhT", torch.float32)
     sh = make_shape(q, v, g, scale, chunk)
+    _check_shape(dO, "dO", v.shape, q.dtype)
+    _check_shape(dhT, "dhT", _state_shape(sh), torch.float32)
+    _check(ws, "ws")
+    if out is not None:
+        if len(out) != 6:
+            raise ValueError("out must be (dq, dk, dv, dg, dbeta, dh0)")
+        for t, name, shape, dt in zip(out, ("dq", "dk", "dv", "dg", "dbeta", "dh0"),
+                                      (q.shape, k.shape, v.shape, g.shape, beta.shape,
+                                       _state_shape(sh)),
+                                      (q.dtype, q.dtype, q.dtype, torch.float32, torch.float32,
+                                       torch.float32)):
+            if t is None and name != "dh0":
+                raise ValueError(f"out: {name} is required")
+            _check_shape(t, name, shape, dt)
     if out is None:
         out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g),
                torch.empty_like(beta),
@@ -234,8 +286,9 @@ def gdn_decode_step(q, k, v, g, beta, state, *, scale=None, o=None):
         g = g.unsqueeze(1)
         beta = beta.unsqueeze(1)
     _check_inputs(q, k, v, g, beta)
-    _check(state, "state", torch.float32)
     sh = make_shape(q, v, g, scale, None)
+    _check_shape(state, "state", _state_shape(sh), torch.float32)
+    _check_shape(o, "o", (sh.B, 1, sh.H, sh.Dv), q.dtype)
     if o is None:
         o = torch.empty((sh.B, 1, sh.H, sh.Dv), dtype=q.dtype, device=q.device)
     _call(lib().gdn_decode_step, "gdn_decode_step", ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v),

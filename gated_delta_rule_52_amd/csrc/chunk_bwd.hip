@@ -1359,14 +1359,27 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     static_assert(NPART * HC <= NTHR_F, "one column thread per (part, channel)");
     constexpr int PT = C + 8;  // bf16 pitch: 16-byte rows, banks spread
     constexpr int PH = HC + 1; // fp32 pitch of the result tables
-    // score gradients, bf16: dPs (unscaled, lower incl. diagonal) and dA (strictly
-    // lower) by rows and transposed, the transposed dA with beta_i folded in
-    __shared__ __align__(16) bf16 sP[C][PT], sPT[C][PT], sA[C][PT], sAT[C][PT];
-    __shared__ __align__(16) bf16 sQKT[HC][PT], sKKT[HC][PT];  // level tables, channel-major
-    // level results: query rows scale*R1, key rows scale*R1 + R2 (sR); query rows'
-    // R2 (sR2, C/2 rows); before the levels sR also holds the dKh row-sum partials
-    __shared__ float sR[C][PH], sR2[C / 2][PH];
+    // LDS, one buffer with named parts:
+    //  score gradients, bf16: dPs (unscaled, lower incl. diagonal) and dA (strictly
+    //  lower) by rows and transposed, the transposed dA with beta_i folded in;
+    //  level tables (channel-major); level results: query rows scale*R1, key rows
+    //  scale*R1 + R2 (sR), query rows' R2 (sR2, C/2 rows).  Before the levels sR
+    //  also holds the dKh row-sum partials.  Per-head decay uses, after its score
+    //  products, the first 3 C x PH fp32 tables' worth of bytes for their results.
+    constexpr int TB = C * PT * 2, O_QK = 4 * TB, O_KK = O_QK + HC * PT * 2;
+    constexpr int O_R = O_KK + HC * PT * 2, O_R2 = O_R + C * PH * 4, LDSB = O_R2 + (C / 2) * PH * 4;
+    static_assert(3 * C * PH * 4 <= O_R, "per-head results fit below the level results");
+    __shared__ __align__(16) char sbuf[LDSB];
+    bf16 (*sP)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);
+    bf16 (*sPT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + TB);
+    bf16 (*sA)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + 2 * TB);
+    bf16 (*sAT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + 3 * TB);
+    bf16 (*sQKT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + O_QK);
+    bf16 (*sKKT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + O_KK);
+    float (*sR)[PH] = reinterpret_cast<float (*)[PH]>(sbuf + O_R);
+    float (*sR2)[PH] = reinterpret_cast<float (*)[PH]>(sbuf + O_R2);
     __shared__ float sbeta[C], stot[NPART][HC];
+    __shared__ float sG[C];  // per-head decay: chunk-local inclusive cumsum of g
     float (*sext)[HC] = reinterpret_cast<float (*)[HC]>(&sR[0][0]);
 
     // block -> (chunk-head, half): the two halves of a chunk-head are 8 ids
@@ -1438,6 +1451,17 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         }
         if (tid < C) sbeta[tid] = tid < nvalid ? bv : 0.f;
     }
+    if constexpr (!PCH) {
+        if (w == 0) {  // G_i = g_0 + ... + g_i, inclusive prefix sum across the wave (C = 64)
+            float x = tid < nvalid ? g[tok0 + (size_t)min(tid, nvalid - 1) * H] : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (tid >= off) x += y;
+            }
+            sG[tid] = x;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < RPP; ++i) a[i] = expf(a[i]);
     {
@@ -1487,6 +1511,98 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         for (int pp = 0; pp < NPART; ++pp) sacc += sext[pp][cl];
         dG[RPP - 1] += sacc + Gm[RPP - 1] * dgmi[(size_t)ch * DK + c];
     }
+    if constexpr (!PCH) {
+        // ---- Per-head decay: the decay between tokens j <= i is the scalar
+        // E_ij = exp(G_i - G_j), the same for every channel, so with dP~ = dPs o E
+        // and dA~ = dA o E all score gradients are three MFMA products per tile:
+        //   X = scale dP~ K  (dq),   R = dA~ K  (query side of dk and dbeta),
+        //   Y = scale dP~^T Q + (diag(beta) dA~)^T K  (key side of dk),
+        // and dG = q o X + beta k o R - k o Y (the diagonal, E = 1, cancels in dG).
+        // Scale the score tables by E in place (rows: E(i, j); transposed: E(j', i')).
+        for (int e = tid; e < 2 * C * (C / 8); e += NTHR_F) {
+            const bool tr = e >= C * (C / 8);
+            const int f = tr ? e - C * (C / 8) : e;
+            const int rr = f / (C / 8), c0 = (f % (C / 8)) * 8;
+            bf16* t1 = tr ? &sPT[rr][c0] : &sP[rr][c0];
+            bf16* t2 = tr ? &sAT[rr][c0] : &sA[rr][c0];
+            uint4 w1 = *reinterpret_cast<const uint4*>(t1), w2 = *reinterpret_cast<const uint4*>(t2);
+            uint32_t u1[4] = {w1.x, w1.y, w1.z, w1.w}, u2[4] = {w2.x, w2.y, w2.z, w2.w};
+            float ev[8];
+#pragma unroll
+            for (int z = 0; z < 8; ++z) {
+                const int i = tr ? c0 + z : rr, j = tr ? rr : c0 + z;  // element (i, j) of the C x C matrix
+                ev[z] = j <= i ? expf(sG[i] - sG[j]) : 0.f;
+            }
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                const float p0v = __uint_as_float(u1[z] << 16) * ev[2 * z], p1v = __uint_as_float(u1[z] & 0xFFFF0000u) * ev[2 * z + 1];
+                const float a0v = __uint_as_float(u2[z] << 16) * ev[2 * z], a1v = __uint_as_float(u2[z] & 0xFFFF0000u) * ev[2 * z + 1];
+                u1[z] = (uint32_t)f32_to_bf16(p0v).bits | ((uint32_t)f32_to_bf16(p1v).bits << 16);
+                u2[z] = (uint32_t)f32_to_bf16(a0v).bits | ((uint32_t)f32_to_bf16(a1v).bits << 16);
+            }
+            *reinterpret_cast<uint4*>(t1) = uint4{u1[0], u1[1], u1[2], u1[3]};
+            *reinterpret_cast<uint4*>(t2) = uint4{u2[0], u2[1], u2[2], u2[3]};
+        }
+        // q^T and k^T, channel-major (the level tables with factor 1)
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < RPP; i += 8) {
+                const uint2 q0 = pack4_bf16(qv[i], qv[i + 1], qv[i + 2], qv[i + 3]);
+                const uint2 q1 = pack4_bf16(qv[i + 4], qv[i + 5], qv[i + 6], qv[i + 7]);
+                const uint2 k0 = pack4_bf16(kv[i], kv[i + 1], kv[i + 2], kv[i + 3]);
+                const uint2 k1 = pack4_bf16(kv[i + 4], kv[i + 5], kv[i + 6], kv[i + 7]);
+                *reinterpret_cast<uint4*>(&sQKT[cl][p0 + i]) = uint4{q0.x, q0.y, q1.x, q1.y};
+                *reinterpret_cast<uint4*>(&sKKT[cl][p0 + i]) = uint4{k0.x, k0.y, k1.x, k1.y};
+            }
+        }
+        __syncthreads();
+        constexpr int T3 = NB * (HC / 16), M3 = (T3 + NW - 1) / NW;
+        f32x4 xr[M3], rr2[M3], yr[M3];
+#pragma unroll
+        for (int m = 0; m < M3; ++m) {
+            const int idx = w + NW * m;
+            const int ti = (idx % T3) / (HC / 16), tj = idx % (HC / 16);
+            xr[m] = mma_kc<C>(zero4(), &sP[ti * 16][0], PT, &sKKT[tj * 16][0], PT);
+            rr2[m] = mma_kc<C>(zero4(), &sA[ti * 16][0], PT, &sKKT[tj * 16][0], PT);
+            const f32x4 y1 = mma_kc<C>(zero4(), &sPT[ti * 16][0], PT, &sQKT[tj * 16][0], PT);
+            yr[m] = mma_kc<C>(zero4(), &sAT[ti * 16][0], PT, &sKKT[tj * 16][0], PT);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                xr[m][r] *= scale;
+                yr[m][r] += scale * y1[r];
+            }
+        }
+        __syncthreads();  // every read of the tables is done: their bytes take the results
+        float (*sX)[PH] = reinterpret_cast<float (*)[PH]>(sbuf);
+        float (*sRq)[PH] = reinterpret_cast<float (*)[PH]>(sbuf + C * PH * 4);
+        float (*sY)[PH] = reinterpret_cast<float (*)[PH]>(sbuf + 2 * C * PH * 4);
+#pragma unroll
+        for (int m = 0; m < M3; ++m) {
+            const int idx = w + NW * m;
+            if (idx < T3) {
+                const int ti = idx / (HC / 16), tj = idx % (HC / 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
+                    sX[i][j] = xr[m][r];
+                    sRq[i][j] = rr2[m][r];
+                    sY[i][j] = yr[m][r];
+                }
+            }
+        }
+        __syncthreads();
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                const int r = p0 + i;
+                const float X = sX[r][cl], R = sRq[r][cl], Y = sY[r][cl], bt = sbeta[r];
+                dq[i] += X;
+                dk[i] += bt * R + Y;
+                dG[i] += qv[i] * X + bt * kv[i] * R - kv[i] * Y;
+                dbr[i] += kv[i] * R;
+            }
+        }
+    } else {
     // ---- diagonal scores (decay 1): P_ii = q_i . k_i
     if (cp) {
 #pragma unroll
@@ -1631,6 +1747,8 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             dG[j] -= kv[j] * cs[j];
         }
     }
+
+    }  // per-channel decay
 
     // ---- dg = reverse cumulative sum of dG over the chunk (the part sums go
     // through stot, no longer needed); dq, dk, dg out; dbeta partials

@@ -391,6 +391,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     __shared__ __align__(16) float sA[C][PC];  // A (beta rows), strictly lower; later T in bf16
     __shared__ __align__(16) bf16 sXT[DK][PT];  // X_K^T, then X_V^T
     __shared__ float sbeta[C], stot[NPART][DK];
+    __shared__ float sG[C];  // per-head decay: chunk-local inclusive cumsum of g
     bf16 (*sX)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf);
     bf16 (*sY)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf + C * PA * 2);
     float (*sT)[PC] = reinterpret_cast<float (*)[PC]>(sbuf);
@@ -431,6 +432,18 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         for (int i = 0; i < RPP; ++i) pt *= a[i];
         if (cp) stot[part][c] = pt;
     }
+    if constexpr (!PCH) {
+        static_assert(C == 64, "one token per lane of wave 0");
+        if (w == 0) {  // G_i = g_0 + ... + g_i, inclusive prefix sum across the wave
+            float x = l < nvalid ? g[tok0 + (size_t)min(l, nvalid - 1) * H] : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (l >= off) x += y;
+            }
+            sG[l] = x;
+        }
+    }
     // level 0: unscaled rows, the diagonal P_ii = q_i . k_i
     if (cp) {
 #pragma unroll
@@ -441,16 +454,51 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     }
     __syncthreads();
     f32x4 dP = zero4(), dA = zero4();
-    if (w < NB) {
-        const f32x4 tp = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sY[w * 16][0], PA);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dP[r] = (4 * lq + r == lr) ? tp[r] : 0.f;
-    }
     // off-diagonal 16-tiles: waves NB.. own tile idx with (idx % (NW - NB)) == w - NB
     constexpr int OW = NW - NB, MOFF = (NOFF + OW - 1) / OW;
     f32x4 accP[MOFF], accA[MOFF];
 #pragma unroll
     for (int m = 0; m < MOFF; ++m) accP[m] = accA[m] = zero4();
+    if constexpr (!PCH) {
+        // Per-head decay: the decay between tokens j <= i is the scalar
+        // exp(G_i - G_j) <= 1, the same for every key channel, so each score is
+        // the plain product q_i . k_j (or k_i . k_j) times it: one MFMA product
+        // per 16-tile instead of the block-boundary split.
+        if (w < NB) {
+            const f32x4 tp = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sY[w * 16][0], PA);
+            const f32x4 ta = mma_kc<DK>(zero4(), &sY[w * 16][0], PA, &sY[w * 16][0], PA);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 4 * lq + r, j = lr;
+                const float e = j <= i ? expf(sG[w * 16 + i] - sG[w * 16 + j]) : 0.f;
+                dP[r] = tp[r] * e;
+                dA[r] = j < i ? ta[r] * e : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < MOFF; ++m) {
+                const int idx = (w - NB) + OW * m;
+                if (idx < NOFF) {
+                    int ti, tj;
+                    off_tile(idx, ti, tj);
+                    accP[m] = mma_kc<DK>(zero4(), &sX[ti * 16][0], PA, &sY[tj * 16][0], PA);
+                    accA[m] = mma_kc<DK>(zero4(), &sY[ti * 16][0], PA, &sY[tj * 16][0], PA);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float e = expf(sG[ti * 16 + 4 * lq + r] - sG[tj * 16 + lr]);
+                        accP[m][r] *= e;
+                        accA[m][r] *= e;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    } else {
+    if (w < NB) {
+        const f32x4 tp = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sY[w * 16][0], PA);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dP[r] = (4 * lq + r == lr) ? tp[r] : 0.f;
+    }
     __syncthreads();
 
 #pragma unroll
@@ -534,6 +582,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         }
         __syncthreads();
     }
+    }  // per-channel decay
 
     // ---- scores out: Ps (bf16) and, for training, Ps^T; A (x beta) to LDS
     bf16* Psc = Psb + (size_t)ch * C * C;

@@ -140,9 +140,10 @@ def decode(seed: int = 0, B: int = 256, H: int = 16, steps: int = 64) -> dict:
 
 
 def train(seed: int = 0, B: int = 8, dtype: str = "bf16", grads: bool = False,
-          T: int = 4096, H: int = 6, D: int = 128) -> dict:
-    """Training shape: per-channel decay, B=8 (or 4) T=4096 H=6 128x128, zero
-    state; with grads, dO ~ N(0,1) in the input dtype and dhT ~ N(0, 0.01)."""
-    d = make_inputs(B, T, H, D, D, decay="channel", dtype=dtype, seed=seed, grads=grads)
+          T: int = 4096, H: int = 6, D: int = 128, decay: str = "channel") -> dict:
+    """Training shape: per-channel decay (or per-head), B=8 (or 4) T=4096 H=6
+    128x128, zero state; with grads, dO ~ N(0,1) in the input dtype and
+    dhT ~ N(0, 0.01)."""
+    d = make_inputs(B, T, H, D, D, decay=decay, dtype=dtype, seed=seed, grads=grads)
     d["meta"]["chunk"] = 64
     return d
