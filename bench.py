@@ -42,6 +42,7 @@ PAGES_FWDBWD_TOKENS_S = 8 * 4096 / 22.44e-3
 KERNEL_SOURCE = {"prep": "chunk_fwd.hip", "prep_T": "chunk_fwd.hip", "scan": "chunk_fwd.hip",
                  "scan_save": "chunk_fwd.hip", "scan_train": "chunk_fwd.hip",
                  "bscan": "chunk_bwd.hip", "bchunk1": "chunk_bwd.hip", "bchunk2": "chunk_bwd.hip",
+                 "bchunk2_finish": "chunk_bwd.hip",
                  "decode": "decode.hip"}
 CSRC = os.path.join(ROOT, "gated_delta_rule_52_amd", "csrc")
 COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_traffic_fwdbwd_b8_t4096_h6_d128_bf16.md")
