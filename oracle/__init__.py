@@ -41,6 +41,10 @@ def _bind(lib):
     lib.oracle_backward.argtypes = [i, i, i, i, i, i, ctypes.c_double] + [dp] * 14 + [i]
     lib.oracle_backward.restype = i
     lib.oracle_max_threads.restype = i
+    lib.oracle_l2norm_forward.argtypes = [ctypes.c_long, i, ctypes.c_double, dp, dp]
+    lib.oracle_l2norm_forward.restype = i
+    lib.oracle_l2norm_backward.argtypes = [ctypes.c_long, i, ctypes.c_double, dp, dp, dp]
+    lib.oracle_l2norm_backward.restype = i
     return lib
 
 
@@ -76,13 +80,40 @@ def _dims(q, v, g):
     return B, T, H, Dk, Dv, per_channel
 
 
-def forward(q, k, v, g, beta, scale, h0=None, nthreads: int = 0, lib=None):
-    """Returns (o [B,T,H,Dv], hT [B,H,Dk,Dv]) in float64."""
+L2NORM_EPS = 1e-6  # the reading taken for use_qk_l2norm's guard (not printed on the pages)
+
+
+def l2norm(x, eps: float = L2NORM_EPS, lib=None):
+    """x / sqrt(sum(x^2) + eps) over the last dimension (float64)."""
+    x = _f64(x)
+    out = np.zeros_like(x)
+    lib = lib or load()
+    if lib.oracle_l2norm_forward(x.size // x.shape[-1], x.shape[-1], float(eps), _ptr(x), _ptr(out)):
+        raise ValueError("oracle_l2norm_forward: bad dimensions")
+    return out
+
+
+def l2norm_backward(x, dxhat, eps: float = L2NORM_EPS, lib=None):
+    """Gradient with respect to the raw rows x given the gradient of l2norm(x)."""
+    x, dxhat = _f64(x), _f64(dxhat)
+    out = np.zeros_like(x)
+    lib = lib or load()
+    if lib.oracle_l2norm_backward(x.size // x.shape[-1], x.shape[-1], float(eps), _ptr(x),
+                                  _ptr(dxhat), _ptr(out)):
+        raise ValueError("oracle_l2norm_backward: bad dimensions")
+    return out
+
+
+def forward(q, k, v, g, beta, scale, h0=None, nthreads: int = 0, lib=None, qk_l2norm=False):
+    """Returns (o [B,T,H,Dv], hT [B,H,Dk,Dv]) in float64.  With qk_l2norm the
+    q and k rows are L2-normalised first (use_qk_l2norm)."""
+    lib = lib or load()
+    if qk_l2norm:
+        q, k = l2norm(q, lib=lib), l2norm(k, lib=lib)
     q, k, v, g, beta, h0 = map(_f64, (q, k, v, g, beta, h0))
     B, T, H, Dk, Dv, pc = _dims(q, v, g)
     o = np.zeros((B, T, H, Dv))
     hT = np.zeros((B, H, Dk, Dv))
-    lib = lib or load()
     rc = lib.oracle_forward(B, T, H, Dk, Dv, pc, float(scale), _ptr(q), _ptr(k), _ptr(v),
                             _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), int(nthreads))
     if rc != 0:
@@ -90,29 +121,39 @@ def forward(q, k, v, g, beta, scale, h0=None, nthreads: int = 0, lib=None):
     return o, hT
 
 
-def backward(q, k, v, g, beta, scale, dO, h0=None, dhT=None, nthreads: int = 0, lib=None):
-    """Returns dict of float64 gradients dq, dk, dv, dg, dbeta, dh0."""
+def backward(q, k, v, g, beta, scale, dO, h0=None, dhT=None, nthreads: int = 0, lib=None,
+             qk_l2norm=False):
+    """Returns dict of float64 gradients dq, dk, dv, dg, dbeta, dh0 (with
+    qk_l2norm: dq, dk with respect to the raw, unnormalised q and k)."""
+    lib = lib or load()
+    q_raw, k_raw = q, k
+    if qk_l2norm:
+        q, k = l2norm(q, lib=lib), l2norm(k, lib=lib)
     q, k, v, g, beta, h0, dO, dhT = map(_f64, (q, k, v, g, beta, h0, dO, dhT))
     B, T, H, Dk, Dv, pc = _dims(q, v, g)
     out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
                dg=np.zeros_like(g), dbeta=np.zeros_like(beta), dh0=np.zeros((B, H, Dk, Dv)))
-    lib = lib or load()
     rc = lib.oracle_backward(B, T, H, Dk, Dv, pc, float(scale), _ptr(q), _ptr(k), _ptr(v),
                              _ptr(g), _ptr(beta), _ptr(h0), _ptr(dO), _ptr(dhT),
                              _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                              _ptr(out["dbeta"]), _ptr(out["dh0"]), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_backward: bad dimensions")
+    if qk_l2norm:
+        out["dq"] = l2norm_backward(q_raw, out["dq"], lib=lib)
+        out["dk"] = l2norm_backward(k_raw, out["dk"], lib=lib)
     return out
 
 
 def forward_inputs(inp: dict, **kw):
     """forward() on a workload dict from gdn_inputs."""
+    kw.setdefault("qk_l2norm", bool(inp["meta"].get("qk_l2norm", False)))
     return forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["meta"]["scale"],
                    h0=inp.get("h0"), **kw)
 
 
 def backward_inputs(inp: dict, **kw):
+    kw.setdefault("qk_l2norm", bool(inp["meta"].get("qk_l2norm", False)))
     return backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["meta"]["scale"],
                     inp["dO"], h0=inp.get("h0"), dhT=inp.get("dhT"), **kw)
 

@@ -24,6 +24,13 @@
  * reverse.  The states it needs are recomputed segment by segment from
  * float64 checkpoints taken every CKPT tokens.
  *
+ * Optional prologue (gated-deltanet card, "Usage": use_qk_l2norm, the in-kernel
+ * L2 normalisation of queries and keys): every q_t and k_t row (Dk values of one
+ * token and head) is replaced by x / sqrt(sum(x^2) + eps) before the loop; its
+ * adjoint maps the gradient g_hat of the normalised row back to the raw row as
+ * r (g_hat - x_hat (x_hat . g_hat)), r = 1 / sqrt(sum(x^2) + eps).  The pages
+ * name the option but not eps; 1e-6 is this oracle's reading.
+ *
  * Layouts (row-major, contiguous):
  *   q, k [B,T,H,Dk]; v, o, dO [B,T,H,Dv]; beta [B,T,H];
  *   g [B,T,H,Dk] (per channel) or [B,T,H] (per head);
@@ -250,6 +257,36 @@ int oracle_backward(int B, int T, int H, int Dk, int Dv, int per_channel, double
     for (int bh = 0; bh < n; ++bh)
         head_backward(&d, bh / H, bh % H, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta,
                       dh0);
+    return 0;
+}
+
+/* x_hat = x / sqrt(sum(x^2) + eps), row by row over the last dimension D. */
+int oracle_l2norm_forward(long rows, int D, double eps, const double *x, double *xhat)
+{
+    if (rows < 0 || D <= 0) return -1;
+    for (long r = 0; r < rows; ++r) {
+        double s = 0.0;
+        for (int c = 0; c < D; ++c) s += x[r * D + c] * x[r * D + c];
+        const double inv = 1.0 / sqrt(s + eps);
+        for (int c = 0; c < D; ++c) xhat[r * D + c] = x[r * D + c] * inv;
+    }
+    return 0;
+}
+
+/* Adjoint of oracle_l2norm_forward: dx = r (dxhat - xhat (xhat . dxhat)). */
+int oracle_l2norm_backward(long rows, int D, double eps, const double *x, const double *dxhat,
+                           double *dx)
+{
+    if (rows < 0 || D <= 0) return -1;
+    for (long r = 0; r < rows; ++r) {
+        double s = 0.0;
+        for (int c = 0; c < D; ++c) s += x[r * D + c] * x[r * D + c];
+        const double inv = 1.0 / sqrt(s + eps);
+        double dot = 0.0;
+        for (int c = 0; c < D; ++c) dot += x[r * D + c] * inv * dxhat[r * D + c];
+        for (int c = 0; c < D; ++c)
+            dx[r * D + c] = inv * (dxhat[r * D + c] - x[r * D + c] * inv * dot);
+    }
     return 0;
 }
 

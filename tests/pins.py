@@ -282,6 +282,73 @@ def pin_determinism(lib):
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
 
 
+# --------------------------------------------------------------------------
+# P12 the use_qk_l2norm prologue (card, Usage): rows scaled to unit length
+# --------------------------------------------------------------------------
+def pin_l2norm_rows(lib):
+    """Closed form: every normalised row has squared length s / (s + eps)
+    (exactly 1 with eps = 0) and points along the raw row."""
+    x = np.random.default_rng(7).standard_normal((6, 3, 11)) * np.array([1e-2, 1.0, 30.0])[:, None]
+    for eps in (0.0, 1e-6):
+        y = oracle.l2norm(x, eps=eps, lib=lib)
+        s = np.sum(x * x, axis=-1)
+        assert np.allclose(np.sum(y * y, axis=-1), s / (s + eps), rtol=1e-14, atol=0)
+        cos = np.sum(x * y, axis=-1) / np.sqrt(s * np.sum(y * y, axis=-1))
+        assert np.allclose(cos, 1.0, rtol=0, atol=1e-14)
+
+
+def pin_l2norm_scale_invariance(lib):
+    """With normalisation the layer sees only the directions of q and k:
+    rescaling every row by a positive factor changes nothing but the eps
+    guard's share, at most ~eps / |x|^2."""
+    d = _rand(21, 2, 40, 2, 8, 5, decay="channel", h0_std=0.2)
+    rng = np.random.default_rng(3)
+    cq = rng.uniform(0.5, 4.0, d["q"].shape[:3])[..., None]
+    ck = rng.uniform(0.5, 4.0, d["k"].shape[:3])[..., None]
+    o1, h1 = _fwd(lib, d, qk_l2norm=True)
+    d2 = dict(d, q=d["q"] * cq, k=d["k"] * ck)
+    o2, h2 = _fwd(lib, d2, qk_l2norm=True)
+    assert rel_err(o2, o1) < 1e-5 and rel_err(h2, h1) < 1e-5
+
+
+def pin_l2norm_gradient_orthogonal(lib):
+    """The loss depends on q only through q/|q|, so its gradient has no
+    component along q (up to eps / |q|^2): dq . q ~ 0 for every row."""
+    d = _rand(23, 1, 30, 2, 8, 6, decay="head", grads=True)
+    gr = oracle.backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["meta"]["scale"], d["dO"],
+                         dhT=d["dhT"], lib=lib, qk_l2norm=True)
+    for x, dx in ((d["q"], gr["dq"]), (d["k"], gr["dk"])):
+        along = np.abs(np.sum(x * dx, axis=-1)) / (np.linalg.norm(x, axis=-1) * np.linalg.norm(dx, axis=-1) + 1e-300)
+        assert float(np.max(along)) < 1e-5
+
+
+def _loss_l2(lib, d, dO, dhT):
+    o, hT = _fwd(lib, d, qk_l2norm=True)
+    return float(np.sum(o * dO) + np.sum(hT * dhT))
+
+
+def pin_l2norm_fd(lib, seeds=(0, 1), h=1e-6, tol=1e-6):
+    """Central finite differences of the loss with respect to the raw q and k
+    against the backward's dq, dk through the normalisation."""
+    for seed in seeds:
+        d = _rand(140 + seed, 1, 7, 1, 4, 3, decay="channel", h0_std=0.5, grads=True)
+        dO, dhT = d["dO"], d["dhT"]
+        gr = oracle.backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["meta"]["scale"], dO,
+                             h0=d["h0"], dhT=dhT, lib=lib, qk_l2norm=True)
+        for nm, gn in (("q", "dq"), ("k", "dk")):
+            x = d[nm]
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                x0 = x[idx]
+                x[idx] = x0 + h; lp = _loss_l2(lib, d, dO, dhT)
+                x[idx] = x0 - h; lm = _loss_l2(lib, d, dO, dhT)
+                x[idx] = x0
+                num[idx] = (lp - lm) / (2 * h)
+            err = rel_err(gr[gn], num)
+            assert err <= tol, (seed, nm, err)
+
+
 FORWARD_PINS = [pin_worked_example, pin_beta_zero, pin_identity, pin_rewrite, pin_chunk_split,
-                pin_pairwise, pin_scalar, pin_onehot, pin_wipe, pin_determinism]
-ALL_PINS = FORWARD_PINS + [pin_fd_gradients]
+                pin_pairwise, pin_scalar, pin_onehot, pin_wipe, pin_determinism,
+                pin_l2norm_rows, pin_l2norm_scale_invariance, pin_l2norm_gradient_orthogonal]
+ALL_PINS = FORWARD_PINS + [pin_fd_gradients, pin_l2norm_fd]

@@ -38,6 +38,11 @@ MUTANTS = {
     "dv_beta_dropped": ("dv[r * Dv + j] = bt * ddv[j];", "dv[r * Dv + j] = ddv[j];"),
     "dh0_not_carried": ("if (dh0) memcpy(dh0 + sidx, dS, sizeof(double) * SS);",
                         "if (dh0) memset(dh0 + sidx, 0, sizeof(double) * SS);"),
+    # use_qk_l2norm prologue
+    "l2norm_projection_dropped": ("inv * (dxhat[r * D + c] - x[r * D + c] * inv * dot)",
+                                  "inv * dxhat[r * D + c]"),
+    "l2norm_sqrt_dropped": ("const double inv = 1.0 / sqrt(s + eps);\n        for (int c = 0; c < D; ++c) xhat",
+                            "const double inv = 1.0 / (s + eps);\n        for (int c = 0; c < D; ++c) xhat"),
 }
 
 
@@ -56,7 +61,7 @@ def test_pins_catch_mutant(name, tmp_path):
     caught = []
     for pin in pins.ALL_PINS:
         try:
-            if pin is pins.pin_fd_gradients:
+            if pin in (pins.pin_fd_gradients, pins.pin_l2norm_fd):
                 pin(lib, seeds=(0,))
             else:
                 pin(lib)

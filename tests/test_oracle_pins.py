@@ -17,3 +17,7 @@ def test_forward_pin(lib, pin):
 
 def test_fd_gradients(lib):
     pins.pin_fd_gradients(lib)
+
+
+def test_l2norm_fd_gradients(lib):
+    pins.pin_l2norm_fd(lib)
