@@ -42,7 +42,7 @@ PAGES_FWDBWD_TOKENS_S = 8 * 4096 / 22.44e-3
 KERNEL_SOURCE = {"prep": "chunk_fwd.hip", "prep_T": "chunk_fwd.hip", "scan": "chunk_fwd.hip",
                  "scan_save": "chunk_fwd.hip", "scan_train": "chunk_fwd.hip",
                  "bscan": "chunk_bwd.hip", "bchunk1": "chunk_bwd.hip", "bchunk2": "chunk_bwd.hip",
-                 "bchunk2_finish": "chunk_bwd.hip",
+                 "bchunk2_finish": "chunk_bwd.hip", "l2norm_bwd": "chunk_bwd.hip",
                  "decode": "decode.hip"}
 CSRC = os.path.join(ROOT, "gated_delta_rule_52_amd", "csrc")
 COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_traffic_fwdbwd_b8_t4096_h6_d128_bf16.md")
@@ -76,12 +76,13 @@ def measured_traffic(name):
     return ent["traffic_bytes"]
 
 
-def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True):
+def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True, l2n=False):
     """Algorithmic work of one launch of a chunked kernel: HBM bytes (each
     input read once, each output written once, in this design's data layout)
     and the matrix-product flops it must do, split by the operand type of its
     matrix-core instructions.  Counts are per chunk-head, times the launch's
-    B*H*ceil(T/C) chunk-heads.  Returns (bytes, {"f32": flops, "bf16": flops})."""
+    B*H*ceil(T/C) chunk-heads.  l2n: with use_qk_l2norm (the prep writes and
+    bchunk2 reads the rows' scales r).  Returns (bytes, {"f32": flops, "bf16": flops})."""
     NC = (T + C - 1) // C
     n = B * H * NC
     f4 = 4
@@ -98,6 +99,7 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True):
         by += 3 * cd * tb + cc * tb + cv * f4 + DK * f4            # W Qg Kh^T Ps, U, gam
         if name == "prep_T":
             by += (3 * cd + cc) * (tb if bt else 0) + cc * f4      # transposed tables, T
+        by += 2 * C * f4 if l2n else 0                             # r of the q and k rows
         fl[mt] += 2 * (2 * tri * DK) + 2 * tri * (DK + DV)         # P, A; W = T X_K, U = T X_V
         fl["f32"] += 2 * C ** 3 / 3                                # (I + A)^-1
     elif name in ("scan", "scan_save", "scan_train"):
@@ -139,15 +141,18 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True):
             by += cc * f4 + C * f4 + C * f4 + (0 if per_channel else C * f4)
             fl["f32"] += 2 * (2 * tri * DK) + 2 * (2 * C ** 3 / 3)
         fl[mt] += 2 * (2 * tri * DK) + 2 * (2 * tri * DK)             # score gradients of P and A
+        by += 2 * C * f4 if l2n else 0                                # r of the q and k rows
+    elif name == "l2norm_bwd":  # use_qk_l2norm adjoint, in place on dq, dk
+        by = 4 * cd * ib + 2 * C * f4 + 2 * cd * ib                   # q k dq dk, r in; dq dk out
     else:
         return None
     return by * n, {k_: v_ * n for k_, v_ in fl.items()}
 
 
-def roofline(name, dur_s, B, T, H, C, D, in_bytes):
+def roofline(name, dur_s, B, T, H, C, D, in_bytes, l2n=False):
     """Lower bound on one launch's duration from its algorithmic work at the
     published peaks; the largest term names the bound."""
-    by, fl = kernel_work(name, B, T, H, C, D, D, in_bytes)
+    by, fl = kernel_work(name, B, T, H, C, D, D, in_bytes, l2n=l2n)
     terms = {"hbm": by / (PEAK_HBM_GBS * 1e9)}
     for mt, f in fl.items():
         if f:
@@ -176,6 +181,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-head", action="store_true", help="skip the per-head decay measurement")
+    ap.add_argument("--no-l2norm", action="store_true",
+                    help="skip the use_qk_l2norm (raw q, k) measurement")
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward-only measurement (profiling runs: one launch name per kernel)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -371,6 +378,68 @@ def main():
             f"fwd {hfwd:.3f} ms; parity " + ", ".join(f"{k_} {e:.1e}" for k_, e in hpar.items()))
         log("[bench] per-head kernels: " + ", ".join(f"{n} {u:.0f} us" for n, u in hker.items()))
 
+    # ---- use_qk_l2norm: raw q, k rows normalised inside the layer, same shape
+    l2 = None
+    if not args.no_l2norm:
+        linp = gi.train(dtype=dt, B=B, grads=True, qk_scale=1.0)
+        ld = to_device(linp)
+        lq, lk, lv, lg, lbeta, ldO, ldhT = (ld[n] for n in ("q", "k", "v", "g", "beta", "dO", "dhT"))
+        lsh = gdn.make_shape(lq, lv, lg, scale, C, use_qk_l2norm=True)
+        lws_f = gdn.workspace(lsh, False, q.device)
+        lws_b = gdn.workspace(lsh, True, q.device)
+
+        def lstep():
+            gdn.gdn_forward_train(lq, lk, lv, lg, lbeta, None, scale=scale, chunk=C, o=o, hT=hT,
+                                  ws=lws_b, use_qk_l2norm=True)
+            return gdn.gdn_backward_train(lq, lk, lv, lg, lbeta, ldO, lws_b, ldhT, scale=scale,
+                                          chunk=C, out=gout, use_qk_l2norm=True)
+
+        lgr = lstep()
+        torch.cuda.synchronize()
+        lp = [(0, 0), (B - 1, H - 1)]
+        ls = {n: np.stack([linp[n][b, :, h] for b, h in lp], axis=1)[None]
+              for n in ("q", "k", "v", "g", "beta", "dO")}
+        ls["dhT"] = np.stack([linp["dhT"][b, h] for b, h in lp])[None]
+        lo_ref, _ = oracle.forward(ls["q"], ls["k"], ls["v"], ls["g"], ls["beta"], scale,
+                                   qk_l2norm=True)
+        lg_ref = oracle.backward(ls["q"], ls["k"], ls["v"], ls["g"], ls["beta"], scale, ls["dO"],
+                                 dhT=ls["dhT"], qk_l2norm=True)
+        lpar = {"o": rel(np.stack([pick(o, b, h) for b, h in lp], 1)[None], lo_ref)}
+        for name, x in zip(("dq", "dk", "dv", "dg", "dbeta"), lgr[:5]):
+            got = np.stack([pick(x, b, h) for b, h in lp], 1)[None]
+            lpar[name] = rel(got, lg_ref[name])
+        for _ in range(args.warmup):
+            lstep()
+        torch.cuda.synchronize()
+        lrec = LaunchRecorder(args.steps * 16 + 16)
+        ev0.record()
+        with lrec:
+            for _ in range(args.steps):
+                lstep()
+        ev1.record()
+        torch.cuda.synchronize()
+        lms = ev0.elapsed_time(ev1) / args.steps
+        lker = {n: float(np.mean(ms)) * 1e3 for n, ms in lrec.by_kernel().items()}
+        lrec.close()
+        ev0.record()
+        for _ in range(args.steps):
+            gdn.gdn_forward(lq, lk, lv, lg, lbeta, None, scale=scale, chunk=C, o=o, hT=hT,
+                            ws=lws_f, use_qk_l2norm=True)
+        ev1.record()
+        torch.cuda.synchronize()
+        lfwd = ev0.elapsed_time(ev1) / args.steps
+        lroof = roofline("l2norm_bwd", lker["l2norm_bwd"] * 1e-6, B, T, H, C, D, in_bytes)
+        l2 = {"workload": "use_qk_l2norm: raw q, k rows (N(0,1) times a log-normal length per "
+                          "row), normalised inside the layer; otherwise as above",
+              "fwdbwd_tokens_per_s": B * T / (lms * 1e-3), "ms_per_step": lms,
+              "fwd_tokens_per_s": B * T / (lfwd * 1e-3), "fwd_ms": lfwd,
+              "kernels_avg_us": lker, "l2norm_bwd_frac_hbm_peak": lroof["frac"],
+              "parity_max_rel_err": lpar, "parity_ok": all(e <= tol for e in lpar.values())}
+        log(f"[bench] use_qk_l2norm: fwd+bwd {lms:.3f} ms ({l2['fwdbwd_tokens_per_s'] / 1e6:.2f} M tokens/s), "
+            f"fwd {lfwd:.3f} ms; parity " + ", ".join(f"{k_} {e:.1e}" for k_, e in lpar.items()))
+        log("[bench] use_qk_l2norm kernels: " + ", ".join(f"{n} {u:.0f} us" for n, u in lker.items())
+            + f"; l2norm_bwd at {100 * lroof['frac']:.1f}% of HBM peak")
+
     # ---- decode: B=256 H=16 128x128 fp32 state, one token per step
     decode = None
     if not args.no_decode:
@@ -462,6 +531,7 @@ def main():
         "kernels": others,
         "roofline": roof,
         "per_head": head,
+        "qk_l2norm": l2,
         "decode": decode,
         "cpu_baseline": cpu,
     }

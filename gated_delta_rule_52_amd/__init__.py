@@ -14,7 +14,11 @@ carry the names of the C entry points in include/gdn.h:
 plus ``new_state`` (the gated-deltanet card's name for gdn_new_state).
 Layouts: q, k [B,T,H,Dk]; v [B,T,H,Dv]; g [B,T,H,Dk] or [B,T,H] (fp32);
 beta [B,T,H] (fp32); states [B,H,Dk,Dv] fp32.  q, k, v share one dtype
-(float32 or bfloat16); outputs take that dtype.
+(float32 or bfloat16); outputs take that dtype.  use_qk_l2norm=True has the
+library scale every q and k row to unit length, x / sqrt(|x|^2 + 1e-6), inside
+the call (the card's option of that name); dq, dk are then the gradients with
+respect to the raw rows, and a training pair must pass the same value to both
+calls.
 """
 from __future__ import annotations
 
@@ -39,7 +43,8 @@ EXPORTS = ("gdn_new_state", "gdn_workspace_bytes", "gdn_forward", "gdn_backward"
 class GdnShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
                 ("Dk", ctypes.c_int), ("Dv", ctypes.c_int), ("dtype", ctypes.c_int),
-                ("decay", ctypes.c_int), ("scale", ctypes.c_float), ("chunk", ctypes.c_int)]
+                ("decay", ctypes.c_int), ("scale", ctypes.c_float), ("chunk", ctypes.c_int),
+                ("qk_l2norm", ctypes.c_int)]
 
 
 class GdnError(RuntimeError):
@@ -119,12 +124,13 @@ def _check_shape(t, name, shape, dtype):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def make_shape(q, v, g, scale=None, chunk=None) -> GdnShape:
+def make_shape(q, v, g, scale=None, chunk=None, use_qk_l2norm=False) -> GdnShape:
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     decay = GDN_DECAY_PER_CHANNEL if g.dim() == 4 else GDN_DECAY_PER_HEAD
     return GdnShape(B, T, H, Dk, Dv, _dtype_code(q), decay,
-                    0.0 if scale is None else float(scale), 0 if chunk is None else int(chunk))
+                    0.0 if scale is None else float(scale), 0 if chunk is None else int(chunk),
+                    int(bool(use_qk_l2norm)))
 
 
 def _call(fn, where, *args):
@@ -182,11 +188,11 @@ def _check_ws(ws):
 
 
 def gdn_forward(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT=None,
-                want_state=True, ws=None):
+                want_state=True, ws=None, use_qk_l2norm=False):
     """Chunked forward.  Returns (o, hT); hT is None when want_state is False.
     Passing hT=h0 carries the state in place."""
     _check_inputs(q, k, v, g, beta)
-    sh = make_shape(q, v, g, scale, chunk)
+    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm)
     _check_shape(h0, "h0", _state_shape(sh), torch.float32)
     _check_shape(o, "o", v.shape, q.dtype)
     _check_shape(hT, "hT", _state_shape(sh), torch.float32)
@@ -204,10 +210,10 @@ def gdn_forward(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT
 
 
 def gdn_backward(q, k, v, g, beta, dO, h0=None, dhT=None, *, scale=None, chunk=None,
-                 want_dh0=True, ws=None):
+                 want_dh0=True, ws=None, use_qk_l2norm=False):
     """Gradients (dq, dk, dv, dg, dbeta, dh0) of sum(o*dO) + sum(hT*dhT)."""
     _check_inputs(q, k, v, g, beta)
-    sh = make_shape(q, v, g, scale, chunk)
+    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm)
     _check_shape(dO, "dO", v.shape, q.dtype)
     _check_shape(h0, "h0", _state_shape(sh), torch.float32)
     _check_shape(dhT, "dhT", _state_shape(sh), torch.float32)
@@ -225,12 +231,12 @@ def gdn_backward(q, k, v, g, beta, dO, h0=None, dhT=None, *, scale=None, chunk=N
 
 
 def gdn_forward_train(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT=None,
-                      ws=None):
+                      ws=None, use_qk_l2norm=False):
     """Training forward: as gdn_forward, and leaves residuals in `ws` (a
     backward-sized workspace, returned) for gdn_backward_train.
     Returns (o, hT, ws)."""
     _check_inputs(q, k, v, g, beta)
-    sh = make_shape(q, v, g, scale, chunk)
+    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm)
     _check_shape(h0, "h0", _state_shape(sh), torch.float32)
     _check_shape(o, "o", v.shape, q.dtype)
     _check_shape(hT, "hT", _state_shape(sh), torch.float32)
@@ -249,10 +255,10 @@ def gdn_forward_train(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=No
 
 
 def gdn_backward_train(q, k, v, g, beta, dO, ws, dhT=None, *, scale=None, chunk=None,
-                       want_dh0=True, out=None):
+                       want_dh0=True, out=None, use_qk_l2norm=False):
     """Training backward from the residuals gdn_forward_train left in `ws`."""
     _check_inputs(q, k, v, g, beta)
-    sh = make_shape(q, v, g, scale, chunk)
+    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm)
     _check_shape(dO, "dO", v.shape, q.dtype)
     _check_shape(dhT, "dhT", _state_shape(sh), torch.float32)
     _check(ws, "ws")
@@ -279,14 +285,14 @@ def gdn_backward_train(q, k, v, g, beta, dO, ws, dhT=None, *, scale=None, chunk=
     return dq, dk, dv, dg, dbeta, dh0
 
 
-def gdn_decode_step(q, k, v, g, beta, state, *, scale=None, o=None):
+def gdn_decode_step(q, k, v, g, beta, state, *, scale=None, o=None, use_qk_l2norm=False):
     """One token for every (b, h); q,k [B,1,H,Dk] (or [B,H,Dk]), state updated in place."""
     if q.dim() == 3:
         q, k, v = q.unsqueeze(1), k.unsqueeze(1), v.unsqueeze(1)
         g = g.unsqueeze(1)
         beta = beta.unsqueeze(1)
     _check_inputs(q, k, v, g, beta)
-    sh = make_shape(q, v, g, scale, None)
+    sh = make_shape(q, v, g, scale, None, use_qk_l2norm)
     _check_shape(state, "state", _state_shape(sh), torch.float32)
     _check_shape(o, "o", (sh.B, 1, sh.H, sh.Dv), q.dtype)
     if o is None:

@@ -1115,7 +1115,8 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
                const float* __restrict__ dKhi, const float* __restrict__ dPsi,
                const float* __restrict__ dT1i, const float* __restrict__ dgmi,
                const float* __restrict__ dbpi, TIn* __restrict__ dqo, TIn* __restrict__ dko,
-               float* __restrict__ dgo, float* __restrict__ dbo, int T, int H, int NC, float scale)
+               float* __restrict__ dgo, float* __restrict__ dbo, int T, int H, int NC, float scale,
+               const float* __restrict__ rni)
 {
     using G = Geo<C, DK, DV>;
     constexpr int PD = G::PD, PC = G::PC, NB = G::NB;
@@ -1162,6 +1163,13 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
         qv[i] = ok ? qx : 0.f;
         kv[i] = ok ? kx : 0.f;
         dq[i] = dk[i] = dG[i] = dbr[i] = 0.f;
+    }
+    if (rni) {  // use_qk_l2norm: the rows the forward used, r x (dq, dk are then d/dx_hat)
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            qv[i] *= rni[((size_t)ch * 2) * C + p0 + i];
+            kv[i] *= rni[((size_t)ch * 2 + 1) * C + p0 + i];
+        }
     }
     {
         // T, dW and beta: every load issued before the first LDS write
@@ -1339,10 +1347,13 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
 // LDS let two workgroups share a CU, so one loads while the other computes.
 // dbeta (and dg for per-head decay) are row sums over all channels: each half
 // writes its partial sums and bchunk2_finish adds them in a fixed order.
+// With L2N (use_qk_l2norm) q and k rows are scaled by the forward's r and
+// dq, dk are written with respect to the normalised rows; l2norm_bwd maps
+// them to the raw rows, which needs whole rows.
 // ---------------------------------------------------------------------------
 constexpr int NTHR_F = 256;  // 4 waves: one per 16-row part
 
-template <int C, int DK, bool PCH>
+template <int C, int DK, bool PCH, bool L2N>
 __global__ void __launch_bounds__(NTHR_F)
 bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
                 const float* __restrict__ beta, const bf16* __restrict__ dQgi,
@@ -1350,7 +1361,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                 const bf16* __restrict__ dPsi, const bf16* __restrict__ dAi,
                 const float* __restrict__ dgmi, bf16* __restrict__ dqo, bf16* __restrict__ dko,
                 float* __restrict__ dgo, float* __restrict__ dbq, float* __restrict__ dgq, int T,
-                int H, int NC, int nch, float scale)
+                int H, int NC, int nch, float scale, const float* __restrict__ rni)
 {
     static_assert(C == 64, "bchunk2c: chunk 64");
     constexpr int HC = DK / 2;  // key channels per workgroup
@@ -1415,6 +1426,18 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         kv[i] = ok ? kx : 0.f;
         dq[i] = dk[i] = dG[i] = dbr[i] = 0.f;
     }
+    float rq[L2N ? RPP : 1], rk[L2N ? RPP : 1];
+    // per-head decay with L2N: all rows' r (q rows, then k rows) in the bytes
+    // of sR2, which only the per-channel levels use
+    float* sRn = reinterpret_cast<float*>(sbuf + O_R2);
+    if constexpr (L2N) {
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            rq[i] = rni[((size_t)ch * 2) * C + p0 + i];
+            rk[i] = rni[((size_t)ch * 2 + 1) * C + p0 + i];
+        }
+        if (!PCH && tid < 2 * C) sRn[tid] = rni[(size_t)ch * 2 * C + tid];
+    }
     {
         // dPs and dA (C x C bf16): rows as they are, and transposed
         constexpr int NC8 = C * C / 8, NU = (NC8 + NTHR_F - 1) / NTHR_F;
@@ -1464,6 +1487,13 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     }
 #pragma unroll
     for (int i = 0; i < RPP; ++i) a[i] = expf(a[i]);
+    if constexpr (L2N) {  // the rows the forward used
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            qv[i] *= rq[i];
+            kv[i] *= rk[i];
+        }
+    }
     {
         float pt = 1.f;
 #pragma unroll
@@ -1519,6 +1549,12 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         //   Y = scale dP~^T Q + (diag(beta) dA~)^T K  (key side of dk),
         // and dG = q o X + beta k o R - k o Y (the diagonal, E = 1, cancels in dG).
         // Scale the score tables by E in place (rows: E(i, j); transposed: E(j', i')).
+        // With L2N (x_hat = r x) the operand tables hold the raw bf16 rows, and
+        // dP~ takes r_q(i) r_k(j), dA~ r_k(i) r_k(j), in both orientations; the
+        // products X', R', Y' against raw rows then give X = X' / r_q(i),
+        // R = R' / r_k(i), Y = Y' / r_k(j), and dG = q o X' + beta k o R' - k o Y'
+        // with the raw q, k: the plain path's arithmetic, whose pairs (i, j)
+        // cancel in dG's reverse sum because both sides read one rounded value.
         for (int e = tid; e < 2 * C * (C / 8); e += NTHR_F) {
             const bool tr = e >= C * (C / 8);
             const int f = tr ? e - C * (C / 8) : e;
@@ -1528,29 +1564,49 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             uint4 w1 = *reinterpret_cast<const uint4*>(t1), w2 = *reinterpret_cast<const uint4*>(t2);
             uint32_t u1[4] = {w1.x, w1.y, w1.z, w1.w}, u2[4] = {w2.x, w2.y, w2.z, w2.w};
             float ev[8];
+            float ev2[8];
 #pragma unroll
             for (int z = 0; z < 8; ++z) {
                 const int i = tr ? c0 + z : rr, j = tr ? rr : c0 + z;  // element (i, j) of the C x C matrix
                 ev[z] = j <= i ? expf(sG[i] - sG[j]) : 0.f;
+                ev2[z] = ev[z];
+                if constexpr (L2N) {
+                    ev[z] *= sRn[i] * sRn[C + j];
+                    ev2[z] *= sRn[C + i] * sRn[C + j];
+                }
             }
 #pragma unroll
             for (int z = 0; z < 4; ++z) {
                 const float p0v = __uint_as_float(u1[z] << 16) * ev[2 * z], p1v = __uint_as_float(u1[z] & 0xFFFF0000u) * ev[2 * z + 1];
-                const float a0v = __uint_as_float(u2[z] << 16) * ev[2 * z], a1v = __uint_as_float(u2[z] & 0xFFFF0000u) * ev[2 * z + 1];
+                const float a0v = __uint_as_float(u2[z] << 16) * ev2[2 * z], a1v = __uint_as_float(u2[z] & 0xFFFF0000u) * ev2[2 * z + 1];
                 u1[z] = (uint32_t)f32_to_bf16(p0v).bits | ((uint32_t)f32_to_bf16(p1v).bits << 16);
                 u2[z] = (uint32_t)f32_to_bf16(a0v).bits | ((uint32_t)f32_to_bf16(a1v).bits << 16);
             }
             *reinterpret_cast<uint4*>(t1) = uint4{u1[0], u1[1], u1[2], u1[3]};
             *reinterpret_cast<uint4*>(t2) = uint4{u2[0], u2[1], u2[2], u2[3]};
         }
-        // q^T and k^T, channel-major (the level tables with factor 1)
+        // q^T and k^T, channel-major (the level tables with factor 1).  With L2N
+        // the raw rows: x_hat / r is within 2^-23 of the raw bf16 value, far
+        // inside half a bf16 step, so the bf16 rounding gives it back exactly.
+        auto raw_q = [&](int i) {
+            return L2N ? to_f32(f32_to_bf16(qv[i] / sRn[p0 + i])) : qv[i];
+        };
+        auto raw_k = [&](int i) {
+            return L2N ? to_f32(f32_to_bf16(kv[i] / sRn[C + p0 + i])) : kv[i];
+        };
         if (cp) {
+            float qx[RPP], kx[RPP];
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                qx[i] = raw_q(i);
+                kx[i] = raw_k(i);
+            }
 #pragma unroll
             for (int i = 0; i < RPP; i += 8) {
-                const uint2 q0 = pack4_bf16(qv[i], qv[i + 1], qv[i + 2], qv[i + 3]);
-                const uint2 q1 = pack4_bf16(qv[i + 4], qv[i + 5], qv[i + 6], qv[i + 7]);
-                const uint2 k0 = pack4_bf16(kv[i], kv[i + 1], kv[i + 2], kv[i + 3]);
-                const uint2 k1 = pack4_bf16(kv[i + 4], kv[i + 5], kv[i + 6], kv[i + 7]);
+                const uint2 q0 = pack4_bf16(qx[i], qx[i + 1], qx[i + 2], qx[i + 3]);
+                const uint2 q1 = pack4_bf16(qx[i + 4], qx[i + 5], qx[i + 6], qx[i + 7]);
+                const uint2 k0 = pack4_bf16(kx[i], kx[i + 1], kx[i + 2], kx[i + 3]);
+                const uint2 k1 = pack4_bf16(kx[i + 4], kx[i + 5], kx[i + 6], kx[i + 7]);
                 *reinterpret_cast<uint4*>(&sQKT[cl][p0 + i]) = uint4{q0.x, q0.y, q1.x, q1.y};
                 *reinterpret_cast<uint4*>(&sKKT[cl][p0 + i]) = uint4{k0.x, k0.y, k1.x, k1.y};
             }
@@ -1596,10 +1652,18 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             for (int i = 0; i < RPP; ++i) {
                 const int r = p0 + i;
                 const float X = sX[r][cl], R = sRq[r][cl], Y = sY[r][cl], bt = sbeta[r];
-                dq[i] += X;
-                dk[i] += bt * R + Y;
-                dG[i] += qv[i] * X + bt * kv[i] * R - kv[i] * Y;
-                dbr[i] += kv[i] * R;
+                if constexpr (L2N) {
+                    const float qr = raw_q(i), kr = raw_k(i);
+                    dq[i] += X / sRn[r];
+                    dk[i] += (bt * R + Y) / sRn[C + r];
+                    dG[i] += qr * X + bt * kr * R - kr * Y;
+                    dbr[i] += kr * R;
+                } else {
+                    dq[i] += X;
+                    dk[i] += bt * R + Y;
+                    dG[i] += qv[i] * X + bt * kv[i] * R - kv[i] * Y;
+                    dbr[i] += kv[i] * R;
+                }
             }
         }
     } else {
@@ -1832,6 +1896,110 @@ bchunk2_finish_kernel(const float* __restrict__ dbpi, const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// l2norm_bwd: the adjoint of use_qk_l2norm, in place.  dq and dk hold the
+// gradients with respect to the normalised rows x_hat = r x; the raw rows'
+// gradients are dx = r (dx_hat - x_hat (x_hat . dx_hat)).  One row (the Dk
+// values of one token and head) per LPR lanes, 16 bytes per lane; the row dot
+// is a fixed butterfly over those lanes (repeatable).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load16(const bf16* p, float (&x)[8])
+{
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(w[e] << 16);
+        x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void load16(const float* p, float (&x)[4])
+{
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void store16(bf16* p, const float (&x)[8])
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)f32_to_bf16(x[2 * e]).bits | ((uint32_t)f32_to_bf16(x[2 * e + 1]).bits << 16);
+    *reinterpret_cast<uint4*>(p) = uint4{w[0], w[1], w[2], w[3]};
+}
+__device__ __forceinline__ void store16(float* p, const float (&x)[4])
+{
+    *reinterpret_cast<float4*>(p) = float4{x[0], x[1], x[2], x[3]};
+}
+
+constexpr int NTHR_L = 256;
+
+template <typename TIn, int DK>
+__global__ void __launch_bounds__(NTHR_L)
+l2norm_bwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ rn,
+                  TIn* __restrict__ dq, TIn* __restrict__ dk, int T, int H, int NC, int C,
+                  long long ntok)
+{
+    constexpr int EPL = 16 / (int)sizeof(TIn);  // elements per lane
+    constexpr int LPR = DK / EPL;               // lanes per row
+    static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0 && NTHR_L % LPR == 0,
+                  "a row is a power-of-two group of lanes inside one wave");
+    const long long gid = (long long)blockIdx.x * NTHR_L + threadIdx.x;
+    // lanes past the last row work on row 0 (every lane joins the butterfly)
+    // and store nothing
+    const bool ok = gid / LPR < ntok;
+    const long long tok = ok ? gid / LPR : 0;
+    const int ln = (int)(gid % LPR);
+    const int h = (int)(tok % H);
+    const long long bt = tok / H;
+    const int t = (int)(bt % T);
+    const long long b = bt / T;
+    const size_t ch = ((size_t)b * H + h) * NC + t / C;
+    const int r = t % C;
+    const float rq = rn[(ch * 2) * C + r], rk = rn[(ch * 2 + 1) * C + r];
+    const size_t e0 = (size_t)tok * DK + (size_t)ln * EPL;
+    float xq[EPL], xk[EPL], gq[EPL], gk[EPL];
+    load16(q + e0, xq);
+    load16(k + e0, xk);
+    load16(dq + e0, gq);
+    load16(dk + e0, gk);
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        xq[e] *= rq;
+        xk[e] *= rk;
+        sq += xq[e] * gq[e];
+        sk += xk[e] * gk[e];
+    }
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) {
+        sq += __shfl_xor(sq, off);
+        sk += __shfl_xor(sk, off);
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        gq[e] = rq * (gq[e] - xq[e] * sq);
+        gk[e] = rk * (gk[e] - xk[e] * sk);
+    }
+    if (ok) {
+        store16(dq + e0, gq);
+        store16(dk + e0, gk);
+    }
+}
+
+template <typename TIn, int DK>
+gdn_status run_l2norm_bwd(const Plan& p, const void* q, const void* k, void* dq, void* dk,
+                          const char* ws, hipStream_t st)
+{
+    constexpr int LPR = DK / (16 / (int)sizeof(TIn));
+    const long long ntok = (long long)p.B * p.T * p.H;
+    const long long nthr = ntok * LPR;
+    dim3 grid((unsigned)((nthr + NTHR_L - 1) / NTHR_L));
+    GDN_LAUNCH("l2norm_bwd", (l2norm_bwd_kernel<TIn, DK>), grid, dim3(NTHR_L), st, (const TIn*)q,
+               (const TIn*)k, (const float*)(ws + p.o_rn), (TIn*)dq, (TIn*)dk, p.T, p.H, p.NC,
+               p.C, ntok);
+    return GDN_OK;
+}
+
+// ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
 template <typename TIn, int C, int DK, int DV>
@@ -1846,6 +2014,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
         if (s != GDN_OK) return s;
     }
     const int BH = p.B * p.H;
+    const float* rn = p.l2n ? (const float*)(ws + p.o_rn) : nullptr;
     if constexpr (bf16_tables<TIn, C, DK>()) {
         const size_t n = p.n_ch;
         dim3 grid((unsigned)(((BH + 7) / 8) * 8 * (DV / 32))), block(NTHR_B);
@@ -1888,20 +2057,23 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
         // here the dW region holds dX_K and the dT1 region dA (bchunk1b)
         const int nch = (int)p.n_ch;
         dim3 g2((unsigned)(((p.n_ch + 7) / 8) * 16));
-        if (p.decay == GDN_DECAY_PER_CHANNEL)
-            GDN_LAUNCH("bchunk2", (bchunk2c_kernel<C, DK, true>), g2, dim3(NTHR_F), st,
-                       (const bf16*)q, (const bf16*)k, g, beta, (const bf16*)(ws + p.o_dQg),
-                       (const bf16*)(ws + p.o_dWg), (const bf16*)(ws + p.o_dKh),
-                       (const bf16*)(ws + p.o_dPs), (const bf16*)(ws + p.o_dT1),
-                       (const float*)(ws + p.o_dgm), (bf16*)dq, (bf16*)dk, dg,
-                       (float*)(ws + p.o_dbq), (float*)(ws + p.o_dgq), p.T, p.H, p.NC, nch, p.scale);
-        else
-            GDN_LAUNCH("bchunk2", (bchunk2c_kernel<C, DK, false>), g2, dim3(NTHR_F), st,
-                       (const bf16*)q, (const bf16*)k, g, beta, (const bf16*)(ws + p.o_dQg),
-                       (const bf16*)(ws + p.o_dWg), (const bf16*)(ws + p.o_dKh),
-                       (const bf16*)(ws + p.o_dPs), (const bf16*)(ws + p.o_dT1),
-                       (const float*)(ws + p.o_dgm), (bf16*)dq, (bf16*)dk, dg,
-                       (float*)(ws + p.o_dbq), (float*)(ws + p.o_dgq), p.T, p.H, p.NC, nch, p.scale);
+        auto launch2 = [&](auto pch, auto l2n) {
+            GDN_LAUNCH("bchunk2",
+                       (bchunk2c_kernel<C, DK, decltype(pch)::value, decltype(l2n)::value>), g2,
+                       dim3(NTHR_F), st, (const bf16*)q, (const bf16*)k, g, beta,
+                       (const bf16*)(ws + p.o_dQg), (const bf16*)(ws + p.o_dWg),
+                       (const bf16*)(ws + p.o_dKh), (const bf16*)(ws + p.o_dPs),
+                       (const bf16*)(ws + p.o_dT1), (const float*)(ws + p.o_dgm), (bf16*)dq,
+                       (bf16*)dk, dg, (float*)(ws + p.o_dbq), (float*)(ws + p.o_dgq), p.T, p.H,
+                       p.NC, nch, p.scale, rn);
+            return GDN_OK;
+        };
+        using TT = std::true_type;
+        using FF = std::false_type;
+        gdn_status s2 = p.decay == GDN_DECAY_PER_CHANNEL
+                            ? (p.l2n ? launch2(TT{}, TT{}) : launch2(TT{}, FF{}))
+                            : (p.l2n ? launch2(FF{}, TT{}) : launch2(FF{}, FF{}));
+        if (s2 != GDN_OK) return s2;
         const long long tot = (long long)p.n_ch * C;
         dim3 gf((unsigned)((tot + 255) / 256));
         if (p.decay == GDN_DECAY_PER_CHANNEL)
@@ -1912,6 +2084,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
             GDN_LAUNCH("bchunk2_finish", (bchunk2_finish_kernel<false>), gf, dim3(256), st,
                        (const float*)(ws + p.o_dbp), (const float*)(ws + p.o_dbq),
                        (const float*)(ws + p.o_dgq), dbeta, dg, p.T, p.H, p.NC, C, tot);
+        if (p.l2n) return run_l2norm_bwd<TIn, DK>(p, q, k, dq, dk, ws, st);
         return GDN_OK;
     }
     if (p.decay == GDN_DECAY_PER_CHANNEL)
@@ -1921,7 +2094,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                            (const float*)(ws + p.o_dKh), (const float*)(ws + p.o_dPs),
                            (const float*)(ws + p.o_dT1), (const float*)(ws + p.o_dgm),
                            (const float*)(ws + p.o_dbp), (TIn*)dq, (TIn*)dk, dg, dbeta, p.T, p.H,
-                           p.NC, p.scale);
+                           p.NC, p.scale, rn);
     else
         GDN_LAUNCH("bchunk2", (bchunk2_kernel<TIn, C, DK, DV, false, MT>), gch, dim3(NTHR2), st,
                            (const TIn*)q, (const TIn*)k, g, beta, (const float*)(ws + p.o_Tm),
@@ -1929,8 +2102,9 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                            (const float*)(ws + p.o_dKh), (const float*)(ws + p.o_dPs),
                            (const float*)(ws + p.o_dT1), (const float*)(ws + p.o_dgm),
                            (const float*)(ws + p.o_dbp), (TIn*)dq, (TIn*)dk, dg, dbeta, p.T, p.H,
-                           p.NC, p.scale);
+                           p.NC, p.scale, rn);
     GDN_HIP_CHECK_LAUNCH();
+    if (p.l2n) return run_l2norm_bwd<TIn, DK>(p, q, k, dq, dk, ws, st);
     return GDN_OK;
 }
 

@@ -43,12 +43,12 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
             const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int NC,
             float scale, float* __restrict__ Wo, float* __restrict__ Uo, float* __restrict__ Qgo,
             float* __restrict__ Kho, float* __restrict__ Pso, float* __restrict__ gamo,
-            float* __restrict__ Tmo)
+            float* __restrict__ Tmo, float* __restrict__ rno)
 {
     using G = Geo<C, DK, DV>;
     constexpr int PD = G::PD, PC = G::PC, NB = G::NB, HALF = G::HALF;
     __shared__ float sq[C][PD], sk[C][PD], sX[C][PD], sY[C][PD], sA[C][PC];
-    __shared__ float sbeta[C], sdiag[C], stot[2][DK];
+    __shared__ float sbeta[C], sdiag[C], stot[2][DK], sRn[2 * C];
 
     const int ch = blockIdx.x;
     const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
@@ -86,6 +86,29 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
         a[i] = expf(gv);
     }
     __syncthreads();
+
+    // ---- use_qk_l2norm (rno set): every q and k row scaled by
+    // r = 1/sqrt(|x|^2 + eps) in place; r kept in rno for the backward
+    if (rno) {
+        for (int r = tid; r < 2 * C; r += NTHR) {
+            const float* row = r < C ? &sq[r][0] : &sk[r - C][0];
+            float s = 0.f;
+            for (int cc = 0; cc < DK; ++cc) {
+                const float x = row[(cc + r) % DK];  // skewed to spread LDS banks
+                s += x * x;
+            }
+            const float rr = 1.f / sqrtf(s + GDN_L2NORM_EPS);
+            sRn[r] = rr;
+            rno[(size_t)ch * 2 * C + r] = rr;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < C * DK; idx += NTHR) {
+            const int r = idx / DK, cc = idx % DK;
+            sq[r][cc] *= sRn[r];
+            sk[r][cc] *= sRn[C + r];
+        }
+        __syncthreads();
+    }
 
     // ---- diagonal scores P_ii = q_i . k_i
     for (int r = tid; r < C; r += NTHR) {
@@ -369,17 +392,21 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
 // (one 16-byte LDS read per MFMA operand); the diagonal scores are a chain of
 // the unscaled rows kept on the diagonal; W = T X_K and U = T X_V are bf16
 // MFMA products with X_K^T, X_V^T written by the column threads.
+// With L2N (use_qk_l2norm) every q and k row is scaled by r = 1/sqrt(|x|^2 +
+// eps): the squared lengths are the diagonals of the Q Q^T and K K^T tiles of
+// the raw rows, r is folded into the products of raw rows and into the rows
+// each thread keeps, and r goes to rno for the backward.
 // ---------------------------------------------------------------------------
 constexpr int NTHR_P = 512;
 
-template <int C, int DK, int DV, bool PCH>
+template <int C, int DK, int DV, bool PCH, bool L2N>
 __global__ void __launch_bounds__(NTHR_P, 4)
 prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
              const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int NC,
              float scale, bf16* __restrict__ Wb, bf16* __restrict__ WTb, float* __restrict__ Uo,
              bf16* __restrict__ Qgb, bf16* __restrict__ QgTb, bf16* __restrict__ KhTb,
              bf16* __restrict__ Khb, bf16* __restrict__ Psb, bf16* __restrict__ PsTb,
-             float* __restrict__ gamo, float* __restrict__ Tmo)
+             float* __restrict__ gamo, float* __restrict__ Tmo, float* __restrict__ rno)
 {
     static_assert(C == 64 && DK == DV, "prep2: chunk 64, Dk == Dv");
     constexpr int NW = NTHR_P / 64, RPP = 16, NPART = C / RPP, NB = C / 16;
@@ -392,6 +419,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     __shared__ __align__(16) bf16 sXT[DK][PT];  // X_K^T, then X_V^T
     __shared__ float sbeta[C], stot[NPART][DK];
     __shared__ float sG[C];  // per-head decay: chunk-local inclusive cumsum of g
+    __shared__ float sRn[2][L2N ? C : 1];  // L2N: 1/sqrt(|q_i|^2 + eps), same for k
     bf16 (*sX)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf);
     bf16 (*sY)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf + C * PA * 2);
     float (*sT)[PC] = reinterpret_cast<float (*)[PC]>(sbuf);
@@ -453,6 +481,36 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         }
     }
     __syncthreads();
+    // L2N, waves w < NB: squared lengths of rows 16w.. from the raw tables
+    // (published to sRn by the next barrier)
+    auto row_norms = [&]() {
+        if constexpr (L2N) {
+            const f32x4 nq = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sX[w * 16][0], PA);
+            const f32x4 nk = mma_kc<DK>(zero4(), &sY[w * 16][0], PA, &sY[w * 16][0], PA);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (4 * lq + r == lr) {
+                    const int i = w * 16 + lr;
+                    const float rq = 1.f / sqrtf(nq[r] + GDN_L2NORM_EPS);
+                    const float rk = 1.f / sqrtf(nk[r] + GDN_L2NORM_EPS);
+                    sRn[0][i] = rq;
+                    sRn[1][i] = rk;
+                    rno[((size_t)ch * 2) * C + i] = rq;
+                    rno[((size_t)ch * 2 + 1) * C + i] = rk;
+                }
+            }
+        }
+    };
+    // L2N, after the barrier that publishes sRn: the rows this thread keeps
+    auto scale_rows = [&]() {
+        if constexpr (L2N) {
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                qv[i] *= sRn[0][p0 + i];
+                kv[i] *= sRn[1][p0 + i];
+            }
+        }
+    };
     f32x4 dP = zero4(), dA = zero4();
     // off-diagonal 16-tiles: waves NB.. own tile idx with (idx % (NW - NB)) == w - NB
     constexpr int OW = NW - NB, MOFF = (NOFF + OW - 1) / OW;
@@ -467,6 +525,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         if (w < NB) {
             const f32x4 tp = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sY[w * 16][0], PA);
             const f32x4 ta = mma_kc<DK>(zero4(), &sY[w * 16][0], PA, &sY[w * 16][0], PA);
+            row_norms();
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 4 * lq + r, j = lr;
@@ -493,13 +552,48 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             }
         }
         __syncthreads();
+        if constexpr (L2N) {  // products of raw rows times r_i r_j
+            if (w < NB) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = w * 16 + 4 * lq + r, j = w * 16 + lr;
+                    dP[r] *= sRn[0][i] * sRn[1][j];
+                    dA[r] *= sRn[1][i] * sRn[1][j];
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < MOFF; ++m) {
+                    const int idx = (w - NB) + OW * m;
+                    if (idx < NOFF) {
+                        int ti, tj;
+                        off_tile(idx, ti, tj);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                            accP[m][r] *= sRn[0][i] * sRn[1][j];
+                            accA[m][r] *= sRn[1][i] * sRn[1][j];
+                        }
+                    }
+                }
+            }
+            scale_rows();
+        }
     } else {
     if (w < NB) {
         const f32x4 tp = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sY[w * 16][0], PA);
+        row_norms();
 #pragma unroll
         for (int r = 0; r < 4; ++r) dP[r] = (4 * lq + r == lr) ? tp[r] : 0.f;
     }
     __syncthreads();
+    if constexpr (L2N) {
+        if (w < NB) {  // P_ii of the raw rows times r_q r_k
+            const int i = w * 16 + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dP[r] *= sRn[0][i] * sRn[1][i];
+        }
+    }
+    scale_rows();  // the level tables below are built from the normalised rows
 
 #pragma unroll
     for (int lvl = 0; (C >> (lvl + 1)) >= 1; ++lvl) {
@@ -1156,6 +1250,7 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
     float* Ps = (float*)(ws + p.o_Ps);
     float* gam = (float*)(ws + p.o_gam);
     float* Tm = want_T ? (float*)(ws + p.o_Tm) : nullptr;
+    float* rn = p.l2n ? (float*)(ws + p.o_rn) : nullptr;
     dim3 grid((unsigned)p.n_ch), block(NTHR);
     if constexpr (bf16_tables<TIn, C, DK>()) {
         const size_t n = p.n_ch;
@@ -1163,26 +1258,28 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
         bf16* Qb = (bf16*)Qg;
         bf16* Kb = (bf16*)Kh;
         bf16* Pb = (bf16*)Ps;
+        auto launch = [&](auto pch, auto l2n) {
+            GDN_LAUNCH(want_T ? "prep_T" : "prep",
+                       (prep2_kernel<C, DK, DV, decltype(pch)::value, decltype(l2n)::value>), grid,
+                       dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g, beta,
+                       p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, U, Qb, Qb + n * C * DK, Kb,
+                       Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm, rn);
+            return GDN_OK;
+        };
+        using TT = std::true_type;
+        using FF = std::false_type;
         if (p.decay == GDN_DECAY_PER_CHANNEL)
-            GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep2_kernel<C, DK, DV, true>), grid,
-                       dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g, beta,
-                       p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, U, Qb, Qb + n * C * DK, Kb,
-                       Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm);
-        else
-            GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep2_kernel<C, DK, DV, false>), grid,
-                       dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g, beta,
-                       p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, U, Qb, Qb + n * C * DK, Kb,
-                       Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm);
-        return GDN_OK;
+            return p.l2n ? launch(TT{}, TT{}) : launch(TT{}, FF{});
+        return p.l2n ? launch(FF{}, TT{}) : launch(FF{}, FF{});
     }
     if (p.decay == GDN_DECAY_PER_CHANNEL)
         GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep_kernel<TIn, C, DK, DV, true, MT>), grid, block, st,
                            (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
-                           p.scale, W, U, Qg, Kh, Ps, gam, Tm);
+                           p.scale, W, U, Qg, Kh, Ps, gam, Tm, rn);
     else
         GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep_kernel<TIn, C, DK, DV, false, MT>), grid, block, st,
                            (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
-                           p.scale, W, U, Qg, Kh, Ps, gam, Tm);
+                           p.scale, W, U, Qg, Kh, Ps, gam, Tm, rn);
     GDN_HIP_CHECK_LAUNCH();
     return GDN_OK;
 }

@@ -8,10 +8,16 @@
 // between the read and the write, and reduces the two Dk-contractions
 // (S'^T k and S'^T q) across lanes (cross-lane shuffles) and across waves (LDS).
 //
+// With L2N (use_qk_l2norm) q and k are first scaled to unit length,
+// x / sqrt(|x|^2 + eps).  S'^T k, S'^T q and q.k are linear in them, so the
+// squared lengths are reduced alongside and the three results rescaled.
+//
 // Thread map: a state row is Dv floats = Dv/4 float4 lanes (VPR).  Thread t
 // owns float4 column c4 = t % VPR of rows r0 + p*RPP, r0 = t / VPR,
 // RPP = NT / VPR, p = 0 .. Dk/RPP - 1.  Consecutive threads touch
 // consecutive 16-byte words of a row, so every load and store is coalesced.
+#include <type_traits>
+
 #include "common.h"
 
 namespace gdn {
@@ -27,7 +33,7 @@ struct DecodeCfg {
     static_assert(64 % VPR == 0 || VPR % 64 == 0, "row must tile a wave");
 };
 
-template <typename TIn, int DK, int DV, bool PER_CHANNEL>
+template <typename TIn, int DK, int DV, bool PER_CHANNEL, bool L2N>
 __global__ void __launch_bounds__((DecodeCfg<DK, DV>::NT))
 decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
               const float* __restrict__ g, const float* __restrict__ beta,
@@ -51,7 +57,7 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
     float a_head = 0.f;
     if (!PER_CHANNEL) a_head = fast_exp(g[bh]);
     float kr[C::NP];
-    float mk[4] = {0.f, 0.f, 0.f, 0.f}, mq[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;
+    float mk[4] = {0.f, 0.f, 0.f, 0.f}, mq[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f, qq = 0.f, kk = 0.f;
 #pragma unroll
     for (int p = 0; p < C::NP; ++p) {
         const int row = r0 + p * C::RPP;
@@ -63,6 +69,10 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
         mk[0] += kv * s[p].x; mk[1] += kv * s[p].y; mk[2] += kv * s[p].z; mk[3] += kv * s[p].w;
         mq[0] += qv * s[p].x; mq[1] += qv * s[p].y; mq[2] += qv * s[p].z; mq[3] += qv * s[p].w;
         qk += qv * kv;
+        if (L2N) {
+            qq += qv * qv;
+            kk += kv * kv;
+        }
     }
     // reduce over the row groups inside a wave (lanes that share c4)
 #pragma unroll
@@ -73,9 +83,13 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
             mq[e] += __shfl_xor(mq[e], off);
         }
         qk += __shfl_xor(qk, off);
+        if (L2N) {
+            qq += __shfl_xor(qq, off);
+            kk += __shfl_xor(kk, off);
+        }
     }
     // reduce across waves through LDS, in a fixed order (deterministic)
-    __shared__ float red[C::NW][C::VPR][9];
+    __shared__ float red[C::NW][C::VPR][11];
     if (C::NW > 1) {
         const int w = t / 64;
         if ((t % 64) < C::VPR) {
@@ -85,6 +99,8 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
                 red[w][c4][4 + e] = mq[e];
             }
             red[w][c4][8] = qk;
+            red[w][c4][9] = qq;
+            red[w][c4][10] = kk;
         }
         __syncthreads();
 #pragma unroll
@@ -98,10 +114,27 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
             mk[e] = a1;
             mq[e] = a2;
         }
-        float a3 = red[0][c4][8];
+        float a3 = red[0][c4][8], a4 = red[0][c4][9], a5 = red[0][c4][10];
 #pragma unroll
-        for (int ww = 1; ww < C::NW; ++ww) a3 += red[ww][c4][8];
+        for (int ww = 1; ww < C::NW; ++ww) {
+            a3 += red[ww][c4][8];
+            a4 += red[ww][c4][9];
+            a5 += red[ww][c4][10];
+        }
         qk = a3;
+        qq = a4;
+        kk = a5;
+    }
+    if (L2N) {
+        const float rq = 1.f / sqrtf(qq + GDN_L2NORM_EPS), rk = 1.f / sqrtf(kk + GDN_L2NORM_EPS);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            mk[e] *= rk;
+            mq[e] *= rq;
+        }
+        qk *= rq * rk;
+#pragma unroll
+        for (int p = 0; p < C::NP; ++p) kr[p] *= rk;
     }
     const float bt = beta[bh];
     float d[4], ov[4];
@@ -130,14 +163,17 @@ static gdn_status launch_decode(const gdn_shape* sh, const void* q, const void* 
 {
     using C = DecodeCfg<DK, DV>;
     dim3 grid(sh->B * sh->H), block(C::NT);
+    auto launch = [&](auto pch, auto l2n) {
+        GDN_LAUNCH("decode", (decode_kernel<TIn, DK, DV, decltype(pch)::value, decltype(l2n)::value>),
+                   grid, block, st, (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, state,
+                   (TIn*)o, sh->H, scale);
+        return GDN_OK;
+    };
+    using TT = std::true_type;
+    using FF = std::false_type;
     if (sh->decay == GDN_DECAY_PER_CHANNEL)
-        GDN_LAUNCH("decode", (decode_kernel<TIn, DK, DV, true>), grid, block, st, (const TIn*)q,
-                           (const TIn*)k, (const TIn*)v, g, beta, state, (TIn*)o, sh->H, scale);
-    else
-        GDN_LAUNCH("decode", (decode_kernel<TIn, DK, DV, false>), grid, block, st, (const TIn*)q,
-                           (const TIn*)k, (const TIn*)v, g, beta, state, (TIn*)o, sh->H, scale);
-    GDN_HIP_CHECK_LAUNCH();
-    return GDN_OK;
+        return sh->qk_l2norm ? launch(TT{}, TT{}) : launch(TT{}, FF{});
+    return sh->qk_l2norm ? launch(FF{}, TT{}) : launch(FF{}, FF{});
 }
 
 template <typename TIn>

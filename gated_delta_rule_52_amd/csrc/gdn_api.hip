@@ -45,6 +45,7 @@ static gdn_status check_shape(const gdn_shape* sh, bool decode)
     if (sh->decay != GDN_DECAY_PER_HEAD && sh->decay != GDN_DECAY_PER_CHANNEL)
         return GDN_ERR_INVALID_ARG;
     if (!(sh->scale >= 0.f)) return GDN_ERR_INVALID_ARG;  // rejects NaN and negatives
+    if (sh->qk_l2norm != 0 && sh->qk_l2norm != 1) return GDN_ERR_INVALID_ARG;
     if (decode && sh->T != 1) return GDN_ERR_INVALID_ARG;
     if (!dim_ok(sh->Dk) || !dim_ok(sh->Dv)) return GDN_ERR_UNSUPPORTED;
     if (!decode) {

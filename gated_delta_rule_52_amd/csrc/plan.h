@@ -10,6 +10,8 @@
 //   Kh  [ch][C][Dk]   Kh = K o exp(G_{C-1} - G)            (key write into the next state)
 //   Ps  [ch][C][C]    Ps = scale * P  (decayed query-key scores, lower incl. diagonal)
 //   gam [ch][Dk]      gam = exp(G_{C-1})                   (whole-chunk decay)
+//   rn  [ch][2][C]    with qk_l2norm: 1 / sqrt(|q_t|^2 + eps) (row 0) and the
+//                     same for k_t (row 1); the backward scales q, k by them
 // backward only:
 //   Tm  [ch][C][C]    T = (I + A)^-1
 //   Sst [ch][Dk][Dv]  state at the start of chunk n
@@ -38,10 +40,11 @@ namespace gdn {
 
 struct Plan {
     int B, T, H, Dk, Dv, C, NC, dtype, decay;
+    bool l2n;  // qk_l2norm
     float scale;
     size_t n_ch;  // B * H * NC
     // byte offsets into the workspace
-    size_t o_W, o_U, o_Qg, o_Kh, o_Ps, o_gam, o_Tm, o_Sst, o_dSt, o_dDt;
+    size_t o_W, o_U, o_Qg, o_Kh, o_Ps, o_gam, o_rn, o_Tm, o_Sst, o_dSt, o_dDt;
     size_t o_dQg, o_dWg, o_dKh, o_dPs, o_dT1, o_dgm, o_dbp, o_Dst, o_dbq, o_dgq;
     size_t ws_fwd_bytes, ws_bwd_bytes;
 };
@@ -63,6 +66,7 @@ inline Plan make_plan(const gdn_shape& s, float scale)
     p.C = s.chunk ? s.chunk : 64;
     p.NC = (s.T + p.C - 1) / p.C;
     p.dtype = s.dtype; p.decay = s.decay; p.scale = scale;
+    p.l2n = s.qk_l2norm != 0;
     p.n_ch = (size_t)s.B * s.H * p.NC;
     const size_t f = sizeof(float), n = p.n_ch, C = p.C, Dk = p.Dk, Dv = p.Dv;
     size_t off = 0;
@@ -72,6 +76,7 @@ inline Plan make_plan(const gdn_shape& s, float scale)
     p.o_Kh = off;  off = align256(off + n * C * Dk * f);
     p.o_Ps = off;  off = align256(off + n * C * C * f);
     p.o_gam = off; off = align256(off + n * Dk * f);
+    p.o_rn = off;  off = align256(off + (p.l2n ? n * 2 * C * f : 0));
     p.ws_fwd_bytes = off;
     p.o_Tm = off;  off = align256(off + n * C * C * f);
     p.o_Sst = off; off = align256(off + n * Dk * Dv * f);

@@ -19,6 +19,10 @@ not use are skipped.
   t % wipe_period == wipe_period - 1 (all b, h, channels).
 * h0 ~ N(0, h0_std) (standard deviation), float32.
 * dO ~ N(0, 1) in the input dtype, dhT ~ N(0, 0.01) float32.
+* raw q, k (qk_scale set; for the use_qk_l2norm option, which normalises
+  inside the layer): the N(0, 1) rows are not normalised but multiplied by
+  exp(qk_scale * z), z ~ N(0, 1), one factor per row, drawn last (q's factors,
+  then k's), so every other draw is unchanged; meta["qk_l2norm"] is set.
 
 Every tensor is rounded to float32; bf16 tensors (q, k, v, dO in bf16 mode) are
 then rounded to nearest-even from the float32 bits.  ``as_f64`` gives the exact
@@ -66,14 +70,17 @@ def _sigmoid(z: np.ndarray) -> np.ndarray:
 def make_inputs(B: int, T: int, H: int, Dk: int, Dv: int, *, decay: str = "channel",
                 dtype: str = "f32", seed: int = 0, h0_std: float | None = None,
                 wipe_period: int | None = None, wipe_value: float = -20.0,
-                grads: bool = False, dO_std: float = 1.0, dhT_std: float = 0.01) -> dict:
+                grads: bool = False, dO_std: float = 1.0, dhT_std: float = 0.01,
+                qk_scale: float | None = None) -> dict:
     """Draw one workload.  Returns a dict of numpy arrays in device form
     (float32, or uint16 bf16 bits for q/k/v/dO when dtype == 'bf16') plus the
     shape metadata under 'meta'."""
     assert decay in ("channel", "head") and dtype in ("f32", "bf16")
     rng = np.random.Generator(np.random.PCG64(seed))
-    q = _l2n(rng.standard_normal((B, T, H, Dk)))
-    k = _l2n(rng.standard_normal((B, T, H, Dk)))
+    q = rng.standard_normal((B, T, H, Dk))
+    k = rng.standard_normal((B, T, H, Dk))
+    if qk_scale is None:
+        q, k = _l2n(q), _l2n(k)
     v = rng.standard_normal((B, T, H, Dv))
     beta = _sigmoid(rng.standard_normal((B, T, H)))
     gshape = (B, T, H, Dk) if decay == "channel" else (B, T, H)
@@ -89,6 +96,9 @@ def make_inputs(B: int, T: int, H: int, Dk: int, Dv: int, *, decay: str = "chann
         dhT = rng.standard_normal((B, H, Dk, Dv)) * dhT_std
         out["dO"] = dO
         out["dhT"] = dhT
+    if qk_scale is not None:
+        q = q * np.exp(qk_scale * rng.standard_normal((B, T, H, 1)))
+        k = k * np.exp(qk_scale * rng.standard_normal((B, T, H, 1)))
     out.update(q=q, k=k, v=v, beta=beta, g=g)
     if h0 is not None:
         out["h0"] = h0
@@ -100,7 +110,7 @@ def make_inputs(B: int, T: int, H: int, Dk: int, Dv: int, *, decay: str = "chann
         else:
             res[name] = x32
     res["meta"] = dict(B=B, T=T, H=H, Dk=Dk, Dv=Dv, decay=decay, dtype=dtype, seed=seed,
-                       scale=float(np.float32(Dk ** -0.5)))
+                       scale=float(np.float32(Dk ** -0.5)), qk_l2norm=qk_scale is not None)
     return res
 
 
@@ -140,10 +150,12 @@ def decode(seed: int = 0, B: int = 256, H: int = 16, steps: int = 64) -> dict:
 
 
 def train(seed: int = 0, B: int = 8, dtype: str = "bf16", grads: bool = False,
-          T: int = 4096, H: int = 6, D: int = 128, decay: str = "channel") -> dict:
+          T: int = 4096, H: int = 6, D: int = 128, decay: str = "channel",
+          qk_scale: float | None = None) -> dict:
     """Training shape: per-channel decay (or per-head), B=8 (or 4) T=4096 H=6
     128x128, zero state; with grads, dO ~ N(0,1) in the input dtype and
-    dhT ~ N(0, 0.01)."""
-    d = make_inputs(B, T, H, D, D, decay=decay, dtype=dtype, seed=seed, grads=grads)
+    dhT ~ N(0, 0.01); with qk_scale, raw q, k for use_qk_l2norm."""
+    d = make_inputs(B, T, H, D, D, decay=decay, dtype=dtype, seed=seed, grads=grads,
+                    qk_scale=qk_scale)
     d["meta"]["chunk"] = 64
     return d

@@ -26,8 +26,14 @@
  *   dq, dk    [B, T, H, Dk] (dtype);  dv [B, T, H, Dv] (dtype)
  *   dg        like g (float32);  dbeta [B, T, H] (float32)
  * Grouped-query repetition of q/k heads is the caller's (gated-deltanet card,
- * "Requirements and limits").  q and k are used as given: callers that want
- * L2-normalised keys normalise them first.
+ * "Requirements and limits").  q and k are used as given unless the shape's
+ * qk_l2norm is set (the card's use_qk_l2norm, "Usage"): then every q and k row
+ * (the Dk values of one token and head) is replaced inside the call by
+ * x / sqrt(sum(x^2) + GDN_L2NORM_EPS) before the recurrence, and dq, dk are the
+ * gradients with respect to the raw, unnormalised rows,
+ * dx = r (dx_hat - x_hat (x_hat . dx_hat)) with r = 1 / sqrt(sum(x^2) + eps).
+ * The card names the option but not its guard; 1e-6 inside the root is the
+ * reading taken here.
  *
  * Errors: every call returns a status.  Bad shapes, NULL required pointers,
  * misaligned pointers and a too-small workspace are rejected before anything
@@ -63,12 +69,17 @@ typedef enum {
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 typedef enum { GDN_DECAY_PER_HEAD = 0, GDN_DECAY_PER_CHANNEL = 1 } gdn_decay;
 
+#define GDN_L2NORM_EPS 1e-6f
+
 typedef struct {
     int B, T, H, Dk, Dv;
-    int dtype;   /* gdn_dtype of q, k, v, o, dO, dq, dk, dv */
-    int decay;   /* gdn_decay */
-    float scale; /* output scale; 0 means Dk^-0.5 (the atomic_ops card passes d^-0.5) */
-    int chunk;   /* chunk length C of the chunked form: 16 or 64; 0 means 64 */
+    int dtype;     /* gdn_dtype of q, k, v, o, dO, dq, dk, dv */
+    int decay;     /* gdn_decay */
+    float scale;   /* output scale; 0 means Dk^-0.5 (the atomic_ops card passes d^-0.5) */
+    int chunk;     /* chunk length C of the chunked form: 16 or 64; 0 means 64 */
+    int qk_l2norm; /* 1: L2-normalise q and k rows inside the call (see above); 0: as given.
+                      A training pair (gdn_forward_train, gdn_backward_train) must pass the
+                      same value to both calls. */
 } gdn_shape;
 
 /*

@@ -53,13 +53,19 @@ def test_workspace_query():
     assert 0 < fwd < bwd
     assert fwd % 256 == 0 and bwd % 256 == 0
     for bad in (dict(Dk=100, Dv=100), dict(chunk=32), dict(B=0), dict(dtype=7), dict(decay=3),
-                dict(Dk=64, Dv=128)):
+                dict(Dk=64, Dv=128), dict(qk_l2norm=2)):
         assert L.gdn_workspace_bytes(ctypes.byref(_shape(**bad)), 0) == 0, bad
+    # use_qk_l2norm adds the per-row scale table [chunk-heads][2][C] fp32 to both sizes
+    sh_n = _shape(qk_l2norm=1)
+    n_ch = 2 * 3 * 2
+    extra = -(-(n_ch * 2 * 64 * 4) // 256) * 256
+    assert L.gdn_workspace_bytes(ctypes.byref(sh_n), 0) == fwd + extra
+    assert L.gdn_workspace_bytes(ctypes.byref(sh_n), 1) == bwd + extra
 
 
 @pytest.mark.parametrize("bad,code", [
     (dict(B=0), 1), (dict(T=-1), 1), (dict(dtype=5), 1), (dict(decay=9), 1),
-    (dict(scale=-1.0), 1), (dict(Dk=48, Dv=48), 2), (dict(chunk=32), 2),
+    (dict(scale=-1.0), 1), (dict(Dk=48, Dv=48), 2), (dict(chunk=32), 2), (dict(qk_l2norm=-1), 1),
 ])
 def test_forward_rejects_bad_shapes_before_launch(bad, code):
     L = gdn.lib()
