@@ -183,6 +183,8 @@ def main():
     ap.add_argument("--no-head", action="store_true", help="skip the per-head decay measurement")
     ap.add_argument("--no-l2norm", action="store_true",
                     help="skip the use_qk_l2norm (raw q, k) measurement")
+    ap.add_argument("--no-safety", action="store_true",
+                    help="skip the numerical-safety options measurement (wy_eps, clip, diag)")
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward-only measurement (profiling runs: one launch name per kernel)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -440,6 +442,52 @@ def main():
         log("[bench] use_qk_l2norm kernels: " + ", ".join(f"{n} {u:.0f} us" for n, u in lker.items())
             + f"; l2norm_bwd at {100 * lroof['frac']:.1f}% of HBM peak")
 
+    # ---- numerical-safety options on the main workload: damping, a bound, counters
+    safety = None
+    if not args.no_safety:
+        from oracle import chunked
+        sopt = dict(wy_eps=1e-3, clip=1e4, diag=True)
+        ssh = gdn.make_shape(q, v, g, scale, C, **sopt)
+        sws_b = gdn.workspace(ssh, True, q.device)
+
+        def sstep():
+            gdn.gdn_forward_train(q, k, v, g, beta, None, scale=scale, chunk=C, o=o, hT=hT,
+                                  ws=sws_b, **sopt)
+            return gdn.gdn_backward_train(q, k, v, g, beta, dO, sws_b, dhT, scale=scale, chunk=C,
+                                          out=gout, **sopt)
+
+        sstep()
+        counts = gdn.gdn_diag_read(ssh, sws_b)
+        sp = [(0, 0), (B - 1, H - 1)]
+        ss = {n: np.stack([inp[n][b, :, h] for b, h in sp], axis=1)[None]
+              for n in ("q", "k", "v", "g", "beta")}
+        so_ref, sh_ref = chunked.forward(ss["q"], ss["k"], ss["v"], ss["g"], ss["beta"], scale,
+                                         chunk=C, wy_eps=sopt["wy_eps"], clip=sopt["clip"])
+        spar = {"o": rel(np.stack([pick(o, b, h) for b, h in sp], 1)[None], so_ref),
+                "hT": rel(np.stack([hT[b, h].cpu().numpy() for b, h in sp])[None], sh_ref)}
+        for _ in range(args.warmup):
+            sstep()
+        torch.cuda.synchronize()
+        srec = LaunchRecorder(args.steps * 32 + 32)
+        ev0.record()
+        with srec:
+            for _ in range(args.steps):
+                sstep()
+        ev1.record()
+        torch.cuda.synchronize()
+        sms = ev0.elapsed_time(ev1) / args.steps
+        sker = {n: float(np.mean(ms)) * 1e3 for n, ms in srec.by_kernel().items()}
+        scnt = {n: len(ms) // args.steps for n, ms in srec.by_kernel().items()}
+        srec.close()
+        safety = {"workload": "main workload with wy_eps=1e-3, clip=1e4, diag on (training pair)",
+                  "fwdbwd_tokens_per_s": B * T / (sms * 1e-3), "ms_per_step": sms,
+                  "kernels_avg_us": sker, "launches_per_step": scnt, "diag_counts": counts,
+                  "parity_max_rel_err_fwd": spar, "parity_ok": all(e <= tol for e in spar.values())}
+        log(f"[bench] safety options: fwd+bwd {sms:.3f} ms ({safety['fwdbwd_tokens_per_s'] / 1e6:.2f} M tokens/s); "
+            f"fwd parity vs chunked oracle " + ", ".join(f"{k_} {e:.1e}" for k_, e in spar.items())
+            + f"; counts {counts}")
+        log("[bench] safety kernels: " + ", ".join(f"{n} {u:.0f} us x{scnt[n]}" for n, u in sker.items()))
+
     # ---- decode: B=256 H=16 128x128 fp32 state, one token per step
     decode = None
     if not args.no_decode:
@@ -532,6 +580,7 @@ def main():
         "roofline": roof,
         "per_head": head,
         "qk_l2norm": l2,
+        "safety_options": safety,
         "decode": decode,
         "cpu_baseline": cpu,
     }

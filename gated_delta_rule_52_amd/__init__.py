@@ -18,7 +18,9 @@ beta [B,T,H] (fp32); states [B,H,Dk,Dv] fp32.  q, k, v share one dtype
 library scale every q and k row to unit length, x / sqrt(|x|^2 + 1e-6), inside
 the call (the card's option of that name); dq, dk are then the gradients with
 respect to the raw rows, and a training pair must pass the same value to both
-calls.
+calls.  The numerical-safety options of the chunked calls (wy_eps damping of
+the WY solve, clip at the stage boundaries, diag stage counters read back with
+gdn_diag_read) follow include/gdn.h.
 """
 from __future__ import annotations
 
@@ -35,7 +37,8 @@ GDN_DECAY_PER_HEAD, GDN_DECAY_PER_CHANNEL = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_ALIGNMENT",
           4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
 EXPORTS = ("gdn_new_state", "gdn_workspace_bytes", "gdn_forward", "gdn_backward",
-           "gdn_forward_train", "gdn_backward_train", "gdn_decode_step", "gdn_status_string",
+           "gdn_forward_train", "gdn_backward_train", "gdn_decode_step", "gdn_diag_read",
+           "gdn_status_string",
            # include/gdn_profile.h
            "gdn_profile_begin", "gdn_profile_end", "gdn_profile_launch_name")
 
@@ -44,7 +47,8 @@ class GdnShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
                 ("Dk", ctypes.c_int), ("Dv", ctypes.c_int), ("dtype", ctypes.c_int),
                 ("decay", ctypes.c_int), ("scale", ctypes.c_float), ("chunk", ctypes.c_int),
-                ("qk_l2norm", ctypes.c_int)]
+                ("qk_l2norm", ctypes.c_int), ("wy_eps", ctypes.c_float), ("clip", ctypes.c_float),
+                ("diag", ctypes.c_int)]
 
 
 class GdnError(RuntimeError):
@@ -81,6 +85,8 @@ def lib():
         L.gdn_backward_train.restype = i
         L.gdn_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_decode_step.restype = i
+        L.gdn_diag_read.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_uint), vp]
+        L.gdn_diag_read.restype = i
         L.gdn_status_string.argtypes = [i]
         L.gdn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -124,13 +130,17 @@ def _check_shape(t, name, shape, dtype):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def make_shape(q, v, g, scale=None, chunk=None, use_qk_l2norm=False) -> GdnShape:
+DIAG_STAGES = ("P", "A", "T", "U", "W", "o", "hT")  # GDN_DIAG_* order
+
+
+def make_shape(q, v, g, scale=None, chunk=None, use_qk_l2norm=False, wy_eps=0.0, clip=0.0,
+               diag=False) -> GdnShape:
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     decay = GDN_DECAY_PER_CHANNEL if g.dim() == 4 else GDN_DECAY_PER_HEAD
     return GdnShape(B, T, H, Dk, Dv, _dtype_code(q), decay,
                     0.0 if scale is None else float(scale), 0 if chunk is None else int(chunk),
-                    int(bool(use_qk_l2norm)))
+                    int(bool(use_qk_l2norm)), float(wy_eps), float(clip), int(bool(diag)))
 
 
 def _call(fn, where, *args):
@@ -188,11 +198,11 @@ def _check_ws(ws):
 
 
 def gdn_forward(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT=None,
-                want_state=True, ws=None, use_qk_l2norm=False):
+                want_state=True, ws=None, use_qk_l2norm=False, wy_eps=0.0, clip=0.0, diag=False):
     """Chunked forward.  Returns (o, hT); hT is None when want_state is False.
     Passing hT=h0 carries the state in place."""
     _check_inputs(q, k, v, g, beta)
-    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm)
+    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm, wy_eps, clip, diag)
     _check_shape(h0, "h0", _state_shape(sh), torch.float32)
     _check_shape(o, "o", v.shape, q.dtype)
     _check_shape(hT, "hT", _state_shape(sh), torch.float32)
@@ -210,10 +220,10 @@ def gdn_forward(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT
 
 
 def gdn_backward(q, k, v, g, beta, dO, h0=None, dhT=None, *, scale=None, chunk=None,
-                 want_dh0=True, ws=None, use_qk_l2norm=False):
+                 want_dh0=True, ws=None, use_qk_l2norm=False, wy_eps=0.0, clip=0.0, diag=False):
     """Gradients (dq, dk, dv, dg, dbeta, dh0) of sum(o*dO) + sum(hT*dhT)."""
     _check_inputs(q, k, v, g, beta)
-    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm)
+    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm, wy_eps, clip, diag)
     _check_shape(dO, "dO", v.shape, q.dtype)
     _check_shape(h0, "h0", _state_shape(sh), torch.float32)
     _check_shape(dhT, "dhT", _state_shape(sh), torch.float32)
@@ -231,12 +241,12 @@ def gdn_backward(q, k, v, g, beta, dO, h0=None, dhT=None, *, scale=None, chunk=N
 
 
 def gdn_forward_train(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT=None,
-                      ws=None, use_qk_l2norm=False):
+                      ws=None, use_qk_l2norm=False, wy_eps=0.0, clip=0.0, diag=False):
     """Training forward: as gdn_forward, and leaves residuals in `ws` (a
     backward-sized workspace, returned) for gdn_backward_train.
     Returns (o, hT, ws)."""
     _check_inputs(q, k, v, g, beta)
-    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm)
+    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm, wy_eps, clip, diag)
     _check_shape(h0, "h0", _state_shape(sh), torch.float32)
     _check_shape(o, "o", v.shape, q.dtype)
     _check_shape(hT, "hT", _state_shape(sh), torch.float32)
@@ -255,10 +265,11 @@ def gdn_forward_train(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=No
 
 
 def gdn_backward_train(q, k, v, g, beta, dO, ws, dhT=None, *, scale=None, chunk=None,
-                       want_dh0=True, out=None, use_qk_l2norm=False):
+                       want_dh0=True, out=None, use_qk_l2norm=False, wy_eps=0.0, clip=0.0,
+                       diag=False):
     """Training backward from the residuals gdn_forward_train left in `ws`."""
     _check_inputs(q, k, v, g, beta)
-    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm)
+    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm, wy_eps, clip, diag)
     _check_shape(dO, "dO", v.shape, q.dtype)
     _check_shape(dhT, "dhT", _state_shape(sh), torch.float32)
     _check(ws, "ws")
@@ -283,6 +294,15 @@ def gdn_backward_train(q, k, v, g, beta, dO, ws, dhT=None, *, scale=None, chunk=
           _ptr(v), _ptr(g), _ptr(beta), _ptr(dO), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv),
           _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(ws), ws.numel(), _stream())
     return dq, dk, dv, dg, dbeta, dh0
+
+
+def gdn_diag_read(shape: GdnShape, ws) -> dict:
+    """Stage counters of the last chunked forward pass run in `ws` (shape with
+    diag set): {stage: (non-finite, |x| > 1e6)}.  Synchronises the stream."""
+    _check(ws, "ws")
+    buf = (ctypes.c_uint * (2 * len(DIAG_STAGES)))()
+    _call(lib().gdn_diag_read, "gdn_diag_read", ctypes.byref(shape), _ptr(ws), buf, _stream())
+    return {st: (int(buf[2 * i]), int(buf[2 * i + 1])) for i, st in enumerate(DIAG_STAGES)}
 
 
 def gdn_decode_step(q, k, v, g, beta, state, *, scale=None, o=None, use_qk_l2norm=False):

@@ -2035,9 +2035,13 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
     }
     dim3 gch((unsigned)p.n_ch);
     if constexpr (bf16_tables<TIn, C, DK>()) {
+        // the WY adjoint takes U = T X_V and W = T X_K as products: with clip the
+        // unclipped copies (clipping is differentiated as the identity)
+        const bool raw = p.clip > 0.f;
         GDN_LAUNCH("bchunk1", (bchunk1b_kernel<C, DK, DV>), gch, dim3(NTHR_C), st, (const bf16*)v,
-                   beta, (const bf16*)dO, (const bf16*)(ws + p.o_Dst), (const float*)(ws + p.o_U),
-                   (const float*)(ws + p.o_Tm), (const bf16*)(ws + p.o_W),
+                   beta, (const bf16*)dO, (const bf16*)(ws + p.o_Dst),
+                   (const float*)(ws + (raw ? p.o_Ur : p.o_U)), (const float*)(ws + p.o_Tm),
+                   (const bf16*)(ws + (raw ? p.o_Wr : p.o_W)),
                    (const float*)(ws + p.o_Sst), (const float*)(ws + p.o_dSt),
                    (const float*)(ws + p.o_dDt), (bf16*)dv, (float*)(ws + p.o_dQg),
                    (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh), (float*)(ws + p.o_dPs),
@@ -2128,11 +2132,23 @@ gdn_status backward_dispatch(const Plan& p, const void* q, const void* k, const 
                              const float* dhT, void* dq, void* dk, void* dv, float* dg,
                              float* dbeta, float* dh0, void* ws, bool recompute, hipStream_t st)
 {
-    if (p.dtype == GDN_BF16)
-        return backward_dt<bf16>(p, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
+    gdn_status s =
+        p.dtype == GDN_BF16
+            ? backward_dt<bf16>(p, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
+                                (char*)ws, recompute, st)
+            : backward_dt<float>(p, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
                                  (char*)ws, recompute, st);
-    return backward_dt<float>(p, q, k, v, g, beta, h0, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
-                              (char*)ws, recompute, st);
+    if (s != GDN_OK || !(p.clip > 0.f)) return s;
+    // clip: the gradient outputs cross the layer's boundary
+    const size_t tok = (size_t)p.B * p.T * p.H;
+    const size_t nq = tok * p.Dk, nv = tok * p.Dv;
+    const size_t ng = p.decay == GDN_DECAY_PER_CHANNEL ? nq : tok;
+    const int bf = p.dtype == GDN_BF16;
+    const SafeSeg segs[6] = {{dq, nq, bf, nullptr},  {dk, nq, bf, nullptr},
+                             {dv, nv, bf, nullptr},  {dg, ng, 0, nullptr},
+                             {dbeta, tok, 0, nullptr},
+                             {dh0, (size_t)p.B * p.H * p.Dk * p.Dv, 0, nullptr}};
+    return safe_pass(segs, 6, p.clip, st);
 }
 
 }  // namespace gdn

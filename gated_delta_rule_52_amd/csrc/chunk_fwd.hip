@@ -43,12 +43,13 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
             const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int NC,
             float scale, float* __restrict__ Wo, float* __restrict__ Uo, float* __restrict__ Qgo,
             float* __restrict__ Kho, float* __restrict__ Pso, float* __restrict__ gamo,
-            float* __restrict__ Tmo, float* __restrict__ rno)
+            float* __restrict__ Tmo, float* __restrict__ rno, Safety sf)
 {
     using G = Geo<C, DK, DV>;
     constexpr int PD = G::PD, PC = G::PC, NB = G::NB, HALF = G::HALF;
     __shared__ float sq[C][PD], sk[C][PD], sX[C][PD], sY[C][PD], sA[C][PC];
     __shared__ float sbeta[C], sdiag[C], stot[2][DK], sRn[2 * C];
+    __shared__ unsigned int sdg[NDIAG_PREP];  // stage counts (clip or diag set)
 
     const int ch = blockIdx.x;
     const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
@@ -60,6 +61,11 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
     const TIn* kb = k + tok0 * DK;
     const TIn* vb = v + tok0 * DV;
     const size_t rsK = (size_t)H * DK, rsV = (size_t)H * DV;
+    const bool safe = sf.on();
+    if (tid < NDIAG_PREP) sdg[tid] = 0u;
+    auto grd = [&](float x, int stage) {
+        return safe ? guard(x, sf.clip, sf.diag ? &sdg[2 * stage] : nullptr) : x;
+    };
 
     // ---- loads: q, k rows (zero past T), beta (zero past T)
     for (int idx = tid; idx < C * DK / 4; idx += NTHR) {
@@ -212,8 +218,8 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
-                pv[r] = scale * accP[s][r];
-                sA[i][j] = sbeta[i] * accA[s][r];
+                pv[r] = scale * grd(accP[s][r], GDN_DIAG_P);
+                sA[i][j] = grd(sbeta[i] * accA[s][r], GDN_DIAG_A);
             }
             put_ps(ti * 16 + acc_row(0), tj * 16 + acc_col(), pv);
         }
@@ -224,8 +230,8 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = t * 16 + acc_row(r), j = t * 16 + acc_col();
-            pv[r] = scale * (i > j ? dP[r] : (i == j ? sdiag[i] : 0.f));
-            sA[i][j] = i > j ? sbeta[i] * dA[r] : 0.f;
+            pv[r] = scale * (i > j ? grd(dP[r], GDN_DIAG_P) : (i == j ? grd(sdiag[i], GDN_DIAG_P) : 0.f));
+            sA[i][j] = i > j ? grd(sbeta[i] * dA[r], GDN_DIAG_A) : 0.f;
         }
         put_ps(t * 16 + acc_row(0), t * 16 + acc_col(), pv);
     }
@@ -309,7 +315,7 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
                 float s = (i == j) ? 1.f : 0.f;
 #pragma unroll
                 for (int m = 0; m < i; ++m) s -= sA[bb * 16 + i][bb * 16 + m] * x[m];
-                x[i] = s;
+                x[i] = s * sf.dinv;  // diagonal (1 + wy_eps)
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) sT[(bb * 16 + i) * PC + bb * 16 + j] = x[i];
@@ -343,6 +349,13 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
         }
         __syncthreads();
     }
+    if (safe) {  // the solve's output crosses a stage boundary
+        for (int idx = tid; idx < C * C; idx += NTHR) {
+            float* t = &sT[(idx / C) * PC + idx % C];
+            *t = grd(*t, GDN_DIAG_T);
+        }
+        __syncthreads();
+    }
     if (Tmo) {
         float* Tm = Tmo + (size_t)ch * C * C;
         for (int idx = tid; idx < C * C; idx += NTHR) Tm[idx] = sT[(idx / C) * PC + idx % C];
@@ -363,6 +376,8 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
     for (int idx = w; idx < NB * (DK / 16); idx += 4) {
         const int ti = idx / (DK / 16), tj = idx % (DK / 16);
         f32x4 acc = mma16<MT_F32>(zero4(), &sT[ti * 16 * PC], PC, 1, &sY[0][tj * 16], PD, 1, 16 * (ti + 1));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = grd(acc[r], GDN_DIAG_W);
         if (BT) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -380,7 +395,11 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
         const int ti = idx / (DV / 16), tj = idx % (DV / 16);
         f32x4 acc = mma16<MT_F32>(zero4(), &sT[ti * 16 * PC], PC, 1, &sq[0][tj * 16], PD, 1, 16 * (ti + 1));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Up[(ti * 16 + acc_row(r)) * DV + tj * 16 + acc_col()] = acc[r];
+        for (int r = 0; r < 4; ++r) Up[(ti * 16 + acc_row(r)) * DV + tj * 16 + acc_col()] = grd(acc[r], GDN_DIAG_U);
+    }
+    if (safe) {
+        __syncthreads();
+        flush_counts(sdg, sf.diag, NDIAG_PREP);
     }
 }
 
@@ -396,17 +415,22 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
 // eps): the squared lengths are the diagonals of the Q Q^T and K K^T tiles of
 // the raw rows, r is folded into the products of raw rows and into the rows
 // each thread keeps, and r goes to rno for the backward.
+// With SAFE (clip or diag) the stage values P, A, T, U, W pass through guard();
+// the solve's diagonal is damped by sf.dinv = 1 / (1 + wy_eps) in every instance.
+// Uro, Wro (training with clip): U and W also before clipping, which the
+// backward's WY adjoint needs (clipping is differentiated as the identity).
 // ---------------------------------------------------------------------------
 constexpr int NTHR_P = 512;
 
-template <int C, int DK, int DV, bool PCH, bool L2N>
+template <int C, int DK, int DV, bool PCH, bool L2N, bool SAFE>
 __global__ void __launch_bounds__(NTHR_P, 4)
 prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
              const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int NC,
              float scale, bf16* __restrict__ Wb, bf16* __restrict__ WTb, float* __restrict__ Uo,
              bf16* __restrict__ Qgb, bf16* __restrict__ QgTb, bf16* __restrict__ KhTb,
              bf16* __restrict__ Khb, bf16* __restrict__ Psb, bf16* __restrict__ PsTb,
-             float* __restrict__ gamo, float* __restrict__ Tmo, float* __restrict__ rno)
+             float* __restrict__ gamo, float* __restrict__ Tmo, float* __restrict__ rno,
+             Safety sf, float* __restrict__ Uro, bf16* __restrict__ Wro)
 {
     static_assert(C == 64 && DK == DV, "prep2: chunk 64, Dk == Dv");
     constexpr int NW = NTHR_P / 64, RPP = 16, NPART = C / RPP, NB = C / 16;
@@ -420,6 +444,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     __shared__ float sbeta[C], stot[NPART][DK];
     __shared__ float sG[C];  // per-head decay: chunk-local inclusive cumsum of g
     __shared__ float sRn[2][L2N ? C : 1];  // L2N: 1/sqrt(|q_i|^2 + eps), same for k
+    __shared__ unsigned int sdg[SAFE ? NDIAG_PREP : 1];  // SAFE: this workgroup's stage counts
     bf16 (*sX)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf);
     bf16 (*sY)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf + C * PA * 2);
     float (*sT)[PC] = reinterpret_cast<float (*)[PC]>(sbuf);
@@ -437,6 +462,9 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     const bool bwdt = Tmo != nullptr;
     const bool cp = tid < NPART * DK;
     const int c = tid % DK, part = cp ? tid / DK : 0, p0 = part * RPP;
+    if (SAFE && tid < NDIAG_PREP) sdg[tid] = 0u;
+    auto sd = [&](int stage) -> unsigned int* { return SAFE && sf.diag ? &sdg[2 * stage] : nullptr; };
+    auto grd = [&](float x, int stage) { return SAFE ? guard(x, sf.clip, sd(stage)) : x; };
 
     float a[RPP], qv[RPP], kv[RPP];
 #pragma unroll
@@ -697,8 +725,8 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                    pv[r] = scale * accP[m][r];
-                    sA[i][j] = sbeta[i] * accA[m][r];
+                    pv[r] = scale * grd(accP[m][r], GDN_DIAG_P);
+                    sA[i][j] = grd(sbeta[i] * accA[m][r], GDN_DIAG_A);
                 }
                 put_ps(ti * 16 + 4 * lq, tj * 16 + lr, pv);
             }
@@ -709,8 +737,8 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = t * 16 + 4 * lq + r, j = t * 16 + lr;
-            pv[r] = i >= j ? scale * dP[r] : 0.f;
-            sA[i][j] = i > j ? sbeta[i] * dA[r] : 0.f;
+            pv[r] = i >= j ? scale * grd(dP[r], GDN_DIAG_P) : 0.f;
+            sA[i][j] = i > j ? grd(sbeta[i] * dA[r], GDN_DIAG_A) : 0.f;
         }
         put_ps(t * 16 + 4 * lq, t * 16 + lr, pv);
     }
@@ -774,7 +802,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             float sacc = (i == j) ? 1.f : 0.f;
 #pragma unroll
             for (int m = 0; m < i; ++m) sacc -= sA[bb * 16 + i][bb * 16 + m] * x[m];
-            x[i] = sacc;
+            x[i] = sacc * sf.dinv;  // diagonal (1 + wy_eps)
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) sT[bb * 16 + i][bb * 16 + j] = x[i];
@@ -805,7 +833,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     // T out (fp32, training) and its bf16 copy (over sA, no longer needed)
     for (int idx = tid; idx < C * C; idx += NTHR_P) {
         const int i = idx / C, j = idx % C;
-        const float tv = sT[i][j];
+        const float tv = grd(sT[i][j], GDN_DIAG_T);
         if (bwdt) Tmo[(size_t)ch * C * C + idx] = tv;
         sTb[i][j] = f32_to_bf16(tv);
     }
@@ -815,7 +843,14 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     for (int idx = w; idx < TW; idx += NW) {
         const int ti = idx / (DK / 16), tj = idx % (DK / 16);
         const int K = ((16 * (ti + 1) + 31) / 32) * 32;
-        const f32x4 acc = mma_kc_dyn(zero4(), &sTb[ti * 16][0], PT, &sXT[tj * 16][0], PT, K);
+        f32x4 acc = mma_kc_dyn(zero4(), &sTb[ti * 16][0], PT, &sXT[tj * 16][0], PT, K);
+        if (SAFE && Wro) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Wro[(size_t)ch * C * DK + (ti * 16 + 4 * lq + r) * DK + tj * 16 + lr] = f32_to_bf16(acc[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = grd(acc[r], GDN_DIAG_W);
         bf16* Wc = Wb + (size_t)ch * C * DK;
 #pragma unroll
         for (int r = 0; r < 4; ++r) Wc[(ti * 16 + 4 * lq + r) * DK + tj * 16 + lr] = f32_to_bf16(acc[r]);
@@ -843,8 +878,16 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         const int K = ((16 * (ti + 1) + 31) / 32) * 32;
         const f32x4 acc = mma_kc_dyn(zero4(), &sTb[ti * 16][0], PT, &sXT[tj * 16][0], PT, K);
         float* Uc = Uo + (size_t)ch * C * DV;
+        if (SAFE && Uro) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Uc[(ti * 16 + 4 * lq + r) * DV + tj * 16 + lr] = acc[r];
+            for (int r = 0; r < 4; ++r) Uro[(size_t)ch * C * DV + (ti * 16 + 4 * lq + r) * DV + tj * 16 + lr] = acc[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Uc[(ti * 16 + 4 * lq + r) * DV + tj * 16 + lr] = grd(acc[r], GDN_DIAG_U);
+    }
+    if constexpr (SAFE) {
+        __syncthreads();
+        flush_counts(sdg, sf.diag, NDIAG_PREP);
     }
 }
 
@@ -1251,6 +1294,10 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
     float* gam = (float*)(ws + p.o_gam);
     float* Tm = want_T ? (float*)(ws + p.o_Tm) : nullptr;
     float* rn = p.l2n ? (float*)(ws + p.o_rn) : nullptr;
+    const Safety sf{p.clip, p.dinv, p.diag ? (unsigned int*)(ws + p.o_dgc) : nullptr};
+    const bool raw = want_T && p.clip > 0.f;  // the training forward keeps U, W unclipped too
+    float* Uro = raw ? (float*)(ws + p.o_Ur) : nullptr;
+    bf16* Wro = raw ? (bf16*)(ws + p.o_Wr) : nullptr;
     dim3 grid((unsigned)p.n_ch), block(NTHR);
     if constexpr (bf16_tables<TIn, C, DK>()) {
         const size_t n = p.n_ch;
@@ -1258,28 +1305,29 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
         bf16* Qb = (bf16*)Qg;
         bf16* Kb = (bf16*)Kh;
         bf16* Pb = (bf16*)Ps;
-        auto launch = [&](auto pch, auto l2n) {
+        auto launch = [&](auto pch, auto l2n, auto safe) {
             GDN_LAUNCH(want_T ? "prep_T" : "prep",
-                       (prep2_kernel<C, DK, DV, decltype(pch)::value, decltype(l2n)::value>), grid,
-                       dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g, beta,
-                       p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, U, Qb, Qb + n * C * DK, Kb,
-                       Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm, rn);
+                       (prep2_kernel<C, DK, DV, decltype(pch)::value, decltype(l2n)::value,
+                                     decltype(safe)::value>),
+                       grid, dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g,
+                       beta, p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, U, Qb, Qb + n * C * DK,
+                       Kb, Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm, rn, sf, Uro, Wro);
             return GDN_OK;
         };
-        using TT = std::true_type;
-        using FF = std::false_type;
-        if (p.decay == GDN_DECAY_PER_CHANNEL)
-            return p.l2n ? launch(TT{}, TT{}) : launch(TT{}, FF{});
-        return p.l2n ? launch(FF{}, TT{}) : launch(FF{}, FF{});
+        return with_bool(p.decay == GDN_DECAY_PER_CHANNEL, [&](auto pch) {
+            return with_bool(p.l2n, [&](auto l2n) {
+                return with_bool(sf.on(), [&](auto safe) { return launch(pch, l2n, safe); });
+            });
+        });
     }
     if (p.decay == GDN_DECAY_PER_CHANNEL)
         GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep_kernel<TIn, C, DK, DV, true, MT>), grid, block, st,
                            (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
-                           p.scale, W, U, Qg, Kh, Ps, gam, Tm, rn);
+                           p.scale, W, U, Qg, Kh, Ps, gam, Tm, rn, sf);
     else
         GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep_kernel<TIn, C, DK, DV, false, MT>), grid, block, st,
                            (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
-                           p.scale, W, U, Qg, Kh, Ps, gam, Tm, rn);
+                           p.scale, W, U, Qg, Kh, Ps, gam, Tm, rn, sf);
     GDN_HIP_CHECK_LAUNCH();
     return GDN_OK;
 }
@@ -1337,13 +1385,41 @@ gdn_status forward_dt(const Plan& p, const void* q, const void* k, const void* v
     return GDN_ERR_UNSUPPORTED;
 }
 
+__global__ void zero_words_kernel(unsigned int* __restrict__ w, int n)
+{
+    if ((int)threadIdx.x < n) w[threadIdx.x] = 0u;
+}
+
+// Numerical-safety options around a forward pass: the stage counters start at
+// zero (a fill kernel, so the pass can be captured), and after the scan the
+// outputs o and hT cross their stage boundary.
+static gdn_status safety_begin(const Plan& p, char* ws, hipStream_t st)
+{
+    if (!p.diag) return GDN_OK;
+    GDN_LAUNCH("zero_words", zero_words_kernel, dim3(1), dim3(64), st,
+               (unsigned int*)(ws + p.o_dgc), GDN_DIAG_WORDS);
+    return GDN_OK;
+}
+
+static gdn_status safety_outputs(const Plan& p, void* o, float* hT, char* ws, hipStream_t st)
+{
+    unsigned int* dg = p.diag ? (unsigned int*)(ws + p.o_dgc) : nullptr;
+    const size_t no = (size_t)p.B * p.T * p.H * p.Dv, nh = (size_t)p.B * p.H * p.Dk * p.Dv;
+    const SafeSeg segs[2] = {{o, no, p.dtype == GDN_BF16, dg ? dg + 2 * GDN_DIAG_O : nullptr},
+                             {hT, nh, 0, dg ? dg + 2 * GDN_DIAG_HT : nullptr}};
+    return safe_pass(segs, 2, p.clip, st);
+}
+
 gdn_status forward_dispatch(const Plan& p, const void* q, const void* k, const void* v,
                             const float* g, const float* beta, const float* h0, void* o, float* hT,
                             void* ws, hipStream_t st)
 {
-    if (p.dtype == GDN_BF16)
-        return forward_dt<bf16>(p, q, k, v, g, beta, h0, o, hT, (char*)ws, st);
-    return forward_dt<float>(p, q, k, v, g, beta, h0, o, hT, (char*)ws, st);
+    gdn_status s = safety_begin(p, (char*)ws, st);
+    if (s != GDN_OK) return s;
+    s = p.dtype == GDN_BF16 ? forward_dt<bf16>(p, q, k, v, g, beta, h0, o, hT, (char*)ws, st)
+                            : forward_dt<float>(p, q, k, v, g, beta, h0, o, hT, (char*)ws, st);
+    if (s != GDN_OK) return s;
+    return safety_outputs(p, o, hT, (char*)ws, st);
 }
 
 // Forward recompute for the backward pass: the prep outputs (with T) and the
@@ -1362,9 +1438,9 @@ gdn_status recompute_t(const Plan& p, const void* q, const void* k, const void* 
     return run_scan<TIn, C, DK, DV, MT, true, false>(p, h0, nullptr, nullptr, ws, st);
 }
 
-gdn_status recompute_dispatch(const Plan& p, const void* q, const void* k, const void* v,
-                              const float* g, const float* beta, const float* h0, void* o,
-                              float* hT, bool out, void* ws, hipStream_t st)
+static gdn_status recompute_sized(const Plan& p, const void* q, const void* k, const void* v,
+                                  const float* g, const float* beta, const float* h0, void* o,
+                                  float* hT, bool out, void* ws, hipStream_t st)
 {
 #define GDN_REC(C_, D_)                                                                        \
     if (p.C == C_ && p.Dk == D_ && p.Dv == D_)                                                  \
@@ -1376,6 +1452,17 @@ gdn_status recompute_dispatch(const Plan& p, const void* q, const void* k, const
     GDN_REC(64, 128) GDN_REC(64, 64) GDN_REC(16, 16)
 #undef GDN_REC
     return GDN_ERR_UNSUPPORTED;
+}
+
+gdn_status recompute_dispatch(const Plan& p, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* h0, void* o,
+                              float* hT, bool out, void* ws, hipStream_t st)
+{
+    gdn_status s = safety_begin(p, (char*)ws, st);
+    if (s != GDN_OK) return s;
+    s = recompute_sized(p, q, k, v, g, beta, h0, o, hT, out, ws, st);
+    if (s != GDN_OK || !out) return s;
+    return safety_outputs(p, o, hT, (char*)ws, st);
 }
 
 }  // namespace gdn

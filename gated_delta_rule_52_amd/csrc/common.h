@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdn.h"
 
 namespace gdn {
@@ -65,6 +67,14 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Call f with std::true_type or std::false_type: a runtime flag picks a
+// template instance.
+template <typename F>
+auto with_bool(bool b, F&& f)
+{
+    return b ? f(std::true_type{}) : f(std::false_type{});
+}
 
 // launch recorder (include/gdn_profile.h); no-ops unless a tool enabled it
 void prof_begin(const char* name, hipStream_t st);

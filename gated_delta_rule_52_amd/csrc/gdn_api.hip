@@ -46,6 +46,11 @@ static gdn_status check_shape(const gdn_shape* sh, bool decode)
         return GDN_ERR_INVALID_ARG;
     if (!(sh->scale >= 0.f)) return GDN_ERR_INVALID_ARG;  // rejects NaN and negatives
     if (sh->qk_l2norm != 0 && sh->qk_l2norm != 1) return GDN_ERR_INVALID_ARG;
+    if (!(sh->wy_eps >= 0.f && sh->wy_eps <= 1e30f)) return GDN_ERR_INVALID_ARG;  // also NaN
+    if (!(sh->clip >= 0.f && sh->clip <= 3.0e38f)) return GDN_ERR_INVALID_ARG;
+    if (sh->diag != 0 && sh->diag != 1) return GDN_ERR_INVALID_ARG;
+    // the options act on the chunked form's stages; the decode step has none
+    if (decode && (sh->wy_eps != 0.f || sh->clip != 0.f || sh->diag)) return GDN_ERR_UNSUPPORTED;
     if (decode && sh->T != 1) return GDN_ERR_INVALID_ARG;
     if (!dim_ok(sh->Dk) || !dim_ok(sh->Dv)) return GDN_ERR_UNSUPPORTED;
     if (!decode) {
@@ -187,6 +192,19 @@ gdn_status gdn_backward_train(const gdn_shape* sh, const void* q, const void* k,
 {
     return backward_common(sh, q, k, v, g, beta, nullptr, dO, dhT, dq, dk, dv, dg, dbeta, dh0,
                            ws, ws_bytes, stream, false);
+}
+
+gdn_status gdn_diag_read(const gdn_shape* sh, const void* ws, unsigned int* counts, void* stream)
+{
+    gdn_status s = check_shape(sh, false);
+    if (s != GDN_OK) return s;
+    if (!sh->diag || !ws || !counts) return GDN_ERR_INVALID_ARG;
+    Plan p = make_plan(*sh, eff_scale(sh));
+    if (hipMemcpyAsync(counts, (const char*)ws + p.o_dgc, GDN_DIAG_WORDS * sizeof(unsigned int),
+                       hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GDN_ERR_HIP;
+    return GDN_OK;
 }
 
 gdn_status gdn_decode_step(const gdn_shape* sh, const void* q, const void* k, const void* v,

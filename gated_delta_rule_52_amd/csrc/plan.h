@@ -12,6 +12,7 @@
 //   gam [ch][Dk]      gam = exp(G_{C-1})                   (whole-chunk decay)
 //   rn  [ch][2][C]    with qk_l2norm: 1 / sqrt(|q_t|^2 + eps) (row 0) and the
 //                     same for k_t (row 1); the backward scales q, k by them
+//   dgc [GDN_DIAG_WORDS] uint32, with diag: the stage counters of the forward
 // backward only:
 //   Tm  [ch][C][C]    T = (I + A)^-1
 //   Sst [ch][Dk][Dv]  state at the start of chunk n
@@ -23,6 +24,8 @@
 //   Dst [ch][C][Dv]   the chunk deltas D (bf16; bf16 inputs at chunk 64 only)
 //   dbq [ch][2][C]    per channel-half partial dbeta, dgq [ch][2][C] partial
 //                     per-head dg (bf16 inputs at chunk 64)
+//   Ur  [ch][C][Dv], Wr [ch][C][Dk] (bf16): with clip, the products T X_V and
+//                     T X_K before clipping, for the WY adjoint of the bf16 path
 // With bf16 inputs at chunk 64 the tables W, Qg, Kh, Ps are bf16 and each
 // region holds two of them (the second, transposed or row-major, for the
 // backward scan), and the backward's hand-offs are bf16 too: dQg, dKh, dPs;
@@ -42,10 +45,12 @@ struct Plan {
     int B, T, H, Dk, Dv, C, NC, dtype, decay;
     bool l2n;  // qk_l2norm
     float scale;
+    float clip, dinv;  // numerical-safety options: clip bound, 1 / (1 + wy_eps)
+    bool diag;
     size_t n_ch;  // B * H * NC
     // byte offsets into the workspace
-    size_t o_W, o_U, o_Qg, o_Kh, o_Ps, o_gam, o_rn, o_Tm, o_Sst, o_dSt, o_dDt;
-    size_t o_dQg, o_dWg, o_dKh, o_dPs, o_dT1, o_dgm, o_dbp, o_Dst, o_dbq, o_dgq;
+    size_t o_W, o_U, o_Qg, o_Kh, o_Ps, o_gam, o_rn, o_dgc, o_Tm, o_Sst, o_dSt, o_dDt;
+    size_t o_dQg, o_dWg, o_dKh, o_dPs, o_dT1, o_dgm, o_dbp, o_Dst, o_dbq, o_dgq, o_Ur, o_Wr;
     size_t ws_fwd_bytes, ws_bwd_bytes;
 };
 
@@ -67,6 +72,9 @@ inline Plan make_plan(const gdn_shape& s, float scale)
     p.NC = (s.T + p.C - 1) / p.C;
     p.dtype = s.dtype; p.decay = s.decay; p.scale = scale;
     p.l2n = s.qk_l2norm != 0;
+    p.clip = s.clip;
+    p.dinv = 1.0f / (1.0f + s.wy_eps);
+    p.diag = s.diag != 0;
     p.n_ch = (size_t)s.B * s.H * p.NC;
     const size_t f = sizeof(float), n = p.n_ch, C = p.C, Dk = p.Dk, Dv = p.Dv;
     size_t off = 0;
@@ -77,6 +85,7 @@ inline Plan make_plan(const gdn_shape& s, float scale)
     p.o_Ps = off;  off = align256(off + n * C * C * f);
     p.o_gam = off; off = align256(off + n * Dk * f);
     p.o_rn = off;  off = align256(off + (p.l2n ? n * 2 * C * f : 0));
+    p.o_dgc = off; off = align256(off + (p.diag ? GDN_DIAG_WORDS * sizeof(unsigned int) : 0));
     p.ws_fwd_bytes = off;
     p.o_Tm = off;  off = align256(off + n * C * C * f);
     p.o_Sst = off; off = align256(off + n * Dk * Dv * f);
@@ -92,6 +101,9 @@ inline Plan make_plan(const gdn_shape& s, float scale)
     p.o_Dst = off; off = align256(off + n * C * Dv * 2);
     p.o_dbq = off; off = align256(off + n * 2 * C * f);
     p.o_dgq = off; off = align256(off + n * 2 * C * f);
+    const bool raw = s.clip > 0.f;
+    p.o_Ur = off;  off = align256(off + (raw ? n * C * Dv * f : 0));
+    p.o_Wr = off;  off = align256(off + (raw ? n * C * Dk * 2 : 0));
     p.ws_bwd_bytes = off;
     return p;
 }

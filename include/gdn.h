@@ -71,6 +71,24 @@ typedef enum { GDN_DECAY_PER_HEAD = 0, GDN_DECAY_PER_CHANNEL = 1 } gdn_decay;
 
 #define GDN_L2NORM_EPS 1e-6f
 
+/* Stage boundaries of the chunked forward that the numerical-safety options act
+ * on (atomic_ops card, "Features": chunk scores -> WY block solve -> recompute
+ * -> inter-chunk scan): the scores P (unscaled) and A (with beta), the solve's
+ * T, the recompute's U and W, the outputs o and the final state hT. */
+enum {
+    GDN_DIAG_P = 0,
+    GDN_DIAG_A = 1,
+    GDN_DIAG_T = 2,
+    GDN_DIAG_U = 3,
+    GDN_DIAG_W = 4,
+    GDN_DIAG_O = 5,
+    GDN_DIAG_HT = 6,
+    GDN_DIAG_STAGES = 7
+};
+/* counters: word 2*stage counts non-finite values, word 2*stage+1 finite
+ * values with |x| > 1e6 */
+#define GDN_DIAG_WORDS (2 * GDN_DIAG_STAGES)
+
 typedef struct {
     int B, T, H, Dk, Dv;
     int dtype;     /* gdn_dtype of q, k, v, o, dO, dq, dk, dv */
@@ -80,6 +98,18 @@ typedef struct {
     int qk_l2norm; /* 1: L2-normalise q and k rows inside the call (see above); 0: as given.
                       A training pair (gdn_forward_train, gdn_backward_train) must pass the
                       same value to both calls. */
+    /* Numerical-safety options of the chunked calls (atomic_ops card, "Features"
+     * and "Debugging"); all zero = off.  Not supported by gdn_decode_step.  A
+     * training pair must pass the same values to both calls. */
+    float wy_eps;  /* >= 0: the WY block solve inverts (1 + wy_eps) I + A instead of
+                      I + A (damping on the diagonal); results then depend on the chunk */
+    float clip;    /* >= 0; > 0: at each stage boundary (GDN_DIAG_*) values are made
+                      finite (NaN -> 0, +-inf -> +-clip) and clamped to [-clip, clip],
+                      and so are dq, dk, dv, dg, dbeta, dh0; gradients take the clipping
+                      as the identity */
+    int diag;      /* 1: the forward counts, per stage boundary and before clipping,
+                      non-finite values and finite values with |x| > 1e6 into counters
+                      in the workspace (read with gdn_diag_read); never changes values */
 } gdn_shape;
 
 /*
@@ -168,6 +198,19 @@ gdn_status gdn_backward_train(const gdn_shape *shape, const void *q, const void 
 gdn_status gdn_decode_step(const gdn_shape *shape, const void *q, const void *k, const void *v,
                            const float *g, const float *beta, float *state, void *o,
                            void *stream);
+
+/*
+ * gdn_diag_read -- copy the stage counters of the last chunked forward pass run
+ * in `ws` (gdn_forward, gdn_forward_train, or the recompute inside gdn_backward,
+ * which has no o / hT stage) to host memory: counts[GDN_DIAG_WORDS].  The
+ * shape must have diag = 1 and match the call that ran.  Synchronises `stream`
+ * (atomic_ops card, "Debugging": per-stage reports of non-finite or > 1e6
+ * values; diagnostic only).
+ * Errors: GDN_ERR_INVALID_ARG for a bad shape, diag = 0, NULL ws or counts;
+ * GDN_ERR_HIP if the copy fails.
+ */
+gdn_status gdn_diag_read(const gdn_shape *shape, const void *ws, unsigned int *counts,
+                         void *stream);
 
 /* gdn_status_string -- static, human-readable name of a status code. */
 const char *gdn_status_string(gdn_status status);

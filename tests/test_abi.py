@@ -66,6 +66,8 @@ def test_workspace_query():
 @pytest.mark.parametrize("bad,code", [
     (dict(B=0), 1), (dict(T=-1), 1), (dict(dtype=5), 1), (dict(decay=9), 1),
     (dict(scale=-1.0), 1), (dict(Dk=48, Dv=48), 2), (dict(chunk=32), 2), (dict(qk_l2norm=-1), 1),
+    (dict(wy_eps=-0.5), 1), (dict(wy_eps=float("nan")), 1), (dict(clip=-1.0), 1),
+    (dict(clip=float("inf")), 1), (dict(diag=2), 1),
 ])
 def test_forward_rejects_bad_shapes_before_launch(bad, code):
     L = gdn.lib()
@@ -98,3 +100,25 @@ def test_profile_recorder_arguments():
     assert L.gdn_profile_begin(ev, 0) == 1
     assert L.gdn_profile_begin(ev, 1 << 20) == 1
     assert L.gdn_profile_end() == 0
+
+
+def test_safety_options_host_checks():
+    """The decode step has no stage boundaries: the options are refused there;
+    the counters can only be read with diag set; diag adds one 256-byte region
+    and clip two tables to the training workspace."""
+    L = gdn.lib()
+    p = ctypes.c_void_p(256)
+    for kw in (dict(wy_eps=0.1), dict(clip=5.0), dict(diag=1)):
+        sh = _shape(T=1, **kw)
+        assert L.gdn_decode_step(ctypes.byref(sh), p, p, p, p, p, p, p, None) == 2, kw
+    buf = (ctypes.c_uint * 14)()
+    assert L.gdn_diag_read(ctypes.byref(_shape()), p, buf, None) == 1
+    assert L.gdn_diag_read(ctypes.byref(_shape(diag=1)), None, buf, None) == 1
+    base = L.gdn_workspace_bytes(ctypes.byref(_shape()), 0)
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(diag=1)), 0) == base + 256
+    bwd = L.gdn_workspace_bytes(ctypes.byref(_shape()), 1)
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(wy_eps=0.3)), 1) == bwd
+    # clip: the training forward also keeps U (fp32) and W (bf16) before clipping
+    n_ch = 2 * 3 * 2
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(clip=8.0)), 1) == \
+        bwd + n_ch * 64 * 128 * 4 + n_ch * 64 * 128 * 2
