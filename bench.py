@@ -522,6 +522,52 @@ def main():
                   "algorithmic_bytes_per_step": dbytes}
         log(f"[bench] decode {kdec * 1e3:.1f} us/step, {decode['achieved_GBs']:.0f} GB/s")
 
+        # the same decode from a checkpoint plus a buffer of recent tokens: a step
+        # reads the checkpoint, the buffer folds into it once per `depth` steps
+        s0 = torch.from_numpy(dinp["h0"]).cuda()
+        ref_state = s0.clone()
+        for t in range(8):
+            gdn.gdn_decode_step(*steps_in[t], ref_state, o=od)
+        replay = {"workload": "the decode workload above through gdn_replay_step (checkpoint "
+                              "read each step; buffer of depth tokens folded in when full)"}
+        for depth in (4, 8, 16):
+            ck = s0.clone()
+            buf = gdn.gdn_replay_buffer(Bd, Hd, D, D, depth)
+            for t in range(8):
+                gdn.gdn_replay_step(*steps_in[t], ck, buf, depth, o=od)
+            gdn.gdn_replay_fold(ck, buf, depth)
+            torch.cuda.synchronize()
+            agree = float((ck - ref_state).abs().max() / ref_state.abs().max())
+            gdn.gdn_replay_fold(ck, buf, depth)
+            rrec = LaunchRecorder(nd)
+            ev0.record()
+            with rrec:
+                for i in range(nd):
+                    gdn.gdn_replay_step(*steps_in[i % 8], ck, buf, depth, o=od)
+            ev1.record()
+            torch.cuda.synchronize()
+            ms_rep = ev0.elapsed_time(ev1) / nd
+            krep = float(np.mean(rrec.by_kernel()["replay_step"]))
+            rrec.close()
+            # per (b, h) and step, averaged over a fill of the buffer: checkpoint read,
+            # its write once per depth steps, the buffer read (on average (depth-1)/2
+            # tokens of key, decays and delta) and one token appended, the inputs and o
+            tokb = 3 * D * 4
+            rbytes = Bd * Hd * (D * D * 4 * (1 + 1 / depth) + (depth - 1) / 2 * tokb + tokb
+                                + 4 * D * 4 + 4 + D * 4)
+            replay[f"depth{depth}"] = {
+                "ms_per_step": ms_rep, "kernel_us": krep * 1e3,
+                "tokens_per_s": Bd / (ms_rep * 1e-3),
+                "speedup_vs_decode_kernel": kdec / krep,
+                "algorithmic_bytes_per_step": rbytes,
+                "achieved_GBs": rbytes / (krep * 1e-3) / 1e9,
+                "frac_hbm_peak": rbytes / (krep * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "state_rel_diff_vs_decode_after_8": agree}
+            log(f"[bench] replay decode depth {depth}: {krep * 1e3:.1f} us/step "
+                f"({kdec / krep:.2f}x the decode step), {replay[f'depth{depth}']['achieved_GBs']:.0f} GB/s "
+                f"algorithmic; state vs decode {agree:.1e}")
+        decode["replay"] = replay
+
     # ---- CPU oracle on this host: the same workload (every (batch, head)
     # sequence unless that would take much longer than ~30 s of wall time)
     cpu = None

@@ -38,6 +38,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "G
           4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
 EXPORTS = ("gdn_new_state", "gdn_workspace_bytes", "gdn_forward", "gdn_backward",
            "gdn_forward_train", "gdn_backward_train", "gdn_decode_step", "gdn_diag_read",
+           "gdn_replay_buffer_bytes", "gdn_replay_reset", "gdn_replay_step", "gdn_replay_fold",
            "gdn_status_string",
            # include/gdn_profile.h
            "gdn_profile_begin", "gdn_profile_end", "gdn_profile_launch_name")
@@ -87,6 +88,14 @@ def lib():
         L.gdn_decode_step.restype = i
         L.gdn_diag_read.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_uint), vp]
         L.gdn_diag_read.restype = i
+        L.gdn_replay_buffer_bytes.argtypes = [sp, i]
+        L.gdn_replay_buffer_bytes.restype = sz
+        L.gdn_replay_reset.argtypes = [sp, vp, i, vp]
+        L.gdn_replay_reset.restype = i
+        L.gdn_replay_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, i, vp, vp]
+        L.gdn_replay_step.restype = i
+        L.gdn_replay_fold.argtypes = [sp, vp, vp, i, vp]
+        L.gdn_replay_fold.restype = i
         L.gdn_status_string.argtypes = [i]
         L.gdn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -320,3 +329,58 @@ def gdn_decode_step(q, k, v, g, beta, state, *, scale=None, o=None, use_qk_l2nor
     _call(lib().gdn_decode_step, "gdn_decode_step", ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v),
           _ptr(g), _ptr(beta), _ptr(state), _ptr(o), _stream())
     return o
+
+
+# ---------------------------------------------------------------------------
+# decode from a checkpoint plus a buffer of recent tokens (include/gdn.h)
+# ---------------------------------------------------------------------------
+def _replay_shape(B, H, Dk, Dv, per_channel, dtype=GDN_F32, scale=None):
+    decay = GDN_DECAY_PER_CHANNEL if per_channel else GDN_DECAY_PER_HEAD
+    return GdnShape(B, 1, H, Dk, Dv, dtype, decay, 0.0 if scale is None else float(scale), 0)
+
+
+def gdn_replay_buffer(B: int, H: int, Dk: int, Dv: int, depth: int, *, per_channel=True,
+                      device="cuda") -> torch.Tensor:
+    """An empty token buffer of the given depth (1..16) for B x H sequences."""
+    sh = _replay_shape(B, H, Dk, Dv, per_channel)
+    n = int(lib().gdn_replay_buffer_bytes(ctypes.byref(sh), int(depth)))
+    if n == 0:
+        raise GdnError(1, "gdn_replay_buffer_bytes")
+    buf = torch.empty(n, dtype=torch.uint8, device=device)
+    _call(lib().gdn_replay_reset, "gdn_replay_reset", ctypes.byref(sh), _ptr(buf), int(depth),
+          _stream())
+    return buf
+
+
+def gdn_replay_step(q, k, v, g, beta, ckpt, buf, depth, *, scale=None, o=None):
+    """One token for every (b, h) from the checkpoint and the buffer; q,k
+    [B,1,H,Dk] (or [B,H,Dk]).  Returns o; ckpt changes only when the buffer
+    fills (it is then folded in)."""
+    if q.dim() == 3:
+        q, k, v = q.unsqueeze(1), k.unsqueeze(1), v.unsqueeze(1)
+        g = g.unsqueeze(1)
+        beta = beta.unsqueeze(1)
+    _check_inputs(q, k, v, g, beta)
+    sh = make_shape(q, v, g, scale, None)
+    _check_shape(ckpt, "ckpt", _state_shape(sh), torch.float32)
+    _check(buf, "buf")
+    _check_shape(o, "o", (sh.B, 1, sh.H, sh.Dv), q.dtype)
+    if buf.numel() < int(lib().gdn_replay_buffer_bytes(ctypes.byref(sh), int(depth))):
+        raise ValueError("buf is smaller than gdn_replay_buffer_bytes for this shape and depth")
+    if o is None:
+        o = torch.empty((sh.B, 1, sh.H, sh.Dv), dtype=q.dtype, device=q.device)
+    _call(lib().gdn_replay_step, "gdn_replay_step", ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v),
+          _ptr(g), _ptr(beta), _ptr(ckpt), _ptr(buf), int(depth), _ptr(o), _stream())
+    return o
+
+
+def gdn_replay_fold(ckpt, buf, depth, *, per_channel=True):
+    """Fold the buffer into the checkpoint: ckpt becomes the current state."""
+    _check(ckpt, "ckpt", torch.float32)
+    _check(buf, "buf")
+    B, H, Dk, Dv = ckpt.shape
+    sh = _replay_shape(B, H, Dk, Dv, per_channel)
+    if buf.numel() < int(lib().gdn_replay_buffer_bytes(ctypes.byref(sh), int(depth))):
+        raise ValueError("buf is smaller than gdn_replay_buffer_bytes for this shape and depth")
+    _call(lib().gdn_replay_fold, "gdn_replay_fold", ctypes.byref(sh), _ptr(ckpt), _ptr(buf),
+          int(depth), _stream())

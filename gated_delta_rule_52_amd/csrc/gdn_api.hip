@@ -21,6 +21,12 @@ gdn_status recompute_dispatch(const Plan& p, const void* q, const void* k, const
                               const float* g, const float* beta, const float* h0, void* o,
                               float* hT, bool out, void* ws, hipStream_t st);
 
+gdn_status replay_dispatch(const gdn_shape* sh, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, float* ckpt, void* buf, int depth,
+                           void* o, float scale, bool token, hipStream_t st);
+size_t replay_buffer_bytes(int BH, int Dk, int Dv, int depth, bool pch);
+gdn_status replay_reset(void* buf, int BH, hipStream_t st);
+
 __global__ void fill_zero_kernel(float4* __restrict__ p, size_t n4)
 {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -205,6 +211,49 @@ gdn_status gdn_diag_read(const gdn_shape* sh, const void* ws, unsigned int* coun
         return GDN_ERR_HIP;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GDN_ERR_HIP;
     return GDN_OK;
+}
+
+static bool depth_ok(int depth) { return depth >= 1 && depth <= 16; }
+
+size_t gdn_replay_buffer_bytes(const gdn_shape* sh, int depth)
+{
+    if (check_shape(sh, true) != GDN_OK || !depth_ok(depth)) return 0;
+    return replay_buffer_bytes(sh->B * sh->H, sh->Dk, sh->Dv, depth,
+                               sh->decay == GDN_DECAY_PER_CHANNEL);
+}
+
+gdn_status gdn_replay_reset(const gdn_shape* sh, void* buf, int depth, void* stream)
+{
+    gdn_status s = check_shape(sh, true);
+    if (s != GDN_OK) return s;
+    if (!buf || !depth_ok(depth)) return GDN_ERR_INVALID_ARG;
+    if (!aligned16(buf)) return GDN_ERR_ALIGNMENT;
+    return replay_reset(buf, sh->B * sh->H, (hipStream_t)stream);
+}
+
+gdn_status gdn_replay_step(const gdn_shape* sh, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, float* ckpt, void* buf, int depth,
+                           void* o, void* stream)
+{
+    gdn_status s = check_shape(sh, true);
+    if (s != GDN_OK) return s;
+    if (!q || !k || !v || !g || !beta || !ckpt || !buf || !o || !depth_ok(depth))
+        return GDN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, ckpt, buf, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN_ERR_ALIGNMENT;
+    return replay_dispatch(sh, q, k, v, g, beta, ckpt, buf, depth, o, eff_scale(sh), true,
+                           (hipStream_t)stream);
+}
+
+gdn_status gdn_replay_fold(const gdn_shape* sh, float* ckpt, void* buf, int depth, void* stream)
+{
+    gdn_status s = check_shape(sh, true);
+    if (s != GDN_OK) return s;
+    if (!ckpt || !buf || !depth_ok(depth)) return GDN_ERR_INVALID_ARG;
+    if (!aligned16(ckpt) || !aligned16(buf)) return GDN_ERR_ALIGNMENT;
+    return replay_dispatch(sh, nullptr, nullptr, nullptr, nullptr, nullptr, ckpt, buf, depth,
+                           nullptr, eff_scale(sh), false, (hipStream_t)stream);
 }
 
 gdn_status gdn_decode_step(const gdn_shape* sh, const void* q, const void* k, const void* v,

@@ -200,6 +200,32 @@ gdn_status gdn_decode_step(const gdn_shape *shape, const void *q, const void *k,
                            void *stream);
 
 /*
+ * Decode with a checkpoint and a buffer of recent tokens (the ReplaySSM idea:
+ * news digest "Gated DeltaNet", the blurb on state traffic in SSM decoding).
+ * The state of each (batch, head) is a checkpoint `ckpt` [B,H,Dk,Dv] fp32 plus
+ * up to `depth` (1..16) buffered tokens (their key, accumulated log-decay and
+ * delta).  gdn_replay_step reads the checkpoint, computes the token's output
+ * and delta directly (no state write), and appends to the buffer; when the
+ * buffer fills it folds it into the checkpoint.  Outputs and, after
+ * gdn_replay_fold, the state are those of gdn_decode_step (same recurrence,
+ * reassociated; equal up to fp32 rounding).  Shapes as gdn_decode_step
+ * (T == 1, no numerical-safety options); `buf` is caller-owned device memory of
+ * gdn_replay_buffer_bytes(shape, depth) bytes, emptied by gdn_replay_reset
+ * before first use.  Every call must pass the same depth and decay kind.
+ * Errors: GDN_ERR_INVALID_ARG for a bad shape or depth or a NULL pointer,
+ * GDN_ERR_ALIGNMENT, GDN_ERR_UNSUPPORTED for sizes gdn_decode_step refuses.
+ */
+size_t gdn_replay_buffer_bytes(const gdn_shape *shape, int depth);
+gdn_status gdn_replay_reset(const gdn_shape *shape, void *buf, int depth, void *stream);
+gdn_status gdn_replay_step(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, float *ckpt, void *buf, int depth,
+                           void *o, void *stream);
+/* gdn_replay_fold -- fold the buffer into the checkpoint (ckpt becomes the
+ * current state) and empty it; q, k, v, g, beta are not read. */
+gdn_status gdn_replay_fold(const gdn_shape *shape, float *ckpt, void *buf, int depth,
+                           void *stream);
+
+/*
  * gdn_diag_read -- copy the stage counters of the last chunked forward pass run
  * in `ws` (gdn_forward, gdn_forward_train, or the recompute inside gdn_backward,
  * which has no o / hT stage) to host memory: counts[GDN_DIAG_WORDS].  The

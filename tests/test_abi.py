@@ -122,3 +122,25 @@ def test_safety_options_host_checks():
     n_ch = 2 * 3 * 2
     assert L.gdn_workspace_bytes(ctypes.byref(_shape(clip=8.0)), 1) == \
         bwd + n_ch * 64 * 128 * 4 + n_ch * 64 * 128 * 2
+
+
+def test_replay_host_checks():
+    """The checkpoint-and-buffer decode: depth 1..16, decode shapes only, and
+    the buffer size follows the layout (token count, keys, decays, deltas)."""
+    L = gdn.lib()
+    sh = _shape(T=1)
+    assert L.gdn_replay_buffer_bytes(ctypes.byref(sh), 0) == 0
+    assert L.gdn_replay_buffer_bytes(ctypes.byref(sh), 17) == 0
+    assert L.gdn_replay_buffer_bytes(ctypes.byref(_shape(T=2)), 4) == 0
+    a = lambda x: -(-x // 256) * 256
+    BH = 2 * 3
+    assert L.gdn_replay_buffer_bytes(ctypes.byref(sh), 4) == \
+        a(4 * BH) + a(4 * BH * 4 * 128) + a(4 * BH * 4 * 128) + a(4 * BH * 4 * 128)
+    assert L.gdn_replay_buffer_bytes(ctypes.byref(_shape(T=1, decay=0)), 4) == \
+        a(4 * BH) + a(4 * BH * 4 * 128) + a(4 * BH * 4) + a(4 * BH * 4 * 128)
+    p = ctypes.c_void_p(256)
+    assert L.gdn_replay_step(ctypes.byref(sh), p, p, p, p, p, p, p, 0, p, None) == 1
+    assert L.gdn_replay_step(ctypes.byref(sh), p, p, p, p, p, None, p, 4, p, None) == 1
+    assert L.gdn_replay_step(ctypes.byref(_shape(T=1, clip=1.0)), p, p, p, p, p, p, p, 4, p, None) == 2
+    assert L.gdn_replay_fold(ctypes.byref(sh), p, None, 4, None) == 1
+    assert L.gdn_replay_reset(ctypes.byref(sh), ctypes.c_void_p(258), 4, None) == 3
