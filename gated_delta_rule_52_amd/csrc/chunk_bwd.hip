@@ -602,14 +602,6 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     const int lr = l & 15, lq = l >> 4;
     const size_t tok0 = ((size_t)b * T + t0) * H + h;
 
-    {
-        const float* Tp = Tmi + (size_t)ch * C * C;
-        for (int idx = tid; idx < C * C / 4; idx += NTHR_C) {
-            const int r = idx / (C / 4), c4 = (idx % (C / 4)) * 4;
-            st4(&sT[r][c4], load4<float>(Tp + r * C + c4));
-        }
-        for (int r = tid; r < C; r += NTHR_C) sbeta[r] = r < nvalid ? beta[tok0 + (size_t)r * H] : 0.f;
-    }
     const float* Sp = Sst + (size_t)ch * DK * DV;
     const float* dSp = dSt + (size_t)ch * DK * DV;
     const float* dDp = dDt + (size_t)ch * C * DV;
@@ -690,6 +682,17 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 #pragma unroll
         for (int r = 0; r < 4; ++r) dbr[m][r] = 0.f;
 
+    // prologue, one round of loads: the first Dv tile, T, beta and W, then T and
+    // beta into LDS and the tile stashed
+    fetch(0);
+    constexpr int NT4 = (C * C / 4 + NTHR_C - 1) / NTHR_C;
+    float4 tv[NT4];
+    {
+        const float* Tp = Tmi + (size_t)ch * C * C;
+#pragma unroll
+        for (int u = 0; u < NT4; ++u) tv[u] = load4<float>(Tp + 4 * min(tid + NTHR_C * u, C * C / 4 - 1));
+    }
+    const float bv0 = beta[tok0 + (size_t)min(tid % C, nvalid - 1) * H];
     constexpr int NK8 = (C * DK / 8 + NTHR_C - 1) / NTHR_C;
     uint4 wv[NK8];  // W rows (bf16) for the keys' WY adjoint after the Dv loop
     {
@@ -698,8 +701,12 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         for (int u = 0; u < NK8; ++u)
             wv[u] = *reinterpret_cast<const uint4*>(Wp + 8 * min(tid + NTHR_C * u, C * DK / 8 - 1));
     }
-    __syncthreads();  // sbeta ready for the first stash
-    fetch(0);
+#pragma unroll
+    for (int u = 0; u < NT4; ++u) {
+        const int idx = tid + NTHR_C * u;
+        if (idx < C * C / 4) st4(&sT[idx / (C / 4)][(idx % (C / 4)) * 4], tv[u]);
+    }
+    if (tid < C) sbeta[tid] = tid < nvalid ? bv0 : 0.f;
     stash();
     __syncthreads();
     // one Dv tile; the last one is peeled (MORE = false) so that the prefetch and
