@@ -409,16 +409,18 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
 // owns one key channel of one 16-token tile and keeps its q, k and exp(g) in
 // registers; the level tables are bf16 rows with the channel index contiguous
 // (one 16-byte LDS read per MFMA operand); the diagonal scores are a chain of
-// the unscaled rows kept on the diagonal; W = T X_K and U = T X_V are bf16
-// MFMA products with X_K^T, X_V^T written by the column threads.
+// the unscaled rows kept on the diagonal; W = T X_K is a bf16 MFMA product
+// with X_K^T written by the column threads.  U = T X_V is left to wy_u, which
+// reads the bf16 T written here: loading v this late would wait for every
+// table store before it (one completion counter for loads and stores).
 // With L2N (use_qk_l2norm) every q and k row is scaled by r = 1/sqrt(|x|^2 +
 // eps): the squared lengths are the diagonals of the Q Q^T and K K^T tiles of
 // the raw rows, r is folded into the products of raw rows and into the rows
 // each thread keeps, and r goes to rno for the backward.
 // With SAFE (clip or diag) the stage values P, A, T, U, W pass through guard();
 // the solve's diagonal is damped by sf.dinv = 1 / (1 + wy_eps) in every instance.
-// Uro, Wro (training with clip): U and W also before clipping, which the
-// backward's WY adjoint needs (clipping is differentiated as the identity).
+// Wro (training with clip): W also before clipping, which the backward's WY
+// adjoint needs (clipping is differentiated as the identity).
 // ---------------------------------------------------------------------------
 constexpr int NTHR_P = 512;
 
@@ -426,11 +428,11 @@ template <int C, int DK, int DV, bool PCH, bool L2N, bool SAFE>
 __global__ void __launch_bounds__(NTHR_P, 4)
 prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
              const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int NC,
-             float scale, bf16* __restrict__ Wb, bf16* __restrict__ WTb, float* __restrict__ Uo,
+             float scale, bf16* __restrict__ Wb, bf16* __restrict__ WTb, bf16* __restrict__ Tbo,
              bf16* __restrict__ Qgb, bf16* __restrict__ QgTb, bf16* __restrict__ KhTb,
              bf16* __restrict__ Khb, bf16* __restrict__ Psb, bf16* __restrict__ PsTb,
              float* __restrict__ gamo, float* __restrict__ Tmo, float* __restrict__ rno,
-             Safety sf, float* __restrict__ Uro, bf16* __restrict__ Wro)
+             Safety sf, bf16* __restrict__ Wro)
 {
     static_assert(C == 64 && DK == DV, "prep2: chunk 64, Dk == Dv");
     constexpr int NW = NTHR_P / 64, RPP = 16, NPART = C / RPP, NB = C / 16;
@@ -440,7 +442,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     constexpr int SBUF = cmax(2 * C * PA * 2, 2 * C * PC * 4);
     __shared__ __align__(16) char sbuf[SBUF];
     __shared__ __align__(16) float sA[C][PC];  // A (beta rows), strictly lower; later T in bf16
-    __shared__ __align__(16) bf16 sXT[DK][PT];  // X_K^T, then X_V^T
+    __shared__ __align__(16) bf16 sXT[DK][PT];  // X_K^T
     __shared__ float sbeta[C], stot[NPART][DK];
     __shared__ float sG[C];  // per-head decay: chunk-local inclusive cumsum of g
     __shared__ float sRn[2][L2N ? C : 1];  // L2N: 1/sqrt(|q_i|^2 + eps), same for k
@@ -706,6 +708,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     }
     }  // per-channel decay
 
+
     // ---- scores out: Ps (bf16) and, for training, Ps^T; A (x beta) to LDS
     bf16* Psc = Psb + (size_t)ch * C * C;
     bf16* PsTc = PsTb + (size_t)ch * C * C;
@@ -777,15 +780,24 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         bf16* Khc = Khb + (size_t)ch * C * DK;
 #pragma unroll
         for (int i = 0; i < RPP; ++i) Qgc[(p0 + i) * DK + c] = f32_to_bf16(qg[i]);
+        // a thread's 16 rows of one channel are 32 contiguous bytes of the
+        // transposed tables: two 16-byte stores each
 #pragma unroll
-        for (int i = 0; i < RPP; i += 4) {
-            *reinterpret_cast<uint2*>(&KhTc[c * C + p0 + i]) = pack4_bf16(kh[i], kh[i + 1], kh[i + 2], kh[i + 3]);
-            *reinterpret_cast<uint2*>(&sXT[c][p0 + i]) = pack4_bf16(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
+        for (int i = 0; i < RPP; i += 8) {
+            const uint2 k0 = pack4_bf16(kh[i], kh[i + 1], kh[i + 2], kh[i + 3]);
+            const uint2 k1 = pack4_bf16(kh[i + 4], kh[i + 5], kh[i + 6], kh[i + 7]);
+            *reinterpret_cast<uint4*>(&KhTc[c * C + p0 + i]) = uint4{k0.x, k0.y, k1.x, k1.y};
         }
+#pragma unroll
+        for (int i = 0; i < RPP; i += 4)
+            *reinterpret_cast<uint2*>(&sXT[c][p0 + i]) = pack4_bf16(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
         if (bwdt) {
 #pragma unroll
-            for (int i = 0; i < RPP; i += 4)
-                *reinterpret_cast<uint2*>(&QgTc[c * C + p0 + i]) = pack4_bf16(qg[i], qg[i + 1], qg[i + 2], qg[i + 3]);
+            for (int i = 0; i < RPP; i += 8) {
+                const uint2 q0 = pack4_bf16(qg[i], qg[i + 1], qg[i + 2], qg[i + 3]);
+                const uint2 q1 = pack4_bf16(qg[i + 4], qg[i + 5], qg[i + 6], qg[i + 7]);
+                *reinterpret_cast<uint4*>(&QgTc[c * C + p0 + i]) = uint4{q0.x, q0.y, q1.x, q1.y};
+            }
 #pragma unroll
             for (int i = 0; i < RPP; ++i) Khc[(p0 + i) * DK + c] = f32_to_bf16(kh[i]);
         }
@@ -831,11 +843,13 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         __syncthreads();
     }
     // T out (fp32, training) and its bf16 copy (over sA, no longer needed)
-    for (int idx = tid; idx < C * C; idx += NTHR_P) {
-        const int i = idx / C, j = idx % C;
-        const float tv = grd(sT[i][j], GDN_DIAG_T);
-        if (bwdt) Tmo[(size_t)ch * C * C + idx] = tv;
-        sTb[i][j] = f32_to_bf16(tv);
+    for (int idx = tid; idx < C * C / 4; idx += NTHR_P) {  // 4 consecutive columns per thread
+        const int i = idx / (C / 4), j = (idx % (C / 4)) * 4;
+        float tv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tv[e] = grd(sT[i][j + e], GDN_DIAG_T);
+        if (bwdt) *reinterpret_cast<float4*>(&Tmo[(size_t)ch * C * C + i * C + j]) = float4{tv[0], tv[1], tv[2], tv[3]};
+        *reinterpret_cast<uint2*>(&sTb[i][j]) = pack4_bf16(tv[0], tv[1], tv[2], tv[3]);
     }
     __syncthreads();
     // ---- W = T X_K (bf16 out, and W^T for training)
@@ -858,36 +872,101 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             *reinterpret_cast<uint2*>(&WTb[(size_t)ch * C * DK + (tj * 16 + lr) * C + ti * 16 + 4 * lq]) =
                 pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
     }
-    __syncthreads();
-    // ---- X_V^T = (beta V)^T, then U = T X_V (fp32 out)
-    if (cp) {
-        float xv[RPP];
-#pragma unroll
-        for (int i = 0; i < RPP; ++i) {
-            const int r = p0 + i;
-            const float vx = to_f32(v[tok0 * DV + min(r, nvalid - 1) * rsK + c]);
-            xv[i] = r < nvalid ? sbeta[r] * vx : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < RPP; i += 4)
-            *reinterpret_cast<uint2*>(&sXT[c][p0 + i]) = pack4_bf16(xv[i], xv[i + 1], xv[i + 2], xv[i + 3]);
-    }
-    __syncthreads();
-    for (int idx = w; idx < TW; idx += NW) {
-        const int ti = idx / (DV / 16), tj = idx % (DV / 16);
-        const int K = ((16 * (ti + 1) + 31) / 32) * 32;
-        const f32x4 acc = mma_kc_dyn(zero4(), &sTb[ti * 16][0], PT, &sXT[tj * 16][0], PT, K);
-        float* Uc = Uo + (size_t)ch * C * DV;
-        if (SAFE && Uro) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Uro[(size_t)ch * C * DV + (ti * 16 + 4 * lq + r) * DV + tj * 16 + lr] = acc[r];
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Uc[(ti * 16 + 4 * lq + r) * DV + tj * 16 + lr] = grd(acc[r], GDN_DIAG_U);
+    // T in bf16 for U = T X_V (wy_u): rows of the LDS copy, 16 bytes per thread
+    for (int idx = tid; idx < C * C / 8; idx += NTHR_P) {
+        const int i = idx / (C / 8), j = (idx % (C / 8)) * 8;
+        *reinterpret_cast<uint4*>(&Tbo[(size_t)ch * C * C + i * C + j]) =
+            *reinterpret_cast<const uint4*>(&sTb[i][j]);
     }
     if constexpr (SAFE) {
         __syncthreads();
         flush_counts(sdg, sf.diag, NDIAG_PREP);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// wy_u: U = T diag(beta) V for one chunk-head (bf16 inputs at chunk 64), from
+// the bf16 T that prep2 wrote: T rows and the chunk's v rows (transposed, beta
+// folded in) into LDS, then bf16 MFMA products over the lower-triangular T;
+// U fp32 out.  With SAFE the values pass through guard() (the U stage), and
+// Uro (training with clip) also gets them before clipping.
+// ---------------------------------------------------------------------------
+constexpr int NTHR_U = 256;
+
+template <int C, int DV, bool SAFE>
+__global__ void __launch_bounds__(NTHR_U)
+wy_u_kernel(const bf16* __restrict__ Tbi, const bf16* __restrict__ v, const float* __restrict__ beta,
+            float* __restrict__ Uo, int T, int H, int NC, Safety sf, float* __restrict__ Uro)
+{
+    constexpr int PT = C + 8, NW = NTHR_U / 64, NB = C / 16;
+    constexpr int NT8 = C * C / 8, NV8 = C * DV / 8;
+    constexpr int QT = (NT8 + NTHR_U - 1) / NTHR_U, QV = (NV8 + NTHR_U - 1) / NTHR_U;
+    __shared__ __align__(16) bf16 sT[C][PT];
+    __shared__ __align__(16) bf16 sXV[DV][PT];  // (beta V)^T
+    __shared__ float sbeta[C];
+    __shared__ unsigned int sdg[2];
+    const int ch = blockIdx.x;
+    const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
+    const int t0 = n * C;
+    const int nvalid = min(C, T - t0);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
+    const size_t tok0 = ((size_t)b * T + t0) * H + h;
+    const size_t rsV = (size_t)H * DV;
+    if (SAFE && tid < 2) sdg[tid] = 0u;
+
+    uint4 tw[QT], vw[QV];
+#pragma unroll
+    for (int u = 0; u < QT; ++u)
+        tw[u] = *reinterpret_cast<const uint4*>(Tbi + (size_t)ch * C * C + 8 * min(tid + NTHR_U * u, NT8 - 1));
+#pragma unroll
+    for (int u = 0; u < QV; ++u) {
+        const int idx = min(tid + NTHR_U * u, NV8 - 1);
+        const int r = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
+        vw[u] = *reinterpret_cast<const uint4*>(v + tok0 * DV + min(r, nvalid - 1) * rsV + j0);
+    }
+    const float bv = beta[tok0 + (size_t)min(tid % C, nvalid - 1) * H];
+    if (tid < C) sbeta[tid] = tid < nvalid ? bv : 0.f;
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+        const int idx = tid + NTHR_U * u;
+        if (idx < NT8) *reinterpret_cast<uint4*>(&sT[idx / (C / 8)][(idx % (C / 8)) * 8]) = tw[u];
+    }
+    __syncthreads();  // sbeta
+#pragma unroll
+    for (int u = 0; u < QV; ++u) {
+        const int idx = tid + NTHR_U * u;
+        if (idx < NV8) {
+            const int r = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
+            const float bt = r < nvalid ? sbeta[r] : 0.f;
+            const uint32_t wd[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sXV[j0 + 2 * e][r] = f32_to_bf16(bt * __uint_as_float(wd[e] << 16));
+                sXV[j0 + 2 * e + 1][r] = f32_to_bf16(bt * __uint_as_float(wd[e] & 0xFFFF0000u));
+            }
+        }
+    }
+    __syncthreads();
+    unsigned int* sd = SAFE && sf.diag ? &sdg[0] : nullptr;
+    constexpr int TU = NB * (DV / 16);
+    float* Uc = Uo + (size_t)ch * C * DV;
+    for (int idx = w; idx < TU; idx += NW) {
+        const int ti = idx / (DV / 16), tj = idx % (DV / 16);
+        const int K = ((16 * (ti + 1) + 31) / 32) * 32;  // T is lower triangular
+        // the tile of U^T = X_V^T T^T: a lane holds 4 consecutive columns of one U row
+        f32x4 acc = mma_kc_dyn(zero4(), &sXV[tj * 16][0], PT, &sT[ti * 16][0], PT, K);
+        const size_t e = (size_t)(ti * 16 + lr) * DV + tj * 16 + 4 * lq;
+        if (SAFE && Uro)
+            *reinterpret_cast<float4*>(&Uro[(size_t)ch * C * DV + e]) = float4{acc[0], acc[1], acc[2], acc[3]};
+        if (SAFE) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = guard(acc[r], sf.clip, sd);
+        }
+        *reinterpret_cast<float4*>(&Uc[e]) = float4{acc[0], acc[1], acc[2], acc[3]};
+    }
+    if constexpr (SAFE) {
+        __syncthreads();
+        flush_counts(sdg, sf.diag ? sf.diag + 2 * GDN_DIAG_U : nullptr, 2);
     }
 }
 
@@ -1305,19 +1384,26 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
         bf16* Qb = (bf16*)Qg;
         bf16* Kb = (bf16*)Kh;
         bf16* Pb = (bf16*)Ps;
+        bf16* Tb = (bf16*)(ws + p.o_Tb);
         auto launch = [&](auto pch, auto l2n, auto safe) {
             GDN_LAUNCH(want_T ? "prep_T" : "prep",
                        (prep2_kernel<C, DK, DV, decltype(pch)::value, decltype(l2n)::value,
                                      decltype(safe)::value>),
                        grid, dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g,
-                       beta, p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, U, Qb, Qb + n * C * DK,
-                       Kb, Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm, rn, sf, Uro, Wro);
+                       beta, p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, Tb, Qb, Qb + n * C * DK,
+                       Kb, Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm, rn, sf, Wro);
             return GDN_OK;
         };
-        return with_bool(p.decay == GDN_DECAY_PER_CHANNEL, [&](auto pch) {
+        gdn_status s = with_bool(p.decay == GDN_DECAY_PER_CHANNEL, [&](auto pch) {
             return with_bool(p.l2n, [&](auto l2n) {
                 return with_bool(sf.on(), [&](auto safe) { return launch(pch, l2n, safe); });
             });
+        });
+        if (s != GDN_OK) return s;
+        return with_bool(sf.on(), [&](auto safe) {
+            GDN_LAUNCH("wy_u", (wy_u_kernel<C, DV, decltype(safe)::value>), grid, dim3(NTHR_U), st,
+                       (const bf16*)Tb, (const bf16*)v, beta, U, p.T, p.H, p.NC, sf, Uro);
+            return GDN_OK;
         });
     }
     if (p.decay == GDN_DECAY_PER_CHANNEL)
