@@ -1433,6 +1433,22 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         kv[i] = ok ? kx : 0.f;
         dq[i] = dk[i] = dG[i] = dbr[i] = 0.f;
     }
+    // the bchunk1 hand-offs of this thread's rows, in the same round of loads
+    // (two bf16 per word); used after the first barrier
+    uint32_t hQ[RPP / 2], hK[RPP / 2], hX[RPP / 2];
+    {
+        const size_t e0 = (size_t)ch * C * DK + c;
+#pragma unroll
+        for (int i = 0; i < RPP; i += 2) {
+            const size_t a0 = e0 + (size_t)(p0 + i) * DK, a1 = a0 + DK;
+            hQ[i / 2] = (uint32_t)dQgi[a0].bits | ((uint32_t)dQgi[a1].bits << 16);
+            hK[i / 2] = (uint32_t)dKhi[a0].bits | ((uint32_t)dKhi[a1].bits << 16);
+            hX[i / 2] = (uint32_t)dXKi[a0].bits | ((uint32_t)dXKi[a1].bits << 16);
+        }
+    }
+    auto hw = [](const uint32_t* h, int i) {
+        return __uint_as_float((i & 1) ? (h[i / 2] & 0xFFFF0000u) : (h[i / 2] << 16));
+    };
     float rq[L2N ? RPP : 1], rk[L2N ? RPP : 1];
     // per-head decay with L2N: all rows' r (q rows, then k rows) in the bytes
     // of sR2, which only the per-channel levels use
@@ -1511,7 +1527,6 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
 
     // ---- Gamma, Kh factor; contributions of dQg, dKh; X_K = diag(beta) K o Gamma
     if (cp) {
-        const size_t e0 = (size_t)ch * C * DK + c;
         float pre = 1.f, suf = 1.f;
         for (int pp = 0; pp < part; ++pp) pre *= stot[pp][cl];
         for (int pp = part + 1; pp < NPART; ++pp) suf *= stot[pp][cl];
@@ -1525,8 +1540,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
 #pragma unroll
         for (int i = RPP - 1; i >= 0; --i) {
             const int r = p0 + i;
-            const float dqg = to_f32(dQgi[e0 + r * DK]), dkh = to_f32(dKhi[e0 + r * DK]);
-            const float dx = to_f32(dXKi[e0 + r * DK]);
+            const float dqg = hw(hQ, i), dkh = hw(hK, i), dx = hw(hX, i);
             dq[i] += scale * Gm[i] * dqg;
             dG[i] += scale * qv[i] * Gm[i] * dqg;
             const float khv = kv[i] * kap;
