@@ -1172,9 +1172,17 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         }
     }
 
-    uint4 pf[QPT];
-    float upf[MD][4], gpf[MS][4];
-    auto fetch = [&](int n) {  // chunk n tables -> registers
+    // Two register sets of prefetched tables: chunk n + 1 arrives in one while
+    // chunk n + 2 is fetched into the other, so two steps of compute cover the
+    // latency.  Fetches are unconditional (the chunk index is clamped; the tail
+    // re-reads the last chunk) and the loop body is a pair of steps with the
+    // sets fixed, so the waits are exact.
+    using PFW = uint4[QPT];
+    using UF = float[MD][4];
+    using GF = float[MS][4];
+    uint4 pfA[QPT], pfB[QPT];
+    float upA[MD][4], upB[MD][4], gpA[MS][4], gpB[MS][4];
+    auto fetch = [&](int n, PFW& pf, UF& upf, GF& gpf) {  // chunk n tables -> registers
         const size_t ch = (size_t)bh * NC + n;
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
@@ -1203,7 +1211,8 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             for (int r = 0; r < 4; ++r) gpf[m][r] = gami[ch * DK + si * 16 + 4 * lq + r];
         }
     };
-    auto stash = [&]() {  // registers -> LDS tables
+    float uc[MD][4], gc[MS][4];
+    auto stash = [&](PFW& pf, UF& upf, GF& gpf) {  // registers -> LDS tables, U and gam
         // keep the use of the prefetched words here: hoisted into the compute
         // phase they would make it wait for the prefetch
         __builtin_amdgcn_sched_barrier(0);
@@ -1223,23 +1232,23 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 *reinterpret_cast<uint4*>(&sP[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
             }
         }
+#pragma unroll
+        for (int m = 0; m < MD; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) uc[m][r] = upf[m][r];
+#pragma unroll
+        for (int m = 0; m < MS; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
     };
-    fetch(0);
-    stash();
-    float uc[MD][4], gc[MS][4];
-#pragma unroll
-    for (int m = 0; m < MD; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) uc[m][r] = upf[m][r];
-#pragma unroll
-    for (int m = 0; m < MS; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
+    fetch(0, pfA, upA, gpA);
+    stash(pfA, upA, gpA);
     __syncthreads();
+    fetch(min(1, NC - 1), pfB, upB, gpB);
 
     // Each step's outputs are staged in LDS and written with 16-byte stores after
-    // the step's prefetch wait (issued before it, the wait would also cover them:
-    // loads and stores share one counter).
+    // the step's stash (issued before the wait for the prefetch, that wait would
+    // also cover them: loads and stores share one counter).
     if (SAVE) {  // chunk 0 starts from h0
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
@@ -1250,10 +1259,12 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 Sst[((size_t)bh * NC * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = sacc[m][r];
         }
     }
-    for (int n = 0; n < NC; ++n) {
+    // one step: chunk n with its tables in LDS; `nx` holds chunk n + 1 (stashed
+    // at the end), `fr` is free and takes chunk n + 2
+    auto step = [&](int n, PFW& pnx, UF& unx, GF& gnx, PFW& pfr, UF& ufr, GF& gfr) {
         const size_t ch = (size_t)bh * NC + n;
         const int pb = n & 1;
-        if (n + 1 < NC) fetch(n + 1);
+        fetch(min(n + 2, NC - 1), pfr, ufr, gfr);
         // D = U - W S  and  O1 = Qg S
         f32x4 o1[MD];
 #pragma unroll
@@ -1301,17 +1312,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             }
         }
         __syncthreads();
-        if (n + 1 < NC) {
-            stash();
-#pragma unroll
-            for (int m = 0; m < MD; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) uc[m][r] = upf[m][r];
-#pragma unroll
-            for (int m = 0; m < MS; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
-        }
+        stash(pnx, unx, gnx);  // chunk n + 1 (at the last step a harmless repeat)
         __syncthreads();
         // this step's stores, from the staging: the start state of chunk n + 1,
         // then D and o of chunk n (rows of BV contiguous elements)
@@ -1343,7 +1344,13 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                         *reinterpret_cast<const uint4*>(&sOr[pb][i][j8]);
             }
         }
+    };
+    int n = 0;
+    for (; n + 1 < NC; n += 2) {
+        step(n, pfB, upB, gpB, pfA, upA, gpA);
+        step(n + 1, pfA, upA, gpA, pfB, upB, gpB);
     }
+    if (n < NC) step(n, pfB, upB, gpB, pfA, upA, gpA);
     if (hT) {
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
