@@ -223,9 +223,15 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
         }
     }
 
-    uint4 pf[QPT];
-    float gpf[MS][4];
-    auto fetch = [&](int n) {
+    // Two register sets of prefetched tables (the reverse scan's chunk n - 1
+    // arrives in one while chunk n - 2 is fetched into the other): unconditional
+    // fetches (clamped chunk index) and a loop body of two steps with the sets
+    // fixed keep the waits exact.
+    using PFW = uint4[QPT];
+    using GF = float[MS][4];
+    uint4 pfA[QPT], pfB[QPT];
+    float gpA[MS][4], gpB[MS][4];
+    auto fetch = [&](int n, PFW& pf, GF& gpf) {
         const size_t ch = (size_t)bh * NC + n;
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
@@ -255,7 +261,8 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
             for (int r = 0; r < 4; ++r) gpf[m][r] = gami[ch * DK + si * 16 + 4 * lq + r];
         }
     };
-    auto stash = [&]() {
+    float gc[MS][4];
+    auto stash = [&](PFW& pf, GF& gpf) {
         // keep the use of the prefetched words here: hoisted into the compute
         // phase they would make it wait for the prefetch
         __builtin_amdgcn_sched_barrier(0);
@@ -284,50 +291,51 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
                 }
             }
         }
+#pragma unroll
+        for (int m = 0; m < MS; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
     };
-    float gc[MS][4];
-    fetch(NC - 1);
-    stash();
-#pragma unroll
-    for (int m = 0; m < MS; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
+    fetch(NC - 1, pfA, gpA);
+    stash(pfA, gpA);
     __syncthreads();
+    fetch(max(NC - 2, 0), pfB, gpB);
 
-    for (int n = NC - 1; n >= 0; --n) {
+    // one step: chunk n in LDS; `nx` holds chunk n - 1 (stashed at the end),
+    // `fr` is free and takes chunk n - 2
+    auto step = [&](int n, PFW& pnx, GF& gnx, PFW& pfr, GF& gfr) {
         const size_t ch = (size_t)bh * NC + n;
-        if (n > 0) fetch(n - 1);
+        fetch(max(n - 2, 0), pfr, gfr);
+        // every wave owns MS state tiles and MD delta tiles (TS, TD are
+        // multiples of the wave count): no guards, so the stores are counted
+        // exactly and the stash below waits only for its own prefetch
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
             const int idx = w + NW * m;
-            if (idx < TS) {
-                const int si = idx / (BV / 16), sj = idx % (BV / 16);
+            const int si = idx / (BV / 16), sj = idx % (BV / 16);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dSt[(ch * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = dacc[m][r];
-            }
+            for (int r = 0; r < 4; ++r)
+                dSt[(ch * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = dacc[m][r];
         }
         // dD = scale P^T dO + Kh dS'
 #pragma unroll
         for (int m = 0; m < MD; ++m) {
             const int idx = w + NW * m;
-            if (idx < TD) {
-                const int ti = idx / (BV / 16), tj = idx % (BV / 16);
-                f32x4 acc = mma_kc<C>(zero4(), &sPT[ti * 16][0], PT, &sdOt[tj * 16][0], PT);
-                acc = mma_kc<DK>(acc, &sK[ti * 16][0], PA, &sdSt[tj * 16][0], PA);
+            const int ti = idx / (BV / 16), tj = idx % (BV / 16);
+            f32x4 acc = mma_kc<C>(zero4(), &sPT[ti * 16][0], PT, &sdOt[tj * 16][0], PT);
+            acc = mma_kc<DK>(acc, &sK[ti * 16][0], PA, &sdSt[tj * 16][0], PA);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dDt[(ch * C + ti * 16 + 4 * lq + r) * DV + v0 + tj * 16 + lr] = acc[r];
-                *reinterpret_cast<uint2*>(&sdDt[tj * 16 + lr][ti * 16 + 4 * lq]) =
-                    pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
-            }
+            for (int r = 0; r < 4; ++r)
+                dDt[(ch * C + ti * 16 + 4 * lq + r) * DV + v0 + tj * 16 + lr] = acc[r];
+            *reinterpret_cast<uint2*>(&sdDt[tj * 16 + lr][ti * 16 + 4 * lq]) =
+                pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
         }
         __syncthreads();
         // dS <- gam o dS' + Qg^T dO - W^T dD
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
             const int idx = w + NW * m;
-            if (idx < TS) {
+            {
                 const int si = idx / (BV / 16), sj = idx % (BV / 16);
                 f32x4 acc;
 #pragma unroll
@@ -341,15 +349,15 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
             }
         }
         __syncthreads();
-        if (n > 0) {
-            stash();
-#pragma unroll
-            for (int m = 0; m < MS; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
-        }
+        stash(pnx, gnx);  // chunk n - 1 (at the last step a harmless repeat)
         __syncthreads();
+    };
+    int n = NC - 1;
+    for (; n >= 1; n -= 2) {
+        step(n, pfB, gpB, pfA, gpA);
+        step(n - 1, pfA, gpA, pfB, gpB);
     }
+    if (n == 0) step(0, pfB, gpB, pfA, gpA);
     if (dh0) {
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
