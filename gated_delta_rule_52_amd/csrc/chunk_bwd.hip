@@ -166,14 +166,16 @@ bscan_kernel(const float* __restrict__ Qgi, const float* __restrict__ Khi,
 
 
 // ---------------------------------------------------------------------------
-// reverse scan over bf16 chunk tables (bf16 inputs): the structure of the
-// forward scan2 -- 8 waves, dS slice in accumulator registers, K-contiguous
-// bf16 operands (P^T, Kh, Qg^T, W^T, dO^T, dS'^T, dD^T), next chunk prefetched.
+// bscan over bf16 tables -- 8 waves, dS slice in accumulator registers.  The
+// four tables of a chunk (P^T, Kh, Qg^T, W^T; K-contiguous bf16 rows) go
+// straight from memory into one of two LDS buffers (16-byte direct loads, rows
+// swizzled instead of padded), one chunk ahead; the dO slice and the decay
+// come through registers (dO is transposed on the way).
 // ---------------------------------------------------------------------------
 constexpr int NTHR_B = 512;
 
 template <int C, int DK, int DV>
-__global__ void __launch_bounds__(NTHR_B) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ void __launch_bounds__(NTHR_B)
 bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
               const bf16* __restrict__ QgTb, const bf16* __restrict__ WTb,
               const float* __restrict__ gami, const bf16* __restrict__ dO,
@@ -183,21 +185,27 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
     constexpr int BV = 32, NS = DV / BV, NW = NTHR_B / 64;
     constexpr int PA = DK + 8, PT = C + 8;
     constexpr int TD = (C / 16) * (BV / 16), TS = (DK / 16) * (BV / 16);
-    constexpr int MD = (TD + NW - 1) / NW, MS = (TS + NW - 1) / NW;
-    // 16-byte words of one chunk's tables, whole multiples of the thread count
-    // (branch-free prefetch: the compiler waits exactly for it, not for the
-    // stores issued after it); the dO slice has QO <= NTHR_B words
-    constexpr int QP = C * C / 8, QW = C * DK / 8, QK = DK * C / 8, QO = C * BV / 8;
-    constexpr int QALL = QP + QW + 2 * QK + QO, QPT = (QALL + NTHR_B - 1) / NTHR_B;
-    // every table is a whole number of words per thread (the dO slice fills part
-    // of the last slot), so the table of word slot q is known at compile time and
-    // the prefetch has no branches: the compiler then waits exactly for it, not
-    // also for the stores issued after it
-    static_assert(QP % NTHR_B == 0 && QW % NTHR_B == 0 && QK % NTHR_B == 0 && QO <= NTHR_B, "");
-    static_assert(QP + QW + 2 * QK == (QPT - 1) * NTHR_B, "dO in the last slot");
-    static_assert(TD % NW == 0 && TS % NW == 0, "tile split");
-    __shared__ __align__(16) bf16 sPT[C][PT], sK[C][PA], sQT[DK][PT], sWT[DK][PT], sdSt[BV][PA],
-        sdOt[BV][PT], sdDt[BV][PT];
+    constexpr int MD = TD / NW, MS = TS / NW;
+    static_assert(TD % NW == 0 && TS % NW == 0, "every wave owns whole tiles");
+    // tables as 16-byte words: row widths, sizes and offsets within a buffer
+    constexpr int WC = C / 8, WK = DK / 8;
+    constexpr int OP = 0, OK = OP + C * WC, OQ = OK + C * WK, OW = OQ + DK * WC, QT = OW + DK * WC;
+    constexpr int NQ = QT / NTHR_B;
+    static_assert(OK % NTHR_B == 0 && OQ % NTHR_B == 0 && OW % NTHR_B == 0 && QT % NTHR_B == 0,
+                  "every load instruction lies in one table");
+    constexpr int QO = C * BV / 8, QG = DK / 4;  // dO slice and decay words (through registers)
+    static_assert(QO + QG <= NTHR_B, "");
+    // two buffers, separate arrays: the compiler then sees that reads of one
+    // cannot alias the direct loads into the other and does not wait for them
+    __shared__ __align__(16) uint4 sTab0[QT], sTab1[QT];
+    __shared__ __align__(16) bf16 sdSt[BV][PA], sdOt[BV][PT], sdDt[BV][PT];
+    // 2-byte views for the transposed writes: one index expression per write
+    // keeps each address a single step from its array (the alias information
+    // that spares those writes a wait for the direct loads is kept)
+    uint16_t* const dSt16 = &sdSt[0][0].bits;
+    uint16_t* const dDt16 = &sdDt[0][0].bits;
+    uint16_t* const dOt16 = &sdOt[0][0].bits;
+    __shared__ __align__(16) float sgam[DK];  // the chunk's whole-chunk decay
 
     const int x = blockIdx.x;
     const int grp = x / (8 * NS), rem = x % (8 * NS);
@@ -208,166 +216,142 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int lr = l & 15, lq = l >> 4;
 
+    // The state and delta tiles are computed transposed (rows along Dv): a
+    // lane's four accumulator values are then four consecutive Dv columns of
+    // one row of dS (or dD), stored with one 16-byte write; their bf16 copies
+    // in LDS (K-contiguous operands of the next products) take 2-byte writes.
+    // dS tile m of this wave: dacc[m][r] = dS[si*16 + lr][v0 + sj*16 + 4 lq + r].
     f32x4 dacc[MS];
 #pragma unroll
     for (int m = 0; m < MS; ++m) {
         const int idx = w + NW * m;
+        const int si = idx / (BV / 16), sj = idx % (BV / 16);
         dacc[m] = zero4();
-        if (idx < TS) {
-            const int si = idx / (BV / 16), sj = idx % (BV / 16);
+        if (dhT)
+            dacc[m] = *reinterpret_cast<const f32x4*>(
+                dhT + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dacc[m][r] = dhT ? dhT[((size_t)bh * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] : 0.f;
-            *reinterpret_cast<uint2*>(&sdSt[sj * 16 + lr][si * 16 + 4 * lq]) =
-                pack4_bf16(dacc[m][0], dacc[m][1], dacc[m][2], dacc[m][3]);
-        }
+        for (int r = 0; r < 4; ++r) dSt16[(sj * 16 + 4 * lq + r) * PA + si * 16 + lr] = f32_to_bf16(dacc[m][r]).bits;
     }
 
-    // Two register sets of prefetched tables (the reverse scan's chunk n - 1
-    // arrives in one while chunk n - 2 is fetched into the other): unconditional
-    // fetches (clamped chunk index) and a loop body of two steps with the sets
-    // fixed keep the waits exact.
-    using PFW = uint4[QPT];
-    using GF = float[MS][4];
-    uint4 pfA[QPT], pfB[QPT];
-    float gpA[MS][4], gpB[MS][4];
-    auto fetch = [&](int n, PFW& pf, GF& gpf) {
+    // slot tid + NTHR_B q of a buffer takes table word (row, w ^ (row & 7)),
+    // (row, w) being the slot's place in its table
+    int goff[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int g0 = q * NTHR_B;
+        const int wpr = (g0 >= OK && g0 < OQ) ? WK : WC;
+        const int s = g0 + tid - (g0 < OK ? OP : g0 < OQ ? OK : g0 < OW ? OQ : OW);
+        const int row = s / wpr, wd = s % wpr;
+        goff[q] = (row * wpr + (wd ^ (row & 7))) * 8;
+    }
+    auto fetch_tables = [&](int n, uint4* buf) {
         const size_t ch = (size_t)bh * NC + n;
 #pragma unroll
-        for (int q = 0; q < QPT; ++q) {
-            const int idx = tid + NTHR_B * q;
-            uint4 val = uint4{0u, 0u, 0u, 0u};
-            if (q * NTHR_B < QP) {
-                val = reinterpret_cast<const uint4*>(PsTb + ch * C * C)[idx];
-            } else if (q * NTHR_B < QP + QW) {
-                val = reinterpret_cast<const uint4*>(Khb + ch * C * DK)[idx - QP];
-            } else if (q * NTHR_B < QP + QW + QK) {
-                val = reinterpret_cast<const uint4*>(QgTb + ch * C * DK)[idx - QP - QW];
-            } else if (q * NTHR_B < QP + QW + 2 * QK) {
-                val = reinterpret_cast<const uint4*>(WTb + ch * C * DK)[idx - QP - QW - QK];
-            } else {  // dO slice: rows past the end (or threads past the slice) repeat a valid word, then zero
-                const int e = min(idx - QP - QW - 2 * QK, QO - 1);
-                const int r = e / (BV / 8), j0 = (e % (BV / 8)) * 8;
-                const int t = n * C + r;
-                const uint4 ov = *reinterpret_cast<const uint4*>(dO + (((size_t)b * T + min(t, T - 1)) * H + h) * DV + v0 + j0);
-                val = t < T ? ov : uint4{0u, 0u, 0u, 0u};
-            }
-            pf[q] = val;
-        }
-#pragma unroll
-        for (int m = 0; m < MS; ++m) {
-            const int si = (w + NW * m) / (BV / 16);  // w + NW m < TS for every wave
-#pragma unroll
-            for (int r = 0; r < 4; ++r) gpf[m][r] = gami[ch * DK + si * 16 + 4 * lq + r];
+        for (int q = 0; q < NQ; ++q) {
+            const int g0 = q * NTHR_B;
+            const bf16* src = g0 < OK ? PsTb + ch * C * C
+                            : g0 < OQ ? Khb + ch * C * DK
+                            : g0 < OW ? QgTb + ch * C * DK
+                                      : WTb + ch * C * DK;
+            dma16(src + goff[q], buf + g0 + 64 * w);
         }
     };
-    float gc[MS][4];
-    auto stash = [&](PFW& pf, GF& gpf) {
-        // keep the use of the prefetched words here: hoisted into the compute
-        // phase they would make it wait for the prefetch
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < QPT; ++q) {
-            const int idx = tid + NTHR_B * q;
-            if (q * NTHR_B < QP) {
-                *reinterpret_cast<uint4*>(&sPT[idx / (C / 8)][(idx % (C / 8)) * 8]) = pf[q];
-            } else if (q * NTHR_B < QP + QW) {
-                const int e = idx - QP;
-                *reinterpret_cast<uint4*>(&sK[e / (DK / 8)][(e % (DK / 8)) * 8]) = pf[q];
-            } else if (q * NTHR_B < QP + QW + QK) {
-                const int e = idx - QP - QW;
-                *reinterpret_cast<uint4*>(&sQT[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
-            } else if (q * NTHR_B < QP + QW + 2 * QK) {
-                const int e = idx - QP - QW - QK;
-                *reinterpret_cast<uint4*>(&sWT[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
-            } else if (idx < QALL) {  // dO row r, columns j0..j0+7 -> dO^T
-                const int e = idx - QP - QW - 2 * QK;
-                const int r = e / (BV / 8), j0 = (e % (BV / 8)) * 8;
-                const uint32_t u[4] = {pf[q].x, pf[q].y, pf[q].z, pf[q].w};
-#pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                    sdOt[j0 + 2 * z][r].bits = (uint16_t)(u[z] & 0xFFFFu);
-                    sdOt[j0 + 2 * z + 1][r].bits = (uint16_t)(u[z] >> 16);
-                }
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < MS; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
+    // the dO slice (threads < QO: row e / 4, columns 8 (e % 4) ..) and the decay
+    // (the next QG threads); the rest repeat a valid dO word.  Rows past the end
+    // are clamped here and zeroed in stash_words().
+    const bool is_gam = tid >= QO && tid < QO + QG;
+    const int eo = min(tid, QO - 1), ro = eo / (BV / 8), jo = (eo % (BV / 8)) * 8;
+    uint4 pw;
+    auto fetch_words = [&](int n) {
+        const size_t ch = (size_t)bh * NC + n;
+        const int t = min(n * C + ro, T - 1);
+        const uint4* src = is_gam ? reinterpret_cast<const uint4*>(gami + ch * DK) + (tid - QO)
+                                  : reinterpret_cast<const uint4*>(dO + (((size_t)b * T + t) * H + h) * DV + v0 + jo);
+        pw = *src;
     };
-    fetch(NC - 1, pfA, gpA);
-    stash(pfA, gpA);
-    __syncthreads();
-    fetch(max(NC - 2, 0), pfB, gpB);
+    auto stash_words = [&](int n) {
+        if (tid < QO) {  // dO row ro, columns jo..jo+7 -> dO^T (zero past the end)
+            const bool live = n * C + ro < T;
+            const uint32_t u[4] = {live ? pw.x : 0u, live ? pw.y : 0u, live ? pw.z : 0u, live ? pw.w : 0u};
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                dOt16[(jo + 2 * z) * PT + ro] = (uint16_t)(u[z] & 0xFFFFu);
+                dOt16[(jo + 2 * z + 1) * PT + ro] = (uint16_t)(u[z] >> 16);
+            }
+        } else if (is_gam) {
+            *reinterpret_cast<uint4*>(&sgam[4 * (tid - QO)]) = pw;
+        }
+    };
+    // vector memory operations issued after a chunk's table loads and before
+    // the wait for them: the dO/decay word and the step's dS and dD stores
+    constexpr int AFTER = 1 + MS + MD;
 
-    // one step: chunk n in LDS; `nx` holds chunk n - 1 (stashed at the end),
-    // `fr` is free and takes chunk n - 2
-    auto step = [&](int n, PFW& pnx, GF& gnx, PFW& pfr, GF& gfr) {
+    // chunk n sits in buffer (NC - 1 - n) & 1: the steps of a pair of chunks
+    // use fixed buffers
+    fetch_tables(NC - 1, sTab0);
+    fetch_words(NC - 1);
+    stash_words(NC - 1);
+    wait_vmcnt<0>();  // the direct loads have landed
+    __syncthreads();
+
+    auto step = [&](int n, const uint4* tb, uint4* tnx) {
         const size_t ch = (size_t)bh * NC + n;
-        fetch(max(n - 2, 0), pfr, gfr);
-        // every wave owns MS state tiles and MD delta tiles (TS, TD are
-        // multiples of the wave count): no guards, so the stores are counted
-        // exactly and the stash below waits only for its own prefetch
+        const int nx = max(n - 1, 0);  // at n = 0 a harmless reload into the idle buffer
+        fetch_tables(nx, tnx);
+        fetch_words(nx);
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
             const int idx = w + NW * m;
             const int si = idx / (BV / 16), sj = idx % (BV / 16);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dSt[(ch * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = dacc[m][r];
+            *reinterpret_cast<f32x4*>(dSt + (ch * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq) = dacc[m];
         }
-        // dD = scale P^T dO + Kh dS'
+        // dD^T = scale dO^T P + dS'^T Kh^T: acc[r] = dD[ti*16 + lr][v0 + tj*16 + 4 lq + r]
 #pragma unroll
         for (int m = 0; m < MD; ++m) {
             const int idx = w + NW * m;
             const int ti = idx / (BV / 16), tj = idx % (BV / 16);
-            f32x4 acc = mma_kc<C>(zero4(), &sPT[ti * 16][0], PT, &sdOt[tj * 16][0], PT);
-            acc = mma_kc<DK>(acc, &sK[ti * 16][0], PA, &sdSt[tj * 16][0], PA);
+            f32x4 acc = mma_kc_bsw<C, WC>(zero4(), &sdOt[tj * 16][0], PT, tb + OP, ti * 16);
+            acc = mma_kc_bsw<DK, WK>(acc, &sdSt[tj * 16][0], PA, tb + OK, ti * 16);
+            *reinterpret_cast<f32x4*>(dDt + (ch * C + ti * 16 + lr) * DV + v0 + tj * 16 + 4 * lq) = acc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dDt[(ch * C + ti * 16 + 4 * lq + r) * DV + v0 + tj * 16 + lr] = acc[r];
-            *reinterpret_cast<uint2*>(&sdDt[tj * 16 + lr][ti * 16 + 4 * lq]) =
-                pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+            for (int r = 0; r < 4; ++r) dDt16[(tj * 16 + 4 * lq + r) * PT + ti * 16 + lr] = f32_to_bf16(acc[r]).bits;
         }
         __syncthreads();
-        // dS <- gam o dS' + Qg^T dO - W^T dD
+        // dS^T <- dS'^T o gam + dO^T Qg - dD^T W
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
             const int idx = w + NW * m;
-            {
-                const int si = idx / (BV / 16), sj = idx % (BV / 16);
-                f32x4 acc;
+            const int si = idx / (BV / 16), sj = idx % (BV / 16);
+            const float gk = sgam[si * 16 + lr];
+            f32x4 acc;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = gc[m][r] * dacc[m][r];
-                acc = mma_kc<C>(acc, &sQT[si * 16][0], PT, &sdOt[sj * 16][0], PT);
-                const f32x4 wd = mma_kc<C>(zero4(), &sWT[si * 16][0], PT, &sdDt[sj * 16][0], PT);
+            for (int r = 0; r < 4; ++r) acc[r] = gk * dacc[m][r];
+            acc = mma_kc_bsw<C, WC>(acc, &sdOt[sj * 16][0], PT, tb + OQ, si * 16);
+            const f32x4 wd = mma_kc_bsw<C, WC>(zero4(), &sdDt[sj * 16][0], PT, tb + OW, si * 16);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dacc[m][r] = acc[r] - wd[r];
-                *reinterpret_cast<uint2*>(&sdSt[sj * 16 + lr][si * 16 + 4 * lq]) =
-                    pack4_bf16(dacc[m][0], dacc[m][1], dacc[m][2], dacc[m][3]);
+            for (int r = 0; r < 4; ++r) {
+                dacc[m][r] = acc[r] - wd[r];
+                dSt16[(sj * 16 + 4 * lq + r) * PA + si * 16 + lr] = f32_to_bf16(dacc[m][r]).bits;
             }
         }
         __syncthreads();
-        stash(pnx, gnx);  // chunk n - 1 (at the last step a harmless repeat)
+        stash_words(nx);
+        wait_vmcnt<AFTER>();  // chunk nx's tables have landed
         __syncthreads();
     };
     int n = NC - 1;
     for (; n >= 1; n -= 2) {
-        step(n, pfB, gpB, pfA, gpA);
-        step(n - 1, pfA, gpA, pfB, gpB);
+        step(n, sTab0, sTab1);
+        step(n - 1, sTab1, sTab0);
     }
-    if (n == 0) step(0, pfB, gpB, pfA, gpA);
+    if (n == 0) step(0, sTab0, sTab1);
     if (dh0) {
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
             const int idx = w + NW * m;
-            if (idx < TS) {
-                const int si = idx / (BV / 16), sj = idx % (BV / 16);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dh0[((size_t)bh * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = dacc[m][r];
-            }
+            const int si = idx / (BV / 16), sj = idx % (BV / 16);
+            *reinterpret_cast<f32x4*>(dh0 + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq) = dacc[m];
         }
     }
 }

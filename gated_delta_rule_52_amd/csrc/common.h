@@ -68,6 +68,30 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// 16-byte direct load from global memory into LDS: lane i's word lands at
+// lds_wave_base + 16 i (the base is the same for the whole wave).  Written as
+// inline assembly so that the compiler sees no pending LDS write (it would
+// otherwise wait for the load before every LDS access it cannot tell apart
+// from the target, and at every barrier); the caller waits for it with an
+// explicit vmcnt and a barrier before reading the words.  The memory clobber
+// keeps the compiler's memory operations on their side of the load, so the
+// number of vector memory operations issued after it is what the code shows.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_wave_base)
+{
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(gptr) : "memory", "m0");
+}
+
+// s_waitcnt with only the vector memory count limited (expcnt and lgkmcnt at
+// their maxima); N < 16
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x3F70 | N);
+}
+
 // Call f with std::true_type or std::false_type: a runtime flag picks a
 // template instance.
 template <typename F>
