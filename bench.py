@@ -319,15 +319,20 @@ def main():
 
     # ---- forward only
     ms_fwd = fwd_tps = None
+    fwd_kernels = None
     if not args.no_fwd:
         for _ in range(3):
             fwd()
         torch.cuda.synchronize()
+        frec = LaunchRecorder(args.steps * 8 + 8)
         ev0.record()
-        for _ in range(args.steps):
-            fwd()
+        with frec:
+            for _ in range(args.steps):
+                fwd()
         ev1.record()
         torch.cuda.synchronize()
+        fwd_kernels = {name: float(np.mean(ms)) * 1e3 for name, ms in frec.by_kernel().items()}
+        frec.close()
         ms_fwd = ev0.elapsed_time(ev1) / args.steps
         fwd_tps = B * T / (ms_fwd * 1e-3)
         log(f"[bench] fwd {ms_fwd:.3f} ms ({fwd_tps / 1e6:.2f} M tokens/s)")
@@ -629,6 +634,7 @@ def main():
                    "parallelism": "single GPU"},
         "fwd_tokens_per_s": fwd_tps,
         "fwd_ms": ms_fwd,
+        "fwd_kernels_us": fwd_kernels,
         "parity_ok": parity_ok,
         "parity_max_rel_err": par,
         "kernels": others,

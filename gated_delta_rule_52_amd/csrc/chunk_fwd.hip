@@ -1112,7 +1112,8 @@ scan_kernel(const float* __restrict__ Wi, const float* __restrict__ Ui,
 
 
 // ---------------------------------------------------------------------------
-// scan over bf16 chunk tables (bf16 inputs): 8 waves; the fp32 state slice
+// scan2: the state-saving forward scans (training forward, backward
+// recompute) over bf16 chunk tables (bf16 inputs): 8 waves; the fp32 state slice
 // lives in the MFMA accumulators of its owner waves for the whole sequence,
 // its bf16 copy S^T [BV][DK] in LDS is the B operand of W S and Qg S; every
 // operand is K-contiguous (one 16-byte LDS read per lane per MFMA); the next
@@ -1366,6 +1367,189 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
 }
 
 // ---------------------------------------------------------------------------
+// scan3: the forward scan without saved states (gdn_forward), over bf16 chunk
+// tables.  8 waves, one (b, h, 32-wide Dv slice) per workgroup.  The fp32
+// state slice lives in the MFMA accumulators of its owner waves for the whole
+// sequence, computed transposed (rows along Dv): a lane's four accumulator
+// values are four consecutive Dv columns of one row of S (or of o); the bf16
+// copies S^T [BV][DK] and D^T [BV][C] in LDS are the K-contiguous A operands
+// of the products.  Everything a chunk reads (P, W, Qg, Kh^T: the B operands;
+// the U slice; the decay) goes straight from global memory into one of two
+// LDS buffers (swizzled rows, one chunk ahead) by direct loads waited for
+// explicitly: the loop holds no register loads, so the compiler places no
+// waits of its own, and the only vector memory operations after a chunk's
+// loads are the step's output stores, counted exactly.  (The state-saving
+// scans keep scan2: their extra stores, issued after a register prefetch two
+// chunks ahead, measured faster there.)
+// ---------------------------------------------------------------------------
+template <int C, int DK, int DV>
+__global__ void __launch_bounds__(NTHR_S)
+scan3_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
+             const bf16* __restrict__ KhTb, const bf16* __restrict__ Psb,
+             const float* __restrict__ Ui, const float* __restrict__ gami,
+             const float* __restrict__ h0, bf16* __restrict__ o, float* __restrict__ hT,
+             int BH, int T, int H, int NC)
+{
+    constexpr int BV = 32, NS = DV / BV, NW = NTHR_S / 64;
+    constexpr int PA = DK + 8, PT = C + 8;  // bf16 pitches: rows 16-byte aligned, banks spread
+    constexpr int TD = (C / 16) * (BV / 16), TS = (DK / 16) * (BV / 16);
+    constexpr int MD = TD / NW, MS = TS / NW;
+    static_assert(TD % NW == 0 && TS % NW == 0, "every wave owns whole tiles");
+    // a buffer as 16-byte words: the four tables (row widths WC, WK), then the
+    // U slice [C][BV] fp32 (BV / 4 words a row) and the decay (DK / 4 words,
+    // loaded by wave 0: a whole wave of words, the upper ones repeats)
+    constexpr int WC = C / 8, WK = DK / 8, WU = BV / 4;
+    constexpr int OP = 0, OW = OP + C * WC, OQ = OW + C * WK, OK = OQ + C * WK, QT = OK + DK * WC;
+    constexpr int OU = QT, OG = OU + C * WU, QB = OG + 64;
+    constexpr int NQ = QT / NTHR_S;
+    static_assert(OW % NTHR_S == 0 && OQ % NTHR_S == 0 && OK % NTHR_S == 0 && QT % NTHR_S == 0,
+                  "every load instruction lies in one table");
+    static_assert(C * WU == NTHR_S && WU == 8 && DK / 4 <= 64, "one U word per thread, decay in one wave");
+    // two buffers, separate arrays: the compiler then sees that reads of one
+    // cannot alias the direct loads into the other and does not wait for them
+    __shared__ __align__(16) uint4 sTab0[QB], sTab1[QB];
+    __shared__ __align__(16) bf16 sSt[BV][PA], sDt[BV][PT];
+    // 2-byte views for the transposed writes: one index expression per write
+    // keeps each address a single step from its array (the alias information
+    // that spares those writes a wait for the direct loads is kept)
+    uint16_t* const St16 = &sSt[0][0].bits;
+    uint16_t* const Dt16 = &sDt[0][0].bits;
+
+    const int x = blockIdx.x;
+    const int grp = x / (8 * NS), rem = x % (8 * NS);
+    const int sl = rem / 8, bh = grp * 8 + rem % 8;
+    if (bh >= BH) return;
+    const int b = bh / H, h = bh % H;
+    const int v0 = sl * BV;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+
+    // state tile m of this wave: sacc[m][r] = S[si*16 + lr][v0 + sj*16 + 4 lq + r]
+    f32x4 sacc[MS];
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        const int idx = w + NW * m;
+        const int si = idx / (BV / 16), sj = idx % (BV / 16);
+        sacc[m] = zero4();
+        if (h0)
+            sacc[m] = *reinterpret_cast<const f32x4*>(
+                h0 + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) St16[(sj * 16 + 4 * lq + r) * PA + si * 16 + lr] = f32_to_bf16(sacc[m][r]).bits;
+    }
+
+    // slot tid + NTHR_S q of a buffer takes table word (row, w ^ (row & 7)),
+    // (row, w) being the slot's place in its table; the U slice likewise
+    int goff[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int g0 = q * NTHR_S;
+        const int wpr = (g0 >= OW && g0 < OK) ? WK : WC;
+        const int s = g0 + tid - (g0 < OW ? OP : g0 < OQ ? OW : g0 < OK ? OQ : OK);
+        const int row = s / wpr, wd = s % wpr;
+        goff[q] = (row * wpr + (wd ^ (row & 7))) * 8;
+    }
+    const int urow = tid / WU, uoff = urow * DV + v0 + 4 * ((tid % WU) ^ (urow & 7));
+    auto fetch = [&](int n, uint4* buf) {
+        const size_t ch = (size_t)bh * NC + n;
+        if (w == 0) dma16(gami + ch * DK + 4 * (l % (DK / 4)), buf + OG);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int g0 = q * NTHR_S;
+            const bf16* src = g0 < OW ? Psb + ch * C * C
+                            : g0 < OQ ? Wb + ch * C * DK
+                            : g0 < OK ? Qgb + ch * C * DK
+                                      : KhTb + ch * C * DK;
+            dma16(src + goff[q], buf + g0 + 64 * w);
+        }
+        dma16(Ui + ch * C * DV + uoff, buf + OU + 64 * w);
+    };
+    // vector memory operations issued after a chunk's loads and before the
+    // wait for them: the step's output stores (the last step, whose stores may
+    // be skipped past T, does not wait)
+    constexpr int AFTER = MD;
+    static_assert(AFTER < 16, "vmcnt field");
+
+    // chunk n sits in buffer n & 1: the steps of a pair of chunks use fixed buffers
+    fetch(0, sTab0);
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    // LAST: the sequence's last chunk (a harmless reload of it into the idle
+    // buffer, output rows past T skipped, no wait)
+    auto step = [&](int n, const uint4* tb, uint4* tnx, auto last_c) {
+        constexpr bool LAST = decltype(last_c)::value;
+        fetch(LAST ? n : n + 1, tnx);
+        // D^T = U^T - S^T W^T and O1^T = S^T Qg^T: acc[r] = D[ti*16 + lr][v0 + tj*16 + 4 lq + r]
+        f32x4 o1[MD];
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            const int idx = w + NW * m;
+            const int ti = idx / (BV / 16), tj = idx % (BV / 16);
+            const f32x4 ws = mma_kc_bsw<DK, WK>(zero4(), &sSt[tj * 16][0], PA, tb + OW, ti * 16);
+            const f32x4 u4 = *reinterpret_cast<const f32x4*>(tb + OU + (ti * 16 + lr) * WU + ((tj * 4 + lq) ^ (lr & 7)));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Dt16[(tj * 16 + 4 * lq + r) * PT + ti * 16 + lr] = f32_to_bf16(u4[r] - ws[r]).bits;
+            o1[m] = mma_kc_bsw<DK, WK>(zero4(), &sSt[tj * 16][0], PA, tb + OQ, ti * 16);
+        }
+        __syncthreads();
+        // O^T += D^T P^T (P lower triangular: columns past the tile row are zero)
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            const int idx = w + NW * m;
+            const int ti = idx / (BV / 16), tj = idx % (BV / 16);
+            f32x4 acc;
+            if (16 * (ti + 1) <= 32)
+                acc = mma_kc_bsw<32, WC>(o1[m], &sDt[tj * 16][0], PT, tb + OP, ti * 16);
+            else
+                acc = mma_kc_bsw<C, WC>(o1[m], &sDt[tj * 16][0], PT, tb + OP, ti * 16);
+            const int t = n * C + ti * 16 + lr;
+            if (!LAST || t < T)
+                *reinterpret_cast<uint2*>(o + (((size_t)b * T + t) * H + h) * DV + v0 + tj * 16 + 4 * lq) =
+                    pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+        }
+        // S^T <- S^T o gam + D^T Kh
+        const float* sg = reinterpret_cast<const float*>(tb + OG);
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + NW * m;
+            const int si = idx / (BV / 16), sj = idx % (BV / 16);
+            const float gk = sg[si * 16 + lr];
+            f32x4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = gk * sacc[m][r];
+            sacc[m] = mma_kc_bsw<C, WC>(acc, &sDt[sj * 16][0], PT, tb + OK, si * 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) St16[(sj * 16 + 4 * lq + r) * PA + si * 16 + lr] = f32_to_bf16(sacc[m][r]).bits;
+        }
+        if constexpr (!LAST) {
+            wait_vmcnt<AFTER>();  // chunk n + 1's loads have landed
+            __syncthreads();
+        }
+    };
+    int n = 0;
+    for (; n + 2 < NC; n += 2) {
+        step(n, sTab0, sTab1, std::false_type{});
+        step(n + 1, sTab1, sTab0, std::false_type{});
+    }
+    if (n + 2 == NC) {
+        step(n, sTab0, sTab1, std::false_type{});
+        step(n + 1, sTab1, sTab0, std::true_type{});
+    } else {
+        step(n, sTab0, sTab1, std::true_type{});
+    }
+    wait_vmcnt<0>();  // the last step's reload into the idle buffer
+    if (hT) {
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = w + NW * m;
+            const int si = idx / (BV / 16), sj = idx % (BV / 16);
+            *reinterpret_cast<f32x4*>(hT + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq) = sacc[m];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
 template <typename TIn, int C, int DK, int DV, int MT>
@@ -1434,13 +1618,21 @@ gdn_status run_scan(const Plan& p, const float* h0, void* o, float* hT, char* ws
     if constexpr (bf16_tables<TIn, C, DK>()) {
         const size_t n = p.n_ch;
         dim3 grid((unsigned)(ngrp * 8 * (DV / 32))), block(NTHR_S);
-        GDN_LAUNCH(SAVE ? (OUT ? "scan_train" : "scan_save") : "scan",
-                   (scan2_kernel<C, DK, DV, SAVE, OUT>), grid, block, st,
-                   (const bf16*)(ws + p.o_W), (const bf16*)(ws + p.o_Qg),
-                   (const bf16*)(ws + p.o_Kh), (const bf16*)(ws + p.o_Ps),
-                   (const float*)(ws + p.o_U), (const float*)(ws + p.o_gam), h0, (bf16*)o, hT,
-                   SAVE ? (float*)(ws + p.o_Sst) : nullptr, SAVE ? (bf16*)(ws + p.o_Dst) : nullptr,
-                   BH, p.T, p.H, p.NC);
+        if constexpr (!SAVE) {
+            GDN_LAUNCH("scan", (scan3_kernel<C, DK, DV>), grid, block, st,
+                       (const bf16*)(ws + p.o_W), (const bf16*)(ws + p.o_Qg),
+                       (const bf16*)(ws + p.o_Kh), (const bf16*)(ws + p.o_Ps),
+                       (const float*)(ws + p.o_U), (const float*)(ws + p.o_gam), h0, (bf16*)o, hT,
+                       BH, p.T, p.H, p.NC);
+        } else {
+            GDN_LAUNCH(SAVE ? (OUT ? "scan_train" : "scan_save") : "scan",
+                       (scan2_kernel<C, DK, DV, SAVE, OUT>), grid, block, st,
+                       (const bf16*)(ws + p.o_W), (const bf16*)(ws + p.o_Qg),
+                       (const bf16*)(ws + p.o_Kh), (const bf16*)(ws + p.o_Ps),
+                       (const float*)(ws + p.o_U), (const float*)(ws + p.o_gam), h0, (bf16*)o, hT,
+                       SAVE ? (float*)(ws + p.o_Sst) : nullptr, SAVE ? (bf16*)(ws + p.o_Dst) : nullptr,
+                       BH, p.T, p.H, p.NC);
+        }
         (void)n;
         return GDN_OK;
     }

@@ -71,6 +71,20 @@ def test_ragged_lengths(chunk, T):
     assert rel_err(host(hT), h_ref) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 200, 256])
+def test_ragged_lengths_bf16(T):
+    """bf16 tables at chunk 64: one, two, three and four chunks (odd and even
+    counts), ragged and whole last chunks, from a random start state."""
+    D = 128
+    log(f"ragged bf16 T={T} D={D}")
+    inp = gi.make_inputs(2, T, 3, D, D, decay="channel", dtype="bf16", seed=100 + T, h0_std=0.1)
+    o, hT = gpu_forward(inp)
+    o_ref, h_ref = oracle.forward_inputs(inp)
+    eo, eh = rel_err(host(o), o_ref), rel_err(host(hT), h_ref)
+    log(f"  o {eo:.3e} hT {eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("decay", ["channel", "head"])
 @pytest.mark.parametrize("D", [64, 128])
