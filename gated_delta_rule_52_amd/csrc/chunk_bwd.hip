@@ -543,7 +543,7 @@ __global__ void __launch_bounds__(NTHR_C)
 bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const bf16* __restrict__ dO, const bf16* __restrict__ Dst,
                 const float* __restrict__ Ui, const float* __restrict__ Tmi,
-                const bf16* __restrict__ Wbi, const float* __restrict__ Sst,
+                const bf16* __restrict__ Wbi, const bf16* __restrict__ Sst,
                 const float* __restrict__ dSt, const float* __restrict__ dDt,
                 bf16* __restrict__ dvo, float* __restrict__ dQgo, float* __restrict__ dWgo,
                 float* __restrict__ dKho, float* __restrict__ dPso, float* __restrict__ dT1o,
@@ -594,7 +594,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     const int lr = l & 15, lq = l >> 4;
     const size_t tok0 = ((size_t)b * T + t0) * H + h;
 
-    const float* Sp = Sst + (size_t)ch * DK * DV;
+    const bf16* Sp = Sst + (size_t)ch * DK * DV;  // bf16 chunk-start states
     const float* dSp = dSt + (size_t)ch * DK * DV;
     const float* dDp = dDt + (size_t)ch * C * DV;
     const bf16* Dp = Dst + (size_t)ch * C * DV;
@@ -605,7 +605,8 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // S words, two dS words, one dD and one U word, one D-or-dO word and one v
     // word; rows past the end are clamped on load and zeroed in stash().
     static_assert(NS4 == QS * NTHR_C && ND4 == NTHR_C && NB8 == NTHR_C / 2, "tile split");
-    float4 pS[QS], pdS[QS], pdD, pU;
+    uint2 pS[QS];  // four bf16 state values
+    float4 pdS[QS], pdD, pU;
     uint4 pa, pb;  // threads < NB8: D and v words; threads >= NB8: dO word (and an unused v word)
     const bool lowh = tid < NB8;
     const int e8 = lowh ? tid : tid - NB8;
@@ -618,7 +619,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         for (int q = 0; q < QS; ++q) {
             const int idx = tid + NTHR_C * q;
             const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
-            pS[q] = load4<float>(Sp + i * DV + v0 + j4);
+            pS[q] = *reinterpret_cast<const uint2*>(Sp + i * DV + v0 + j4);
             pdS[q] = load4<float>(dSp + i * DV + v0 + j4);
         }
         pdD = load4<float>(dDp + rd * DV + v0 + jd);
@@ -638,9 +639,12 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         for (int q = 0; q < QS; ++q) {
             const int idx = tid + NTHR_C * q;
             const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
-            const float4 a4 = pS[q], d4 = pdS[q];
-            dgm_part[q] += a4.x * d4.x + a4.y * d4.y + a4.z * d4.z + a4.w * d4.w;
-            *reinterpret_cast<uint2*>(&sS[i][j4]) = pack4_bf16(a4.x, a4.y, a4.z, a4.w);
+            const uint2 s2 = pS[q];
+            const float4 d4 = pdS[q];
+            const float ax = __uint_as_float(s2.x << 16), ay = __uint_as_float(s2.x & 0xFFFF0000u);
+            const float az = __uint_as_float(s2.y << 16), aw = __uint_as_float(s2.y & 0xFFFF0000u);
+            dgm_part[q] += ax * d4.x + ay * d4.y + az * d4.z + aw * d4.w;
+            *reinterpret_cast<uint2*>(&sS[i][j4]) = s2;
             *reinterpret_cast<uint2*>(&sdS[i][j4]) = pack4_bf16(d4.x, d4.y, d4.z, d4.w);
         }
         st4(&sdDf[rd][jd], pdD);
@@ -2055,7 +2059,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                    beta, (const bf16*)dO, (const bf16*)(ws + p.o_Dst),
                    (const float*)(ws + (raw ? p.o_Ur : p.o_U)), (const float*)(ws + p.o_Tm),
                    (const bf16*)(ws + (raw ? p.o_Wr : p.o_W)),
-                   (const float*)(ws + p.o_Sst), (const float*)(ws + p.o_dSt),
+                   (const bf16*)(ws + p.o_Sst), (const float*)(ws + p.o_dSt),
                    (const float*)(ws + p.o_dDt), (bf16*)dv, (float*)(ws + p.o_dQg),
                    (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh), (float*)(ws + p.o_dPs),
                    (float*)(ws + p.o_dT1), (float*)(ws + p.o_dgm), (float*)(ws + p.o_dbp), p.T, p.H,

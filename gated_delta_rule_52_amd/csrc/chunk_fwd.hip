@@ -1127,7 +1127,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
              const bf16* __restrict__ KhTb, const bf16* __restrict__ Psb,
              const float* __restrict__ Ui, const float* __restrict__ gami,
              const float* __restrict__ h0, bf16* __restrict__ o, float* __restrict__ hT,
-             float* __restrict__ Sst, bf16* __restrict__ Dst, int BH, int T, int H, int NC)
+             bf16* __restrict__ Sst, bf16* __restrict__ Dst, int BH, int T, int H, int NC)
 {
     constexpr int BV = 32, NS = DV / BV, NW = NTHR_S / 64;
     constexpr int PA = DK + 8, PT = C + 8;  // bf16 pitches: rows 16-byte aligned, banks spread
@@ -1143,9 +1143,10 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
     static_assert(TD % NW == 0 && TS % NW == 0, "tile split");
     __shared__ __align__(16) bf16 sW[C][PA], sQ[C][PA], sKT[DK][PT], sP[C][PT], sSt[BV][PA], sDt[BV][PT];
     // staging of each step's outputs (double-buffered by step parity), written
-    // out with 16-byte stores: the next chunk's start state (fp32), D and o (bf16)
-    constexpr int PF = BV + 4, PO = BV + 8;
-    __shared__ __align__(16) float sSf[2][DK][PF];
+    // out with 16-byte stores: the next chunk's start state, D and o (bf16; the
+    // saved states feed the backward's bf16 products and its decay-gradient sums)
+    constexpr int PO = BV + 8;
+    __shared__ __align__(16) bf16 sSf[2][DK][PO];
     __shared__ __align__(16) bf16 sDr[2][C][PO], sOr[2][C][PO];
 
     const int x = blockIdx.x;
@@ -1257,7 +1258,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             const int si = idx / (BV / 16), sj = idx % (BV / 16);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Sst[((size_t)bh * NC * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = sacc[m][r];
+                Sst[((size_t)bh * NC * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = f32_to_bf16(sacc[m][r]);
         }
     }
     // one step: chunk n with its tables in LDS; `nx` holds chunk n + 1 (stashed
@@ -1309,7 +1310,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 pack4_bf16(sacc[m][0], sacc[m][1], sacc[m][2], sacc[m][3]);
             if (SAVE) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sSf[pb][si * 16 + 4 * lq + r][sj * 16 + lr] = sacc[m][r];
+                for (int r = 0; r < 4; ++r) sSf[pb][si * 16 + 4 * lq + r][sj * 16 + lr] = f32_to_bf16(sacc[m][r]);
             }
         }
         __syncthreads();
@@ -1318,14 +1319,14 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         // this step's stores, from the staging: the start state of chunk n + 1,
         // then D and o of chunk n (rows of BV contiguous elements)
         if (SAVE && n + 1 < NC) {
-            constexpr int NF4 = DK * BV / 4;
+            constexpr int NF8 = DK * BV / 8;  // 16-byte words of the bf16 state slice
 #pragma unroll
-            for (int u = 0; u < (NF4 + NTHR_S - 1) / NTHR_S; ++u) {
+            for (int u = 0; u < (NF8 + NTHR_S - 1) / NTHR_S; ++u) {
                 const int e = tid + NTHR_S * u;
-                if (e < NF4) {
-                    const int i = e / (BV / 4), j4 = (e % (BV / 4)) * 4;
-                    *reinterpret_cast<float4*>(&Sst[((ch + 1) * DK + i) * DV + v0 + j4]) =
-                        *reinterpret_cast<const float4*>(&sSf[pb][i][j4]);
+                if (e < NF8) {
+                    const int i = e / (BV / 8), j8 = (e % (BV / 8)) * 8;
+                    *reinterpret_cast<uint4*>(&Sst[((ch + 1) * DK + i) * DV + v0 + j8]) =
+                        *reinterpret_cast<const uint4*>(&sSf[pb][i][j8]);
                 }
             }
         }
@@ -1630,7 +1631,7 @@ gdn_status run_scan(const Plan& p, const float* h0, void* o, float* hT, char* ws
                        (const bf16*)(ws + p.o_W), (const bf16*)(ws + p.o_Qg),
                        (const bf16*)(ws + p.o_Kh), (const bf16*)(ws + p.o_Ps),
                        (const float*)(ws + p.o_U), (const float*)(ws + p.o_gam), h0, (bf16*)o, hT,
-                       SAVE ? (float*)(ws + p.o_Sst) : nullptr, SAVE ? (bf16*)(ws + p.o_Dst) : nullptr,
+                       SAVE ? (bf16*)(ws + p.o_Sst) : nullptr, SAVE ? (bf16*)(ws + p.o_Dst) : nullptr,
                        BH, p.T, p.H, p.NC);
         }
         (void)n;

@@ -71,7 +71,7 @@ def make_inputs(B: int, T: int, H: int, Dk: int, Dv: int, *, decay: str = "chann
                 dtype: str = "f32", seed: int = 0, h0_std: float | None = None,
                 wipe_period: int | None = None, wipe_value: float = -20.0,
                 grads: bool = False, dO_std: float = 1.0, dhT_std: float = 0.01,
-                qk_scale: float | None = None) -> dict:
+                qk_scale: float | None = None, g_scale: float = 1.0) -> dict:
     """Draw one workload.  Returns a dict of numpy arrays in device form
     (float32, or uint16 bf16 bits for q/k/v/dO when dtype == 'bf16') plus the
     shape metadata under 'meta'."""
@@ -84,7 +84,7 @@ def make_inputs(B: int, T: int, H: int, Dk: int, Dv: int, *, decay: str = "chann
     v = rng.standard_normal((B, T, H, Dv))
     beta = _sigmoid(rng.standard_normal((B, T, H)))
     gshape = (B, T, H, Dk) if decay == "channel" else (B, T, H)
-    g = -_softplus(rng.standard_normal(gshape))
+    g = -_softplus(rng.standard_normal(gshape)) * g_scale  # g_scale < 1: weaker decay
     if wipe_period:
         g[:, wipe_period - 1::wipe_period] = wipe_value
     out = {}

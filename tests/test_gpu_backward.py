@@ -7,7 +7,7 @@ import torch
 import gdn_inputs as gi
 import oracle
 from gpu_util import TOL, host, log, rel_err, to_dev_inputs
-from test_gpu_forward import sub_heads
+from test_gpu_forward import gpu_forward, sub_heads
 
 pytestmark = pytest.mark.gpu
 
@@ -62,6 +62,27 @@ def test_medium_gradients(dtype, decay, D):
     got = gpu_backward(inp)
     ref = oracle.backward_inputs(inp)
     compare(got, ref, TOL[dtype], f"medium {dtype} {decay} D={D}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("decay", ["channel", "head"])
+def test_weak_decay_gradients(dtype, decay):
+    """Decay a hundred times weaker than the default draw (a chunk keeps about
+    e^-0.5 of its start state instead of e^-50), so the state carried across
+    chunks, the saved chunk-start states and the whole-chunk decay gradient
+    weigh in every output and gradient."""
+    log(f"weak decay {dtype} {decay}")
+    inp = gi.make_inputs(2, 512, 3, 128, 128, decay=decay, dtype=dtype, seed=23, h0_std=0.1,
+                         grads=True, g_scale=0.01)
+    inp["meta"]["chunk"] = 64
+    o, hT = gpu_forward(inp)
+    o_ref, h_ref = oracle.forward_inputs(inp)
+    eo, eh = rel_err(host(o), o_ref), rel_err(host(hT), h_ref)
+    log(f"  forward: o {eo:.2e}  hT {eh:.2e}")
+    assert eo <= TOL[dtype] and eh <= TOL[dtype]
+    got = gpu_backward(inp)
+    ref = oracle.backward_inputs(inp)
+    compare(got, ref, TOL[dtype], f"weak decay {dtype} {decay}")
 
 
 def test_no_h0_no_dhT():
