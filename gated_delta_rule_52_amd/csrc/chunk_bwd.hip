@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(NTHR_B)
 bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
               const bf16* __restrict__ QgTb, const bf16* __restrict__ WTb,
               const float* __restrict__ gami, const bf16* __restrict__ dO,
-              const float* __restrict__ dhT, float* __restrict__ dSt, float* __restrict__ dDt,
+              const float* __restrict__ dhT, bf16* __restrict__ dSt, float* __restrict__ dDt,
               float* __restrict__ dh0, int BH, int T, int H, int NC)
 {
     constexpr int BV = 32, NS = DV / BV, NW = NTHR_B / 64;
@@ -304,7 +304,10 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
         for (int m = 0; m < MS; ++m) {
             const int idx = w + NW * m;
             const int si = idx / (BV / 16), sj = idx % (BV / 16);
-            *reinterpret_cast<f32x4*>(dSt + (ch * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq) = dacc[m];
+            // bf16: the backward's products read it as bf16, the decay-gradient
+            // sum accumulates in fp32
+            *reinterpret_cast<uint2*>(dSt + (ch * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq) =
+                pack4_bf16(dacc[m][0], dacc[m][1], dacc[m][2], dacc[m][3]);
         }
         // dD^T = scale dO^T P + dS'^T Kh^T: acc[r] = dD[ti*16 + lr][v0 + tj*16 + 4 lq + r]
 #pragma unroll
@@ -544,7 +547,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const bf16* __restrict__ dO, const bf16* __restrict__ Dst,
                 const float* __restrict__ Ui, const float* __restrict__ Tmi,
                 const bf16* __restrict__ Wbi, const bf16* __restrict__ Sst,
-                const float* __restrict__ dSt, const float* __restrict__ dDt,
+                const bf16* __restrict__ dSt, const float* __restrict__ dDt,
                 bf16* __restrict__ dvo, float* __restrict__ dQgo, float* __restrict__ dWgo,
                 float* __restrict__ dKho, float* __restrict__ dPso, float* __restrict__ dT1o,
                 float* __restrict__ dgmo, float* __restrict__ dbpo, int T, int H, int NC)
@@ -594,8 +597,8 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     const int lr = l & 15, lq = l >> 4;
     const size_t tok0 = ((size_t)b * T + t0) * H + h;
 
-    const bf16* Sp = Sst + (size_t)ch * DK * DV;  // bf16 chunk-start states
-    const float* dSp = dSt + (size_t)ch * DK * DV;
+    const bf16* Sp = Sst + (size_t)ch * DK * DV;    // bf16 chunk-start states
+    const bf16* dSp = dSt + (size_t)ch * DK * DV;   // bf16 chunk-end state gradients
     const float* dDp = dDt + (size_t)ch * C * DV;
     const bf16* Dp = Dst + (size_t)ch * C * DV;
     const float* Up = Ui + (size_t)ch * C * DV;
@@ -605,8 +608,8 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // S words, two dS words, one dD and one U word, one D-or-dO word and one v
     // word; rows past the end are clamped on load and zeroed in stash().
     static_assert(NS4 == QS * NTHR_C && ND4 == NTHR_C && NB8 == NTHR_C / 2, "tile split");
-    uint2 pS[QS];  // four bf16 state values
-    float4 pdS[QS], pdD, pU;
+    uint2 pS[QS], pdS[QS];  // four bf16 values each
+    float4 pdD, pU;
     uint4 pa, pb;  // threads < NB8: D and v words; threads >= NB8: dO word (and an unused v word)
     const bool lowh = tid < NB8;
     const int e8 = lowh ? tid : tid - NB8;
@@ -620,7 +623,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             const int idx = tid + NTHR_C * q;
             const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
             pS[q] = *reinterpret_cast<const uint2*>(Sp + i * DV + v0 + j4);
-            pdS[q] = load4<float>(dSp + i * DV + v0 + j4);
+            pdS[q] = *reinterpret_cast<const uint2*>(dSp + i * DV + v0 + j4);
         }
         pdD = load4<float>(dDp + rd * DV + v0 + jd);
         pU = load4<float>(Up + rd * DV + v0 + jd);
@@ -639,13 +642,14 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         for (int q = 0; q < QS; ++q) {
             const int idx = tid + NTHR_C * q;
             const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
-            const uint2 s2 = pS[q];
-            const float4 d4 = pdS[q];
+            const uint2 s2 = pS[q], d2 = pdS[q];
             const float ax = __uint_as_float(s2.x << 16), ay = __uint_as_float(s2.x & 0xFFFF0000u);
             const float az = __uint_as_float(s2.y << 16), aw = __uint_as_float(s2.y & 0xFFFF0000u);
-            dgm_part[q] += ax * d4.x + ay * d4.y + az * d4.z + aw * d4.w;
+            const float dx = __uint_as_float(d2.x << 16), dy = __uint_as_float(d2.x & 0xFFFF0000u);
+            const float dz = __uint_as_float(d2.y << 16), dw = __uint_as_float(d2.y & 0xFFFF0000u);
+            dgm_part[q] += ax * dx + ay * dy + az * dz + aw * dw;
             *reinterpret_cast<uint2*>(&sS[i][j4]) = s2;
-            *reinterpret_cast<uint2*>(&sdS[i][j4]) = pack4_bf16(d4.x, d4.y, d4.z, d4.w);
+            *reinterpret_cast<uint2*>(&sdS[i][j4]) = d2;
         }
         st4(&sdDf[rd][jd], pdD);
         *reinterpret_cast<uint2*>(&sdD[rd][jd]) = pack4_bf16(pdD.x, pdD.y, pdD.z, pdD.w);
@@ -2038,7 +2042,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
         GDN_LAUNCH("bscan", (bscan2_kernel<C, DK, DV>), grid, block, st,
                    (const bf16*)(ws + p.o_Ps) + n * C * C, (const bf16*)(ws + p.o_Kh) + n * C * DK,
                    (const bf16*)(ws + p.o_Qg) + n * C * DK, (const bf16*)(ws + p.o_W) + n * C * DK,
-                   (const float*)(ws + p.o_gam), (const bf16*)dO, dhT, (float*)(ws + p.o_dSt),
+                   (const float*)(ws + p.o_gam), (const bf16*)dO, dhT, (bf16*)(ws + p.o_dSt),
                    (float*)(ws + p.o_dDt), dh0, BH, p.T, p.H, p.NC);
     } else {
         using SC = BScanCfg<DV>;
@@ -2059,7 +2063,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                    beta, (const bf16*)dO, (const bf16*)(ws + p.o_Dst),
                    (const float*)(ws + (raw ? p.o_Ur : p.o_U)), (const float*)(ws + p.o_Tm),
                    (const bf16*)(ws + (raw ? p.o_Wr : p.o_W)),
-                   (const bf16*)(ws + p.o_Sst), (const float*)(ws + p.o_dSt),
+                   (const bf16*)(ws + p.o_Sst), (const bf16*)(ws + p.o_dSt),
                    (const float*)(ws + p.o_dDt), (bf16*)dv, (float*)(ws + p.o_dQg),
                    (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh), (float*)(ws + p.o_dPs),
                    (float*)(ws + p.o_dT1), (float*)(ws + p.o_dgm), (float*)(ws + p.o_dbp), p.T, p.H,
