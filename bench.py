@@ -124,11 +124,11 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True, l2n=False)
             fl[mt] += 6 * C * DK * DV + 2 * tri * DV
     elif name == "bscan":
         by = cc * tb + 3 * cd * tb + DK * f4 + cv * ib             # Ps^T Kh Qg^T W^T, gam, dO
-        by += kv * tb + cv * f4                                    # dS (chunk ends), dD
+        by += kv * tb + cv * tb                                    # dS (chunk ends), dD
         fl[mt] += 6 * C * DK * DV + 2 * tri * DV
     elif name == "bchunk1":
         it = 2 if bt else 4
-        by = 2 * cv * ib + C * f4 + cc * f4 + 2 * kv * tb + cv * f4   # v dO, beta, T, S, dS, dD
+        by = 2 * cv * ib + C * f4 + cc * f4 + 2 * kv * tb + cv * tb   # v dO, beta, T, S, dS, dD
         by += (cv * 2 + cv * f4 + cd * tb) if bt else (cd + cv) * f4  # D, U, W | W, U (D = U - W S)
         by += cv * ib + 3 * cd * it + 2 * cc * it + DK * f4 + C * f4  # dv, dQg dX_K|dW dKh, dPs dA|dT1, dgam, dbeta
         fl[mt] += 6 * C * DK * DV + 2 * tri * DV + 2 * C * C * DV     # dQg dW dKh, dPs, dX_V U^T | dD X_V^T

@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(NTHR_B)
 bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
               const bf16* __restrict__ QgTb, const bf16* __restrict__ WTb,
               const float* __restrict__ gami, const bf16* __restrict__ dO,
-              const float* __restrict__ dhT, bf16* __restrict__ dSt, float* __restrict__ dDt,
+              const float* __restrict__ dhT, bf16* __restrict__ dSt, bf16* __restrict__ dDt,
               float* __restrict__ dh0, int BH, int T, int H, int NC)
 {
     constexpr int BV = 32, NS = DV / BV, NW = NTHR_B / 64;
@@ -316,7 +316,8 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
             const int ti = idx / (BV / 16), tj = idx % (BV / 16);
             f32x4 acc = mma_kc_bsw<C, WC>(zero4(), &sdOt[tj * 16][0], PT, tb + OP, ti * 16);
             acc = mma_kc_bsw<DK, WK>(acc, &sdSt[tj * 16][0], PA, tb + OK, ti * 16);
-            *reinterpret_cast<f32x4*>(dDt + (ch * C + ti * 16 + lr) * DV + v0 + tj * 16 + 4 * lq) = acc;
+            *reinterpret_cast<uint2*>(dDt + (ch * C + ti * 16 + lr) * DV + v0 + tj * 16 + 4 * lq) =
+                pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) dDt16[(tj * 16 + 4 * lq + r) * PT + ti * 16 + lr] = f32_to_bf16(acc[r]).bits;
         }
@@ -547,7 +548,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const bf16* __restrict__ dO, const bf16* __restrict__ Dst,
                 const float* __restrict__ Ui, const float* __restrict__ Tmi,
                 const bf16* __restrict__ Wbi, const bf16* __restrict__ Sst,
-                const bf16* __restrict__ dSt, const float* __restrict__ dDt,
+                const bf16* __restrict__ dSt, const bf16* __restrict__ dDt,
                 bf16* __restrict__ dvo, float* __restrict__ dQgo, float* __restrict__ dWgo,
                 float* __restrict__ dKho, float* __restrict__ dPso, float* __restrict__ dT1o,
                 float* __restrict__ dgmo, float* __restrict__ dbpo, int T, int H, int NC)
@@ -599,7 +600,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 
     const bf16* Sp = Sst + (size_t)ch * DK * DV;    // bf16 chunk-start states
     const bf16* dSp = dSt + (size_t)ch * DK * DV;   // bf16 chunk-end state gradients
-    const float* dDp = dDt + (size_t)ch * C * DV;
+    const bf16* dDp = dDt + (size_t)ch * C * DV;    // bf16 delta gradients
     const bf16* Dp = Dst + (size_t)ch * C * DV;
     const float* Up = Ui + (size_t)ch * C * DV;
 
@@ -608,8 +609,8 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // S words, two dS words, one dD and one U word, one D-or-dO word and one v
     // word; rows past the end are clamped on load and zeroed in stash().
     static_assert(NS4 == QS * NTHR_C && ND4 == NTHR_C && NB8 == NTHR_C / 2, "tile split");
-    uint2 pS[QS], pdS[QS];  // four bf16 values each
-    float4 pdD, pU;
+    uint2 pS[QS], pdS[QS], pdD;  // four bf16 values each
+    float4 pU;
     uint4 pa, pb;  // threads < NB8: D and v words; threads >= NB8: dO word (and an unused v word)
     const bool lowh = tid < NB8;
     const int e8 = lowh ? tid : tid - NB8;
@@ -625,7 +626,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             pS[q] = *reinterpret_cast<const uint2*>(Sp + i * DV + v0 + j4);
             pdS[q] = *reinterpret_cast<const uint2*>(dSp + i * DV + v0 + j4);
         }
-        pdD = load4<float>(dDp + rd * DV + v0 + jd);
+        pdD = *reinterpret_cast<const uint2*>(dDp + rd * DV + v0 + jd);
         pU = load4<float>(Up + rd * DV + v0 + jd);
         const bf16* src = lowh ? Dp + r8 * DV + v0 + j8 : dO + tokr + v0 + j8;
         pa = *reinterpret_cast<const uint4*>(src);
@@ -651,8 +652,9 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             *reinterpret_cast<uint2*>(&sS[i][j4]) = s2;
             *reinterpret_cast<uint2*>(&sdS[i][j4]) = d2;
         }
-        st4(&sdDf[rd][jd], pdD);
-        *reinterpret_cast<uint2*>(&sdD[rd][jd]) = pack4_bf16(pdD.x, pdD.y, pdD.z, pdD.w);
+        st4(&sdDf[rd][jd], float4{__uint_as_float(pdD.x << 16), __uint_as_float(pdD.x & 0xFFFF0000u),
+                                  __uint_as_float(pdD.y << 16), __uint_as_float(pdD.y & 0xFFFF0000u)});
+        *reinterpret_cast<uint2*>(&sdD[rd][jd]) = pdD;
         *reinterpret_cast<uint2*>(&sU[rd][jd]) = pack4_bf16(pU.x, pU.y, pU.z, pU.w);
         if (lowh) {
             *reinterpret_cast<uint4*>(&sD[r8][j8]) = pa;
@@ -2043,7 +2045,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                    (const bf16*)(ws + p.o_Ps) + n * C * C, (const bf16*)(ws + p.o_Kh) + n * C * DK,
                    (const bf16*)(ws + p.o_Qg) + n * C * DK, (const bf16*)(ws + p.o_W) + n * C * DK,
                    (const float*)(ws + p.o_gam), (const bf16*)dO, dhT, (bf16*)(ws + p.o_dSt),
-                   (float*)(ws + p.o_dDt), dh0, BH, p.T, p.H, p.NC);
+                   (bf16*)(ws + p.o_dDt), dh0, BH, p.T, p.H, p.NC);
     } else {
         using SC = BScanCfg<DV>;
         dim3 grid((unsigned)(((BH + 7) / 8) * 8 * SC::NS)), block(NTHR);
@@ -2064,7 +2066,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                    (const float*)(ws + (raw ? p.o_Ur : p.o_U)), (const float*)(ws + p.o_Tm),
                    (const bf16*)(ws + (raw ? p.o_Wr : p.o_W)),
                    (const bf16*)(ws + p.o_Sst), (const bf16*)(ws + p.o_dSt),
-                   (const float*)(ws + p.o_dDt), (bf16*)dv, (float*)(ws + p.o_dQg),
+                   (const bf16*)(ws + p.o_dDt), (bf16*)dv, (float*)(ws + p.o_dQg),
                    (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh), (float*)(ws + p.o_dPs),
                    (float*)(ws + p.o_dT1), (float*)(ws + p.o_dgm), (float*)(ws + p.o_dbp), p.T, p.H,
                    p.NC);
