@@ -206,6 +206,14 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
     uint16_t* const dDt16 = &sdDt[0][0].bits;
     uint16_t* const dOt16 = &sdOt[0][0].bits;
     __shared__ __align__(16) float sgam[DK];  // the chunk's whole-chunk decay
+    // staging of the saved rows (bf16): dS at the chunk's end, written out at
+    // the start of the step, and dD, written out after the mid-step barrier;
+    // whole 64-byte row slices per store, all stores unconditional
+    constexpr int PR = BV + 8;
+    __shared__ __align__(16) bf16 sSo[DK][PR], sDo[C][PR];
+    constexpr int ES = DK * BV / NTHR_B;  // bf16 of dS per thread: one 16- or 8-byte word
+    static_assert((ES == 8 || ES == 4) && ES * NTHR_B == DK * BV && C * BV == 4 * NTHR_B,
+                  "one dS word and one dD word (4 bf16) per thread");
 
     const int x = blockIdx.x;
     const int grp = x / (8 * NS), rem = x % (8 * NS);
@@ -232,6 +240,8 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
                 dhT + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq);
 #pragma unroll
         for (int r = 0; r < 4; ++r) dSt16[(sj * 16 + 4 * lq + r) * PA + si * 16 + lr] = f32_to_bf16(dacc[m][r]).bits;
+        *reinterpret_cast<uint2*>(&sSo[si * 16 + lr][sj * 16 + 4 * lq]) =
+            pack4_bf16(dacc[m][0], dacc[m][1], dacc[m][2], dacc[m][3]);
     }
 
     // slot tid + NTHR_B q of a buffer takes table word (row, w ^ (row & 7)),
@@ -285,7 +295,7 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
     };
     // vector memory operations issued after a chunk's table loads and before
     // the wait for them: the dO/decay word and the step's dS and dD stores
-    constexpr int AFTER = 1 + MS + MD;
+    constexpr int AFTER = 1 + 1 + 1;
 
     // chunk n sits in buffer (NC - 1 - n) & 1: the steps of a pair of chunks
     // use fixed buffers
@@ -300,14 +310,15 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
         const int nx = max(n - 1, 0);  // at n = 0 a harmless reload into the idle buffer
         fetch_tables(nx, tnx);
         fetch_words(nx);
-#pragma unroll
-        for (int m = 0; m < MS; ++m) {
-            const int idx = w + NW * m;
-            const int si = idx / (BV / 16), sj = idx % (BV / 16);
-            // bf16: the backward's products read it as bf16, the decay-gradient
-            // sum accumulates in fp32
-            *reinterpret_cast<uint2*>(dSt + (ch * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq) =
-                pack4_bf16(dacc[m][0], dacc[m][1], dacc[m][2], dacc[m][3]);
+        {  // dS at the end of chunk n (bf16: the backward's products read it as
+           // bf16, the decay-gradient sum accumulates in fp32), from the staging
+            const int i = tid / (BV / ES), je = (tid % (BV / ES)) * ES;
+            if constexpr (ES == 8)
+                *reinterpret_cast<uint4*>(dSt + (ch * DK + i) * DV + v0 + je) =
+                    *reinterpret_cast<const uint4*>(&sSo[i][je]);
+            else
+                *reinterpret_cast<uint2*>(dSt + (ch * DK + i) * DV + v0 + je) =
+                    *reinterpret_cast<const uint2*>(&sSo[i][je]);
         }
         // dD^T = scale dO^T P + dS'^T Kh^T: acc[r] = dD[ti*16 + lr][v0 + tj*16 + 4 lq + r]
 #pragma unroll
@@ -316,12 +327,15 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
             const int ti = idx / (BV / 16), tj = idx % (BV / 16);
             f32x4 acc = mma_kc_bsw<C, WC>(zero4(), &sdOt[tj * 16][0], PT, tb + OP, ti * 16);
             acc = mma_kc_bsw<DK, WK>(acc, &sdSt[tj * 16][0], PA, tb + OK, ti * 16);
-            *reinterpret_cast<uint2*>(dDt + (ch * C + ti * 16 + lr) * DV + v0 + tj * 16 + 4 * lq) =
-                pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+            *reinterpret_cast<uint2*>(&sDo[ti * 16 + lr][tj * 16 + 4 * lq]) = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) dDt16[(tj * 16 + 4 * lq + r) * PT + ti * 16 + lr] = f32_to_bf16(acc[r]).bits;
         }
         __syncthreads();
+        {  // dD of chunk n, from the staging
+            const int i = tid / (BV / 4), j4 = (tid % (BV / 4)) * 4;
+            *reinterpret_cast<uint2*>(dDt + (ch * C + i) * DV + v0 + j4) = *reinterpret_cast<const uint2*>(&sDo[i][j4]);
+        }
         // dS^T <- dS'^T o gam + dO^T Qg - dD^T W
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
@@ -338,9 +352,16 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
                 dacc[m][r] = acc[r] - wd[r];
                 dSt16[(sj * 16 + 4 * lq + r) * PA + si * 16 + lr] = f32_to_bf16(dacc[m][r]).bits;
             }
+            *reinterpret_cast<uint2*>(&sSo[si * 16 + lr][sj * 16 + 4 * lq]) =
+                pack4_bf16(dacc[m][0], dacc[m][1], dacc[m][2], dacc[m][3]);
         }
         __syncthreads();
         stash_words(nx);
+        // every thread waits for its word here, right after the stash (the
+        // threads that stash nothing too): otherwise the compiler waits for it
+        // where its registers are next written, after the next direct loads,
+        // and that wait also covers those loads
+        asm volatile("" ::"v"(pw.x), "v"(pw.y), "v"(pw.z), "v"(pw.w));
         wait_vmcnt<AFTER>();  // chunk nx's tables have landed
         __syncthreads();
     };
