@@ -12,7 +12,12 @@ heads are checked against the CPU oracle (atomic_ops card, "Reproduce": timings
 are correctness-gated).
 
 Printed: ONE JSON line.  value = tokens/s of the fwd+bwd step (tokens = B*T
-per call, each token carrying all H heads).  Also reported: forward-only
+per call, each token carrying all H heads).  The step is timed as one HIP-graph
+replay of the two library calls (captured once; the library allocates nothing
+and issues no memset on this path), used only when three check replays, each
+after its outputs were overwritten with NaN, reproduce the eager calls bitwise;
+the eager calls' time is reported beside it (and is the headline otherwise,
+or with --no-graph).  Also reported: forward-only
 tokens/s, the decode step (B=256, H=16, 128x128 state) in GB/s, per-kernel
 device times from HIP events recorded around each launch on its stream, the
 roofline of the dominant kernel, and the CPU oracle timed on this host.
@@ -180,6 +185,48 @@ def roofline(name, dur_s, B, T, H, C, D, in_bytes, l2n=False):
     return r
 
 
+def graph_replay(fn, outs, args):
+    """Capture one call of fn (all its launches) in a HIP graph and time
+    --steps replays.  Each of three check replays must reproduce the eager
+    call's outputs bitwise: the outputs are overwritten with NaN before each
+    replay, and an eager call and a synchronization sit between replays."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    want = [x.clone() for x in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    same = True
+    for _ in range(3):
+        for x in outs:
+            x.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        same &= all(torch.equal(x, y) for x, y in zip(outs, want))
+        fn()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    del graph
+    return {"ms_per_step": ms, "replays_equal_eager_bitwise": bool(same)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +243,8 @@ def main():
                     help="skip the numerical-safety options measurement (wy_eps, clip, diag)")
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward-only measurement (profiling runs: one launch name per kernel)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -319,7 +368,7 @@ def main():
 
     # ---- forward only
     ms_fwd = fwd_tps = None
-    fwd_kernels = None
+    fwd_kernels = fwd_graph = None
     if not args.no_fwd:
         for _ in range(3):
             fwd()
@@ -336,6 +385,22 @@ def main():
         ms_fwd = ev0.elapsed_time(ev1) / args.steps
         fwd_tps = B * T / (ms_fwd * 1e-3)
         log(f"[bench] fwd {ms_fwd:.3f} ms ({fwd_tps / 1e6:.2f} M tokens/s)")
+        if not args.no_graph:
+            fwd_graph = graph_replay(fwd, (o, hT), args)
+            fwd_graph["tokens_per_s"] = B * T / (fwd_graph["ms_per_step"] * 1e-3)
+            log(f"[bench] fwd graph replay {fwd_graph['ms_per_step']:.3f} ms "
+                f"({fwd_graph['tokens_per_s'] / 1e6:.2f} M tokens/s), replays equal eager: "
+                f"{fwd_graph['replays_equal_eager_bitwise']}")
+
+    # ---- the same step captured once in a HIP graph and replayed (the library
+    # allocates nothing and issues no memset on this path, so it can be
+    # captured; replays remove the launch gaps between the step's kernels)
+    graph_res = graph_replay(step, (o, hT) + tuple(gout), args) if not args.no_graph else None
+    if graph_res:
+        graph_res["tokens_per_s"] = B * T / (graph_res["ms_per_step"] * 1e-3)
+        log(f"[bench] graph replay {graph_res['ms_per_step']:.3f} ms/step "
+            f"({graph_res['tokens_per_s'] / 1e6:.2f} M tokens/s), replays equal eager: "
+            f"{graph_res['replays_equal_eager_bitwise']}")
 
     # ---- per-head decay (one log-decay per token and head) at the same shape
     head = None
@@ -613,6 +678,16 @@ def main():
         log("[bench] calibration copy: 1 GiB read + 1 GiB written")
         del src, dst
 
+    # headline: the step as one HIP-graph replay when every check replay
+    # reproduced the eager step bitwise, else the eager calls
+    use_graph = bool(graph_res and graph_res["replays_equal_eager_bitwise"])
+    eager = {"ms_per_step": ms_step, "tokens_per_s": value}
+    if use_graph:
+        ms_step, value = graph_res["ms_per_step"], graph_res["tokens_per_s"]
+    use_fgraph = bool(fwd_graph and fwd_graph["replays_equal_eager_bitwise"])
+    fwd_eager = {"ms": ms_fwd, "tokens_per_s": fwd_tps}
+    if use_fgraph:
+        ms_fwd, fwd_tps = fwd_graph["ms_per_step"], fwd_graph["tokens_per_s"]
     line = {
         "metric": "tokens/s fwd and fwd+bwd at B=8 T=4096 H=6 d=128; % MFMA/HBM peak",
         "value": value,
@@ -632,9 +707,17 @@ def main():
                                f"T={T} H={H} Dk=Dv={D}, chunk {C}, {dt} q/k/v, fp32 state",
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": D,
                    "parallelism": "single GPU"},
+        "timing": ("one HIP-graph replay of gdn_forward_train + gdn_backward_train per step "
+                   "(check replays bitwise equal to the eager calls)") if use_graph
+                  else "eager library calls",
+        "eager": eager,
         "fwd_tokens_per_s": fwd_tps,
         "fwd_ms": ms_fwd,
+        "fwd_timing": "HIP-graph replay of gdn_forward" if use_fgraph else "eager gdn_forward",
+        "fwd_eager": fwd_eager,
         "fwd_kernels_us": fwd_kernels,
+        "graph_replay": graph_res,
+        "fwd_graph_replay": fwd_graph,
         "parity_ok": parity_ok,
         "parity_max_rel_err": par,
         "kernels": others,
