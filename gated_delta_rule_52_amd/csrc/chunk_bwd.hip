@@ -575,7 +575,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 float* __restrict__ dgmo, float* __restrict__ dbpo, int T, int H, int NC)
 {
     constexpr int BW = 32, NW = NTHR_C / 64, NB = C / 16;
-    constexpr int PB = BW + 8, PF = BW + 4, PC = C + 4;
+    constexpr int PB = BW + 8, PF = BW + 4;
     constexpr int T3 = NB * (DK / 16), M3 = (T3 + NW - 1) / NW;
     constexpr int T2 = NB * NB, M2 = (T2 + NW - 1) / NW;
     constexpr int TD = NB * (BW / 16), MD = (TD + NW - 1) / NW;
@@ -588,11 +588,13 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // Dv-streaming tiles, and after the Dv loop the key WY-adjoint tables, share sbuf
     constexpr int O_dS = DK * PB * 2, O_dO = 2 * DK * PB * 2, O_D = O_dO + C * PB * 2;
     constexpr int O_dD = O_D + C * PB * 2, O_U = O_dD + C * PB * 2, O_dX = O_U + C * PB * 2;
-    constexpr int O_dDf = O_dX + C * PB * 2, O_v = O_dDf + C * PF * 4, STREAM = O_v + C * PF * 4;
-    constexpr int O_TTh = DK * PT * 2, O_TTl = O_TTh + C * PT * 2, O_W = O_TTl + C * PT * 2;
+    constexpr int O_dDT = O_dX + C * PB * 2, O_v = O_dDT + BW * PT * 2, STREAM = O_v + C * PF * 4;
+    constexpr int O_W = DK * PT * 2;
     constexpr int O_Xh = O_W + C * PK * 2, O_Xl = O_Xh + C * PK * 2, ENDP = O_Xl + C * PK * 2;
     __shared__ __align__(16) char sbuf[cmax(STREAM, ENDP)];
-    __shared__ __align__(16) float sT[C][PC];
+    // T^T as high + low bf16 parts (16 significant bits), for dX_V = T^T dD in
+    // the Dv loop and dX_K = T^T dW after it; built once from the loaded T
+    __shared__ __align__(16) bf16 sTTh[C][PT], sTTl[C][PT];
     __shared__ __align__(16) bf16 sDV[C][DV + 8];  // dv, written out after the Dv loop
     __shared__ float sbeta[C], sred[NW][C];
     bf16 (*sS)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf);
@@ -602,11 +604,9 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     bf16 (*sdD)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_dD);
     bf16 (*sU)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_U);    // U and dX_V tiles,
     bf16 (*sdX)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_dX);  // for G1 = dX_V U^T
-    float (*sdDf)[PF] = reinterpret_cast<float (*)[PF]>(sbuf + O_dDf);
+    uint16_t* const dDT16 = reinterpret_cast<uint16_t*>(sbuf + O_dDT);  // dD^T [BW][PT]
     float (*sv)[PF] = reinterpret_cast<float (*)[PF]>(sbuf + O_v);
     bf16 (*sdWT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);          // dW^T
-    bf16 (*sTTh)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + O_TTh);  // T^T, high part
-    bf16 (*sTTl)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + O_TTl);  // T^T, low part
     bf16 (*sW)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + O_W);
     bf16 (*sXh)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + O_Xh);    // dX_K, high part
     bf16 (*sXl)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + O_Xl);    // dX_K, low part
@@ -673,9 +673,11 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             *reinterpret_cast<uint2*>(&sS[i][j4]) = s2;
             *reinterpret_cast<uint2*>(&sdS[i][j4]) = d2;
         }
-        st4(&sdDf[rd][jd], float4{__uint_as_float(pdD.x << 16), __uint_as_float(pdD.x & 0xFFFF0000u),
-                                  __uint_as_float(pdD.y << 16), __uint_as_float(pdD.y & 0xFFFF0000u)});
         *reinterpret_cast<uint2*>(&sdD[rd][jd]) = pdD;
+        dDT16[(jd + 0) * PT + rd] = (uint16_t)(pdD.x & 0xFFFFu);
+        dDT16[(jd + 1) * PT + rd] = (uint16_t)(pdD.x >> 16);
+        dDT16[(jd + 2) * PT + rd] = (uint16_t)(pdD.y & 0xFFFFu);
+        dDT16[(jd + 3) * PT + rd] = (uint16_t)(pdD.y >> 16);
         *reinterpret_cast<uint2*>(&sU[rd][jd]) = pack4_bf16(pU.x, pU.y, pU.z, pU.w);
         if (lowh) {
             *reinterpret_cast<uint4*>(&sD[r8][j8]) = pa;
@@ -725,9 +727,18 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             wv[u] = *reinterpret_cast<const uint4*>(Wp + 8 * min(tid + NTHR_C * u, C * DK / 8 - 1));
     }
 #pragma unroll
-    for (int u = 0; u < NT4; ++u) {
+    for (int u = 0; u < NT4; ++u) {  // T[r][c0 + e] -> T^T[c0 + e][r], high and low parts
         const int idx = tid + NTHR_C * u;
-        if (idx < C * C / 4) st4(&sT[idx / (C / 4)][(idx % (C / 4)) * 4], tv[u]);
+        if (idx < C * C / 4) {
+            const int r = idx / (C / 4), c0 = (idx % (C / 4)) * 4;
+            const float tt[4] = {tv[u].x, tv[u].y, tv[u].z, tv[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16 hi = f32_to_bf16(tt[e]);
+                sTTh[c0 + e][r] = hi;
+                sTTl[c0 + e][r] = f32_to_bf16(tt[e] - to_f32(hi));
+            }
+        }
     }
     if (tid < C) sbeta[tid] = tid < nvalid ? bv0 : 0.f;
     stash();
@@ -738,13 +749,15 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     auto tile = [&](int v0, auto more_c) {
         constexpr bool MORE = decltype(more_c)::value;
         if constexpr (MORE) fetch(v0 + BW);
-        // dX_V = T^T dD (fp32): dv = beta dX_V, and <dX_V, v> for dbeta
+        // dX_V = T^T dD (dD bf16, T^T as high + low bf16 parts, fp32
+        // accumulation): dv = beta dX_V, and <dX_V, v> for dbeta
 #pragma unroll
         for (int m = 0; m < MD; ++m) {
             const int idx = w + NW * m;
             if (idx < TD) {
                 const int ti = idx / (BW / 16), tj = idx % (BW / 16);
-                const f32x4 dx = mma16k<MT_F32, C>(zero4(), &sT[0][ti * 16], 1, PC, &sdDf[0][tj * 16], PF, 1);
+                f32x4 dx = mma_kc<C>(zero4(), &sTTh[ti * 16][0], PT, reinterpret_cast<const bf16*>(dDT16) + tj * 16 * PT, PT);
+                dx = mma_kc<C>(dx, &sTTl[ti * 16][0], PT, reinterpret_cast<const bf16*>(dDT16) + tj * 16 * PT, PT);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
@@ -834,21 +847,6 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // ---- WY adjoint of the keys (W = T X_K):  dX_K = T^T dW and
     //   dA = -T^T (dU X_V^T + dW X_K^T) T^T = -(dX_V U^T + dX_K W^T) = -(G1 + dX_K W^T),
     // on bf16 MFMA with T and dX_K as high + low bf16 parts (16 significant bits).
-    // T^T: thread -> 8 consecutive columns of one row
-    for (int idx = tid; idx < C * C / 8; idx += NTHR_C) {
-        const int i = idx / (C / 8), k0 = (idx % (C / 8)) * 8;
-        float hv[8], lv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float t = sT[k0 + e][i];
-            hv[e] = to_f32(f32_to_bf16(t));
-            lv[e] = t - hv[e];
-        }
-        const uint2 h0 = pack4_bf16(hv[0], hv[1], hv[2], hv[3]), h1 = pack4_bf16(hv[4], hv[5], hv[6], hv[7]);
-        const uint2 l0 = pack4_bf16(lv[0], lv[1], lv[2], lv[3]), l1 = pack4_bf16(lv[4], lv[5], lv[6], lv[7]);
-        *reinterpret_cast<uint4*>(&sTTh[i][k0]) = uint4{h0.x, h0.y, h1.x, h1.y};
-        *reinterpret_cast<uint4*>(&sTTl[i][k0]) = uint4{l0.x, l0.y, l1.x, l1.y};
-    }
 #pragma unroll
     for (int u = 0; u < NK8; ++u) {
         const int idx = tid + NTHR_C * u;
