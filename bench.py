@@ -44,7 +44,7 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 # (Marin note, "Single-device benchmark") -> B*T / 22.44 ms
 PAGES_FWDBWD_TOKENS_S = 8 * 4096 / 22.44e-3
 # kernel launch name -> the source file that defines it (for the counter digest)
-KERNEL_SOURCE = {"prep": "chunk_fwd.hip", "prep_T": "chunk_fwd.hip", "wy_u": "chunk_fwd.hip",
+KERNEL_SOURCE = {"prep": "chunk_fwd.hip", "prep_T": "chunk_fwd.hip",
                  "scan": "chunk_fwd.hip",
                  "scan_save": "chunk_fwd.hip", "scan_train": "chunk_fwd.hip",
                  "bscan": "chunk_bwd.hip", "bchunk1": "chunk_bwd.hip", "bchunk2": "chunk_bwd.hip",
@@ -103,19 +103,12 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True, l2n=False)
     if name in ("prep", "prep_T"):
         by = 2 * cd * ib + gb + C * f4                             # q k, g, beta
         by += 3 * cd * tb + cc * tb + DK * f4                      # W Qg Kh^T Ps, gam
-        if bt:   # bf16 T out; U = T X_V is wy_u's
-            by += cc * 2
-            fl[mt] += 2 * (2 * tri * DK) + 2 * tri * DK            # P, A; W = T X_K
-        else:    # v in, U out
-            by += cv * ib + cv * f4
-            fl[mt] += 2 * (2 * tri * DK) + 2 * tri * (DK + DV)     # P, A; W = T X_K, U = T X_V
+        by += cv * ib + cv * f4                                    # v in, U out
+        fl[mt] += 2 * (2 * tri * DK) + 2 * tri * (DK + DV)         # P, A; W = T X_K, U = T X_V
         if name == "prep_T":
             by += (3 * cd + cc) * (tb if bt else 0) + cc * f4      # transposed tables, T
         by += 2 * C * f4 if l2n else 0                             # r of the q and k rows
         fl["f32"] += 2 * C ** 3 / 3                                # (I + A)^-1
-    elif name == "wy_u":  # U = T diag(beta) V (bf16 tables)
-        by = cc * 2 + cv * ib + C * f4 + cv * f4                   # T, v, beta in; U out
-        fl["bf16"] += 2 * tri * DV
     elif name in ("scan", "scan_save", "scan_train"):
         by = 3 * cd * tb + cc * tb + cv * f4 + DK * f4             # W Qg Kh Ps, U, gam
         if name == "scan_save":                                    # deltas and states only

@@ -410,17 +410,18 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
 // registers; the level tables are bf16 rows with the channel index contiguous
 // (one 16-byte LDS read per MFMA operand); the diagonal scores are a chain of
 // the unscaled rows kept on the diagonal; W = T X_K is a bf16 MFMA product
-// with X_K^T written by the column threads.  U = T X_V is left to wy_u, which
-// reads the bf16 T written here: loading v this late would wait for every
-// table store before it (one completion counter for loads and stores).
+// with X_K^T written by the column threads; U = T X_V likewise, with X_V^T =
+// (beta V)^T stashed into the level-table bytes once T is done.  v is loaded
+// right after the level loop, before any table store: a load issued after
+// them would wait for them (one completion counter for loads and stores).
 // With L2N (use_qk_l2norm) every q and k row is scaled by r = 1/sqrt(|x|^2 +
 // eps): the squared lengths are the diagonals of the Q Q^T and K K^T tiles of
 // the raw rows, r is folded into the products of raw rows and into the rows
 // each thread keeps, and r goes to rno for the backward.
 // With SAFE (clip or diag) the stage values P, A, T, U, W pass through guard();
 // the solve's diagonal is damped by sf.dinv = 1 / (1 + wy_eps) in every instance.
-// Wro (training with clip): W also before clipping, which the backward's WY
-// adjoint needs (clipping is differentiated as the identity).
+// Wro, Uro (training with clip): W and U also before clipping, which the
+// backward's WY adjoint needs (clipping is differentiated as the identity).
 // ---------------------------------------------------------------------------
 constexpr int NTHR_P = 512;
 
@@ -428,11 +429,11 @@ template <int C, int DK, int DV, bool PCH, bool L2N, bool SAFE>
 __global__ void __launch_bounds__(NTHR_P, 4)
 prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
              const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int NC,
-             float scale, bf16* __restrict__ Wb, bf16* __restrict__ WTb, bf16* __restrict__ Tbo,
+             float scale, bf16* __restrict__ Wb, bf16* __restrict__ WTb, float* __restrict__ Uo,
              bf16* __restrict__ Qgb, bf16* __restrict__ QgTb, bf16* __restrict__ KhTb,
              bf16* __restrict__ Khb, bf16* __restrict__ Psb, bf16* __restrict__ PsTb,
              float* __restrict__ gamo, float* __restrict__ Tmo, float* __restrict__ rno,
-             Safety sf, bf16* __restrict__ Wro)
+             Safety sf, bf16* __restrict__ Wro, float* __restrict__ Uro)
 {
     static_assert(C == 64 && DK == DV, "prep2: chunk 64, Dk == Dv");
     constexpr int NW = NTHR_P / 64, RPP = 16, NPART = C / RPP, NB = C / 16;
@@ -709,6 +710,19 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     }  // per-channel decay
 
 
+    // v rows for U = T X_V at the end, loaded before any table store (a load
+    // issued after them would wait for them: one completion counter for loads
+    // and stores) and after the level loop (kept out of its registers); rows
+    // past the end are clamped here and zeroed through beta = 0
+    constexpr int NV8 = C * DV / 8, QV = NV8 / NTHR_P;
+    static_assert(QV * NTHR_P == NV8, "whole v words per thread");
+    uint4 vw[QV];
+#pragma unroll
+    for (int u = 0; u < QV; ++u) {
+        const int idx = tid + NTHR_P * u, r = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
+        vw[u] = *reinterpret_cast<const uint4*>(v + tok0 * DV + (size_t)min(r, nvalid - 1) * H * DV + j0);
+    }
+
     // ---- scores out: Ps (bf16) and, for training, Ps^T; A (x beta) to LDS
     bf16* Psc = Psb + (size_t)ch * C * C;
     bf16* PsTc = PsTb + (size_t)ch * C * C;
@@ -852,6 +866,20 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         *reinterpret_cast<uint2*>(&sTb[i][j]) = pack4_bf16(tv[0], tv[1], tv[2], tv[3]);
     }
     __syncthreads();
+    // X_V^T = (beta V)^T into the level-table bytes (free now that T is in sTb)
+    bf16 (*sXV)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);
+    static_assert(DV * PT * 2 <= SBUF, "X_V^T fits the level-table bytes");
+#pragma unroll
+    for (int u = 0; u < QV; ++u) {
+        const int idx = tid + NTHR_P * u, r = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
+        const float bt = sbeta[r];
+        const uint32_t wd[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sXV[j0 + 2 * e][r] = f32_to_bf16(bt * __uint_as_float(wd[e] << 16));
+            sXV[j0 + 2 * e + 1][r] = f32_to_bf16(bt * __uint_as_float(wd[e] & 0xFFFF0000u));
+        }
+    }
     // ---- W = T X_K (bf16 out, and W^T for training)
     constexpr int TW = NB * (DK / 16);
     for (int idx = w; idx < TW; idx += NW) {
@@ -872,101 +900,25 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             *reinterpret_cast<uint2*>(&WTb[(size_t)ch * C * DK + (tj * 16 + lr) * C + ti * 16 + 4 * lq]) =
                 pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
     }
-    // T in bf16 for U = T X_V (wy_u): rows of the LDS copy, 16 bytes per thread
-    for (int idx = tid; idx < C * C / 8; idx += NTHR_P) {
-        const int i = idx / (C / 8), j = (idx % (C / 8)) * 8;
-        *reinterpret_cast<uint4*>(&Tbo[(size_t)ch * C * C + i * C + j]) =
-            *reinterpret_cast<const uint4*>(&sTb[i][j]);
-    }
-    if constexpr (SAFE) {
-        __syncthreads();
-        flush_counts(sdg, sf.diag, NDIAG_PREP);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// wy_u: U = T diag(beta) V for one chunk-head (bf16 inputs at chunk 64), from
-// the bf16 T that prep2 wrote: T rows and the chunk's v rows (transposed, beta
-// folded in) into LDS, then bf16 MFMA products over the lower-triangular T;
-// U fp32 out.  With SAFE the values pass through guard() (the U stage), and
-// Uro (training with clip) also gets them before clipping.
-// ---------------------------------------------------------------------------
-constexpr int NTHR_U = 256;
-
-template <int C, int DV, bool SAFE>
-__global__ void __launch_bounds__(NTHR_U)
-wy_u_kernel(const bf16* __restrict__ Tbi, const bf16* __restrict__ v, const float* __restrict__ beta,
-            float* __restrict__ Uo, int T, int H, int NC, Safety sf, float* __restrict__ Uro)
-{
-    constexpr int PT = C + 8, NW = NTHR_U / 64, NB = C / 16;
-    constexpr int NT8 = C * C / 8, NV8 = C * DV / 8;
-    constexpr int QT = (NT8 + NTHR_U - 1) / NTHR_U, QV = (NV8 + NTHR_U - 1) / NTHR_U;
-    __shared__ __align__(16) bf16 sT[C][PT];
-    __shared__ __align__(16) bf16 sXV[DV][PT];  // (beta V)^T
-    __shared__ float sbeta[C];
-    __shared__ unsigned int sdg[2];
-    const int ch = blockIdx.x;
-    const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
-    const int t0 = n * C;
-    const int nvalid = min(C, T - t0);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
-    const size_t tok0 = ((size_t)b * T + t0) * H + h;
-    const size_t rsV = (size_t)H * DV;
-    if (SAFE && tid < 2) sdg[tid] = 0u;
-
-    uint4 tw[QT], vw[QV];
-#pragma unroll
-    for (int u = 0; u < QT; ++u)
-        tw[u] = *reinterpret_cast<const uint4*>(Tbi + (size_t)ch * C * C + 8 * min(tid + NTHR_U * u, NT8 - 1));
-#pragma unroll
-    for (int u = 0; u < QV; ++u) {
-        const int idx = min(tid + NTHR_U * u, NV8 - 1);
-        const int r = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
-        vw[u] = *reinterpret_cast<const uint4*>(v + tok0 * DV + min(r, nvalid - 1) * rsV + j0);
-    }
-    const float bv = beta[tok0 + (size_t)min(tid % C, nvalid - 1) * H];
-    if (tid < C) sbeta[tid] = tid < nvalid ? bv : 0.f;
-#pragma unroll
-    for (int u = 0; u < QT; ++u) {
-        const int idx = tid + NTHR_U * u;
-        if (idx < NT8) *reinterpret_cast<uint4*>(&sT[idx / (C / 8)][(idx % (C / 8)) * 8]) = tw[u];
-    }
-    __syncthreads();  // sbeta
-#pragma unroll
-    for (int u = 0; u < QV; ++u) {
-        const int idx = tid + NTHR_U * u;
-        if (idx < NV8) {
-            const int r = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
-            const float bt = r < nvalid ? sbeta[r] : 0.f;
-            const uint32_t wd[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sXV[j0 + 2 * e][r] = f32_to_bf16(bt * __uint_as_float(wd[e] << 16));
-                sXV[j0 + 2 * e + 1][r] = f32_to_bf16(bt * __uint_as_float(wd[e] & 0xFFFF0000u));
-            }
-        }
-    }
-    __syncthreads();
-    unsigned int* sd = SAFE && sf.diag ? &sdg[0] : nullptr;
+    __syncthreads();  // X_V^T complete
+    // ---- U = T X_V (fp32 out; Uro, training with clip: also before clipping).
+    // The tile of U^T = X_V^T T^T: a lane holds 4 consecutive columns of one U row
     constexpr int TU = NB * (DV / 16);
     float* Uc = Uo + (size_t)ch * C * DV;
     for (int idx = w; idx < TU; idx += NW) {
         const int ti = idx / (DV / 16), tj = idx % (DV / 16);
         const int K = ((16 * (ti + 1) + 31) / 32) * 32;  // T is lower triangular
-        // the tile of U^T = X_V^T T^T: a lane holds 4 consecutive columns of one U row
-        f32x4 acc = mma_kc_dyn(zero4(), &sXV[tj * 16][0], PT, &sT[ti * 16][0], PT, K);
+        f32x4 acc = mma_kc_dyn(zero4(), &sXV[tj * 16][0], PT, &sTb[ti * 16][0], PT, K);
         const size_t e = (size_t)(ti * 16 + lr) * DV + tj * 16 + 4 * lq;
         if (SAFE && Uro)
             *reinterpret_cast<float4*>(&Uro[(size_t)ch * C * DV + e]) = float4{acc[0], acc[1], acc[2], acc[3]};
-        if (SAFE) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = guard(acc[r], sf.clip, sd);
-        }
+        for (int r = 0; r < 4; ++r) acc[r] = grd(acc[r], GDN_DIAG_U);
         *reinterpret_cast<float4*>(&Uc[e]) = float4{acc[0], acc[1], acc[2], acc[3]};
     }
     if constexpr (SAFE) {
         __syncthreads();
-        flush_counts(sdg, sf.diag ? sf.diag + 2 * GDN_DIAG_U : nullptr, 2);
+        flush_counts(sdg, sf.diag, NDIAG_PREP);
     }
 }
 
@@ -1576,26 +1528,19 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
         bf16* Qb = (bf16*)Qg;
         bf16* Kb = (bf16*)Kh;
         bf16* Pb = (bf16*)Ps;
-        bf16* Tb = (bf16*)(ws + p.o_Tb);
         auto launch = [&](auto pch, auto l2n, auto safe) {
             GDN_LAUNCH(want_T ? "prep_T" : "prep",
                        (prep2_kernel<C, DK, DV, decltype(pch)::value, decltype(l2n)::value,
                                      decltype(safe)::value>),
                        grid, dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g,
-                       beta, p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, Tb, Qb, Qb + n * C * DK,
-                       Kb, Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm, rn, sf, Wro);
+                       beta, p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, U, Qb, Qb + n * C * DK,
+                       Kb, Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm, rn, sf, Wro, Uro);
             return GDN_OK;
         };
-        gdn_status s = with_bool(p.decay == GDN_DECAY_PER_CHANNEL, [&](auto pch) {
+        return with_bool(p.decay == GDN_DECAY_PER_CHANNEL, [&](auto pch) {
             return with_bool(p.l2n, [&](auto l2n) {
                 return with_bool(sf.on(), [&](auto safe) { return launch(pch, l2n, safe); });
             });
-        });
-        if (s != GDN_OK) return s;
-        return with_bool(sf.on(), [&](auto safe) {
-            GDN_LAUNCH("wy_u", (wy_u_kernel<C, DV, decltype(safe)::value>), grid, dim3(NTHR_U), st,
-                       (const bf16*)Tb, (const bf16*)v, beta, U, p.T, p.H, p.NC, sf, Uro);
-            return GDN_OK;
         });
     }
     if (p.decay == GDN_DECAY_PER_CHANNEL)

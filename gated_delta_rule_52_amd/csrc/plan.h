@@ -13,7 +13,6 @@
 //   rn  [ch][2][C]    with qk_l2norm: 1 / sqrt(|q_t|^2 + eps) (row 0) and the
 //                     same for k_t (row 1); the backward scales q, k by them
 //   dgc [GDN_DIAG_WORDS] uint32, with diag: the stage counters of the forward
-//   Tb  [ch][C][C]    bf16 T (bf16 inputs at chunk 64): prep2 -> wy_u, U = T X_V
 // backward only:
 //   Tm  [ch][C][C]    T = (I + A)^-1
 //   Sst [ch][Dk][Dv]  state at the start of chunk n
@@ -50,7 +49,7 @@ struct Plan {
     bool diag;
     size_t n_ch;  // B * H * NC
     // byte offsets into the workspace
-    size_t o_W, o_U, o_Qg, o_Kh, o_Ps, o_gam, o_rn, o_dgc, o_Tb, o_Tm, o_Sst, o_dSt, o_dDt;
+    size_t o_W, o_U, o_Qg, o_Kh, o_Ps, o_gam, o_rn, o_dgc, o_Tm, o_Sst, o_dSt, o_dDt;
     size_t o_dQg, o_dWg, o_dKh, o_dPs, o_dT1, o_dgm, o_dbp, o_Dst, o_dbq, o_dgq, o_Ur, o_Wr;
     size_t ws_fwd_bytes, ws_bwd_bytes;
 };
@@ -87,8 +86,6 @@ inline Plan make_plan(const gdn_shape& s, float scale)
     p.o_gam = off; off = align256(off + n * Dk * f);
     p.o_rn = off;  off = align256(off + (p.l2n ? n * 2 * C * f : 0));
     p.o_dgc = off; off = align256(off + (p.diag ? GDN_DIAG_WORDS * sizeof(unsigned int) : 0));
-    const bool bt = s.dtype == GDN_BF16 && p.C == 64 && p.Dk >= 64;  // bf16 chunk tables
-    p.o_Tb = off;  off = align256(off + (bt ? n * C * C * 2 : 0));
     p.ws_fwd_bytes = off;
     p.o_Tm = off;  off = align256(off + n * C * C * f);
     p.o_Sst = off; off = align256(off + n * Dk * Dv * f);
