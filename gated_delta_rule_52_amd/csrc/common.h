@@ -21,13 +21,21 @@ struct bf16 {
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(((uint32_t)x.bits) << 16); }
 
-// float -> bf16, round to nearest even (inputs here are finite)
+// float -> bf16, round to nearest even, on the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32: two values per instruction)
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 in one 32-bit word, a in the low half
+__device__ __forceinline__ uint32_t cvt2_bf16(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+
 __device__ __forceinline__ bf16 f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
     bf16 r;
-    r.bits = (uint16_t)(u >> 16);
+    r.bits = __builtin_bit_cast(uint16_t, (__bf16)f);
     return r;
 }
 

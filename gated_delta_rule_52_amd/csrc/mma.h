@@ -211,8 +211,7 @@ __device__ __forceinline__ f32x4 mma_kc16(f32x4 acc, const bf16* __restrict__ A,
 // four consecutive bf16 (8 bytes) from four floats, round to nearest even
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d)
 {
-    return uint2{(uint32_t)f32_to_bf16(a).bits | ((uint32_t)f32_to_bf16(b).bits << 16),
-                 (uint32_t)f32_to_bf16(c).bits | ((uint32_t)f32_to_bf16(d).bits << 16)};
+    return uint2{cvt2_bf16(a, b), cvt2_bf16(c, d)};
 }
 
 }  // namespace gdn
