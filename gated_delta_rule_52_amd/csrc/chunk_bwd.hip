@@ -1530,7 +1530,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         }
     }
 #pragma unroll
-    for (int i = 0; i < RPP; ++i) a[i] = expf(a[i]);
+    for (int i = 0; i < RPP; ++i) a[i] = fast_exp(a[i]);
     if constexpr (L2N) {  // the rows the forward used
 #pragma unroll
         for (int i = 0; i < RPP; ++i) {
@@ -1610,7 +1610,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
 #pragma unroll
             for (int z = 0; z < 8; ++z) {
                 const int i = tr ? c0 + z : rr, j = tr ? rr : c0 + z;  // element (i, j) of the C x C matrix
-                ev[z] = j <= i ? expf(sG[i] - sG[j]) : 0.f;
+                ev[z] = j <= i ? fast_exp(sG[i] - sG[j]) : 0.f;
                 ev2[z] = ev[z];
                 if constexpr (L2N) {
                     ev[z] *= sRn[i] * sRn[C + j];

@@ -480,7 +480,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         const float qx = to_f32(q[tok0 * DK + rr * rsK + c]);
         const float kx = to_f32(k[tok0 * DK + rr * rsK + c]);
         const bool ok = cp && r < nvalid;
-        a[i] = expf(ok ? gx : 0.f);
+        a[i] = fast_exp(ok ? gx : 0.f);
         qv[i] = ok ? qx : 0.f;
         kv[i] = ok ? kx : 0.f;
     }
@@ -560,7 +560,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 4 * lq + r, j = lr;
-                const float e = j <= i ? expf(sG[w * 16 + i] - sG[w * 16 + j]) : 0.f;
+                const float e = j <= i ? fast_exp(sG[w * 16 + i] - sG[w * 16 + j]) : 0.f;
                 dP[r] = tp[r] * e;
                 dA[r] = j < i ? ta[r] * e : 0.f;
             }
@@ -575,7 +575,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
                     accA[m] = mma_kc<DK>(zero4(), &sY[ti * 16][0], PA, &sY[tj * 16][0], PA);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float e = expf(sG[ti * 16 + 4 * lq + r] - sG[tj * 16 + lr]);
+                        const float e = fast_exp(sG[ti * 16 + 4 * lq + r] - sG[tj * 16 + lr]);
                         accP[m][r] *= e;
                         accA[m][r] *= e;
                     }
