@@ -236,6 +236,8 @@ def main():
                     help="skip the numerical-safety options measurement (wy_eps, clip, diag)")
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward-only measurement (profiling runs: one launch name per kernel)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the other-dtype and half-batch measurements")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -394,6 +396,88 @@ def main():
         log(f"[bench] graph replay {graph_res['ms_per_step']:.3f} ms/step "
             f"({graph_res['tokens_per_s'] / 1e6:.2f} M tokens/s), replays equal eager: "
             f"{graph_res['replays_equal_eager_bitwise']}")
+
+    # ---- the same layer at the other input dtype and at B/2 (the pages quote
+    # their training-shape figures for fp32 and bf16 inputs and for B = 4 and 8)
+    def variant(vdt, vB, label):
+        vinp = gi.train(dtype=vdt, B=vB, grads=True)
+        vd = to_device(vinp)
+        vq, vk, vv, vg, vbeta, vdO, vdhT = (vd[n] for n in ("q", "k", "v", "g", "beta", "dO", "dhT"))
+        vsh = gdn.make_shape(vq, vv, vg, scale, C)
+        vws_f = gdn.workspace(vsh, False, vq.device)
+        vws_b = gdn.workspace(vsh, True, vq.device)
+        vo = torch.empty_like(vv)
+        vhT = torch.empty((vB, H, D, D), dtype=torch.float32, device="cuda")
+        vgout = (torch.empty_like(vq), torch.empty_like(vk), torch.empty_like(vv),
+                 torch.empty_like(vg), torch.empty_like(vbeta), torch.empty_like(vhT))
+
+        def vstep():
+            gdn.gdn_forward_train(vq, vk, vv, vg, vbeta, None, scale=scale, chunk=C, o=vo, hT=vhT,
+                                  ws=vws_b)
+            return gdn.gdn_backward_train(vq, vk, vv, vg, vbeta, vdO, vws_b, vdhT, scale=scale,
+                                          chunk=C, out=vgout)
+
+        def vfwd():
+            gdn.gdn_forward(vq, vk, vv, vg, vbeta, None, scale=scale, chunk=C, o=vo, hT=vhT,
+                            ws=vws_f)
+
+        vgr = vstep()
+        torch.cuda.synchronize()
+        vp = [(0, 0), (vB - 1, H - 1)]
+        vs = {n: np.stack([vinp[n][b, :, h] for b, h in vp], axis=1)[None]
+              for n in ("q", "k", "v", "g", "beta", "dO")}
+        vs["dhT"] = np.stack([vinp["dhT"][b, h] for b, h in vp])[None]
+        vo_ref, vh_ref = oracle.forward(vs["q"], vs["k"], vs["v"], vs["g"], vs["beta"], scale)
+        vg_ref = oracle.backward(vs["q"], vs["k"], vs["v"], vs["g"], vs["beta"], scale, vs["dO"],
+                                 dhT=vs["dhT"])
+        vpar = {"o": rel(np.stack([pick(vo, b, h) for b, h in vp], 1)[None], vo_ref),
+                "hT": rel(np.stack([vhT[b, h].cpu().numpy() for b, h in vp])[None], vh_ref)}
+        for name, x in zip(("dq", "dk", "dv", "dg", "dbeta"), vgr[:5]):
+            got = np.stack([pick(x, b, h) for b, h in vp], 1)[None]
+            vpar[name] = rel(got, vg_ref[name])
+        vpar["dh0"] = rel(np.stack([vgr[5][b, h].cpu().numpy() for b, h in vp])[None], vg_ref["dh0"])
+        vtol = 2e-2 if vdt == "bf16" else 1e-5
+        for _ in range(args.warmup):
+            vstep()
+        torch.cuda.synchronize()
+        vrec = LaunchRecorder(args.steps * 16 + 16)
+        ev0.record()
+        with vrec:
+            for _ in range(args.steps):
+                vstep()
+        ev1.record()
+        torch.cuda.synchronize()
+        vms = ev0.elapsed_time(ev1) / args.steps
+        vker = {n: float(np.mean(ms)) * 1e3 for n, ms in vrec.by_kernel().items()}
+        vrec.close()
+        for _ in range(args.warmup):
+            vfwd()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            vfwd()
+        ev1.record()
+        torch.cuda.synchronize()
+        vfms = ev0.elapsed_time(ev1) / args.steps
+        vin_bytes = 2 if vdt == "bf16" else 4
+        vdom = max(vker, key=vker.get)
+        res = {"workload": f"{label}: per-channel decay, B={vB} T={T} H={H} Dk=Dv={D}, chunk {C}, "
+                           f"{vdt} q/k/v, fp32 state; eager library calls",
+               "fwdbwd_tokens_per_s": vB * T / (vms * 1e-3), "ms_per_step": vms,
+               "fwd_tokens_per_s": vB * T / (vfms * 1e-3), "fwd_ms": vfms,
+               "kernels_avg_us": vker,
+               "dominant_kernel_roofline": dict(roofline(vdom, vker[vdom] * 1e-6, vB, T, H, C, D,
+                                                         vin_bytes), kernel=vdom),
+               "parity_max_rel_err": vpar, "parity_ok": all(e <= vtol for e in vpar.values())}
+        log(f"[bench] {label}: fwd+bwd {vms:.3f} ms, fwd {vfms:.3f} ms, parity ok {res['parity_ok']}")
+        del vws_f, vws_b
+        return res
+
+    variants = None
+    if not args.no_variants:
+        other = "f32" if dt == "bf16" else "bf16"
+        variants = {other: variant(other, B, f"{other} inputs"),
+                    f"B{B // 2}": variant(dt, B // 2, f"B={B // 2}")}
 
     # ---- per-head decay (one log-decay per token and head) at the same shape
     head = None
@@ -716,6 +800,7 @@ def main():
         "kernels": others,
         "roofline": roof,
         "per_head": head,
+        "variants": variants,
         "qk_l2norm": l2,
         "safety_options": safety,
         "decode": decode,
