@@ -50,20 +50,32 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
     const TIn* vp = v + (size_t)bh * DV;
     float4* S = reinterpret_cast<float4*>(state + (size_t)bh * DK * DV);
 
+    // the Dk-vectors (decay, k, q): one element per thread, shared through LDS,
+    // exp taken once per row (instead of every thread loading and exponentiating
+    // its rows' values)
+    static_assert(DK <= C::NT, "one Dk element per thread");
+    __shared__ float sa[DK], sk[DK], sq[DK];
+    const int te = t < DK ? t : DK - 1;  // unconditional loads (the extra threads repeat one)
+    const float ga = PER_CHANNEL ? g[(size_t)bh * DK + te] : g[bh];
+    const TIn gk = kp[te], gq = qp[te];
     float4 s[C::NP];
 #pragma unroll
     for (int p = 0; p < C::NP; ++p) s[p] = S[(r0 + p * C::RPP) * C::VPR + c4];
+    if (t < DK) {
+        sa[t] = fast_exp(ga);
+        sk[t] = to_f32(gk);
+        sq[t] = to_f32(gq);
+    }
+    __syncthreads();
 
-    float a_head = 0.f;
-    if (!PER_CHANNEL) a_head = fast_exp(g[bh]);
     float kr[C::NP];
     float mk[4] = {0.f, 0.f, 0.f, 0.f}, mq[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f, qq = 0.f, kk = 0.f;
 #pragma unroll
     for (int p = 0; p < C::NP; ++p) {
         const int row = r0 + p * C::RPP;
-        const float a = PER_CHANNEL ? fast_exp(g[(size_t)bh * DK + row]) : a_head;
-        const float kv = to_f32(kp[row]);
-        const float qv = to_f32(qp[row]);
+        const float a = sa[row];
+        const float kv = sk[row];
+        const float qv = sq[row];
         kr[p] = kv;
         s[p].x *= a; s[p].y *= a; s[p].z *= a; s[p].w *= a;
         mk[0] += kv * s[p].x; mk[1] += kv * s[p].y; mk[2] += kv * s[p].z; mk[3] += kv * s[p].w;
