@@ -768,7 +768,15 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         }
     }
 
-    // ---- Gamma, Kh factor, gam: Qg, Kh outputs and X_K^T = (beta K o Gamma)^T
+    // ---- Gamma, Kh factor, gam: Qg, Kh outputs and X_K^T = (beta K o Gamma)^T.
+    // Qg and Kh rows are staged in the level-table bytes (free after the score
+    // products) and leave as whole rows, 16 bytes per thread, instead of one
+    // 2-byte store per row and thread.
+    bf16 (*sQs)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf);
+    bf16 (*sKs)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf + C * PA * 2);
+    static_assert(2 * C * PA * 2 <= SBUF, "staged Qg and Kh fit the level-table bytes");
+    bf16* Qgc = Qgb + (size_t)ch * C * DK;
+    bf16* Khc = Khb + (size_t)ch * C * DK;
     if (cp) {
         float pre = 1.f, suf = 1.f;
         for (int pp = 0; pp < part; ++pp) pre *= stot[pp][c];
@@ -788,12 +796,10 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             kh[i] = kv[i] * kap;
             kap *= a[i];
         }
-        bf16* Qgc = Qgb + (size_t)ch * C * DK;
         bf16* QgTc = QgTb + (size_t)ch * C * DK;
         bf16* KhTc = KhTb + (size_t)ch * C * DK;
-        bf16* Khc = Khb + (size_t)ch * C * DK;
 #pragma unroll
-        for (int i = 0; i < RPP; ++i) Qgc[(p0 + i) * DK + c] = f32_to_bf16(qg[i]);
+        for (int i = 0; i < RPP; ++i) sQs[p0 + i][c] = f32_to_bf16(qg[i]);
         // a thread's 16 rows of one channel are 32 contiguous bytes of the
         // transposed tables: two 16-byte stores each
 #pragma unroll
@@ -813,9 +819,16 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
                 *reinterpret_cast<uint4*>(&QgTc[c * C + p0 + i]) = uint4{q0.x, q0.y, q1.x, q1.y};
             }
 #pragma unroll
-            for (int i = 0; i < RPP; ++i) Khc[(p0 + i) * DK + c] = f32_to_bf16(kh[i]);
+            for (int i = 0; i < RPP; ++i) sKs[p0 + i][c] = f32_to_bf16(kh[i]);
         }
     }
+    __syncthreads();  // staged rows complete
+    for (int idx = tid; idx < C * DK / 8; idx += NTHR_P) {
+        const int r = idx / (DK / 8), c0 = (idx % (DK / 8)) * 8;
+        *reinterpret_cast<uint4*>(&Qgc[r * DK + c0]) = *reinterpret_cast<const uint4*>(&sQs[r][c0]);
+        if (bwdt) *reinterpret_cast<uint4*>(&Khc[r * DK + c0]) = *reinterpret_cast<const uint4*>(&sKs[r][c0]);
+    }
+    __syncthreads();  // the staged rows are read: sT takes their bytes
     for (int idx = tid; idx < C * PC; idx += NTHR_P) (&sT[0][0])[idx] = 0.f;
     __syncthreads();
 
