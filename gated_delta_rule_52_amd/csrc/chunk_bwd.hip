@@ -896,9 +896,8 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // dgam: the BW/4 threads of one state row hold its partial sums
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
-        float sgm = dgm_part[q];
-#pragma unroll
-        for (int off = 1; off < BW / 4; off <<= 1) sgm += __shfl_xor(sgm, off);
+        static_assert(BW / 4 == 8, "eight threads per state row");
+        const float sgm = lane8_sum(dgm_part[q]);
         const int idx = tid + NTHR_C * q;
         if (idx < NS4 && (idx % (BW / 4)) == 0) dgmo[(size_t)ch * DK + idx / (BW / 4)] = sgm;
     }
@@ -913,9 +912,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             const int ti = idx / (BW / 16);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float sb = dbr[m][r];
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) sb += __shfl_xor(sb, off);
+                const float sb = lane16_sum(dbr[m][r]);
                 if (lr == 0) sred[w][ti * 16 + 4 * lq + r] = sb;
             }
         }
@@ -1893,8 +1890,8 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
 #pragma unroll
             for (int cc = sub; cc < HC; cc += 4) sb += sR[r][cc];
         }
-        sb += __shfl_xor(sb, 1);
-        sb += __shfl_xor(sb, 2);
+        sb += dpp_mov<0xB1>(sb);  // quad sum: neighbour swap, pair swap
+        sb += dpp_mov<0x4E>(sb);
         if (r < C && sub == 0) dbq[((size_t)ch * 2 + half) * C + r] = sb;
     }
     if (!PCH) {
@@ -1911,8 +1908,8 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
 #pragma unroll
             for (int cc = sub; cc < HC; cc += 4) sg += sR[r][cc];
         }
-        sg += __shfl_xor(sg, 1);
-        sg += __shfl_xor(sg, 2);
+        sg += dpp_mov<0xB1>(sg);  // quad sum: neighbour swap, pair swap
+        sg += dpp_mov<0x4E>(sg);
         if (r < C && sub == 0) dgq[((size_t)ch * 2 + half) * C + r] = sg;
     }
 }

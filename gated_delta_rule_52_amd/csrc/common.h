@@ -47,6 +47,30 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return f32
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane sums inside a DPP row (16 lanes) by DPP moves, which stay in the VALU
+// instead of a round trip through the LDS crossbar (ds_bpermute).  Every lane
+// of a group receives the group's sum, bitwise equal across the group.  All 16
+// lanes of the row must be active.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// sum over aligned groups of 8 lanes: neighbour swap, pair swap, mirror in 8
+__device__ __forceinline__ float lane8_sum(float x)
+{
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);  // row_half_mirror: lane i <- 7-i
+    return x;
+}
+// sum over a whole row of 16 lanes
+__device__ __forceinline__ float lane16_sum(float x)
+{
+    x = lane8_sum(x);
+    x += dpp_mov<0x140>(x);  // row_mirror: lane i <- 15-i
+    return x;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA (CDNA3/CDNA4 matrix cores), wave64
 //
