@@ -558,8 +558,11 @@ bchunk1_kernel(const TIn* __restrict__ v, const float* __restrict__ beta,
 // bchunk1 over bf16 tables (bf16 inputs): 8 waves, Dv streamed in 32-column
 // tiles with the next tile prefetched into registers; D comes from the forward
 // (saved by the scan); the five contractions over Dv are single K = 32 bf16
-// MFMAs on K-contiguous LDS tiles; dgam is summed from the fp32 states as they
-// are loaded; dX_V = T^T dD stays in fp32.
+// MFMAs on K-contiguous LDS tiles; dgam is summed from the states as they are
+// loaded; dX_V = T^T dD stays in fp32.  Persistent, one workgroup per CU (the
+// LDS allows no second): each workgroup takes every gridDim.x-th chunk-head and
+// loads the next one's first tile, T, beta and W while it computes the WY
+// adjoint of the keys of the current one.
 // ---------------------------------------------------------------------------
 constexpr int NTHR_C = 512;
 
@@ -572,7 +575,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const bf16* __restrict__ dSt, const bf16* __restrict__ dDt,
                 bf16* __restrict__ dvo, float* __restrict__ dQgo, float* __restrict__ dWgo,
                 float* __restrict__ dKho, float* __restrict__ dPso, float* __restrict__ dT1o,
-                float* __restrict__ dgmo, float* __restrict__ dbpo, int T, int H, int NC)
+                float* __restrict__ dgmo, float* __restrict__ dbpo, int T, int H, int NC, int nch)
 {
     constexpr int BW = 32, NW = NTHR_C / 64, NB = C / 16;
     constexpr int PB = BW + 8, PF = BW + 4;
@@ -611,19 +614,23 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     bf16 (*sXh)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + O_Xh);    // dX_K, high part
     bf16 (*sXl)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + O_Xl);    // dX_K, low part
 
-    const int ch = blockIdx.x;
-    const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
-    const int t0 = n * C;
-    const int nvalid = min(C, T - t0);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int lr = l & 15, lq = l >> 4;
-    const size_t tok0 = ((size_t)b * T + t0) * H + h;
-
-    const bf16* Sp = Sst + (size_t)ch * DK * DV;    // bf16 chunk-start states
-    const bf16* dSp = dSt + (size_t)ch * DK * DV;   // bf16 chunk-end state gradients
-    const bf16* dDp = dDt + (size_t)ch * C * DV;    // bf16 delta gradients
-    const bf16* Dp = Dst + (size_t)ch * C * DV;
-    const float* Up = Ui + (size_t)ch * C * DV;
+    if ((int)blockIdx.x >= nch) return;  // whole workgroup
+    // chunk-head ch -> its valid rows and first token
+    auto geo = [&](int c, int& nv, size_t& tk) {
+        const int n = c % NC, bh = c / NC, h = bh % H, b = bh / H;
+        nv = min(C, T - n * C);
+        tk = ((size_t)b * T + (size_t)n * C) * H + h;
+    };
+    // the chunk the prefetch reads (the current one inside the Dv loop, the
+    // next one of this workgroup during the current one's WY-adjoint tail)
+    const bf16 *Sp, *dSp, *dDp, *Dp;  // bf16 chunk-start states, chunk-end state gradients, delta gradients, D
+    const float* Up;
+    size_t tokr;  // this thread's token row of dO and v
+    int nvalid;   // of the chunk being computed
+    size_t tok0;
+    bool row8;
 
     // Prefetch of one Dv tile, branch-free (a load under a divergent branch makes
     // the compiler wait for it where the branches join): every thread loads two
@@ -636,9 +643,19 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     const bool lowh = tid < NB8;
     const int e8 = lowh ? tid : tid - NB8;
     const int r8 = e8 / (BW / 8), j8 = (e8 % (BW / 8)) * 8;
-    const bool row8 = r8 < nvalid;
-    const size_t tokr = (tok0 + (size_t)min(r8, nvalid - 1) * H) * DV;
     const int rd = tid / (BW / 4), jd = (tid % (BW / 4)) * 4;  // dD / U word of this thread
+    auto fetch_from = [&](int c) {
+        int nv;
+        size_t tk;
+        geo(c, nv, tk);
+        Sp = Sst + (size_t)c * DK * DV;
+        dSp = dSt + (size_t)c * DK * DV;
+        dDp = dDt + (size_t)c * C * DV;
+        Dp = Dst + (size_t)c * C * DV;
+        Up = Ui + (size_t)c * C * DV;
+        tokr = (tk + (size_t)min(r8, nv - 1) * H) * DV;
+        return tk + (size_t)min(tid % C, nv - 1) * H;  // this thread's beta token
+    };
     auto fetch = [&](int v0) {
 #pragma unroll
         for (int q = 0; q < QS; ++q) {
@@ -696,233 +713,277 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         }
     };
 
-    f32x4 aQ[M3], aW[M3], aK[M3], aP[M2], aT[M2];
-#pragma unroll
-    for (int m = 0; m < M3; ++m) aQ[m] = aW[m] = aK[m] = zero4();
-#pragma unroll
-    for (int m = 0; m < M2; ++m) aP[m] = aT[m] = zero4();
-    float dbr[MD][4];
-#pragma unroll
-    for (int m = 0; m < MD; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dbr[m][r] = 0.f;
-
-    // prologue, one round of loads: the first Dv tile, T, beta and W, then T and
-    // beta into LDS and the tile stashed
-    fetch(0);
+    // prologue loads of a chunk: its first Dv tile, T, beta and W (W is used
+    // after the Dv loop); issued for the first chunk here and for each next one
+    // during the tail of the one before, so the tail hides their latency
     constexpr int NT4 = (C * C / 4 + NTHR_C - 1) / NTHR_C;
+    constexpr int NK8 = (C * DK / 8 + NTHR_C - 1) / NTHR_C;
     float4 tv[NT4];
-    {
-        const float* Tp = Tmi + (size_t)ch * C * C;
+    float bv0;
+    uint4 wv[NK8];  // W rows (bf16) for the keys' WY adjoint after the Dv loop
+    auto prologue_loads = [&](int c) {
+        const size_t tb = fetch_from(c);
+        fetch(0);
+        const float* Tp = Tmi + (size_t)c * C * C;
 #pragma unroll
         for (int u = 0; u < NT4; ++u) tv[u] = load4<float>(Tp + 4 * min(tid + NTHR_C * u, C * C / 4 - 1));
-    }
-    const float bv0 = beta[tok0 + (size_t)min(tid % C, nvalid - 1) * H];
-    constexpr int NK8 = (C * DK / 8 + NTHR_C - 1) / NTHR_C;
-    uint4 wv[NK8];  // W rows (bf16) for the keys' WY adjoint after the Dv loop
-    {
-        const bf16* Wp = Wbi + (size_t)ch * C * DK;
+        bv0 = beta[tb];
+        const bf16* Wp = Wbi + (size_t)c * C * DK;
 #pragma unroll
         for (int u = 0; u < NK8; ++u)
             wv[u] = *reinterpret_cast<const uint4*>(Wp + 8 * min(tid + NTHR_C * u, C * DK / 8 - 1));
-    }
+    };
+    prologue_loads(blockIdx.x);
+
+    // the WY-adjoint tail's outputs of the previous chunk (chunk-head pch),
+    // held in registers and stored after the next chunk's prologue: a global
+    // store issued after the prefetch would be waited for with it (the memory
+    // counter completes in issue order)
+    constexpr int NX8 = (C * DK / 8 + NTHR_C - 1) / NTHR_C;
+    uint4 oX[NX8];
+    float oA[M2][4], oG[QS], oB;
+    int pch = -1;
+    auto put_tail = [&]() {
+        bf16* dXp = reinterpret_cast<bf16*>(dWgo) + (size_t)pch * C * DK;
 #pragma unroll
-    for (int u = 0; u < NT4; ++u) {  // T[r][c0 + e] -> T^T[c0 + e][r], high and low parts
-        const int idx = tid + NTHR_C * u;
-        if (idx < C * C / 4) {
-            const int r = idx / (C / 4), c0 = (idx % (C / 4)) * 4;
-            const float tt[4] = {tv[u].x, tv[u].y, tv[u].z, tv[u].w};
+        for (int u = 0; u < NX8; ++u) {
+            const int idx = tid + NTHR_C * u;
+            if (idx < C * DK / 8) *reinterpret_cast<uint4*>(dXp + idx * 8) = oX[u];
+        }
+        bf16* dAp = reinterpret_cast<bf16*>(dT1o) + (size_t)pch * C * C;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bf16 hi = f32_to_bf16(tt[e]);
-                sTTh[c0 + e][r] = hi;
-                sTTl[c0 + e][r] = f32_to_bf16(tt[e] - to_f32(hi));
+        for (int m = 0; m < M2; ++m) {
+            const int idx = w + NW * m;
+            if (idx < T2) {
+                const int ti = idx / NB, tj = idx % NB;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dAp[(ti * 16 + 4 * lq + r) * C + tj * 16 + lr] = f32_to_bf16(oA[m][r]);
             }
         }
-    }
-    if (tid < C) sbeta[tid] = tid < nvalid ? bv0 : 0.f;
-    stash();
-    __syncthreads();
-    // one Dv tile; the last one is peeled (MORE = false) so that the prefetch and
-    // its stash need no run-time guard: with one, the compiler cannot match the
-    // two and waits for every outstanding load and store at the top of the loop
-    auto tile = [&](int v0, auto more_c) {
-        constexpr bool MORE = decltype(more_c)::value;
-        if constexpr (MORE) fetch(v0 + BW);
-        // dX_V = T^T dD (dD bf16, T^T as high + low bf16 parts, fp32
-        // accumulation): dv = beta dX_V, and <dX_V, v> for dbeta
 #pragma unroll
-        for (int m = 0; m < MD; ++m) {
-            const int idx = w + NW * m;
-            if (idx < TD) {
-                const int ti = idx / (BW / 16), tj = idx % (BW / 16);
-                f32x4 dx = mma_kc<C>(zero4(), &sTTh[ti * 16][0], PT, reinterpret_cast<const bf16*>(dDT16) + tj * 16 * PT, PT);
-                dx = mma_kc<C>(dx, &sTTl[ti * 16][0], PT, reinterpret_cast<const bf16*>(dDT16) + tj * 16 * PT, PT);
+        for (int q = 0; q < QS; ++q) {
+            const int idx = tid + NTHR_C * q;
+            if (idx < NS4 && (idx % (BW / 4)) == 0) dgmo[(size_t)pch * DK + idx / (BW / 4)] = oG[q];
+        }
+        if (tid < C) dbpo[(size_t)pch * C + tid] = oB;
+    };
+
+    // persistent: this workgroup takes chunk-heads blockIdx.x, + gridDim.x, ...
+    for (int ch = blockIdx.x;;) {
+        geo(ch, nvalid, tok0);
+        row8 = r8 < nvalid;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                    sDV[i][v0 + j] = f32_to_bf16(sbeta[i] * dx[r]);
-                    dbr[m][r] += dx[r] * sv[i][j];
-                    sdX[i][j] = f32_to_bf16(dx[r]);
+        for (int q = 0; q < QS; ++q) dgm_part[q] = 0.f;
+        f32x4 aQ[M3], aW[M3], aK[M3], aP[M2], aT[M2];
+#pragma unroll
+        for (int m = 0; m < M3; ++m) aQ[m] = aW[m] = aK[m] = zero4();
+#pragma unroll
+        for (int m = 0; m < M2; ++m) aP[m] = aT[m] = zero4();
+        float dbr[MD][4];
+#pragma unroll
+        for (int m = 0; m < MD; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dbr[m][r] = 0.f;
+
+        // T^T and beta into LDS, the first tile stashed
+#pragma unroll
+        for (int u = 0; u < NT4; ++u) {  // T[r][c0 + e] -> T^T[c0 + e][r], high and low parts
+            const int idx = tid + NTHR_C * u;
+            if (idx < C * C / 4) {
+                const int r = idx / (C / 4), c0 = (idx % (C / 4)) * 4;
+                const float tt[4] = {tv[u].x, tv[u].y, tv[u].z, tv[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bf16 hi = f32_to_bf16(tt[e]);
+                    sTTh[c0 + e][r] = hi;
+                    sTTl[c0 + e][r] = f32_to_bf16(tt[e] - to_f32(hi));
                 }
             }
         }
+        if (tid < C) sbeta[tid] = tid < nvalid ? bv0 : 0.f;
+        stash();
+        __syncthreads();
+        if (pch >= 0) put_tail();  // the previous chunk's, now that the prefetch is used
+        // one Dv tile; the last one is peeled (MORE = false) so that the prefetch and
+        // its stash need no run-time guard: with one, the compiler cannot match the
+        // two and waits for every outstanding load and store at the top of the loop
+        auto tile = [&](int v0, auto more_c) {
+            constexpr bool MORE = decltype(more_c)::value;
+            if constexpr (MORE) fetch(v0 + BW);
+            // dX_V = T^T dD (dD bf16, T^T as high + low bf16 parts, fp32
+            // accumulation): dv = beta dX_V, and <dX_V, v> for dbeta
+#pragma unroll
+            for (int m = 0; m < MD; ++m) {
+                const int idx = w + NW * m;
+                if (idx < TD) {
+                    const int ti = idx / (BW / 16), tj = idx % (BW / 16);
+                    f32x4 dx = mma_kc<C>(zero4(), &sTTh[ti * 16][0], PT, reinterpret_cast<const bf16*>(dDT16) + tj * 16 * PT, PT);
+                    dx = mma_kc<C>(dx, &sTTl[ti * 16][0], PT, reinterpret_cast<const bf16*>(dDT16) + tj * 16 * PT, PT);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                        sDV[i][v0 + j] = f32_to_bf16(sbeta[i] * dx[r]);
+                        dbr[m][r] += dx[r] * sv[i][j];
+                        sdX[i][j] = f32_to_bf16(dx[r]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < M3; ++m) {
+                const int idx = w + NW * m;
+                if (idx < T3) {
+                    const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+                    aQ[m] = mma_kc<BW>(aQ[m], &sdO[ti * 16][0], PB, &sS[tj * 16][0], PB);
+                    aW[m] = mma_kc<BW>(aW[m], &sdD[ti * 16][0], PB, &sS[tj * 16][0], PB);
+                    aK[m] = mma_kc<BW>(aK[m], &sD[ti * 16][0], PB, &sdS[tj * 16][0], PB);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < M2; ++m) {
+                const int idx = w + NW * m;
+                if (idx < T2) {
+                    const int ti = idx / NB, tj = idx % NB;
+                    aP[m] = mma_kc<BW>(aP[m], &sdO[ti * 16][0], PB, &sD[tj * 16][0], PB);
+                }
+            }
+            __syncthreads();  // the dX_V tile is complete
+#pragma unroll
+            for (int m = 0; m < M2; ++m) {
+                const int idx = w + NW * m;
+                if (idx < T2) {
+                    const int ti = idx / NB, tj = idx % NB;
+                    aT[m] = mma_kc<BW>(aT[m], &sdX[ti * 16][0], PB, &sU[tj * 16][0], PB);
+                }
+            }
+            __syncthreads();
+            if constexpr (MORE) {
+                stash();
+                __syncthreads();
+            }
+        };
+        for (int v0 = 0; v0 + BW < DV; v0 += BW) tile(v0, std::true_type{});
+        tile(DV - BW, std::false_type{});
+
+        // dv out: the loop stores nothing to global memory (a store there would be
+        // waited for with the next prefetch)
+        for (int idx = tid; idx < C * DV / 8; idx += NTHR_C) {
+            const int r = idx / (DV / 8), c0 = (idx % (DV / 8)) * 8;
+            if (r < nvalid)
+                *reinterpret_cast<uint4*>(dvo + (tok0 + (size_t)r * H) * DV + c0) =
+                    *reinterpret_cast<const uint4*>(&sDV[r][c0]);
+        }
+        // outputs (bf16: the consumer reads them as gradients of bf16-rounded products)
+        bf16* dQp = reinterpret_cast<bf16*>(dQgo) + (size_t)ch * C * DK;
+        bf16* dKp = reinterpret_cast<bf16*>(dKho) + (size_t)ch * C * DK;
 #pragma unroll
         for (int m = 0; m < M3; ++m) {
             const int idx = w + NW * m;
             if (idx < T3) {
                 const int ti = idx / (DK / 16), tj = idx % (DK / 16);
-                aQ[m] = mma_kc<BW>(aQ[m], &sdO[ti * 16][0], PB, &sS[tj * 16][0], PB);
-                aW[m] = mma_kc<BW>(aW[m], &sdD[ti * 16][0], PB, &sS[tj * 16][0], PB);
-                aK[m] = mma_kc<BW>(aK[m], &sD[ti * 16][0], PB, &sdS[tj * 16][0], PB);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                    dQp[i * DK + j] = f32_to_bf16(aQ[m][r]);
+                    dKp[i * DK + j] = f32_to_bf16(aK[m][r]);
+                }
+                // dW = -aW, stored transposed for dX_K = T^T dW (4 consecutive rows per lane)
+                *reinterpret_cast<uint2*>(&sdWT[tj * 16 + lr][ti * 16 + 4 * lq]) =
+                    pack4_bf16(-aW[m][0], -aW[m][1], -aW[m][2], -aW[m][3]);
             }
         }
+        bf16* dPp = reinterpret_cast<bf16*>(dPso) + (size_t)ch * C * C;
 #pragma unroll
         for (int m = 0; m < M2; ++m) {
             const int idx = w + NW * m;
             if (idx < T2) {
                 const int ti = idx / NB, tj = idx % NB;
-                aP[m] = mma_kc<BW>(aP[m], &sdO[ti * 16][0], PB, &sD[tj * 16][0], PB);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                    dPp[i * C + j] = f32_to_bf16(aP[m][r]);
+                }
             }
         }
-        __syncthreads();  // the dX_V tile is complete
+
+        // ---- WY adjoint of the keys (W = T X_K):  dX_K = T^T dW and
+        //   dA = -T^T (dU X_V^T + dW X_K^T) T^T = -(dX_V U^T + dX_K W^T) = -(G1 + dX_K W^T),
+        // on bf16 MFMA with T and dX_K as high + low bf16 parts (16 significant bits).
 #pragma unroll
-        for (int m = 0; m < M2; ++m) {
+        for (int u = 0; u < NK8; ++u) {
+            const int idx = tid + NTHR_C * u;
+            if (idx < C * DK / 8) *reinterpret_cast<uint4*>(&sW[idx / (DK / 8)][(idx % (DK / 8)) * 8]) = wv[u];
+        }
+        __syncthreads();
+        // the next chunk's prologue loads, in flight through the tail (the last
+        // workgroup's final chunk repeats itself: loads stay unconditional)
+        prologue_loads(min(ch + (int)gridDim.x, nch - 1));
+#pragma unroll
+        for (int m = 0; m < M3; ++m) {
             const int idx = w + NW * m;
-            if (idx < T2) {
-                const int ti = idx / NB, tj = idx % NB;
-                aT[m] = mma_kc<BW>(aT[m], &sdX[ti * 16][0], PB, &sU[tj * 16][0], PB);
+            if (idx < T3) {
+                const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+                f32x4 acc = mma_kc<C>(zero4(), &sTTh[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
+                acc = mma_kc<C>(acc, &sTTl[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                    const bf16 hi = f32_to_bf16(acc[r]);
+                    sXh[i][j] = hi;
+                    sXl[i][j] = f32_to_bf16(acc[r] - to_f32(hi));
+                }
             }
         }
         __syncthreads();
-        if constexpr (MORE) {
-            stash();
-            __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NX8; ++u) {  // dX_K (bf16) rows, stored in place of dW
+            const int idx = min(tid + NTHR_C * u, C * DK / 8 - 1);
+            oX[u] = *reinterpret_cast<const uint4*>(&sXh[idx / (DK / 8)][(idx % (DK / 8)) * 8]);
         }
-    };
-    for (int v0 = 0; v0 + BW < DV; v0 += BW) tile(v0, std::true_type{});
-    tile(DV - BW, std::false_type{});
-
-    // dv out: the loop stores nothing to global memory (a store there would be
-    // waited for with the next prefetch)
-    for (int idx = tid; idx < C * DV / 8; idx += NTHR_C) {
-        const int r = idx / (DV / 8), c0 = (idx % (DV / 8)) * 8;
-        if (r < nvalid)
-            *reinterpret_cast<uint4*>(dvo + (tok0 + (size_t)r * H) * DV + c0) =
-                *reinterpret_cast<const uint4*>(&sDV[r][c0]);
-    }
-    // outputs (bf16: the consumer reads them as gradients of bf16-rounded products)
-    bf16* dQp = reinterpret_cast<bf16*>(dQgo) + (size_t)ch * C * DK;
-    bf16* dKp = reinterpret_cast<bf16*>(dKho) + (size_t)ch * C * DK;
 #pragma unroll
-    for (int m = 0; m < M3; ++m) {
-        const int idx = w + NW * m;
-        if (idx < T3) {
-            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+        for (int m = 0; m < M2; ++m) {
+            const int idx = w + NW * m;
+            if (idx < T2) {
+                const int ti = idx / NB, tj = idx % NB;
+                f32x4 acc = mma_kc<DK>(aT[m], &sXh[ti * 16][0], PK, &sW[tj * 16][0], PK);
+                acc = mma_kc<DK>(acc, &sXl[ti * 16][0], PK, &sW[tj * 16][0], PK);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                dQp[i * DK + j] = f32_to_bf16(aQ[m][r]);
-                dKp[i * DK + j] = f32_to_bf16(aK[m][r]);
-            }
-            // dW = -aW, stored transposed for dX_K = T^T dW (4 consecutive rows per lane)
-            *reinterpret_cast<uint2*>(&sdWT[tj * 16 + lr][ti * 16 + 4 * lq]) =
-                pack4_bf16(-aW[m][0], -aW[m][1], -aW[m][2], -aW[m][3]);
-        }
-    }
-    bf16* dPp = reinterpret_cast<bf16*>(dPso) + (size_t)ch * C * C;
-#pragma unroll
-    for (int m = 0; m < M2; ++m) {
-        const int idx = w + NW * m;
-        if (idx < T2) {
-            const int ti = idx / NB, tj = idx % NB;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                dPp[i * C + j] = f32_to_bf16(aP[m][r]);
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                    oA[m][r] = i > j ? -acc[r] : 0.f;
+                }
             }
         }
-    }
-
-    // ---- WY adjoint of the keys (W = T X_K):  dX_K = T^T dW and
-    //   dA = -T^T (dU X_V^T + dW X_K^T) T^T = -(dX_V U^T + dX_K W^T) = -(G1 + dX_K W^T),
-    // on bf16 MFMA with T and dX_K as high + low bf16 parts (16 significant bits).
-#pragma unroll
-    for (int u = 0; u < NK8; ++u) {
-        const int idx = tid + NTHR_C * u;
-        if (idx < C * DK / 8) *reinterpret_cast<uint4*>(&sW[idx / (DK / 8)][(idx % (DK / 8)) * 8]) = wv[u];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < M3; ++m) {
-        const int idx = w + NW * m;
-        if (idx < T3) {
-            const int ti = idx / (DK / 16), tj = idx % (DK / 16);
-            f32x4 acc = mma_kc<C>(zero4(), &sTTh[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
-            acc = mma_kc<C>(acc, &sTTl[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                const bf16 hi = f32_to_bf16(acc[r]);
-                sXh[i][j] = hi;
-                sXl[i][j] = f32_to_bf16(acc[r] - to_f32(hi));
-            }
-        }
-    }
-    __syncthreads();
-    {
-        // dX_K out (bf16), in place of dW
-        bf16* dXp = reinterpret_cast<bf16*>(dWgo) + (size_t)ch * C * DK;
-        for (int idx = tid; idx < C * DK / 8; idx += NTHR_C) {
-            const int r = idx / (DK / 8), c0 = (idx % (DK / 8)) * 8;
-            *reinterpret_cast<uint4*>(dXp + r * DK + c0) = *reinterpret_cast<const uint4*>(&sXh[r][c0]);
-        }
-    }
-    bf16* dAp = reinterpret_cast<bf16*>(dT1o) + (size_t)ch * C * C;
-#pragma unroll
-    for (int m = 0; m < M2; ++m) {
-        const int idx = w + NW * m;
-        if (idx < T2) {
-            const int ti = idx / NB, tj = idx % NB;
-            f32x4 acc = mma_kc<DK>(aT[m], &sXh[ti * 16][0], PK, &sW[tj * 16][0], PK);
-            acc = mma_kc<DK>(acc, &sXl[ti * 16][0], PK, &sW[tj * 16][0], PK);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                dAp[i * C + j] = f32_to_bf16(i > j ? -acc[r] : 0.f);
-            }
-        }
-    }
-    // dgam: the BW/4 threads of one state row hold its partial sums
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
+        // dgam: the BW/4 threads of one state row hold its partial sums
         static_assert(BW / 4 == 8, "eight threads per state row");
-        const float sgm = lane8_sum(dgm_part[q]);
-        const int idx = tid + NTHR_C * q;
-        if (idx < NS4 && (idx % (BW / 4)) == 0) dgmo[(size_t)ch * DK + idx / (BW / 4)] = sgm;
-    }
-    // dbeta part: row sums of dX_V o v over the 16 columns of each tile, then
-    // over the column tiles (fixed order)
-    for (int idx = tid; idx < NW * C; idx += NTHR_C) (&sred[0][0])[idx] = 0.f;
-    __syncthreads();
 #pragma unroll
-    for (int m = 0; m < MD; ++m) {
-        const int idx = w + NW * m;
-        if (idx < TD) {
-            const int ti = idx / (BW / 16);
+        for (int q = 0; q < QS; ++q) oG[q] = lane8_sum(dgm_part[q]);
+        // dbeta part: row sums of dX_V o v over the 16 columns of each tile, then
+        // over the column tiles (fixed order)
+        for (int idx = tid; idx < NW * C; idx += NTHR_C) (&sred[0][0])[idx] = 0.f;
+        __syncthreads();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float sb = lane16_sum(dbr[m][r]);
-                if (lr == 0) sred[w][ti * 16 + 4 * lq + r] = sb;
+        for (int m = 0; m < MD; ++m) {
+            const int idx = w + NW * m;
+            if (idx < TD) {
+                const int ti = idx / (BW / 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sb = lane16_sum(dbr[m][r]);
+                    if (lr == 0) sred[w][ti * 16 + 4 * lq + r] = sb;
+                }
             }
         }
+        __syncthreads();
+        static_assert(C <= NTHR_C, "one dbeta row per thread");
+        oB = 0.f;
+        if (tid < C)
+            for (int ww = 0; ww < NW; ++ww) oB += sred[ww][tid];
+        pch = ch;
+        ch += gridDim.x;
+        if (ch >= nch) break;
+        __syncthreads();  // the tail's LDS reads are done before the next chunk's writes
     }
-    __syncthreads();
-    for (int r = tid; r < C; r += NTHR_C) {
-        float sb = 0.f;
-        for (int ww = 0; ww < NW; ++ww) sb += sred[ww][r];
-        dbpo[(size_t)ch * C + r] = sb;
-    }
+    put_tail();
 }
 
 // Score gradients, decay chain rule and outputs, shared by both bchunk2
@@ -2077,7 +2138,9 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
         // the WY adjoint takes U = T X_V and W = T X_K as products: with clip the
         // unclipped copies (clipping is differentiated as the identity)
         const bool raw = p.clip > 0.f;
-        GDN_LAUNCH("bchunk1", (bchunk1b_kernel<C, DK, DV>), gch, dim3(NTHR_C), st, (const bf16*)v,
+        // persistent, one workgroup per CU (its LDS allows no second one)
+        const dim3 gp((unsigned)std::min<long long>(p.n_ch, device_cus()));
+        GDN_LAUNCH("bchunk1", (bchunk1b_kernel<C, DK, DV>), gp, dim3(NTHR_C), st, (const bf16*)v,
                    beta, (const bf16*)dO, (const bf16*)(ws + p.o_Dst),
                    (const float*)(ws + (raw ? p.o_Ur : p.o_U)), (const float*)(ws + p.o_Tm),
                    (const bf16*)(ws + (raw ? p.o_Wr : p.o_W)),
@@ -2085,7 +2148,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                    (const bf16*)(ws + p.o_dDt), (bf16*)dv, (float*)(ws + p.o_dQg),
                    (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh), (float*)(ws + p.o_dPs),
                    (float*)(ws + p.o_dT1), (float*)(ws + p.o_dgm), (float*)(ws + p.o_dbp), p.T, p.H,
-                   p.NC);
+                   p.NC, (int)p.n_ch);
     } else
     GDN_LAUNCH("bchunk1", (bchunk1_kernel<TIn, C, DK, DV, MT>), gch, dim3(NTHR), st,
                        (const TIn*)v, beta, (const TIn*)dO, (const float*)(ws + p.o_W),

@@ -1,6 +1,8 @@
 // chunk_common.h -- geometry and small device helpers of the chunked kernels.
 #pragma once
 
+#include <atomic>
+
 #include "common.h"
 #include "mma.h"
 
@@ -175,6 +177,22 @@ __global__ void __launch_bounds__(256) safe_pass_kernel(SafeSegs segs)
     if (sg.n == 0) return;
     if (sg.bf16) safe_seg<bf16>(sg, segs.clip);
     else safe_seg<float>(sg, segs.clip);
+}
+
+// Compute units of the current device, cached per device: the grid of a
+// persistent kernel that keeps one workgroup per CU.  Only the grid size
+// depends on it (not the results); a failed query falls back to 256.
+inline int device_cus()
+{
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 // Launch one pass over `count` segments (no-op when nothing is asked for).
