@@ -723,13 +723,18 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         vw[u] = *reinterpret_cast<const uint4*>(v + tok0 * DV + (size_t)min(r, nvalid - 1) * H * DV + j0);
     }
 
-    // ---- scores out: Ps (bf16) and, for training, Ps^T; A (x beta) to LDS
+    // ---- scores out: Ps (bf16) and, for training, Ps^T; A (x beta) to LDS.
+    // Ps and Ps^T are staged in the level-table bytes (free after the score
+    // products) and leave as whole rows, 16 bytes per thread
+    bf16 (*sPs)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);
+    bf16 (*sPsT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + C * PT * 2);
+    static_assert(2 * C * PT * 2 <= SBUF, "staged Ps and Ps^T fit the level-table bytes");
     bf16* Psc = Psb + (size_t)ch * C * C;
     bf16* PsTc = PsTb + (size_t)ch * C * C;
     auto put_ps = [&](int i0, int j, const float (&pv)[4]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Psc[(i0 + r) * C + j] = f32_to_bf16(pv[r]);
-        if (bwdt) *reinterpret_cast<uint2*>(&PsTc[j * C + i0]) = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+        for (int r = 0; r < 4; ++r) sPs[i0 + r][j] = f32_to_bf16(pv[r]);
+        if (bwdt) *reinterpret_cast<uint2*>(&sPsT[j][i0]) = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
     };
     if (w >= NB) {
 #pragma unroll
@@ -762,11 +767,18 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     for (int idx = tid; idx < C * C; idx += NTHR_P) {
         const int i = idx / C, j = idx % C;
         if (i / 16 < j / 16) {
-            Psc[idx] = f32_to_bf16(0.f);
-            if (bwdt) PsTc[j * C + i] = f32_to_bf16(0.f);
+            sPs[i][j] = f32_to_bf16(0.f);
+            if (bwdt) sPsT[j][i] = f32_to_bf16(0.f);
             sA[i][j] = 0.f;
         }
     }
+    __syncthreads();  // staged Ps rows complete
+    for (int idx = tid; idx < C * C / 8; idx += NTHR_P) {
+        const int r = idx / (C / 8), c0 = (idx % (C / 8)) * 8;
+        *reinterpret_cast<uint4*>(&Psc[r * C + c0]) = *reinterpret_cast<const uint4*>(&sPs[r][c0]);
+        if (bwdt) *reinterpret_cast<uint4*>(&PsTc[r * C + c0]) = *reinterpret_cast<const uint4*>(&sPsT[r][c0]);
+    }
+    __syncthreads();  // the staged Ps rows are read: Qg and Kh take their bytes
 
     // ---- Gamma, Kh factor, gam: Qg, Kh outputs and X_K^T = (beta K o Gamma)^T.
     // Qg and Kh rows are staged in the level-table bytes (free after the score
