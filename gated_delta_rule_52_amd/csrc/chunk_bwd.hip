@@ -720,7 +720,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     constexpr int NK8 = (C * DK / 8 + NTHR_C - 1) / NTHR_C;
     float4 tv[NT4];
     float bv0;
-    uint4 wv[NK8];  // W rows (bf16) for the keys' WY adjoint after the Dv loop
+    u32x4 wv[NK8];  // W rows (bf16) for the keys' WY adjoint after the Dv loop
     auto prologue_loads = [&](int c) {
         const size_t tb = fetch_from(c);
         fetch(0);
@@ -731,7 +731,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         const bf16* Wp = Wbi + (size_t)c * C * DK;
 #pragma unroll
         for (int u = 0; u < NK8; ++u)
-            wv[u] = *reinterpret_cast<const uint4*>(Wp + 8 * min(tid + NTHR_C * u, C * DK / 8 - 1));
+            wv[u] = *reinterpret_cast<const u32x4*>(Wp + 8 * min(tid + NTHR_C * u, C * DK / 8 - 1));
     };
     prologue_loads(blockIdx.x);
 
@@ -740,7 +740,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // store issued after the prefetch would be waited for with it (the memory
     // counter completes in issue order)
     constexpr int NX8 = (C * DK / 8 + NTHR_C - 1) / NTHR_C;
-    uint4 oX[NX8];
+    u32x4 oX[NX8];
     float oA[M2][4], oG[QS], oB;
     int pch = -1;
     auto put_tail = [&]() {
@@ -748,7 +748,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 #pragma unroll
         for (int u = 0; u < NX8; ++u) {
             const int idx = tid + NTHR_C * u;
-            if (idx < C * DK / 8) *reinterpret_cast<uint4*>(dXp + idx * 8) = oX[u];
+            if (idx < C * DK / 8) *reinterpret_cast<u32x4*>(dXp + idx * 8) = oX[u];
         }
         bf16* dAp = reinterpret_cast<bf16*>(dT1o) + (size_t)pch * C * C;
 #pragma unroll
@@ -911,7 +911,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 #pragma unroll
         for (int u = 0; u < NK8; ++u) {
             const int idx = tid + NTHR_C * u;
-            if (idx < C * DK / 8) *reinterpret_cast<uint4*>(&sW[idx / (DK / 8)][(idx % (DK / 8)) * 8]) = wv[u];
+            if (idx < C * DK / 8) *reinterpret_cast<u32x4*>(&sW[idx / (DK / 8)][(idx % (DK / 8)) * 8]) = wv[u];
         }
         __syncthreads();
         // the next chunk's prologue loads, in flight through the tail (the last
@@ -937,7 +937,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 #pragma unroll
         for (int u = 0; u < NX8; ++u) {  // dX_K (bf16) rows, stored in place of dW
             const int idx = min(tid + NTHR_C * u, C * DK / 8 - 1);
-            oX[u] = *reinterpret_cast<const uint4*>(&sXh[idx / (DK / 8)][(idx % (DK / 8)) * 8]);
+            oX[u] = *reinterpret_cast<const u32x4*>(&sXh[idx / (DK / 8)][(idx % (DK / 8)) * 8]);
         }
 #pragma unroll
         for (int m = 0; m < M2; ++m) {

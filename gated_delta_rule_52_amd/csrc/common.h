@@ -84,6 +84,9 @@ __device__ __forceinline__ float lane16_sum(float x)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+// 16 bytes as a native vector: unlike HIP's uint4 (a struct copied with
+// memcpy), an array of these stays in registers when it is held across loops
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c)
 {
