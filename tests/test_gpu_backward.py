@@ -85,19 +85,20 @@ def test_weak_decay_gradients(dtype, decay):
     compare(got, ref, TOL[dtype], f"weak decay {dtype} {decay}")
 
 
-@pytest.mark.parametrize("decay", ["channel", "head"])
-def test_more_chunk_heads_than_workgroups(decay):
+@pytest.mark.parametrize("decay,D", [("channel", 128), ("head", 128), ("channel", 64)])
+def test_more_chunk_heads_than_workgroups(decay, D):
     """B=3 T=1000 H=6: 288 chunk-heads (more than the chip has CUs) with a
     ragged last chunk, so the persistent backward kernel takes several
     chunk-heads per workgroup, loading each next one during the tail of the
-    one before; weak decay lets the chunk-start states weigh in."""
-    log(f"more chunk-heads than workgroups, bf16 {decay}")
-    inp = gi.make_inputs(3, 1000, 6, 128, 128, decay=decay, dtype="bf16", seed=37, h0_std=0.1,
+    one before; weak decay lets the chunk-start states weigh in.  At 64x64
+    the Dv loop is one prefetching tile and the last."""
+    log(f"more chunk-heads than workgroups, bf16 {decay} D={D}")
+    inp = gi.make_inputs(3, 1000, 6, D, D, decay=decay, dtype="bf16", seed=37, h0_std=0.1,
                          grads=True, g_scale=0.01)
     inp["meta"]["chunk"] = 64
     got = gpu_backward(inp)
     ref = oracle.backward_inputs(inp)
-    compare(got, ref, TOL["bf16"], f"many chunk-heads {decay}")
+    compare(got, ref, TOL["bf16"], f"many chunk-heads {decay} D={D}")
 
 
 def test_no_h0_no_dhT():
