@@ -1497,15 +1497,21 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
 
     float a[RPP], qv[RPP], kv[RPP], Gm[RPP];
     float dq[RPP], dk[RPP], dG[RPP], dbr[RPP];
+    // token-row offsets from the chunk's first row: 32-bit (rsK * C < 2^31)
+    const uint32_t rs32 = (uint32_t)rsK;
+    const bf16* qb = q + tok0 * DK;
+    const bf16* kb = k + tok0 * DK;
+    const float* gb = PCH ? g + tok0 * DK : g + tok0;
 #pragma unroll
     for (int i = 0; i < RPP; ++i) {
         const int r = p0 + i;
         // rows past the end read the last valid row (all loads unconditional)
         // and are then replaced by g = q = k = 0
-        const int rr = min(r, nvalid - 1);
-        const float gx = PCH ? g[(tok0 + (size_t)rr * H) * DK + c] : g[tok0 + (size_t)rr * H];
-        const float qx = to_f32(q[tok0 * DK + rr * rsK + c]);
-        const float kx = to_f32(k[tok0 * DK + rr * rsK + c]);
+        const uint32_t rr = (uint32_t)min(r, nvalid - 1);
+        const uint32_t off = rr * rs32 + (uint32_t)c;
+        const float gx = PCH ? ld32(gb, off) : ld32(gb, rr * (uint32_t)H);
+        const float qx = to_f32(ld32(qb, off));
+        const float kx = to_f32(ld32(kb, off));
         const bool ok = cp && r < nvalid;
         a[i] = ok ? gx : 0.f;  // log-decay until the table loads are out
         qv[i] = ok ? qx : 0.f;
@@ -1516,13 +1522,15 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     // (two bf16 per word); used after the first barrier
     uint32_t hQ[RPP / 2], hK[RPP / 2], hX[RPP / 2];
     {
-        const size_t e0 = (size_t)ch * C * DK + c;
+        const bf16* hQb = dQgi + (size_t)ch * C * DK;
+        const bf16* hKb = dKhi + (size_t)ch * C * DK;
+        const bf16* hXb = dXKi + (size_t)ch * C * DK;
 #pragma unroll
         for (int i = 0; i < RPP; i += 2) {
-            const size_t a0 = e0 + (size_t)(p0 + i) * DK, a1 = a0 + DK;
-            hQ[i / 2] = (uint32_t)dQgi[a0].bits | ((uint32_t)dQgi[a1].bits << 16);
-            hK[i / 2] = (uint32_t)dKhi[a0].bits | ((uint32_t)dKhi[a1].bits << 16);
-            hX[i / 2] = (uint32_t)dXKi[a0].bits | ((uint32_t)dXKi[a1].bits << 16);
+            const uint32_t a0 = (uint32_t)((p0 + i) * DK + c), a1 = a0 + DK;
+            hQ[i / 2] = (uint32_t)ld32(hQb, a0).bits | ((uint32_t)ld32(hQb, a1).bits << 16);
+            hK[i / 2] = (uint32_t)ld32(hKb, a0).bits | ((uint32_t)ld32(hKb, a1).bits << 16);
+            hX[i / 2] = (uint32_t)ld32(hXb, a0).bits | ((uint32_t)ld32(hXb, a1).bits << 16);
         }
     }
     auto hw = [](const uint32_t* h, int i) {
@@ -1936,9 +1944,10 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             dG[i] += add;
             sR[r][cl] = dbr[i];
             if (r < nvalid) {
-                dqo[tok0 * DK + r * rsK + c] = f32_to_bf16(dq[i]);
-                dko[tok0 * DK + r * rsK + c] = f32_to_bf16(dk[i]);
-                if (PCH) dgo[(tok0 + (size_t)r * H) * DK + c] = dG[i];
+                const uint32_t off = (uint32_t)r * rs32 + (uint32_t)c;
+                st32(dqo + tok0 * DK, off, f32_to_bf16(dq[i]));
+                st32(dko + tok0 * DK, off, f32_to_bf16(dk[i]));
+                if (PCH) st32(dgo + tok0 * DK, off, dG[i]);
             }
         }
     }

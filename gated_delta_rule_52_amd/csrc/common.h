@@ -47,6 +47,19 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return f32
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Element `off` of a workgroup-uniform base pointer, with the byte offset
+// formed in 32 bits: the access then takes the scalar base plus a 32-bit lane
+// offset, instead of a 64-bit address computed per lane.  The caller
+// guarantees off * sizeof(T) < 2^32.
+template <typename T> __device__ __forceinline__ T ld32(const T* base, uint32_t off)
+{
+    return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off * (uint32_t)sizeof(T));
+}
+template <typename T> __device__ __forceinline__ void st32(T* base, uint32_t off, T x)
+{
+    *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off * (uint32_t)sizeof(T)) = x;
+}
+
 // Lane sums inside a DPP row (16 lanes) by DPP moves, which stay in the VALU
 // instead of a round trip through the LDS crossbar (ds_bpermute).  Every lane
 // of a group receives the group's sum, bitwise equal across the group.  All 16

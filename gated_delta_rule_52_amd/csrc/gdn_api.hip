@@ -63,6 +63,10 @@ static gdn_status check_shape(const gdn_shape* sh, bool decode)
         const int C = sh->chunk ? sh->chunk : 64;
         if (C != 16 && C != 64) return GDN_ERR_UNSUPPORTED;
         if (!plan_supported(sh->Dk, sh->Dv, C)) return GDN_ERR_UNSUPPORTED;
+        // a chunk's token rows are addressed with 32-bit offsets from its first
+        // row (H * max(Dk, Dv) elements per token row, C rows)
+        const long long D = sh->Dk > sh->Dv ? sh->Dk : sh->Dv;
+        if ((long long)sh->H * D * C > (1LL << 28)) return GDN_ERR_UNSUPPORTED;
     }
     return GDN_OK;
 }

@@ -53,8 +53,10 @@ def test_workspace_query():
     assert 0 < fwd < bwd
     assert fwd % 256 == 0 and bwd % 256 == 0
     for bad in (dict(Dk=100, Dv=100), dict(chunk=32), dict(B=0), dict(dtype=7), dict(decay=3),
-                dict(Dk=64, Dv=128), dict(qk_l2norm=2)):
+                dict(Dk=64, Dv=128), dict(qk_l2norm=2), dict(H=32769)):
         assert L.gdn_workspace_bytes(ctypes.byref(_shape(**bad)), 0) == 0, bad
+    # the largest head count a chunk's 32-bit row offsets allow at 128 x 128
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(B=1, T=64, H=32768)), 0) > 0
     # use_qk_l2norm adds the per-row scale table [chunk-heads][2][C] fp32 to both sizes
     sh_n = _shape(qk_l2norm=1)
     n_ch = 2 * 3 * 2
