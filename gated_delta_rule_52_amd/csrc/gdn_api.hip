@@ -67,6 +67,8 @@ static gdn_status check_shape(const gdn_shape* sh, bool decode)
         // row (H * max(Dk, Dv) elements per token row, C rows)
         const long long D = sh->Dk > sh->Dv ? sh->Dk : sh->Dv;
         if ((long long)sh->H * D * C > (1LL << 28)) return GDN_ERR_UNSUPPORTED;
+        // chunk-heads are counted in 32-bit ints (grids, persistent loops)
+        if ((long long)sh->B * sh->H * ((sh->T + C - 1) / C) > 0x7FFFFFFFLL) return GDN_ERR_UNSUPPORTED;
     }
     return GDN_OK;
 }

@@ -47,8 +47,8 @@
  * any T >= 0 (a ragged last chunk is processed as if padded with tokens that
  * have g = 0 and beta = 0, which leave the state exactly unchanged; their
  * outputs are not written); B, H >= 1, and for chunked calls
- * H * max(Dk, Dv) * chunk <= 2^28 (H <= 32768 at 128 x 128).  Anything else:
- * GDN_ERR_UNSUPPORTED.
+ * H * max(Dk, Dv) * chunk <= 2^28 (H <= 32768 at 128 x 128) and
+ * B * H * ceil(T / chunk) < 2^31.  Anything else: GDN_ERR_UNSUPPORTED.
  */
 #ifndef GDN_H
 #define GDN_H
