@@ -156,26 +156,129 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True, l2n=False)
     return by * n, {k_: v_ * n for k_, v_ in fl.items()}
 
 
-def roofline(name, dur_s, B, T, H, C, D, in_bytes, l2n=False):
-    """Lower bound on one launch's duration from its algorithmic work at the
-    published peaks; the largest term names the bound."""
-    by, fl = kernel_work(name, B, T, H, C, D, D, in_bytes, l2n=l2n)
-    terms = {"hbm": by / (PEAK_HBM_GBS * 1e9)}
+# The method's own work per token-head (one token of one head), as the layer's
+# inputs are read once and its outputs written once: q, k, v, g, beta, o in the
+# forward; q, k, v, g, beta, dO in and dq, dk, dv, dg, dbeta out in the backward.
+# bf16 inputs at 128 x 128 with per-channel decay: 1,540 B forward, 2,824 B
+# backward, 4,364 B forward + backward; fp32 inputs: 2,564, 4,616, 7,180 B.  The
+# chunk tables, chunk-start states and gradients handed between kernels are this
+# design's choice, not the method's, and are not counted.  Matrix-product work of
+# the chunked form per chunk of 64 tokens of one head (Dk = Dv = 128): forward
+# 8.52 MFLOP (cross-block scores 0.52, T21 merge 0.13, U and W 1.05, scan 6.82),
+# backward about 17.2 MFLOP.
+def method_bytes_per_token_head(name, D, in_bytes, per_channel=True):
+    """Share of the layer's own inputs and outputs that kernel `name` must move
+    per token-head (each input it reads once, each output it writes once).
+    Summing over the kernels counts an input read by two kernels twice; the
+    step totals use method_step_bytes."""
+    ib, gb = in_bytes, (D * 4 if per_channel else 4)
+    return {"prep": 3 * D * ib + gb + 4, "prep_T": 3 * D * ib + gb + 4,
+            "scan": D * ib, "scan_train": D * ib, "scan_save": 0,
+            "bscan": D * ib,                                   # dO
+            "bchunk1": 3 * D * ib + 4,                         # v, dO, beta in; dv out
+            "bchunk2": 4 * D * ib + 2 * gb + 4,                # q, k, g, beta in; dq, dk, dg out
+            "bchunk2_finish": 4,                               # dbeta out
+            "l2norm_bwd": 4 * D * ib}.get(name)
+
+
+def method_step_bytes(D, in_bytes, per_channel=True, backward=True):
+    """The method's bytes per token-head for a forward (or forward + backward)
+    pass: each input of the pass read once, each output written once."""
+    ib, gb = in_bytes, (D * 4 if per_channel else 4)
+    fwd = 3 * D * ib + gb + 4 + D * ib
+    bwd = (3 * D * ib + gb + 4 + D * ib) + (3 * D * ib + gb + 4)
+    return fwd + bwd if backward else fwd
+
+
+METHOD_MFLOP_PER_CHUNK_HEAD = {"fwd": 0.52 + 0.13 + 1.05 + 6.82, "bwd": 17.2}
+
+
+def roofline(name, dur_s, B, T, H, C, D, in_bytes, l2n=False, per_channel=True):
+    """Roofline of one launch.  achieved = the method's bytes for this kernel
+    (method_bytes_per_token_head x the B*T*H token-heads of one launch) over
+    the launch's duration; the bound is the larger of that byte floor at the
+    HBM peak and the kernel's matrix-product work at the dense MFMA peak of its
+    operand type.  The bytes this design moves (chunk tables, hand-offs) are
+    reported beside it as design_bytes_per_launch and frac_design."""
+    units = B * T * H
+    mb = method_bytes_per_token_head(name, D, in_bytes, per_channel) * units
+    by, fl = kernel_work(name, B, T, H, C, D, D, in_bytes, per_channel=per_channel, l2n=l2n)
+    terms = {"hbm": mb / (PEAK_HBM_GBS * 1e9)}
     for mt, f in fl.items():
         if f:
             terms["mfma_" + mt] = f / (PEAK_TFLOPS[mt] * 1e12)
     bound = max(terms, key=terms.get)
     if bound == "hbm":
-        r = {"bound": "hbm", "achieved": by / dur_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        r = {"bound": "hbm", "achieved": mb / dur_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
         mt = bound[5:]
         r = {"bound": "mfma", "achieved": fl[mt] / dur_s / 1e12, "peak": PEAK_TFLOPS[mt],
              "unit": "TFLOP/s", "mfma_dtype": mt}
     r["frac"] = r["achieved"] / r["peak"]
     r["floor_us"] = {k_: v_ * 1e6 for k_, v_ in terms.items()}
-    r["algorithmic_bytes_per_launch"] = by
-    r["algorithmic_flops_per_launch"] = fl
+    r["method_bytes_per_token_head"] = mb / units
+    r["token_heads_per_launch"] = units
+    r["method_bytes_per_launch"] = mb
+    r["design_bytes_per_launch"] = by
+    r["frac_design"] = by / dur_s / 1e9 / PEAK_HBM_GBS
+    r["mfma_flops_per_launch"] = fl
     return r
+
+
+def step_roofline(ms, B, T, H, C, D, in_bytes, backward=True, per_channel=True):
+    """The whole pass against the method's floor: bytes (each input read once,
+    each output written once) at the HBM peak, and the chunked form's
+    matrix-product flops at the dense MFMA peak of the operand type."""
+    units = B * T * H
+    by = method_step_bytes(D, in_bytes, per_channel, backward) * units
+    n_ch = B * H * ((T + C - 1) // C)
+    mflop = METHOD_MFLOP_PER_CHUNK_HEAD["fwd"] + (METHOD_MFLOP_PER_CHUNK_HEAD["bwd"] if backward else 0.0)
+    fl = mflop * 1e6 * n_ch * (D / 128) ** 2
+    mt = "bf16" if in_bytes == 2 else "f32"
+    s = ms * 1e-3
+    return {"method_bytes_per_token_head": by / units, "method_bytes": by,
+            "achieved_GBs": by / s / 1e9, "frac_hbm": by / s / 1e9 / PEAK_HBM_GBS,
+            "hbm_floor_us": by / (PEAK_HBM_GBS * 1e9) * 1e6,
+            "mfma_flops": fl, "mfma_dtype": mt, "achieved_TFLOPs": fl / s / 1e12,
+            "frac_mfma": fl / s / 1e12 / PEAK_TFLOPS[mt],
+            "mfma_floor_us": fl / (PEAK_TFLOPS[mt] * 1e12) * 1e6,
+            "bound": "hbm" if by / PEAK_HBM_GBS / 1e9 >= fl / PEAK_TFLOPS[mt] / 1e12 else "mfma"}
+
+
+def parity_gate(checks):
+    """Refuse to report throughput when a correctness check failed (atomic_ops
+    card, "Reproduce": a row that does not match is rejected; Marin note,
+    "Single-device benchmark": results are checked before timing).  `checks`
+    maps a row name to its pass flag; on any failure the names go to stderr and
+    the process exits with status 3 before anything is printed on stdout."""
+    bad = [name for name, ok in checks.items() if not ok]
+    if bad:
+        print("bench.py: parity check failed for " + ", ".join(bad)
+              + "; no throughput is reported", file=sys.stderr, flush=True)
+        sys.exit(3)
+
+
+def emit(line, checks):
+    """Print the one JSON result line, only if every check in `checks` passed."""
+    parity_gate(checks)
+    print(json.dumps(line), flush=True)
+
+
+def median_sync_ms(fn, n=20):
+    """Median over n calls of fn, each between two synchronisations and timed
+    with events on the current stream (the Marin note's protocol: median of 20
+    synchronised calls)."""
+    import torch
+    times = []
+    for _ in range(n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return float(np.median(times))
 
 
 def graph_replay(fn, outs, args):
@@ -299,7 +402,7 @@ def main():
     log("[bench] correctness gate")
     grads = step()
     torch.cuda.synchronize()
-    pairs = [(0, 0), (B - 1, H - 1)]
+    pairs = [(0, 0), (B // 2 - 1, H // 2), (B // 2, 1), (B - 1, H - 1)]
 
     def pick(x, b, h):
         return x[b, :, h].float().cpu().numpy().astype(np.float64)
@@ -324,6 +427,8 @@ def main():
     tol = 2e-2 if dt == "bf16" else 1e-5
     parity_ok = all(e <= tol for e in par.values())
     log(f"[bench] parity (max rel err, tol {tol}): " + ", ".join(f"{k_} {e:.2e}" for k_, e in par.items()))
+    checks = {f"fwd+bwd B={B} {dt}": parity_ok}
+    parity_gate(checks)  # nothing is timed unless the headline workload is correct
 
     # ---- fwd+bwd: warmup, then exactly K timed steps
     for _ in range(args.warmup):
@@ -345,6 +450,8 @@ def main():
     per = {name: (float(np.mean(ms)), len(ms)) for name, ms in rec.by_kernel().items()}
     rec.close()
     log(f"[bench] fwd+bwd {ms_step:.3f} ms/step ({value / 1e6:.2f} M tokens/s); wall {wall:.3f} s")
+    med_step = median_sync_ms(step)
+    log(f"[bench] fwd+bwd median of 20 synchronised calls {med_step:.3f} ms")
     for name, (ms, cnt) in sorted(per.items(), key=lambda x: -x[1][0] * x[1][1]):
         log(f"[bench]   {name:8s} {ms * 1e3:9.1f} us x {cnt // args.steps}/step")
 
@@ -352,17 +459,20 @@ def main():
     dom = max(per, key=lambda n: per[n][0] * per[n][1])
     roof = roofline(dom, per[dom][0] * 1e-3, B, T, H, C, D, in_bytes)
     roof["traffic"] = measured_traffic(dom) if dt == "bf16" and B == 8 else None
+    roof["traffic_over_method_bytes"] = (roof["traffic"] / roof["method_bytes_per_launch"]
+                                         if roof["traffic"] else None)
     roof["kernel"] = dom
     roof["avg_launch_us"] = per[dom][0] * 1e3
     roof["launches_timed"] = per[dom][1]
-    others = {n: {"us": ms * 1e3, "bound": r["bound"], "frac": r["frac"]}
+    others = {n: {"us": ms * 1e3, "bound": r["bound"], "frac": r["frac"],
+                  "frac_design": r["frac_design"]}
               for n, (ms, _) in per.items()
               for r in [roofline(n, ms * 1e-3, B, T, H, C, D, in_bytes)]}
     log(f"[bench] dominant {dom}: {roof['achieved']:.0f} {roof['unit']} of {roof['peak']:.0f} "
         f"({100 * roof['frac']:.1f}%, {roof['bound']}-bound); traffic {roof['traffic']}")
 
     # ---- forward only
-    ms_fwd = fwd_tps = None
+    ms_fwd = fwd_tps = med_fwd = None
     fwd_kernels = fwd_graph = None
     if not args.no_fwd:
         for _ in range(3):
@@ -379,7 +489,9 @@ def main():
         frec.close()
         ms_fwd = ev0.elapsed_time(ev1) / args.steps
         fwd_tps = B * T / (ms_fwd * 1e-3)
-        log(f"[bench] fwd {ms_fwd:.3f} ms ({fwd_tps / 1e6:.2f} M tokens/s)")
+        med_fwd = median_sync_ms(fwd)
+        log(f"[bench] fwd {ms_fwd:.3f} ms ({fwd_tps / 1e6:.2f} M tokens/s); median of 20 "
+            f"synchronised calls {med_fwd:.3f} ms")
         if not args.no_graph:
             fwd_graph = graph_replay(fwd, (o, hT), args)
             fwd_graph["tokens_per_s"] = B * T / (fwd_graph["ms_per_step"] * 1e-3)
@@ -468,6 +580,8 @@ def main():
                "kernels_avg_us": vker,
                "dominant_kernel_roofline": dict(roofline(vdom, vker[vdom] * 1e-6, vB, T, H, C, D,
                                                          vin_bytes), kernel=vdom),
+               "step_roofline": step_roofline(vms, vB, T, H, C, D, vin_bytes),
+               "fwd_roofline": step_roofline(vfms, vB, T, H, C, D, vin_bytes, backward=False),
                "parity_max_rel_err": vpar, "parity_ok": all(e <= vtol for e in vpar.values())}
         log(f"[bench] {label}: fwd+bwd {vms:.3f} ms, fwd {vfms:.3f} ms, parity ok {res['parity_ok']}")
         del vws_f, vws_b
@@ -478,6 +592,8 @@ def main():
         other = "f32" if dt == "bf16" else "bf16"
         variants = {other: variant(other, B, f"{other} inputs"),
                     f"B{B // 2}": variant(dt, B // 2, f"B={B // 2}")}
+        for key, res in variants.items():
+            checks[f"variant {key}"] = res["parity_ok"]
 
     # ---- per-head decay (one log-decay per token and head) at the same shape
     head = None
@@ -532,6 +648,7 @@ def main():
                 "fwd_tokens_per_s": B * T / (hfwd * 1e-3), "fwd_ms": hfwd,
                 "kernels_avg_us": hker, "parity_max_rel_err": hpar,
                 "parity_ok": all(e <= tol for e in hpar.values())}
+        checks["per-head decay"] = head["parity_ok"]
         log(f"[bench] per-head: fwd+bwd {hms:.3f} ms ({head['fwdbwd_tokens_per_s'] / 1e6:.2f} M tokens/s), "
             f"fwd {hfwd:.3f} ms; parity " + ", ".join(f"{k_} {e:.1e}" for k_, e in hpar.items()))
         log("[bench] per-head kernels: " + ", ".join(f"{n} {u:.0f} us" for n, u in hker.items()))
@@ -593,6 +710,7 @@ def main():
               "fwd_tokens_per_s": B * T / (lfwd * 1e-3), "fwd_ms": lfwd,
               "kernels_avg_us": lker, "l2norm_bwd_frac_hbm_peak": lroof["frac"],
               "parity_max_rel_err": lpar, "parity_ok": all(e <= tol for e in lpar.values())}
+        checks["use_qk_l2norm"] = l2["parity_ok"]
         log(f"[bench] use_qk_l2norm: fwd+bwd {lms:.3f} ms ({l2['fwdbwd_tokens_per_s'] / 1e6:.2f} M tokens/s), "
             f"fwd {lfwd:.3f} ms; parity " + ", ".join(f"{k_} {e:.1e}" for k_, e in lpar.items()))
         log("[bench] use_qk_l2norm kernels: " + ", ".join(f"{n} {u:.0f} us" for n, u in lker.items())
@@ -639,6 +757,7 @@ def main():
                   "fwdbwd_tokens_per_s": B * T / (sms * 1e-3), "ms_per_step": sms,
                   "kernels_avg_us": sker, "launches_per_step": scnt, "diag_counts": counts,
                   "parity_max_rel_err_fwd": spar, "parity_ok": all(e <= tol for e in spar.values())}
+        checks["safety options"] = safety["parity_ok"]
         log(f"[bench] safety options: fwd+bwd {sms:.3f} ms ({safety['fwdbwd_tokens_per_s'] / 1e6:.2f} M tokens/s); "
             f"fwd parity vs chunked oracle " + ", ".join(f"{k_} {e:.1e}" for k_, e in spar.items())
             + f"; counts {counts}")
@@ -655,9 +774,25 @@ def main():
             steps_in.append(tuple(torch.from_numpy(np.ascontiguousarray(dinp[n][:, t])).cuda()
                                   for n in ("q", "k", "v", "g", "beta")))
         od = torch.empty((Bd, 1, Hd, D), dtype=torch.float32, device="cuda")
+        o_steps = []
         for t in range(8):
             gdn.gdn_decode_step(*steps_in[t], state, o=od)
+            o_steps.append(od.clone())
         torch.cuda.synchronize()
+        # correctness: the 8 steps against the oracle's forward over the same 8
+        # tokens from the same h0, on sampled (batch, head) pairs
+        dp = [(0, 0), (97, 5), (Bd - 1, Hd - 1)]
+        dsub = {n: np.stack([dinp[n][b, :, h] for b, h in dp], axis=1)[None]
+                for n in ("q", "k", "v", "g", "beta")}
+        dh0 = np.stack([dinp["h0"][b, h] for b, h in dp])[None]
+        do_ref, dh_ref = oracle.forward(dsub["q"], dsub["k"], dsub["v"], dsub["g"], dsub["beta"],
+                                        scale, h0=dh0)
+        do_got = np.stack([np.stack([o_steps[t][b, 0, h].cpu().numpy() for t in range(8)])
+                           for b, h in dp], axis=1)[None]
+        dh_got = np.stack([state[b, h].cpu().numpy() for b, h in dp])[None]
+        dpar = {"o": rel(do_got, do_ref), "state": rel(dh_got, dh_ref)}
+        checks["decode"] = all(e <= 1e-5 for e in dpar.values())
+        log(f"[bench] decode parity after 8 steps: o {dpar['o']:.1e}, state {dpar['state']:.1e}")
         nd = 64
         drec = LaunchRecorder(nd)
         ev0.record()
@@ -675,7 +810,8 @@ def main():
                   "tokens_per_s": Bd / (ms_dec * 1e-3),
                   "achieved_GBs": dbytes / (kdec * 1e-3) / 1e9,
                   "frac_hbm_peak": dbytes / (kdec * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                  "algorithmic_bytes_per_step": dbytes}
+                  "algorithmic_bytes_per_step": dbytes,
+                  "parity_max_rel_err_8_steps": dpar}
         log(f"[bench] decode {kdec * 1e3:.1f} us/step, {decode['achieved_GBs']:.0f} GB/s")
 
         # the same decode from a checkpoint plus a buffer of recent tokens: a step
@@ -719,32 +855,78 @@ def main():
                 "achieved_GBs": rbytes / (krep * 1e-3) / 1e9,
                 "frac_hbm_peak": rbytes / (krep * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "state_rel_diff_vs_decode_after_8": agree}
+            checks[f"replay depth {depth}"] = agree <= 1e-5
             log(f"[bench] replay decode depth {depth}: {krep * 1e3:.1f} us/step "
                 f"({kdec / krep:.2f}x the decode step), {replay[f'depth{depth}']['achieved_GBs']:.0f} GB/s "
                 f"algorithmic; state vs decode {agree:.1e}")
         decode["replay"] = replay
 
-    # ---- CPU oracle on this host: the same workload (every (batch, head)
-    # sequence unless that would take much longer than ~30 s of wall time)
+    # ---- CPU oracle on this host: the token-serial reference as it stands
+    # (float64, and its float32 instantiation), OpenMP over the (batch, head)
+    # sequences, on the same inputs widened exactly from the device's bits;
+    # each figure the median of 3 runs
     cpu = None
     if not args.no_cpu:
         nthr = oracle.max_threads()
-        nh = min(B * H, 8 * nthr)
-        pairs = [(i // H, i % H) for i in range(nh)]
-        s = {n: np.stack([inp[n][b, :, h] for b, h in pairs], axis=1)[None]
-             for n in ("q", "k", "v", "g", "beta", "dO")}
-        s = {n: (x if x.dtype != np.uint16 else gi.as_f64(x)) for n, x in s.items()}
-        s = {n: np.ascontiguousarray(x, dtype=np.float64) for n, x in s.items()}
-        s["dhT"] = np.stack([inp["dhT"][b, h] for b, h in pairs])[None].astype(np.float64)
-        log(f"[bench] cpu oracle: {nh} heads x {T} tokens fwd+bwd on {nthr} threads")
-        t0 = time.perf_counter()
-        oracle.forward(s["q"], s["k"], s["v"], s["g"], s["beta"], scale)
-        oracle.backward(s["q"], s["k"], s["v"], s["g"], s["beta"], scale, s["dO"], dhT=s["dhT"])
-        tc = time.perf_counter() - t0
-        cpu = {"value": (nh / H) * T / tc, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
-               "sample": f"{nh} of {B * H} (batch, head) sequences of T={T}, fwd+bwd, float64 "
-                         f"token-serial, inputs widened from {dt}; tokens = heads/H*T; {tc:.1f} s"}
-        log(f"[bench] cpu oracle {cpu['value']:.0f} tokens/s in {tc:.1f} s")
+
+        def f64(x):
+            return np.ascontiguousarray(gi.as_f64(x))
+
+        def med3(fn):
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                fn()
+                ts.append(time.perf_counter() - t0)
+            return float(np.median(ts))
+
+        s = {n: f64(inp[n]) for n in ("q", "k", "v", "g", "beta", "dO", "dhT")}
+        s32 = {n: x.astype(np.float32) for n, x in s.items()}
+        log(f"[bench] cpu oracle: B={B} T={T} H={H} fwd and fwd+bwd, float64 and float32, "
+            f"{nthr} threads, median of 3")
+        t_fwd = med3(lambda: oracle.forward(s["q"], s["k"], s["v"], s["g"], s["beta"], scale))
+        t_fb = med3(lambda: (oracle.forward(s["q"], s["k"], s["v"], s["g"], s["beta"], scale),
+                             oracle.backward(s["q"], s["k"], s["v"], s["g"], s["beta"], scale,
+                                             s["dO"], dhT=s["dhT"])))
+        t_fwd32 = med3(lambda: oracle.forward_f32(s32["q"], s32["k"], s32["v"], s32["g"],
+                                                  s32["beta"], scale))
+        t_fb32 = med3(lambda: (oracle.forward_f32(s32["q"], s32["k"], s32["v"], s32["g"],
+                                                  s32["beta"], scale),
+                               oracle.backward_f32(s32["q"], s32["k"], s32["v"], s32["g"],
+                                                   s32["beta"], scale, s32["dO"], dhT=s32["dhT"])))
+        del s, s32
+        # decode: 64 consecutive steps of the B=256 H=16 128x128 workload from its
+        # h0 (the oracle's forward over the 64 tokens is those 64 steps)
+        dci = gi.decode(steps=64)
+        sd = {n: f64(dci[n]) for n in ("q", "k", "v", "g", "beta", "h0")}
+        t_dec = med3(lambda: oracle.forward(sd["q"], sd["k"], sd["v"], sd["g"], sd["beta"], scale,
+                                            h0=sd["h0"]))
+        sd32 = {n: x.astype(np.float32) for n, x in sd.items()}
+        del sd
+        t_dec32 = med3(lambda: oracle.forward_f32(sd32["q"], sd32["k"], sd32["v"], sd32["g"],
+                                                  sd32["beta"], scale, h0=sd32["h0"]))
+        del sd32, dci
+        Bd = 256
+        cpu = {"value": B * T / t_fb, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+               "sample": (f"the whole workload: all {B * H} (batch, head) sequences of T={T}, "
+                          f"forward + backward (oracle.forward then oracle.backward, which "
+                          f"recomputes its states from 64-token checkpoints), float64 "
+                          f"token-serial, inputs widened exactly from {dt}; median of 3 runs "
+                          f"({t_fb:.2f} s); tokens = B*T"),
+               "os_cpu_count": os.cpu_count(), "omp_threads": nthr,
+               "fwd_tokens_per_s": B * T / t_fwd,
+               "f32_fwdbwd_tokens_per_s": B * T / t_fb32,
+               "f32_fwd_tokens_per_s": B * T / t_fwd32,
+               "decode_tokens_per_s": Bd * 64 / t_dec,
+               "f32_decode_tokens_per_s": Bd * 64 / t_dec32,
+               "seconds_median": {"fwdbwd": t_fb, "fwd": t_fwd, "decode64": t_dec,
+                                  "f32_fwdbwd": t_fb32, "f32_fwd": t_fwd32, "f32_decode64": t_dec32},
+               "decode_sample": "64 steps of B=256 H=16 Dk=Dv=128 per-channel decay from h0 "
+                                "(tokens = 256 per step)"}
+        log(f"[bench] cpu oracle (float64): fwd+bwd {cpu['value']:.0f} tokens/s, fwd "
+            f"{cpu['fwd_tokens_per_s']:.0f}, decode {cpu['decode_tokens_per_s']:.0f}; float32: "
+            f"fwd+bwd {cpu['f32_fwdbwd_tokens_per_s']:.0f}, fwd {cpu['f32_fwd_tokens_per_s']:.0f}, "
+            f"decode {cpu['f32_decode_tokens_per_s']:.0f}; {nthr} threads of {os.cpu_count()} cpus")
 
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -788,7 +970,12 @@ def main():
                    "(check replays bitwise equal to the eager calls)") if use_graph
                   else "eager library calls",
         "eager": eager,
+        "median_sync_ms": med_step,
+        "median_sync_tokens_per_s": B * T / (med_step * 1e-3),
+        "step_roofline": step_roofline(ms_step, B, T, H, C, D, in_bytes),
         "fwd_tokens_per_s": fwd_tps,
+        "fwd_median_sync_ms": med_fwd,
+        "fwd_roofline": step_roofline(ms_fwd, B, T, H, C, D, in_bytes, backward=False) if ms_fwd else None,
         "fwd_ms": ms_fwd,
         "fwd_timing": "HIP-graph replay of gdn_forward" if use_fgraph else "eager gdn_forward",
         "fwd_eager": fwd_eager,
@@ -805,8 +992,9 @@ def main():
         "safety_options": safety,
         "decode": decode,
         "cpu_baseline": cpu,
+        "parity_checks": checks,
     }
-    print(json.dumps(line), flush=True)
+    emit(line, checks)
 
 
 if __name__ == "__main__":

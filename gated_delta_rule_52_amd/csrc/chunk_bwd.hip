@@ -916,7 +916,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         __syncthreads();
         // the next chunk's prologue loads, in flight through the tail (the last
         // workgroup's final chunk repeats itself: loads stay unconditional)
-        prologue_loads(min(ch + (int)gridDim.x, nch - 1));
+        prologue_loads((int)min((long long)ch + gridDim.x, (long long)nch - 1));
 #pragma unroll
         for (int m = 0; m < M3; ++m) {
             const int idx = w + NW * m;
@@ -979,8 +979,8 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         if (tid < C)
             for (int ww = 0; ww < NW; ++ww) oB += sred[ww][tid];
         pch = ch;
+        if ((long long)ch + gridDim.x >= nch) break;
         ch += gridDim.x;
-        if (ch >= nch) break;
         __syncthreads();  // the tail's LDS reads are done before the next chunk's writes
     }
     put_tail();

@@ -962,7 +962,7 @@ __global__ void __launch_bounds__(NTHR)
 scan_kernel(const float* __restrict__ Wi, const float* __restrict__ Ui,
             const float* __restrict__ Qgi, const float* __restrict__ Khi,
             const float* __restrict__ Psi, const float* __restrict__ gami,
-            const float* __restrict__ h0, TIn* __restrict__ o, float* __restrict__ hT,
+            const float* h0, TIn* __restrict__ o, float* hT,
             float* __restrict__ Sst, int BH, int T, int H, int NC)
 {
     using G = Geo<C, DK, DV>;
@@ -1103,7 +1103,7 @@ __global__ void __launch_bounds__(NTHR_S)
 scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
              const bf16* __restrict__ KhTb, const bf16* __restrict__ Psb,
              const float* __restrict__ Ui, const float* __restrict__ gami,
-             const float* __restrict__ h0, bf16* __restrict__ o, float* __restrict__ hT,
+             const float* h0, bf16* __restrict__ o, float* hT,
              bf16* __restrict__ Sst, bf16* __restrict__ Dst, int BH, int T, int H, int NC)
 {
     constexpr int BV = 32, NS = DV / BV, NW = NTHR_S / 64;
@@ -1365,7 +1365,7 @@ __global__ void __launch_bounds__(NTHR_S)
 scan3_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
              const bf16* __restrict__ KhTb, const bf16* __restrict__ Psb,
              const float* __restrict__ Ui, const float* __restrict__ gami,
-             const float* __restrict__ h0, bf16* __restrict__ o, float* __restrict__ hT,
+             const float* h0, bf16* __restrict__ o, float* hT,
              int BH, int T, int H, int NC)
 {
     constexpr int BV = 32, NS = DV / BV, NW = NTHR_S / 64;

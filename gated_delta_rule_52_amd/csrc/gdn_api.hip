@@ -67,8 +67,12 @@ static gdn_status check_shape(const gdn_shape* sh, bool decode)
         // row (H * max(Dk, Dv) elements per token row, C rows)
         const long long D = sh->Dk > sh->Dv ? sh->Dk : sh->Dv;
         if ((long long)sh->H * D * C > (1LL << 28)) return GDN_ERR_UNSUPPORTED;
-        // chunk-heads are counted in 32-bit ints (grids, persistent loops)
-        if ((long long)sh->B * sh->H * ((sh->T + C - 1) / C) > 0x7FFFFFFFLL) return GDN_ERR_UNSUPPORTED;
+        // token-heads of the padded chunks: every launch of a chunked call has at
+        // most 32 work-items per token-head (the fp32 L2-normalisation adjoint;
+        // the chunk kernels take at most 512 per chunk-head of 64), so a grid's
+        // work-item count stays below 2^32 and chunk-head indices fit in int
+        if ((long long)sh->B * sh->H * ((sh->T + C - 1) / C) * C >= (1LL << 27))
+            return GDN_ERR_UNSUPPORTED;
     }
     return GDN_OK;
 }

@@ -48,7 +48,9 @@
  * have g = 0 and beta = 0, which leave the state exactly unchanged; their
  * outputs are not written); B, H >= 1, and for chunked calls
  * H * max(Dk, Dv) * chunk <= 2^28 (H <= 32768 at 128 x 128) and
- * B * H * ceil(T / chunk) < 2^31.  Anything else: GDN_ERR_UNSUPPORTED.
+ * B * H * ceil(T / chunk) * chunk < 2^27 (the token-heads of one call, the last
+ * chunk counted whole; the largest launch has 32 work-items per token-head).
+ * Anything else: GDN_ERR_UNSUPPORTED, before any launch.
  */
 #ifndef GDN_H
 #define GDN_H

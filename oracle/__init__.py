@@ -24,12 +24,23 @@ CFLAGS = ["-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-std=c11"
 _lib = None
 
 
+LIB_F32 = os.path.join(_HERE, "libgdn_oracle_f32.so")
+
+
 def build(force: bool = False, src: str = SRC, out: str = LIB, extra: tuple = ()) -> str:
-    """Compile the C oracle with gcc (host code only)."""
+    """Compile the C oracle with gcc (host code only).  Building the float64
+    library also builds its float32 instantiation (same source,
+    -DORACLE_REAL=float), which only the CPU-baseline timing uses."""
     if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
         tmp = out + ".tmp"
         subprocess.run(["gcc", *CFLAGS, *extra, src, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, out)
+    if out == LIB and src == SRC and not extra:
+        if force or not os.path.exists(LIB_F32) or os.path.getmtime(LIB_F32) < os.path.getmtime(src):
+            tmp = LIB_F32 + ".tmp"
+            subprocess.run(["gcc", *CFLAGS, "-DORACLE_REAL=float", src, "-o", tmp, "-lm"],
+                           check=True)
+            os.replace(tmp, LIB_F32)
     return out
 
 
@@ -63,6 +74,71 @@ def _ptr(x):
         return None
     assert x.dtype == np.float64 and x.flags.c_contiguous
     return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+_lib32 = None
+
+
+def load_f32():
+    """The float32 instantiation of the oracle (same source and entry points,
+    every value and operation in float32).  Timing use only: the float64
+    oracle is the reference."""
+    global _lib32
+    if _lib32 is None:
+        build()
+        L = ctypes.CDLL(LIB_F32)
+        fp = ctypes.POINTER(ctypes.c_float)
+        i = ctypes.c_int
+        L.oracle_forward.argtypes = [i, i, i, i, i, i, ctypes.c_float] + [fp] * 8 + [i]
+        L.oracle_forward.restype = i
+        L.oracle_backward.argtypes = [i, i, i, i, i, i, ctypes.c_float] + [fp] * 14 + [i]
+        L.oracle_backward.restype = i
+        _lib32 = L
+    return _lib32
+
+
+def _p32(x):
+    if x is None:
+        return None
+    assert x.dtype == np.float32 and x.flags.c_contiguous
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _f32(x):
+    if x is None:
+        return None
+    if x.dtype == np.uint16:  # bf16 bits
+        x = (x.astype(np.uint32) << 16).view(np.float32)
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def forward_f32(q, k, v, g, beta, scale, h0=None, nthreads: int = 0):
+    """forward() computed by the float32 instantiation; float32 results."""
+    L = load_f32()
+    q, k, v, g, beta, h0 = map(_f32, (q, k, v, g, beta, h0))
+    B, T, H, Dk, Dv, pc = _dims(q, v, g)
+    o = np.zeros((B, T, H, Dv), np.float32)
+    hT = np.zeros((B, H, Dk, Dv), np.float32)
+    if L.oracle_forward(B, T, H, Dk, Dv, pc, float(scale), _p32(q), _p32(k), _p32(v), _p32(g),
+                        _p32(beta), _p32(h0), _p32(o), _p32(hT), int(nthreads)):
+        raise ValueError("oracle_forward (float32): bad dimensions")
+    return o, hT
+
+
+def backward_f32(q, k, v, g, beta, scale, dO, h0=None, dhT=None, nthreads: int = 0):
+    """backward() computed by the float32 instantiation; float32 results."""
+    L = load_f32()
+    q, k, v, g, beta, h0, dO, dhT = map(_f32, (q, k, v, g, beta, h0, dO, dhT))
+    B, T, H, Dk, Dv, pc = _dims(q, v, g)
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+               dg=np.zeros_like(g), dbeta=np.zeros_like(beta),
+               dh0=np.zeros((B, H, Dk, Dv), np.float32))
+    if L.oracle_backward(B, T, H, Dk, Dv, pc, float(scale), _p32(q), _p32(k), _p32(v), _p32(g),
+                         _p32(beta), _p32(h0), _p32(dO), _p32(dhT), _p32(out["dq"]),
+                         _p32(out["dk"]), _p32(out["dv"]), _p32(out["dg"]), _p32(out["dbeta"]),
+                         _p32(out["dh0"]), int(nthreads)):
+        raise ValueError("oracle_backward (float32): bad dimensions")
+    return out
 
 
 def _f64(x):

@@ -31,13 +31,18 @@
  * r (g_hat - x_hat (x_hat . g_hat)), r = 1 / sqrt(sum(x^2) + eps).  The pages
  * name the option but not eps; 1e-6 is this oracle's reading.
  *
+ * Element type: `real`, float64 unless the file is compiled with
+ * -DORACLE_REAL=float, which gives the float32 instantiation of the same code
+ * (timed only, as a second CPU baseline; the float64 build is the reference).
+ * <tgmath.h> makes exp and sqrt follow the element type.
+ *
  * Layouts (row-major, contiguous):
  *   q, k [B,T,H,Dk]; v, o, dO [B,T,H,Dv]; beta [B,T,H];
  *   g [B,T,H,Dk] (per channel) or [B,T,H] (per head);
  *   h0, hT, dhT, dh0 [B,H,Dk,Dv].
  */
-#include <math.h>
 #include <stdlib.h>
+#include <tgmath.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -45,34 +50,39 @@
 
 #define CKPT 64
 
+#ifndef ORACLE_REAL
+#define ORACLE_REAL double
+#endif
+typedef ORACLE_REAL real;
+
 typedef struct {
     int B, T, H, Dk, Dv, per_channel;
-    double scale;
+    real scale;
 } dims;
 
 static size_t tok(const dims *d, int b, int t, int h) { return ((size_t)b * d->T + t) * d->H + h; }
 
 /* exp(g) for one token of one head into a[Dk] */
-static void decay_factors(const dims *d, const double *g, int b, int t, int h, double *a)
+static void decay_factors(const dims *d, const real *g, int b, int t, int h, real *a)
 {
     if (d->per_channel) {
-        const double *gp = g + tok(d, b, t, h) * d->Dk;
+        const real *gp = g + tok(d, b, t, h) * d->Dk;
         for (int i = 0; i < d->Dk; ++i) a[i] = exp(gp[i]);
     } else {
-        double e = exp(g[tok(d, b, t, h)]);
+        real e = exp(g[tok(d, b, t, h)]);
         for (int i = 0; i < d->Dk; ++i) a[i] = e;
     }
 }
 
 /* One token of the recurrence on S in place.  Optionally returns m and d. */
-static void step(const dims *d, double *S, const double *a, const double *kt, const double *vt,
-                 double bt, double *m, double *dd)
+static void step(const dims *d, real *S, const real *a, const real *kt, const real *vt,
+                 real bt, real *m, real *dd)
 {
     const int Dk = d->Dk, Dv = d->Dv;
     for (int i = 0; i < Dk; ++i)
         for (int j = 0; j < Dv; ++j) S[i * Dv + j] *= a[i];
     for (int j = 0; j < Dv; ++j) {
-        double s = 0.0;
+        real s = 0.0;
         for (int i = 0; i < Dk; ++i) s += kt[i] * S[i * Dv + j];
         m[j] = s;
     }
@@ -81,32 +91,32 @@ static void step(const dims *d, double *S, const double *a, const double *kt, co
         for (int j = 0; j < Dv; ++j) S[i * Dv + j] += kt[i] * dd[j];
 }
 
-static void read_out(const dims *d, const double *S, const double *qt, double *ot)
+static void read_out(const dims *d, const real *S, const real *qt, real *ot)
 {
     for (int j = 0; j < d->Dv; ++j) {
-        double s = 0.0;
+        real s = 0.0;
         for (int i = 0; i < d->Dk; ++i) s += qt[i] * S[i * d->Dv + j];
         ot[j] = d->scale * s;
     }
 }
 
-static void head_forward(const dims *d, int b, int h, const double *q, const double *k,
-                         const double *v, const double *g, const double *beta,
-                         const double *h0, double *o, double *hT)
+static void head_forward(const dims *d, int b, int h, const real *q, const real *k,
+                         const real *v, const real *g, const real *beta,
+                         const real *h0, real *o, real *hT)
 {
     const int Dk = d->Dk, Dv = d->Dv;
-    double *S = calloc((size_t)Dk * Dv, sizeof(double));
-    double *a = malloc(sizeof(double) * Dk), *m = malloc(sizeof(double) * Dv),
-           *dd = malloc(sizeof(double) * Dv);
+    real *S = calloc((size_t)Dk * Dv, sizeof(real));
+    real *a = malloc(sizeof(real) * Dk), *m = malloc(sizeof(real) * Dv),
+           *dd = malloc(sizeof(real) * Dv);
     const size_t sidx = ((size_t)b * d->H + h) * Dk * Dv;
-    if (h0) memcpy(S, h0 + sidx, sizeof(double) * Dk * Dv);
+    if (h0) memcpy(S, h0 + sidx, sizeof(real) * Dk * Dv);
     for (int t = 0; t < d->T; ++t) {
         const size_t r = tok(d, b, t, h);
         decay_factors(d, g, b, t, h, a);
         step(d, S, a, k + r * Dk, v + r * Dv, beta[r], m, dd);
         read_out(d, S, q + r * Dk, o + r * Dv);
     }
-    if (hT) memcpy(hT + sidx, S, sizeof(double) * Dk * Dv);
+    if (hT) memcpy(hT + sidx, S, sizeof(real) * Dk * Dv);
     free(S); free(a); free(m); free(dd);
 }
 
@@ -120,9 +130,9 @@ static void set_threads(int nthreads)
 }
 
 /* Forward over all (b, h).  h0 and hT may be NULL.  Returns 0, or -1 on bad dims. */
-int oracle_forward(int B, int T, int H, int Dk, int Dv, int per_channel, double scale,
-                   const double *q, const double *k, const double *v, const double *g,
-                   const double *beta, const double *h0, double *o, double *hT, int nthreads)
+int oracle_forward(int B, int T, int H, int Dk, int Dv, int per_channel, real scale,
+                   const real *q, const real *k, const real *v, const real *g,
+                   const real *beta, const real *h0, real *o, real *hT, int nthreads)
 {
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
     dims d = {B, T, H, Dk, Dv, per_channel != 0, scale};
@@ -135,77 +145,77 @@ int oracle_forward(int B, int T, int H, int Dk, int Dv, int per_channel, double 
 }
 
 /* Reverse pass of one (b, h).  dhT may be NULL (zero); dh0 may be NULL. */
-static void head_backward(const dims *d, int b, int h, const double *q, const double *k,
-                          const double *v, const double *g, const double *beta,
-                          const double *h0, const double *dO, const double *dhT, double *dq,
-                          double *dk, double *dv, double *dg, double *dbeta, double *dh0)
+static void head_backward(const dims *d, int b, int h, const real *q, const real *k,
+                          const real *v, const real *g, const real *beta,
+                          const real *h0, const real *dO, const real *dhT, real *dq,
+                          real *dk, real *dv, real *dg, real *dbeta, real *dh0)
 {
     const int Dk = d->Dk, Dv = d->Dv, T = d->T;
     const size_t SS = (size_t)Dk * Dv;
     const size_t sidx = ((size_t)b * d->H + h) * SS;
     const int nseg = (T + CKPT - 1) / CKPT;
     /* ck[s] = state before token s*CKPT */
-    double *ck = malloc(sizeof(double) * SS * (nseg > 0 ? nseg : 1));
-    double *S = calloc(SS, sizeof(double));
-    double *prev = malloc(sizeof(double) * SS * CKPT); /* S_{t-1} for each t of a segment */
-    double *a = malloc(sizeof(double) * Dk), *m = malloc(sizeof(double) * Dv),
-           *dd = malloc(sizeof(double) * Dv);
-    double *dS = calloc(SS, sizeof(double)), *Sp = malloc(sizeof(double) * SS),
-           *St = malloc(sizeof(double) * SS);
-    double *ddv = malloc(sizeof(double) * Dv), *dm = malloc(sizeof(double) * Dv),
-           *dgc = malloc(sizeof(double) * Dk);
+    real *ck = malloc(sizeof(real) * SS * (nseg > 0 ? nseg : 1));
+    real *S = calloc(SS, sizeof(real));
+    real *prev = malloc(sizeof(real) * SS * CKPT); /* S_{t-1} for each t of a segment */
+    real *a = malloc(sizeof(real) * Dk), *m = malloc(sizeof(real) * Dv),
+           *dd = malloc(sizeof(real) * Dv);
+    real *dS = calloc(SS, sizeof(real)), *Sp = malloc(sizeof(real) * SS),
+           *St = malloc(sizeof(real) * SS);
+    real *ddv = malloc(sizeof(real) * Dv), *dm = malloc(sizeof(real) * Dv),
+           *dgc = malloc(sizeof(real) * Dk);
 
-    if (h0) memcpy(S, h0 + sidx, sizeof(double) * SS);
+    if (h0) memcpy(S, h0 + sidx, sizeof(real) * SS);
     for (int t = 0; t < T; ++t) {
-        if (t % CKPT == 0) memcpy(ck + (size_t)(t / CKPT) * SS, S, sizeof(double) * SS);
+        if (t % CKPT == 0) memcpy(ck + (size_t)(t / CKPT) * SS, S, sizeof(real) * SS);
         const size_t r = tok(d, b, t, h);
         decay_factors(d, g, b, t, h, a);
         step(d, S, a, k + r * Dk, v + r * Dv, beta[r], m, dd);
     }
-    if (dhT) memcpy(dS, dhT + sidx, sizeof(double) * SS);
+    if (dhT) memcpy(dS, dhT + sidx, sizeof(real) * SS);
 
     for (int s = nseg - 1; s >= 0; --s) {
         const int t0 = s * CKPT, t1 = (t0 + CKPT < T) ? t0 + CKPT : T;
-        memcpy(S, ck + (size_t)s * SS, sizeof(double) * SS);
+        memcpy(S, ck + (size_t)s * SS, sizeof(real) * SS);
         for (int t = t0; t < t1; ++t) {
-            memcpy(prev + (size_t)(t - t0) * SS, S, sizeof(double) * SS);
+            memcpy(prev + (size_t)(t - t0) * SS, S, sizeof(real) * SS);
             const size_t r = tok(d, b, t, h);
             decay_factors(d, g, b, t, h, a);
             step(d, S, a, k + r * Dk, v + r * Dv, beta[r], m, dd);
         }
         for (int t = t1 - 1; t >= t0; --t) {
             const size_t r = tok(d, b, t, h);
-            const double *qt = q + r * Dk, *kt = k + r * Dk, *vt = v + r * Dv, *dot = dO + r * Dv;
-            const double bt = beta[r];
+            const real *qt = q + r * Dk, *kt = k + r * Dk, *vt = v + r * Dv, *dot = dO + r * Dv;
+            const real bt = beta[r];
             /* rebuild S'_t, m_t, d_t and S_t from S_{t-1} */
             decay_factors(d, g, b, t, h, a);
-            const double *Sm1 = prev + (size_t)(t - t0) * SS;
+            const real *Sm1 = prev + (size_t)(t - t0) * SS;
             for (int i = 0; i < Dk; ++i)
                 for (int j = 0; j < Dv; ++j) Sp[i * Dv + j] = a[i] * Sm1[i * Dv + j];
-            memcpy(St, Sm1, sizeof(double) * SS);
+            memcpy(St, Sm1, sizeof(real) * SS);
             step(d, St, a, kt, vt, bt, m, dd);
 
             /* o_t = scale S_t^T q_t */
             for (int i = 0; i < Dk; ++i)
                 for (int j = 0; j < Dv; ++j) dS[i * Dv + j] += d->scale * qt[i] * dot[j];
             for (int i = 0; i < Dk; ++i) {
-                double s2 = 0.0;
+                real s2 = 0.0;
                 for (int j = 0; j < Dv; ++j) s2 += St[i * Dv + j] * dot[j];
                 dq[r * Dk + i] = d->scale * s2;
             }
             /* S_t = S'_t + k_t d_t^T */
             for (int j = 0; j < Dv; ++j) {
-                double s2 = 0.0;
+                real s2 = 0.0;
                 for (int i = 0; i < Dk; ++i) s2 += dS[i * Dv + j] * kt[i];
                 ddv[j] = s2;
             }
             for (int i = 0; i < Dk; ++i) {
-                double s2 = 0.0;
+                real s2 = 0.0;
                 for (int j = 0; j < Dv; ++j) s2 += dS[i * Dv + j] * dd[j];
                 dk[r * Dk + i] = s2;
             }
             /* d_t = beta_t (v_t - m_t) */
-            double db = 0.0;
+            real db = 0.0;
             for (int j = 0; j < Dv; ++j) {
                 dv[r * Dv + j] = bt * ddv[j];
                 db += ddv[j] * (vt[j] - m[j]);
@@ -214,7 +224,7 @@ static void head_backward(const dims *d, int b, int h, const double *q, const do
             dbeta[r] = db;
             /* m_t = S'_t^T k_t: dS' = dS + k_t dm^T, dk_t += S'_t dm */
             for (int i = 0; i < Dk; ++i) {
-                double s2 = 0.0;
+                real s2 = 0.0;
                 for (int j = 0; j < Dv; ++j) {
                     dS[i * Dv + j] += kt[i] * dm[j];
                     s2 += Sp[i * Dv + j] * dm[j];
@@ -223,7 +233,7 @@ static void head_backward(const dims *d, int b, int h, const double *q, const do
             }
             /* S'_t = diag(exp g_t) S_{t-1}: dg_i = sum_j dS'_ij S'_ij; dS_{t-1} = a dS' */
             for (int i = 0; i < Dk; ++i) {
-                double s2 = 0.0;
+                real s2 = 0.0;
                 for (int j = 0; j < Dv; ++j) s2 += dS[i * Dv + j] * Sp[i * Dv + j];
                 dgc[i] = s2;
                 for (int j = 0; j < Dv; ++j) dS[i * Dv + j] *= a[i];
@@ -231,22 +241,22 @@ static void head_backward(const dims *d, int b, int h, const double *q, const do
             if (d->per_channel) {
                 for (int i = 0; i < Dk; ++i) dg[r * Dk + i] = dgc[i];
             } else {
-                double s2 = 0.0;
+                real s2 = 0.0;
                 for (int i = 0; i < Dk; ++i) s2 += dgc[i];
                 dg[r] = s2;
             }
         }
     }
-    if (dh0) memcpy(dh0 + sidx, dS, sizeof(double) * SS);
+    if (dh0) memcpy(dh0 + sidx, dS, sizeof(real) * SS);
     free(ck); free(S); free(prev); free(a); free(m); free(dd); free(dS); free(Sp); free(St);
     free(ddv); free(dm); free(dgc);
 }
 
 /* Gradients of sum(o * dO) + sum(hT * dhT) with respect to q, k, v, g, beta, h0. */
-int oracle_backward(int B, int T, int H, int Dk, int Dv, int per_channel, double scale,
-                    const double *q, const double *k, const double *v, const double *g,
-                    const double *beta, const double *h0, const double *dO, const double *dhT,
-                    double *dq, double *dk, double *dv, double *dg, double *dbeta, double *dh0,
+int oracle_backward(int B, int T, int H, int Dk, int Dv, int per_channel, real scale,
+                    const real *q, const real *k, const real *v, const real *g,
+                    const real *beta, const real *h0, const real *dO, const real *dhT,
+                    real *dq, real *dk, real *dv, real *dg, real *dbeta, real *dh0,
                     int nthreads)
 {
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
@@ -261,28 +271,28 @@ int oracle_backward(int B, int T, int H, int Dk, int Dv, int per_channel, double
 }
 
 /* x_hat = x / sqrt(sum(x^2) + eps), row by row over the last dimension D. */
-int oracle_l2norm_forward(long rows, int D, double eps, const double *x, double *xhat)
+int oracle_l2norm_forward(long rows, int D, real eps, const real *x, real *xhat)
 {
     if (rows < 0 || D <= 0) return -1;
     for (long r = 0; r < rows; ++r) {
-        double s = 0.0;
+        real s = 0.0;
         for (int c = 0; c < D; ++c) s += x[r * D + c] * x[r * D + c];
-        const double inv = 1.0 / sqrt(s + eps);
+        const real inv = 1.0 / sqrt(s + eps);
         for (int c = 0; c < D; ++c) xhat[r * D + c] = x[r * D + c] * inv;
     }
     return 0;
 }
 
 /* Adjoint of oracle_l2norm_forward: dx = r (dxhat - xhat (xhat . dxhat)). */
-int oracle_l2norm_backward(long rows, int D, double eps, const double *x, const double *dxhat,
-                           double *dx)
+int oracle_l2norm_backward(long rows, int D, real eps, const real *x, const real *dxhat,
+                           real *dx)
 {
     if (rows < 0 || D <= 0) return -1;
     for (long r = 0; r < rows; ++r) {
-        double s = 0.0;
+        real s = 0.0;
         for (int c = 0; c < D; ++c) s += x[r * D + c] * x[r * D + c];
-        const double inv = 1.0 / sqrt(s + eps);
-        double dot = 0.0;
+        const real inv = 1.0 / sqrt(s + eps);
+        real dot = 0.0;
         for (int c = 0; c < D; ++c) dot += x[r * D + c] * inv * dxhat[r * D + c];
         for (int c = 0; c < D; ++c)
             dx[r * D + c] = inv * (dxhat[r * D + c] - x[r * D + c] * inv * dot);

@@ -57,7 +57,11 @@ def test_workspace_query():
         assert L.gdn_workspace_bytes(ctypes.byref(_shape(**bad)), 0) == 0, bad
     # the largest head count a chunk's 32-bit row offsets allow at 128 x 128
     assert L.gdn_workspace_bytes(ctypes.byref(_shape(B=1, T=64, H=32768)), 0) > 0
-    # chunk-heads counted in 32-bit ints: B * H * ceil(T / 64) < 2^31
+    # token-heads of one call (last chunk counted whole) below 2^27, so every
+    # launch's work-item count stays below 2^32
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(B=2 ** 11, T=2 ** 12, H=16)), 0) == 0
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(B=2 ** 11, T=2 ** 12 - 63, H=16)), 0) == 0
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(B=2 ** 11, T=2 ** 12 - 64, H=16)), 0) > 0
     assert L.gdn_workspace_bytes(ctypes.byref(_shape(B=2 ** 20, T=2 ** 14, H=8)), 0) == 0
     # use_qk_l2norm adds the per-row scale table [chunk-heads][2][C] fp32 to both sizes
     sh_n = _shape(qk_l2norm=1)

@@ -158,3 +158,43 @@ def test_training_pair_equals_separate_calls(dtype, decay):
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("decay", ["channel", "head"])
+def test_long_state_carry_training_shape(dtype, decay):
+    """B=8 T=4096 H=6 128x128 (the training shape) with a decay a hundred times
+    weaker than the default draw: each 64-token chunk keeps about e^-0.5 of its
+    start state, so the state is carried through all 64 chunks (the gated-deltanet
+    card's "long product chain", Requirements) and the saved chunk-start states,
+    chunk deltas and state gradients weigh in every result.  h0 ~ N(0, 0.1).
+    gdn_forward, and the training pair gdn_forward_train + gdn_backward_train,
+    against the oracle on sampled heads: o, hT and all six gradients."""
+    import gated_delta_rule_52_amd as gdn
+    log(f"long state carry, training shape, {dtype} {decay}")
+    inp = gi.make_inputs(8, 4096, 6, 128, 128, decay=decay, dtype=dtype, seed=29, h0_std=0.1,
+                         grads=True, g_scale=0.01)
+    d = to_dev_inputs(inp)
+    sc = inp["meta"]["scale"]
+    o1, h1 = gdn.gdn_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], scale=sc)
+    o2, h2, ws = gdn.gdn_forward_train(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], scale=sc)
+    grads = gdn.gdn_backward_train(d["q"], d["k"], d["v"], d["g"], d["beta"], d["dO"], ws, d["dhT"],
+                                   scale=sc)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    pairs = [(0, 0), (7, 5), (3, 2), (5, 1)]
+    s = sub_heads(inp, pairs)
+    o_ref, h_ref = oracle.forward(s["q"], s["k"], s["v"], s["g"], s["beta"], sc, h0=s["h0"])
+    ref = oracle.backward(s["q"], s["k"], s["v"], s["g"], s["beta"], sc, s["dO"], h0=s["h0"],
+                          dhT=s["dhT"])
+    eo = rel_err(np.stack([host(o1[b, :, h]) for b, h in pairs], axis=1)[None], o_ref)
+    eh = rel_err(np.stack([host(h1[b, h]) for b, h in pairs])[None], h_ref)
+    log(f"  forward: o {eo:.2e}  hT {eh:.2e}")
+    assert eo <= TOL[dtype] and eh <= TOL[dtype]
+    sel = {}
+    for name, x in zip(NAMES, grads):
+        if name == "dh0":
+            sel[name] = torch.stack([x[b, h] for b, h in pairs])[None]
+        else:
+            sel[name] = torch.stack([x[b, :, h] for b, h in pairs], dim=1)[None]
+    compare(sel, ref, TOL[dtype], f"long carry {dtype} {decay}")

@@ -205,3 +205,31 @@ def test_decode_equals_chunked():
     o_dec = torch.cat(outs, dim=1)
     assert rel_err(host(o_dec), host(o)) <= TOL["f32"]
     assert rel_err(host(S), host(hT)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("decay", ["channel", "head"])
+def test_bf16_split_calls_in_place(decay):
+    """bf16 inputs, B=2 T=1024 H=4 128x128 with h0 ~ N(0, 0.1) and weak decay (the
+    state carries across chunks): 8 calls of 128 tokens, each writing its final
+    state over its initial state (hT aliasing h0, the in-place carry the
+    gated-deltanet card's Usage describes), equal one call bitwise."""
+    import gated_delta_rule_52_amd as gdn
+    log(f"bf16 split calls in place, {decay}")
+    inp = gi.make_inputs(2, 1024, 4, 128, 128, decay=decay, dtype="bf16", seed=19, h0_std=0.1,
+                         g_scale=0.01)
+    d = to_dev_inputs(inp)
+    sc = inp["meta"]["scale"]
+    o, hT = gdn.gdn_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], scale=sc)
+    S = d["h0"].clone()
+    outs = []
+    for t0 in range(0, 1024, 128):
+        sl = slice(t0, t0 + 128)
+        o_c, _ = gdn.gdn_forward(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                                 d["v"][:, sl].contiguous(), d["g"][:, sl].contiguous(),
+                                 d["beta"][:, sl].contiguous(), S, scale=sc, hT=S)
+        outs.append(o_c)
+    torch.cuda.synchronize()
+    o_split = torch.cat(outs, dim=1)
+    assert torch.equal(o_split, o) and torch.equal(S, hT)
+    o_ref, h_ref = oracle.forward_inputs(inp)
+    assert rel_err(host(o), o_ref) <= TOL["bf16"] and rel_err(host(hT), h_ref) <= TOL["bf16"]

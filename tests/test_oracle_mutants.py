@@ -22,10 +22,10 @@ MUTANTS = {
                           "        step(d, S, a, k + r * Dk, v + r * Dv, beta[r], m, dd);"),
     "per_channel_collapsed": ("a[i] = exp(gp[i]);", "a[i] = exp(gp[0]);"),
     "scale_dropped": ("ot[j] = d->scale * s;", "ot[j] = s;"),
-    "h0_ignored": ("if (h0) memcpy(S, h0 + sidx, sizeof(double) * Dk * Dv);", ""),
+    "h0_ignored": ("if (h0) memcpy(S, h0 + sidx, sizeof(real) * Dk * Dv);", ""),
     "decay_after_read": ("for (int i = 0; i < Dk; ++i)\n        for (int j = 0; j < Dv; ++j) S[i * Dv + j] *= a[i];\n"
-                         "    for (int j = 0; j < Dv; ++j) {\n        double s = 0.0;\n        for (int i = 0; i < Dk; ++i) s += kt[i] * S[i * Dv + j];\n        m[j] = s;\n    }",
-                         "for (int j = 0; j < Dv; ++j) {\n        double s = 0.0;\n        for (int i = 0; i < Dk; ++i) s += kt[i] * S[i * Dv + j];\n        m[j] = s;\n    }\n"
+                         "    for (int j = 0; j < Dv; ++j) {\n        real s = 0.0;\n        for (int i = 0; i < Dk; ++i) s += kt[i] * S[i * Dv + j];\n        m[j] = s;\n    }",
+                         "for (int j = 0; j < Dv; ++j) {\n        real s = 0.0;\n        for (int i = 0; i < Dk; ++i) s += kt[i] * S[i * Dv + j];\n        m[j] = s;\n    }\n"
                          "    for (int i = 0; i < Dk; ++i)\n        for (int j = 0; j < Dv; ++j) S[i * Dv + j] *= a[i];"),
     # backward
     "dbeta_sign": ("dbeta[r] = db;", "dbeta[r] = -db;"),
@@ -36,13 +36,13 @@ MUTANTS = {
     "dq_scale_dropped": ("dq[r * Dk + i] = d->scale * s2;", "dq[r * Dk + i] = s2;"),
     "dS_not_decayed": ("for (int j = 0; j < Dv; ++j) dS[i * Dv + j] *= a[i];", ""),
     "dv_beta_dropped": ("dv[r * Dv + j] = bt * ddv[j];", "dv[r * Dv + j] = ddv[j];"),
-    "dh0_not_carried": ("if (dh0) memcpy(dh0 + sidx, dS, sizeof(double) * SS);",
-                        "if (dh0) memset(dh0 + sidx, 0, sizeof(double) * SS);"),
+    "dh0_not_carried": ("if (dh0) memcpy(dh0 + sidx, dS, sizeof(real) * SS);",
+                        "if (dh0) memset(dh0 + sidx, 0, sizeof(real) * SS);"),
     # use_qk_l2norm prologue
     "l2norm_projection_dropped": ("inv * (dxhat[r * D + c] - x[r * D + c] * inv * dot)",
                                   "inv * dxhat[r * D + c]"),
-    "l2norm_sqrt_dropped": ("const double inv = 1.0 / sqrt(s + eps);\n        for (int c = 0; c < D; ++c) xhat",
-                            "const double inv = 1.0 / (s + eps);\n        for (int c = 0; c < D; ++c) xhat"),
+    "l2norm_sqrt_dropped": ("const real inv = 1.0 / sqrt(s + eps);\n        for (int c = 0; c < D; ++c) xhat",
+                            "const real inv = 1.0 / (s + eps);\n        for (int c = 0; c < D; ++c) xhat"),
 }
 
 
