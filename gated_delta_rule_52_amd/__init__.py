@@ -36,7 +36,8 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_DECAY_PER_HEAD, GDN_DECAY_PER_CHANNEL = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_ALIGNMENT",
           4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
-EXPORTS = ("gdn_new_state", "gdn_workspace_bytes", "gdn_forward", "gdn_backward",
+EXPORTS = ("gdn_new_state", "gdn_workspace_bytes", "gdn_forward", "gdn_forward_noalloc",
+           "gdn_backward",
            "gdn_forward_train", "gdn_backward_train", "gdn_decode_step", "gdn_diag_read",
            "gdn_replay_buffer_bytes", "gdn_replay_reset", "gdn_replay_step", "gdn_replay_fold",
            "gdn_status_string",
@@ -78,6 +79,8 @@ def lib():
         L.gdn_workspace_bytes.restype = sz
         L.gdn_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_forward.restype = i
+        L.gdn_forward_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.gdn_forward_noalloc.restype = i
         L.gdn_backward.argtypes = [sp] + [vp] * 15 + [sz, vp]
         L.gdn_backward.restype = i
         L.gdn_forward_train.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -225,6 +228,30 @@ def gdn_forward(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT
         ws = workspace(sh, False, q.device)
     _call(lib().gdn_forward, "gdn_forward", ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
           _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), _ptr(ws), ws.numel(), _stream())
+    return o, hT
+
+
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/gdn.h
+
+
+def gdn_forward_noalloc(q, k, v, g, beta, h0=None, *, scale=None, chunk=None, o=None, hT=None,
+                        use_qk_l2norm=False, wy_eps=0.0, clip=0.0):
+    """gdn_forward whose workspace is the library's static per-device array
+    (nothing is allocated for it; the shape's forward workspace must fit in
+    GDN_NOALLOC_SCRATCH_BYTES).  Calls overlapping on one device race.
+    Pass o and hT to allocate nothing here either.  Returns (o, hT)."""
+    _check_inputs(q, k, v, g, beta)
+    sh = make_shape(q, v, g, scale, chunk, use_qk_l2norm, wy_eps, clip, False)
+    _check_shape(h0, "h0", _state_shape(sh), torch.float32)
+    _check_shape(o, "o", v.shape, q.dtype)
+    _check_shape(hT, "hT", _state_shape(sh), torch.float32)
+    B, T, H, _ = q.shape
+    if o is None:
+        o = torch.empty((B, T, H, sh.Dv), dtype=q.dtype, device=q.device)
+    if hT is None:
+        hT = torch.empty((B, H, sh.Dk, sh.Dv), dtype=torch.float32, device=q.device)
+    _call(lib().gdn_forward_noalloc, "gdn_forward_noalloc", ctypes.byref(sh), _ptr(q), _ptr(k),
+          _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), _stream())
     return o, hT
 
 

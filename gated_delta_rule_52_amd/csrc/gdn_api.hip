@@ -3,6 +3,8 @@
 // allocates device memory; every launch goes to the caller's stream.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "plan.h"
 
@@ -36,6 +38,32 @@ __global__ void fill_zero_kernel(float4* __restrict__ p, size_t n4)
 }  // namespace gdn
 
 using namespace gdn;
+
+// Workspace of gdn_forward_noalloc.  In host code `scratch` is only a handle for
+// hipGetSymbolAddress: the device address of each device's copy is looked up
+// once per device (with that device current) and kept in scratch_ptr; kernels
+// and every other host use take that address, never the array's name.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];  // device address of `scratch` on device i, or null
+
+gdn_status scratch_on_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return GDN_OK;
+}
+}  // namespace
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -145,6 +173,23 @@ gdn_status gdn_forward(const gdn_shape* sh, const void* q, const void* k, const 
     Plan p = make_plan(*sh, eff_scale(sh));
     if (p.ws_fwd_bytes && (!ws || ws_bytes < p.ws_fwd_bytes)) return GDN_ERR_WORKSPACE;
     return forward_dispatch(p, q, k, v, g, beta, h0, o, hT, ws, (hipStream_t)stream);
+}
+
+gdn_status gdn_forward_noalloc(const gdn_shape* sh, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const float* h0, void* o,
+                               float* hT, void* stream)
+{
+    gdn_status s = check_shape(sh, false);
+    if (s != GDN_OK) return s;
+    if (sh->diag) return GDN_ERR_UNSUPPORTED;
+    const size_t need = gdn_workspace_bytes(sh, 0);
+    if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need) {
+        s = scratch_on_current_device(&ws);
+        if (s != GDN_OK) return s;
+    }
+    return gdn_forward(sh, q, k, v, g, beta, h0, o, hT, ws, need, stream);
 }
 
 static gdn_status backward_common(const gdn_shape* sh, const void* q, const void* k,

@@ -157,6 +157,27 @@ gdn_status gdn_forward(const gdn_shape *shape, const void *q, const void *k, con
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * gdn_forward_noalloc -- gdn_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and results (bitwise), with the
+ * workspace taken from a static device array of GDN_NOALLOC_SCRATCH_BYTES that
+ * every device holds from the library's first use on it until the process
+ * ends.  The call allocates nothing.  Every call on one device shares that
+ * device's array, so calls that overlap on one device (concurrent streams or
+ * host threads) race and must be serialised by the caller; consecutive calls on
+ * one stream are safe.  The shape must have diag = 0 (the stage counters would
+ * sit in the shared array, out of the caller's reach).
+ * Errors: as gdn_forward; GDN_ERR_WORKSPACE when gdn_workspace_bytes(shape, 0)
+ * exceeds GDN_NOALLOC_SCRATCH_BYTES (64 MiB: at 128 x 128 with chunk 64 about
+ * 450 chunk-heads, e.g. B = 1, H = 6, T = 4096); GDN_ERR_UNSUPPORTED for diag = 1;
+ * GDN_ERR_HIP if the array's device address cannot be obtained.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+gdn_status gdn_forward_noalloc(const gdn_shape *shape, const void *q, const void *k,
+                               const void *v, const float *g, const float *beta, const float *h0,
+                               void *o, float *hT, void *stream);
+
+/*
  * gdn_backward -- gradients of the chunked forward with respect to q, k, v, g,
  * beta and h0, given dO = dL/do and dhT = dL/dhT (NULL = zero).  The forward
  * intermediates are recomputed from the inputs (nothing is kept between
