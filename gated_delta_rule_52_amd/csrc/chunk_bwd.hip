@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "chunk_common.h"
+#include "kperm.h"
 #include "plan.h"
 
 namespace gdn {
@@ -166,54 +167,46 @@ bscan_kernel(const float* __restrict__ Qgi, const float* __restrict__ Khi,
 
 
 // ---------------------------------------------------------------------------
-// bscan over bf16 tables -- 8 waves, dS slice in accumulator registers.  The
-// four tables of a chunk (P^T, Kh, Qg^T, W^T; K-contiguous bf16 rows) go
-// straight from memory into one of two LDS buffers (16-byte direct loads, rows
-// swizzled instead of padded), one chunk ahead; the dO slice and the decay
-// come through registers (dO is transposed on the way).
+// bscan4: the reverse scan of the state gradient over bf16 chunk tables (bf16
+// inputs, chunk 64), built like scan4: two waves per (b, h, 32-wide Dv slice),
+// wave w owning 16 columns of dS for the whole sequence in MFMA accumulators
+// that are the operands of the next products (kperm.h).  Per chunk n, from the
+// last to the first, with dS' the gradient at the chunk's end and the chunk's
+// Kh, P^T, Qg^T, W^T (K index permuted), the dO slice and the decay in LDS:
+//     dD  = Kh dS' + P^T dO                 (P^T upper triangular)
+//     dS <- gam o dS' + Qg^T dO - W^T dD    (the gradient at the chunk's start)
+// dS' and dD leave as bf16 rows for bchunk1 (transposed by a 0/1 MFMA so a
+// lane stores four consecutive columns).  The dO operand (K along tokens) is
+// gathered from the LDS copy of the slice, eight 2-byte reads per fragment.
+// Two load waves bring the next chunk in and warm the L2, as in scan4.
 // ---------------------------------------------------------------------------
-constexpr int NTHR_B = 512;
+constexpr int NTHR_B4 = 256;  // waves 0, 1 compute; waves 2, 3 load
 
-template <int C, int DK, int DV>
-__global__ void __launch_bounds__(NTHR_B)
-bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
-              const bf16* __restrict__ QgTb, const bf16* __restrict__ WTb,
-              const float* __restrict__ gami, const bf16* __restrict__ dO,
-              const float* __restrict__ dhT, bf16* __restrict__ dSt, bf16* __restrict__ dDt,
-              float* __restrict__ dh0, int BH, int T, int H, int NC)
+template <int DK, int DV>
+__global__ void __launch_bounds__(NTHR_B4) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bscan4_kernel(const bf16* __restrict__ Khp, const bf16* __restrict__ PTp,
+              const bf16* __restrict__ QTp, const bf16* __restrict__ WTp,
+              const float* __restrict__ gami, const bf16* __restrict__ dO, const float* dhT,
+              bf16* __restrict__ dSt, bf16* __restrict__ dDt, float* dh0, int BH, int T, int H,
+              int NC)
 {
-    constexpr int BV = 32, NS = DV / BV, NW = NTHR_B / 64;
-    constexpr int PA = DK + 8, PT = C + 8;
-    constexpr int TD = (C / 16) * (BV / 16), TS = (DK / 16) * (BV / 16);
-    constexpr int MD = TD / NW, MS = TS / NW;
-    static_assert(TD % NW == 0 && TS % NW == 0, "every wave owns whole tiles");
-    // tables as 16-byte words: row widths, sizes and offsets within a buffer
-    constexpr int WC = C / 8, WK = DK / 8;
-    constexpr int OP = 0, OK = OP + C * WC, OQ = OK + C * WK, OW = OQ + DK * WC, QT = OW + DK * WC;
-    constexpr int NQ = QT / NTHR_B;
-    static_assert(OK % NTHR_B == 0 && OQ % NTHR_B == 0 && OW % NTHR_B == 0 && QT % NTHR_B == 0,
-                  "every load instruction lies in one table");
-    constexpr int QO = C * BV / 8, QG = DK / 4;  // dO slice and decay words (through registers)
-    static_assert(QO + QG <= NTHR_B, "");
-    // two buffers, separate arrays: the compiler then sees that reads of one
-    // cannot alias the direct loads into the other and does not wait for them
-    __shared__ __align__(16) uint4 sTab0[QT], sTab1[QT];
-    __shared__ __align__(16) bf16 sdSt[BV][PA], sdOt[BV][PT], sdDt[BV][PT];
-    // 2-byte views for the transposed writes: one index expression per write
-    // keeps each address a single step from its array (the alias information
-    // that spares those writes a wait for the direct loads is kept)
-    uint16_t* const dSt16 = &sdSt[0][0].bits;
-    uint16_t* const dDt16 = &sdDt[0][0].bits;
-    uint16_t* const dOt16 = &sdOt[0][0].bits;
-    __shared__ __align__(16) float sgam[DK];  // the chunk's whole-chunk decay
-    // staging of the saved rows (bf16): dS at the chunk's end, written out at
-    // the start of the step, and dD, written out after the mid-step barrier;
-    // whole 64-byte row slices per store, all stores unconditional
-    constexpr int PR = BV + 8;
-    __shared__ __align__(16) bf16 sSo[DK][PR], sDo[C][PR];
-    constexpr int ES = DK * BV / NTHR_B;  // bf16 of dS per thread: one 16- or 8-byte word
-    static_assert((ES == 8 || ES == 4) && ES * NTHR_B == DK * BV && C * BV == 4 * NTHR_B,
-                  "one dS word and one dD word (4 bf16) per thread");
+    constexpr int C = 64, BV = 32, NS = DV / BV;
+    constexpr int NT = DK / 16, KB = DK / 32;
+    constexpr int WK = DK / 8, WC = C / 8;
+    // a buffer in 16-byte words: Kh [C][WK], P^T [C][WC], Qg^T [DK][WC],
+    // W^T [DK][WC] (swizzled, kswz), the dO slice [C][BV] bf16 (plain), the decay
+    constexpr int OKh = 0, OPT = OKh + C * WK, OQT = OPT + C * WC, OWT = OQT + DK * WC;
+    constexpr int OdO = OWT + DK * WC, OG = OdO + C * BV / 8, QB = OG + 64;
+    constexpr int NL = 128;  // threads of the two load waves
+    constexpr int NQT = OdO / NL, NQO = (C * BV / 8) / NL;
+    static_assert(OPT % NL == 0 && OQT % NL == 0 && OWT % NL == 0 && OdO % NL == 0 &&
+                  NQO * NL == C * BV / 8, "each load lies in one table");
+    // 128-byte lines of a chunk's tables and decay (the dO slice: one line a row)
+    constexpr int LT = (C * DK + C * C + 2 * DK * C) * 2 / 128, LG = DK * 4 / 128;
+    constexpr int NWARM = 2;
+    static_assert(C + (NWARM * NL - C) * NS >= LT + LG, "every line of a chunk is warmed");
+    __shared__ __align__(16) uint4 sTab0[QB], sTab1[QB];
+    __shared__ __align__(16) uint32_t sSink[2][64];
 
     const int x = blockIdx.x;
     const int grp = x / (8 * NS), rem = x % (8 * NS);
@@ -222,162 +215,185 @@ bscan2_kernel(const bf16* __restrict__ PsTb, const bf16* __restrict__ Khb,
     const int b = bh / H, h = bh % H;
     const int v0 = sl * BV;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int lr = l & 15, lq = l >> 4;
+    const int ln = l & 15, lg = l >> 4;
+    const bool loader = w >= 2;
+    const int lt = tid & (NL - 1), lw = w & 1;
+    const int vc = v0 + 16 * lw;
 
-    // The state and delta tiles are computed transposed (rows along Dv): a
-    // lane's four accumulator values are then four consecutive Dv columns of
-    // one row of dS (or dD), stored with one 16-byte write; their bf16 copies
-    // in LDS (K-contiguous operands of the next products) take 2-byte writes.
-    // dS tile m of this wave: dacc[m][r] = dS[si*16 + lr][v0 + sj*16 + 4 lq + r].
-    f32x4 dacc[MS];
+    // dS tile t: ds[t][r] = dS[16 t + 4 lg + r][vc + ln]
+    f32x4 ds[NT];
 #pragma unroll
-    for (int m = 0; m < MS; ++m) {
-        const int idx = w + NW * m;
-        const int si = idx / (BV / 16), sj = idx % (BV / 16);
-        dacc[m] = zero4();
-        if (dhT)
-            dacc[m] = *reinterpret_cast<const f32x4*>(
-                dhT + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq);
+    for (int t = 0; t < NT; ++t) ds[t] = zero4();
+    if (dhT && !loader) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dSt16[(sj * 16 + 4 * lq + r) * PA + si * 16 + lr] = f32_to_bf16(dacc[m][r]).bits;
-        *reinterpret_cast<uint2*>(&sSo[si * 16 + lr][sj * 16 + 4 * lq]) =
-            pack4_bf16(dacc[m][0], dacc[m][1], dacc[m][2], dacc[m][3]);
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ds[t][r] = dhT[((size_t)bh * DK + 16 * t + 4 * lg + r) * DV + vc + ln];
     }
+    const bf16x8 id_lo = frag_ident(0), id_hi = frag_ident(1);
 
-    // slot tid + NTHR_B q of a buffer takes table word (row, w ^ (row & 7)),
-    // (row, w) being the slot's place in its table
-    int goff[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int g0 = q * NTHR_B;
-        const int wpr = (g0 >= OK && g0 < OQ) ? WK : WC;
-        const int s = g0 + tid - (g0 < OK ? OP : g0 < OQ ? OK : g0 < OW ? OQ : OW);
-        const int row = s / wpr, wd = s % wpr;
-        goff[q] = (row * wpr + (wd ^ (row & 7))) * 8;
-    }
-    auto fetch_tables = [&](int n, uint4* buf) {
+    auto fetch = [&](int n, uint4* buf) __attribute__((always_inline)) {
         const size_t ch = (size_t)bh * NC + n;
+        if (lw == 0) dma16(gami + ch * DK + 4 * (l % (DK / 4)), buf + OG);
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int g0 = q * NTHR_B;
-            const bf16* src = g0 < OK ? PsTb + ch * C * C
-                            : g0 < OQ ? Khb + ch * C * DK
-                            : g0 < OW ? QgTb + ch * C * DK
-                                      : WTb + ch * C * DK;
-            dma16(src + goff[q], buf + g0 + 64 * w);
+        for (int q = 0; q < NQT; ++q) {
+            const int s0 = q * NL;
+            const int wpr = s0 < OPT ? WK : WC;
+            const int off = s0 < OPT ? OKh : s0 < OQT ? OPT : s0 < OWT ? OQT : OWT;
+            const bf16* tab = s0 < OPT ? Khp + ch * C * DK
+                            : s0 < OQT ? PTp + ch * C * C
+                            : s0 < OWT ? QTp + ch * DK * C
+                                       : WTp + ch * DK * C;
+            const int ls = s0 + lt - off, r = ls / wpr, ws = ls % wpr;
+            const int wd = ws ^ (wpr == 16 ? (r & 15) : ((r >> 1) & 7));
+            dma16(tab + (r * wpr + wd) * 8, buf + s0 + 64 * lw);
+        }
+        // dO rows of the chunk (rows past T repeat the last one: their P^T and
+        // Qg^T columns are zero)
+#pragma unroll
+        for (int q = 0; q < NQO; ++q) {
+            const int su = q * NL + lt, r = su / (BV / 8);
+            const int t = min(n * C + r, T - 1);
+            dma16(dO + (((size_t)b * T + t) * H + h) * DV + v0 + 8 * (su % (BV / 8)),
+                  buf + OdO + q * NL + 64 * lw);
         }
     };
-    // the dO slice (threads < QO: row e / 4, columns 8 (e % 4) ..) and the decay
-    // (the next QG threads); the rest repeat a valid dO word.  Rows past the end
-    // are clamped here and zeroed in stash_words().
-    const bool is_gam = tid >= QO && tid < QO + QG;
-    const int eo = min(tid, QO - 1), ro = eo / (BV / 8), jo = (eo % (BV / 8)) * 8;
-    uint4 pw;
-    auto fetch_words = [&](int n) {
+    // chunk n's lines -> L2: the dO slice, and every NS-th line of the tables
+    // and decay (the other slices of the head, on the same XCD, take the rest)
+    auto warm = [&](int n) __attribute__((always_inline)) {
         const size_t ch = (size_t)bh * NC + n;
-        const int t = min(n * C + ro, T - 1);
-        const uint4* src = is_gam ? reinterpret_cast<const uint4*>(gami + ch * DK) + (tid - QO)
-                                  : reinterpret_cast<const uint4*>(dO + (((size_t)b * T + t) * H + h) * DV + v0 + jo);
-        pw = *src;
-    };
-    auto stash_words = [&](int n) {
-        if (tid < QO) {  // dO row ro, columns jo..jo+7 -> dO^T (zero past the end)
-            const bool live = n * C + ro < T;
-            const uint32_t u[4] = {live ? pw.x : 0u, live ? pw.y : 0u, live ? pw.z : 0u, live ? pw.w : 0u};
 #pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                dOt16[(jo + 2 * z) * PT + ro] = (uint16_t)(u[z] & 0xFFFFu);
-                dOt16[(jo + 2 * z + 1) * PT + ro] = (uint16_t)(u[z] >> 16);
+        for (int q = 0; q < NWARM; ++q) {
+            const int s = q * NL + lt;
+            const char* p;
+            if (s < C) {
+                const int t = min(n * C + s, T - 1);
+                p = reinterpret_cast<const char*>(dO + (((size_t)b * T + t) * H + h) * DV + v0);
+            } else {
+                const int L = min((s - C) * NS + sl, LT + LG - 1);
+                constexpr int L1 = C * DK * 2 / 128, L2 = L1 + C * C * 2 / 128, L3 = L2 + DK * C * 2 / 128;
+                p = L < L1 ? reinterpret_cast<const char*>(Khp + ch * C * DK) + 128 * L
+                  : L < L2 ? reinterpret_cast<const char*>(PTp + ch * C * C) + 128 * (L - L1)
+                  : L < L3 ? reinterpret_cast<const char*>(QTp + ch * DK * C) + 128 * (L - L2)
+                  : L < LT ? reinterpret_cast<const char*>(WTp + ch * DK * C) + 128 * (L - L3)
+                           : reinterpret_cast<const char*>(gami + ch * DK) + 128 * (L - LT);
             }
-        } else if (is_gam) {
-            *reinterpret_cast<uint4*>(&sgam[4 * (tid - QO)]) = pw;
+            warm_line(p, &sSink[lw][0]);
         }
     };
-    // vector memory operations issued after a chunk's table loads and before
-    // the wait for them: the dO/decay word and the step's dS and dD stores
-    constexpr int AFTER = 1 + 1 + 1;
 
-    // chunk n sits in buffer (NC - 1 - n) & 1: the steps of a pair of chunks
-    // use fixed buffers
-    fetch_tables(NC - 1, sTab0);
-    fetch_words(NC - 1);
-    stash_words(NC - 1);
-    wait_vmcnt<0>();  // the direct loads have landed
-    __syncthreads();
-
-    auto step = [&](int n, const uint4* tb, uint4* tnx) {
+    auto compute = [&](int n, const uint4* tb) __attribute__((always_inline)) {
         const size_t ch = (size_t)bh * NC + n;
-        const int nx = max(n - 1, 0);  // at n = 0 a harmless reload into the idle buffer
-        fetch_tables(nx, tnx);
-        fetch_words(nx);
-        {  // dS at the end of chunk n (bf16: the backward's products read it as
-           // bf16, the decay-gradient sum accumulates in fp32), from the staging
-            const int i = tid / (BV / ES), je = (tid % (BV / ES)) * ES;
-            if constexpr (ES == 8)
-                *reinterpret_cast<uint4*>(dSt + (ch * DK + i) * DV + v0 + je) =
-                    *reinterpret_cast<const uint4*>(&sSo[i][je]);
-            else
-                *reinterpret_cast<uint2*>(dSt + (ch * DK + i) * DV + v0 + je) =
-                    *reinterpret_cast<const uint2*>(&sSo[i][je]);
-        }
-        // dD^T = scale dO^T P + dS'^T Kh^T: acc[r] = dD[ti*16 + lr][v0 + tj*16 + 4 lq + r]
+        const uint16_t* tO = reinterpret_cast<const uint16_t*>(tb + OdO);
+        const f32x4* tG = reinterpret_cast<const f32x4*>(tb + OG);
+        bf16x8 dsb[KB];  // dS' (the chunk's end) as operand fragments
 #pragma unroll
-        for (int m = 0; m < MD; ++m) {
-            const int idx = w + NW * m;
-            const int ti = idx / (BV / 16), tj = idx % (BV / 16);
-            f32x4 acc = mma_kc_bsw<C, WC>(zero4(), &sdOt[tj * 16][0], PT, tb + OP, ti * 16);
-            acc = mma_kc_bsw<DK, WK>(acc, &sdSt[tj * 16][0], PA, tb + OK, ti * 16);
-            *reinterpret_cast<uint2*>(&sDo[ti * 16 + lr][tj * 16 + 4 * lq]) = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+        for (int kb = 0; kb < KB; ++kb) dsb[kb] = frag_acc(ds[2 * kb], ds[2 * kb + 1]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dDt16[(tj * 16 + 4 * lq + r) * PT + ti * 16 + lr] = f32_to_bf16(acc[r]).bits;
+        for (int t = 0; t < NT; ++t) {
+            const f32x4 tr = mfma_bf16_16x16x32(dsb[t / 2], (t & 1) ? id_hi : id_lo, zero4());
+            *reinterpret_cast<uint2*>(&dSt[(ch * DK + 16 * t + ln) * DV + vc + 4 * lg]) =
+                pack4_bf16(tr[0], tr[1], tr[2], tr[3]);
         }
-        __syncthreads();
-        {  // dD of chunk n, from the staging
-            const int i = tid / (BV / 4), j4 = (tid % (BV / 4)) * 4;
-            *reinterpret_cast<uint2*>(dDt + (ch * C + i) * DV + v0 + j4) = *reinterpret_cast<const uint2*>(&sDo[i][j4]);
-        }
-        // dS^T <- dS'^T o gam + dO^T Qg - dD^T W
+        // dO as the operand with K along tokens: slot e of lane group lg is token
+        // 32 kb + 4 lg + e (e < 4) or 32 kb + 16 + 4 lg + e - 4
+        bf16x8 dob[2];
 #pragma unroll
-        for (int m = 0; m < MS; ++m) {
-            const int idx = w + NW * m;
-            const int si = idx / (BV / 16), sj = idx % (BV / 16);
-            const float gk = sgam[si * 16 + lr];
+        for (int kb = 0; kb < 2; ++kb) {
+            u32x4 wv;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const int t0 = 32 * kb + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
+                wv[e / 2] = (uint32_t)tO[t0 * BV + 16 * lw + ln] |
+                            ((uint32_t)tO[(t0 + 1) * BV + 16 * lw + ln] << 16);
+            }
+            dob[kb] = __builtin_bit_cast(bf16x8, wv);
+        }
+        // dD = Kh dS' + P^T dO (the fragments of a product are read before its
+        // MFMAs: one wave per SIMD has no other wave to cover the LDS latency)
+        bf16x8 kf[KB][4], pf[4][2];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) kf[kb][ti] = frag_lds<WK>(tb + OKh, 16 * ti, kb);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int kb = ti / 2; kb < 2; ++kb) pf[ti][kb] = frag_lds<WC>(tb + OPT, 16 * ti, kb);
+        f32x4 dd[4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) dd[ti] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) dd[ti] = mfma_bf16_16x16x32(kf[kb][ti], dsb[kb], dd[ti]);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int kb = ti / 2; kb < 2; ++kb) dd[ti] = mfma_bf16_16x16x32(pf[ti][kb], dob[kb], dd[ti]);
+        const bf16x8 ddb[2] = {frag_acc(dd[0], dd[1]), frag_acc(dd[2], dd[3])};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const f32x4 tr = mfma_bf16_16x16x32(ddb[t / 2], (t & 1) ? id_hi : id_lo, zero4());
+            *reinterpret_cast<uint2*>(&dDt[(ch * C + 16 * t + ln) * DV + vc + 4 * lg]) =
+                pack4_bf16(tr[0], tr[1], tr[2], tr[3]);
+        }
+        const bf16x8 ddn[2] = {frag_neg(ddb[0]), frag_neg(ddb[1])};
+        // dS <- gam o dS' + Qg^T dO - W^T dD
+        bf16x8 qf[NT][2], wf[NT][2];
+        f32x4 gv[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            gv[t] = tG[4 * t + lg];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                qf[t][kb] = frag_lds<WC>(tb + OQT, 16 * t, kb);
+                wf[t][kb] = frag_lds<WC>(tb + OWT, 16 * t, kb);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
             f32x4 acc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = gk * dacc[m][r];
-            acc = mma_kc_bsw<C, WC>(acc, &sdOt[sj * 16][0], PT, tb + OQ, si * 16);
-            const f32x4 wd = mma_kc_bsw<C, WC>(zero4(), &sdDt[sj * 16][0], PT, tb + OW, si * 16);
+            for (int r = 0; r < 4; ++r) acc[r] = gv[t][r] * ds[t][r];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                dacc[m][r] = acc[r] - wd[r];
-                dSt16[(sj * 16 + 4 * lq + r) * PA + si * 16 + lr] = f32_to_bf16(dacc[m][r]).bits;
-            }
-            *reinterpret_cast<uint2*>(&sSo[si * 16 + lr][sj * 16 + 4 * lq]) =
-                pack4_bf16(dacc[m][0], dacc[m][1], dacc[m][2], dacc[m][3]);
+            for (int kb = 0; kb < 2; ++kb) acc = mfma_bf16_16x16x32(qf[t][kb], dob[kb], acc);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) acc = mfma_bf16_16x16x32(wf[t][kb], ddn[kb], acc);
+            ds[t] = acc;
         }
-        __syncthreads();
-        stash_words(nx);
-        // every thread waits for its word here, right after the stash (the
-        // threads that stash nothing too): otherwise the compiler waits for it
-        // where its registers are next written, after the next direct loads,
-        // and that wait also covers those loads
-        asm volatile("" ::"v"(pw.x), "v"(pw.y), "v"(pw.z), "v"(pw.w));
-        wait_vmcnt<AFTER>();  // chunk nx's tables have landed
+    };
+
+    auto step = [&](int n, const uint4* cur, uint4* nxt) __attribute__((always_inline)) {
+        if (loader) {
+            fetch(max(n - 1, 0), nxt);
+            warm(max(n - 3, 0));
+            wait_vm<NWARM>();  // chunk n - 1 has landed
+        } else {
+            compute(n, cur);
+        }
         __syncthreads();
     };
-    int n = NC - 1;
-    for (; n >= 1; n -= 2) {
-        step(n, sTab0, sTab1);
-        step(n - 1, sTab1, sTab0);
+    if (loader) {
+        fetch(NC - 1, sTab0);
+        warm(max(NC - 2, 0));
+        warm(max(NC - 3, 0));
+        wait_vm<2 * NWARM>();
     }
-    if (n == 0) step(0, sTab0, sTab1);
-    if (dh0) {
+    __syncthreads();
+    int i = 0;
+    for (; i + 1 < NC; i += 2) {
+        step(NC - 1 - i, sTab0, sTab1);
+        step(NC - 2 - i, sTab1, sTab0);
+    }
+    if (i < NC) step(NC - 1 - i, sTab0, sTab1);
+    wait_vm<0>();  // no direct load may still write the LDS when the workgroup ends
+    if (dh0 && !loader) {
 #pragma unroll
-        for (int m = 0; m < MS; ++m) {
-            const int idx = w + NW * m;
-            const int si = idx / (BV / 16), sj = idx % (BV / 16);
-            *reinterpret_cast<f32x4*>(dh0 + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq) = dacc[m];
-        }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dh0[((size_t)bh * DK + 16 * t + 4 * lg + r) * DV + vc + ln] = ds[t][r];
     }
 }
 
@@ -2126,9 +2142,10 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
     const float* rn = p.l2n ? (const float*)(ws + p.o_rn) : nullptr;
     if constexpr (bf16_tables<TIn, C, DK>()) {
         const size_t n = p.n_ch;
-        dim3 grid((unsigned)(((BH + 7) / 8) * 8 * (DV / 32))), block(NTHR_B);
-        GDN_LAUNCH("bscan", (bscan2_kernel<C, DK, DV>), grid, block, st,
-                   (const bf16*)(ws + p.o_Ps) + n * C * C, (const bf16*)(ws + p.o_Kh) + n * C * DK,
+        // the backward tables are the second of the two in each region (plan.h)
+        dim3 grid((unsigned)(((BH + 7) / 8) * 8 * (DV / 32))), block(NTHR_B4);
+        GDN_LAUNCH("bscan", (bscan4_kernel<DK, DV>), grid, block, st,
+                   (const bf16*)(ws + p.o_Kh) + n * C * DK, (const bf16*)(ws + p.o_Ps) + n * C * C,
                    (const bf16*)(ws + p.o_Qg) + n * C * DK, (const bf16*)(ws + p.o_W) + n * C * DK,
                    (const float*)(ws + p.o_gam), (const bf16*)dO, dhT, (bf16*)(ws + p.o_dSt),
                    (bf16*)(ws + p.o_dDt), dh0, BH, p.T, p.H, p.NC);

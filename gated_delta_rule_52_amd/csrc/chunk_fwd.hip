@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "chunk_common.h"
+#include "kperm.h"
 #include "plan.h"
 
 namespace gdn {
@@ -734,7 +735,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     auto put_ps = [&](int i0, int j, const float (&pv)[4]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sPs[i0 + r][j] = f32_to_bf16(pv[r]);
-        if (bwdt) *reinterpret_cast<uint2*>(&sPsT[j][i0]) = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
+        if (bwdt) *reinterpret_cast<uint2*>(&sPsT[j][kperm_pos(i0)]) = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
     };
     if (w >= NB) {
 #pragma unroll
@@ -768,7 +769,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         const int i = idx / C, j = idx % C;
         if (i / 16 < j / 16) {
             sPs[i][j] = f32_to_bf16(0.f);
-            if (bwdt) sPsT[j][i] = f32_to_bf16(0.f);
+            if (bwdt) sPsT[j][kperm_pos(i)] = f32_to_bf16(0.f);
             sA[i][j] = 0.f;
         }
     }
@@ -824,14 +825,13 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         for (int i = 0; i < RPP; i += 4)
             *reinterpret_cast<uint2*>(&sXT[c][p0 + i]) = pack4_bf16(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
         if (bwdt) {
+            // the backward scan's Qg^T and Kh: contraction index permuted (kperm.h)
 #pragma unroll
-            for (int i = 0; i < RPP; i += 8) {
-                const uint2 q0 = pack4_bf16(qg[i], qg[i + 1], qg[i + 2], qg[i + 3]);
-                const uint2 q1 = pack4_bf16(qg[i + 4], qg[i + 5], qg[i + 6], qg[i + 7]);
-                *reinterpret_cast<uint4*>(&QgTc[c * C + p0 + i]) = uint4{q0.x, q0.y, q1.x, q1.y};
-            }
+            for (int i = 0; i < RPP; i += 4)
+                *reinterpret_cast<uint2*>(&QgTc[c * C + kperm_pos(p0 + i)]) =
+                    pack4_bf16(qg[i], qg[i + 1], qg[i + 2], qg[i + 3]);
 #pragma unroll
-            for (int i = 0; i < RPP; ++i) sKs[p0 + i][c] = f32_to_bf16(kh[i]);
+            for (int i = 0; i < RPP; ++i) sKs[p0 + i][kperm_pos(c)] = f32_to_bf16(kh[i]);
         }
     }
     __syncthreads();  // staged rows complete
@@ -921,8 +921,8 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         bf16* Wc = Wb + (size_t)ch * C * DK;
 #pragma unroll
         for (int r = 0; r < 4; ++r) Wc[(ti * 16 + 4 * lq + r) * DK + tj * 16 + lr] = f32_to_bf16(acc[r]);
-        if (bwdt)
-            *reinterpret_cast<uint2*>(&WTb[(size_t)ch * C * DK + (tj * 16 + lr) * C + ti * 16 + 4 * lq]) =
+        if (bwdt)  // the backward scan's W^T: token index permuted (kperm.h)
+            *reinterpret_cast<uint2*>(&WTb[(size_t)ch * C * DK + (tj * 16 + lr) * C + kperm_pos(ti * 16 + 4 * lq)]) =
                 pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();  // X_V^T complete
