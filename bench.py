@@ -358,6 +358,10 @@ def main():
     import gdn_inputs as gi
     from gated_delta_rule_52_amd.profile import LaunchRecorder
 
+    # the measurement build: the library's kernels and entry points plus the
+    # launch recorder that times each launch on its stream
+    gdn.use_measurement_build()
+
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
 

@@ -148,12 +148,16 @@ auto with_bool(bool b, F&& f)
     return b ? f(std::true_type{}) : f(std::false_type{});
 }
 
-// launch recorder (include/gdn_profile.h); no-ops unless a tool enabled it
+#ifdef GDN_PROFILE
+// launch recorder (include/gdn_profile.h), only in the measurement build
+// (libgdn_prof.so); no-ops unless a tool enabled it
 void prof_begin(const char* name, hipStream_t st);
 void prof_end(hipStream_t st);
+#endif
 
 }  // namespace gdn
 
+#ifdef GDN_PROFILE
 // Launch a kernel on `st` between the recorder's marks, then check the launch.
 #define GDN_LAUNCH(name, kernel, grid, block, st, ...)                   \
     do {                                                                 \
@@ -162,6 +166,15 @@ void prof_end(hipStream_t st);
         ::gdn::prof_end(st);                                             \
         if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;         \
     } while (0)
+#else
+// Launch a kernel on `st`, then check the launch.
+#define GDN_LAUNCH(name, kernel, grid, block, st, ...)                   \
+    do {                                                                 \
+        (void)(name);                                                    \
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, __VA_ARGS__);     \
+        if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;         \
+    } while (0)
+#endif
 
 #define GDN_HIP_CHECK_LAUNCH()                                   \
     do {                                                         \

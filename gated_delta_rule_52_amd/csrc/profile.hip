@@ -1,4 +1,7 @@
-// profile.hip -- the launch recorder declared in include/gdn_profile.h.
+// profile.hip -- the launch recorder declared in include/gdn_profile.h.  It
+// exists only in the measurement build (GDN_PROFILE defined, libgdn_prof.so);
+// the library proper keeps no recorder and exports none of these symbols.
+#ifdef GDN_PROFILE
 #include "common.h"
 #include "gdn_profile.h"
 
@@ -56,3 +59,5 @@ const char* gdn_profile_launch_name(int j)
 }
 
 }  // extern "C"
+
+#endif  // GDN_PROFILE

@@ -1,5 +1,7 @@
 """Binding of include/gdn_profile.h: per-launch device timings of the
-library's kernels, taken with HIP events recorded on each launch's stream."""
+library's kernels, taken with HIP events recorded on each launch's stream.
+The recorder exists only in the measurement build: call
+gated_delta_rule_52_amd.use_measurement_build() before the first library call."""
 from __future__ import annotations
 
 import collections
@@ -29,6 +31,9 @@ def hip():
 
 def _bind():
     L = lib()
+    if not hasattr(L, "gdn_profile_begin"):
+        raise RuntimeError("the launch recorder is only in libgdn_prof.so: call "
+                           "gated_delta_rule_52_amd.use_measurement_build() first")
     L.gdn_profile_begin.argtypes = [ctypes.c_void_p, ctypes.c_int]
     L.gdn_profile_begin.restype = ctypes.c_int
     L.gdn_profile_end.argtypes = []

@@ -1,7 +1,10 @@
 /*
  * gdn_profile.h -- launch-level timing of the gated delta-rule library, for
  * measurement tools (benchmarks, roofline reports).  Not needed to use the
- * layer.
+ * layer, and not part of the library proper: only the measurement build,
+ * libgdn_prof.so (the same sources compiled with GDN_PROFILE defined), exports
+ * these entry points and consults the recorder around its launches; libgdn.so
+ * keeps no recorder.
  *
  * gdn_profile_begin(events, n_pairs): from now on, the library records
  * events[2j] on the launch stream right before its j-th kernel launch and
@@ -15,8 +18,9 @@
  * gdn_profile_launch_name(j) is the kernel name of recorded launch j (a
  * static string), or NULL when j is out of range.
  * Errors: gdn_profile_begin returns GDN_ERR_INVALID_ARG for NULL events or
- * n_pairs outside [1, GDN_PROFILE_MAX].  The recorder is process-global and
- * not thread-safe: profile one host thread at a time.
+ * n_pairs outside [1, GDN_PROFILE_MAX].  In the measurement build the
+ * recorder is process-global and not thread-safe: profile one host thread at
+ * a time.
  */
 #ifndef GDN_PROFILE_H
 #define GDN_PROFILE_H

@@ -12,24 +12,31 @@ import gated_delta_rule_52_amd as gdn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_symbols():
-    names = set()
-    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
-        if h.endswith(".h"):
-            src = open(os.path.join(ROOT, "include", h)).read()
-            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-            names |= set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src))
-    return sorted(names)
+def declared_symbols(header):
+    src = open(os.path.join(ROOT, "include", header)).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src)))
 
 
 def test_header_declares_the_boundary():
-    assert declared_symbols() == sorted(gdn.EXPORTS)
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["gdn.h", "gdn_profile.h"]
+    assert declared_symbols("gdn.h") == sorted(gdn.EXPORTS)
+    assert declared_symbols("gdn_profile.h") == sorted(gdn.PROFILE_EXPORTS)
 
 
 def test_library_exports_every_declared_symbol():
     L = gdn.lib()
-    for name in declared_symbols():
+    for name in declared_symbols("gdn.h"):
         assert hasattr(L, name), name
+    # the library proper keeps no launch recorder
+    for name in declared_symbols("gdn_profile.h"):
+        assert not hasattr(L, name), name
+
+
+def test_measurement_build_exports_the_recorder_too():
+    P = ctypes.CDLL(gdn.PROFILE_LIB_PATH)
+    for name in declared_symbols("gdn.h") + declared_symbols("gdn_profile.h"):
+        assert hasattr(P, name), name
 
 
 def test_status_strings():
@@ -101,7 +108,7 @@ def test_null_and_misaligned_pointers_rejected():
 
 
 def test_profile_recorder_arguments():
-    L = gdn.lib()
+    L = ctypes.CDLL(gdn.PROFILE_LIB_PATH)
     L.gdn_profile_begin.argtypes = [ctypes.c_void_p, ctypes.c_int]
     assert L.gdn_profile_begin(None, 4) == 1
     ev = (ctypes.c_void_p * 2)()
