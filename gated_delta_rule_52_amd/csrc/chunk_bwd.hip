@@ -1445,18 +1445,57 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
 // bchunk2c: bf16 inputs at chunk 64, after bchunk1b has taken the WY adjoint
 // (dX_K and dA).  One workgroup takes one chunk-head and half of its key
 // channels: score gradients by the block-boundary split, the decay chain rule
-// and the outputs dq, dk, dg of those channels.  256 threads and < 80 KB of
-// LDS let two workgroups share a CU, so one loads while the other computes.
+// and the outputs dq, dk, dg of those channels.  A thread owns one channel of
+// eight consecutive token rows (a part); < 80 KB of LDS and < 128 VGPRs let
+// two workgroups (four waves per SIMD) share a CU.
 // dbeta (and dg for per-head decay) are row sums over all channels: each half
 // writes its partial sums and bchunk2_finish adds them in a fixed order.
 // With L2N (use_qk_l2norm) q and k rows are scaled by the forward's r and
 // dq, dk are written with respect to the normalised rows; l2norm_bwd maps
 // them to the raw rows, which needs whole rows.
 // ---------------------------------------------------------------------------
-constexpr int NTHR_F = 256;  // 4 waves: one per 16-row part
+// threads of a bchunk2c workgroup: one per (8-row part, key channel of the half)
+template <int C, int DK>
+constexpr int bchunk2c_threads()
+{
+    return (C / 8) * (DK / 2);
+}
+
+// Channel-major bf16 tables of bchunk2c (a channel's C = 64 token rows as eight
+// 16-byte slots of 8 rows): slot s of channel ch sits at ch * 8 + (s ^ ((ch >> 1)
+// & 7)), so the 16 channels of an MFMA B fragment read 16 distinct 16-byte bank
+// groups, and the 16 threads of a part writing their slots do too.
+__device__ __forceinline__ int ctab_slot(int ch, int s) { return ch * 8 + (s ^ ((ch >> 1) & 7)); }
+
+// 16x16 tile (rows of A x channels ch0..ch0+15) summed over K = 16, 32 or 64
+// token rows from kb (a multiple of 8; of 32 when K >= 32): A row-major bf16,
+// K contiguous, pointing at the first summed column; B from a channel-major
+// table.  K = 16 runs on the K = 32 instruction with a zero upper B half.
+template <int K>
+__device__ __forceinline__ f32x4 mma_ctab(f32x4 acc, const bf16* __restrict__ A, int lda,
+                                          const uint4* __restrict__ tab, int ch0, int kb)
+{
+    const int l = lane_id(), r = l & 15, kk = l >> 4;
+    if constexpr (K == 16) {
+        const int ko = 8 * (kk & 1);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + ko);
+        bf16x8 b = __builtin_bit_cast(bf16x8, tab[ctab_slot(ch0 + r, (kb + ko) / 8)]);
+        if (kk >= 2) b = bf16x8{};
+        return mfma_bf16_16x16x32(a, b, acc);
+    } else {
+        static_assert(K % 32 == 0, "K = 16, 32 or 64");
+#pragma unroll
+        for (int k = 0; k < K; k += 32) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + k + 8 * kk);
+            const bf16x8 b = __builtin_bit_cast(bf16x8, tab[ctab_slot(ch0 + r, (kb + k) / 8 + kk)]);
+            acc = mfma_bf16_16x16x32(a, b, acc);
+        }
+        return acc;
+    }
+}
 
 template <int C, int DK, bool PCH, bool L2N>
-__global__ void __launch_bounds__(NTHR_F)
+__global__ void __launch_bounds__((C / 8) * (DK / 2))  // bchunk2c_threads
 bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
                 const float* __restrict__ beta, const bf16* __restrict__ dQgi,
                 const bf16* __restrict__ dXKi, const bf16* __restrict__ dKhi,
@@ -1467,28 +1506,31 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
 {
     static_assert(C == 64, "bchunk2c: chunk 64");
     constexpr int HC = DK / 2;  // key channels per workgroup
+    constexpr int NTHR_F = bchunk2c_threads<C, DK>();
     constexpr int NB = C / 16, NW = NTHR_F / 64;
-    constexpr int RPP = 16, NPART = C / RPP;
-    static_assert(NPART * HC <= NTHR_F, "one column thread per (part, channel)");
+    constexpr int RPP = 8, NPART = C / RPP;
+    static_assert(NPART * HC == NTHR_F, "one column thread per (part, channel)");
     constexpr int PT = C + 8;  // bf16 pitch: 16-byte rows, banks spread
     constexpr int PH = HC + 1; // fp32 pitch of the result tables
     // LDS, one buffer with named parts:
     //  score gradients, bf16: dPs (unscaled, lower incl. diagonal) and dA (strictly
     //  lower) by rows and transposed, the transposed dA with beta_i folded in;
-    //  level tables (channel-major); level results: query rows scale*R1, key rows
-    //  scale*R1 + R2 (sR), query rows' R2 (sR2, C/2 rows).  Before the levels sR
-    //  also holds the dKh row-sum partials.  Per-head decay uses, after its score
-    //  products, the first 3 C x PH fp32 tables' worth of bytes for their results.
-    constexpr int TB = C * PT * 2, O_QK = 4 * TB, O_KK = O_QK + HC * PT * 2;
-    constexpr int O_R = O_KK + HC * PT * 2, O_R2 = O_R + C * PH * 4, LDSB = O_R2 + (C / 2) * PH * 4;
+    //  level tables (channel-major, ctab_slot); level results: query rows
+    //  scale*R1, key rows scale*R1 + R2 (sR), query rows' R2 (sR2, C/2 rows).
+    //  Before the levels sR also holds the dKh row-sum partials.  Per-head decay
+    //  uses, after its score products, the first 3 C x PH fp32 tables' worth of
+    //  bytes for their results.
+    static_assert(C == 8 * 8, "channel-major tables of eight 8-row slots");
+    constexpr int TB = C * PT * 2, O_QK = 4 * TB, O_KK = O_QK + HC * C * 2;
+    constexpr int O_R = O_KK + HC * C * 2, O_R2 = O_R + C * PH * 4, LDSB = O_R2 + (C / 2) * PH * 4;
     static_assert(3 * C * PH * 4 <= O_R, "per-head results fit below the level results");
     __shared__ __align__(16) char sbuf[LDSB];
     bf16 (*sP)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);
     bf16 (*sPT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + TB);
     bf16 (*sA)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + 2 * TB);
     bf16 (*sAT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + 3 * TB);
-    bf16 (*sQKT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + O_QK);
-    bf16 (*sKKT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + O_KK);
+    uint4* sQK = reinterpret_cast<uint4*>(sbuf + O_QK);  // q rows (times a factor), by channel
+    uint4* sKK = reinterpret_cast<uint4*>(sbuf + O_KK);  // k rows (times a factor), by channel
     float (*sR)[PH] = reinterpret_cast<float (*)[PH]>(sbuf + O_R);
     float (*sR2)[PH] = reinterpret_cast<float (*)[PH]>(sbuf + O_R2);
     __shared__ float sbeta[C], stot[NPART][HC];
@@ -1731,8 +1773,8 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                 const uint2 q1 = pack4_bf16(qx[i + 4], qx[i + 5], qx[i + 6], qx[i + 7]);
                 const uint2 k0 = pack4_bf16(kx[i], kx[i + 1], kx[i + 2], kx[i + 3]);
                 const uint2 k1 = pack4_bf16(kx[i + 4], kx[i + 5], kx[i + 6], kx[i + 7]);
-                *reinterpret_cast<uint4*>(&sQKT[cl][p0 + i]) = uint4{q0.x, q0.y, q1.x, q1.y};
-                *reinterpret_cast<uint4*>(&sKKT[cl][p0 + i]) = uint4{k0.x, k0.y, k1.x, k1.y};
+                sQK[ctab_slot(cl, (p0 + i) / 8)] = uint4{q0.x, q0.y, q1.x, q1.y};
+                sKK[ctab_slot(cl, (p0 + i) / 8)] = uint4{k0.x, k0.y, k1.x, k1.y};
             }
         }
         __syncthreads();
@@ -1742,10 +1784,10 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         for (int m = 0; m < M3; ++m) {
             const int idx = w + NW * m;
             const int ti = (idx % T3) / (HC / 16), tj = idx % (HC / 16);
-            xr[m] = mma_kc<C>(zero4(), &sP[ti * 16][0], PT, &sKKT[tj * 16][0], PT);
-            rr2[m] = mma_kc<C>(zero4(), &sA[ti * 16][0], PT, &sKKT[tj * 16][0], PT);
-            const f32x4 y1 = mma_kc<C>(zero4(), &sPT[ti * 16][0], PT, &sQKT[tj * 16][0], PT);
-            yr[m] = mma_kc<C>(zero4(), &sAT[ti * 16][0], PT, &sKKT[tj * 16][0], PT);
+            xr[m] = mma_ctab<C>(zero4(), &sP[ti * 16][0], PT, sKK, tj * 16, 0);
+            rr2[m] = mma_ctab<C>(zero4(), &sA[ti * 16][0], PT, sKK, tj * 16, 0);
+            const f32x4 y1 = mma_ctab<C>(zero4(), &sPT[ti * 16][0], PT, sQK, tj * 16, 0);
+            yr[m] = mma_ctab<C>(zero4(), &sAT[ti * 16][0], PT, sKK, tj * 16, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 xr[m][r] *= scale;
@@ -1801,14 +1843,19 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         }
     }
 
-    // ---- pairs that span two 16-token tiles: levels h = 32, 16 of the
+    // ---- pairs that span two 8-token parts: levels h = 32, 16, 8 of the
     // block-boundary split.  With F the level factor of each own row (query
     // rows prod_{s=m+1..r} a_s, key rows prod_{s=r+1..m} a_s, m the last token
     // of the earlier half) the tables hold (q o F)^T and (k o F)^T, and
     //   query rows: R1 = dPs KK,      R2 = dA KK
     //   key rows:   R1 = dPs^T QK,    R2 = (diag(beta) dA)^T KK
+    // At h = 32, 16 a 16-row MFMA tile is all query or all key rows.  At h = 8
+    // its rows 8..15 are query rows and 0..7 key rows of one 16-token block: a
+    // lane of the A operand supplies dPs (query row, key columns) or dPs^T (key
+    // row, query columns) and zeros elsewhere, and the B operand's key rows come
+    // from KK and its query rows from QK, so one product gives both sides.
 #pragma unroll
-    for (int lvl = 0; lvl < 2; ++lvl) {
+    for (int lvl = 0; lvl < 3; ++lvl) {
         const int hl = C >> (lvl + 1);
         float F[RPP];
         const int base = (p0 / (2 * hl)) * (2 * hl);
@@ -1839,8 +1886,8 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                 const uint2 q1 = pack4_bf16(qv[i + 4] * F[i + 4], qv[i + 5] * F[i + 5], qv[i + 6] * F[i + 6], qv[i + 7] * F[i + 7]);
                 const uint2 k0 = pack4_bf16(kv[i] * F[i], kv[i + 1] * F[i + 1], kv[i + 2] * F[i + 2], kv[i + 3] * F[i + 3]);
                 const uint2 k1 = pack4_bf16(kv[i + 4] * F[i + 4], kv[i + 5] * F[i + 5], kv[i + 6] * F[i + 6], kv[i + 7] * F[i + 7]);
-                *reinterpret_cast<uint4*>(&sQKT[cl][p0 + i]) = uint4{q0.x, q0.y, q1.x, q1.y};
-                *reinterpret_cast<uint4*>(&sKKT[cl][p0 + i]) = uint4{k0.x, k0.y, k1.x, k1.y};
+                sQK[ctab_slot(cl, (p0 + i) / 8)] = uint4{q0.x, q0.y, q1.x, q1.y};
+                sKK[ctab_slot(cl, (p0 + i) / 8)] = uint4{k0.x, k0.y, k1.x, k1.y};
             }
         }
         __syncthreads();
@@ -1852,23 +1899,41 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                 const int ti = idx / (HC / 16), tj = idx % (HC / 16);
                 const int tbase = (ti * 16 / (2 * hl)) * (2 * hl);
                 const bool qt = ti * 16 >= tbase + hl;
-                const int kb = qt ? tbase : tbase + hl;  // first row of the summed half
-                const bf16* A1 = qt ? &sP[ti * 16][kb] : &sPT[ti * 16][kb];
-                const bf16* A2 = qt ? &sA[ti * 16][kb] : &sAT[ti * 16][kb];
-                const bf16* B1 = qt ? &sKKT[tj * 16][kb] : &sQKT[tj * 16][kb];
-                const bf16* B2 = &sKKT[tj * 16][kb];
                 f32x4 r1, r2;
-                if (hl == 32) {
-                    r1 = mma_kc<32>(zero4(), A1, PT, B1, PT);
-                    r2 = mma_kc<32>(zero4(), A2, PT, B2, PT);
+                if (hl >= 16) {
+                    const int kb = qt ? tbase : tbase + hl;  // first row of the summed half
+                    const bf16* A1 = qt ? &sP[ti * 16][kb] : &sPT[ti * 16][kb];
+                    const bf16* A2 = qt ? &sA[ti * 16][kb] : &sAT[ti * 16][kb];
+                    const uint4* B1 = qt ? sKK : sQK;
+                    if (hl == 32) {
+                        r1 = mma_ctab<32>(zero4(), A1, PT, B1, tj * 16, kb);
+                        r2 = mma_ctab<32>(zero4(), A2, PT, sKK, tj * 16, kb);
+                    } else {
+                        r1 = mma_ctab<16>(zero4(), A1, PT, B1, tj * 16, kb);
+                        r2 = mma_ctab<16>(zero4(), A2, PT, sKK, tj * 16, kb);
+                    }
                 } else {
-                    r1 = mma_kc16(zero4(), A1, PT, B1, PT);
-                    r2 = mma_kc16(zero4(), A2, PT, B2, PT);
+                    // h = 8, K = the tile's own 16 rows on the K = 32 instruction:
+                    // lane (row rr, K half ko); lanes of the upper K half (kk >= 2)
+                    // supply zeros
+                    const int l = lane_id(), rr = l & 15, kk = l >> 4, ko = 8 * (kk & 1);
+                    const int row = ti * 16 + rr;
+                    const bool qrow = rr >= 8;
+                    const bool live = kk < 2 && (qrow ? ko == 0 : ko == 8);
+                    bf16x8 a1 = *reinterpret_cast<const bf16x8*>(qrow ? &sP[row][ti * 16] : &sPT[row][ti * 16 + 8]);
+                    bf16x8 a2 = *reinterpret_cast<const bf16x8*>(qrow ? &sA[row][ti * 16] : &sAT[row][ti * 16 + 8]);
+                    const int slot = ctab_slot(tj * 16 + rr, 2 * ti + (kk & 1));
+                    bf16x8 b1 = __builtin_bit_cast(bf16x8, ko == 0 ? sKK[slot] : sQK[slot]);
+                    bf16x8 b2 = __builtin_bit_cast(bf16x8, sKK[slot]);
+                    if (!live) a1 = a2 = bf16x8{};
+                    if (kk >= 2) b1 = b2 = bf16x8{};
+                    r1 = mfma_bf16_16x16x32(a1, b1, zero4());
+                    r2 = mfma_bf16_16x16x32(a2, b2, zero4());
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
-                    if (qt) {
+                    if (hl >= 16 ? qt : (i & 15) >= 8) {
                         sR[i][j] = scale * r1[r];
                         sR2[(i / (2 * hl)) * hl + (i % hl)][j] = r2[r];
                     } else {
@@ -1901,8 +1966,8 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         }
     }
 
-    // ---- pairs inside one 16-token tile (j < i), on VALU: this thread owns
-    // channel c of all 16 rows of its tile; E_ij = prod_{s=j+1..i} a_s.  Row
+    // ---- pairs inside one 8-token part (j < i), on VALU: this thread owns
+    // channel c of all 8 rows of its part; E_ij = prod_{s=j+1..i} a_s.  Row
     // sums rq (of dP E k), ra (of dA E k) and column sums cs (of dP E q +
     // dA E beta k) give the decay gradient too: d/dG_i E_ij = E_ij = -d/dG_j E_ij.
     if (cp) {
@@ -2192,7 +2257,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
         auto launch2 = [&](auto pch, auto l2n) {
             GDN_LAUNCH("bchunk2",
                        (bchunk2c_kernel<C, DK, decltype(pch)::value, decltype(l2n)::value>), g2,
-                       dim3(NTHR_F), st, (const bf16*)q, (const bf16*)k, g, beta,
+                       dim3(bchunk2c_threads<C, DK>()), st, (const bf16*)q, (const bf16*)k, g, beta,
                        (const bf16*)(ws + p.o_dQg), (const bf16*)(ws + p.o_dWg),
                        (const bf16*)(ws + p.o_dKh), (const bf16*)(ws + p.o_dPs),
                        (const bf16*)(ws + p.o_dT1), (const float*)(ws + p.o_dgm), (bf16*)dq,
