@@ -707,10 +707,19 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             *reinterpret_cast<uint2*>(&sdS[i][j4]) = d2;
         }
         *reinterpret_cast<uint2*>(&sdD[rd][jd]) = pdD;
-        dDT16[(jd + 0) * PT + rd] = (uint16_t)(pdD.x & 0xFFFFu);
-        dDT16[(jd + 1) * PT + rd] = (uint16_t)(pdD.x >> 16);
-        dDT16[(jd + 2) * PT + rd] = (uint16_t)(pdD.y & 0xFFFFu);
-        dDT16[(jd + 3) * PT + rd] = (uint16_t)(pdD.y >> 16);
+        {
+            // dD^T as 32-bit words of two rows: lanes l and l + 8 of a 16-lane
+            // row hold rows rd (even) and rd + 1 of the same four columns; the
+            // lower one writes columns jd, jd + 1 and the upper one jd + 2, jd + 3
+            const bool up = (tid & 8) != 0;
+            const uint32_t give = up ? pdD.x : pdD.y;
+            const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)give, 0x128, 0xF, 0xF, false);  // row_ror:8
+            const uint32_t mine = up ? pdD.y : pdD.x;
+            const uint32_t lo = up ? got : mine, hi = up ? mine : got;  // rows rd & ~1, rd | 1
+            const int r0 = rd & ~1, c0 = jd + (up ? 2 : 0);
+            *reinterpret_cast<uint32_t*>(&dDT16[c0 * PT + r0]) = (lo & 0xFFFFu) | (hi << 16);
+            *reinterpret_cast<uint32_t*>(&dDT16[(c0 + 1) * PT + r0]) = (lo >> 16) | (hi & 0xFFFF0000u);
+        }
         *reinterpret_cast<uint2*>(&sU[rd][jd]) = pack4_bf16(pU.x, pU.y, pU.z, pU.w);
         if (lowh) {
             *reinterpret_cast<uint4*>(&sD[r8][j8]) = pa;
@@ -772,8 +781,10 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             const int idx = w + NW * m;
             if (idx < T2) {
                 const int ti = idx / NB, tj = idx % NB;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dAp[(ti * 16 + 4 * lq + r) * C + tj * 16 + lr] = f32_to_bf16(oA[m][r]);
+                const uint2 wa = acc_colpairs(f32x4{oA[m][0], oA[m][1], oA[m][2], oA[m][3]});
+                const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
+                *reinterpret_cast<uint32_t*>(&dAp[i2 * C + j2]) = wa.x;
+                *reinterpret_cast<uint32_t*>(&dAp[(i2 + 1) * C + j2]) = wa.y;
             }
         }
 #pragma unroll
@@ -835,13 +846,20 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                     const int ti = idx / (BW / 16), tj = idx % (BW / 16);
                     f32x4 dx = mma_kc<C>(zero4(), &sTTh[ti * 16][0], PT, reinterpret_cast<const bf16*>(dDT16) + tj * 16 * PT, PT);
                     dx = mma_kc<C>(dx, &sTTl[ti * 16][0], PT, reinterpret_cast<const bf16*>(dDT16) + tj * 16 * PT, PT);
+                    f32x4 bdx;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                        sDV[i][v0 + j] = f32_to_bf16(sbeta[i] * dx[r]);
+                        bdx[r] = sbeta[i] * dx[r];
                         dbr[m][r] += dx[r] * sv[i][j];
-                        sdX[i][j] = f32_to_bf16(dx[r]);
                     }
+                    // dv and dX_V as 32-bit words of column pairs
+                    const uint2 wv2 = acc_colpairs(bdx), wx2 = acc_colpairs(dx);
+                    const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
+                    *reinterpret_cast<uint32_t*>(&sDV[i2][v0 + j2]) = wv2.x;
+                    *reinterpret_cast<uint32_t*>(&sDV[i2 + 1][v0 + j2]) = wv2.y;
+                    *reinterpret_cast<uint32_t*>(&sdX[i2][j2]) = wx2.x;
+                    *reinterpret_cast<uint32_t*>(&sdX[i2 + 1][j2]) = wx2.y;
                 }
             }
 #pragma unroll
@@ -896,11 +914,13 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             const int idx = w + NW * m;
             if (idx < T3) {
                 const int ti = idx / (DK / 16), tj = idx % (DK / 16);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                    dQp[i * DK + j] = f32_to_bf16(aQ[m][r]);
-                    dKp[i * DK + j] = f32_to_bf16(aK[m][r]);
+                {
+                    const uint2 wq = acc_colpairs(aQ[m]), wk = acc_colpairs(aK[m]);
+                    const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
+                    *reinterpret_cast<uint32_t*>(&dQp[i2 * DK + j2]) = wq.x;
+                    *reinterpret_cast<uint32_t*>(&dQp[(i2 + 1) * DK + j2]) = wq.y;
+                    *reinterpret_cast<uint32_t*>(&dKp[i2 * DK + j2]) = wk.x;
+                    *reinterpret_cast<uint32_t*>(&dKp[(i2 + 1) * DK + j2]) = wk.y;
                 }
                 // dW = -aW, stored transposed for dX_K = T^T dW (4 consecutive rows per lane)
                 *reinterpret_cast<uint2*>(&sdWT[tj * 16 + lr][ti * 16 + 4 * lq]) =
@@ -913,11 +933,10 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             const int idx = w + NW * m;
             if (idx < T2) {
                 const int ti = idx / NB, tj = idx % NB;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                    dPp[i * C + j] = f32_to_bf16(aP[m][r]);
-                }
+                const uint2 wp = acc_colpairs(aP[m]);
+                const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
+                *reinterpret_cast<uint32_t*>(&dPp[i2 * C + j2]) = wp.x;
+                *reinterpret_cast<uint32_t*>(&dPp[(i2 + 1) * C + j2]) = wp.y;
             }
         }
 
@@ -940,13 +959,18 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const int ti = idx / (DK / 16), tj = idx % (DK / 16);
                 f32x4 acc = mma_kc<C>(zero4(), &sTTh[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
                 acc = mma_kc<C>(acc, &sTTl[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
+                f32x4 hi, lo;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                    const bf16 hi = f32_to_bf16(acc[r]);
-                    sXh[i][j] = hi;
-                    sXl[i][j] = f32_to_bf16(acc[r] - to_f32(hi));
+                    hi[r] = to_f32(f32_to_bf16(acc[r]));
+                    lo[r] = acc[r] - hi[r];
                 }
+                const uint2 wh = acc_colpairs(hi), wl = acc_colpairs(lo);
+                const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
+                *reinterpret_cast<uint32_t*>(&sXh[i2][j2]) = wh.x;
+                *reinterpret_cast<uint32_t*>(&sXh[i2 + 1][j2]) = wh.y;
+                *reinterpret_cast<uint32_t*>(&sXl[i2][j2]) = wl.x;
+                *reinterpret_cast<uint32_t*>(&sXl[i2 + 1][j2]) = wl.y;
             }
         }
         __syncthreads();
@@ -1467,35 +1491,59 @@ constexpr int bchunk2c_threads()
 // groups, and the 16 threads of a part writing their slots do too.
 __device__ __forceinline__ int ctab_slot(int ch, int s) { return ch * 8 + (s ^ ((ch >> 1) & 7)); }
 
-// 16x16 tile (rows of A x channels ch0..ch0+15) summed over K = 16, 32 or 64
-// token rows from kb (a multiple of 8; of 32 when K >= 32): A row-major bf16,
-// K contiguous, pointing at the first summed column; B from a channel-major
-// table.  K = 16 runs on the K = 32 instruction with a zero upper B half.
-template <int K>
-__device__ __forceinline__ f32x4 mma_ctab(f32x4 acc, const bf16* __restrict__ A, int lda,
-                                          const uint4* __restrict__ tab, int ch0, int kb)
+// B fragment of a channel-major table: lane (r, kk) supplies 8-row slot
+// slot0 + kk of channel ch0 + r; HALF (K = 16): lanes kk >= 2 supply zeros and
+// the others slots slot0, slot0 + 1
+template <bool HALF>
+__device__ __forceinline__ bf16x8 ctab_frag(const uint4* __restrict__ tab, int ch0, int slot0)
 {
-    const int l = lane_id(), r = l & 15, kk = l >> 4;
-    if constexpr (K == 16) {
-        const int ko = 8 * (kk & 1);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + ko);
-        bf16x8 b = __builtin_bit_cast(bf16x8, tab[ctab_slot(ch0 + r, (kb + ko) / 8)]);
-        if (kk >= 2) b = bf16x8{};
-        return mfma_bf16_16x16x32(a, b, acc);
-    } else {
-        static_assert(K % 32 == 0, "K = 16, 32 or 64");
+    const int l = lane_id(), kk = l >> 4;
+    const bf16x8 b = __builtin_bit_cast(bf16x8, tab[ctab_slot(ch0 + (l & 15), slot0 + (HALF ? kk & 1 : kk))]);
+    return HALF && kk >= 2 ? bf16x8{} : b;
+}
+
+// Score tables of bchunk2c (dPs, dA): C = 64 token rows of 64 bf16, 128 bytes
+// a row.  16-byte unit u of row R sits at R * 8 + (u ^ sswz(R)).  With this
+// swizzle both operand reads below touch every LDS bank once per access phase:
+// the 16-byte reads of 16 rows (K along a row) and the transposing 8-byte
+// reads (K down the rows).
+__device__ __forceinline__ int sswz(int R) { return (R & 2) | ((R >> 1) & 4); }
+__device__ __forceinline__ int sunit(int R, int u) { return R * 8 + (u ^ sswz(R)); }
+
+// MFMA A operand with K along the rows of a score table:
+// A(m, k) = X(r0 + m, k0 + k), k0 a multiple of 8.  HALF (K = 16): lanes kk >= 2
+// repeat kk - 2 (their B operand is zero).
+template <bool HALF>
+__device__ __forceinline__ bf16x8 sfrag_row(const uint4* X, int r0, int k0)
+{
+    const int l = lane_id(), kk = HALF ? (l >> 4) & 1 : l >> 4;
+    return __builtin_bit_cast(bf16x8, X[sunit(r0 + (l & 15), (k0 >> 3) + kk)]);
+}
+
+// MFMA A operand of the transpose, K down the rows: A(m, k) = X(k0 + k, m0 + m),
+// from two transposing loads (ds_read_b64_tr_b16).  Within each group of 16
+// lanes such a load hands lane i element i & 3 of the four 16-bit values read
+// by lane 4 e + (i >> 2), as its element e (e = 0..3).  So lane j of group g
+// reads row k0 + 8 g + 4 h + (j >> 2), columns m0 + 4 (j & 3) .. + 3, and lane m
+// receives X(k0 + 8 g + 4 h + e, m0 + m) = A(m, 8 g + 4 h + e).  m0 is a multiple
+// of 16.  HALF (K = 16): groups g >= 2 repeat g - 2.
+template <bool HALF>
+__device__ __forceinline__ bf16x8 sfrag_tr(const uint4* X, int k0, int m0)
+{
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int l = lane_id(), j = l & 15, g = HALF ? (l >> 4) & 1 : l >> 4;
+    s16x4 v[2];
 #pragma unroll
-        for (int k = 0; k < K; k += 32) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + k + 8 * kk);
-            const bf16x8 b = __builtin_bit_cast(bf16x8, tab[ctab_slot(ch0 + r, (kb + k) / 8 + kk)]);
-            acc = mfma_bf16_16x16x32(a, b, acc);
-        }
-        return acc;
+    for (int h = 0; h < 2; ++h) {
+        const int k = k0 + 8 * g + 4 * h + (j >> 2);
+        const char* p = reinterpret_cast<const char*>(X + sunit(k, (m0 >> 3) + ((j & 3) >> 1))) + 8 * (j & 1);
+        v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
     }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 template <int C, int DK, bool PCH, bool L2N>
-__global__ void __launch_bounds__((C / 8) * (DK / 2))  // bchunk2c_threads
+__global__ void __launch_bounds__((C / 8) * (DK / 2)) __attribute__((amdgpu_waves_per_eu(4)))  // bchunk2c_threads; 4 waves per SIMD: 2 workgroups a CU
 bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
                 const float* __restrict__ beta, const bf16* __restrict__ dQgi,
                 const bf16* __restrict__ dXKi, const bf16* __restrict__ dKhi,
@@ -1510,32 +1558,39 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     constexpr int NB = C / 16, NW = NTHR_F / 64;
     constexpr int RPP = 8, NPART = C / RPP;
     static_assert(NPART * HC == NTHR_F, "one column thread per (part, channel)");
-    constexpr int PT = C + 8;  // bf16 pitch: 16-byte rows, banks spread
-    constexpr int PH = HC + 1; // fp32 pitch of the result tables
     // LDS, one buffer with named parts:
-    //  score gradients, bf16: dPs (unscaled, lower incl. diagonal) and dA (strictly
-    //  lower) by rows and transposed, the transposed dA with beta_i folded in;
-    //  level tables (channel-major, ctab_slot); level results: query rows
-    //  scale*R1, key rows scale*R1 + R2 (sR), query rows' R2 (sR2, C/2 rows).
-    //  Before the levels sR also holds the dKh row-sum partials.  Per-head decay
-    //  uses, after its score products, the first 3 C x PH fp32 tables' worth of
-    //  bytes for their results.
-    static_assert(C == 8 * 8, "channel-major tables of eight 8-row slots");
-    constexpr int TB = C * PT * 2, O_QK = 4 * TB, O_KK = O_QK + HC * C * 2;
-    constexpr int O_R = O_KK + HC * C * 2, O_R2 = O_R + C * PH * 4, LDSB = O_R2 + (C / 2) * PH * 4;
-    static_assert(3 * C * PH * 4 <= O_R, "per-head results fit below the level results");
+    //  score gradients, bf16, by rows (sunit): dPs (unscaled, lower incl.
+    //  diagonal) and dA (strictly lower); their transposes are read from the
+    //  same tables with transposing loads;
+    //  level tables (channel-major, ctab_slot): q and k rows times the level
+    //  factor, and the k rows times beta as well (the key side of dA^T);
+    //  level results (fp32 [rows][HC], ridx): query rows scale*R1, key rows
+    //  scale*R1 + R2 (sR), query rows' R2 (sR2, C/2 rows).  Before the levels sR
+    //  also holds the dKh row-sum partials.  Per-head decay uses, after its score
+    //  products, the first three C x HC fp32 tables' worth of bytes for their
+    //  results.
+    static_assert(C == 8 * 8, "score rows and channel-major tables of eight 16-byte units");
+    constexpr int TB = C * C * 2, O_QK = 2 * TB, O_KK = O_QK + HC * C * 2, O_KB = O_KK + HC * C * 2;
+    constexpr int O_R = O_KB + HC * C * 2, O_R2 = O_R + C * (HC + 1) * 4, LDSB = O_R2 + (C / 2) * (HC + 1) * 4;
+    static_assert(3 * C * (HC + 1) * 4 <= O_R2, "per-head results fit below sR2 (sR is not live then)");
     __shared__ __align__(16) char sbuf[LDSB];
-    bf16 (*sP)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);
-    bf16 (*sPT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + TB);
-    bf16 (*sA)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + 2 * TB);
-    bf16 (*sAT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + 3 * TB);
+    uint4* sPv = reinterpret_cast<uint4*>(sbuf);        // dPs rows
+    uint4* sAv = reinterpret_cast<uint4*>(sbuf + TB);   // dA rows
     uint4* sQK = reinterpret_cast<uint4*>(sbuf + O_QK);  // q rows (times a factor), by channel
     uint4* sKK = reinterpret_cast<uint4*>(sbuf + O_KK);  // k rows (times a factor), by channel
-    float (*sR)[PH] = reinterpret_cast<float (*)[PH]>(sbuf + O_R);
-    float (*sR2)[PH] = reinterpret_cast<float (*)[PH]>(sbuf + O_R2);
+    uint4* sKB = reinterpret_cast<uint4*>(sbuf + O_KB);  // beta k rows (times a factor), by channel
+    float* sR = reinterpret_cast<float*>(sbuf + O_R);
+    float* sR2 = reinterpret_cast<float*>(sbuf + O_R2);
+    // fp32 [rows][HC] tables, rows padded by one word
+    constexpr int PH = HC + 1;
+    auto ridx = [](int i, int j) { return i * PH + j; };
+    // element (R, c) of a score table
+    auto sel = [](const uint4* X, int R, int c) {
+        return to_f32(reinterpret_cast<const bf16*>(X + sunit(R, c >> 3))[c & 7]);
+    };
     __shared__ float sbeta[C], stot[NPART][HC];
     __shared__ float sG[C];  // per-head decay: chunk-local inclusive cumsum of g
-    float (*sext)[HC] = reinterpret_cast<float (*)[HC]>(&sR[0][0]);
+    float (*sext)[HC] = reinterpret_cast<float (*)[HC]>(sR);
 
     // block -> (chunk-head, half): the two halves of a chunk-head are 8 ids
     // apart, so they run on the same XCD and share its L2 for the C x C tables
@@ -1612,32 +1667,20 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         const bf16* Pp = dPsi + (size_t)ch * C * C;
         const bf16* Ap = dAi + (size_t)ch * C * C;
         uint4 pw[NU], aw[NU];
-        float bw[NU];
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int idx = min(tid + NTHR_F * u, NC8 - 1);
             pw[u] = *reinterpret_cast<const uint4*>(Pp + 8 * idx);
             aw[u] = *reinterpret_cast<const uint4*>(Ap + 8 * idx);
-            bw[u] = beta[tok0 + (size_t)min(idx / (C / 8), nvalid - 1) * H];
         }
         const float bv = beta[tok0 + (size_t)min(tid % C, nvalid - 1) * H];
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int idx = tid + NTHR_F * u;
             if (idx < NC8) {
-                const int i = idx / (C / 8), j0 = (idx % (C / 8)) * 8;
-                *reinterpret_cast<uint4*>(&sP[i][j0]) = pw[u];
-                *reinterpret_cast<uint4*>(&sA[i][j0]) = aw[u];
-                const float bi = i < nvalid ? bw[u] : 0.f;
-                const uint32_t pu[4] = {pw[u].x, pw[u].y, pw[u].z, pw[u].w};
-                const uint32_t au[4] = {aw[u].x, aw[u].y, aw[u].z, aw[u].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sPT[j0 + 2 * e][i].bits = (uint16_t)(pu[e] & 0xFFFFu);
-                    sPT[j0 + 2 * e + 1][i].bits = (uint16_t)(pu[e] >> 16);
-                    sAT[j0 + 2 * e][i] = f32_to_bf16(bi * __uint_as_float(au[e] << 16));
-                    sAT[j0 + 2 * e + 1][i] = f32_to_bf16(bi * __uint_as_float(au[e] & 0xFFFF0000u));
-                }
+                const int i = idx / (C / 8), uu = idx % (C / 8);
+                sPv[sunit(i, uu)] = pw[u];
+                sAv[sunit(i, uu)] = aw[u];
             }
         }
         if (tid < C) sbeta[tid] = tid < nvalid ? bv : 0.f;
@@ -1714,26 +1757,24 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         //   X = scale dP~ K  (dq),   R = dA~ K  (query side of dk and dbeta),
         //   Y = scale dP~^T Q + (diag(beta) dA~)^T K  (key side of dk),
         // and dG = q o X + beta k o R - k o Y (the diagonal, E = 1, cancels in dG).
-        // Scale the score tables by E in place (rows: E(i, j); transposed: E(j', i')).
-        // With L2N (x_hat = r x) the operand tables hold the raw bf16 rows, and
-        // dP~ takes r_q(i) r_k(j), dA~ r_k(i) r_k(j), in both orientations; the
-        // products X', R', Y' against raw rows then give X = X' / r_q(i),
+        // Scale the score tables by E in place; the transposed operands are read
+        // from the same scaled values.  With L2N (x_hat = r x) the operand tables
+        // hold the raw bf16 rows, and dP~ takes r_q(i) r_k(j), dA~ r_k(i) r_k(j);
+        // the products X', R', Y' against raw rows then give X = X' / r_q(i),
         // R = R' / r_k(i), Y = Y' / r_k(j), and dG = q o X' + beta k o R' - k o Y'
         // with the raw q, k: the plain path's arithmetic, whose pairs (i, j)
         // cancel in dG's reverse sum because both sides read one rounded value.
-        for (int e = tid; e < 2 * C * (C / 8); e += NTHR_F) {
-            const bool tr = e >= C * (C / 8);
-            const int f = tr ? e - C * (C / 8) : e;
-            const int rr = f / (C / 8), c0 = (f % (C / 8)) * 8;
-            bf16* t1 = tr ? &sPT[rr][c0] : &sP[rr][c0];
-            bf16* t2 = tr ? &sAT[rr][c0] : &sA[rr][c0];
-            uint4 w1 = *reinterpret_cast<const uint4*>(t1), w2 = *reinterpret_cast<const uint4*>(t2);
+        for (int e = tid; e < C * (C / 8); e += NTHR_F) {
+            const int rr = e / (C / 8), uu = e % (C / 8), c0 = uu * 8;
+            uint4* t1 = &sPv[sunit(rr, uu)];
+            uint4* t2 = &sAv[sunit(rr, uu)];
+            uint4 w1 = *t1, w2 = *t2;
             uint32_t u1[4] = {w1.x, w1.y, w1.z, w1.w}, u2[4] = {w2.x, w2.y, w2.z, w2.w};
             float ev[8];
             float ev2[8];
 #pragma unroll
             for (int z = 0; z < 8; ++z) {
-                const int i = tr ? c0 + z : rr, j = tr ? rr : c0 + z;  // element (i, j) of the C x C matrix
+                const int i = rr, j = c0 + z;  // element (i, j) of the C x C matrix
                 ev[z] = j <= i ? fast_exp(sG[i] - sG[j]) : 0.f;
                 ev2[z] = ev[z];
                 if constexpr (L2N) {
@@ -1748,10 +1789,10 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                 u1[z] = (uint32_t)f32_to_bf16(p0v).bits | ((uint32_t)f32_to_bf16(p1v).bits << 16);
                 u2[z] = (uint32_t)f32_to_bf16(a0v).bits | ((uint32_t)f32_to_bf16(a1v).bits << 16);
             }
-            *reinterpret_cast<uint4*>(t1) = uint4{u1[0], u1[1], u1[2], u1[3]};
-            *reinterpret_cast<uint4*>(t2) = uint4{u2[0], u2[1], u2[2], u2[3]};
+            *t1 = uint4{u1[0], u1[1], u1[2], u1[3]};
+            *t2 = uint4{u2[0], u2[1], u2[2], u2[3]};
         }
-        // q^T and k^T, channel-major (the level tables with factor 1).  With L2N
+        // q^T, k^T and (beta k)^T, channel-major (the level tables with factor 1).  With L2N
         // the raw rows: x_hat / r is within 2^-23 of the raw bf16 value, far
         // inside half a bf16 step, so the bf16 rounding gives it back exactly.
         auto raw_q = [&](int i) {
@@ -1773,8 +1814,14 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                 const uint2 q1 = pack4_bf16(qx[i + 4], qx[i + 5], qx[i + 6], qx[i + 7]);
                 const uint2 k0 = pack4_bf16(kx[i], kx[i + 1], kx[i + 2], kx[i + 3]);
                 const uint2 k1 = pack4_bf16(kx[i + 4], kx[i + 5], kx[i + 6], kx[i + 7]);
+                float bk[8];
+#pragma unroll
+                for (int z = 0; z < 8; ++z) bk[z] = sbeta[p0 + i + z] * kx[i + z];
+                const uint2 b0 = pack4_bf16(bk[0], bk[1], bk[2], bk[3]);
+                const uint2 b1 = pack4_bf16(bk[4], bk[5], bk[6], bk[7]);
                 sQK[ctab_slot(cl, (p0 + i) / 8)] = uint4{q0.x, q0.y, q1.x, q1.y};
                 sKK[ctab_slot(cl, (p0 + i) / 8)] = uint4{k0.x, k0.y, k1.x, k1.y};
+                sKB[ctab_slot(cl, (p0 + i) / 8)] = uint4{b0.x, b0.y, b1.x, b1.y};
             }
         }
         __syncthreads();
@@ -1784,10 +1831,18 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         for (int m = 0; m < M3; ++m) {
             const int idx = w + NW * m;
             const int ti = (idx % T3) / (HC / 16), tj = idx % (HC / 16);
-            xr[m] = mma_ctab<C>(zero4(), &sP[ti * 16][0], PT, sKK, tj * 16, 0);
-            rr2[m] = mma_ctab<C>(zero4(), &sA[ti * 16][0], PT, sKK, tj * 16, 0);
-            const f32x4 y1 = mma_ctab<C>(zero4(), &sPT[ti * 16][0], PT, sQK, tj * 16, 0);
-            yr[m] = mma_ctab<C>(zero4(), &sAT[ti * 16][0], PT, sKK, tj * 16, 0);
+            f32x4 y1 = zero4();
+            xr[m] = rr2[m] = yr[m] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < C; kb += 32) {
+                const bf16x8 ap = sfrag_row<false>(sPv, ti * 16, kb), aa = sfrag_row<false>(sAv, ti * 16, kb);
+                const bf16x8 tp = sfrag_tr<false>(sPv, kb, ti * 16), ta = sfrag_tr<false>(sAv, kb, ti * 16);
+                const bf16x8 bk = ctab_frag<false>(sKK, tj * 16, kb / 8);
+                xr[m] = mfma_bf16_16x16x32(ap, bk, xr[m]);
+                rr2[m] = mfma_bf16_16x16x32(aa, bk, rr2[m]);
+                y1 = mfma_bf16_16x16x32(tp, ctab_frag<false>(sQK, tj * 16, kb / 8), y1);
+                yr[m] = mfma_bf16_16x16x32(ta, ctab_frag<false>(sKB, tj * 16, kb / 8), yr[m]);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 xr[m][r] *= scale;
@@ -1795,9 +1850,9 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             }
         }
         __syncthreads();  // every read of the tables is done: their bytes take the results
-        float (*sX)[PH] = reinterpret_cast<float (*)[PH]>(sbuf);
-        float (*sRq)[PH] = reinterpret_cast<float (*)[PH]>(sbuf + C * PH * 4);
-        float (*sY)[PH] = reinterpret_cast<float (*)[PH]>(sbuf + 2 * C * PH * 4);
+        float* sX = reinterpret_cast<float*>(sbuf);
+        float* sRq = reinterpret_cast<float*>(sbuf + C * PH * 4);
+        float* sY = reinterpret_cast<float*>(sbuf + 2 * C * PH * 4);
 #pragma unroll
         for (int m = 0; m < M3; ++m) {
             const int idx = w + NW * m;
@@ -1806,9 +1861,9 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
-                    sX[i][j] = xr[m][r];
-                    sRq[i][j] = rr2[m][r];
-                    sY[i][j] = yr[m][r];
+                    sX[ridx(i, j)] = xr[m][r];
+                    sRq[ridx(i, j)] = rr2[m][r];
+                    sY[ridx(i, j)] = yr[m][r];
                 }
             }
         }
@@ -1817,7 +1872,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
 #pragma unroll
             for (int i = 0; i < RPP; ++i) {
                 const int r = p0 + i;
-                const float X = sX[r][cl], R = sRq[r][cl], Y = sY[r][cl], bt = sbeta[r];
+                const float X = sX[ridx(r, cl)], R = sRq[ridx(r, cl)], Y = sY[ridx(r, cl)], bt = sbeta[r];
                 if constexpr (L2N) {
                     const float qr = raw_q(i), kr = raw_k(i);
                     dq[i] += X / sRn[r];
@@ -1837,7 +1892,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     if (cp) {
 #pragma unroll
         for (int i = 0; i < RPP; ++i) {
-            const float dp = scale * to_f32(sP[p0 + i][p0 + i]);
+            const float dp = scale * sel(sPv, p0 + i, p0 + i);
             dq[i] += dp * kv[i];
             dk[i] += dp * qv[i];
         }
@@ -1882,17 +1937,23 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         if (cp) {
 #pragma unroll
             for (int i = 0; i < RPP; i += 8) {
+                float kf[8];
+#pragma unroll
+                for (int z = 0; z < 8; ++z) kf[z] = kv[i + z] * F[i + z];
                 const uint2 q0 = pack4_bf16(qv[i] * F[i], qv[i + 1] * F[i + 1], qv[i + 2] * F[i + 2], qv[i + 3] * F[i + 3]);
                 const uint2 q1 = pack4_bf16(qv[i + 4] * F[i + 4], qv[i + 5] * F[i + 5], qv[i + 6] * F[i + 6], qv[i + 7] * F[i + 7]);
-                const uint2 k0 = pack4_bf16(kv[i] * F[i], kv[i + 1] * F[i + 1], kv[i + 2] * F[i + 2], kv[i + 3] * F[i + 3]);
-                const uint2 k1 = pack4_bf16(kv[i + 4] * F[i + 4], kv[i + 5] * F[i + 5], kv[i + 6] * F[i + 6], kv[i + 7] * F[i + 7]);
+                const uint2 k0 = pack4_bf16(kf[0], kf[1], kf[2], kf[3]);
+                const uint2 k1 = pack4_bf16(kf[4], kf[5], kf[6], kf[7]);
+                const uint2 b0 = pack4_bf16(sbeta[p0 + i] * kf[0], sbeta[p0 + i + 1] * kf[1], sbeta[p0 + i + 2] * kf[2], sbeta[p0 + i + 3] * kf[3]);
+                const uint2 b1 = pack4_bf16(sbeta[p0 + i + 4] * kf[4], sbeta[p0 + i + 5] * kf[5], sbeta[p0 + i + 6] * kf[6], sbeta[p0 + i + 7] * kf[7]);
                 sQK[ctab_slot(cl, (p0 + i) / 8)] = uint4{q0.x, q0.y, q1.x, q1.y};
                 sKK[ctab_slot(cl, (p0 + i) / 8)] = uint4{k0.x, k0.y, k1.x, k1.y};
+                sKB[ctab_slot(cl, (p0 + i) / 8)] = uint4{b0.x, b0.y, b1.x, b1.y};
             }
         }
         __syncthreads();
         constexpr int T3 = NB * (HC / 16), M3 = (T3 + NW - 1) / NW;
-#pragma unroll
+#pragma unroll 1  // one tile at a time: its fragments only are live
         for (int m = 0; m < M3; ++m) {
             const int idx = w + NW * m;
             if (idx < T3) {
@@ -1901,43 +1962,57 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                 const bool qt = ti * 16 >= tbase + hl;
                 f32x4 r1, r2;
                 if (hl >= 16) {
+                    // query tiles: dPs and dA rows against k F; key tiles: their
+                    // transposes against q F and beta k F
                     const int kb = qt ? tbase : tbase + hl;  // first row of the summed half
-                    const bf16* A1 = qt ? &sP[ti * 16][kb] : &sPT[ti * 16][kb];
-                    const bf16* A2 = qt ? &sA[ti * 16][kb] : &sAT[ti * 16][kb];
-                    const uint4* B1 = qt ? sKK : sQK;
                     if (hl == 32) {
-                        r1 = mma_ctab<32>(zero4(), A1, PT, B1, tj * 16, kb);
-                        r2 = mma_ctab<32>(zero4(), A2, PT, sKK, tj * 16, kb);
+                        const bf16x8 a1 = qt ? sfrag_row<false>(sPv, ti * 16, kb) : sfrag_tr<false>(sPv, kb, ti * 16);
+                        const bf16x8 a2 = qt ? sfrag_row<false>(sAv, ti * 16, kb) : sfrag_tr<false>(sAv, kb, ti * 16);
+                        r1 = mfma_bf16_16x16x32(a1, ctab_frag<false>(qt ? sKK : sQK, tj * 16, kb / 8), zero4());
+                        r2 = mfma_bf16_16x16x32(a2, ctab_frag<false>(qt ? sKK : sKB, tj * 16, kb / 8), zero4());
                     } else {
-                        r1 = mma_ctab<16>(zero4(), A1, PT, B1, tj * 16, kb);
-                        r2 = mma_ctab<16>(zero4(), A2, PT, sKK, tj * 16, kb);
+                        const bf16x8 a1 = qt ? sfrag_row<true>(sPv, ti * 16, kb) : sfrag_tr<true>(sPv, kb, ti * 16);
+                        const bf16x8 a2 = qt ? sfrag_row<true>(sAv, ti * 16, kb) : sfrag_tr<true>(sAv, kb, ti * 16);
+                        r1 = mfma_bf16_16x16x32(a1, ctab_frag<true>(qt ? sKK : sQK, tj * 16, kb / 8), zero4());
+                        r2 = mfma_bf16_16x16x32(a2, ctab_frag<true>(qt ? sKK : sKB, tj * 16, kb / 8), zero4());
                     }
                 } else {
                     // h = 8, K = the tile's own 16 rows on the K = 32 instruction:
-                    // lane (row rr, K half ko); lanes of the upper K half (kk >= 2)
-                    // supply zeros
-                    const int l = lane_id(), rr = l & 15, kk = l >> 4, ko = 8 * (kk & 1);
-                    const int row = ti * 16 + rr;
+                    // lane (row rr, K half kk & 1); lanes kk >= 2 supply zeros.  A
+                    // query row takes its dPs / dA row over the key half (a row
+                    // read), a key row dPs^T / dA^T over the query half (a
+                    // transposing read); both reads run on every lane
+                    const int l = lane_id(), rr = l & 15, kk = l >> 4, kh = kk & 1;
                     const bool qrow = rr >= 8;
-                    const bool live = kk < 2 && (qrow ? ko == 0 : ko == 8);
-                    bf16x8 a1 = *reinterpret_cast<const bf16x8*>(qrow ? &sP[row][ti * 16] : &sPT[row][ti * 16 + 8]);
-                    bf16x8 a2 = *reinterpret_cast<const bf16x8*>(qrow ? &sA[row][ti * 16] : &sAT[row][ti * 16 + 8]);
-                    const int slot = ctab_slot(tj * 16 + rr, 2 * ti + (kk & 1));
-                    bf16x8 b1 = __builtin_bit_cast(bf16x8, ko == 0 ? sKK[slot] : sQK[slot]);
-                    bf16x8 b2 = __builtin_bit_cast(bf16x8, sKK[slot]);
-                    if (!live) a1 = a2 = bf16x8{};
-                    if (kk >= 2) b1 = b2 = bf16x8{};
-                    r1 = mfma_bf16_16x16x32(a1, b1, zero4());
-                    r2 = mfma_bf16_16x16x32(a2, b2, zero4());
+                    const bool live = kk < 2 && (qrow ? kh == 0 : kh == 1);
+                    // B: the key half's rows (kh = 0) k F, the query half's q F and
+                    // beta k F
+                    const int slot = ctab_slot(tj * 16 + rr, 2 * ti + kh);
+                    {
+                        const bf16x8 p_row = sfrag_row<true>(sPv, ti * 16, ti * 16);
+                        const bf16x8 p_tr = sfrag_tr<true>(sPv, ti * 16, ti * 16);
+                        const bf16x8 a1 = live ? (qrow ? p_row : p_tr) : bf16x8{};
+                        bf16x8 b1 = __builtin_bit_cast(bf16x8, kh == 0 ? sKK[slot] : sQK[slot]);
+                        if (kk >= 2) b1 = bf16x8{};
+                        r1 = mfma_bf16_16x16x32(a1, b1, zero4());
+                    }
+                    {
+                        const bf16x8 a_row = sfrag_row<true>(sAv, ti * 16, ti * 16);
+                        const bf16x8 a_tr = sfrag_tr<true>(sAv, ti * 16, ti * 16);
+                        const bf16x8 a2 = live ? (qrow ? a_row : a_tr) : bf16x8{};
+                        bf16x8 b2 = __builtin_bit_cast(bf16x8, kh == 0 ? sKK[slot] : sKB[slot]);
+                        if (kk >= 2) b2 = bf16x8{};
+                        r2 = mfma_bf16_16x16x32(a2, b2, zero4());
+                    }
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
                     if (hl >= 16 ? qt : (i & 15) >= 8) {
-                        sR[i][j] = scale * r1[r];
-                        sR2[(i / (2 * hl)) * hl + (i % hl)][j] = r2[r];
+                        sR[ridx(i, j)] = scale * r1[r];
+                        sR2[ridx((i / (2 * hl)) * hl + (i % hl), j)] = r2[r];
                     } else {
-                        sR[i][j] = scale * r1[r] + r2[r];
+                        sR[ridx(i, j)] = scale * r1[r] + r2[r];
                     }
                 }
             }
@@ -1948,7 +2023,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
 #pragma unroll
                 for (int i = 0; i < RPP; ++i) {
                     const int r = p0 + i;
-                    const float R1 = sR[r][cl], R2 = sR2[(r / (2 * hl)) * hl + (r % hl)][cl];
+                    const float R1 = sR[ridx(r, cl)], R2 = sR2[ridx((r / (2 * hl)) * hl + (r % hl), cl)];
                     const float bt = sbeta[r];
                     dq[i] += F[i] * R1;
                     dk[i] += bt * F[i] * R2;
@@ -1958,7 +2033,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             } else {
 #pragma unroll
                 for (int i = 0; i < RPP; ++i) {
-                    const float R = sR[p0 + i][cl];
+                    const float R = sR[ridx(p0 + i, cl)];
                     dk[i] += F[i] * R;
                     dG[i] -= kv[i] * F[i] * R;
                 }
@@ -1978,12 +2053,18 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         for (int i = 1; i < RPP; ++i) {
             const int r = p0 + i;
             const float bi = sbeta[r], bki = bi * kv[i], sqi = scale * qv[i];
+            // this row's columns p0 .. p0 + 7: one 16-byte unit of each table
+            const u32x4 pu = __builtin_bit_cast(u32x4, sPv[sunit(r, p0 >> 3)]);
+            const u32x4 au = __builtin_bit_cast(u32x4, sAv[sunit(r, p0 >> 3)]);
+            auto ext = [](const u32x4& u, int j) {
+                return __uint_as_float((j & 1) ? (u[j >> 1] & 0xFFFF0000u) : (u[j >> 1] << 16));
+            };
             float rq = 0.f, ra = 0.f, E = 1.f;
 #pragma unroll
             for (int j = i - 1; j >= 0; --j) {
                 E *= a[j + 1];
-                const float tP = to_f32(sP[r][p0 + j]) * E;
-                const float tA = to_f32(sA[r][p0 + j]) * E;
+                const float tP = ext(pu, j) * E;
+                const float tA = ext(au, j) * E;
                 rq += tP * kv[j];
                 ra += tA * kv[j];
                 cs[j] += tP * sqi + tA * bki;
@@ -2023,7 +2104,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         for (int i = 0; i < RPP; ++i) {
             const int r = p0 + i;
             dG[i] += add;
-            sR[r][cl] = dbr[i];
+            sR[ridx(r, cl)] = dbr[i];
             if (r < nvalid) {
                 const uint32_t off = (uint32_t)r * rs32 + (uint32_t)c;
                 st32(dqo + tok0 * DK, off, f32_to_bf16(dq[i]));
@@ -2039,7 +2120,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         float sb = 0.f;
         if (r < C) {
 #pragma unroll
-            for (int cc = sub; cc < HC; cc += 4) sb += sR[r][cc];
+            for (int cc = sub; cc < HC; cc += 4) sb += sR[ridx(r, cc)];
         }
         sb += dpp_mov<0xB1>(sb);  // quad sum: neighbour swap, pair swap
         sb += dpp_mov<0x4E>(sb);
@@ -2050,14 +2131,14 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         __syncthreads();
         if (cp) {
 #pragma unroll
-            for (int i = 0; i < RPP; ++i) sR[p0 + i][cl] = dG[i];
+            for (int i = 0; i < RPP; ++i) sR[ridx(p0 + i, cl)] = dG[i];
         }
         __syncthreads();
         const int r = tid >> 2, sub = tid & 3;
         float sg = 0.f;
         if (r < C) {
 #pragma unroll
-            for (int cc = sub; cc < HC; cc += 4) sg += sR[r][cc];
+            for (int cc = sub; cc < HC; cc += 4) sg += sR[ridx(r, cc)];
         }
         sg += dpp_mov<0xB1>(sg);  // quad sum: neighbour swap, pair swap
         sg += dpp_mov<0x4E>(sg);

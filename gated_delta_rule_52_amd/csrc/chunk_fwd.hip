@@ -1255,9 +1255,11 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
 #pragma unroll
             for (int r = 0; r < 4; ++r) dv[r] = uc[m][r] - ws[r];
             *reinterpret_cast<uint2*>(&sDt[tj * 16 + lr][ti * 16 + 4 * lq]) = pack4_bf16(dv[0], dv[1], dv[2], dv[3]);
-            if (SAVE) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sDr[pb][ti * 16 + 4 * lq + r][tj * 16 + lr] = f32_to_bf16(dv[r]);
+            if (SAVE) {  // staged as 32-bit words of column pairs
+                const uint2 wd = acc_colpairs(f32x4{dv[0], dv[1], dv[2], dv[3]});
+                const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
+                *reinterpret_cast<uint32_t*>(&sDr[pb][i2][j2]) = wd.x;
+                *reinterpret_cast<uint32_t*>(&sDr[pb][i2 + 1][j2]) = wd.y;
             }
             if (OUT) o1[m] = mma_kc<DK>(zero4(), &sQ[ti * 16][0], PA, &sSt[tj * 16][0], PA);
         }
@@ -1270,8 +1272,10 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 // P is lower triangular: columns past the tile row are zero
                 const int K = ((16 * (ti + 1) + 31) / 32) * 32;
                 const f32x4 acc = mma_kc_dyn(o1[m], &sP[ti * 16][0], PT, &sDt[tj * 16][0], PT, K);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sOr[pb][ti * 16 + 4 * lq + r][tj * 16 + lr] = f32_to_bf16(acc[r]);
+                const uint2 wo = acc_colpairs(acc);
+                const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
+                *reinterpret_cast<uint32_t*>(&sOr[pb][i2][j2]) = wo.x;
+                *reinterpret_cast<uint32_t*>(&sOr[pb][i2 + 1][j2]) = wo.y;
             }
         }
         // S <- gam o S + Kh^T D
@@ -1286,8 +1290,10 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             *reinterpret_cast<uint2*>(&sSt[sj * 16 + lr][si * 16 + 4 * lq]) =
                 pack4_bf16(sacc[m][0], sacc[m][1], sacc[m][2], sacc[m][3]);
             if (SAVE) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sSf[pb][si * 16 + 4 * lq + r][sj * 16 + lr] = f32_to_bf16(sacc[m][r]);
+                const uint2 wsf = acc_colpairs(sacc[m]);
+                const int i2 = si * 16 + 4 * lq + 2 * (lr & 1), j2 = sj * 16 + (lr & ~1);
+                *reinterpret_cast<uint32_t*>(&sSf[pb][i2][j2]) = wsf.x;
+                *reinterpret_cast<uint32_t*>(&sSf[pb][i2 + 1][j2]) = wsf.y;
             }
         }
         __syncthreads();

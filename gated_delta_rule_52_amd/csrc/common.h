@@ -116,6 +116,22 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// bf16 pairs of neighbouring columns of an MFMA accumulator tile: lanes l and
+// l ^ 1 hold columns j and j ^ 1 of the same four rows 4 (l / 16) + r.  After one
+// exchange the even lane holds rows 0, 1 and the odd lane rows 2, 3 of those
+// four, each as one 32-bit word of columns (j & ~1, j | 1) rounded to bf16:
+// .x is row 4 (l / 16) + 2 (l & 1), .y the row after it.  Both lanes of every
+// pair must be active.
+__device__ __forceinline__ uint2 acc_colpairs(f32x4 v)
+{
+    const bool odd = (lane_id() & 1) != 0;
+    const float s0 = odd ? v[0] : v[2], s1 = odd ? v[1] : v[3];  // the rows the neighbour writes
+    const float n0 = dpp_mov<0xB1>(s0), n1 = dpp_mov<0xB1>(s1);  // quad_perm [1,0,3,2]
+    const float a0 = odd ? n0 : v[0], b0 = odd ? v[2] : n0;
+    const float a1 = odd ? n1 : v[1], b1 = odd ? v[3] : n1;
+    return uint2{cvt2_bf16(a0, b0), cvt2_bf16(a1, b1)};
+}
+
 // 16-byte direct load from global memory into LDS: lane i's word lands at
 // lds_wave_base + 16 i (the base is the same for the whole wave).  Written as
 // inline assembly so that the compiler sees no pending LDS write (it would
