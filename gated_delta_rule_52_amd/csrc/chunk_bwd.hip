@@ -30,6 +30,7 @@
 #include "chunk_common.h"
 #include "kperm.h"
 #include "plan.h"
+#include "swz.h"
 
 namespace gdn {
 
@@ -594,7 +595,9 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 float* __restrict__ dgmo, float* __restrict__ dbpo, int T, int H, int NC, int nch)
 {
     constexpr int BW = 32, NW = NTHR_C / 64, NB = C / 16;
-    constexpr int PB = BW + 8, PF = BW + 4;
+    constexpr int PF = BW + 4;
+    static_assert(BW == 4 * 8 && C == 8 * 8 && (DK == 128 || DK == 64), "table row widths of the swizzles");
+    using SwK = std::conditional_t<DK == 128, SwzU16, SwzU8>;  // [C][DK] tables
     constexpr int T3 = NB * (DK / 16), M3 = (T3 + NW - 1) / NW;
     constexpr int T2 = NB * NB, M2 = (T2 + NW - 1) / NW;
     constexpr int TD = NB * (BW / 16), MD = (TD + NW - 1) / NW;
@@ -603,32 +606,37 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     constexpr int NB8 = C * BW / 8;                  // uint4 words of a bf16 [C][BW] tile
     constexpr int ND4 = C * BW / 4;                  // float4 words of dD
     static_assert(NB8 <= NTHR_C / 2 && ND4 <= NTHR_C, "tile split assumes C*BW <= 2048");
-    constexpr int PT = C + 8, PK = DK + 8;  // bf16 pitches of the key WY-adjoint tables
-    // Dv-streaming tiles, and after the Dv loop the key WY-adjoint tables, share sbuf
-    constexpr int O_dS = DK * PB * 2, O_dO = 2 * DK * PB * 2, O_D = O_dO + C * PB * 2;
-    constexpr int O_dD = O_D + C * PB * 2, O_U = O_dD + C * PB * 2, O_dX = O_U + C * PB * 2;
-    constexpr int O_dDT = O_dX + C * PB * 2, O_v = O_dDT + BW * PT * 2, STREAM = O_v + C * PF * 4;
-    constexpr int O_W = DK * PT * 2;
-    constexpr int O_Xh = O_W + C * PK * 2, O_Xl = O_Xh + C * PK * 2, ENDP = O_Xl + C * PK * 2;
+    // Dv-streaming tiles, and after the Dv loop the key WY-adjoint tables, share
+    // sbuf.  bf16 tables are swizzled rows (swz.h): the [rows][BW] tiles SwzU4,
+    // dW^T [DK][C] SwzU8w, W and dX_K [C][DK] SwK; T [C][C] (SwzU8) is read
+    // transposed by transposing loads, and so is dD for dX_V = T^T dD.
+    constexpr int R4 = BW * 2;  // bytes of a [rows][BW] bf16 row
+    constexpr int O_dS = DK * R4, O_dO = 2 * DK * R4, O_D = O_dO + C * R4;
+    constexpr int O_dD = O_D + C * R4, O_U = O_dD + C * R4, O_dX = O_U + C * R4;
+    constexpr int O_v = O_dX + C * R4, STREAM = O_v + C * PF * 4;
+    constexpr int O_W = DK * C * 2;
+    constexpr int O_Xh = O_W + C * DK * 2, O_Xl = O_Xh + C * DK * 2, ENDP = O_Xl + C * DK * 2;
     __shared__ __align__(16) char sbuf[cmax(STREAM, ENDP)];
-    // T^T as high + low bf16 parts (16 significant bits), for dX_V = T^T dD in
-    // the Dv loop and dX_K = T^T dW after it; built once from the loaded T
-    __shared__ __align__(16) bf16 sTTh[C][PT], sTTl[C][PT];
+    // T as high + low bf16 parts (16 significant bits), for dX_V = T^T dD in the
+    // Dv loop and dX_K = T^T dW after it; built once from the loaded T
+    __shared__ __align__(16) uint4 sTh[C * C / 8], sTl[C * C / 8];
     __shared__ __align__(16) bf16 sDV[C][DV + 8];  // dv, written out after the Dv loop
     __shared__ float sbeta[C], sred[NW][C];
-    bf16 (*sS)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf);
-    bf16 (*sdS)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_dS);
-    bf16 (*sdO)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_dO);
-    bf16 (*sD)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_D);
-    bf16 (*sdD)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_dD);
-    bf16 (*sU)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_U);    // U and dX_V tiles,
-    bf16 (*sdX)[PB] = reinterpret_cast<bf16 (*)[PB]>(sbuf + O_dX);  // for G1 = dX_V U^T
-    uint16_t* const dDT16 = reinterpret_cast<uint16_t*>(sbuf + O_dDT);  // dD^T [BW][PT]
+    char* const sS = sbuf;
+    char* const sdS = sbuf + O_dS;
+    char* const sdO = sbuf + O_dO;
+    char* const sD = sbuf + O_D;
+    char* const sdD = sbuf + O_dD;
+    char* const sU = sbuf + O_U;    // U and dX_V tiles,
+    char* const sdX = sbuf + O_dX;  // for G1 = dX_V U^T
     float (*sv)[PF] = reinterpret_cast<float (*)[PF]>(sbuf + O_v);
-    bf16 (*sdWT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);          // dW^T
-    bf16 (*sW)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + O_W);
-    bf16 (*sXh)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + O_Xh);    // dX_K, high part
-    bf16 (*sXl)[PK] = reinterpret_cast<bf16 (*)[PK]>(sbuf + O_Xl);    // dX_K, low part
+    char* const sdWT = sbuf;  // dW^T
+    char* const sW = sbuf + O_W;
+    char* const sXh = sbuf + O_Xh;  // dX_K, high part
+    char* const sXl = sbuf + O_Xl;  // dX_K, low part
+    // 4 (8) bf16 at column c of row r of a [rows][BW] tile
+    auto at4 = [](char* t, int r, int c) { return reinterpret_cast<uint2*>(swz_at<SwzU4>(t, r, c)); };
+    auto at8 = [](char* t, int r, int c) { return reinterpret_cast<uint4*>(swz_at<SwzU4>(t, r, c)); };
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int lr = l & 15, lq = l >> 4;
@@ -703,26 +711,13 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             const float dx = __uint_as_float(d2.x << 16), dy = __uint_as_float(d2.x & 0xFFFF0000u);
             const float dz = __uint_as_float(d2.y << 16), dw = __uint_as_float(d2.y & 0xFFFF0000u);
             dgm_part[q] += ax * dx + ay * dy + az * dz + aw * dw;
-            *reinterpret_cast<uint2*>(&sS[i][j4]) = s2;
-            *reinterpret_cast<uint2*>(&sdS[i][j4]) = d2;
+            *at4(sS, i, j4) = s2;
+            *at4(sdS, i, j4) = d2;
         }
-        *reinterpret_cast<uint2*>(&sdD[rd][jd]) = pdD;
-        {
-            // dD^T as 32-bit words of two rows: lanes l and l + 8 of a 16-lane
-            // row hold rows rd (even) and rd + 1 of the same four columns; the
-            // lower one writes columns jd, jd + 1 and the upper one jd + 2, jd + 3
-            const bool up = (tid & 8) != 0;
-            const uint32_t give = up ? pdD.x : pdD.y;
-            const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)give, 0x128, 0xF, 0xF, false);  // row_ror:8
-            const uint32_t mine = up ? pdD.y : pdD.x;
-            const uint32_t lo = up ? got : mine, hi = up ? mine : got;  // rows rd & ~1, rd | 1
-            const int r0 = rd & ~1, c0 = jd + (up ? 2 : 0);
-            *reinterpret_cast<uint32_t*>(&dDT16[c0 * PT + r0]) = (lo & 0xFFFFu) | (hi << 16);
-            *reinterpret_cast<uint32_t*>(&dDT16[(c0 + 1) * PT + r0]) = (lo >> 16) | (hi & 0xFFFF0000u);
-        }
-        *reinterpret_cast<uint2*>(&sU[rd][jd]) = pack4_bf16(pU.x, pU.y, pU.z, pU.w);
+        *at4(sdD, rd, jd) = pdD;
+        *at4(sU, rd, jd) = pack4_bf16(pU.x, pU.y, pU.z, pU.w);
         if (lowh) {
-            *reinterpret_cast<uint4*>(&sD[r8][j8]) = pa;
+            *at8(sD, r8, j8) = pa;
             const uint4 vb = row8 ? pb : uint4{0u, 0u, 0u, 0u};
             const uint32_t u[4] = {vb.x, vb.y, vb.z, vb.w};
             float vv[8];
@@ -734,7 +729,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             st4(&sv[r8][j8], float4{vv[0], vv[1], vv[2], vv[3]});
             st4(&sv[r8][j8 + 4], float4{vv[4], vv[5], vv[6], vv[7]});
         } else {
-            *reinterpret_cast<uint4*>(&sdO[r8][j8]) = row8 ? pa : uint4{0u, 0u, 0u, 0u};
+            *at8(sdO, r8, j8) = row8 ? pa : uint4{0u, 0u, 0u, 0u};
         }
     };
 
@@ -812,19 +807,21 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 #pragma unroll
             for (int r = 0; r < 4; ++r) dbr[m][r] = 0.f;
 
-        // T^T and beta into LDS, the first tile stashed
+        // T (high and low parts) and beta into LDS, the first tile stashed
 #pragma unroll
-        for (int u = 0; u < NT4; ++u) {  // T[r][c0 + e] -> T^T[c0 + e][r], high and low parts
+        for (int u = 0; u < NT4; ++u) {  // T[r][c0 .. c0 + 3]
             const int idx = tid + NTHR_C * u;
             if (idx < C * C / 4) {
                 const int r = idx / (C / 4), c0 = (idx % (C / 4)) * 4;
                 const float tt[4] = {tv[u].x, tv[u].y, tv[u].z, tv[u].w};
+                float hi[4], lo[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const bf16 hi = f32_to_bf16(tt[e]);
-                    sTTh[c0 + e][r] = hi;
-                    sTTl[c0 + e][r] = f32_to_bf16(tt[e] - to_f32(hi));
+                    hi[e] = to_f32(f32_to_bf16(tt[e]));
+                    lo[e] = tt[e] - hi[e];
                 }
+                *reinterpret_cast<uint2*>(swz_at<SwzU8>(sTh, r, c0)) = pack4_bf16(hi[0], hi[1], hi[2], hi[3]);
+                *reinterpret_cast<uint2*>(swz_at<SwzU8>(sTl, r, c0)) = pack4_bf16(lo[0], lo[1], lo[2], lo[3]);
             }
         }
         if (tid < C) sbeta[tid] = tid < nvalid ? bv0 : 0.f;
@@ -837,15 +834,21 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         auto tile = [&](int v0, auto more_c) {
             constexpr bool MORE = decltype(more_c)::value;
             if constexpr (MORE) fetch(v0 + BW);
-            // dX_V = T^T dD (dD bf16, T^T as high + low bf16 parts, fp32
-            // accumulation): dv = beta dX_V, and <dX_V, v> for dbeta
+            // dX_V = T^T dD (dD bf16, T as high + low bf16 parts, fp32
+            // accumulation; T^T and dD read with K down their rows): dv = beta
+            // dX_V, and <dX_V, v> for dbeta
 #pragma unroll
             for (int m = 0; m < MD; ++m) {
                 const int idx = w + NW * m;
                 if (idx < TD) {
                     const int ti = idx / (BW / 16), tj = idx % (BW / 16);
-                    f32x4 dx = mma_kc<C>(zero4(), &sTTh[ti * 16][0], PT, reinterpret_cast<const bf16*>(dDT16) + tj * 16 * PT, PT);
-                    dx = mma_kc<C>(dx, &sTTl[ti * 16][0], PT, reinterpret_cast<const bf16*>(dDT16) + tj * 16 * PT, PT);
+                    f32x4 dx = zero4();
+#pragma unroll 1  // one K block's fragments live at a time (the kernel sits at the VGPR limit)
+                    for (int k0 = 0; k0 < C; k0 += 32) {
+                        const bf16x8 bd = frag_cols<SwzU4>(sdD, k0, tj * 16);
+                        dx = mfma_bf16_16x16x32(frag_cols<SwzU8>(sTh, k0, ti * 16), bd, dx);
+                        dx = mfma_bf16_16x16x32(frag_cols<SwzU8>(sTl, k0, ti * 16), bd, dx);
+                    }
                     f32x4 bdx;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -858,8 +861,8 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                     const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
                     *reinterpret_cast<uint32_t*>(&sDV[i2][v0 + j2]) = wv2.x;
                     *reinterpret_cast<uint32_t*>(&sDV[i2 + 1][v0 + j2]) = wv2.y;
-                    *reinterpret_cast<uint32_t*>(&sdX[i2][j2]) = wx2.x;
-                    *reinterpret_cast<uint32_t*>(&sdX[i2 + 1][j2]) = wx2.y;
+                    *reinterpret_cast<uint32_t*>(swz_at<SwzU4>(sdX, i2, j2)) = wx2.x;
+                    *reinterpret_cast<uint32_t*>(swz_at<SwzU4>(sdX, i2 + 1, j2)) = wx2.y;
                 }
             }
 #pragma unroll
@@ -867,9 +870,10 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const int idx = w + NW * m;
                 if (idx < T3) {
                     const int ti = idx / (DK / 16), tj = idx % (DK / 16);
-                    aQ[m] = mma_kc<BW>(aQ[m], &sdO[ti * 16][0], PB, &sS[tj * 16][0], PB);
-                    aW[m] = mma_kc<BW>(aW[m], &sdD[ti * 16][0], PB, &sS[tj * 16][0], PB);
-                    aK[m] = mma_kc<BW>(aK[m], &sD[ti * 16][0], PB, &sdS[tj * 16][0], PB);
+                    const bf16x8 bs = frag_rows<SwzU4>(sS, tj * 16, 0);
+                    aQ[m] = mfma_bf16_16x16x32(frag_rows<SwzU4>(sdO, ti * 16, 0), bs, aQ[m]);
+                    aW[m] = mfma_bf16_16x16x32(frag_rows<SwzU4>(sdD, ti * 16, 0), bs, aW[m]);
+                    aK[m] = mfma_bf16_16x16x32(frag_rows<SwzU4>(sD, ti * 16, 0), frag_rows<SwzU4>(sdS, tj * 16, 0), aK[m]);
                 }
             }
 #pragma unroll
@@ -877,7 +881,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const int idx = w + NW * m;
                 if (idx < T2) {
                     const int ti = idx / NB, tj = idx % NB;
-                    aP[m] = mma_kc<BW>(aP[m], &sdO[ti * 16][0], PB, &sD[tj * 16][0], PB);
+                    aP[m] = mfma_bf16_16x16x32(frag_rows<SwzU4>(sdO, ti * 16, 0), frag_rows<SwzU4>(sD, tj * 16, 0), aP[m]);
                 }
             }
             __syncthreads();  // the dX_V tile is complete
@@ -886,7 +890,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const int idx = w + NW * m;
                 if (idx < T2) {
                     const int ti = idx / NB, tj = idx % NB;
-                    aT[m] = mma_kc<BW>(aT[m], &sdX[ti * 16][0], PB, &sU[tj * 16][0], PB);
+                    aT[m] = mfma_bf16_16x16x32(frag_rows<SwzU4>(sdX, ti * 16, 0), frag_rows<SwzU4>(sU, tj * 16, 0), aT[m]);
                 }
             }
             __syncthreads();
@@ -923,7 +927,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                     *reinterpret_cast<uint32_t*>(&dKp[(i2 + 1) * DK + j2]) = wk.y;
                 }
                 // dW = -aW, stored transposed for dX_K = T^T dW (4 consecutive rows per lane)
-                *reinterpret_cast<uint2*>(&sdWT[tj * 16 + lr][ti * 16 + 4 * lq]) =
+                *reinterpret_cast<uint2*>(swz_at<SwzU8w>(sdWT, tj * 16 + lr, ti * 16 + 4 * lq)) =
                     pack4_bf16(-aW[m][0], -aW[m][1], -aW[m][2], -aW[m][3]);
             }
         }
@@ -946,7 +950,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 #pragma unroll
         for (int u = 0; u < NK8; ++u) {
             const int idx = tid + NTHR_C * u;
-            if (idx < C * DK / 8) *reinterpret_cast<u32x4*>(&sW[idx / (DK / 8)][(idx % (DK / 8)) * 8]) = wv[u];
+            if (idx < C * DK / 8) *reinterpret_cast<u32x4*>(swz_at<SwK>(sW, idx / (DK / 8), (idx % (DK / 8)) * 8)) = wv[u];
         }
         __syncthreads();
         // the next chunk's prologue loads, in flight through the tail (the last
@@ -957,8 +961,13 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             const int idx = w + NW * m;
             if (idx < T3) {
                 const int ti = idx / (DK / 16), tj = idx % (DK / 16);
-                f32x4 acc = mma_kc<C>(zero4(), &sTTh[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
-                acc = mma_kc<C>(acc, &sTTl[ti * 16][0], PT, &sdWT[tj * 16][0], PT);
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int k0 = 0; k0 < C; k0 += 32) {
+                    const bf16x8 bw = frag_rows<SwzU8w>(sdWT, tj * 16, k0 / 8);
+                    acc = mfma_bf16_16x16x32(frag_cols<SwzU8>(sTh, k0, ti * 16), bw, acc);
+                    acc = mfma_bf16_16x16x32(frag_cols<SwzU8>(sTl, k0, ti * 16), bw, acc);
+                }
                 f32x4 hi, lo;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -967,25 +976,30 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 }
                 const uint2 wh = acc_colpairs(hi), wl = acc_colpairs(lo);
                 const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
-                *reinterpret_cast<uint32_t*>(&sXh[i2][j2]) = wh.x;
-                *reinterpret_cast<uint32_t*>(&sXh[i2 + 1][j2]) = wh.y;
-                *reinterpret_cast<uint32_t*>(&sXl[i2][j2]) = wl.x;
-                *reinterpret_cast<uint32_t*>(&sXl[i2 + 1][j2]) = wl.y;
+                *reinterpret_cast<uint32_t*>(swz_at<SwK>(sXh, i2, j2)) = wh.x;
+                *reinterpret_cast<uint32_t*>(swz_at<SwK>(sXh, i2 + 1, j2)) = wh.y;
+                *reinterpret_cast<uint32_t*>(swz_at<SwK>(sXl, i2, j2)) = wl.x;
+                *reinterpret_cast<uint32_t*>(swz_at<SwK>(sXl, i2 + 1, j2)) = wl.y;
             }
         }
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < NX8; ++u) {  // dX_K (bf16) rows, stored in place of dW
             const int idx = min(tid + NTHR_C * u, C * DK / 8 - 1);
-            oX[u] = *reinterpret_cast<const u32x4*>(&sXh[idx / (DK / 8)][(idx % (DK / 8)) * 8]);
+            oX[u] = *reinterpret_cast<const u32x4*>(swz_at<SwK>(sXh, idx / (DK / 8), (idx % (DK / 8)) * 8));
         }
 #pragma unroll
         for (int m = 0; m < M2; ++m) {
             const int idx = w + NW * m;
             if (idx < T2) {
                 const int ti = idx / NB, tj = idx % NB;
-                f32x4 acc = mma_kc<DK>(aT[m], &sXh[ti * 16][0], PK, &sW[tj * 16][0], PK);
-                acc = mma_kc<DK>(acc, &sXl[ti * 16][0], PK, &sW[tj * 16][0], PK);
+                f32x4 acc = aT[m];
+#pragma unroll
+                for (int u0 = 0; u0 < DK / 8; u0 += 4) {
+                    const bf16x8 bw = frag_rows<SwK>(sW, tj * 16, u0);
+                    acc = mfma_bf16_16x16x32(frag_rows<SwK>(sXh, ti * 16, u0), bw, acc);
+                    acc = mfma_bf16_16x16x32(frag_rows<SwK>(sXl, ti * 16, u0), bw, acc);
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
@@ -1502,46 +1516,6 @@ __device__ __forceinline__ bf16x8 ctab_frag(const uint4* __restrict__ tab, int c
     return HALF && kk >= 2 ? bf16x8{} : b;
 }
 
-// Score tables of bchunk2c (dPs, dA): C = 64 token rows of 64 bf16, 128 bytes
-// a row.  16-byte unit u of row R sits at R * 8 + (u ^ sswz(R)).  With this
-// swizzle both operand reads below touch every LDS bank once per access phase:
-// the 16-byte reads of 16 rows (K along a row) and the transposing 8-byte
-// reads (K down the rows).
-__device__ __forceinline__ int sswz(int R) { return (R & 2) | ((R >> 1) & 4); }
-__device__ __forceinline__ int sunit(int R, int u) { return R * 8 + (u ^ sswz(R)); }
-
-// MFMA A operand with K along the rows of a score table:
-// A(m, k) = X(r0 + m, k0 + k), k0 a multiple of 8.  HALF (K = 16): lanes kk >= 2
-// repeat kk - 2 (their B operand is zero).
-template <bool HALF>
-__device__ __forceinline__ bf16x8 sfrag_row(const uint4* X, int r0, int k0)
-{
-    const int l = lane_id(), kk = HALF ? (l >> 4) & 1 : l >> 4;
-    return __builtin_bit_cast(bf16x8, X[sunit(r0 + (l & 15), (k0 >> 3) + kk)]);
-}
-
-// MFMA A operand of the transpose, K down the rows: A(m, k) = X(k0 + k, m0 + m),
-// from two transposing loads (ds_read_b64_tr_b16).  Within each group of 16
-// lanes such a load hands lane i element i & 3 of the four 16-bit values read
-// by lane 4 e + (i >> 2), as its element e (e = 0..3).  So lane j of group g
-// reads row k0 + 8 g + 4 h + (j >> 2), columns m0 + 4 (j & 3) .. + 3, and lane m
-// receives X(k0 + 8 g + 4 h + e, m0 + m) = A(m, 8 g + 4 h + e).  m0 is a multiple
-// of 16.  HALF (K = 16): groups g >= 2 repeat g - 2.
-template <bool HALF>
-__device__ __forceinline__ bf16x8 sfrag_tr(const uint4* X, int k0, int m0)
-{
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    const int l = lane_id(), j = l & 15, g = HALF ? (l >> 4) & 1 : l >> 4;
-    s16x4 v[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int k = k0 + 8 * g + 4 * h + (j >> 2);
-        const char* p = reinterpret_cast<const char*>(X + sunit(k, (m0 >> 3) + ((j & 3) >> 1))) + 8 * (j & 1);
-        v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-    }
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 template <int C, int DK, bool PCH, bool L2N>
 __global__ void __launch_bounds__((C / 8) * (DK / 2)) __attribute__((amdgpu_waves_per_eu(4)))  // bchunk2c_threads; 4 waves per SIMD: 2 workgroups a CU
 bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
@@ -1559,7 +1533,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     constexpr int RPP = 8, NPART = C / RPP;
     static_assert(NPART * HC == NTHR_F, "one column thread per (part, channel)");
     // LDS, one buffer with named parts:
-    //  score gradients, bf16, by rows (sunit): dPs (unscaled, lower incl.
+    //  score gradients, bf16, by rows (SwzU8): dPs (unscaled, lower incl.
     //  diagonal) and dA (strictly lower); their transposes are read from the
     //  same tables with transposing loads;
     //  level tables (channel-major, ctab_slot): q and k rows times the level
@@ -1586,7 +1560,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     auto ridx = [](int i, int j) { return i * PH + j; };
     // element (R, c) of a score table
     auto sel = [](const uint4* X, int R, int c) {
-        return to_f32(reinterpret_cast<const bf16*>(X + sunit(R, c >> 3))[c & 7]);
+        return to_f32(reinterpret_cast<const bf16*>(X + swz_slot<SwzU8>(R, c >> 3))[c & 7]);
     };
     __shared__ float sbeta[C], stot[NPART][HC];
     __shared__ float sG[C];  // per-head decay: chunk-local inclusive cumsum of g
@@ -1679,8 +1653,8 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             const int idx = tid + NTHR_F * u;
             if (idx < NC8) {
                 const int i = idx / (C / 8), uu = idx % (C / 8);
-                sPv[sunit(i, uu)] = pw[u];
-                sAv[sunit(i, uu)] = aw[u];
+                sPv[swz_slot<SwzU8>(i, uu)] = pw[u];
+                sAv[swz_slot<SwzU8>(i, uu)] = aw[u];
             }
         }
         if (tid < C) sbeta[tid] = tid < nvalid ? bv : 0.f;
@@ -1766,8 +1740,8 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         // cancel in dG's reverse sum because both sides read one rounded value.
         for (int e = tid; e < C * (C / 8); e += NTHR_F) {
             const int rr = e / (C / 8), uu = e % (C / 8), c0 = uu * 8;
-            uint4* t1 = &sPv[sunit(rr, uu)];
-            uint4* t2 = &sAv[sunit(rr, uu)];
+            uint4* t1 = &sPv[swz_slot<SwzU8>(rr, uu)];
+            uint4* t2 = &sAv[swz_slot<SwzU8>(rr, uu)];
             uint4 w1 = *t1, w2 = *t2;
             uint32_t u1[4] = {w1.x, w1.y, w1.z, w1.w}, u2[4] = {w2.x, w2.y, w2.z, w2.w};
             float ev[8];
@@ -1835,8 +1809,8 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             xr[m] = rr2[m] = yr[m] = zero4();
 #pragma unroll
             for (int kb = 0; kb < C; kb += 32) {
-                const bf16x8 ap = sfrag_row<false>(sPv, ti * 16, kb), aa = sfrag_row<false>(sAv, ti * 16, kb);
-                const bf16x8 tp = sfrag_tr<false>(sPv, kb, ti * 16), ta = sfrag_tr<false>(sAv, kb, ti * 16);
+                const bf16x8 ap = frag_rows<SwzU8, false>(sPv, ti * 16, kb / 8), aa = frag_rows<SwzU8, false>(sAv, ti * 16, kb / 8);
+                const bf16x8 tp = frag_cols<SwzU8, false>(sPv, kb, ti * 16), ta = frag_cols<SwzU8, false>(sAv, kb, ti * 16);
                 const bf16x8 bk = ctab_frag<false>(sKK, tj * 16, kb / 8);
                 xr[m] = mfma_bf16_16x16x32(ap, bk, xr[m]);
                 rr2[m] = mfma_bf16_16x16x32(aa, bk, rr2[m]);
@@ -1966,13 +1940,13 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                     // transposes against q F and beta k F
                     const int kb = qt ? tbase : tbase + hl;  // first row of the summed half
                     if (hl == 32) {
-                        const bf16x8 a1 = qt ? sfrag_row<false>(sPv, ti * 16, kb) : sfrag_tr<false>(sPv, kb, ti * 16);
-                        const bf16x8 a2 = qt ? sfrag_row<false>(sAv, ti * 16, kb) : sfrag_tr<false>(sAv, kb, ti * 16);
+                        const bf16x8 a1 = qt ? frag_rows<SwzU8, false>(sPv, ti * 16, kb / 8) : frag_cols<SwzU8, false>(sPv, kb, ti * 16);
+                        const bf16x8 a2 = qt ? frag_rows<SwzU8, false>(sAv, ti * 16, kb / 8) : frag_cols<SwzU8, false>(sAv, kb, ti * 16);
                         r1 = mfma_bf16_16x16x32(a1, ctab_frag<false>(qt ? sKK : sQK, tj * 16, kb / 8), zero4());
                         r2 = mfma_bf16_16x16x32(a2, ctab_frag<false>(qt ? sKK : sKB, tj * 16, kb / 8), zero4());
                     } else {
-                        const bf16x8 a1 = qt ? sfrag_row<true>(sPv, ti * 16, kb) : sfrag_tr<true>(sPv, kb, ti * 16);
-                        const bf16x8 a2 = qt ? sfrag_row<true>(sAv, ti * 16, kb) : sfrag_tr<true>(sAv, kb, ti * 16);
+                        const bf16x8 a1 = qt ? frag_rows<SwzU8, true>(sPv, ti * 16, kb / 8) : frag_cols<SwzU8, true>(sPv, kb, ti * 16);
+                        const bf16x8 a2 = qt ? frag_rows<SwzU8, true>(sAv, ti * 16, kb / 8) : frag_cols<SwzU8, true>(sAv, kb, ti * 16);
                         r1 = mfma_bf16_16x16x32(a1, ctab_frag<true>(qt ? sKK : sQK, tj * 16, kb / 8), zero4());
                         r2 = mfma_bf16_16x16x32(a2, ctab_frag<true>(qt ? sKK : sKB, tj * 16, kb / 8), zero4());
                     }
@@ -1989,16 +1963,16 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                     // beta k F
                     const int slot = ctab_slot(tj * 16 + rr, 2 * ti + kh);
                     {
-                        const bf16x8 p_row = sfrag_row<true>(sPv, ti * 16, ti * 16);
-                        const bf16x8 p_tr = sfrag_tr<true>(sPv, ti * 16, ti * 16);
+                        const bf16x8 p_row = frag_rows<SwzU8, true>(sPv, ti * 16, 2 * ti);
+                        const bf16x8 p_tr = frag_cols<SwzU8, true>(sPv, ti * 16, ti * 16);
                         const bf16x8 a1 = live ? (qrow ? p_row : p_tr) : bf16x8{};
                         bf16x8 b1 = __builtin_bit_cast(bf16x8, kh == 0 ? sKK[slot] : sQK[slot]);
                         if (kk >= 2) b1 = bf16x8{};
                         r1 = mfma_bf16_16x16x32(a1, b1, zero4());
                     }
                     {
-                        const bf16x8 a_row = sfrag_row<true>(sAv, ti * 16, ti * 16);
-                        const bf16x8 a_tr = sfrag_tr<true>(sAv, ti * 16, ti * 16);
+                        const bf16x8 a_row = frag_rows<SwzU8, true>(sAv, ti * 16, 2 * ti);
+                        const bf16x8 a_tr = frag_cols<SwzU8, true>(sAv, ti * 16, ti * 16);
                         const bf16x8 a2 = live ? (qrow ? a_row : a_tr) : bf16x8{};
                         bf16x8 b2 = __builtin_bit_cast(bf16x8, kh == 0 ? sKK[slot] : sKB[slot]);
                         if (kk >= 2) b2 = bf16x8{};
@@ -2054,8 +2028,8 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
             const int r = p0 + i;
             const float bi = sbeta[r], bki = bi * kv[i], sqi = scale * qv[i];
             // this row's columns p0 .. p0 + 7: one 16-byte unit of each table
-            const u32x4 pu = __builtin_bit_cast(u32x4, sPv[sunit(r, p0 >> 3)]);
-            const u32x4 au = __builtin_bit_cast(u32x4, sAv[sunit(r, p0 >> 3)]);
+            const u32x4 pu = __builtin_bit_cast(u32x4, sPv[swz_slot<SwzU8>(r, p0 >> 3)]);
+            const u32x4 au = __builtin_bit_cast(u32x4, sAv[swz_slot<SwzU8>(r, p0 >> 3)]);
             auto ext = [](const u32x4& u, int j) {
                 return __uint_as_float((j & 1) ? (u[j >> 1] & 0xFFFF0000u) : (u[j >> 1] << 16));
             };

@@ -1,0 +1,87 @@
+// swz.h -- swizzled LDS tables of bf16 rows and their MFMA operand reads.
+//
+// A table holds rows of U 16-byte units (8 bf16 each); unit u of row r sits at
+// slot r * U + (u ^ f(r)).  The gfx950 LDS has 64 banks of 4 bytes.  A 16-byte
+// read is served in four phases of 16 lanes, a lane's phase being
+// 2 * bit5 + (bit2 ^ bit3 ^ bit4) of its lane id, and a phase is free of bank
+// conflicts when its lanes touch distinct 16-byte bank groups (address bits
+// 4..7).  An 8-byte read (plain or transposing) is served in two phases of 32
+// lanes over 256 bytes; 8-byte writes in four phases of 16 lanes, 16-byte
+// writes in eight phases of 8 lanes, both over 128 bytes.  (Measured with the
+// hardware's bank-conflict counter on single-wave access patterns.)  Each f
+// below was chosen, by checking every access pattern of its tables against
+// these rules, so that the operand reads of its tables hit every bank once.
+#pragma once
+
+#include "common.h"
+
+namespace gdn {
+
+// 4 units (32 bf16) a row: 16-byte row reads and transposing reads
+struct SwzU4 {
+    static constexpr int U = 4;
+    __device__ static int f(int r) { return (((r >> 1) & 1) << 1) ^ (((r >> 3) & 1) * 3); }
+};
+// 8 units (64 bf16) a row: 16-byte row reads and transposing reads
+struct SwzU8 {
+    static constexpr int U = 8;
+    __device__ static int f(int r) { return (r & 2) | ((r >> 1) & 4); }
+};
+// 8 units a row: 16-byte row reads, rows written as four-row column pieces
+struct SwzU8w {
+    static constexpr int U = 8;
+    __device__ static int f(int r) { return (r >> 1) & 7; }
+};
+// 16 units (128 bf16) a row: 16-byte row reads
+struct SwzU16 {
+    static constexpr int U = 16;
+    __device__ static int f(int r) { return r & 15; }
+};
+
+template <class S>
+__device__ __forceinline__ int swz_slot(int r, int u)
+{
+    return r * S::U + (u ^ S::f(r));
+}
+
+// address of bf16 column c of row r
+template <class S>
+__device__ __forceinline__ bf16* swz_at(void* tab, int r, int c)
+{
+    return reinterpret_cast<bf16*>(reinterpret_cast<uint4*>(tab) + swz_slot<S>(r, c >> 3)) + (c & 7);
+}
+
+// MFMA operand with K along the rows (v_mfma_f32_16x16x32_bf16 A, or B given as
+// B^T rows): lane (r, kk) supplies unit u0 + kk of row r0 + r, i.e. operand row
+// r, K = 8 u0 + 8 kk .. + 7.  HALF (K = 16): lanes kk >= 2 repeat kk - 2 (the
+// caller zeros the other operand there).
+template <class S, bool HALF = false>
+__device__ __forceinline__ bf16x8 frag_rows(const void* tab, int r0, int u0)
+{
+    const int l = lane_id(), kk = HALF ? (l >> 4) & 1 : l >> 4;
+    return __builtin_bit_cast(bf16x8, reinterpret_cast<const uint4*>(tab)[swz_slot<S>(r0 + (l & 15), u0 + kk)]);
+}
+
+// MFMA operand with K down the rows: operand(m, k) = X(k0 + k, m0 + m), from two
+// transposing loads (ds_read_b64_tr_b16).  Within each group of 16 lanes such a
+// load hands lane i element i & 3 of the four 16-bit values read by lane
+// 4 e + (i >> 2), as its element e (e = 0..3).  So lane j of group g reads row
+// k0 + 8 g + 4 h + (j >> 2), columns m0 + 4 (j & 3) .. + 3, and lane m receives
+// X(k0 + 8 g + 4 h + e, m0 + m), the operand's K = 8 g + 4 h + e.  m0 is a
+// multiple of 16.  HALF (K = 16): groups g >= 2 repeat g - 2.
+template <class S, bool HALF = false>
+__device__ __forceinline__ bf16x8 frag_cols(const void* tab, int k0, int m0)
+{
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int l = lane_id(), j = l & 15, g = HALF ? (l >> 4) & 1 : l >> 4;
+    s16x4 v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int k = k0 + 8 * g + 4 * h + (j >> 2);
+        const bf16* p = swz_at<S>(const_cast<void*>(tab), k, m0 + 4 * (j & 3));
+        v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+}  // namespace gdn
