@@ -173,7 +173,9 @@ bscan_kernel(const float* __restrict__ Qgi, const float* __restrict__ Khi,
 // wave w owning 16 columns of dS for the whole sequence in MFMA accumulators
 // that are the operands of the next products (kperm.h).  Per chunk n, from the
 // last to the first, with dS' the gradient at the chunk's end and the chunk's
-// Kh, P^T, Qg^T, W^T (K index permuted), the dO slice and the decay in LDS:
+// forward tables Kh^T, Ps, Qg, W, the dO slice and the decay in LDS (the
+// transposes Kh, P^T, Qg^T, W^T are their operands, read with transposing
+// loads in the K order of kperm.h):
 //     dD  = Kh dS' + P^T dO                 (P^T upper triangular)
 //     dS <- gam o dS' + Qg^T dO - W^T dD    (the gradient at the chunk's start)
 // dS' and dD leave as bf16 rows for bchunk1 (transposed by a 0/1 MFMA so a
@@ -185,8 +187,8 @@ constexpr int NTHR_B4 = 256;  // waves 0, 1 compute; waves 2, 3 load
 
 template <int DK, int DV>
 __global__ void __launch_bounds__(NTHR_B4) __attribute__((amdgpu_waves_per_eu(1, 1)))
-bscan4_kernel(const bf16* __restrict__ Khp, const bf16* __restrict__ PTp,
-              const bf16* __restrict__ QTp, const bf16* __restrict__ WTp,
+bscan4_kernel(const bf16* __restrict__ KhTp, const bf16* __restrict__ Psp,
+              const bf16* __restrict__ Qgp, const bf16* __restrict__ Wp,
               const float* __restrict__ gami, const bf16* __restrict__ dO, const float* dhT,
               bf16* __restrict__ dSt, bf16* __restrict__ dDt, float* dh0, int BH, int T, int H,
               int NC)
@@ -194,13 +196,15 @@ bscan4_kernel(const bf16* __restrict__ Khp, const bf16* __restrict__ PTp,
     constexpr int C = 64, BV = 32, NS = DV / BV;
     constexpr int NT = DK / 16, KB = DK / 32;
     constexpr int WK = DK / 8, WC = C / 8;
-    // a buffer in 16-byte words: Kh [C][WK], P^T [C][WC], Qg^T [DK][WC],
-    // W^T [DK][WC] (swizzled, kswz), the dO slice [C][BV] bf16 (plain), the decay
-    constexpr int OKh = 0, OPT = OKh + C * WK, OQT = OPT + C * WC, OWT = OQT + DK * WC;
-    constexpr int OdO = OWT + DK * WC, OG = OdO + C * BV / 8, QB = OG + 64;
+    // a buffer in 16-byte words: Kh^T [DK][WC], Ps [C][WC] (SwzK8), Qg [C][WK],
+    // W [C][WK] (SK), the dO slice [C][BV] bf16 (plain), the decay
+    using SK = std::conditional_t<DK == 128, SwzK16, SwzK8>;
+    static_assert(WC == SwzK8::U && WK == SK::U, "row widths of the swizzles");
+    constexpr int OKh = 0, OPs = OKh + DK * WC, OQg = OPs + C * WC, OW = OQg + C * WK;
+    constexpr int OdO = OW + C * WK, OG = OdO + C * BV / 8, QB = OG + 64;
     constexpr int NL = 128;  // threads of the two load waves
     constexpr int NQT = OdO / NL, NQO = (C * BV / 8) / NL;
-    static_assert(OPT % NL == 0 && OQT % NL == 0 && OWT % NL == 0 && OdO % NL == 0 &&
+    static_assert(OPs % NL == 0 && OQg % NL == 0 && OW % NL == 0 && OdO % NL == 0 &&
                   NQO * NL == C * BV / 8, "each load lies in one table");
     // 128-byte lines of a chunk's tables and decay (the dO slice: one line a row)
     constexpr int LT = (C * DK + C * C + 2 * DK * C) * 2 / 128, LG = DK * 4 / 128;
@@ -239,14 +243,16 @@ bscan4_kernel(const bf16* __restrict__ Khp, const bf16* __restrict__ PTp,
 #pragma unroll
         for (int q = 0; q < NQT; ++q) {
             const int s0 = q * NL;
-            const int wpr = s0 < OPT ? WK : WC;
-            const int off = s0 < OPT ? OKh : s0 < OQT ? OPT : s0 < OWT ? OQT : OWT;
-            const bf16* tab = s0 < OPT ? Khp + ch * C * DK
-                            : s0 < OQT ? PTp + ch * C * C
-                            : s0 < OWT ? QTp + ch * DK * C
-                                       : WTp + ch * DK * C;
+            const bool kq = s0 >= OQg;  // Qg and W rows; Kh^T and Ps rows otherwise
+            const int wpr = kq ? WK : WC;
+            const int off = s0 < OPs ? OKh : s0 < OQg ? OPs : s0 < OW ? OQg : OW;
+            const bf16* tab = s0 < OPs ? KhTp + ch * C * DK
+                            : s0 < OQg ? Psp + ch * C * C
+                            : s0 < OW  ? Qgp + ch * C * DK
+                                       : Wp + ch * C * DK;
+            // slot (r, ws) of the swizzled table holds the row's unit ws ^ f(r)
             const int ls = s0 + lt - off, r = ls / wpr, ws = ls % wpr;
-            const int wd = ws ^ (wpr == 16 ? (r & 15) : ((r >> 1) & 7));
+            const int wd = ws ^ (kq ? SK::f(r) : SwzK8::f(r));
             dma16(tab + (r * wpr + wd) * 8, buf + s0 + 64 * lw);
         }
         // dO rows of the chunk (rows past T repeat the last one: their P^T and
@@ -273,10 +279,10 @@ bscan4_kernel(const bf16* __restrict__ Khp, const bf16* __restrict__ PTp,
             } else {
                 const int L = min((s - C) * NS + sl, LT + LG - 1);
                 constexpr int L1 = C * DK * 2 / 128, L2 = L1 + C * C * 2 / 128, L3 = L2 + DK * C * 2 / 128;
-                p = L < L1 ? reinterpret_cast<const char*>(Khp + ch * C * DK) + 128 * L
-                  : L < L2 ? reinterpret_cast<const char*>(PTp + ch * C * C) + 128 * (L - L1)
-                  : L < L3 ? reinterpret_cast<const char*>(QTp + ch * DK * C) + 128 * (L - L2)
-                  : L < LT ? reinterpret_cast<const char*>(WTp + ch * DK * C) + 128 * (L - L3)
+                p = L < L1 ? reinterpret_cast<const char*>(KhTp + ch * C * DK) + 128 * L
+                  : L < L2 ? reinterpret_cast<const char*>(Psp + ch * C * C) + 128 * (L - L1)
+                  : L < L3 ? reinterpret_cast<const char*>(Qgp + ch * DK * C) + 128 * (L - L2)
+                  : L < LT ? reinterpret_cast<const char*>(Wp + ch * DK * C) + 128 * (L - L3)
                            : reinterpret_cast<const char*>(gami + ch * DK) + 128 * (L - LT);
             }
             warm_line(p, &sSink[lw][0]);
@@ -316,11 +322,11 @@ bscan4_kernel(const bf16* __restrict__ Khp, const bf16* __restrict__ PTp,
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) kf[kb][ti] = frag_lds<WK>(tb + OKh, 16 * ti, kb);
+            for (int ti = 0; ti < 4; ++ti) kf[kb][ti] = frag_cols_kperm<SwzK8>(tb + OKh, 32 * kb, 16 * ti);
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-            for (int kb = ti / 2; kb < 2; ++kb) pf[ti][kb] = frag_lds<WC>(tb + OPT, 16 * ti, kb);
+            for (int kb = ti / 2; kb < 2; ++kb) pf[ti][kb] = frag_cols_kperm<SwzK8>(tb + OPs, 32 * kb, 16 * ti);
         f32x4 dd[4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) dd[ti] = zero4();
@@ -348,8 +354,8 @@ bscan4_kernel(const bf16* __restrict__ Khp, const bf16* __restrict__ PTp,
             gv[t] = tG[4 * t + lg];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                qf[t][kb] = frag_lds<WC>(tb + OQT, 16 * t, kb);
-                wf[t][kb] = frag_lds<WC>(tb + OWT, 16 * t, kb);
+                qf[t][kb] = frag_cols_kperm<SK>(tb + OQg, 32 * kb, 16 * t);
+                wf[t][kb] = frag_cols_kperm<SK>(tb + OW, 32 * kb, 16 * t);
             }
         }
 #pragma unroll
@@ -2261,12 +2267,11 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
     const int BH = p.B * p.H;
     const float* rn = p.l2n ? (const float*)(ws + p.o_rn) : nullptr;
     if constexpr (bf16_tables<TIn, C, DK>()) {
-        const size_t n = p.n_ch;
-        // the backward tables are the second of the two in each region (plan.h)
+        // the forward tables (plan.h)
         dim3 grid((unsigned)(((BH + 7) / 8) * 8 * (DV / 32))), block(NTHR_B4);
         GDN_LAUNCH("bscan", (bscan4_kernel<DK, DV>), grid, block, st,
-                   (const bf16*)(ws + p.o_Kh) + n * C * DK, (const bf16*)(ws + p.o_Ps) + n * C * C,
-                   (const bf16*)(ws + p.o_Qg) + n * C * DK, (const bf16*)(ws + p.o_W) + n * C * DK,
+                   (const bf16*)(ws + p.o_Kh), (const bf16*)(ws + p.o_Ps),
+                   (const bf16*)(ws + p.o_Qg), (const bf16*)(ws + p.o_W),
                    (const float*)(ws + p.o_gam), (const bf16*)dO, dhT, (bf16*)(ws + p.o_dSt),
                    (bf16*)(ws + p.o_dDt), dh0, BH, p.T, p.H, p.NC);
     } else {

@@ -30,7 +30,6 @@
 #include <type_traits>
 
 #include "chunk_common.h"
-#include "kperm.h"
 #include "plan.h"
 
 namespace gdn {
@@ -430,9 +429,8 @@ template <int C, int DK, int DV, bool PCH, bool L2N, bool SAFE>
 __global__ void __launch_bounds__(NTHR_P, 4)
 prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
              const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int NC,
-             float scale, bf16* __restrict__ Wb, bf16* __restrict__ WTb, float* __restrict__ Uo,
-             bf16* __restrict__ Qgb, bf16* __restrict__ QgTb, bf16* __restrict__ KhTb,
-             bf16* __restrict__ Khb, bf16* __restrict__ Psb, bf16* __restrict__ PsTb,
+             float scale, bf16* __restrict__ Wb, float* __restrict__ Uo,
+             bf16* __restrict__ Qgb, bf16* __restrict__ KhTb, bf16* __restrict__ Psb,
              float* __restrict__ gamo, float* __restrict__ Tmo, float* __restrict__ rno,
              Safety sf, bf16* __restrict__ Wro, float* __restrict__ Uro)
 {
@@ -724,18 +722,15 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         vw[u] = *reinterpret_cast<const uint4*>(v + tok0 * DV + (size_t)min(r, nvalid - 1) * H * DV + j0);
     }
 
-    // ---- scores out: Ps (bf16) and, for training, Ps^T; A (x beta) to LDS.
-    // Ps and Ps^T are staged in the level-table bytes (free after the score
-    // products) and leave as whole rows, 16 bytes per thread
+    // ---- scores out: Ps (bf16); A (x beta) to LDS.  Ps is staged in the
+    // level-table bytes (free after the score products) and leaves as whole
+    // rows, 16 bytes per thread
     bf16 (*sPs)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);
-    bf16 (*sPsT)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf + C * PT * 2);
-    static_assert(2 * C * PT * 2 <= SBUF, "staged Ps and Ps^T fit the level-table bytes");
+    static_assert(C * PT * 2 <= SBUF, "staged Ps fits the level-table bytes");
     bf16* Psc = Psb + (size_t)ch * C * C;
-    bf16* PsTc = PsTb + (size_t)ch * C * C;
     auto put_ps = [&](int i0, int j, const float (&pv)[4]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sPs[i0 + r][j] = f32_to_bf16(pv[r]);
-        if (bwdt) *reinterpret_cast<uint2*>(&sPsT[j][kperm_pos(i0)]) = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
     };
     if (w >= NB) {
 #pragma unroll
@@ -769,7 +764,6 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         const int i = idx / C, j = idx % C;
         if (i / 16 < j / 16) {
             sPs[i][j] = f32_to_bf16(0.f);
-            if (bwdt) sPsT[j][kperm_pos(i)] = f32_to_bf16(0.f);
             sA[i][j] = 0.f;
         }
     }
@@ -777,19 +771,16 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     for (int idx = tid; idx < C * C / 8; idx += NTHR_P) {
         const int r = idx / (C / 8), c0 = (idx % (C / 8)) * 8;
         *reinterpret_cast<uint4*>(&Psc[r * C + c0]) = *reinterpret_cast<const uint4*>(&sPs[r][c0]);
-        if (bwdt) *reinterpret_cast<uint4*>(&PsTc[r * C + c0]) = *reinterpret_cast<const uint4*>(&sPsT[r][c0]);
     }
-    __syncthreads();  // the staged Ps rows are read: Qg and Kh take their bytes
+    __syncthreads();  // the staged Ps rows are read: Qg takes their bytes
 
-    // ---- Gamma, Kh factor, gam: Qg, Kh outputs and X_K^T = (beta K o Gamma)^T.
-    // Qg and Kh rows are staged in the level-table bytes (free after the score
+    // ---- Gamma, Kh factor, gam: Qg, Kh^T outputs and X_K^T = (beta K o Gamma)^T.
+    // Qg rows are staged in the level-table bytes (free after the score
     // products) and leave as whole rows, 16 bytes per thread, instead of one
     // 2-byte store per row and thread.
     bf16 (*sQs)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf);
-    bf16 (*sKs)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf + C * PA * 2);
-    static_assert(2 * C * PA * 2 <= SBUF, "staged Qg and Kh fit the level-table bytes");
+    static_assert(C * PA * 2 <= SBUF, "staged Qg fits the level-table bytes");
     bf16* Qgc = Qgb + (size_t)ch * C * DK;
-    bf16* Khc = Khb + (size_t)ch * C * DK;
     if (cp) {
         float pre = 1.f, suf = 1.f;
         for (int pp = 0; pp < part; ++pp) pre *= stot[pp][c];
@@ -809,7 +800,6 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             kh[i] = kv[i] * kap;
             kap *= a[i];
         }
-        bf16* QgTc = QgTb + (size_t)ch * C * DK;
         bf16* KhTc = KhTb + (size_t)ch * C * DK;
 #pragma unroll
         for (int i = 0; i < RPP; ++i) sQs[p0 + i][c] = f32_to_bf16(qg[i]);
@@ -824,21 +814,11 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
         for (int i = 0; i < RPP; i += 4)
             *reinterpret_cast<uint2*>(&sXT[c][p0 + i]) = pack4_bf16(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
-        if (bwdt) {
-            // the backward scan's Qg^T and Kh: contraction index permuted (kperm.h)
-#pragma unroll
-            for (int i = 0; i < RPP; i += 4)
-                *reinterpret_cast<uint2*>(&QgTc[c * C + kperm_pos(p0 + i)]) =
-                    pack4_bf16(qg[i], qg[i + 1], qg[i + 2], qg[i + 3]);
-#pragma unroll
-            for (int i = 0; i < RPP; ++i) sKs[p0 + i][kperm_pos(c)] = f32_to_bf16(kh[i]);
-        }
     }
     __syncthreads();  // staged rows complete
     for (int idx = tid; idx < C * DK / 8; idx += NTHR_P) {
         const int r = idx / (DK / 8), c0 = (idx % (DK / 8)) * 8;
         *reinterpret_cast<uint4*>(&Qgc[r * DK + c0]) = *reinterpret_cast<const uint4*>(&sQs[r][c0]);
-        if (bwdt) *reinterpret_cast<uint4*>(&Khc[r * DK + c0]) = *reinterpret_cast<const uint4*>(&sKs[r][c0]);
     }
     __syncthreads();  // the staged rows are read: sT takes their bytes
     for (int idx = tid; idx < C * PC; idx += NTHR_P) (&sT[0][0])[idx] = 0.f;
@@ -921,9 +901,6 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         bf16* Wc = Wb + (size_t)ch * C * DK;
 #pragma unroll
         for (int r = 0; r < 4; ++r) Wc[(ti * 16 + 4 * lq + r) * DK + tj * 16 + lr] = f32_to_bf16(acc[r]);
-        if (bwdt)  // the backward scan's W^T: token index permuted (kperm.h)
-            *reinterpret_cast<uint2*>(&WTb[(size_t)ch * C * DK + (tj * 16 + lr) * C + kperm_pos(ti * 16 + 4 * lq)]) =
-                pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();  // X_V^T complete
     // ---- U = T X_V (fp32 out; Uro, training with clip: also before clipping).
@@ -1554,7 +1531,6 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
     bf16* Wro = raw ? (bf16*)(ws + p.o_Wr) : nullptr;
     dim3 grid((unsigned)p.n_ch), block(NTHR);
     if constexpr (bf16_tables<TIn, C, DK>()) {
-        const size_t n = p.n_ch;
         bf16* Wb = (bf16*)W;
         bf16* Qb = (bf16*)Qg;
         bf16* Kb = (bf16*)Kh;
@@ -1564,8 +1540,7 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
                        (prep2_kernel<C, DK, DV, decltype(pch)::value, decltype(l2n)::value,
                                      decltype(safe)::value>),
                        grid, dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g,
-                       beta, p.T, p.H, p.NC, p.scale, Wb, Wb + n * C * DK, U, Qb, Qb + n * C * DK,
-                       Kb, Kb + n * C * DK, Pb, Pb + n * C * C, gam, Tm, rn, sf, Wro, Uro);
+                       beta, p.T, p.H, p.NC, p.scale, Wb, U, Qb, Kb, Pb, gam, Tm, rn, sf, Wro, Uro);
             return GDN_OK;
         };
         return with_bool(p.decay == GDN_DECAY_PER_CHANNEL, [&](auto pch) {

@@ -3,8 +3,8 @@
 // A v_mfma_f32_16x16x32_bf16 operand lane l (row or column l%16, lane group
 // g = l/16) supplies the eight K values at positions 8g..8g+7 of a 32-long K
 // block, while an accumulator tile leaves lane l holding rows 4g..4g+3 of its
-// 16 rows.  If every table a scan reads stores its K index, inside each block of
-// 32, in the order
+// 16 rows.  If every operand a scan reads from memory supplies its K index,
+// inside each block of 32, in the order
 //     stored position 8g + j  <-  index 4g + j          (j = 0..3)
 //     stored position 8g + j  <-  index 16 + 4g + j - 4 (j = 4..7)
 // then the eight values a lane must supply for K block kb are exactly the four
@@ -19,13 +19,6 @@
 #include "common.h"
 
 namespace gdn {
-
-// index k (any non-negative int) -> its stored position
-__host__ __device__ constexpr int kperm_pos(int k)
-{
-    const int c = k & 31, og = c >> 2, e = c & 3;
-    return (k & ~31) + 4 * (og < 4 ? 2 * og : 2 * (og - 4) + 1) + e;
-}
 
 // operand fragment from two accumulator tiles (rows 32kb.. and 32kb + 16..),
 // rounded to bf16 nearest-even
@@ -56,27 +49,6 @@ __device__ __forceinline__ bf16x8 frag_ident(int half)
         w[j >> 1] = one;
     }
     return __builtin_bit_cast(bf16x8, w);
-}
-
-// Swizzled LDS tables of 16-byte words, row-major with WPR words a row: word w
-// of row r sits in slot r * WPR + (w ^ swz(r)).  A fragment read (rows r0 + m,
-// m = 0..15, one word each) then touches 16 distinct 16-byte bank groups for
-// WPR = 16 (256-byte rows) and WPR = 8 (128-byte rows).
-template <int WPR>
-__device__ __forceinline__ int kswz(int r)
-{
-    static_assert(WPR == 16 || WPR == 8, "256- or 128-byte rows");
-    return WPR == 16 ? (r & 15) : ((r >> 1) & 7);
-}
-
-// operand fragment of K block kb from rows r0.. of a swizzled table: lane
-// (g = l/16, m = l%16) reads word 4 kb + g of row r0 + m
-template <int WPR>
-__device__ __forceinline__ bf16x8 frag_lds(const uint4* tab, int r0, int kb)
-{
-    const int l = lane_id(), r = r0 + (l & 15);
-    const uint4 v = tab[r * WPR + ((4 * kb + (l >> 4)) ^ kswz<WPR>(r))];
-    return __builtin_bit_cast(bf16x8, v);
 }
 
 // Touch the 128-byte line holding gptr so that it is in the L2 when the real

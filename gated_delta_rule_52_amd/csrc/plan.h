@@ -26,12 +26,11 @@
 //                     per-head dg (bf16 inputs at chunk 64)
 //   Ur  [ch][C][Dv], Wr [ch][C][Dk] (bf16): with clip, the products T X_V and
 //                     T X_K before clipping, for the WY adjoint of the bf16 path
-// With bf16 inputs at chunk 64 the tables W, Qg, Kh, Ps are bf16 and each
-// region holds two of them: the forward scan's (W [C][Dk], Qg [C][Dk],
-// Kh^T [Dk][C], Ps [C][C]) and then the backward scan's (W^T [Dk][C],
-// Qg^T [Dk][C], Kh [C][Dk], Ps^T [C][C]), the latter with their contraction
-// (column) index stored in the K-permuted order of kperm.h; the backward's
-// hand-offs are bf16 too: dQg, dKh, dPs;
+// With bf16 inputs at chunk 64 the tables W, Qg, Kh, Ps are bf16, in the
+// first half of their fp32-sized regions, in one orientation: W [C][Dk],
+// Qg [C][Dk], Kh^T [Dk][C], Ps [C][C] (the backward scan reads their
+// transposes with transposing LDS loads); the backward's hand-offs are bf16
+// too: dQg, dKh, dPs;
 // the dW region holds dX_K = T^T dW and the dT1 region the strictly lower
 // dA = -(dX_V U^T + dX_K W^T).
 // G is the chunk-local inclusive cumulative log-decay and Gamma = exp(G).

@@ -38,6 +38,17 @@ struct SwzU16 {
     __device__ static int f(int r) { return r & 15; }
 };
 
+// 8 (16) units a row, read only by transposing loads in the K-permuted order
+// of kperm.h (frag_cols_kperm)
+struct SwzK8 {
+    static constexpr int U = 8;
+    __device__ static int f(int r) { return r & 6; }
+};
+struct SwzK16 {
+    static constexpr int U = 16;
+    __device__ static int f(int r) { return 2 * (r & 7); }
+};
+
 template <class S>
 __device__ __forceinline__ int swz_slot(int r, int u)
 {
@@ -78,6 +89,25 @@ __device__ __forceinline__ bf16x8 frag_cols(const void* tab, int k0, int m0)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int k = k0 + 8 * g + 4 * h + (j >> 2);
+        const bf16* p = swz_at<S>(const_cast<void*>(tab), k, m0 + 4 * (j & 3));
+        v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// As frag_cols, with the operand's K index in the order of kperm.h: position
+// 8 g + e (e < 4) holds K index 4 g + e and position 8 g + 4 + e index
+// 16 + 4 g + e, within the 32-long block from k0.  Lane j of group g reads row
+// k0 + 16 h + 4 g + (j >> 2) in load h.
+template <class S>
+__device__ __forceinline__ bf16x8 frag_cols_kperm(const void* tab, int k0, int m0)
+{
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int l = lane_id(), j = l & 15, g = l >> 4;
+    s16x4 v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int k = k0 + 16 * h + 4 * g + (j >> 2);
         const bf16* p = swz_at<S>(const_cast<void*>(tab), k, m0 + 4 * (j & 3));
         v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
     }
