@@ -106,7 +106,7 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True, l2n=False)
         by += cv * ib + cv * f4                                    # v in, U out
         fl[mt] += 2 * (2 * tri * DK) + 2 * tri * (DK + DV)         # P, A; W = T X_K, U = T X_V
         if name == "prep_T":
-            by += (3 * cd + cc) * (tb if bt else 0) + cc * f4      # transposed tables, T
+            by += cc * f4                                          # T
         by += 2 * C * f4 if l2n else 0                             # r of the q and k rows
         fl["f32"] += 2 * C ** 3 / 3                                # (I + A)^-1
     elif name in ("scan", "scan_save", "scan_train"):
@@ -121,7 +121,7 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True, l2n=False)
                 by += kv * tb + (cv * 2 if bt else 0)              # chunk-start states, D
             fl[mt] += 6 * C * DK * DV + 2 * tri * DV
     elif name == "bscan":
-        by = cc * tb + 3 * cd * tb + DK * f4 + cv * ib             # Ps^T Kh Qg^T W^T, gam, dO
+        by = cc * tb + 3 * cd * tb + DK * f4 + cv * ib             # Ps Kh^T Qg W, gam, dO
         by += kv * tb + cv * tb                                    # dS (chunk ends), dD
         fl[mt] += 6 * C * DK * DV + 2 * tri * DV
     elif name == "bchunk1":
