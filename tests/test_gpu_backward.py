@@ -166,8 +166,9 @@ def test_long_state_carry_training_shape(dtype, decay):
     """B=8 T=4096 H=6 128x128 (the training shape) with a decay a hundred times
     weaker than the default draw: each 64-token chunk keeps about e^-0.5 of its
     start state, so the state is carried through all 64 chunks (the gated-deltanet
-    card's "long product chain", Requirements) and the saved chunk-start states,
-    chunk deltas and state gradients weigh in every result.  h0 ~ N(0, 0.1).
+    card, Requirements: the state is a long chain of products) and the saved
+    chunk-start states, chunk deltas and state gradients weigh in every result.
+    h0 ~ N(0, 0.1).
     gdn_forward, and the training pair gdn_forward_train + gdn_backward_train,
     against the oracle on sampled heads: o, hT and all six gradients."""
     import gated_delta_rule_52_amd as gdn
