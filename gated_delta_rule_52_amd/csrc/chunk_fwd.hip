@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "chunk_common.h"
+#include "swz.h"
 #include "plan.h"
 
 namespace gdn {
@@ -1084,9 +1085,12 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
              bf16* __restrict__ Sst, bf16* __restrict__ Dst, int BH, int T, int H, int NC)
 {
     constexpr int BV = 32, NS = DV / BV, NW = NTHR_S / 64;
-    constexpr int PA = DK + 8, PT = C + 8;  // bf16 pitches: rows 16-byte aligned, banks spread
     constexpr int TD = (C / 16) * (BV / 16), TS = (DK / 16) * (BV / 16);
     constexpr int MD = (TD + NW - 1) / NW, MS = (TS + NW - 1) / NW;
+    // bf16 tables as swizzled rows (swz.h): rows of DK values SA, rows of C values SC
+    using SA = std::conditional_t<DK == 128, SwzU16, SwzU8w>;
+    using SC = SwzU8w;
+    static_assert(C == 64 && (DK == 128 || DK == 64), "row widths of the swizzles");
     // 16-byte words of one chunk's tables.  Each table is a whole number of words
     // per thread, so the table of word slot q is known at compile time and the
     // prefetch has no branches: the compiler then waits exactly for it, not also
@@ -1095,7 +1099,9 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
     constexpr int QALL = 2 * QW + QK + QP, QPT = (QALL + NTHR_S - 1) / NTHR_S;
     static_assert(QW % NTHR_S == 0 && QK % NTHR_S == 0 && QP % NTHR_S == 0, "table split");
     static_assert(TD % NW == 0 && TS % NW == 0, "tile split");
-    __shared__ __align__(16) bf16 sW[C][PA], sQ[C][PA], sKT[DK][PT], sP[C][PT], sSt[BV][PA], sDt[BV][PT];
+    // W, Qg [C][DK], Kh^T [DK][C], Ps [C][C], and the bf16 copies S^T [BV][DK], D^T [BV][C]
+    __shared__ __align__(16) uint4 sW[C * DK / 8], sQ[C * DK / 8], sKT[DK * C / 8], sP[C * C / 8],
+        sSt[BV * DK / 8], sDt[BV * C / 8];
     // staging of each step's outputs (double-buffered by step parity), written
     // out with 16-byte stores: the next chunk's start state, D and o (bf16; the
     // saved states feed the backward's bf16 products and its decay-gradient sums)
@@ -1123,7 +1129,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 sacc[m][r] = h0 ? h0[((size_t)bh * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] : 0.f;
-            *reinterpret_cast<uint2*>(&sSt[sj * 16 + lr][si * 16 + 4 * lq]) =
+            *reinterpret_cast<uint2*>(swz_at<SA>(sSt, sj * 16 + lr, si * 16 + 4 * lq)) =
                 pack4_bf16(sacc[m][0], sacc[m][1], sacc[m][2], sacc[m][3]);
         }
     }
@@ -1176,16 +1182,16 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         for (int q = 0; q < QPT; ++q) {
             const int idx = tid + NTHR_S * q;
             if (q * NTHR_S < QW) {
-                *reinterpret_cast<uint4*>(&sW[idx / (DK / 8)][(idx % (DK / 8)) * 8]) = pf[q];
+                *reinterpret_cast<uint4*>(swz_at<SA>(sW, idx / (DK / 8), (idx % (DK / 8)) * 8)) = pf[q];
             } else if (q * NTHR_S < 2 * QW) {
                 const int e = idx - QW;
-                *reinterpret_cast<uint4*>(&sQ[e / (DK / 8)][(e % (DK / 8)) * 8]) = pf[q];
+                *reinterpret_cast<uint4*>(swz_at<SA>(sQ, e / (DK / 8), (e % (DK / 8)) * 8)) = pf[q];
             } else if (q * NTHR_S < 2 * QW + QK) {
                 const int e = idx - 2 * QW;
-                *reinterpret_cast<uint4*>(&sKT[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
+                *reinterpret_cast<uint4*>(swz_at<SC>(sKT, e / (C / 8), (e % (C / 8)) * 8)) = pf[q];
             } else {
                 const int e = idx - 2 * QW - QK;
-                *reinterpret_cast<uint4*>(&sP[e / (C / 8)][(e % (C / 8)) * 8]) = pf[q];
+                *reinterpret_cast<uint4*>(swz_at<SC>(sP, e / (C / 8), (e % (C / 8)) * 8)) = pf[q];
             }
         }
 #pragma unroll
@@ -1227,18 +1233,26 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         for (int m = 0; m < MD; ++m) {
             const int idx = w + NW * m;
             const int ti = idx / (BV / 16), tj = idx % (BV / 16);
-            f32x4 ws = mma_kc<DK>(zero4(), &sW[ti * 16][0], PA, &sSt[tj * 16][0], PA);
+            f32x4 ws = zero4();
+#pragma unroll
+            for (int u0 = 0; u0 < DK / 8; u0 += 4)
+                ws = mfma_bf16_16x16x32(frag_rows<SA>(sW, ti * 16, u0), frag_rows<SA>(sSt, tj * 16, u0), ws);
             float dv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) dv[r] = uc[m][r] - ws[r];
-            *reinterpret_cast<uint2*>(&sDt[tj * 16 + lr][ti * 16 + 4 * lq]) = pack4_bf16(dv[0], dv[1], dv[2], dv[3]);
+            *reinterpret_cast<uint2*>(swz_at<SC>(sDt, tj * 16 + lr, ti * 16 + 4 * lq)) = pack4_bf16(dv[0], dv[1], dv[2], dv[3]);
             if (SAVE) {  // staged as 32-bit words of column pairs
                 const uint2 wd = acc_colpairs(f32x4{dv[0], dv[1], dv[2], dv[3]});
                 const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
                 *reinterpret_cast<uint32_t*>(&sDr[pb][i2][j2]) = wd.x;
                 *reinterpret_cast<uint32_t*>(&sDr[pb][i2 + 1][j2]) = wd.y;
             }
-            if (OUT) o1[m] = mma_kc<DK>(zero4(), &sQ[ti * 16][0], PA, &sSt[tj * 16][0], PA);
+            if (OUT) {
+                o1[m] = zero4();
+#pragma unroll
+                for (int u0 = 0; u0 < DK / 8; u0 += 4)
+                    o1[m] = mfma_bf16_16x16x32(frag_rows<SA>(sQ, ti * 16, u0), frag_rows<SA>(sSt, tj * 16, u0), o1[m]);
+            }
         }
         __syncthreads();
         if (OUT) {
@@ -1248,7 +1262,9 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 const int ti = idx / (BV / 16), tj = idx % (BV / 16);
                 // P is lower triangular: columns past the tile row are zero
                 const int K = ((16 * (ti + 1) + 31) / 32) * 32;
-                const f32x4 acc = mma_kc_dyn(o1[m], &sP[ti * 16][0], PT, &sDt[tj * 16][0], PT, K);
+                f32x4 acc = o1[m];
+                for (int u0 = 0; u0 < K / 8; u0 += 4)
+                    acc = mfma_bf16_16x16x32(frag_rows<SC>(sP, ti * 16, u0), frag_rows<SC>(sDt, tj * 16, u0), acc);
                 const uint2 wo = acc_colpairs(acc);
                 const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
                 *reinterpret_cast<uint32_t*>(&sOr[pb][i2][j2]) = wo.x;
@@ -1263,8 +1279,11 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             f32x4 acc;
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = gc[m][r] * sacc[m][r];
-            sacc[m] = mma_kc<C>(acc, &sKT[si * 16][0], PT, &sDt[sj * 16][0], PT);
-            *reinterpret_cast<uint2*>(&sSt[sj * 16 + lr][si * 16 + 4 * lq]) =
+#pragma unroll
+            for (int u0 = 0; u0 < C / 8; u0 += 4)
+                acc = mfma_bf16_16x16x32(frag_rows<SC>(sKT, si * 16, u0), frag_rows<SC>(sDt, sj * 16, u0), acc);
+            sacc[m] = acc;
+            *reinterpret_cast<uint2*>(swz_at<SA>(sSt, sj * 16 + lr, si * 16 + 4 * lq)) =
                 pack4_bf16(sacc[m][0], sacc[m][1], sacc[m][2], sacc[m][3]);
             if (SAVE) {
                 const uint2 wsf = acc_colpairs(sacc[m]);
@@ -1352,9 +1371,12 @@ scan3_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
              int BH, int T, int H, int NC)
 {
     constexpr int BV = 32, NS = DV / BV, NW = NTHR_S / 64;
-    constexpr int PA = DK + 8, PT = C + 8;  // bf16 pitches: rows 16-byte aligned, banks spread
     constexpr int TD = (C / 16) * (BV / 16), TS = (DK / 16) * (BV / 16);
     constexpr int MD = TD / NW, MS = TS / NW;
+    // bf16 tables as swizzled rows (swz.h): rows of DK values SA, rows of C values SC
+    using SA = std::conditional_t<DK == 128, SwzU16, SwzU8w>;
+    using SC = SwzU8w;
+    static_assert(C == 64 && (DK == 128 || DK == 64), "row widths of the swizzles");
     static_assert(TD % NW == 0 && TS % NW == 0, "every wave owns whole tiles");
     // a buffer as 16-byte words: the four tables (row widths WC, WK), then the
     // U slice [C][BV] fp32 (BV / 4 words a row) and the decay (DK / 4 words,
@@ -1369,12 +1391,12 @@ scan3_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
     // two buffers, separate arrays: the compiler then sees that reads of one
     // cannot alias the direct loads into the other and does not wait for them
     __shared__ __align__(16) uint4 sTab0[QB], sTab1[QB];
-    __shared__ __align__(16) bf16 sSt[BV][PA], sDt[BV][PT];
+    __shared__ __align__(16) uint4 sSt[BV * DK / 8], sDt[BV * C / 8];  // S^T, D^T (SA, SC)
     // 2-byte views for the transposed writes: one index expression per write
     // keeps each address a single step from its array (the alias information
     // that spares those writes a wait for the direct loads is kept)
-    uint16_t* const St16 = &sSt[0][0].bits;
-    uint16_t* const Dt16 = &sDt[0][0].bits;
+    uint16_t* const St16 = reinterpret_cast<uint16_t*>(sSt);
+    uint16_t* const Dt16 = reinterpret_cast<uint16_t*>(sDt);
 
     const int x = blockIdx.x;
     const int grp = x / (8 * NS), rem = x % (8 * NS);
@@ -1396,11 +1418,12 @@ scan3_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             sacc[m] = *reinterpret_cast<const f32x4*>(
                 h0 + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + sj * 16 + 4 * lq);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) St16[(sj * 16 + 4 * lq + r) * PA + si * 16 + lr] = f32_to_bf16(sacc[m][r]).bits;
+        for (int r = 0; r < 4; ++r) St16[swz_elem<SA>(sj * 16 + 4 * lq + r, si * 16 + lr)] = f32_to_bf16(sacc[m][r]).bits;
     }
 
-    // slot tid + NTHR_S q of a buffer takes table word (row, w ^ (row & 7)),
-    // (row, w) being the slot's place in its table; the U slice likewise
+    // slot tid + NTHR_S q of a buffer takes table word (row, w ^ f(row)), (row, w)
+    // being the slot's place in its table (rows of DK values SA, of C values
+    // SC); the U slice takes word (row, w ^ (row & 7))
     int goff[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
@@ -1408,7 +1431,7 @@ scan3_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         const int wpr = (g0 >= OW && g0 < OK) ? WK : WC;
         const int s = g0 + tid - (g0 < OW ? OP : g0 < OQ ? OW : g0 < OK ? OQ : OK);
         const int row = s / wpr, wd = s % wpr;
-        goff[q] = (row * wpr + (wd ^ (row & 7))) * 8;
+        goff[q] = (row * wpr + (wd ^ (wpr == WK ? SA::f(row) : SC::f(row)))) * 8;
     }
     const int urow = tid / WU, uoff = urow * DV + v0 + 4 * ((tid % WU) ^ (urow & 7));
     auto fetch = [&](int n, uint4* buf) {
@@ -1447,11 +1470,17 @@ scan3_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         for (int m = 0; m < MD; ++m) {
             const int idx = w + NW * m;
             const int ti = idx / (BV / 16), tj = idx % (BV / 16);
-            const f32x4 ws = mma_kc_bsw<DK, WK>(zero4(), &sSt[tj * 16][0], PA, tb + OW, ti * 16);
+            f32x4 ws = zero4();
+#pragma unroll
+            for (int u0 = 0; u0 < WK; u0 += 4)
+                ws = mfma_bf16_16x16x32(frag_rows<SA>(sSt, tj * 16, u0), frag_rows<SA>(tb + OW, ti * 16, u0), ws);
             const f32x4 u4 = *reinterpret_cast<const f32x4*>(tb + OU + (ti * 16 + lr) * WU + ((tj * 4 + lq) ^ (lr & 7)));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Dt16[(tj * 16 + 4 * lq + r) * PT + ti * 16 + lr] = f32_to_bf16(u4[r] - ws[r]).bits;
-            o1[m] = mma_kc_bsw<DK, WK>(zero4(), &sSt[tj * 16][0], PA, tb + OQ, ti * 16);
+            for (int r = 0; r < 4; ++r) Dt16[swz_elem<SC>(tj * 16 + 4 * lq + r, ti * 16 + lr)] = f32_to_bf16(u4[r] - ws[r]).bits;
+            o1[m] = zero4();
+#pragma unroll
+            for (int u0 = 0; u0 < WK; u0 += 4)
+                o1[m] = mfma_bf16_16x16x32(frag_rows<SA>(sSt, tj * 16, u0), frag_rows<SA>(tb + OQ, ti * 16, u0), o1[m]);
         }
         __syncthreads();
         // O^T += D^T P^T (P lower triangular: columns past the tile row are zero)
@@ -1459,11 +1488,9 @@ scan3_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         for (int m = 0; m < MD; ++m) {
             const int idx = w + NW * m;
             const int ti = idx / (BV / 16), tj = idx % (BV / 16);
-            f32x4 acc;
-            if (16 * (ti + 1) <= 32)
-                acc = mma_kc_bsw<32, WC>(o1[m], &sDt[tj * 16][0], PT, tb + OP, ti * 16);
-            else
-                acc = mma_kc_bsw<C, WC>(o1[m], &sDt[tj * 16][0], PT, tb + OP, ti * 16);
+            f32x4 acc = mfma_bf16_16x16x32(frag_rows<SC>(sDt, tj * 16, 0), frag_rows<SC>(tb + OP, ti * 16, 0), o1[m]);
+            if (16 * (ti + 1) > 32)
+                acc = mfma_bf16_16x16x32(frag_rows<SC>(sDt, tj * 16, 4), frag_rows<SC>(tb + OP, ti * 16, 4), acc);
             const int t = n * C + ti * 16 + lr;
             if (!LAST || t < T)
                 *reinterpret_cast<uint2*>(o + (((size_t)b * T + t) * H + h) * DV + v0 + tj * 16 + 4 * lq) =
@@ -1479,9 +1506,12 @@ scan3_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             f32x4 acc;
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = gk * sacc[m][r];
-            sacc[m] = mma_kc_bsw<C, WC>(acc, &sDt[sj * 16][0], PT, tb + OK, si * 16);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) St16[(sj * 16 + 4 * lq + r) * PA + si * 16 + lr] = f32_to_bf16(sacc[m][r]).bits;
+            for (int u0 = 0; u0 < WC; u0 += 4)
+                acc = mfma_bf16_16x16x32(frag_rows<SC>(sDt, sj * 16, u0), frag_rows<SC>(tb + OK, si * 16, u0), acc);
+            sacc[m] = acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) St16[swz_elem<SA>(sj * 16 + 4 * lq + r, si * 16 + lr)] = f32_to_bf16(sacc[m][r]).bits;
         }
         if constexpr (!LAST) {
             wait_vmcnt<AFTER>();  // chunk n + 1's loads have landed

@@ -174,27 +174,6 @@ __device__ __forceinline__ f32x4 mma_kc_dyn(f32x4 acc, const bf16* __restrict__ 
     return acc;
 }
 
-// As mma_kc, with Bt in a compact swizzled LDS table of 16-byte words: row j
-// holds WPR words, and word w of row j sits in slot j*WPR + (w ^ (j & 7)), so
-// the 16-byte reads of eight consecutive rows at one word hit distinct banks
-// without row padding.  row0 (the tile's first row) is a multiple of 16.
-template <int K, int WPR>
-__device__ __forceinline__ f32x4 mma_kc_bsw(f32x4 acc, const bf16* __restrict__ A, int lda,
-                                            const uint4* __restrict__ Bt, int row0)
-{
-    static_assert(WPR % 8 == 0 && K <= 8 * WPR, "swizzle within whole groups of 8 words");
-    const int l = lane_id();
-    const int r = l & 15, kk = l >> 4;
-    const uint4* brow = Bt + (row0 + r) * WPR;
-#pragma unroll
-    for (int k = 0; k < K; k += 32) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + k + 8 * kk);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(brow + ((k / 8 + kk) ^ (r & 7)));
-        acc = mfma_bf16_16x16x32(a, b, acc);
-    }
-    return acc;
-}
-
 // K = 16 on the 16x16x32 instruction: the lanes of the upper K half read an
 // in-range copy of the lower half and supply a zero B operand.
 __device__ __forceinline__ f32x4 mma_kc16(f32x4 acc, const bf16* __restrict__ A, int lda,

@@ -55,6 +55,13 @@ __device__ __forceinline__ int swz_slot(int r, int u)
     return r * S::U + (u ^ S::f(r));
 }
 
+// index (in bf16 elements) of column c of row r
+template <class S>
+__device__ __forceinline__ int swz_elem(int r, int c)
+{
+    return swz_slot<S>(r, c >> 3) * 8 + (c & 7);
+}
+
 // address of bf16 column c of row r
 template <class S>
 __device__ __forceinline__ bf16* swz_at(void* tab, int r, int c)
