@@ -51,23 +51,4 @@ __device__ __forceinline__ bf16x8 frag_ident(int half)
     return __builtin_bit_cast(bf16x8, w);
 }
 
-// Touch the 128-byte line holding gptr so that it is in the L2 when the real
-// load comes: a 4-byte direct load into an LDS sink that nobody reads (lane i
-// writes sink_wave_base + 4 i).  Counted by vmcnt like any load.
-__device__ __forceinline__ void warm_line(const void* gptr, const void* sink_wave_base)
-{
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)sink_wave_base);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0v), "v"(gptr) : "memory", "m0");
-}
-
-// s_waitcnt with only the vector memory count limited, 0 <= N < 64 (gfx9
-// encoding: vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14)
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 }  // namespace gdn
