@@ -97,6 +97,7 @@ bscan_kernel(const float* __restrict__ Qgi, const float* __restrict__ Khi,
                 st4(&sK[r][c4], load4<float>(Kp + r * DK + c4));
                 st4(&sW[r][c4], load4<float>(Wp + r * DK + c4));
             }
+
             const float* Pp = Psi + ch * C * C;
             for (int idx = tid; idx < C * C / 4; idx += NTHR) {
                 const int r = idx / (C / 4), c4 = (idx % (C / 4)) * 4;
@@ -166,6 +167,194 @@ bscan_kernel(const float* __restrict__ Qgi, const float* __restrict__ Khi,
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// bscanf: the reverse scan over fp32 chunk tables (fp32 inputs, chunk 64) on
+// v_mfma_f32_16x16x4_f32, the counterpart of scanf.  8 waves, one (b, h,
+// 32-wide Dv slice) per workgroup; the state gradient dS' lives transposed in
+// the MFMA accumulators of its owner waves (a lane's four values are four
+// consecutive Dv columns of one row of dS').  Per chunk, two phases:
+//   A: dD^T = dS'^T Kh^T + dO^T P                      (reads Kh^T, P, dO)
+//   B: dS^T = gam dS'^T + dO^T Qg - dD^T W              (reads Qg, W, dO, gam)
+// dS'^T and -dD^T go through LDS as K-contiguous A operands; the forward's
+// tables are read down their columns (4-byte reads, K = 4 g + e, on the fp32
+// row swizzle that keeps them free of bank conflicts), and so is the dO slice,
+// whose rows are stored in an order (row s at s ^ bit2(s), its units XOR-ed by
+// 4 bit3) that makes those reads conflict-free too.  Direct loads bring Qg, W
+// and the decay of this chunk during phase A and Kh^T, P and dO of the next
+// (earlier) chunk during phase B; dO has two buffers, being read in both
+// phases.  dO rows past the sequence end are loaded from its last row: the
+// rows of P and Qg they meet are zero there.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ void __launch_bounds__(512)
+bscanf_kernel(const float* __restrict__ KhTt, const float* __restrict__ Pst,
+              const float* __restrict__ Qgt, const float* __restrict__ Wt,
+              const float* __restrict__ gami, const float* __restrict__ dO,
+              const float* __restrict__ dhT, float* __restrict__ dSt, float* __restrict__ dDt,
+              float* __restrict__ dh0, int BH, int T, int H, int NC)
+{
+    constexpr int C = 64, BV = 32, NS = DV / BV, NW = 8, NT = 64 * NW;
+    constexpr int TS = (DK / 16) * (BV / 16), MS = TS / NW;
+    static_assert(DK == 128 || DK == 64, "64 or 128 key channels");
+    static_assert((C / 16) * (BV / 16) == NW && TS % NW == 0, "one dD tile and whole state tiles per wave");
+    using SK = SwzF<DK / 4>;  // rows of DK floats
+    using SC = SwzF<C / 4>;   // rows of C floats
+    constexpr int UK = DK / 4, UC = C / 4, UB = BV / 4;
+    // LDS in 16-byte units.  group A: Kh^T [DK][C], P [C][C]; group B: Qg, W [C][DK], decay
+    constexpr int OK = 0, OP = OK + DK * UC, OQ = OP + C * UC, OW = OQ + C * UK, OG = OW + C * UK;
+    constexpr int NTAB = OG + 64;
+    constexpr int NQK = C * UK / NT, NQC = DK * UC / NT, NQP = C * UC / NT;
+    static_assert(C * UK % NT == 0 && C * UC % NT == 0 && C * UB == NT,
+                  "every direct-load instruction lies in one table");
+    __shared__ __align__(16) f32x4 tab[NTAB];
+    __shared__ __align__(16) f32x4 sdO0[C * UB], sdO1[C * UB];
+    __shared__ __align__(16) f32x4 sSt[BV * UK], sDt[BV * UC];
+    float* const St = reinterpret_cast<float*>(sSt);
+    float* const Dt = reinterpret_cast<float*>(sDt);
+
+    const int x = blockIdx.x;
+    const int grp = x / (8 * NS), rem = x % (8 * NS);
+    const int sl = rem / 8, bh = grp * 8 + rem % 8;
+    if (bh >= BH) return;
+    const int b = bh / H, h = bh % H;
+    const int v0 = sl * BV;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+    const int tj = w & 1, ti = w >> 1;
+
+    int gk[NQK], gc[NQC];
+#pragma unroll
+    for (int q = 0; q < NQK; ++q) {
+        const int s = q * NT + tid, row = s / UK, u = s % UK;
+        gk[q] = (row * UK + (u ^ SK::f(row))) * 4;
+    }
+#pragma unroll
+    for (int q = 0; q < NQC; ++q) {
+        const int s = q * NT + tid, row = s / UC, u = s % UC;
+        gc[q] = (row * UC + (u ^ SC::f(row))) * 4;
+    }
+    // dO slot tid: stored row pr holds token row pr ^ bit2(pr), stored unit
+    // pu holds unit pu ^ 4 bit3(pr) of the slice
+    const int pr = tid / UB, pu = tid % UB;
+    const int orow = pr ^ ((pr >> 2) & 1), ocol = v0 + 4 * (pu ^ (((pr >> 3) & 1) << 2));
+    auto fetchA = [&](int n, f32x4* sdo) {
+        const size_t ch = (size_t)bh * NC + n;
+#pragma unroll
+        for (int q = 0; q < NQC; ++q) dma16(KhTt + ch * C * DK + gc[q], tab + OK + q * NT + 64 * w);
+#pragma unroll
+        for (int q = 0; q < NQP; ++q) dma16(Pst + ch * C * C + gc[q], tab + OP + q * NT + 64 * w);
+        const int t = min(n * C + orow, T - 1);
+        dma16(dO + (((size_t)b * T + t) * H + h) * DV + ocol, sdo + 64 * w);
+    };
+    auto fetchB = [&](int n) {
+        const size_t ch = (size_t)bh * NC + n;
+        if (w == 0) dma16(gami + ch * DK + 4 * (l % (DK / 4)), tab + OG);
+#pragma unroll
+        for (int q = 0; q < NQK; ++q) {
+            dma16(Qgt + ch * C * DK + gk[q], tab + OQ + q * NT + 64 * w);
+            dma16(Wt + ch * C * DK + gk[q], tab + OW + q * NT + 64 * w);
+        }
+    };
+    // operand with K = token rows: lane (m, g) receives dO(k0 + 4 g + e, tj*16 + m)
+    auto dO_cols = [&](const f32x4* sdo, int k0) {
+        const float* t = reinterpret_cast<const float*>(sdo);
+        const int c = tj * 16 + lr;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = k0 + 4 * lq + e, r = s ^ ((s >> 2) & 1);
+            v[e] = t[(r * UB + ((c >> 2) ^ (((r >> 3) & 1) << 2))) * 4 + (c & 3)];
+        }
+        return v;
+    };
+
+    // state tile m: sacc[m][r] = dS'[si*16 + lr][v0 + tj*16 + 4 lq + r], si = ti + 4 m
+    f32x4 sacc[MS];
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        const int si = ti + (NW / 2) * m;
+        sacc[m] = zero4();
+        if (dhT)
+            sacc[m] = *reinterpret_cast<const f32x4*>(dhT + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + tj * 16 + 4 * lq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) St[swzf_idx<SK>(tj * 16 + 4 * lq + r, si * 16 + lr)] = sacc[m][r];
+    }
+    fetchA(NC - 1, ((NC - 1) & 1) ? sdO1 : sdO0);
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    constexpr int AFTERB = MS + 1;  // dS' and dD stores issued after group B
+    static_assert(AFTERB < 16, "vmcnt field");
+    auto step = [&](int n, const f32x4* sdo, f32x4* sdo_next, auto last_c) {
+        constexpr bool LAST = decltype(last_c)::value;
+        const size_t ch = (size_t)bh * NC + n;
+        fetchB(n);
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int si = ti + (NW / 2) * m;
+            *reinterpret_cast<f32x4*>(dSt + (ch * DK + si * 16 + lr) * DV + v0 + tj * 16 + 4 * lq) = sacc[m];
+        }
+        // phase A: acc[r] = dD^T[tj*16 + 4 lq + r][ti*16 + lr]
+        f32x4 dd = zero4();
+#pragma unroll
+        for (int u0 = 0; u0 < UK; u0 += 4)
+            dd = mma_f32_k16(ffrag_rows<SK>(sSt, tj * 16, u0), ffrag_cols<SC>(tab + OK, 4 * u0, ti * 16), dd);
+        // P^T dO: P[s][t] is zero for s < t, so K runs from the tile's first row
+        for (int k0 = ti * 16; k0 < C; k0 += 16)
+            dd = mma_f32_k16(dO_cols(sdo, k0), ffrag_cols<SC>(tab + OP, k0, ti * 16), dd);
+        *reinterpret_cast<f32x4*>(dDt + (ch * C + ti * 16 + lr) * DV + v0 + tj * 16 + 4 * lq) = dd;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Dt[swzf_idx<SC>(tj * 16 + 4 * lq + r, ti * 16 + lr)] = -dd[r];
+        wait_vmcnt<AFTERB>();  // Qg, W, gam of this chunk have landed
+        __syncthreads();
+        if constexpr (!LAST) fetchA(n - 1, sdo_next);
+        // phase B: dS^T = gam dS'^T + dO^T Qg + (-dD^T) W
+        const float* sg = reinterpret_cast<const float*>(tab + OG);
+        f32x4 acc[MS];
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const float gk = sg[(ti + (NW / 2) * m) * 16 + lr];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[m][r] = gk * sacc[m][r];
+        }
+#pragma unroll
+        for (int kb = 0; kb < C / 16; ++kb) {
+            const f32x4 ao = dO_cols(sdo, 16 * kb);
+            const f32x4 ad = ffrag_rows<SC>(sDt, tj * 16, 4 * kb);
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int si = ti + (NW / 2) * m;
+                acc[m] = mma_f32_k16(ao, ffrag_cols<SK>(tab + OQ, 16 * kb, si * 16), acc[m]);
+                acc[m] = mma_f32_k16(ad, ffrag_cols<SK>(tab + OW, 16 * kb, si * 16), acc[m]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int si = ti + (NW / 2) * m;
+            sacc[m] = acc[m];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) St[swzf_idx<SK>(tj * 16 + 4 * lq + r, si * 16 + lr)] = acc[m][r];
+        }
+        if constexpr (!LAST) {
+            wait_vmcnt<0>();  // Kh^T, P, dO of the next chunk have landed
+            __syncthreads();
+        }
+    };
+    // chunk n reads dO buffer n & 1
+    for (int n = NC - 1; n > 0; --n) {
+        if (n & 1) step(n, sdO1, sdO0, std::false_type{});
+        else step(n, sdO0, sdO1, std::false_type{});
+    }
+    step(0, sdO0, sdO1, std::true_type{});
+    if (dh0) {
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int si = ti + (NW / 2) * m;
+            *reinterpret_cast<f32x4*>(dh0 + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + tj * 16 + 4 * lq) = sacc[m];
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // bscan4: the reverse scan of the state gradient over bf16 chunk tables (bf16
@@ -2274,6 +2463,13 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                    (const bf16*)(ws + p.o_Qg), (const bf16*)(ws + p.o_W),
                    (const float*)(ws + p.o_gam), (const bf16*)dO, dhT, (bf16*)(ws + p.o_dSt),
                    (bf16*)(ws + p.o_dDt), dh0, BH, p.T, p.H, p.NC);
+    } else if constexpr (f32_tables<TIn, C, DK>()) {
+        dim3 grid((unsigned)(((BH + 7) / 8) * 8 * (DV / 32))), block(512);
+        GDN_LAUNCH("bscan", (bscanf_kernel<DK, DV>), grid, block, st,
+                   (const float*)(ws + p.o_Kh), (const float*)(ws + p.o_Ps),
+                   (const float*)(ws + p.o_Qg), (const float*)(ws + p.o_W),
+                   (const float*)(ws + p.o_gam), (const float*)dO, dhT, (float*)(ws + p.o_dSt),
+                   (float*)(ws + p.o_dDt), dh0, BH, p.T, p.H, p.NC);
     } else {
         using SC = BScanCfg<DV>;
         dim3 grid((unsigned)(((BH + 7) / 8) * 8 * SC::NS)), block(NTHR);

@@ -55,6 +55,15 @@ constexpr bool bf16_tables()
     return sizeof(TIn) == 2 && C == 64 && DK >= 64;
 }
 
+// fp32 inputs at chunk 64 run the fp32-operand scans: their tables stay fp32,
+// with Kh stored transposed (Kh^T [DK][C], like the bf16 tables) so that every
+// operand of the forward scan is a K-contiguous row read.
+template <typename TIn, int C, int DK>
+constexpr bool f32_tables()
+{
+    return sizeof(TIn) == 4 && C == 64 && DK >= 64;
+}
+
 template <typename TIn>
 __device__ __forceinline__ float4 load4(const TIn* p);
 template <>

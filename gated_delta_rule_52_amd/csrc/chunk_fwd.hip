@@ -299,9 +299,16 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
             float* Qg = Qgo + (size_t)ch * C * DK;
             float* Kh = Kho + (size_t)ch * C * DK;
 #pragma unroll
-            for (int i = 0; i < HALF; ++i) {
-                Qg[(part * HALF + i) * DK + c] = qgv[i];
-                Kh[(part * HALF + i) * DK + c] = khv[i];
+            for (int i = 0; i < HALF; ++i) Qg[(part * HALF + i) * DK + c] = qgv[i];
+            if constexpr (f32_tables<TIn, C, DK>()) {
+                // Kh^T [DK][C]: this channel's row, its half in 16-byte words
+#pragma unroll
+                for (int i = 0; i < HALF; i += 4)
+                    *reinterpret_cast<float4*>(&Kh[c * C + part * HALF + i]) =
+                        make_float4(khv[i], khv[i + 1], khv[i + 2], khv[i + 3]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < HALF; ++i) Kh[(part * HALF + i) * DK + c] = khv[i];
             }
         }
     }
@@ -1541,6 +1548,179 @@ scan3_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
 }
 
 // ---------------------------------------------------------------------------
+// scanf: the forward scans over fp32 chunk tables (fp32 inputs, chunk 64) on
+// v_mfma_f32_16x16x4_f32.  8 waves, one (b, h, 32-wide Dv slice) per
+// workgroup, the fp32 state slice in the MFMA accumulators of its owner waves
+// for the whole sequence, computed transposed (a lane's four values are four
+// consecutive Dv columns of one row of S, of D or of o).  S^T [BV][DK] and
+// D^T [BV][C] go through LDS as the K-contiguous A operands; the tables W, Qg
+// (rows t), P (rows t) and Kh^T (rows of channels) are the B operands, read
+// along their rows too, so every operand read is one 16-byte LDS read per lane
+// per four MFMAs, on the fp32 row swizzle (SwzF) that keeps them free of bank
+// conflicts.  Per chunk, two phases split by a barrier:
+//   1: D^T = U^T - S^T W^T and O1^T = S^T Qg^T   (reads W, Qg, U)
+//   2: O^T = O1^T + D^T P^T and S^T <- gam S^T + D^T Kh   (reads P, Kh^T, gam)
+// The tables are loaded straight into LDS by direct loads, each group while
+// the other phase runs: P, Kh^T and gam of this chunk during phase 1, W, Qg and
+// U of the next chunk during phase 2 (fp32 tables of two chunks do not fit the
+// LDS together).  The waits count the stores issued after each group.
+// ---------------------------------------------------------------------------
+template <int C, int DK, int DV, bool SAVE, bool OUT>
+__global__ void __launch_bounds__(NTHR_S)
+scanf_kernel(const float* __restrict__ Wt, const float* __restrict__ Qgt,
+             const float* __restrict__ KhTt, const float* __restrict__ Pst,
+             const float* __restrict__ Ui, const float* __restrict__ gami,
+             const float* h0, float* __restrict__ o, float* hT, float* __restrict__ Sst,
+             int BH, int T, int H, int NC)
+{
+    constexpr int BV = 32, NS = DV / BV, NW = NTHR_S / 64;
+    constexpr int TS = (DK / 16) * (BV / 16), MS = TS / NW;
+    static_assert(C == 64 && (DK == 128 || DK == 64), "chunk 64, 64 or 128 key channels");
+    static_assert((C / 16) * (BV / 16) == NW && TS % NW == 0, "one D tile and whole state tiles per wave");
+    using SK = SwzF<DK / 4>;  // rows of DK floats
+    using SC = SwzF<C / 4>;   // rows of C floats
+    constexpr int UK = DK / 4, UC = C / 4, UB = BV / 4;
+    // LDS in 16-byte units.  group 1: W [C][DK], Qg [C][DK], the U slice [C][BV]
+    constexpr int OW = 0, OQ = OW + C * UK, OU = OQ + C * UK, G1 = OU + C * UB;
+    // group 2: P [C][C], Kh^T [DK][C], the decay (one wave of words, repeats above DK)
+    constexpr int OP = G1, OK = OP + C * UC, OG = OK + DK * UC, NTAB = OG + 64;
+    constexpr int NQK = C * UK / NTHR_S, NQC = DK * UC / NTHR_S, NQP = C * UC / NTHR_S;
+    static_assert(C * UK % NTHR_S == 0 && C * UC % NTHR_S == 0 && C * UB == NTHR_S,
+                  "every direct-load instruction lies in one table");
+    static_assert(DK / 4 <= 64, "decay in one wave of words");
+    __shared__ __align__(16) f32x4 tab[NTAB];
+    __shared__ __align__(16) f32x4 sSt[BV * UK], sDt[BV * UC];
+    float* const St = reinterpret_cast<float*>(sSt);
+    float* const Dt = reinterpret_cast<float*>(sDt);
+
+    const int x = blockIdx.x;
+    const int grp = x / (8 * NS), rem = x % (8 * NS);
+    const int sl = rem / 8, bh = grp * 8 + rem % 8;
+    if (bh >= BH) return;
+    const int b = bh / H, h = bh % H;
+    const int v0 = sl * BV;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+    // this wave's D tile (rows of D^T tj, columns ti) and state tiles (sj = tj, si)
+    const int tj = w & 1, ti = w >> 1;
+
+    // slot tid + NTHR_S q of a table takes the table's unit (row, u ^ f(row))
+    int gk[NQK], gc[NQC];
+#pragma unroll
+    for (int q = 0; q < NQK; ++q) {
+        const int s = q * NTHR_S + tid, row = s / UK, u = s % UK;
+        gk[q] = (row * UK + (u ^ SK::f(row))) * 4;
+    }
+#pragma unroll
+    for (int q = 0; q < NQC; ++q) {
+        const int s = q * NTHR_S + tid, row = s / UC, u = s % UC;
+        gc[q] = (row * UC + (u ^ SC::f(row))) * 4;
+    }
+    const int urow = tid / UB, uoff = urow * DV + v0 + 4 * ((tid % UB) ^ (urow & 7));
+    auto fetch1 = [&](int n) {
+        const size_t ch = (size_t)bh * NC + n;
+#pragma unroll
+        for (int q = 0; q < NQK; ++q) {
+            dma16(Wt + ch * C * DK + gk[q], tab + OW + q * NTHR_S + 64 * w);
+            dma16(Qgt + ch * C * DK + gk[q], tab + OQ + q * NTHR_S + 64 * w);
+        }
+        dma16(Ui + ch * C * DV + uoff, tab + OU + 64 * w);
+    };
+    auto fetch2 = [&](int n) {
+        const size_t ch = (size_t)bh * NC + n;
+        if (w == 0) dma16(gami + ch * DK + 4 * (l % (DK / 4)), tab + OG);
+#pragma unroll
+        for (int q = 0; q < NQP; ++q) dma16(Pst + ch * C * C + gc[q], tab + OP + q * NTHR_S + 64 * w);
+#pragma unroll
+        for (int q = 0; q < NQC; ++q) dma16(KhTt + ch * C * DK + gc[q], tab + OK + q * NTHR_S + 64 * w);
+    };
+
+    // state tile m: sacc[m][r] = S[si*16 + lr][v0 + tj*16 + 4 lq + r], si = ti + 4 m
+    f32x4 sacc[MS];
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        const int si = ti + (NW / 2) * m;
+        sacc[m] = zero4();
+        if (h0)
+            sacc[m] = *reinterpret_cast<const f32x4*>(h0 + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + tj * 16 + 4 * lq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) St[swzf_idx<SK>(tj * 16 + 4 * lq + r, si * 16 + lr)] = sacc[m][r];
+    }
+    fetch1(0);
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    constexpr int AFTER2 = SAVE ? MS : 0;  // stores issued after group 2
+    constexpr int AFTER1 = OUT ? 1 : 0;    // stores issued after group 1
+    auto step = [&](int n, auto last_c) {
+        constexpr bool LAST = decltype(last_c)::value;
+        const size_t ch = (size_t)bh * NC + n;
+        fetch2(n);
+        if (SAVE) {
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                const int si = ti + (NW / 2) * m;
+                *reinterpret_cast<f32x4*>(Sst + (ch * DK + si * 16 + lr) * DV + v0 + tj * 16 + 4 * lq) = sacc[m];
+            }
+        }
+        // phase 1: acc[r] = D^T[tj*16 + 4 lq + r][ti*16 + lr] = D[ti*16 + lr][v0 + tj*16 + 4 lq + r]
+        f32x4 ws = zero4(), o1 = zero4();
+#pragma unroll
+        for (int u0 = 0; u0 < UK; u0 += 4) {
+            const f32x4 a = ffrag_rows<SK>(sSt, tj * 16, u0);
+            ws = mma_f32_k16(a, ffrag_rows<SK>(tab + OW, ti * 16, u0), ws);
+            if (OUT) o1 = mma_f32_k16(a, ffrag_rows<SK>(tab + OQ, ti * 16, u0), o1);
+        }
+        {
+            const int ur = ti * 16 + lr;
+            const f32x4 u4 = tab[OU + ur * UB + ((tj * 4 + lq) ^ (ur & 7))];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Dt[swzf_idx<SC>(tj * 16 + 4 * lq + r, ti * 16 + lr)] = u4[r] - ws[r];
+        }
+        wait_vmcnt<AFTER2>();  // P, Kh^T, gam of this chunk have landed
+        __syncthreads();
+        if constexpr (!LAST) fetch1(n + 1);
+        // phase 2: O^T += D^T P^T (P lower triangular: K up to the tile's last row)
+        if (OUT) {
+            for (int u0 = 0; u0 < 4 * (ti + 1); u0 += 4)
+                o1 = mma_f32_k16(ffrag_rows<SC>(sDt, tj * 16, u0), ffrag_rows<SC>(tab + OP, ti * 16, u0), o1);
+            const int t = n * C + ti * 16 + lr;
+            if (!LAST || t < T)
+                *reinterpret_cast<f32x4*>(o + (((size_t)b * T + t) * H + h) * DV + v0 + tj * 16 + 4 * lq) = o1;
+        }
+        // S^T <- S^T o gam + D^T Kh
+        const float* sg = reinterpret_cast<const float*>(tab + OG);
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int si = ti + (NW / 2) * m;
+            const float gk = sg[si * 16 + lr];
+            f32x4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = gk * sacc[m][r];
+#pragma unroll
+            for (int u0 = 0; u0 < UC; u0 += 4)
+                acc = mma_f32_k16(ffrag_rows<SC>(sDt, tj * 16, u0), ffrag_rows<SC>(tab + OK, si * 16, u0), acc);
+            sacc[m] = acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) St[swzf_idx<SK>(tj * 16 + 4 * lq + r, si * 16 + lr)] = acc[r];
+        }
+        if constexpr (!LAST) {
+            wait_vmcnt<AFTER1>();  // W, Qg, U of the next chunk have landed
+            __syncthreads();
+        }
+    };
+    for (int n = 0; n + 1 < NC; ++n) step(n, std::false_type{});
+    step(NC - 1, std::true_type{});
+    if (hT) {
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int si = ti + (NW / 2) * m;
+            *reinterpret_cast<f32x4*>(hT + ((size_t)bh * DK + si * 16 + lr) * DV + v0 + tj * 16 + 4 * lq) = sacc[m];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
 template <typename TIn, int C, int DK, int DV, int MT>
@@ -1616,6 +1796,15 @@ gdn_status run_scan(const Plan& p, const float* h0, void* o, float* hT, char* ws
                        BH, p.T, p.H, p.NC);
         }
         (void)n;
+        return GDN_OK;
+    }
+    if constexpr (f32_tables<TIn, C, DK>()) {
+        dim3 grid((unsigned)(ngrp * 8 * (DV / 32))), block(NTHR_S);
+        GDN_LAUNCH(SAVE ? (OUT ? "scan_train" : "scan_save") : "scan", (scanf_kernel<C, DK, DV, SAVE, OUT>),
+                   grid, block, st, (const float*)(ws + p.o_W), (const float*)(ws + p.o_Qg),
+                   (const float*)(ws + p.o_Kh), (const float*)(ws + p.o_Ps),
+                   (const float*)(ws + p.o_U), (const float*)(ws + p.o_gam), h0, (float*)o, hT,
+                   SAVE ? (float*)(ws + p.o_Sst) : nullptr, BH, p.T, p.H, p.NC);
         return GDN_OK;
     }
     dim3 grid((unsigned)(ngrp * 8 * SC::NS)), block(NTHR);

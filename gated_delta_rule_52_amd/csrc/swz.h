@@ -121,4 +121,64 @@ __device__ __forceinline__ bf16x8 frag_cols_kperm(const void* tab, int k0, int m
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// ---------------------------------------------------------------------------
+// fp32 tables: rows of U 16-byte units (4 floats each), U a multiple of 16,
+// unit u of row r at slot r * U + (u ^ f(r)), f(r) = 2 h(r) with
+//   h = (bit0 of r) | (bit1 ^ bit2 of r) << 1 | (bit3 of r) << 2.
+// Two reads are free of bank conflicts on it (v_mfma_f32_16x16x4_f32 operands,
+// r0, k0, c0 multiples of 16, u0 of 4):
+//  * 16-byte row fragments: lane (m, g) = (l % 16, l / 16) reads unit u0 + g of
+//    row r0 + m.  f leaves bit 0 alone, so the two lane groups of a 16-byte
+//    read phase differ in it; inside a group the eight rows of the phase give
+//    eight different h.
+//  * 4-byte column reads: lane (m, g) reads row k0 + 4 g + e, column c0 + m.
+//    Bit 1 of f permutes the four units of a 16-column block, bits 2 and 3
+//    move the block by g: the 64 lanes hit 64 different banks.
+// The 4-byte writes of accumulator tiles (lane (m, g) writing row x + 4 g + r,
+// column y + m) are the column pattern and free of conflicts too.
+template <int U_>
+struct SwzF {
+    static constexpr int U = U_;
+    static_assert(U % 16 == 0, "bank groups repeat every 16 units");
+    __device__ static int f(int r) { return 2 * ((r & 1) | (((r >> 1) ^ (r >> 2)) & 1) << 1 | ((r >> 3) & 1) << 2); }
+};
+
+// index (in floats) of column c of row r
+template <class S>
+__device__ __forceinline__ int swzf_idx(int r, int c)
+{
+    return swz_slot<S>(r, c >> 2) * 4 + (c & 3);
+}
+
+// K-contiguous operand: lane (m, g) receives unit u0 + g of row r0 + m, its
+// element e being the operand's K index 4 (u0 + g) + e of MFMA e
+template <class S>
+__device__ __forceinline__ f32x4 ffrag_rows(const void* tab, int r0, int u0)
+{
+    const int l = lane_id();
+    return reinterpret_cast<const f32x4*>(tab)[swz_slot<S>(r0 + (l & 15), u0 + (l >> 4))];
+}
+
+// Operand with K down the rows: lane (m, g) receives X(k0 + 4 g + e, c0 + m)
+// as element e, matching the K order of ffrag_rows over the same 16-block
+template <class S>
+__device__ __forceinline__ f32x4 ffrag_cols(const void* tab, int k0, int c0)
+{
+    const int l = lane_id(), m = l & 15, g = l >> 4;
+    const float* t = reinterpret_cast<const float*>(tab);
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = t[swzf_idx<S>(k0 + 4 * g + e, c0 + m)];
+    return v;
+}
+
+// acc += A B over one 16-long K block given as the four fp32 MFMAs of two
+// matching fragments
+__device__ __forceinline__ f32x4 mma_f32_k16(f32x4 a, f32x4 b, f32x4 acc)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma_f32_16x16x4(a[e], b[e], acc);
+    return acc;
+}
+
 }  // namespace gdn
