@@ -767,6 +767,214 @@ bchunk1_kernel(const TIn* __restrict__ v, const float* __restrict__ beta,
 
 
 // ---------------------------------------------------------------------------
+// bchunk1f: the chunk-local contractions of the backward over fp32 operands
+// (fp32 inputs, chunk 64) on v_mfma_f32_16x16x4_f32, one workgroup of 8 waves
+// per chunk-head, streaming Dv in 64-column slices through LDS (S, dS, dO,
+// dD, v and the recomputed D, rows on the fp32 swizzle).  Per slice:
+//   1: D^T = U^T - S^T W^T and dX_V^T = dD^T T (dv = beta dX_V, dbeta through U)
+//   2: dQg^T += S dO^T, dW^T += S dD^T, dKh^T += dS D^T, dPs^T += D dO^T,
+//      dT1^T += v dD^T (times beta of the key row at the end), dgam += dS o S
+// Every product is computed transposed, so that each result leaves as
+// 16-byte rows of the [C][*] outputs; its A operands are rows of the [*][Dv]
+// slice tables and its B operands rows of the [C][Dv] ones, both read along
+// Dv (the contraction index).  Phase 1 reads S, dD and T down their columns
+// instead; the W rows of a wave's 16 tokens are held in registers for the
+// whole chunk-head.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ void __launch_bounds__(512)
+bchunk1f_kernel(const float* __restrict__ v, const float* __restrict__ beta,
+                const float* __restrict__ dO, const float* __restrict__ Wi,
+                const float* __restrict__ Ui, const float* __restrict__ Tmi,
+                const float* __restrict__ Sst, const float* __restrict__ dSt,
+                const float* __restrict__ dDt, float* __restrict__ dvo, float* __restrict__ dQgo,
+                float* __restrict__ dWgo, float* __restrict__ dKho, float* __restrict__ dPso,
+                float* __restrict__ dT1o, float* __restrict__ dgmo, float* __restrict__ dbpo, int T,
+                int H, int NC)
+{
+    constexpr int C = 64, BW = 64, NT = 512, NSL = DV / BW;
+    constexpr int NI = DK / 16, MI = NI / 2;  // key-channel tiles, per wave
+    static_assert(DK == 128 || DK == 64, "64 or 128 key channels");
+    static_assert(DV % BW == 0, "whole 64-column slices");
+    using SF = SwzF<BW / 4>;  // every slice table: rows of 64 floats
+    constexpr int UW = BW / 4;
+    __shared__ __align__(16) f32x4 sS[DK * UW], sdS[DK * UW], sdO[C * UW], sdD[C * UW], sD[C * UW], sv[C * UW];
+    __shared__ __align__(16) f32x4 sT[C * (C / 4)];  // T [C][C], the same row swizzle
+    __shared__ float sred[2][C];
+
+    const int ch = blockIdx.x;
+    const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
+    const int t0 = n * C;
+    const int nvalid = min(C, T - t0);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+    const size_t tok0 = ((size_t)b * T + t0) * H + h;  // token index of row 0
+    // this wave: tokens ti*16.. (the B side), key-channel tiles ih*MI.., key
+    // rows sh*32.. (dPs, dT1), and in phase 1 the slice's column tiles jh, jh + 2
+    const int ti = w & 3, ih = w >> 2, sh = w >> 2, jh = w >> 2;
+    const int tr = ti * 16 + lr;  // this lane's token row on the B side
+
+    // W rows of this wave's tokens: wf[kb][e] = W[tr][16 kb + 4 lq + e]
+    f32x4 wf[NI];
+    {
+        const float* Wp = Wi + ((size_t)ch * C + tr) * DK + 4 * lq;
+#pragma unroll
+        for (int kb = 0; kb < NI; ++kb) wf[kb] = *reinterpret_cast<const f32x4*>(Wp + 16 * kb);
+    }
+    const float btr = tr < nvalid ? beta[tok0 + (size_t)tr * H] : 0.f;
+    // T: loaded with the first slice
+#pragma unroll
+    for (int q = 0; q < C * (C / 4) / NT; ++q) {
+        const int s = q * NT + tid, row = s / (C / 4), u = (s % (C / 4)) ^ SF::f(row);
+        dma16(Tmi + ((size_t)ch * C + row) * C + 4 * u, sT + q * NT + 64 * w);
+    }
+
+    // slice loads: slot q * NT + tid of a table takes unit (row, u ^ f(row))
+    auto fetch = [&](int v0) {
+#pragma unroll
+        for (int q = 0; q < DK * UW / NT; ++q) {
+            const int s = q * NT + tid, row = s / UW, u = (s % UW) ^ SF::f(row);
+            const size_t go = ((size_t)ch * DK + row) * DV + v0 + 4 * u;
+            dma16(Sst + go, sS + q * NT + 64 * w);
+            dma16(dSt + go, sdS + q * NT + 64 * w);
+        }
+#pragma unroll
+        for (int q = 0; q < C * UW / NT; ++q) {
+            const int s = q * NT + tid, row = s / UW, u = (s % UW) ^ SF::f(row);
+            const int rc = min(row, nvalid - 1);  // rows past the end: zeroed after the wait
+            const size_t tk = (tok0 + (size_t)rc * H) * DV + v0 + 4 * u;
+            dma16(dO + tk, sdO + q * NT + 64 * w);
+            dma16(v + tk, sv + q * NT + 64 * w);
+            dma16(dDt + ((size_t)ch * C + row) * DV + v0 + 4 * u, sdD + q * NT + 64 * w);
+        }
+    };
+
+    f32x4 aQ[MI], aW[MI], aK[MI], aP[2], aT[2];
+#pragma unroll
+    for (int m = 0; m < MI; ++m) aQ[m] = aW[m] = aK[m] = zero4();
+    aP[0] = aP[1] = aT[0] = aT[1] = zero4();
+    float dbp = 0.f;
+    // dgam: TPR threads per key-channel row, UPT units of the slice each
+    f32x4 dgm = zero4();
+    constexpr int TPR = NT / DK, UPT = UW / TPR;
+    const int grow = tid / TPR, gu0 = (tid % TPR) * UPT;
+
+    fetch(0);
+    for (int sl = 0; sl < NSL; ++sl) {
+        const int v0 = sl * BW;
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (nvalid < C) {  // zero dO and v past the sequence end (its last chunk only)
+            for (int idx = tid; idx < (C - nvalid) * UW; idx += NT) {
+                const int row = nvalid + idx / UW, u = idx % UW;
+                sdO[row * UW + u] = zero4();
+                sv[row * UW + u] = zero4();
+            }
+            __syncthreads();
+        }
+        // phase 1: D^T, dX_V^T for column tiles jh, jh + 2 (acc[r] at column
+        // jt*16 + 4 lq + r of the slice, token tr)
+#pragma unroll
+        for (int jm = 0; jm < 2; ++jm) {
+            const int jt = jh + 2 * jm;
+            f32x4 ws = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NI; ++kb) ws = mma_f32_k16(ffrag_cols<SF>(sS, 16 * kb, jt * 16), wf[kb], ws);
+            const f32x4 u4 = *reinterpret_cast<const f32x4*>(Ui + ((size_t)ch * C + tr) * DV + v0 + jt * 16 + 4 * lq);
+            f32x4 d;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) d[r] = u4[r] - ws[r];
+            sD[swz_slot<SF>(tr, jt * 4 + lq)] = d;
+            f32x4 dx = zero4();
+            // T lower triangular: T[s][t] = 0 for s < t
+            for (int kb = ti; kb < C / 16; ++kb)
+                dx = mma_f32_k16(ffrag_cols<SF>(sdD, 16 * kb, jt * 16), ffrag_cols<SF>(sT, 16 * kb, ti * 16), dx);
+            const f32x4 vv = sv[swz_slot<SF>(tr, jt * 4 + lq)];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dbp += dx[r] * vv[r];
+            if (tr < nvalid) {
+                f32x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = btr * dx[r];
+                *reinterpret_cast<f32x4*>(dvo + (tok0 + (size_t)tr * H) * DV + v0 + jt * 16 + 4 * lq) = o;
+            }
+        }
+        // dgam partial: sum over this thread's units of its row of dS o S
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+            const f32x4 a = sS[swz_slot<SF>(grow, gu0 + u)], c = sdS[swz_slot<SF>(grow, gu0 + u)];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dgm[r] += a[r] * c[r];
+        }
+        __syncthreads();
+        // phase 2: the contractions over the slice's Dv columns
+#pragma unroll 1
+        for (int kb = 0; kb < UW / 4; ++kb) {
+            const int u0 = 4 * kb;
+            const f32x4 bO = ffrag_rows<SF>(sdO, ti * 16, u0), bD = ffrag_rows<SF>(sdD, ti * 16, u0),
+                        bX = ffrag_rows<SF>(sD, ti * 16, u0);
+#pragma unroll
+            for (int m = 0; m < MI; ++m) {
+                const int i0 = (ih * MI + m) * 16;
+                const f32x4 aS = ffrag_rows<SF>(sS, i0, u0), adS = ffrag_rows<SF>(sdS, i0, u0);
+                aQ[m] = mma_f32_k16(aS, bO, aQ[m]);
+                aW[m] = mma_f32_k16(aS, bD, aW[m]);
+                aK[m] = mma_f32_k16(adS, bX, aK[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int s0 = sh * 32 + 16 * m;
+                aP[m] = mma_f32_k16(ffrag_rows<SF>(sD, s0, u0), bO, aP[m]);
+                aT[m] = mma_f32_k16(ffrag_rows<SF>(sv, s0, u0), bD, aT[m]);
+            }
+        }
+        if (sl + 1 < NSL) {
+            __syncthreads();
+            fetch(v0 + BW);
+        }
+    }
+
+    // outputs: lane values are 16-byte pieces of row tr
+    {
+        const size_t rk = ((size_t)ch * C + tr) * DK + 4 * lq;
+#pragma unroll
+        for (int m = 0; m < MI; ++m) {
+            const int i0 = (ih * MI + m) * 16;
+            *reinterpret_cast<f32x4*>(dQgo + rk + i0) = aQ[m];
+            *reinterpret_cast<f32x4*>(dWgo + rk + i0) = -aW[m];
+            *reinterpret_cast<f32x4*>(dKho + rk + i0) = aK[m];
+        }
+        const size_t rc = ((size_t)ch * C + tr) * C + 4 * lq;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int s0 = sh * 32 + 16 * m;
+            // dT1 = dD (beta v)^T: beta of the key rows s0 + 4 lq + r
+            f32x4 bk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int sr = s0 + 4 * lq + r;
+                bk[r] = sr < nvalid ? beta[tok0 + (size_t)sr * H] : 0.f;
+            }
+            *reinterpret_cast<f32x4*>(dPso + rc + s0) = aP[m];
+            *reinterpret_cast<f32x4*>(dT1o + rc + s0) = aT[m] * bk;
+        }
+    }
+    // dgam: the TPR threads of a row are neighbouring lanes
+    {
+        float sgm = dgm[0] + dgm[1] + dgm[2] + dgm[3];
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) sgm += __shfl_xor(sgm, o);
+        if (tid % TPR == 0) dgmo[(size_t)ch * DK + grow] = sgm;
+    }
+    // dbeta through U: the four lane groups, then the two waves of a token tile
+    dbp += __shfl_xor(dbp, 16);
+    dbp += __shfl_xor(dbp, 32);
+    if (lq == 0) sred[jh][tr] = dbp;
+    __syncthreads();
+    if (tid < C) dbpo[(size_t)ch * C + tid] = sred[0][tid] + sred[1][tid];
+}
+
+// ---------------------------------------------------------------------------
 // bchunk1 over bf16 tables (bf16 inputs): 8 waves, Dv streamed in 32-column
 // tiles with the next tile prefetched into registers; D comes from the forward
 // (saved by the scan); the five contractions over Dv are single K = 32 bf16
@@ -2496,6 +2704,14 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                    (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh), (float*)(ws + p.o_dPs),
                    (float*)(ws + p.o_dT1), (float*)(ws + p.o_dgm), (float*)(ws + p.o_dbp), p.T, p.H,
                    p.NC, (int)p.n_ch);
+    } else if constexpr (f32_tables<TIn, C, DK>()) {
+        GDN_LAUNCH("bchunk1", (bchunk1f_kernel<DK, DV>), gch, dim3(512), st, (const float*)v, beta,
+                   (const float*)dO, (const float*)(ws + p.o_W), (const float*)(ws + p.o_U),
+                   (const float*)(ws + p.o_Tm), (const float*)(ws + p.o_Sst),
+                   (const float*)(ws + p.o_dSt), (const float*)(ws + p.o_dDt), (float*)dv,
+                   (float*)(ws + p.o_dQg), (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh),
+                   (float*)(ws + p.o_dPs), (float*)(ws + p.o_dT1), (float*)(ws + p.o_dgm),
+                   (float*)(ws + p.o_dbp), p.T, p.H, p.NC);
     } else
     GDN_LAUNCH("bchunk1", (bchunk1_kernel<TIn, C, DK, DV, MT>), gch, dim3(NTHR), st,
                        (const TIn*)v, beta, (const TIn*)dO, (const float*)(ws + p.o_W),
