@@ -933,6 +933,475 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 }
 
 // ---------------------------------------------------------------------------
+// prepf: prep over fp32 tables (fp32 inputs, chunk 64) on
+// v_mfma_f32_16x16x4_f32, with prep2's structure: 8 waves; a column thread
+// owns one key channel of one 16-token part and keeps its q, k and exp(g) in
+// registers; the level tables are fp32 rows with the channel index contiguous
+// on the fp32 row swizzle (one 16-byte LDS read per lane per four MFMAs).  The
+// score tiles, W and U are computed transposed (P^T = Y X^T and so on), so a
+// lane's four values are four consecutive columns of one output row, stored
+// as 16 bytes.  Kh goes out transposed (Kh^T [DK][C]).  exp is the library
+// expf throughout.  With SAFE the stage values P, A, T, U, W pass through
+// guard(); the solve's diagonal is damped by sf.dinv in every instance.
+// ---------------------------------------------------------------------------
+template <int C, int DK, int DV, bool PCH, bool L2N, bool SAFE>
+__global__ void __launch_bounds__(NTHR_P)
+prepf_kernel(const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+             const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int NC,
+             float scale, float* __restrict__ Wo, float* __restrict__ Uo,
+             float* __restrict__ Qgo, float* __restrict__ KhTo, float* __restrict__ Pso,
+             float* __restrict__ gamo, float* __restrict__ Tmo, float* __restrict__ rno, Safety sf)
+{
+    static_assert(C == 64 && DK == DV && (DK == 64 || DK == 128), "prepf: chunk 64, Dk == Dv");
+    constexpr int NW = NTHR_P / 64, RPP = 16, NPART = C / RPP, NB = C / 16;
+    constexpr int PC = C + 4, UK = DK / 4, UC = C / 4;
+    constexpr int NOFF = NB * (NB - 1) / 2;
+    using SK = SwzF<UK>;  // rows of DK floats
+    using SC = SwzF<UC>;  // rows of C floats
+    // level tables (fp32, swizzled); after the level loop the same bytes hold
+    // T and the merge scratch, then X_V^T
+    constexpr int SBUF = cmax(2 * C * DK * 4, cmax(2 * C * PC * 4, DV * C * 4));
+    __shared__ __align__(16) char sbuf[SBUF];
+    __shared__ __align__(16) float sA[C][PC];  // A (beta rows), strictly lower; later T (swizzled)
+    __shared__ __align__(16) f32x4 sXT[DK * UC];  // X_K^T [DK][C]
+    __shared__ float sbeta[C], stot[NPART][DK];
+    __shared__ float sG[C];  // per-head decay: chunk-local inclusive cumsum of g
+    __shared__ float sRn[2][L2N ? C : 1];
+    __shared__ unsigned int sdg[SAFE ? NDIAG_PREP : 1];
+    f32x4* const sX = reinterpret_cast<f32x4*>(sbuf);
+    f32x4* const sY = reinterpret_cast<f32x4*>(sbuf + C * DK * 4);
+    float* const Xf = reinterpret_cast<float*>(sX);
+    float* const Yf = reinterpret_cast<float*>(sY);
+    float (*sT)[PC] = reinterpret_cast<float (*)[PC]>(sbuf);
+    float (*sYt)[PC] = reinterpret_cast<float (*)[PC]>(sbuf + C * PC * 4);
+    f32x4* const sTs = reinterpret_cast<f32x4*>(&sA[0][0]);  // T [C][C] swizzled (SC)
+    static_assert(C * C * 4 <= C * PC * 4, "swizzled T fits the A bytes");
+
+    const int ch = blockIdx.x;
+    const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
+    const int t0 = n * C;
+    const int nvalid = min(C, T - t0);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+    const size_t tok0 = ((size_t)b * T + t0) * H + h;
+    const size_t rsK = (size_t)H * DK;
+    const bool bwdt = Tmo != nullptr;
+    const bool cp = tid < NPART * DK;
+    const int c = tid % DK, part = cp ? tid / DK : 0, p0 = part * RPP;
+    if (SAFE && tid < NDIAG_PREP) sdg[tid] = 0u;
+    auto sd = [&](int stage) -> unsigned int* { return SAFE && sf.diag ? &sdg[2 * stage] : nullptr; };
+    auto grd = [&](float x, int stage) { return SAFE ? guard(x, sf.clip, sd(stage)) : x; };
+    // Y_a X_b^T over the key channels: acc[r] = sum_c Y[a0 + 4 lq + r][c] X[b0 + lr][c]
+    auto kc = [&](f32x4 acc, const f32x4* A, int a0, const f32x4* B, int b0) {
+#pragma unroll
+        for (int u0 = 0; u0 < UK; u0 += 4) acc = mma_f32_k16(ffrag_rows<SK>(A, a0, u0), ffrag_rows<SK>(B, b0, u0), acc);
+        return acc;
+    };
+
+    float a[RPP], qv[RPP], kv[RPP];
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) {
+        const int r = p0 + i;
+        const int rr = min(r, nvalid - 1);
+        const float gx = PCH ? g[(tok0 + (size_t)rr * H) * DK + c] : g[tok0 + (size_t)rr * H];
+        const float qx = q[tok0 * DK + rr * rsK + c];
+        const float kx = k[tok0 * DK + rr * rsK + c];
+        const bool ok = cp && r < nvalid;
+        a[i] = expf(ok ? gx : 0.f);
+        qv[i] = ok ? qx : 0.f;
+        kv[i] = ok ? kx : 0.f;
+    }
+    for (int r = tid; r < C; r += NTHR_P) sbeta[r] = r < nvalid ? beta[tok0 + (size_t)r * H] : 0.f;
+    {
+        float pt = 1.f;
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) pt *= a[i];
+        if (cp) stot[part][c] = pt;
+    }
+    if constexpr (!PCH) {
+        if (w == 0) {  // G_i = g_0 + ... + g_i, inclusive prefix sum across the wave
+            float x = l < nvalid ? g[tok0 + (size_t)min(l, nvalid - 1) * H] : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (l >= off) x += y;
+            }
+            sG[l] = x;
+        }
+    }
+    // level 0: unscaled rows
+    if (cp) {
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            Xf[swzf_idx<SK>(p0 + i, c)] = qv[i];
+            Yf[swzf_idx<SK>(p0 + i, c)] = kv[i];
+        }
+    }
+    __syncthreads();
+    auto row_norms = [&]() {
+        if constexpr (L2N) {
+            const f32x4 nq = kc(zero4(), sX, w * 16, sX, w * 16);
+            const f32x4 nk = kc(zero4(), sY, w * 16, sY, w * 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (4 * lq + r == lr) {
+                    const int i = w * 16 + lr;
+                    const float rq = 1.f / sqrtf(nq[r] + GDN_L2NORM_EPS);
+                    const float rk = 1.f / sqrtf(nk[r] + GDN_L2NORM_EPS);
+                    sRn[0][i] = rq;
+                    sRn[1][i] = rk;
+                    rno[((size_t)ch * 2) * C + i] = rq;
+                    rno[((size_t)ch * 2 + 1) * C + i] = rk;
+                }
+            }
+        }
+    };
+    auto scale_rows = [&]() {
+        if constexpr (L2N) {
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                qv[i] *= sRn[0][p0 + i];
+                kv[i] *= sRn[1][p0 + i];
+            }
+        }
+    };
+    // score tiles, transposed: acc[r] = P[ti*16 + lr][tj*16 + 4 lq + r] (and A)
+    f32x4 dP = zero4(), dA = zero4();
+    constexpr int OW = NW - NB, MOFF = (NOFF + OW - 1) / OW;
+    f32x4 accP[MOFF], accA[MOFF];
+#pragma unroll
+    for (int m = 0; m < MOFF; ++m) accP[m] = accA[m] = zero4();
+    if constexpr (!PCH) {
+        // per head: plain products times exp(G_i - G_j) (<= 1 for j <= i)
+        if (w < NB) {
+            const f32x4 tp = kc(zero4(), sY, w * 16, sX, w * 16);
+            const f32x4 ta = kc(zero4(), sY, w * 16, sY, w * 16);
+            row_norms();
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = lr, j = 4 * lq + r;
+                const float e = j <= i ? expf(sG[w * 16 + i] - sG[w * 16 + j]) : 0.f;
+                dP[r] = tp[r] * e;
+                dA[r] = j < i ? ta[r] * e : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < MOFF; ++m) {
+                const int idx = (w - NB) + OW * m;
+                if (idx < NOFF) {
+                    int ti, tj;
+                    off_tile(idx, ti, tj);
+                    accP[m] = kc(zero4(), sY, tj * 16, sX, ti * 16);
+                    accA[m] = kc(zero4(), sY, tj * 16, sY, ti * 16);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float e = expf(sG[ti * 16 + lr] - sG[tj * 16 + 4 * lq + r]);
+                        accP[m][r] *= e;
+                        accA[m][r] *= e;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if constexpr (L2N) {
+            if (w < NB) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = w * 16 + lr, j = w * 16 + 4 * lq + r;
+                    dP[r] *= sRn[0][i] * sRn[1][j];
+                    dA[r] *= sRn[1][i] * sRn[1][j];
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < MOFF; ++m) {
+                    const int idx = (w - NB) + OW * m;
+                    if (idx < NOFF) {
+                        int ti, tj;
+                        off_tile(idx, ti, tj);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int i = ti * 16 + lr, j = tj * 16 + 4 * lq + r;
+                            accP[m][r] *= sRn[0][i] * sRn[1][j];
+                            accA[m][r] *= sRn[1][i] * sRn[1][j];
+                        }
+                    }
+                }
+            }
+            scale_rows();
+        }
+    } else {
+    if (w < NB) {
+        const f32x4 tp = kc(zero4(), sY, w * 16, sX, w * 16);
+        row_norms();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dP[r] = (4 * lq + r == lr) ? tp[r] : 0.f;
+    }
+    __syncthreads();
+    if constexpr (L2N) {
+        if (w < NB) {
+            const int i = w * 16 + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dP[r] *= sRn[0][i] * sRn[1][i];
+        }
+    }
+    scale_rows();
+
+#pragma unroll
+    for (int lvl = 0; (C >> (lvl + 1)) >= 1; ++lvl) {
+        const int hl = C >> (lvl + 1);
+        float F[RPP];
+        if (hl >= RPP) {
+            const int base = (p0 / (2 * hl)) * (2 * hl);
+            if (p0 >= base + hl) {
+                float pre = 1.f;
+                for (int pp = (base + hl) / RPP; pp < part; ++pp) pre *= stot[pp][c];
+                float Fr = pre;
+#pragma unroll
+                for (int i = 0; i < RPP; ++i) {
+                    Fr *= a[i];
+                    F[i] = Fr;
+                }
+            } else {
+                float suf = 1.f;
+                for (int pp = part + 1; pp < (base + hl) / RPP; ++pp) suf *= stot[pp][c];
+                float Fr = suf;
+#pragma unroll
+                for (int i = RPP - 1; i >= 0; --i) {
+                    F[i] = Fr;
+                    Fr *= a[i];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u0 = 0; u0 < RPP; u0 += (hl < RPP ? hl : RPP)) {
+                if (((p0 + u0) / hl) & 1) {
+                    float Fr = 1.f;
+#pragma unroll
+                    for (int i = 0; i < hl; ++i) {
+                        Fr *= a[u0 + i];
+                        F[u0 + i] = Fr;
+                    }
+                } else {
+                    float Fr = 1.f;
+#pragma unroll
+                    for (int i = hl - 1; i >= 0; --i) {
+                        F[u0 + i] = Fr;
+                        Fr *= a[u0 + i];
+                    }
+                }
+            }
+        }
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < RPP; ++i) {
+                Xf[swzf_idx<SK>(p0 + i, c)] = qv[i] * F[i];
+                Yf[swzf_idx<SK>(p0 + i, c)] = kv[i] * F[i];
+            }
+        }
+        __syncthreads();
+        if (hl >= 16) {
+            if (w >= NB) {
+#pragma unroll
+                for (int m = 0; m < MOFF; ++m) {
+                    const int idx = (w - NB) + OW * m;
+                    if (idx < NOFF) {
+                        int ti, tj;
+                        off_tile(idx, ti, tj);
+                        if (off_tile_level(ti, tj) == hl) {
+                            accP[m] = kc(accP[m], sY, tj * 16, sX, ti * 16);
+                            accA[m] = kc(accA[m], sY, tj * 16, sY, ti * 16);
+                        }
+                    }
+                }
+            }
+        } else if (w < NB) {
+            const f32x4 tp = kc(zero4(), sY, w * 16, sX, w * 16);
+            const f32x4 ta = kc(zero4(), sY, w * 16, sY, w * 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (in_level(lr, 4 * lq + r, hl)) {
+                    dP[r] += tp[r];
+                    dA[r] += ta[r];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    }  // per-channel decay
+
+    // v rows for U at the end (clamped past the end, zeroed through beta = 0)
+    constexpr int NV4 = C * DV / 4, QV = NV4 / NTHR_P;
+    static_assert(QV * NTHR_P == NV4, "whole v words per thread");
+    f32x4 vw[QV];
+#pragma unroll
+    for (int u = 0; u < QV; ++u) {
+        const int idx = tid + NTHR_P * u, r = idx / (DV / 4), j0 = (idx % (DV / 4)) * 4;
+        vw[u] = *reinterpret_cast<const f32x4*>(v + tok0 * DV + (size_t)min(r, nvalid - 1) * H * DV + j0);
+    }
+
+    // ---- scores out: Ps rows (16 bytes a lane), A (x beta) to LDS
+    float* Psc = Pso + (size_t)ch * C * C;
+    if (w >= NB) {
+#pragma unroll
+        for (int m = 0; m < MOFF; ++m) {
+            const int idx = (w - NB) + OW * m;
+            if (idx < NOFF) {
+                int ti, tj;
+                off_tile(idx, ti, tj);
+                const int i = ti * 16 + lr, j0 = tj * 16 + 4 * lq;
+                f32x4 pv, av;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pv[r] = scale * grd(accP[m][r], GDN_DIAG_P);
+                    av[r] = grd(sbeta[i] * accA[m][r], GDN_DIAG_A);
+                }
+                *reinterpret_cast<f32x4*>(&Psc[i * C + j0]) = pv;
+                *reinterpret_cast<f32x4*>(&sA[i][j0]) = av;
+            }
+        }
+    } else {
+        const int i = w * 16 + lr, j0 = w * 16 + 4 * lq;
+        f32x4 pv, av;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = j0 + r;
+            pv[r] = i >= j ? scale * grd(dP[r], GDN_DIAG_P) : 0.f;
+            av[r] = i > j ? grd(sbeta[i] * dA[r], GDN_DIAG_A) : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(&Psc[i * C + j0]) = pv;
+        *reinterpret_cast<f32x4*>(&sA[i][j0]) = av;
+    }
+    for (int idx = tid; idx < C * C / 4; idx += NTHR_P) {  // tiles above the diagonal
+        const int i = idx / (C / 4), j0 = (idx % (C / 4)) * 4;
+        if (i / 16 < j0 / 16) {
+            *reinterpret_cast<f32x4*>(&Psc[i * C + j0]) = zero4();
+            *reinterpret_cast<f32x4*>(&sA[i][j0]) = zero4();
+        }
+    }
+
+    // ---- Gamma, Kh factor, gam: Qg, Kh^T outputs and X_K^T = (beta K o Gamma)^T
+    if (cp) {
+        float pre = 1.f, suf = 1.f;
+        for (int pp = 0; pp < part; ++pp) pre *= stot[pp][c];
+        for (int pp = part + 1; pp < NPART; ++pp) suf *= stot[pp][c];
+        float qg[RPP], kh[RPP], xk[RPP];
+        float Gm = pre;
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) {
+            Gm *= a[i];
+            qg[i] = scale * qv[i] * Gm;
+            xk[i] = sbeta[p0 + i] * kv[i] * Gm;
+        }
+        if (part == NPART - 1) gamo[(size_t)ch * DK + c] = Gm;
+        float kap = suf;
+#pragma unroll
+        for (int i = RPP - 1; i >= 0; --i) {
+            kh[i] = kv[i] * kap;
+            kap *= a[i];
+        }
+        float* Qgc = Qgo + (size_t)ch * C * DK;
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) Qgc[(p0 + i) * DK + c] = qg[i];
+        float* KhTc = KhTo + (size_t)ch * C * DK;
+#pragma unroll
+        for (int i = 0; i < RPP; i += 4) {
+            *reinterpret_cast<f32x4*>(&KhTc[c * C + p0 + i]) = f32x4{kh[i], kh[i + 1], kh[i + 2], kh[i + 3]};
+            sXT[swz_slot<SC>(c, (p0 + i) / 4)] = f32x4{xk[i], xk[i + 1], xk[i + 2], xk[i + 3]};
+        }
+    }
+    __syncthreads();  // the level tables are free: sT takes their bytes
+    for (int idx = tid; idx < C * PC; idx += NTHR_P) (&sT[0][0])[idx] = 0.f;
+    __syncthreads();
+
+    // ---- WY solve: 16x16 diagonal blocks of (I + A)^-1 by forward substitution
+    if (w == 0) {
+        const int bb = lq, j = lr;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float sacc = (i == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) sacc -= sA[bb * 16 + i][bb * 16 + m] * x[m];
+            x[i] = sacc * sf.dinv;  // diagonal (1 + wy_eps)
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sT[bb * 16 + i][bb * 16 + j] = x[i];
+    }
+    __syncthreads();
+    // merge neighbouring diagonal blocks: T21 = -T22 (A21 T11)
+#pragma unroll
+    for (int sz = 16; 2 * sz <= C; sz *= 2) {
+        const int tps = (sz / 16) * (sz / 16);
+        const int ntile = (C / (2 * sz)) * tps;
+        for (int idx = w; idx < ntile; idx += NW) {
+            const int pi = idx / tps, ti = (idx % tps) / (sz / 16), tj = idx % (sz / 16);
+            const int b0 = pi * 2 * sz;
+            f32x4 y = mma16<MT_F32>(zero4(), &sA[b0 + sz + 16 * ti][b0], PC, 1, &sT[b0][b0 + 16 * tj], PC, 1, sz);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sYt[b0 + sz + 16 * ti + 4 * lq + r][b0 + 16 * tj + lr] = y[r];
+        }
+        __syncthreads();
+        for (int idx = w; idx < ntile; idx += NW) {
+            const int pi = idx / tps, ti = (idx % tps) / (sz / 16), tj = idx % (sz / 16);
+            const int b0 = pi * 2 * sz;
+            f32x4 t21 = mma16<MT_F32>(zero4(), &sT[b0 + sz + 16 * ti][b0 + sz], PC, 1, &sYt[b0 + sz][b0 + 16 * tj], PC, 1, sz);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sT[b0 + sz + 16 * ti + 4 * lq + r][b0 + 16 * tj + lr] = -t21[r];
+        }
+        __syncthreads();
+    }
+    // T out (training) and its swizzled copy over sA (no longer needed)
+    for (int idx = tid; idx < C * C / 4; idx += NTHR_P) {
+        const int i = idx / (C / 4), j = (idx % (C / 4)) * 4;
+        f32x4 tv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tv[e] = grd(sT[i][j + e], GDN_DIAG_T);
+        if (bwdt) *reinterpret_cast<f32x4*>(&Tmo[(size_t)ch * C * C + i * C + j]) = tv;
+        sTs[swz_slot<SC>(i, j / 4)] = tv;
+    }
+    __syncthreads();
+    // X_V^T = (beta V)^T into the level-table bytes (free now that T is in sTs)
+    float* const XVf = reinterpret_cast<float*>(sbuf);
+    f32x4* const sXV = reinterpret_cast<f32x4*>(sbuf);
+#pragma unroll
+    for (int u = 0; u < QV; ++u) {
+        const int idx = tid + NTHR_P * u, r = idx / (DV / 4), j0 = (idx % (DV / 4)) * 4;
+        const float bt = sbeta[r];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) XVf[swzf_idx<SC>(j0 + e, r)] = bt * vw[u][e];
+    }
+    // ---- W^T = X_K^T T^T: acc[r] = W[ti*16 + lr][tj*16 + 4 lq + r]
+    constexpr int TW = NB * (DK / 16);
+    float* Wc = Wo + (size_t)ch * C * DK;
+    for (int idx = w; idx < TW; idx += NW) {
+        const int ti = idx / (DK / 16), tj = idx % (DK / 16);
+        f32x4 acc = zero4();
+        for (int u0 = 0; u0 < 4 * (ti + 1); u0 += 4)  // T lower triangular
+            acc = mma_f32_k16(ffrag_rows<SC>(sXT, tj * 16, u0), ffrag_rows<SC>(sTs, ti * 16, u0), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = grd(acc[r], GDN_DIAG_W);
+        *reinterpret_cast<f32x4*>(&Wc[(ti * 16 + lr) * DK + tj * 16 + 4 * lq]) = acc;
+    }
+    __syncthreads();  // X_V^T complete
+    // ---- U^T = X_V^T T^T
+    constexpr int TU = NB * (DV / 16);
+    float* Uc = Uo + (size_t)ch * C * DV;
+    for (int idx = w; idx < TU; idx += NW) {
+        const int ti = idx / (DV / 16), tj = idx % (DV / 16);
+        f32x4 acc = zero4();
+        for (int u0 = 0; u0 < 4 * (ti + 1); u0 += 4)
+            acc = mma_f32_k16(ffrag_rows<SC>(sXV, tj * 16, u0), ffrag_rows<SC>(sTs, ti * 16, u0), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = grd(acc[r], GDN_DIAG_U);
+        *reinterpret_cast<f32x4*>(&Uc[(ti * 16 + lr) * DV + tj * 16 + 4 * lq]) = acc;
+    }
+    if constexpr (SAFE) {
+        __syncthreads();
+        flush_counts(sdg, sf.diag, NDIAG_PREP);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // scan
 // ---------------------------------------------------------------------------
 template <int DV>
@@ -1751,6 +2220,21 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
                                      decltype(safe)::value>),
                        grid, dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g,
                        beta, p.T, p.H, p.NC, p.scale, Wb, U, Qb, Kb, Pb, gam, Tm, rn, sf, Wro, Uro);
+            return GDN_OK;
+        };
+        return with_bool(p.decay == GDN_DECAY_PER_CHANNEL, [&](auto pch) {
+            return with_bool(p.l2n, [&](auto l2n) {
+                return with_bool(sf.on(), [&](auto safe) { return launch(pch, l2n, safe); });
+            });
+        });
+    }
+    if constexpr (f32_tables<TIn, C, DK>()) {
+        auto launch = [&](auto pch, auto l2n, auto safe) {
+            GDN_LAUNCH(want_T ? "prep_T" : "prep",
+                       (prepf_kernel<C, DK, DV, decltype(pch)::value, decltype(l2n)::value,
+                                     decltype(safe)::value>),
+                       grid, dim3(NTHR_P), st, (const float*)q, (const float*)k, (const float*)v, g,
+                       beta, p.T, p.H, p.NC, p.scale, W, U, Qg, Kh, Ps, gam, Tm, rn, sf);
             return GDN_OK;
         };
         return with_bool(p.decay == GDN_DECAY_PER_CHANNEL, [&](auto pch) {
