@@ -770,22 +770,22 @@ bchunk1_kernel(const TIn* __restrict__ v, const float* __restrict__ beta,
 // bchunk1f: the chunk-local contractions of the backward over fp32 operands
 // (fp32 inputs, chunk 64) on v_mfma_f32_16x16x4_f32, one workgroup of 8 waves
 // per chunk-head, streaming Dv in 64-column slices through LDS (S, dS, dO,
-// dD, v and the recomputed D, rows on the fp32 swizzle).  Per slice:
-//   1: D^T = U^T - S^T W^T and dX_V^T = dD^T T (dv = beta dX_V, dbeta through U)
+// dD, v and the chunk deltas D saved by the forward scan, rows on the fp32
+// swizzle).  Per slice:
+//   1: dX_V^T = dD^T T (dv = beta dX_V, dbeta through U)
 //   2: dQg^T += S dO^T, dW^T += S dD^T, dKh^T += dS D^T, dPs^T += D dO^T,
 //      dT1^T += v dD^T (times beta of the key row at the end), dgam += dS o S
 // Every product is computed transposed, so that each result leaves as
 // 16-byte rows of the [C][*] outputs; its A operands are rows of the [*][Dv]
 // slice tables and its B operands rows of the [C][Dv] ones, both read along
-// Dv (the contraction index).  Phase 1 reads S, dD and T down their columns
-// instead; the W rows of a wave's 16 tokens are held in registers for the
-// whole chunk-head.
+// Dv (the contraction index).  Phase 1 reads dD and T down their columns
+// instead.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 __global__ void __launch_bounds__(512)
 bchunk1f_kernel(const float* __restrict__ v, const float* __restrict__ beta,
-                const float* __restrict__ dO, const float* __restrict__ Wi,
-                const float* __restrict__ Ui, const float* __restrict__ Tmi,
+                const float* __restrict__ dO, const float* __restrict__ Dsti,
+                const float* __restrict__ Tmi,
                 const float* __restrict__ Sst, const float* __restrict__ dSt,
                 const float* __restrict__ dDt, float* __restrict__ dvo, float* __restrict__ dQgo,
                 float* __restrict__ dWgo, float* __restrict__ dKho, float* __restrict__ dPso,
@@ -814,13 +814,6 @@ bchunk1f_kernel(const float* __restrict__ v, const float* __restrict__ beta,
     const int ti = w & 3, ih = w >> 2, sh = w >> 2, jh = w >> 2;
     const int tr = ti * 16 + lr;  // this lane's token row on the B side
 
-    // W rows of this wave's tokens: wf[kb][e] = W[tr][16 kb + 4 lq + e]
-    f32x4 wf[NI];
-    {
-        const float* Wp = Wi + ((size_t)ch * C + tr) * DK + 4 * lq;
-#pragma unroll
-        for (int kb = 0; kb < NI; ++kb) wf[kb] = *reinterpret_cast<const f32x4*>(Wp + 16 * kb);
-    }
     const float btr = tr < nvalid ? beta[tok0 + (size_t)tr * H] : 0.f;
     // T: loaded with the first slice
 #pragma unroll
@@ -846,6 +839,7 @@ bchunk1f_kernel(const float* __restrict__ v, const float* __restrict__ beta,
             dma16(dO + tk, sdO + q * NT + 64 * w);
             dma16(v + tk, sv + q * NT + 64 * w);
             dma16(dDt + ((size_t)ch * C + row) * DV + v0 + 4 * u, sdD + q * NT + 64 * w);
+            dma16(Dsti + ((size_t)ch * C + row) * DV + v0 + 4 * u, sD + q * NT + 64 * w);
         }
     };
 
@@ -872,19 +866,11 @@ bchunk1f_kernel(const float* __restrict__ v, const float* __restrict__ beta,
             }
             __syncthreads();
         }
-        // phase 1: D^T, dX_V^T for column tiles jh, jh + 2 (acc[r] at column
+        // phase 1: dX_V^T for column tiles jh, jh + 2 (acc[r] at column
         // jt*16 + 4 lq + r of the slice, token tr)
 #pragma unroll
         for (int jm = 0; jm < 2; ++jm) {
             const int jt = jh + 2 * jm;
-            f32x4 ws = zero4();
-#pragma unroll
-            for (int kb = 0; kb < NI; ++kb) ws = mma_f32_k16(ffrag_cols<SF>(sS, 16 * kb, jt * 16), wf[kb], ws);
-            const f32x4 u4 = *reinterpret_cast<const f32x4*>(Ui + ((size_t)ch * C + tr) * DV + v0 + jt * 16 + 4 * lq);
-            f32x4 d;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) d[r] = u4[r] - ws[r];
-            sD[swz_slot<SF>(tr, jt * 4 + lq)] = d;
             f32x4 dx = zero4();
             // T lower triangular: T[s][t] = 0 for s < t
             for (int kb = ti; kb < C / 16; ++kb)
@@ -2706,7 +2692,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                    p.NC, (int)p.n_ch);
     } else if constexpr (f32_tables<TIn, C, DK>()) {
         GDN_LAUNCH("bchunk1", (bchunk1f_kernel<DK, DV>), gch, dim3(512), st, (const float*)v, beta,
-                   (const float*)dO, (const float*)(ws + p.o_W), (const float*)(ws + p.o_U),
+                   (const float*)dO, (const float*)(ws + p.o_Dst),
                    (const float*)(ws + p.o_Tm), (const float*)(ws + p.o_Sst),
                    (const float*)(ws + p.o_dSt), (const float*)(ws + p.o_dDt), (float*)dv,
                    (float*)(ws + p.o_dQg), (float*)(ws + p.o_dWg), (float*)(ws + p.o_dKh),

@@ -2032,7 +2032,8 @@ scan3_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
 // The tables are loaded straight into LDS by direct loads, each group while
 // the other phase runs: P, Kh^T and gam of this chunk during phase 1, W, Qg and
 // U of the next chunk during phase 2 (fp32 tables of two chunks do not fit the
-// LDS together).  The waits count the stores issued after each group.
+// LDS together).  The waits count the stores issued after each group.  The
+// state-saving instances also store each chunk's start state and its D.
 // ---------------------------------------------------------------------------
 template <int C, int DK, int DV, bool SAVE, bool OUT>
 __global__ void __launch_bounds__(NTHR_S)
@@ -2040,7 +2041,7 @@ scanf_kernel(const float* __restrict__ Wt, const float* __restrict__ Qgt,
              const float* __restrict__ KhTt, const float* __restrict__ Pst,
              const float* __restrict__ Ui, const float* __restrict__ gami,
              const float* h0, float* __restrict__ o, float* hT, float* __restrict__ Sst,
-             int BH, int T, int H, int NC)
+             float* __restrict__ Dst, int BH, int T, int H, int NC)
 {
     constexpr int BV = 32, NS = DV / BV, NW = NTHR_S / 64;
     constexpr int TS = (DK / 16) * (BV / 16), MS = TS / NW;
@@ -2119,7 +2120,7 @@ scanf_kernel(const float* __restrict__ Wt, const float* __restrict__ Qgt,
     wait_vmcnt<0>();
     __syncthreads();
 
-    constexpr int AFTER2 = SAVE ? MS : 0;  // stores issued after group 2
+    constexpr int AFTER2 = SAVE ? MS + 1 : 0;  // stores issued after group 2 (S, D)
     constexpr int AFTER1 = OUT ? 1 : 0;    // stores issued after group 1
     auto step = [&](int n, auto last_c) {
         constexpr bool LAST = decltype(last_c)::value;
@@ -2143,8 +2144,13 @@ scanf_kernel(const float* __restrict__ Wt, const float* __restrict__ Qgt,
         {
             const int ur = ti * 16 + lr;
             const f32x4 u4 = tab[OU + ur * UB + ((tj * 4 + lq) ^ (ur & 7))];
+            f32x4 d;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Dt[swzf_idx<SC>(tj * 16 + 4 * lq + r, ti * 16 + lr)] = u4[r] - ws[r];
+            for (int r = 0; r < 4; ++r) {
+                d[r] = u4[r] - ws[r];
+                Dt[swzf_idx<SC>(tj * 16 + 4 * lq + r, ti * 16 + lr)] = d[r];
+            }
+            if (SAVE) *reinterpret_cast<f32x4*>(Dst + (ch * C + ur) * DV + v0 + tj * 16 + 4 * lq) = d;
         }
         wait_vmcnt<AFTER2>();  // P, Kh^T, gam of this chunk have landed
         __syncthreads();
@@ -2288,7 +2294,8 @@ gdn_status run_scan(const Plan& p, const float* h0, void* o, float* hT, char* ws
                    grid, block, st, (const float*)(ws + p.o_W), (const float*)(ws + p.o_Qg),
                    (const float*)(ws + p.o_Kh), (const float*)(ws + p.o_Ps),
                    (const float*)(ws + p.o_U), (const float*)(ws + p.o_gam), h0, (float*)o, hT,
-                   SAVE ? (float*)(ws + p.o_Sst) : nullptr, BH, p.T, p.H, p.NC);
+                   SAVE ? (float*)(ws + p.o_Sst) : nullptr, SAVE ? (float*)(ws + p.o_Dst) : nullptr,
+                   BH, p.T, p.H, p.NC);
         return GDN_OK;
     }
     dim3 grid((unsigned)(ngrp * 8 * SC::NS)), block(NTHR);

@@ -21,7 +21,8 @@
 //   dQg [ch][C][Dk]   dL/dQg,  dWg [ch][C][Dk] dL/dW,  dKh [ch][C][Dk] dL/dKh
 //   dPs [ch][C][C]    dL/dPs,  dT1 [ch][C][C]  dL/dT through U
 //   dgm [ch][Dk]      dL/dgam, dbp [ch][C]     part of dL/dbeta (through U)
-//   Dst [ch][C][Dv]   the chunk deltas D (bf16; bf16 inputs at chunk 64 only)
+//   Dst [ch][C][Dv]   the chunk deltas D, saved by the state-saving forward scan
+//                     at chunk 64 (bf16 with bf16 inputs, fp32 with fp32 inputs)
 //   dbq [ch][2][C]    per channel-half partial dbeta, dgq [ch][2][C] partial
 //                     per-head dg (bf16 inputs at chunk 64)
 //   Ur  [ch][C][Dv], Wr [ch][C][Dk] (bf16): with clip, the products T X_V and
@@ -100,7 +101,7 @@ inline Plan make_plan(const gdn_shape& s, float scale)
     p.o_dT1 = off; off = align256(off + n * C * C * f);
     p.o_dgm = off; off = align256(off + n * Dk * f);
     p.o_dbp = off; off = align256(off + n * C * f);
-    p.o_Dst = off; off = align256(off + n * C * Dv * 2);
+    p.o_Dst = off; off = align256(off + n * C * Dv * (s.dtype == GDN_F32 ? 4 : 2));
     p.o_dbq = off; off = align256(off + n * 2 * C * f);
     p.o_dgq = off; off = align256(off + n * 2 * C * f);
     const bool raw = s.clip > 0.f;
