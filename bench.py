@@ -93,7 +93,9 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True, l2n=False)
     n = B * H * NC
     f4 = 4
     bt = in_bytes == 2 and C == 64 and DK >= 64  # bf16 chunk tables and intermediates
+    ft = in_bytes == 4 and C == 64 and DK >= 64  # fp32 chunk tables of the fp32-operand kernels
     tb = 2 if bt else 4                          # bytes per table element
+    db = 2 if bt else 4 if ft else 0             # bytes per saved chunk delta D
     ib = in_bytes
     cd, cv, cc, kv = C * DK, C * DV, C * C, DK * DV
     tri = C * (C + 1) // 2                       # lower triangle incl. diagonal
@@ -113,12 +115,12 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True, l2n=False)
         by = 3 * cd * tb + cc * tb + cv * f4 + DK * f4             # W Qg Kh Ps, U, gam
         if name == "scan_save":                                    # deltas and states only
             by -= cd * tb + cc * tb
-            by += kv * tb
+            by += kv * tb + cv * db
             fl[mt] += 4 * C * DK * DV
         else:
             by += cv * ib                                          # o
             if name == "scan_train":
-                by += kv * tb + (cv * 2 if bt else 0)              # chunk-start states, D
+                by += kv * tb + cv * db                            # chunk-start states, D
             fl[mt] += 6 * C * DK * DV + 2 * tri * DV
     elif name == "bscan":
         by = cc * tb + 3 * cd * tb + DK * f4 + cv * ib             # Ps Kh^T Qg W, gam, dO
@@ -127,13 +129,13 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True, l2n=False)
     elif name == "bchunk1":
         it = 2 if bt else 4
         by = 2 * cv * ib + C * f4 + cc * f4 + 2 * kv * tb + cv * tb   # v dO, beta, T, S, dS, dD
-        by += (cv * 2 + cv * f4 + cd * tb) if bt else (cd + cv) * f4  # D, U, W | W, U (D = U - W S)
+        by += (cv * 2 + cv * f4 + cd * tb) if bt else cv * f4 if ft else (cd + cv) * f4  # D, U, W | D | W, U
         by += cv * ib + 3 * cd * it + 2 * cc * it + DK * f4 + C * f4  # dv, dQg dX_K|dW dKh, dPs dA|dT1, dgam, dbeta
         fl[mt] += 6 * C * DK * DV + 2 * tri * DV + 2 * C * C * DV     # dQg dW dKh, dPs, dX_V U^T | dD X_V^T
         fl["f32"] += 2 * tri * DV                                      # dX_V = T^T dD
         if bt:   # keys' WY adjoint: dX_K = T^T dW, dA = -(G1 + dX_K W^T) strictly lower
             fl["bf16"] += 2 * tri * DK + 2 * (C * (C - 1) // 2) * DK
-        else:
+        elif not ft:
             fl[mt] += 2 * C * DK * DV                                  # D = U - W S
     elif name == "bchunk2_finish":  # dbeta (and per-head dg) from the channel-half partials
         by = (3 * C * f4 + C * f4) + (0 if per_channel else 2 * C * f4 + C * f4)
