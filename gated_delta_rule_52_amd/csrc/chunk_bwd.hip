@@ -488,7 +488,7 @@ bscan4_kernel(const bf16* __restrict__ KhTp, const bf16* __restrict__ Psp,
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const f32x4 tr = mfma_bf16_16x16x32(dsb[t / 2], (t & 1) ? id_hi : id_lo, zero4());
-            *reinterpret_cast<uint2*>(&dSt[(ch * DK + 16 * t + ln) * DV + vc + 4 * lg]) =
+            *reinterpret_cast<uint2*>(&dSt[slice32(ch, DK, DV, 16 * t + ln, vc + 4 * lg)]) =
                 pack4_bf16(tr[0], tr[1], tr[2], tr[3]);
         }
         // dO as the operand with K along tokens: slot e of lane group lg is token
@@ -531,7 +531,7 @@ bscan4_kernel(const bf16* __restrict__ KhTp, const bf16* __restrict__ Psp,
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const f32x4 tr = mfma_bf16_16x16x32(ddb[t / 2], (t & 1) ? id_hi : id_lo, zero4());
-            *reinterpret_cast<uint2*>(&dDt[(ch * C + 16 * t + ln) * DV + vc + 4 * lg]) =
+            *reinterpret_cast<uint2*>(&dDt[slice32(ch, C, DV, 16 * t + ln, vc + 4 * lg)]) =
                 pack4_bf16(tr[0], tr[1], tr[2], tr[3]);
         }
         const bf16x8 ddn[2] = {frag_neg(ddb[0]), frag_neg(ddb[1])};
@@ -1061,6 +1061,8 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         int nv;
         size_t tk;
         geo(c, nv, tk);
+        // the saved bf16 arrays are in 32-column slices (slice32): a Dv tile
+        // is one contiguous [rows][32] block at slice v0 / 32
         Sp = Sst + (size_t)c * DK * DV;
         dSp = dSt + (size_t)c * DK * DV;
         dDp = dDt + (size_t)c * C * DV;
@@ -1074,12 +1076,12 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         for (int q = 0; q < QS; ++q) {
             const int idx = tid + NTHR_C * q;
             const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
-            pS[q] = *reinterpret_cast<const uint2*>(Sp + i * DV + v0 + j4);
-            pdS[q] = *reinterpret_cast<const uint2*>(dSp + i * DV + v0 + j4);
+            pS[q] = *reinterpret_cast<const uint2*>(Sp + v0 * DK + i * BW + j4);
+            pdS[q] = *reinterpret_cast<const uint2*>(dSp + v0 * DK + i * BW + j4);
         }
-        pdD = *reinterpret_cast<const uint2*>(dDp + rd * DV + v0 + jd);
+        pdD = *reinterpret_cast<const uint2*>(dDp + v0 * C + rd * BW + jd);
         pU = load4<float>(Up + rd * DV + v0 + jd);
-        const bf16* src = lowh ? Dp + r8 * DV + v0 + j8 : dO + tokr + v0 + j8;
+        const bf16* src = lowh ? Dp + v0 * C + r8 * BW + j8 : dO + tokr + v0 + j8;
         pa = *reinterpret_cast<const uint4*>(src);
         pb = *reinterpret_cast<const uint4*>(v + tokr + v0 + j8);
     };

@@ -55,6 +55,16 @@ constexpr bool bf16_tables()
     return sizeof(TIn) == 2 && C == 64 && DK >= 64;
 }
 
+// Element (i, c) of a chunk-head's [R][Dv] array stored in 32-column slices,
+// [ch][Dv / 32][R][32]: a 32-column tile of R rows is one contiguous block.  The
+// bf16 path keeps its saved states, deltas and their gradients this way: the
+// scans write one 32-column slice per workgroup and bchunk1b reads 32-column
+// tiles, each then whole 128-byte lines.
+__host__ __device__ __forceinline__ size_t slice32(size_t ch, int R, int DV, int i, int c)
+{
+    return ((ch * (size_t)(DV / 32) + (size_t)(c >> 5)) * (size_t)R + (size_t)i) * 32 + (size_t)(c & 31);
+}
+
 // fp32 inputs at chunk 64 run the fp32-operand scans: their tables stay fp32,
 // with Kh stored transposed (Kh^T [DK][C], like the bf16 tables) so that every
 // operand of the forward scan is a K-contiguous row read.

@@ -1694,7 +1694,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             const int si = idx / (BV / 16), sj = idx % (BV / 16);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Sst[((size_t)bh * NC * DK + si * 16 + 4 * lq + r) * DV + v0 + sj * 16 + lr] = f32_to_bf16(sacc[m][r]);
+                Sst[slice32((size_t)bh * NC, DK, DV, si * 16 + 4 * lq + r, v0 + sj * 16 + lr)] = f32_to_bf16(sacc[m][r]);
         }
     }
     // one step: chunk n with its tables in LDS; `nx` holds chunk n + 1 (stashed
@@ -1780,7 +1780,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 const int e = tid + NTHR_S * u;
                 if (e < NF8) {
                     const int i = e / (BV / 8), j8 = (e % (BV / 8)) * 8;
-                    *reinterpret_cast<uint4*>(&Sst[((ch + 1) * DK + i) * DV + v0 + j8]) =
+                    *reinterpret_cast<uint4*>(&Sst[slice32(ch + 1, DK, DV, i, v0 + j8)]) =
                         *reinterpret_cast<const uint4*>(&sSf[pb][i][j8]);
                 }
             }
@@ -1791,7 +1791,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             if (tid < NB8) {
                 const int i = tid / (BV / 8), j8 = (tid % (BV / 8)) * 8;
                 if (SAVE)
-                    *reinterpret_cast<uint4*>(&Dst[(ch * C + i) * DV + v0 + j8]) =
+                    *reinterpret_cast<uint4*>(&Dst[slice32(ch, C, DV, i, v0 + j8)]) =
                         *reinterpret_cast<const uint4*>(&sDr[pb][i][j8]);
             } else if (tid < 2 * NB8) {
                 const int e = tid - NB8, i = e / (BV / 8), j8 = (e % (BV / 8)) * 8;

@@ -27,6 +27,8 @@
 //                     per-head dg (bf16 inputs at chunk 64)
 //   Ur  [ch][C][Dv], Wr [ch][C][Dk] (bf16): with clip, the products T X_V and
 //                     T X_K before clipping, for the WY adjoint of the bf16 path
+// With bf16 inputs at chunk 64, Sst, dSt, dDt and Dst are bf16 in 32-column
+// slices, [ch][Dv / 32][rows][32] (slice32 in chunk_common.h).
 // With bf16 inputs at chunk 64 the tables W, Qg, Kh, Ps are bf16, in the
 // first half of their fp32-sized regions, in one orientation: W [C][Dk],
 // Qg [C][Dk], Kh^T [Dk][C], Ps [C][C] (the backward scan reads their
