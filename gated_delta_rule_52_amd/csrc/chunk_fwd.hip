@@ -893,22 +893,18 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             sXV[j0 + 2 * e + 1][r] = f32_to_bf16(bt * __uint_as_float(wd[e] & 0xFFFF0000u));
         }
     }
-    // ---- W = T X_K (bf16 out, and W^T for training)
+    // ---- W = T X_K (bf16 out).  The tile of W^T = X_K^T T^T: a lane holds 4
+    // consecutive columns of one W row, one 8-byte store
     constexpr int TW = NB * (DK / 16);
     for (int idx = w; idx < TW; idx += NW) {
         const int ti = idx / (DK / 16), tj = idx % (DK / 16);
-        const int K = ((16 * (ti + 1) + 31) / 32) * 32;
-        f32x4 acc = mma_kc_dyn(zero4(), &sTb[ti * 16][0], PT, &sXT[tj * 16][0], PT, K);
-        if (SAFE && Wro) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Wro[(size_t)ch * C * DK + (ti * 16 + 4 * lq + r) * DK + tj * 16 + lr] = f32_to_bf16(acc[r]);
-        }
+        const int K = ((16 * (ti + 1) + 31) / 32) * 32;  // T is lower triangular
+        f32x4 acc = mma_kc_dyn(zero4(), &sXT[tj * 16][0], PT, &sTb[ti * 16][0], PT, K);
+        const size_t e = (size_t)ch * C * DK + (ti * 16 + lr) * DK + tj * 16 + 4 * lq;
+        if (SAFE && Wro) *reinterpret_cast<uint2*>(&Wro[e]) = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = grd(acc[r], GDN_DIAG_W);
-        bf16* Wc = Wb + (size_t)ch * C * DK;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Wc[(ti * 16 + 4 * lq + r) * DK + tj * 16 + lr] = f32_to_bf16(acc[r]);
+        *reinterpret_cast<uint2*>(&Wb[e]) = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();  // X_V^T complete
     // ---- U = T X_V (fp32 out; Uro, training with clip: also before clipping).
