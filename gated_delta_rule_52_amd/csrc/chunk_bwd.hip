@@ -46,7 +46,8 @@ struct BScanCfg {
 };
 
 // ---------------------------------------------------------------------------
-// bscan
+// bscan (fp32 tables; the chunk-16 configurations: chunk 64 runs bscan4 or
+// bscanf)
 // ---------------------------------------------------------------------------
 template <typename TIn, int C, int DK, int DV, int MT>
 __global__ void __launch_bounds__(NTHR)
@@ -56,6 +57,7 @@ bscan_kernel(const float* __restrict__ Qgi, const float* __restrict__ Khi,
              const float* __restrict__ dhT, float* __restrict__ dSt, float* __restrict__ dDt,
              float* __restrict__ dh0, int BH, int T, int H, int NC)
 {
+    static_assert(!bf16_tables<TIn, C, DK>() && !f32_tables<TIn, C, DK>(), "chunk 64 runs bscan4 or bscanf");
     using G = Geo<C, DK, DV>;
     using SC = BScanCfg<DV>;
     constexpr int PD = G::PD, PC = G::PC, BV = SC::BV, NS = SC::NS, PS = SC::PS;
@@ -594,7 +596,8 @@ bscan4_kernel(const bf16* __restrict__ KhTp, const bf16* __restrict__ Psp,
 }
 
 // ---------------------------------------------------------------------------
-// bchunk1
+// bchunk1 (fp32 tables; the chunk-16 configurations: chunk 64 runs bchunk1b or
+// bchunk1f)
 // ---------------------------------------------------------------------------
 template <typename TIn, int C, int DK, int DV, int MT>
 __global__ void __launch_bounds__(NTHR)
@@ -607,6 +610,7 @@ bchunk1_kernel(const TIn* __restrict__ v, const float* __restrict__ beta,
                float* __restrict__ dT1o, float* __restrict__ dgmo, float* __restrict__ dbpo, int T,
                int H, int NC)
 {
+    static_assert(!bf16_tables<TIn, C, DK>() && !f32_tables<TIn, C, DK>(), "chunk 64 runs bchunk1b or bchunk1f");
     using G = Geo<C, DK, DV>;
     constexpr int PD = G::PD, PC = G::PC, NB = G::NB;
     constexpr int BW = DV >= 32 ? 32 : DV, PW = BW + 4;
@@ -624,10 +628,7 @@ bchunk1_kernel(const TIn* __restrict__ v, const float* __restrict__ beta,
     {
         for (int idx = tid; idx < C * DK / 4; idx += NTHR) {
             const int r = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
-            if constexpr (bf16_tables<TIn, C, DK>())
-                st4(&sW[r][c4], load4<bf16>(reinterpret_cast<const bf16*>(Wi) + (size_t)ch * C * DK + r * DK + c4));
-            else
-                st4(&sW[r][c4], load4<float>(Wi + (size_t)ch * C * DK + r * DK + c4));
+            st4(&sW[r][c4], load4<float>(Wi + (size_t)ch * C * DK + r * DK + c4));
         }
         const float* Tp = Tmi + (size_t)ch * C * C;
         for (int idx = tid; idx < C * C / 4; idx += NTHR) {
@@ -1665,14 +1666,14 @@ bchunk2_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float
     const size_t tok0 = ((size_t)b * T + t0) * H + h;
     const size_t rsK = (size_t)H * DK;
 
-    // intermediate gradients from bchunk1: bf16 with bf16 tables, else fp32
-    constexpr bool BT = bf16_tables<TIn, C, DK>();
-    using IT = typename std::conditional<BT, bf16, float>::type;
-    const IT* dQgI = reinterpret_cast<const IT*>(dQgi);
-    const IT* dWgI = reinterpret_cast<const IT*>(dWgi);
-    const IT* dKhI = reinterpret_cast<const IT*>(dKhi);
-    const IT* dPsI = reinterpret_cast<const IT*>(dPsi);
-    const IT* dT1I = reinterpret_cast<const IT*>(dT1i);
+    // intermediate gradients from bchunk1 (fp32)
+    static_assert(!bf16_tables<TIn, C, DK>(), "bf16 inputs at chunk 64 run bchunk2c");
+    using IT = float;
+    const IT* dQgI = dQgi;
+    const IT* dWgI = dWgi;
+    const IT* dKhI = dKhi;
+    const IT* dPsI = dPsi;
+    const IT* dT1I = dT1i;
 
     // column threads: channel c, rows [p0, p0 + RPP)
     const bool cp = tid < NPART * DK;
@@ -2743,7 +2744,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
                        (const float*)(ws + p.o_dgq), dbeta, dg, p.T, p.H, p.NC, C, tot);
         if (p.l2n) return run_l2norm_bwd<TIn, DK>(p, q, k, dq, dk, ws, st);
         return GDN_OK;
-    }
+    } else {
     if (p.decay == GDN_DECAY_PER_CHANNEL)
         GDN_LAUNCH("bchunk2", (bchunk2_kernel<TIn, C, DK, DV, true, MT>), gch, dim3(NTHR2), st,
                            (const TIn*)q, (const TIn*)k, g, beta, (const float*)(ws + p.o_Tm),
@@ -2763,6 +2764,7 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
     GDN_HIP_CHECK_LAUNCH();
     if (p.l2n) return run_l2norm_bwd<TIn, DK>(p, q, k, dq, dk, ws, st);
     return GDN_OK;
+    }
 }
 
 template <typename TIn>

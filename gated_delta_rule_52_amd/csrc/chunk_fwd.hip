@@ -36,7 +36,7 @@
 namespace gdn {
 
 // ---------------------------------------------------------------------------
-// prep
+// prep (fp32 tables; the chunk-16 configurations: chunk 64 runs prep2 or prepf)
 // ---------------------------------------------------------------------------
 template <typename TIn, int C, int DK, int DV, bool PCH, int MT>
 __global__ void __launch_bounds__(NTHR)
@@ -46,6 +46,7 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
             float* __restrict__ Kho, float* __restrict__ Pso, float* __restrict__ gamo,
             float* __restrict__ Tmo, float* __restrict__ rno, Safety sf)
 {
+    static_assert(!bf16_tables<TIn, C, DK>() && !f32_tables<TIn, C, DK>(), "chunk 64 runs prep2 or prepf");
     using G = Geo<C, DK, DV>;
     constexpr int PD = G::PD, PC = G::PC, NB = G::NB, HALF = G::HALF;
     __shared__ float sq[C][PD], sk[C][PD], sX[C][PD], sY[C][PD], sA[C][PC];
@@ -190,24 +191,11 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
         __syncthreads();
     }
 
-    // ---- scores out: Ps = scale P (global, upper part zero), A (x beta) to LDS.
-    // bf16 inputs: Ps as bf16, and in training also its transpose PsT.
-    constexpr bool BT = bf16_tables<TIn, C, DK>();
-    const size_t nch = gridDim.x;
-    const bool bwdt = Tmo != nullptr;
+    // ---- scores out: Ps = scale P (global, upper part zero), A (x beta) to LDS
     float* Ps = Pso + (size_t)ch * C * C;
-    bf16* Psb = reinterpret_cast<bf16*>(Pso) + (size_t)ch * C * C;
-    bf16* PsTb = reinterpret_cast<bf16*>(Pso) + nch * C * C + (size_t)ch * C * C;
     auto put_ps = [&](int i0, int j, const float (&pv)[4]) {  // rows i0..i0+3, column j
-        if (BT) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Psb[(i0 + r) * C + j] = f32_to_bf16(pv[r]);
-            if (bwdt)
-                *reinterpret_cast<uint2*>(&PsTb[j * C + i0]) = pack4_bf16(pv[0], pv[1], pv[2], pv[3]);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Ps[(i0 + r) * C + j] = pv[r];
-        }
+        for (int r = 0; r < 4; ++r) Ps[(i0 + r) * C + j] = pv[r];
     };
 #pragma unroll
     for (int s = 0; s < G::MAXOFF; ++s) {
@@ -239,12 +227,7 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
     for (int idx = tid; idx < C * C; idx += NTHR) {
         const int i = idx / C, j = idx % C;
         if (i / 16 < j / 16) {
-            if (BT) {
-                Psb[idx] = f32_to_bf16(0.f);
-                if (bwdt) PsTb[j * C + i] = f32_to_bf16(0.f);
-            } else {
-                Ps[idx] = 0.f;
-            }
+            Ps[idx] = 0.f;
             sA[i][j] = 0.f;
         }
     }
@@ -275,41 +258,12 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
             khv[i] = sk[r][c] * kap;
             kap *= a[i];
         }
-        if (BT) {
-            // forward: Qg [C][DK], KhT [DK][C]; training also QgT [DK][C], Kh [C][DK]
-            bf16* Qgb = reinterpret_cast<bf16*>(Qgo) + (size_t)ch * C * DK;
-            bf16* QgTb = reinterpret_cast<bf16*>(Qgo) + nch * C * DK + (size_t)ch * C * DK;
-            bf16* KhTb = reinterpret_cast<bf16*>(Kho) + (size_t)ch * C * DK;
-            bf16* Khb = reinterpret_cast<bf16*>(Kho) + nch * C * DK + (size_t)ch * C * DK;
+        float* Qg = Qgo + (size_t)ch * C * DK;
+        float* Kh = Kho + (size_t)ch * C * DK;
 #pragma unroll
-            for (int i = 0; i < HALF; ++i) Qgb[(part * HALF + i) * DK + c] = f32_to_bf16(qgv[i]);
-#pragma unroll
-            for (int i = 0; i < HALF; i += 4)
-                *reinterpret_cast<uint2*>(&KhTb[c * C + part * HALF + i]) =
-                    pack4_bf16(khv[i], khv[i + 1], khv[i + 2], khv[i + 3]);
-            if (bwdt) {
-#pragma unroll
-                for (int i = 0; i < HALF; i += 4)
-                    *reinterpret_cast<uint2*>(&QgTb[c * C + part * HALF + i]) =
-                        pack4_bf16(qgv[i], qgv[i + 1], qgv[i + 2], qgv[i + 3]);
-#pragma unroll
-                for (int i = 0; i < HALF; ++i) Khb[(part * HALF + i) * DK + c] = f32_to_bf16(khv[i]);
-            }
-        } else {
-            float* Qg = Qgo + (size_t)ch * C * DK;
-            float* Kh = Kho + (size_t)ch * C * DK;
-#pragma unroll
-            for (int i = 0; i < HALF; ++i) Qg[(part * HALF + i) * DK + c] = qgv[i];
-            if constexpr (f32_tables<TIn, C, DK>()) {
-                // Kh^T [DK][C]: this channel's row, its half in 16-byte words
-#pragma unroll
-                for (int i = 0; i < HALF; i += 4)
-                    *reinterpret_cast<float4*>(&Kh[c * C + part * HALF + i]) =
-                        make_float4(khv[i], khv[i + 1], khv[i + 2], khv[i + 3]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < HALF; ++i) Kh[(part * HALF + i) * DK + c] = khv[i];
-            }
+        for (int i = 0; i < HALF; ++i) {
+            Qg[(part * HALF + i) * DK + c] = qgv[i];
+            Kh[(part * HALF + i) * DK + c] = khv[i];
         }
     }
 
@@ -379,24 +333,13 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
     }
     __syncthreads();
     float* Wp = Wo + (size_t)ch * C * DK;
-    bf16* Wb = reinterpret_cast<bf16*>(Wo) + (size_t)ch * C * DK;
-    bf16* WTb = reinterpret_cast<bf16*>(Wo) + nch * C * DK + (size_t)ch * C * DK;
     for (int idx = w; idx < NB * (DK / 16); idx += 4) {
         const int ti = idx / (DK / 16), tj = idx % (DK / 16);
         f32x4 acc = mma16<MT_F32>(zero4(), &sT[ti * 16 * PC], PC, 1, &sY[0][tj * 16], PD, 1, 16 * (ti + 1));
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = grd(acc[r], GDN_DIAG_W);
-        if (BT) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Wb[(ti * 16 + acc_row(r)) * DK + tj * 16 + acc_col()] = f32_to_bf16(acc[r]);
-            if (bwdt)
-                *reinterpret_cast<uint2*>(&WTb[(tj * 16 + acc_col()) * C + ti * 16 + acc_row(0)]) =
-                    pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Wp[(ti * 16 + acc_row(r)) * DK + tj * 16 + acc_col()] = acc[r];
-        }
+        for (int r = 0; r < 4; ++r) Wp[(ti * 16 + acc_row(r)) * DK + tj * 16 + acc_col()] = acc[r];
     }
     float* Up = Uo + (size_t)ch * C * DV;
     for (int idx = w; idx < NB * (DV / 16); idx += 4) {
@@ -1398,7 +1341,8 @@ prepf_kernel(const float* __restrict__ q, const float* __restrict__ k, const flo
 }
 
 // ---------------------------------------------------------------------------
-// scan
+// scan (fp32 tables; the chunk-16 configurations: chunk 64 runs scan2, scan3
+// or scanf)
 // ---------------------------------------------------------------------------
 template <int DV>
 struct ScanCfg {
@@ -1415,6 +1359,7 @@ scan_kernel(const float* __restrict__ Wi, const float* __restrict__ Ui,
             const float* h0, TIn* __restrict__ o, float* hT,
             float* __restrict__ Sst, int BH, int T, int H, int NC)
 {
+    static_assert(!bf16_tables<TIn, C, DK>() && !f32_tables<TIn, C, DK>(), "chunk 64 runs scan2, scan3 or scanf");
     using G = Geo<C, DK, DV>;
     using SC = ScanCfg<DV>;
     constexpr int PD = G::PD, PC = G::PC, BV = SC::BV, NS = SC::NS, PS = SC::PS;
@@ -2245,15 +2190,16 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
             });
         });
     }
-    if (p.decay == GDN_DECAY_PER_CHANNEL)
-        GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep_kernel<TIn, C, DK, DV, true, MT>), grid, block, st,
-                           (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
-                           p.scale, W, U, Qg, Kh, Ps, gam, Tm, rn, sf);
-    else
-        GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep_kernel<TIn, C, DK, DV, false, MT>), grid, block, st,
-                           (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
-                           p.scale, W, U, Qg, Kh, Ps, gam, Tm, rn, sf);
-    GDN_HIP_CHECK_LAUNCH();
+    if constexpr (!bf16_tables<TIn, C, DK>() && !f32_tables<TIn, C, DK>()) {
+        if (p.decay == GDN_DECAY_PER_CHANNEL)
+            GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep_kernel<TIn, C, DK, DV, true, MT>), grid, block, st,
+                       (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
+                       p.scale, W, U, Qg, Kh, Ps, gam, Tm, rn, sf);
+        else
+            GDN_LAUNCH(want_T ? "prep_T" : "prep", (prep_kernel<TIn, C, DK, DV, false, MT>), grid, block, st,
+                       (const TIn*)q, (const TIn*)k, (const TIn*)v, g, beta, p.T, p.H, p.NC,
+                       p.scale, W, U, Qg, Kh, Ps, gam, Tm, rn, sf);
+    }
     return GDN_OK;
 }
 
@@ -2294,13 +2240,14 @@ gdn_status run_scan(const Plan& p, const float* h0, void* o, float* hT, char* ws
                    BH, p.T, p.H, p.NC);
         return GDN_OK;
     }
-    dim3 grid((unsigned)(ngrp * 8 * SC::NS)), block(NTHR);
-    GDN_LAUNCH(SAVE ? (OUT ? "scan_train" : "scan_save") : "scan", (scan_kernel<TIn, C, DK, DV, MT, SAVE, OUT>), grid, block, st,
-                       (const float*)(ws + p.o_W), (const float*)(ws + p.o_U),
-                       (const float*)(ws + p.o_Qg), (const float*)(ws + p.o_Kh),
-                       (const float*)(ws + p.o_Ps), (const float*)(ws + p.o_gam), h0, (TIn*)o, hT,
-                       SAVE ? (float*)(ws + p.o_Sst) : nullptr, BH, p.T, p.H, p.NC);
-    GDN_HIP_CHECK_LAUNCH();
+    if constexpr (!bf16_tables<TIn, C, DK>() && !f32_tables<TIn, C, DK>()) {
+        dim3 grid((unsigned)(ngrp * 8 * SC::NS)), block(NTHR);
+        GDN_LAUNCH(SAVE ? (OUT ? "scan_train" : "scan_save") : "scan", (scan_kernel<TIn, C, DK, DV, MT, SAVE, OUT>),
+                   grid, block, st, (const float*)(ws + p.o_W), (const float*)(ws + p.o_U),
+                   (const float*)(ws + p.o_Qg), (const float*)(ws + p.o_Kh),
+                   (const float*)(ws + p.o_Ps), (const float*)(ws + p.o_gam), h0, (TIn*)o, hT,
+                   SAVE ? (float*)(ws + p.o_Sst) : nullptr, BH, p.T, p.H, p.NC);
+    }
     return GDN_OK;
 }
 
