@@ -129,12 +129,13 @@ def kernel_work(name, B, T, H, C, DK, DV, in_bytes, per_channel=True, l2n=False)
     elif name == "bchunk1":
         it = 2 if bt else 4
         by = 2 * cv * ib + C * f4 + cc * f4 + 2 * kv * tb + cv * tb   # v dO, beta, T, S, dS, dD
-        by += (cv * 2 + cv * f4 + cd * tb) if bt else cv * f4 if ft else (cd + cv) * f4  # D, U, W | D | W, U
+        by += (cv * 2 + cd * tb) if bt else cv * f4 if ft else (cd + cv) * f4  # D, W | D | W, U
         by += cv * ib + 3 * cd * it + 2 * cc * it + DK * f4 + C * f4  # dv, dQg dX_K|dW dKh, dPs dA|dT1, dgam, dbeta
-        fl[mt] += 6 * C * DK * DV + 2 * tri * DV + 2 * C * C * DV     # dQg dW dKh, dPs, dX_V U^T | dD X_V^T
+        fl[mt] += 6 * C * DK * DV + 2 * tri * DV + 2 * C * C * DV     # dQg dW dKh, dPs, dX_V V^T | dD X_V^T
         fl["f32"] += 2 * tri * DV                                      # dX_V = T^T dD
-        if bt:   # keys' WY adjoint: dX_K = T^T dW, dA = -(G1 + dX_K W^T) strictly lower
-            fl["bf16"] += 2 * tri * DK + 2 * (C * (C - 1) // 2) * DK
+        if bt:   # keys' WY adjoint: dX_K = T^T dW, G1 = (dX_V V^T) diag(beta) T^T,
+                 # dA = -(G1 + dX_K W^T) strictly lower
+            fl["bf16"] += 2 * tri * DK + 2 * tri * C + 2 * (C * (C - 1) // 2) * DK
         elif not ft:
             fl[mt] += 2 * C * DK * DV                                  # D = U - W S
     elif name == "bchunk2_finish":  # dbeta (and per-head dg) from the channel-half partials

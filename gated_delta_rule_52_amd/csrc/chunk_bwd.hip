@@ -977,7 +977,7 @@ template <int C, int DK, int DV>
 __global__ void __launch_bounds__(NTHR_C)
 bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const bf16* __restrict__ dO, const bf16* __restrict__ Dst,
-                const float* __restrict__ Ui, const float* __restrict__ Tmi,
+                const float* __restrict__ Tmi,
                 const bf16* __restrict__ Wbi, const bf16* __restrict__ Sst,
                 const bf16* __restrict__ dSt, const bf16* __restrict__ dDt,
                 bf16* __restrict__ dvo, float* __restrict__ dQgo, float* __restrict__ dWgo,
@@ -1006,7 +1006,11 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     constexpr int O_v = O_dX + C * R4, STREAM = O_v + C * PF * 4;
     constexpr int O_W = DK * C * 2;
     constexpr int O_Xh = O_W + C * DK * 2, O_Xl = O_Xh + C * DK * 2, ENDP = O_Xl + C * DK * 2;
-    __shared__ __align__(16) char sbuf[cmax(STREAM, ENDP)];
+    // the tail's M diag(beta) parts (2 x C x C bf16): in the dv staging bytes
+    // when they fit there (Dv = 128), else after the tail's tables
+    constexpr bool M_IN_DV = 2 * C * C * 2 <= C * (DV + 8) * 2;
+    constexpr int ENDM = M_IN_DV ? ENDP : ENDP + 2 * C * C * 2;
+    __shared__ __align__(16) char sbuf[cmax(STREAM, ENDM)];
     // T as high + low bf16 parts (16 significant bits), for dX_V = T^T dD in the
     // Dv loop and dX_K = T^T dW after it; built once from the loaded T
     __shared__ __align__(16) uint4 sTh[C * C / 8], sTl[C * C / 8];
@@ -1017,8 +1021,8 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     char* const sdO = sbuf + O_dO;
     char* const sD = sbuf + O_D;
     char* const sdD = sbuf + O_dD;
-    char* const sU = sbuf + O_U;    // U and dX_V tiles,
-    char* const sdX = sbuf + O_dX;  // for G1 = dX_V U^T
+    char* const sV = sbuf + O_U;    // v and dX_V tiles, for
+    char* const sdX = sbuf + O_dX;  // M = dX_V V^T
     float (*sv)[PF] = reinterpret_cast<float (*)[PF]>(sbuf + O_v);
     char* const sdWT = sbuf;  // dW^T
     char* const sW = sbuf + O_W;
@@ -1040,7 +1044,6 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // the chunk the prefetch reads (the current one inside the Dv loop, the
     // next one of this workgroup during the current one's WY-adjoint tail)
     const bf16 *Sp, *dSp, *dDp, *Dp;  // bf16 chunk-start states, chunk-end state gradients, delta gradients, D
-    const float* Up;
     size_t tokr;  // this thread's token row of dO and v
     int nvalid;   // of the chunk being computed
     size_t tok0;
@@ -1048,16 +1051,15 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 
     // Prefetch of one Dv tile, branch-free (a load under a divergent branch makes
     // the compiler wait for it where the branches join): every thread loads two
-    // S words, two dS words, one dD and one U word, one D-or-dO word and one v
-    // word; rows past the end are clamped on load and zeroed in stash().
+    // S words, two dS words, one dD word, one D-or-dO word and one v word; rows
+    // past the end are clamped on load and zeroed in stash().
     static_assert(NS4 == QS * NTHR_C && ND4 == NTHR_C && NB8 == NTHR_C / 2, "tile split");
     uint2 pS[QS], pdS[QS], pdD;  // four bf16 values each
-    float4 pU;
     uint4 pa, pb;  // threads < NB8: D and v words; threads >= NB8: dO word (and an unused v word)
     const bool lowh = tid < NB8;
     const int e8 = lowh ? tid : tid - NB8;
     const int r8 = e8 / (BW / 8), j8 = (e8 % (BW / 8)) * 8;
-    const int rd = tid / (BW / 4), jd = (tid % (BW / 4)) * 4;  // dD / U word of this thread
+    const int rd = tid / (BW / 4), jd = (tid % (BW / 4)) * 4;  // dD word of this thread
     auto fetch_from = [&](int c) {
         int nv;
         size_t tk;
@@ -1068,7 +1070,6 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         dSp = dSt + (size_t)c * DK * DV;
         dDp = dDt + (size_t)c * C * DV;
         Dp = Dst + (size_t)c * C * DV;
-        Up = Ui + (size_t)c * C * DV;
         tokr = (tk + (size_t)min(r8, nv - 1) * H) * DV;
         return tk + (size_t)min(tid % C, nv - 1) * H;  // this thread's beta token
     };
@@ -1081,7 +1082,6 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             pdS[q] = *reinterpret_cast<const uint2*>(dSp + v0 * DK + i * BW + j4);
         }
         pdD = *reinterpret_cast<const uint2*>(dDp + v0 * C + rd * BW + jd);
-        pU = load4<float>(Up + rd * DV + v0 + jd);
         const bf16* src = lowh ? Dp + v0 * C + r8 * BW + j8 : dO + tokr + v0 + j8;
         pa = *reinterpret_cast<const uint4*>(src);
         pb = *reinterpret_cast<const uint4*>(v + tokr + v0 + j8);
@@ -1107,10 +1107,10 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             *at4(sdS, i, j4) = d2;
         }
         *at4(sdD, rd, jd) = pdD;
-        *at4(sU, rd, jd) = pack4_bf16(pU.x, pU.y, pU.z, pU.w);
         if (lowh) {
             *at8(sD, r8, j8) = pa;
             const uint4 vb = row8 ? pb : uint4{0u, 0u, 0u, 0u};
+            *at8(sV, r8, j8) = vb;
             const uint32_t u[4] = {vb.x, vb.y, vb.z, vb.w};
             float vv[8];
 #pragma unroll
@@ -1282,7 +1282,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 const int idx = w + NW * m;
                 if (idx < T2) {
                     const int ti = idx / NB, tj = idx % NB;
-                    aT[m] = mfma_bf16_16x16x32(frag_rows<SwzU4>(sdX, ti * 16, 0), frag_rows<SwzU4>(sU, tj * 16, 0), aT[m]);
+                    aT[m] = mfma_bf16_16x16x32(frag_rows<SwzU4>(sdX, ti * 16, 0), frag_rows<SwzU4>(sV, tj * 16, 0), aT[m]);
                 }
             }
             __syncthreads();
@@ -1338,7 +1338,10 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
 
         // ---- WY adjoint of the keys (W = T X_K):  dX_K = T^T dW and
         //   dA = -T^T (dU X_V^T + dW X_K^T) T^T = -(dX_V U^T + dX_K W^T) = -(G1 + dX_K W^T),
-        // on bf16 MFMA with T and dX_K as high + low bf16 parts (16 significant bits).
+        // with G1 = dX_V U^T = M diag(beta) T^T (U = T diag(beta) V, M = dX_V V^T
+        // from the Dv loop): U is not read, and with clip the product is the
+        // unclipped one by construction.  bf16 MFMA with T, M diag(beta) and dX_K
+        // as high + low bf16 parts (16 significant bits).
 #pragma unroll
         for (int u = 0; u < NK8; ++u) {
             const int idx = tid + NTHR_C * u;
@@ -1348,6 +1351,31 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         // the next chunk's prologue loads, in flight through the tail (the last
         // workgroup's final chunk repeats itself: loads stay unconditional)
         prologue_loads((int)min((long long)ch + gridDim.x, (long long)nch - 1));
+        // M diag(beta) (rows i, columns k) as high + low parts (the dv staging
+        // was written out before the barrier above)
+        char* const sMh = M_IN_DV ? reinterpret_cast<char*>(&sDV[0][0]) : sbuf + ENDP;
+        char* const sMl = sMh + C * C * 2;
+#pragma unroll
+        for (int m = 0; m < M2; ++m) {
+            const int idx = w + NW * m;
+            if (idx < T2) {
+                const int ti = idx / NB, tj = idx % NB;
+                const float bk = sbeta[tj * 16 + lr];
+                f32x4 hi, lo;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = aT[m][r] * bk;
+                    hi[r] = to_f32(f32_to_bf16(x));
+                    lo[r] = x - hi[r];
+                }
+                const uint2 wh = acc_colpairs(hi), wl = acc_colpairs(lo);
+                const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
+                *reinterpret_cast<uint32_t*>(swz_at<SwzU8>(sMh, i2, j2)) = wh.x;
+                *reinterpret_cast<uint32_t*>(swz_at<SwzU8>(sMh, i2 + 1, j2)) = wh.y;
+                *reinterpret_cast<uint32_t*>(swz_at<SwzU8>(sMl, i2, j2)) = wl.x;
+                *reinterpret_cast<uint32_t*>(swz_at<SwzU8>(sMl, i2 + 1, j2)) = wl.y;
+            }
+        }
 #pragma unroll
         for (int m = 0; m < M3; ++m) {
             const int idx = w + NW * m;
@@ -1385,12 +1413,27 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             const int idx = w + NW * m;
             if (idx < T2) {
                 const int ti = idx / NB, tj = idx % NB;
-                f32x4 acc = aT[m];
+                f32x4 acc = zero4();
+                if (ti >= tj) {  // dA is strictly lower: tiles above the diagonal are zero
+                    // G1 = (M diag(beta)) T^T; T is lower triangular, so the K block
+                    // from k0 contributes only if k0 <= the tile's last row of T
 #pragma unroll
-                for (int u0 = 0; u0 < DK / 8; u0 += 4) {
-                    const bf16x8 bw = frag_rows<SwK>(sW, tj * 16, u0);
-                    acc = mfma_bf16_16x16x32(frag_rows<SwK>(sXh, ti * 16, u0), bw, acc);
-                    acc = mfma_bf16_16x16x32(frag_rows<SwK>(sXl, ti * 16, u0), bw, acc);
+                    for (int k0 = 0; k0 < C; k0 += 32) {
+                        if (k0 <= tj * 16 + 15) {
+                            const bf16x8 th = frag_rows<SwzU8>(sTh, tj * 16, k0 / 8);
+                            const bf16x8 tl = frag_rows<SwzU8>(sTl, tj * 16, k0 / 8);
+                            const bf16x8 mh = frag_rows<SwzU8>(sMh, ti * 16, k0 / 8);
+                            acc = mfma_bf16_16x16x32(mh, th, acc);
+                            acc = mfma_bf16_16x16x32(mh, tl, acc);
+                            acc = mfma_bf16_16x16x32(frag_rows<SwzU8>(sMl, ti * 16, k0 / 8), th, acc);
+                        }
+                    }
+#pragma unroll
+                    for (int u0 = 0; u0 < DK / 8; u0 += 4) {
+                        const bf16x8 bw = frag_rows<SwK>(sW, tj * 16, u0);
+                        acc = mfma_bf16_16x16x32(frag_rows<SwK>(sXh, ti * 16, u0), bw, acc);
+                        acc = mfma_bf16_16x16x32(frag_rows<SwK>(sXl, ti * 16, u0), bw, acc);
+                    }
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -2679,14 +2722,14 @@ gdn_status backward_t(const Plan& p, const void* q, const void* k, const void* v
     }
     dim3 gch((unsigned)p.n_ch);
     if constexpr (bf16_tables<TIn, C, DK>()) {
-        // the WY adjoint takes U = T X_V and W = T X_K as products: with clip the
-        // unclipped copies (clipping is differentiated as the identity)
+        // the WY adjoint takes W = T X_K as a product: with clip the unclipped
+        // copy (clipping is differentiated as the identity; its U side is formed
+        // from T and v in the kernel)
         const bool raw = p.clip > 0.f;
         // persistent, one workgroup per CU (its LDS allows no second one)
         const dim3 gp((unsigned)std::min<long long>(p.n_ch, device_cus()));
         GDN_LAUNCH("bchunk1", (bchunk1b_kernel<C, DK, DV>), gp, dim3(NTHR_C), st, (const bf16*)v,
-                   beta, (const bf16*)dO, (const bf16*)(ws + p.o_Dst),
-                   (const float*)(ws + (raw ? p.o_Ur : p.o_U)), (const float*)(ws + p.o_Tm),
+                   beta, (const bf16*)dO, (const bf16*)(ws + p.o_Dst), (const float*)(ws + p.o_Tm),
                    (const bf16*)(ws + (raw ? p.o_Wr : p.o_W)),
                    (const bf16*)(ws + p.o_Sst), (const bf16*)(ws + p.o_dSt),
                    (const bf16*)(ws + p.o_dDt), (bf16*)dv, (float*)(ws + p.o_dQg),

@@ -371,8 +371,8 @@ prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __r
 // each thread keeps, and r goes to rno for the backward.
 // With SAFE (clip or diag) the stage values P, A, T, U, W pass through guard();
 // the solve's diagonal is damped by sf.dinv = 1 / (1 + wy_eps) in every instance.
-// Wro, Uro (training with clip): W and U also before clipping, which the
-// backward's WY adjoint needs (clipping is differentiated as the identity).
+// Wro (training with clip): W also before clipping, which the backward's WY
+// adjoint needs (clipping is differentiated as the identity).
 // ---------------------------------------------------------------------------
 constexpr int NTHR_P = 512;
 
@@ -383,7 +383,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
              float scale, bf16* __restrict__ Wb, float* __restrict__ Uo,
              bf16* __restrict__ Qgb, bf16* __restrict__ KhTb, bf16* __restrict__ Psb,
              float* __restrict__ gamo, float* __restrict__ Tmo, float* __restrict__ rno,
-             Safety sf, bf16* __restrict__ Wro, float* __restrict__ Uro)
+             Safety sf, bf16* __restrict__ Wro)
 {
     static_assert(C == 64 && DK == DV, "prep2: chunk 64, Dk == Dv");
     constexpr int NW = NTHR_P / 64, RPP = 16, NPART = C / RPP, NB = C / 16;
@@ -850,7 +850,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         *reinterpret_cast<uint2*>(&Wb[e]) = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();  // X_V^T complete
-    // ---- U = T X_V (fp32 out; Uro, training with clip: also before clipping).
+    // ---- U = T X_V (fp32 out).
     // The tile of U^T = X_V^T T^T: a lane holds 4 consecutive columns of one U row
     constexpr int TU = NB * (DV / 16);
     float* Uc = Uo + (size_t)ch * C * DV;
@@ -859,8 +859,6 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         const int K = ((16 * (ti + 1) + 31) / 32) * 32;  // T is lower triangular
         f32x4 acc = mma_kc_dyn(zero4(), &sXV[tj * 16][0], PT, &sTb[ti * 16][0], PT, K);
         const size_t e = (size_t)(ti * 16 + lr) * DV + tj * 16 + 4 * lq;
-        if (SAFE && Uro)
-            *reinterpret_cast<float4*>(&Uro[(size_t)ch * C * DV + e]) = float4{acc[0], acc[1], acc[2], acc[3]};
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = grd(acc[r], GDN_DIAG_U);
         *reinterpret_cast<float4*>(&Uc[e]) = float4{acc[0], acc[1], acc[2], acc[3]};
@@ -2152,8 +2150,7 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
     float* Tm = want_T ? (float*)(ws + p.o_Tm) : nullptr;
     float* rn = p.l2n ? (float*)(ws + p.o_rn) : nullptr;
     const Safety sf{p.clip, p.dinv, p.diag ? (unsigned int*)(ws + p.o_dgc) : nullptr};
-    const bool raw = want_T && p.clip > 0.f;  // the training forward keeps U, W unclipped too
-    float* Uro = raw ? (float*)(ws + p.o_Ur) : nullptr;
+    const bool raw = want_T && p.clip > 0.f;  // the training forward keeps W unclipped too
     bf16* Wro = raw ? (bf16*)(ws + p.o_Wr) : nullptr;
     dim3 grid((unsigned)p.n_ch), block(NTHR);
     if constexpr (bf16_tables<TIn, C, DK>()) {
@@ -2166,7 +2163,7 @@ gdn_status run_prep(const Plan& p, const void* q, const void* k, const void* v, 
                        (prep2_kernel<C, DK, DV, decltype(pch)::value, decltype(l2n)::value,
                                      decltype(safe)::value>),
                        grid, dim3(NTHR_P), st, (const bf16*)q, (const bf16*)k, (const bf16*)v, g,
-                       beta, p.T, p.H, p.NC, p.scale, Wb, U, Qb, Kb, Pb, gam, Tm, rn, sf, Wro, Uro);
+                       beta, p.T, p.H, p.NC, p.scale, Wb, U, Qb, Kb, Pb, gam, Tm, rn, sf, Wro);
             return GDN_OK;
         };
         return with_bool(p.decay == GDN_DECAY_PER_CHANNEL, [&](auto pch) {

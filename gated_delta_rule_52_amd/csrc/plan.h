@@ -25,8 +25,8 @@
 //                     at chunk 64 (bf16 with bf16 inputs, fp32 with fp32 inputs)
 //   dbq [ch][2][C]    per channel-half partial dbeta, dgq [ch][2][C] partial
 //                     per-head dg (bf16 inputs at chunk 64)
-//   Ur  [ch][C][Dv], Wr [ch][C][Dk] (bf16): with clip, the products T X_V and
-//                     T X_K before clipping, for the WY adjoint of the bf16 path
+//   Wr  [ch][C][Dk] (bf16): with clip, the product T X_K before clipping, for
+//                     the WY adjoint of the bf16 path
 // With bf16 inputs at chunk 64, Sst, dSt, dDt and Dst are bf16 in 32-column
 // slices, [ch][Dv / 32][rows][32] (slice32 in chunk_common.h).
 // With bf16 inputs at chunk 64 the tables W, Qg, Kh, Ps are bf16, in the
@@ -55,7 +55,7 @@ struct Plan {
     size_t n_ch;  // B * H * NC
     // byte offsets into the workspace
     size_t o_W, o_U, o_Qg, o_Kh, o_Ps, o_gam, o_rn, o_dgc, o_Tm, o_Sst, o_dSt, o_dDt;
-    size_t o_dQg, o_dWg, o_dKh, o_dPs, o_dT1, o_dgm, o_dbp, o_Dst, o_dbq, o_dgq, o_Ur, o_Wr;
+    size_t o_dQg, o_dWg, o_dKh, o_dPs, o_dT1, o_dgm, o_dbp, o_Dst, o_dbq, o_dgq, o_Wr;
     size_t ws_fwd_bytes, ws_bwd_bytes;
 };
 
@@ -107,7 +107,6 @@ inline Plan make_plan(const gdn_shape& s, float scale)
     p.o_dbq = off; off = align256(off + n * 2 * C * f);
     p.o_dgq = off; off = align256(off + n * 2 * C * f);
     const bool raw = s.clip > 0.f;
-    p.o_Ur = off;  off = align256(off + (raw ? n * C * Dv * f : 0));
     p.o_Wr = off;  off = align256(off + (raw ? n * C * Dk * 2 : 0));
     p.ws_bwd_bytes = off;
     return p;

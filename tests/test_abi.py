@@ -133,10 +133,9 @@ def test_safety_options_host_checks():
     assert L.gdn_workspace_bytes(ctypes.byref(_shape(diag=1)), 0) == base + 256
     bwd = L.gdn_workspace_bytes(ctypes.byref(_shape()), 1)
     assert L.gdn_workspace_bytes(ctypes.byref(_shape(wy_eps=0.3)), 1) == bwd
-    # clip: the training forward also keeps U (fp32) and W (bf16) before clipping
+    # clip: the training forward also keeps W (bf16) before clipping
     n_ch = 2 * 3 * 2
-    assert L.gdn_workspace_bytes(ctypes.byref(_shape(clip=8.0)), 1) == \
-        bwd + n_ch * 64 * 128 * 4 + n_ch * 64 * 128 * 2
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(clip=8.0)), 1) == bwd + n_ch * 64 * 128 * 2
 
 
 def test_replay_host_checks():
