@@ -398,8 +398,12 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     __shared__ float sG[C];  // per-head decay: chunk-local inclusive cumsum of g
     __shared__ float sRn[2][L2N ? C : 1];  // L2N: 1/sqrt(|q_i|^2 + eps), same for k
     __shared__ unsigned int sdg[SAFE ? NDIAG_PREP : 1];  // SAFE: this workgroup's stage counts
-    bf16 (*sX)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf);
-    bf16 (*sY)[PA] = reinterpret_cast<bf16 (*)[PA]>(sbuf + C * PA * 2);
+    // level tables, channel-major (rows = key channels, columns = tokens; SwzT8):
+    // a column thread writes its rows of one channel as whole 16-byte units,
+    // and the score products read them with transposing loads
+    uint4* const sX = reinterpret_cast<uint4*>(sbuf);
+    uint4* const sY = reinterpret_cast<uint4*>(sbuf + DK * C * 2);
+    static_assert(2 * DK * C * 2 <= SBUF && RPP % 8 == 0, "channel-major level tables");
     float (*sT)[PC] = reinterpret_cast<float (*)[PC]>(sbuf);
     float (*sYt)[PC] = reinterpret_cast<float (*)[PC]>(sbuf + C * PC * 4);
     bf16 (*sTb)[PT] = reinterpret_cast<bf16 (*)[PT]>(&sA[0][0]);
@@ -415,6 +419,24 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     const bool bwdt = Tmo != nullptr;
     const bool cp = tid < NPART * DK;
     const int c = tid % DK, part = cp ? tid / DK : 0, p0 = part * RPP;
+    // this thread's rows of channel c in a level table (row i's value x(i)),
+    // 8 at a time
+    auto put_rows = [&](uint4* tab, auto x) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < RPP; i += 8) {
+            const uint2 lo = pack4_bf16(x(i), x(i + 1), x(i + 2), x(i + 3));
+            const uint2 hi = pack4_bf16(x(i + 4), x(i + 5), x(i + 6), x(i + 7));
+            tab[swz_slot<SwzT8>(c, (p0 + i) / 8)] = uint4{lo.x, lo.y, hi.x, hi.y};
+        }
+    };
+    // 16 x 16 score tile: rows ti*16.. of table A against rows tj*16.. of table
+    // B, summed over the DK channels
+    auto cm_prod = [&](f32x4 acc, const uint4* A, int ti, const uint4* B, int tj) {
+#pragma unroll 2
+        for (int k0 = 0; k0 < DK; k0 += 32)
+            acc = mfma_bf16_16x16x32(frag_cols<SwzT8>(A, k0, ti * 16), frag_cols<SwzT8>(B, k0, tj * 16), acc);
+        return acc;
+    };
     if (SAFE && tid < NDIAG_PREP) sdg[tid] = 0u;
     auto sd = [&](int stage) -> unsigned int* { return SAFE && sf.diag ? &sdg[2 * stage] : nullptr; };
     auto grd = [&](float x, int stage) { return SAFE ? guard(x, sf.clip, sd(stage)) : x; };
@@ -455,19 +477,16 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     }
     // level 0: unscaled rows, the diagonal P_ii = q_i . k_i
     if (cp) {
-#pragma unroll
-        for (int i = 0; i < RPP; ++i) {
-            sX[p0 + i][c] = f32_to_bf16(qv[i]);
-            sY[p0 + i][c] = f32_to_bf16(kv[i]);
-        }
+        put_rows(sX, [&](int i) { return qv[i]; });
+        put_rows(sY, [&](int i) { return kv[i]; });
     }
     __syncthreads();
     // L2N, waves w < NB: squared lengths of rows 16w.. from the raw tables
     // (published to sRn by the next barrier)
     auto row_norms = [&]() {
         if constexpr (L2N) {
-            const f32x4 nq = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sX[w * 16][0], PA);
-            const f32x4 nk = mma_kc<DK>(zero4(), &sY[w * 16][0], PA, &sY[w * 16][0], PA);
+            const f32x4 nq = cm_prod(zero4(), sX, w, sX, w);
+            const f32x4 nk = cm_prod(zero4(), sY, w, sY, w);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if (4 * lq + r == lr) {
@@ -504,8 +523,8 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         // the plain product q_i . k_j (or k_i . k_j) times it: one MFMA product
         // per 16-tile instead of the block-boundary split.
         if (w < NB) {
-            const f32x4 tp = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sY[w * 16][0], PA);
-            const f32x4 ta = mma_kc<DK>(zero4(), &sY[w * 16][0], PA, &sY[w * 16][0], PA);
+            const f32x4 tp = cm_prod(zero4(), sX, w, sY, w);
+            const f32x4 ta = cm_prod(zero4(), sY, w, sY, w);
             row_norms();
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -521,8 +540,8 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
                 if (idx < NOFF) {
                     int ti, tj;
                     off_tile(idx, ti, tj);
-                    accP[m] = mma_kc<DK>(zero4(), &sX[ti * 16][0], PA, &sY[tj * 16][0], PA);
-                    accA[m] = mma_kc<DK>(zero4(), &sY[ti * 16][0], PA, &sY[tj * 16][0], PA);
+                    accP[m] = cm_prod(zero4(), sX, ti, sY, tj);
+                    accA[m] = cm_prod(zero4(), sY, ti, sY, tj);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float e = fast_exp(sG[ti * 16 + 4 * lq + r] - sG[tj * 16 + lr]);
@@ -561,7 +580,7 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         }
     } else {
     if (w < NB) {
-        const f32x4 tp = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sY[w * 16][0], PA);
+        const f32x4 tp = cm_prod(zero4(), sX, w, sY, w);
         row_norms();
 #pragma unroll
         for (int r = 0; r < 4; ++r) dP[r] = (4 * lq + r == lr) ? tp[r] : 0.f;
@@ -622,11 +641,8 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             }
         }
         if (cp) {
-#pragma unroll
-            for (int i = 0; i < RPP; ++i) {
-                sX[p0 + i][c] = f32_to_bf16(qv[i] * F[i]);
-                sY[p0 + i][c] = f32_to_bf16(kv[i] * F[i]);
-            }
+            put_rows(sX, [&](int i) { return qv[i] * F[i]; });
+            put_rows(sY, [&](int i) { return kv[i] * F[i]; });
         }
         __syncthreads();
         if (hl >= 16) {
@@ -638,15 +654,15 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
                         int ti, tj;
                         off_tile(idx, ti, tj);
                         if (off_tile_level(ti, tj) == hl) {
-                            accP[m] = mma_kc<DK>(accP[m], &sX[ti * 16][0], PA, &sY[tj * 16][0], PA);
-                            accA[m] = mma_kc<DK>(accA[m], &sY[ti * 16][0], PA, &sY[tj * 16][0], PA);
+                            accP[m] = cm_prod(accP[m], sX, ti, sY, tj);
+                            accA[m] = cm_prod(accA[m], sY, ti, sY, tj);
                         }
                     }
                 }
             }
         } else if (w < NB) {
-            const f32x4 tp = mma_kc<DK>(zero4(), &sX[w * 16][0], PA, &sY[w * 16][0], PA);
-            const f32x4 ta = mma_kc<DK>(zero4(), &sY[w * 16][0], PA, &sY[w * 16][0], PA);
+            const f32x4 tp = cm_prod(zero4(), sX, w, sY, w);
+            const f32x4 ta = cm_prod(zero4(), sY, w, sY, w);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if (in_level(4 * lq + r, lr, hl)) {

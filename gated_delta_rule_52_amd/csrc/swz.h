@@ -38,6 +38,14 @@ struct SwzU16 {
     __device__ static int f(int r) { return r & 15; }
 };
 
+// 8 units a row, written as 16-byte units of consecutive rows (lane L: row
+// r0 + L, one unit) and read by transposing loads (frag_cols): a channel-major
+// table whose rows are channels and whose columns are tokens
+struct SwzT8 {
+    static constexpr int U = 8;
+    __device__ static int f(int r) { return (r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2); }
+};
+
 // 8 (16) units a row, read only by transposing loads in the K-permuted order
 // of kperm.h (frag_cols_kperm)
 struct SwzK8 {
