@@ -1538,6 +1538,11 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
     // saved states feed the backward's bf16 products and its decay-gradient sums)
     constexpr int PO = BV + 8;
     __shared__ __align__(16) bf16 sSf[2][DK][PO];
+    // the chunk's U slice (fp32 rows, padded so the accumulator-layout reads of
+    // four rows 4 apart hit distinct banks) and decay
+    constexpr int PU = BV + 4;
+    static_assert(C * BV / 4 == NTHR_S && DK / 4 <= NTHR_S, "one U word and at most one decay word per thread");
+    __shared__ __align__(16) float sU[C][PU], sGm[DK];
     __shared__ __align__(16) bf16 sDr[2][C][PO], sOr[2][C][PO];
 
     const int x = blockIdx.x;
@@ -1570,11 +1575,14 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
     // latency.  Fetches are unconditional (the chunk index is clamped; the tail
     // re-reads the last chunk) and the loop body is a pair of steps with the
     // sets fixed, so the waits are exact.
+    // U and the decay go through LDS too: one 16-byte word of each per thread
+    // (the decay word repeats across threads) instead of one 4-byte load per
+    // accumulator value.
     using PFW = uint4[QPT];
-    using UF = float[MD][4];
-    using GF = float[MS][4];
+    using UF = float4;
+    using GF = float4;
     uint4 pfA[QPT], pfB[QPT];
-    float upA[MD][4], upB[MD][4], gpA[MS][4], gpB[MS][4];
+    float4 upA, upB, gpA, gpB;
     auto fetch = [&](int n, PFW& pf, UF& upf, GF& gpf) {  // chunk n tables -> registers
         const size_t ch = (size_t)bh * NC + n;
 #pragma unroll
@@ -1587,28 +1595,18 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             else val = reinterpret_cast<const uint4*>(Psb + ch * C * C)[idx - 2 * QW - QK];
             pf[q] = val;
         }
-#pragma unroll
-        for (int m = 0; m < MD; ++m) {
-            const int idx = w + NW * m;  // < TD for every wave
-            {
-                const int ti = idx / (BV / 16), tj = idx % (BV / 16);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    upf[m][r] = Ui[(ch * C + ti * 16 + 4 * lq + r) * DV + v0 + tj * 16 + lr];
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < MS; ++m) {
-            const int si = (w + NW * m) / (BV / 16);  // w + NW m < TS for every wave
-#pragma unroll
-            for (int r = 0; r < 4; ++r) gpf[m][r] = gami[ch * DK + si * 16 + 4 * lq + r];
-        }
+        upf = load4<float>(Ui + (ch * C + tid / (BV / 4)) * DV + v0 + 4 * (tid % (BV / 4)));
+        gpf = load4<float>(gami + ch * DK + 4 * (tid % (DK / 4)));
     };
-    float uc[MD][4], gc[MS][4];
-    auto stash = [&](PFW& pf, UF& upf, GF& gpf) {  // registers -> LDS tables, U and gam
-        // keep the use of the prefetched words here: hoisted into the compute
-        // phase they would make it wait for the prefetch
+    // Registers -> LDS in two halves, each written while the other half's
+    // tables are read: W and Qg (read in the first phase of a step) during the
+    // second phase of the step before, Kh^T and P (read in the second phase)
+    // during the first phase, so a step needs two barriers.  Keep the use of
+    // the prefetched words inside the stashes: hoisted into the compute phase
+    // they would make it wait for the prefetch.
+    auto stash_wq = [&](PFW& pf, UF& upf) {  // W and Qg words, U
         __builtin_amdgcn_sched_barrier(0);
+        st4(&sU[tid / (BV / 4)][4 * (tid % (BV / 4))], upf);
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
             const int idx = tid + NTHR_S * q;
@@ -1617,6 +1615,15 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             } else if (q * NTHR_S < 2 * QW) {
                 const int e = idx - QW;
                 *reinterpret_cast<uint4*>(swz_at<SA>(sQ, e / (DK / 8), (e % (DK / 8)) * 8)) = pf[q];
+            }
+        }
+    };
+    auto stash_kp = [&](PFW& pf, UF& upf, GF& gpf) {  // Kh^T and P words; U and gam
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < QPT; ++q) {
+            const int idx = tid + NTHR_S * q;
+            if (q * NTHR_S < 2 * QW) {
             } else if (q * NTHR_S < 2 * QW + QK) {
                 const int e = idx - 2 * QW;
                 *reinterpret_cast<uint4*>(swz_at<SC>(sKT, e / (C / 8), (e % (C / 8)) * 8)) = pf[q];
@@ -1625,19 +1632,12 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 *reinterpret_cast<uint4*>(swz_at<SC>(sP, e / (C / 8), (e % (C / 8)) * 8)) = pf[q];
             }
         }
-#pragma unroll
-        for (int m = 0; m < MD; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) uc[m][r] = upf[m][r];
-#pragma unroll
-        for (int m = 0; m < MS; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) gc[m][r] = gpf[m][r];
+        if (tid < DK / 4) st4(&sGm[4 * tid], gpf);
     };
     fetch(0, pfA, upA, gpA);
-    stash(pfA, upA, gpA);
-    __syncthreads();
     fetch(min(1, NC - 1), pfB, upB, gpB);
+    stash_wq(pfA, upA);
+    __syncthreads();
 
     // Each step's outputs are staged in LDS and written with 16-byte stores after
     // the step's stash (issued before the wait for the prefetch, that wait would
@@ -1652,12 +1652,14 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 Sst[slice32((size_t)bh * NC, DK, DV, si * 16 + 4 * lq + r, v0 + sj * 16 + lr)] = f32_to_bf16(sacc[m][r]);
         }
     }
-    // one step: chunk n with its tables in LDS; `nx` holds chunk n + 1 (stashed
-    // at the end), `fr` is free and takes chunk n + 2
-    auto step = [&](int n, PFW& pnx, UF& unx, GF& gnx, PFW& pfr, UF& ufr, GF& gfr) {
+    // one step: chunk n, whose W, Qg and U are in LDS; `cu` holds chunk n (its
+    // Kh^T, P and decay are stashed first) and then takes chunk n + 2, `nx`
+    // holds chunk n + 1 (its W, Qg and U are stashed in the second phase)
+    auto step = [&](int n, PFW& pcu, UF& ucu, GF& gcu, PFW& pnx, UF& unx) {
         const size_t ch = (size_t)bh * NC + n;
         const int pb = n & 1;
-        fetch(min(n + 2, NC - 1), pfr, ufr, gfr);
+        stash_kp(pcu, ucu, gcu);
+        fetch(min(n + 2, NC - 1), pcu, ucu, gcu);
         // D = U - W S  and  O1 = Qg S
         f32x4 o1[MD];
 #pragma unroll
@@ -1670,7 +1672,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 ws = mfma_bf16_16x16x32(frag_rows<SA>(sW, ti * 16, u0), frag_rows<SA>(sSt, tj * 16, u0), ws);
             float dv[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dv[r] = uc[m][r] - ws[r];
+            for (int r = 0; r < 4; ++r) dv[r] = sU[ti * 16 + 4 * lq + r][tj * 16 + lr] - ws[r];
             *reinterpret_cast<uint2*>(swz_at<SC>(sDt, tj * 16 + lr, ti * 16 + 4 * lq)) = pack4_bf16(dv[0], dv[1], dv[2], dv[3]);
             if (SAVE) {  // staged as 32-bit words of column pairs
                 const uint2 wd = acc_colpairs(f32x4{dv[0], dv[1], dv[2], dv[3]});
@@ -1686,6 +1688,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             }
         }
         __syncthreads();
+        stash_wq(pnx, unx);  // chunk n + 1 (at the last step a harmless repeat)
         if (OUT) {
 #pragma unroll
             for (int m = 0; m < MD; ++m) {
@@ -1707,9 +1710,10 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
         for (int m = 0; m < MS; ++m) {
             const int idx = w + NW * m;
             const int si = idx / (BV / 16), sj = idx % (BV / 16);
+            const f32x4 gv = *reinterpret_cast<const f32x4*>(&sGm[si * 16 + 4 * lq]);
             f32x4 acc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = gc[m][r] * sacc[m][r];
+            for (int r = 0; r < 4; ++r) acc[r] = gv[r] * sacc[m][r];
 #pragma unroll
             for (int u0 = 0; u0 < C / 8; u0 += 4)
                 acc = mfma_bf16_16x16x32(frag_rows<SC>(sKT, si * 16, u0), frag_rows<SC>(sDt, sj * 16, u0), acc);
@@ -1723,8 +1727,6 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
                 *reinterpret_cast<uint32_t*>(&sSf[pb][i2 + 1][j2]) = wsf.y;
             }
         }
-        __syncthreads();
-        stash(pnx, unx, gnx);  // chunk n + 1 (at the last step a harmless repeat)
         __syncthreads();
         // this step's stores, from the staging: the start state of chunk n + 1,
         // then D and o of chunk n (rows of BV contiguous elements)
@@ -1759,10 +1761,10 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
     };
     int n = 0;
     for (; n + 1 < NC; n += 2) {
-        step(n, pfB, upB, gpB, pfA, upA, gpA);
-        step(n + 1, pfA, upA, gpA, pfB, upB, gpB);
+        step(n, pfA, upA, gpA, pfB, upB);
+        step(n + 1, pfB, upB, gpB, pfA, upA);
     }
-    if (n < NC) step(n, pfB, upB, gpB, pfA, upA, gpA);
+    if (n < NC) step(n, pfA, upA, gpA, pfB, upB);
     if (hT) {
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
