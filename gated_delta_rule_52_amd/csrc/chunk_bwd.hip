@@ -991,11 +991,12 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     constexpr int T3 = NB * (DK / 16), M3 = (T3 + NW - 1) / NW;
     constexpr int T2 = NB * NB, M2 = (T2 + NW - 1) / NW;
     constexpr int TD = NB * (BW / 16), MD = (TD + NW - 1) / NW;
-    constexpr int NS4 = DK * BW / 4;                 // float4 words of an S tile
-    constexpr int QS = (NS4 + NTHR_C - 1) / NTHR_C;  // per thread
+    constexpr int SWE = DK * BW / NTHR_C;            // bf16 of an S (dS) tile per thread: 8 or 4
+    constexpr int SPR = BW / SWE;                    // threads per S row
+    using SWord = std::conditional_t<SWE == 8, uint4, uint2>;
+    static_assert(SWE * NTHR_C == DK * BW && (SWE == 8 || SWE == 4), "one S word and one dS word per thread");
     constexpr int NB8 = C * BW / 8;                  // uint4 words of a bf16 [C][BW] tile
-    constexpr int ND4 = C * BW / 4;                  // float4 words of dD
-    static_assert(NB8 <= NTHR_C / 2 && ND4 <= NTHR_C, "tile split assumes C*BW <= 2048");
+    static_assert(NB8 == NTHR_C / 2, "two [C][BW] words per thread");
     // Dv-streaming tiles, and after the Dv loop the key WY-adjoint tables, share
     // sbuf.  bf16 tables are swizzled rows (swz.h): the [rows][BW] tiles SwzU4,
     // dW^T [DK][C] SwzU8w, W and dX_K [C][DK] SwK; T [C][C] (SwzU8) is read
@@ -1028,8 +1029,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     char* const sW = sbuf + O_W;
     char* const sXh = sbuf + O_Xh;  // dX_K, high part
     char* const sXl = sbuf + O_Xl;  // dX_K, low part
-    // 4 (8) bf16 at column c of row r of a [rows][BW] tile
-    auto at4 = [](char* t, int r, int c) { return reinterpret_cast<uint2*>(swz_at<SwzU4>(t, r, c)); };
+    // 8 bf16 at column c of row r of a [rows][BW] tile
     auto at8 = [](char* t, int r, int c) { return reinterpret_cast<uint4*>(swz_at<SwzU4>(t, r, c)); };
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -1050,16 +1050,16 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     bool row8;
 
     // Prefetch of one Dv tile, branch-free (a load under a divergent branch makes
-    // the compiler wait for it where the branches join): every thread loads two
-    // S words, two dS words, one dD word, one D-or-dO word and one v word; rows
-    // past the end are clamped on load and zeroed in stash().
-    static_assert(NS4 == QS * NTHR_C && ND4 == NTHR_C && NB8 == NTHR_C / 2, "tile split");
-    uint2 pS[QS], pdS[QS], pdD;  // four bf16 values each
-    uint4 pa, pb;  // threads < NB8: D and v words; threads >= NB8: dO word (and an unused v word)
+    // the compiler wait for it where the branches join): every thread loads one
+    // S word and one dS word (the same elements), and two 16-byte words of the
+    // [C][BW] tiles: threads < NB8 a D word and a v word, the others a dO word
+    // and a dD word; rows past the end are clamped on load and zeroed in stash().
+    SWord pS, pdS;
+    uint4 pa, pb;
     const bool lowh = tid < NB8;
     const int e8 = lowh ? tid : tid - NB8;
     const int r8 = e8 / (BW / 8), j8 = (e8 % (BW / 8)) * 8;
-    const int rd = tid / (BW / 4), jd = (tid % (BW / 4)) * 4;  // dD word of this thread
+    const int rs = tid / SPR, js = (tid % SPR) * SWE;  // S (dS) row and first column of this thread
     auto fetch_from = [&](int c) {
         int nv;
         size_t tk;
@@ -1074,39 +1074,29 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         return tk + (size_t)min(tid % C, nv - 1) * H;  // this thread's beta token
     };
     auto fetch = [&](int v0) {
-#pragma unroll
-        for (int q = 0; q < QS; ++q) {
-            const int idx = tid + NTHR_C * q;
-            const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
-            pS[q] = *reinterpret_cast<const uint2*>(Sp + v0 * DK + i * BW + j4);
-            pdS[q] = *reinterpret_cast<const uint2*>(dSp + v0 * DK + i * BW + j4);
-        }
-        pdD = *reinterpret_cast<const uint2*>(dDp + v0 * C + rd * BW + jd);
+        pS = *reinterpret_cast<const SWord*>(Sp + v0 * DK + rs * BW + js);
+        pdS = *reinterpret_cast<const SWord*>(dSp + v0 * DK + rs * BW + js);
         const bf16* src = lowh ? Dp + v0 * C + r8 * BW + j8 : dO + tokr + v0 + j8;
         pa = *reinterpret_cast<const uint4*>(src);
-        pb = *reinterpret_cast<const uint4*>(v + tokr + v0 + j8);
+        const bf16* srcb = lowh ? v + tokr + v0 + j8 : dDp + v0 * C + r8 * BW + j8;
+        pb = *reinterpret_cast<const uint4*>(srcb);
     };
-    float dgm_part[QS];
-#pragma unroll
-    for (int q = 0; q < QS; ++q) dgm_part[q] = 0.f;
+    float dgm_part = 0.f;
     auto stash = [&]() {
         // keep the use of the prefetched words here: hoisted into the compute
         // phase they would make it wait for the prefetch
         __builtin_amdgcn_sched_barrier(0);
+        {
+            constexpr int NWD = SWE / 2;  // 32-bit words of a thread's S word
+            const uint32_t* sw = reinterpret_cast<const uint32_t*>(&pS);
+            const uint32_t* dw = reinterpret_cast<const uint32_t*>(&pdS);
 #pragma unroll
-        for (int q = 0; q < QS; ++q) {
-            const int idx = tid + NTHR_C * q;
-            const int i = idx / (BW / 4), j4 = (idx % (BW / 4)) * 4;
-            const uint2 s2 = pS[q], d2 = pdS[q];
-            const float ax = __uint_as_float(s2.x << 16), ay = __uint_as_float(s2.x & 0xFFFF0000u);
-            const float az = __uint_as_float(s2.y << 16), aw = __uint_as_float(s2.y & 0xFFFF0000u);
-            const float dx = __uint_as_float(d2.x << 16), dy = __uint_as_float(d2.x & 0xFFFF0000u);
-            const float dz = __uint_as_float(d2.y << 16), dw = __uint_as_float(d2.y & 0xFFFF0000u);
-            dgm_part[q] += ax * dx + ay * dy + az * dz + aw * dw;
-            *at4(sS, i, j4) = s2;
-            *at4(sdS, i, j4) = d2;
+            for (int z = 0; z < NWD; ++z)
+                dgm_part += __uint_as_float(sw[z] << 16) * __uint_as_float(dw[z] << 16) +
+                            __uint_as_float(sw[z] & 0xFFFF0000u) * __uint_as_float(dw[z] & 0xFFFF0000u);
+            *reinterpret_cast<SWord*>(swz_at<SwzU4>(sS, rs, js)) = pS;
+            *reinterpret_cast<SWord*>(swz_at<SwzU4>(sdS, rs, js)) = pdS;
         }
-        *at4(sdD, rd, jd) = pdD;
         if (lowh) {
             *at8(sD, r8, j8) = pa;
             const uint4 vb = row8 ? pb : uint4{0u, 0u, 0u, 0u};
@@ -1122,6 +1112,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             st4(&sv[r8][j8 + 4], float4{vv[4], vv[5], vv[6], vv[7]});
         } else {
             *at8(sdO, r8, j8) = row8 ? pa : uint4{0u, 0u, 0u, 0u};
+            *at8(sdD, r8, j8) = pb;
         }
     };
 
@@ -1153,7 +1144,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // counter completes in issue order)
     constexpr int NX8 = (C * DK / 8 + NTHR_C - 1) / NTHR_C;
     u32x4 oX[NX8];
-    float oA[M2][4], oG[QS], oB;
+    float oA[M2][4], oG, oB;
     int pch = -1;
     auto put_tail = [&]() {
         bf16* dXp = reinterpret_cast<bf16*>(dWgo) + (size_t)pch * C * DK;
@@ -1174,11 +1165,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 *reinterpret_cast<uint32_t*>(&dAp[(i2 + 1) * C + j2]) = wa.y;
             }
         }
-#pragma unroll
-        for (int q = 0; q < QS; ++q) {
-            const int idx = tid + NTHR_C * q;
-            if (idx < NS4 && (idx % (BW / 4)) == 0) dgmo[(size_t)pch * DK + idx / (BW / 4)] = oG[q];
-        }
+        if (tid % SPR == 0) dgmo[(size_t)pch * DK + rs] = oG;
         if (tid < C) dbpo[(size_t)pch * C + tid] = oB;
     };
 
@@ -1186,8 +1173,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     for (int ch = blockIdx.x;;) {
         geo(ch, nvalid, tok0);
         row8 = r8 < nvalid;
-#pragma unroll
-        for (int q = 0; q < QS; ++q) dgm_part[q] = 0.f;
+        dgm_part = 0.f;
         f32x4 aQ[M3], aW[M3], aK[M3], aP[M2], aT[M2];
 #pragma unroll
         for (int m = 0; m < M3; ++m) aQ[m] = aW[m] = aK[m] = zero4();
@@ -1442,10 +1428,10 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                 }
             }
         }
-        // dgam: the BW/4 threads of one state row hold its partial sums
-        static_assert(BW / 4 == 8, "eight threads per state row");
-#pragma unroll
-        for (int q = 0; q < QS; ++q) oG[q] = lane8_sum(dgm_part[q]);
+        // dgam: the SPR threads of one state row (aligned lanes) hold its partial sums
+        static_assert(SPR == 4 || SPR == 8, "four or eight threads per state row");
+        if constexpr (SPR == 4) oG = lane4_sum(dgm_part);
+        else oG = lane8_sum(dgm_part);
         // dbeta part: row sums of dX_V o v over the 16 columns of each tile, then
         // over the column tiles (fixed order)
         for (int idx = tid; idx < NW * C; idx += NTHR_C) (&sred[0][0])[idx] = 0.f;

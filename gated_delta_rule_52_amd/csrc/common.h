@@ -68,6 +68,13 @@ template <int CTRL> __device__ __forceinline__ float dpp_mov(float x)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
+// sum over aligned groups of 4 lanes: neighbour swap, pair swap
+__device__ __forceinline__ float lane4_sum(float x)
+{
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    return x;
+}
 // sum over aligned groups of 8 lanes: neighbour swap, pair swap, mirror in 8
 __device__ __forceinline__ float lane8_sum(float x)
 {
