@@ -388,7 +388,7 @@ bscan4_kernel(const bf16* __restrict__ KhTp, const bf16* __restrict__ Psp,
     constexpr int NT = DK / 16, KB = DK / 32;
     constexpr int WK = DK / 8, WC = C / 8;
     // a buffer in 16-byte words: Kh^T [DK][WC], Ps [C][WC] (SwzK8), Qg [C][WK],
-    // W [C][WK] (SK), the dO slice [C][BV] bf16 (plain), the decay
+    // W [C][WK] (SK), the dO slice [C][BV] bf16 (SwzK4), the decay
     using SK = std::conditional_t<DK == 128, SwzK16, SwzK8>;
     static_assert(WC == SwzK8::U && WK == SK::U, "row widths of the swizzles");
     constexpr int OKh = 0, OPs = OKh + DK * WC, OQg = OPs + C * WC, OW = OQg + C * WK;
@@ -447,12 +447,12 @@ bscan4_kernel(const bf16* __restrict__ KhTp, const bf16* __restrict__ Psp,
             dma16(tab + (r * wpr + wd) * 8, buf + s0 + 64 * lw);
         }
         // dO rows of the chunk (rows past T repeat the last one: their P^T and
-        // Qg^T columns are zero)
+        // Qg^T columns are zero); slot (r, ws) holds the row's unit ws ^ f(r)
 #pragma unroll
         for (int q = 0; q < NQO; ++q) {
             const int su = q * NL + lt, r = su / (BV / 8);
             const int t = min(n * C + r, T - 1);
-            dma16(dO + (((size_t)b * T + t) * H + h) * DV + v0 + 8 * (su % (BV / 8)),
+            dma16(dO + (((size_t)b * T + t) * H + h) * DV + v0 + 8 * ((su % (BV / 8)) ^ SwzK4::f(r)),
                   buf + OdO + q * NL + 64 * lw);
         }
     };
@@ -482,7 +482,6 @@ bscan4_kernel(const bf16* __restrict__ KhTp, const bf16* __restrict__ Psp,
 
     auto compute = [&](int n, const uint4* tb) __attribute__((always_inline)) {
         const size_t ch = (size_t)bh * NC + n;
-        const uint16_t* tO = reinterpret_cast<const uint16_t*>(tb + OdO);
         const f32x4* tG = reinterpret_cast<const f32x4*>(tb + OG);
         bf16x8 dsb[KB];  // dS' (the chunk's end) as operand fragments
 #pragma unroll
@@ -493,20 +492,11 @@ bscan4_kernel(const bf16* __restrict__ KhTp, const bf16* __restrict__ Psp,
             *reinterpret_cast<uint2*>(&dSt[slice32(ch, DK, DV, 16 * t + ln, vc + 4 * lg)]) =
                 pack4_bf16(tr[0], tr[1], tr[2], tr[3]);
         }
-        // dO as the operand with K along tokens: slot e of lane group lg is token
-        // 32 kb + 4 lg + e (e < 4) or 32 kb + 16 + 4 lg + e - 4
+        // dO as the operand with K along tokens (in the K order of kperm.h),
+        // this wave's 16 columns
         bf16x8 dob[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            u32x4 wv;
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const int t0 = 32 * kb + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
-                wv[e / 2] = (uint32_t)tO[t0 * BV + 16 * lw + ln] |
-                            ((uint32_t)tO[(t0 + 1) * BV + 16 * lw + ln] << 16);
-            }
-            dob[kb] = __builtin_bit_cast(bf16x8, wv);
-        }
+        for (int kb = 0; kb < 2; ++kb) dob[kb] = frag_cols_kperm<SwzK4>(tb + OdO, 32 * kb, 16 * lw);
         // dD = Kh dS' + P^T dO (the fragments of a product are read before its
         // MFMAs: one wave per SIMD has no other wave to cover the LDS latency)
         bf16x8 kf[KB][4], pf[4][2];

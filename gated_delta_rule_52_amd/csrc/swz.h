@@ -46,6 +46,13 @@ struct SwzT8 {
     __device__ static int f(int r) { return (r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2); }
 };
 
+// 4 units a row, read only by transposing loads in the K-permuted order
+// (frag_cols_kperm): rows r and r + 4 of a load phase take different unit pairs
+struct SwzK4 {
+    static constexpr int U = 4;
+    __device__ static int f(int r) { return ((r >> 2) & 1) << 1; }
+};
+
 // 8 (16) units a row, read only by transposing loads in the K-permuted order
 // of kperm.h (frag_cols_kperm)
 struct SwzK8 {
