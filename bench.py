@@ -326,6 +326,23 @@ def graph_replay(fn, outs, args):
     return {"ms_per_step": ms, "replays_equal_eager_bitwise": bool(same)}
 
 
+def graph_entry(fn, outs, args, tokens):
+    """graph_replay of a variant's training pair, with its token rate, or None
+    under --no-graph"""
+    if args.no_graph:
+        return None
+    res = graph_replay(fn, outs, args)
+    res["tokens_per_s"] = tokens / (res["ms_per_step"] * 1e-3)
+    return res
+
+
+def graph_note(gr):
+    if not gr:
+        return ""
+    return (f"; graph replay {gr['ms_per_step']:.3f} ms "
+            f"(replays equal eager: {gr['replays_equal_eager_bitwise']})")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -578,19 +595,21 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         vfms = ev0.elapsed_time(ev1) / args.steps
+        vgraph = graph_entry(vstep, (vo, vhT) + vgout, args, vB * T)
         vin_bytes = 2 if vdt == "bf16" else 4
         vdom = max(vker, key=vker.get)
         res = {"workload": f"{label}: per-channel decay, B={vB} T={T} H={H} Dk=Dv={D}, chunk {C}, "
                            f"{vdt} q/k/v, fp32 state; eager library calls",
                "fwdbwd_tokens_per_s": vB * T / (vms * 1e-3), "ms_per_step": vms,
                "fwd_tokens_per_s": vB * T / (vfms * 1e-3), "fwd_ms": vfms,
-               "kernels_avg_us": vker,
+               "graph_replay": vgraph, "kernels_avg_us": vker,
                "dominant_kernel_roofline": dict(roofline(vdom, vker[vdom] * 1e-6, vB, T, H, C, D,
                                                          vin_bytes), kernel=vdom),
                "step_roofline": step_roofline(vms, vB, T, H, C, D, vin_bytes),
                "fwd_roofline": step_roofline(vfms, vB, T, H, C, D, vin_bytes, backward=False),
                "parity_max_rel_err": vpar, "parity_ok": all(e <= vtol for e in vpar.values())}
-        log(f"[bench] {label}: fwd+bwd {vms:.3f} ms, fwd {vfms:.3f} ms, parity ok {res['parity_ok']}")
+        log(f"[bench] {label}: fwd+bwd {vms:.3f} ms, fwd {vfms:.3f} ms, parity ok {res['parity_ok']}"
+            + graph_note(vgraph))
         del vws_f, vws_b
         return res
 
@@ -650,14 +669,17 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         hfwd = ev0.elapsed_time(ev1) / args.steps
+        hgraph = graph_entry(hstep, (o, hT) + hgout, args, B * T)
         head = {"workload": f"per-head decay (g [B,T,H]), otherwise as above",
                 "fwdbwd_tokens_per_s": B * T / (hms * 1e-3), "ms_per_step": hms,
+                "graph_replay": hgraph,
                 "fwd_tokens_per_s": B * T / (hfwd * 1e-3), "fwd_ms": hfwd,
                 "kernels_avg_us": hker, "parity_max_rel_err": hpar,
                 "parity_ok": all(e <= tol for e in hpar.values())}
         checks["per-head decay"] = head["parity_ok"]
         log(f"[bench] per-head: fwd+bwd {hms:.3f} ms ({head['fwdbwd_tokens_per_s'] / 1e6:.2f} M tokens/s), "
-            f"fwd {hfwd:.3f} ms; parity " + ", ".join(f"{k_} {e:.1e}" for k_, e in hpar.items()))
+            f"fwd {hfwd:.3f} ms; parity " + ", ".join(f"{k_} {e:.1e}" for k_, e in hpar.items())
+            + graph_note(hgraph))
         log("[bench] per-head kernels: " + ", ".join(f"{n} {u:.0f} us" for n, u in hker.items()))
 
     # ---- use_qk_l2norm: raw q, k rows normalised inside the layer, same shape
@@ -711,15 +733,17 @@ def main():
         torch.cuda.synchronize()
         lfwd = ev0.elapsed_time(ev1) / args.steps
         lroof = roofline("l2norm_bwd", lker["l2norm_bwd"] * 1e-6, B, T, H, C, D, in_bytes)
+        lgraph = graph_entry(lstep, (o, hT) + tuple(gout), args, B * T)
         l2 = {"workload": "use_qk_l2norm: raw q, k rows (N(0,1) times a log-normal length per "
                           "row), normalised inside the layer; otherwise as above",
               "fwdbwd_tokens_per_s": B * T / (lms * 1e-3), "ms_per_step": lms,
-              "fwd_tokens_per_s": B * T / (lfwd * 1e-3), "fwd_ms": lfwd,
+              "fwd_tokens_per_s": B * T / (lfwd * 1e-3), "fwd_ms": lfwd, "graph_replay": lgraph,
               "kernels_avg_us": lker, "l2norm_bwd_frac_hbm_peak": lroof["frac"],
               "parity_max_rel_err": lpar, "parity_ok": all(e <= tol for e in lpar.values())}
         checks["use_qk_l2norm"] = l2["parity_ok"]
         log(f"[bench] use_qk_l2norm: fwd+bwd {lms:.3f} ms ({l2['fwdbwd_tokens_per_s'] / 1e6:.2f} M tokens/s), "
-            f"fwd {lfwd:.3f} ms; parity " + ", ".join(f"{k_} {e:.1e}" for k_, e in lpar.items()))
+            f"fwd {lfwd:.3f} ms; parity " + ", ".join(f"{k_} {e:.1e}" for k_, e in lpar.items())
+            + graph_note(lgraph))
         log("[bench] use_qk_l2norm kernels: " + ", ".join(f"{n} {u:.0f} us" for n, u in lker.items())
             + f"; l2norm_bwd at {100 * lroof['frac']:.1f}% of HBM peak")
 
@@ -760,14 +784,16 @@ def main():
         sker = {n: float(np.mean(ms)) * 1e3 for n, ms in srec.by_kernel().items()}
         scnt = {n: len(ms) // args.steps for n, ms in srec.by_kernel().items()}
         srec.close()
+        sgraph = graph_entry(sstep, (o, hT) + tuple(gout), args, B * T)
         safety = {"workload": "main workload with wy_eps=1e-3, clip=1e4, diag on (training pair)",
                   "fwdbwd_tokens_per_s": B * T / (sms * 1e-3), "ms_per_step": sms,
+                  "graph_replay": sgraph,
                   "kernels_avg_us": sker, "launches_per_step": scnt, "diag_counts": counts,
                   "parity_max_rel_err_fwd": spar, "parity_ok": all(e <= tol for e in spar.values())}
         checks["safety options"] = safety["parity_ok"]
         log(f"[bench] safety options: fwd+bwd {sms:.3f} ms ({safety['fwdbwd_tokens_per_s'] / 1e6:.2f} M tokens/s); "
             f"fwd parity vs chunked oracle " + ", ".join(f"{k_} {e:.1e}" for k_, e in spar.items())
-            + f"; counts {counts}")
+            + f"; counts {counts}" + graph_note(sgraph))
         log("[bench] safety kernels: " + ", ".join(f"{n} {u:.0f} us x{scnt[n]}" for n, u in sker.items()))
 
     # ---- decode: B=256 H=16 128x128 fp32 state, one token per step
