@@ -1006,6 +1006,10 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // Dv loop and dX_K = T^T dW after it; built once from the loaded T
     __shared__ __align__(16) uint4 sTh[C * C / 8], sTl[C * C / 8];
     __shared__ __align__(16) bf16 sDV[C][DV + 8];  // dv, written out after the Dv loop
+    // dA of the previous chunk-head, staged from its accumulator tiles (32-bit
+    // words of column pairs) until its rows are stored whole, 16 bytes a thread
+    __shared__ __align__(16) bf16 sdA[C][C + 8];
+    static_assert(C * C / 8 == NTHR_C, "one 16-byte dA word per thread");
     __shared__ float sbeta[C], sred[NW][C];
     char* const sS = sbuf;
     char* const sdS = sbuf + O_dS;
@@ -1134,7 +1138,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // counter completes in issue order)
     constexpr int NX8 = (C * DK / 8 + NTHR_C - 1) / NTHR_C;
     u32x4 oX[NX8];
-    float oA[M2][4], oG, oB;
+    float oG, oB;
     int pch = -1;
     auto put_tail = [&]() {
         bf16* dXp = reinterpret_cast<bf16*>(dWgo) + (size_t)pch * C * DK;
@@ -1144,16 +1148,9 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
             if (idx < C * DK / 8) *reinterpret_cast<u32x4*>(dXp + idx * 8) = oX[u];
         }
         bf16* dAp = reinterpret_cast<bf16*>(dT1o) + (size_t)pch * C * C;
-#pragma unroll
-        for (int m = 0; m < M2; ++m) {
-            const int idx = w + NW * m;
-            if (idx < T2) {
-                const int ti = idx / NB, tj = idx % NB;
-                const uint2 wa = acc_colpairs(f32x4{oA[m][0], oA[m][1], oA[m][2], oA[m][3]});
-                const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
-                *reinterpret_cast<uint32_t*>(&dAp[i2 * C + j2]) = wa.x;
-                *reinterpret_cast<uint32_t*>(&dAp[(i2 + 1) * C + j2]) = wa.y;
-            }
+        {
+            const int r = tid / (C / 8), c8 = (tid % (C / 8)) * 8;
+            *reinterpret_cast<uint4*>(&dAp[r * C + c8]) = *reinterpret_cast<const uint4*>(&sdA[r][c8]);
         }
         if (tid % SPR == 0) dgmo[(size_t)pch * DK + rs] = oG;
         if (tid < C) dbpo[(size_t)pch * C + tid] = oB;
@@ -1411,11 +1408,16 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
                         acc = mfma_bf16_16x16x32(frag_rows<SwK>(sXl, ti * 16, u0), bw, acc);
                     }
                 }
+                f32x4 da;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
-                    oA[m][r] = i > j ? -acc[r] : 0.f;
+                    da[r] = i > j ? -acc[r] : 0.f;
                 }
+                const uint2 wa = acc_colpairs(da);
+                const int i2 = ti * 16 + 4 * lq + 2 * (lr & 1), j2 = tj * 16 + (lr & ~1);
+                *reinterpret_cast<uint32_t*>(&sdA[i2][j2]) = wa.x;
+                *reinterpret_cast<uint32_t*>(&sdA[i2 + 1][j2]) = wa.y;
             }
         }
         // dgam: the SPR threads of one state row (aligned lanes) hold its partial sums
