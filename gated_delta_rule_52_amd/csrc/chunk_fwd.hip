@@ -393,7 +393,9 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     constexpr int SBUF = cmax(2 * C * PA * 2, 2 * C * PC * 4);
     __shared__ __align__(16) char sbuf[SBUF];
     __shared__ __align__(16) float sA[C][PC];  // A (beta rows), strictly lower; later T in bf16
-    __shared__ __align__(16) bf16 sXT[DK][PT];  // X_K^T
+    // X_K^T, channel rows (SwzR8): a column thread writes its rows of one
+    // channel as two 16-byte units, the W product reads 16-byte row fragments
+    __shared__ __align__(16) uint4 sXT[DK * C / 8];
     __shared__ float sbeta[C], stot[NPART][DK];
     __shared__ float sG[C];  // per-head decay: chunk-local inclusive cumsum of g
     __shared__ float sRn[2][L2N ? C : 1];  // L2N: 1/sqrt(|q_i|^2 + eps), same for k
@@ -406,7 +408,9 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     static_assert(2 * DK * C * 2 <= SBUF && RPP % 8 == 0, "channel-major level tables");
     float (*sT)[PC] = reinterpret_cast<float (*)[PC]>(sbuf);
     float (*sYt)[PC] = reinterpret_cast<float (*)[PC]>(sbuf + C * PC * 4);
-    bf16 (*sTb)[PT] = reinterpret_cast<bf16 (*)[PT]>(&sA[0][0]);
+    // T in bf16 over sA once T is formed (SwzR8 rows; 16-byte row-fragment reads)
+    uint4* const sTb = reinterpret_cast<uint4*>(&sA[0][0]);
+    static_assert(C * C * 2 <= (int)sizeof(sA), "bf16 T fits sA");
 
     const int ch = blockIdx.x;
     const int n = ch % NC, bh = ch / NC, h = bh % H, b = bh / H;
@@ -779,8 +783,11 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             *reinterpret_cast<uint4*>(&KhTc[c * C + p0 + i]) = uint4{k0.x, k0.y, k1.x, k1.y};
         }
 #pragma unroll
-        for (int i = 0; i < RPP; i += 4)
-            *reinterpret_cast<uint2*>(&sXT[c][p0 + i]) = pack4_bf16(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
+        for (int i = 0; i < RPP; i += 8) {
+            const uint2 lo = pack4_bf16(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
+            const uint2 hi = pack4_bf16(xk[i + 4], xk[i + 5], xk[i + 6], xk[i + 7]);
+            sXT[swz_slot<SwzR8>(c, (p0 + i) / 8)] = uint4{lo.x, lo.y, hi.x, hi.y};
+        }
     }
     __syncthreads();  // staged rows complete
     for (int idx = tid; idx < C * DK / 8; idx += NTHR_P) {
@@ -835,22 +842,24 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
         for (int e = 0; e < 4; ++e) tv[e] = grd(sT[i][j + e], GDN_DIAG_T);
         if (bwdt) *reinterpret_cast<float4*>(&Tmo[(size_t)ch * C * C + i * C + j]) = float4{tv[0], tv[1], tv[2], tv[3]};
-        *reinterpret_cast<uint2*>(&sTb[i][j]) = pack4_bf16(tv[0], tv[1], tv[2], tv[3]);
+        *reinterpret_cast<uint2*>(swz_at<SwzR8>(sTb, i, j)) = pack4_bf16(tv[0], tv[1], tv[2], tv[3]);
     }
     __syncthreads();
-    // X_V^T = (beta V)^T into the level-table bytes (free now that T is in sTb)
-    bf16 (*sXV)[PT] = reinterpret_cast<bf16 (*)[PT]>(sbuf);
-    static_assert(DV * PT * 2 <= SBUF, "X_V^T fits the level-table bytes");
+    // X_V = beta V (token rows) into the level-table bytes (free now that T is
+    // in sTb), one 16-byte word per store; the U product reads it transposed
+    using SXV = std::conditional_t<DV == 128, SwzV16, SwzT8>;
+    static_assert(SXV::U * 8 == DV && C * DV * 2 <= SBUF, "X_V fits the level-table bytes");
+    uint4* const sXV = reinterpret_cast<uint4*>(sbuf);
 #pragma unroll
     for (int u = 0; u < QV; ++u) {
         const int idx = tid + NTHR_P * u, r = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
         const float bt = sbeta[r];
         const uint32_t wd[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
+        uint32_t xw[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sXV[j0 + 2 * e][r] = f32_to_bf16(bt * __uint_as_float(wd[e] << 16));
-            sXV[j0 + 2 * e + 1][r] = f32_to_bf16(bt * __uint_as_float(wd[e] & 0xFFFF0000u));
-        }
+        for (int e = 0; e < 4; ++e)
+            xw[e] = cvt2_bf16(bt * __uint_as_float(wd[e] << 16), bt * __uint_as_float(wd[e] & 0xFFFF0000u));
+        sXV[swz_slot<SXV>(r, j0 / 8)] = uint4{xw[0], xw[1], xw[2], xw[3]};
     }
     // ---- W = T X_K (bf16 out).  The tile of W^T = X_K^T T^T: a lane holds 4
     // consecutive columns of one W row, one 8-byte store
@@ -858,7 +867,9 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     for (int idx = w; idx < TW; idx += NW) {
         const int ti = idx / (DK / 16), tj = idx % (DK / 16);
         const int K = ((16 * (ti + 1) + 31) / 32) * 32;  // T is lower triangular
-        f32x4 acc = mma_kc_dyn(zero4(), &sXT[tj * 16][0], PT, &sTb[ti * 16][0], PT, K);
+        f32x4 acc = zero4();
+        for (int k0 = 0; k0 < K; k0 += 32)
+            acc = mfma_bf16_16x16x32(frag_rows<SwzR8>(sXT, tj * 16, k0 / 8), frag_rows<SwzR8>(sTb, ti * 16, k0 / 8), acc);
         const size_t e = (size_t)ch * C * DK + (ti * 16 + lr) * DK + tj * 16 + 4 * lq;
         if (SAFE && Wro) *reinterpret_cast<uint2*>(&Wro[e]) = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
 #pragma unroll
@@ -873,7 +884,9 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     for (int idx = w; idx < TU; idx += NW) {
         const int ti = idx / (DV / 16), tj = idx % (DV / 16);
         const int K = ((16 * (ti + 1) + 31) / 32) * 32;  // T is lower triangular
-        f32x4 acc = mma_kc_dyn(zero4(), &sXV[tj * 16][0], PT, &sTb[ti * 16][0], PT, K);
+        f32x4 acc = zero4();
+        for (int k0 = 0; k0 < K; k0 += 32)
+            acc = mfma_bf16_16x16x32(frag_cols<SXV>(sXV, k0, tj * 16), frag_rows<SwzR8>(sTb, ti * 16, k0 / 8), acc);
         const size_t e = (size_t)(ti * 16 + lr) * DV + tj * 16 + 4 * lq;
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = grd(acc[r], GDN_DIAG_U);

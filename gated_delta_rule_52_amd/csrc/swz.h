@@ -39,6 +39,19 @@ struct SwzU16 {
 };
 
 // 8 units a row, written as 16-byte units of consecutive rows (lane L: row
+// r0 + L, one unit) and read as 16-byte row fragments (frag_rows)
+struct SwzR8 {
+    static constexpr int U = 8;
+    __device__ static int f(int r) { return r & 7; }
+};
+// 16 units a row, written as whole rows of 16-byte words and read by
+// transposing loads (frag_cols)
+struct SwzV16 {
+    static constexpr int U = 16;
+    __device__ static int f(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
+};
+
+// 8 units a row, written as 16-byte units of consecutive rows (lane L: row
 // r0 + L, one unit) and read by transposing loads (frag_cols): a channel-major
 // table whose rows are channels and whose columns are tokens
 struct SwzT8 {
