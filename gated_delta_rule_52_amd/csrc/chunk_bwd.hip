@@ -1913,10 +1913,11 @@ constexpr int bchunk2c_threads()
 }
 
 // Channel-major bf16 tables of bchunk2c (a channel's C = 64 token rows as eight
-// 16-byte slots of 8 rows): slot s of channel ch sits at ch * 8 + (s ^ ((ch >> 1)
-// & 7)), so the 16 channels of an MFMA B fragment read 16 distinct 16-byte bank
-// groups, and the 16 threads of a part writing their slots do too.
-__device__ __forceinline__ int ctab_slot(int ch, int s) { return ch * 8 + (s ^ ((ch >> 1) & 7)); }
+// 16-byte slots of 8 rows): slot s of channel ch sits at ch * 8 + (s ^ (ch & 7)),
+// so both the B fragments (16 channels, one or two slots) and the slot writes of
+// a part (consecutive channels, one slot) meet no bank conflict under the
+// measured LDS phase rules (swz.h).
+__device__ __forceinline__ int ctab_slot(int ch, int s) { return ch * 8 + (s ^ (ch & 7)); }
 
 // B fragment of a channel-major table: lane (r, kk) supplies 8-row slot
 // slot0 + kk of channel ch0 + r; HALF (K = 16): lanes kk >= 2 supply zeros and
@@ -1958,8 +1959,11 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     //  results.
     static_assert(C == 8 * 8, "score rows and channel-major tables of eight 16-byte units");
     constexpr int TB = C * C * 2, O_QK = 2 * TB, O_KK = O_QK + HC * C * 2, O_KB = O_KK + HC * C * 2;
-    constexpr int O_R = O_KB + HC * C * 2, O_R2 = O_R + C * (HC + 1) * 4, LDSB = O_R2 + (C / 2) * (HC + 1) * 4;
-    static_assert(3 * C * (HC + 1) * 4 <= O_R2, "per-head results fit below sR2 (sR is not live then)");
+    // fp32 [rows][HC] tables, rows padded by four words: the accumulator-tile
+    // writes (rows 4 apart) and the 4-lanes-a-row reads meet no bank conflicts
+    constexpr int PH = HC + 4;
+    constexpr int O_R = O_KB + HC * C * 2, O_R2 = O_R + C * PH * 4, LDSB = O_R2 + (C / 2) * PH * 4;
+    static_assert(3 * C * PH * 4 <= O_R2, "per-head results fit below sR2 (sR is not live then)");
     __shared__ __align__(16) char sbuf[LDSB];
     uint4* sPv = reinterpret_cast<uint4*>(sbuf);        // dPs rows
     uint4* sAv = reinterpret_cast<uint4*>(sbuf + TB);   // dA rows
@@ -1968,8 +1972,6 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     uint4* sKB = reinterpret_cast<uint4*>(sbuf + O_KB);  // beta k rows (times a factor), by channel
     float* sR = reinterpret_cast<float*>(sbuf + O_R);
     float* sR2 = reinterpret_cast<float*>(sbuf + O_R2);
-    // fp32 [rows][HC] tables, rows padded by one word
-    constexpr int PH = HC + 1;
     auto ridx = [](int i, int j) { return i * PH + j; };
     // element (R, c) of a score table
     auto sel = [](const uint4* X, int R, int c) {
