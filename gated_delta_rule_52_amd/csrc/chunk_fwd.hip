@@ -517,7 +517,18 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     };
     f32x4 dP = zero4(), dA = zero4();
     // off-diagonal 16-tiles: waves NB.. own tile idx with (idx % (NW - NB)) == w - NB
+    // (per-head decay)
     constexpr int OW = NW - NB, MOFF = (NOFF + OW - 1) / OW;
+    // Per-channel decay: the P (= X Y^T) and A (= Y Y^T) products of each level
+    // are spread over all eight waves, one product a wave: level 32's tiles
+    // (2,0) (2,1) (3,0) (3,1), level 16's (1,0) (3,2) (waves 0-3), and at the
+    // levels below the four diagonal tiles
+    static_assert(C == 64 && NW == 8, "four 16-tiles a chunk, eight waves");
+    const int pa = w & 1;                                      // 0: P, 1: A
+    const int ti32 = 2 + (w >> 2), tj32 = (w >> 1) & 1;        // level-32 tile
+    const int ti16 = (w >> 1) == 0 ? 1 : 3, tj16 = ti16 - 1;   // level-16 tile (waves 0-3)
+    const int td = w & 3, pd = w >> 2;                         // diagonal tile and product
+    f32x4 a32 = zero4(), a16 = zero4(), ad = zero4();
     f32x4 accP[MOFF], accA[MOFF];
 #pragma unroll
     for (int m = 0; m < MOFF; ++m) accP[m] = accA[m] = zero4();
@@ -583,18 +594,18 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             scale_rows();
         }
     } else {
-    if (w < NB) {
+    if (w < NB) {  // waves 0-3 hold the diagonal P tiles (pd = 0, td = w)
         const f32x4 tp = cm_prod(zero4(), sX, w, sY, w);
         row_norms();
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dP[r] = (4 * lq + r == lr) ? tp[r] : 0.f;
+        for (int r = 0; r < 4; ++r) ad[r] = (4 * lq + r == lr) ? tp[r] : 0.f;
     }
     __syncthreads();
     if constexpr (L2N) {
         if (w < NB) {  // P_ii of the raw rows times r_q r_k
             const int i = w * 16 + lr;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dP[r] *= sRn[0][i] * sRn[1][i];
+            for (int r = 0; r < 4; ++r) ad[r] *= sRn[0][i] * sRn[1][i];
         }
     }
     scale_rows();  // the level tables below are built from the normalised rows
@@ -649,31 +660,15 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             put_rows(sY, [&](int i) { return kv[i] * F[i]; });
         }
         __syncthreads();
-        if (hl >= 16) {
-            if (w >= NB) {
+        if (hl == 32) {
+            a32 = cm_prod(a32, pa ? sY : sX, ti32, sY, tj32);
+        } else if (hl == 16) {
+            if (w < 4) a16 = cm_prod(a16, pa ? sY : sX, ti16, sY, tj16);
+        } else {
+            const f32x4 t = cm_prod(zero4(), pd ? sY : sX, td, sY, td);
 #pragma unroll
-                for (int m = 0; m < MOFF; ++m) {
-                    const int idx = (w - NB) + OW * m;
-                    if (idx < NOFF) {
-                        int ti, tj;
-                        off_tile(idx, ti, tj);
-                        if (off_tile_level(ti, tj) == hl) {
-                            accP[m] = cm_prod(accP[m], sX, ti, sY, tj);
-                            accA[m] = cm_prod(accA[m], sY, ti, sY, tj);
-                        }
-                    }
-                }
-            }
-        } else if (w < NB) {
-            const f32x4 tp = cm_prod(zero4(), sX, w, sY, w);
-            const f32x4 ta = cm_prod(zero4(), sY, w, sY, w);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (in_level(4 * lq + r, lr, hl)) {
-                    dP[r] += tp[r];
-                    dA[r] += ta[r];
-                }
-            }
+            for (int r = 0; r < 4; ++r)
+                if (in_level(4 * lq + r, lr, hl)) ad[r] += t[r];
         }
         __syncthreads();
     }
@@ -703,7 +698,30 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
         for (int r = 0; r < 4; ++r) sPs[i0 + r][j] = f32_to_bf16(pv[r]);
     };
-    if (w >= NB) {
+    if constexpr (PCH) {
+        // one P or A item of a tile: P scaled into the staging, A times beta to sA;
+        // on the diagonal P keeps j <= i and A j < i
+        auto put_item = [&](int ti, int tj, int prod, const f32x4& acc, bool diag) {
+            if (prod == 0) {
+                float pv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                    pv[r] = (!diag || i >= j) ? scale * grd(acc[r], GDN_DIAG_P) : 0.f;
+                }
+                put_ps(ti * 16 + 4 * lq, tj * 16 + lr, pv);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ti * 16 + 4 * lq + r, j = tj * 16 + lr;
+                    sA[i][j] = (!diag || i > j) ? grd(sbeta[i] * acc[r], GDN_DIAG_A) : 0.f;
+                }
+            }
+        };
+        put_item(ti32, tj32, pa, a32, false);
+        if (w < 4) put_item(ti16, tj16, pa, a16, false);
+        put_item(td, td, pd, ad, true);
+    } else if (w >= NB) {
 #pragma unroll
         for (int m = 0; m < MOFF; ++m) {
             const int idx = (w - NB) + OW * m;
