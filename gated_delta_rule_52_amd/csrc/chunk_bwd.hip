@@ -1010,7 +1010,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
     // words of column pairs) until its rows are stored whole, 16 bytes a thread
     __shared__ __align__(16) bf16 sdA[C][C + 8];
     static_assert(C * C / 8 == NTHR_C, "one 16-byte dA word per thread");
-    __shared__ float sbeta[C], sred[NW][C];
+    __shared__ float sbeta[C], sred[BW / 16][C];
     char* const sS = sbuf;
     char* const sdS = sbuf + O_dS;
     char* const sdO = sbuf + O_dO;
@@ -1424,19 +1424,18 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         static_assert(SPR == 4 || SPR == 8, "four or eight threads per state row");
         if constexpr (SPR == 4) oG = lane4_sum(dgm_part);
         else oG = lane8_sum(dgm_part);
-        // dbeta part: row sums of dX_V o v over the 16 columns of each tile, then
+        // dbeta part: row sums of dX_V o v over the 16 columns of each tile (one
+        // slot per row and column tile, each written by the tile's wave), then
         // over the column tiles (fixed order)
-        for (int idx = tid; idx < NW * C; idx += NTHR_C) (&sred[0][0])[idx] = 0.f;
-        __syncthreads();
 #pragma unroll
         for (int m = 0; m < MD; ++m) {
             const int idx = w + NW * m;
             if (idx < TD) {
-                const int ti = idx / (BW / 16);
+                const int ti = idx / (BW / 16), tj = idx % (BW / 16);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float sb = lane16_sum(dbr[m][r]);
-                    if (lr == 0) sred[w][ti * 16 + 4 * lq + r] = sb;
+                    if (lr == 0) sred[tj][ti * 16 + 4 * lq + r] = sb;
                 }
             }
         }
@@ -1444,7 +1443,7 @@ bchunk1b_kernel(const bf16* __restrict__ v, const float* __restrict__ beta,
         static_assert(C <= NTHR_C, "one dbeta row per thread");
         oB = 0.f;
         if (tid < C)
-            for (int ww = 0; ww < NW; ++ww) oB += sred[ww][tid];
+            for (int jj = 0; jj < BW / 16; ++jj) oB += sred[jj][tid];
         pch = ch;
         if ((long long)ch + gridDim.x >= nch) break;
         ch += gridDim.x;
