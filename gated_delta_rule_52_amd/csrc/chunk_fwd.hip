@@ -1344,15 +1344,16 @@ prepf_kernel(const float* __restrict__ q, const float* __restrict__ k, const flo
         sTs[swz_slot<SC>(i, j / 4)] = tv;
     }
     __syncthreads();
-    // X_V^T = (beta V)^T into the level-table bytes (free now that T is in sTs)
-    float* const XVf = reinterpret_cast<float*>(sbuf);
+    // X_V = beta V (token rows) into the level-table bytes (free now that T is
+    // in sTs), one 16-byte word per store; the U product reads it down its
+    // columns (transposed 4-byte writes were 8-way bank conflicted)
+    using SV = SwzF<DV / 4>;  // rows of DV floats
+    static_assert(C * DV * 4 <= SBUF, "X_V fits the level-table bytes");
     f32x4* const sXV = reinterpret_cast<f32x4*>(sbuf);
 #pragma unroll
     for (int u = 0; u < QV; ++u) {
         const int idx = tid + NTHR_P * u, r = idx / (DV / 4), j0 = (idx % (DV / 4)) * 4;
-        const float bt = sbeta[r];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) XVf[swzf_idx<SC>(j0 + e, r)] = bt * vw[u][e];
+        sXV[swz_slot<SV>(r, j0 / 4)] = sbeta[r] * vw[u];
     }
     // ---- W^T = X_K^T T^T: acc[r] = W[ti*16 + lr][tj*16 + 4 lq + r]
     constexpr int TW = NB * (DK / 16);
@@ -1374,7 +1375,7 @@ prepf_kernel(const float* __restrict__ q, const float* __restrict__ k, const flo
         const int ti = idx / (DV / 16), tj = idx % (DV / 16);
         f32x4 acc = zero4();
         for (int u0 = 0; u0 < 4 * (ti + 1); u0 += 4)
-            acc = mma_f32_k16(ffrag_rows<SC>(sXV, tj * 16, u0), ffrag_rows<SC>(sTs, ti * 16, u0), acc);
+            acc = mma_f32_k16(ffrag_cols<SV>(sXV, 4 * u0, tj * 16), ffrag_rows<SC>(sTs, ti * 16, u0), acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = grd(acc[r], GDN_DIAG_U);
         *reinterpret_cast<f32x4*>(&Uc[(ti * 16 + lr) * DV + tj * 16 + 4 * lq]) = acc;
