@@ -2322,21 +2322,26 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                 Fr *= a[i];
             }
         }
+        // a level's products read the key half's rows from KK and the query
+        // half's from QK and KB only, so each part writes just those
         if (cp) {
 #pragma unroll
             for (int i = 0; i < RPP; i += 8) {
                 float kf[8];
 #pragma unroll
                 for (int z = 0; z < 8; ++z) kf[z] = kv[i + z] * F[i + z];
-                const uint2 q0 = pack4_bf16(qv[i] * F[i], qv[i + 1] * F[i + 1], qv[i + 2] * F[i + 2], qv[i + 3] * F[i + 3]);
-                const uint2 q1 = pack4_bf16(qv[i + 4] * F[i + 4], qv[i + 5] * F[i + 5], qv[i + 6] * F[i + 6], qv[i + 7] * F[i + 7]);
-                const uint2 k0 = pack4_bf16(kf[0], kf[1], kf[2], kf[3]);
-                const uint2 k1 = pack4_bf16(kf[4], kf[5], kf[6], kf[7]);
-                const uint2 b0 = pack4_bf16(sbeta[p0 + i] * kf[0], sbeta[p0 + i + 1] * kf[1], sbeta[p0 + i + 2] * kf[2], sbeta[p0 + i + 3] * kf[3]);
-                const uint2 b1 = pack4_bf16(sbeta[p0 + i + 4] * kf[4], sbeta[p0 + i + 5] * kf[5], sbeta[p0 + i + 6] * kf[6], sbeta[p0 + i + 7] * kf[7]);
-                sQK[ctab_slot(cl, (p0 + i) / 8)] = uint4{q0.x, q0.y, q1.x, q1.y};
-                sKK[ctab_slot(cl, (p0 + i) / 8)] = uint4{k0.x, k0.y, k1.x, k1.y};
-                sKB[ctab_slot(cl, (p0 + i) / 8)] = uint4{b0.x, b0.y, b1.x, b1.y};
+                if (qs) {
+                    const uint2 q0 = pack4_bf16(qv[i] * F[i], qv[i + 1] * F[i + 1], qv[i + 2] * F[i + 2], qv[i + 3] * F[i + 3]);
+                    const uint2 q1 = pack4_bf16(qv[i + 4] * F[i + 4], qv[i + 5] * F[i + 5], qv[i + 6] * F[i + 6], qv[i + 7] * F[i + 7]);
+                    const uint2 b0 = pack4_bf16(sbeta[p0 + i] * kf[0], sbeta[p0 + i + 1] * kf[1], sbeta[p0 + i + 2] * kf[2], sbeta[p0 + i + 3] * kf[3]);
+                    const uint2 b1 = pack4_bf16(sbeta[p0 + i + 4] * kf[4], sbeta[p0 + i + 5] * kf[5], sbeta[p0 + i + 6] * kf[6], sbeta[p0 + i + 7] * kf[7]);
+                    sQK[ctab_slot(cl, (p0 + i) / 8)] = uint4{q0.x, q0.y, q1.x, q1.y};
+                    sKB[ctab_slot(cl, (p0 + i) / 8)] = uint4{b0.x, b0.y, b1.x, b1.y};
+                } else {
+                    const uint2 k0 = pack4_bf16(kf[0], kf[1], kf[2], kf[3]);
+                    const uint2 k1 = pack4_bf16(kf[4], kf[5], kf[6], kf[7]);
+                    sKK[ctab_slot(cl, (p0 + i) / 8)] = uint4{k0.x, k0.y, k1.x, k1.y};
+                }
             }
         }
         __syncthreads();
