@@ -895,26 +895,17 @@ prep2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
         *reinterpret_cast<uint2*>(&Wb[e]) = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();  // X_V^T complete
-    // ---- U = T X_V (fp32 out).  For the state-saving scans (with T out) it is
-    // stored transposed, U^T [DV][C]: the tile of U, a lane's 4 consecutive
-    // rows of one column, is one 16-byte U^T store.  For the forward-only scan
-    // U [C][DV]: the tile of U^T = X_V^T T^T, 4 consecutive columns of one row.
+    // ---- U = T X_V (fp32 out).
+    // The tile of U^T = X_V^T T^T: a lane holds 4 consecutive columns of one U row
     constexpr int TU = NB * (DV / 16);
     float* Uc = Uo + (size_t)ch * C * DV;
     for (int idx = w; idx < TU; idx += NW) {
         const int ti = idx / (DV / 16), tj = idx % (DV / 16);
         const int K = ((16 * (ti + 1) + 31) / 32) * 32;  // T is lower triangular
         f32x4 acc = zero4();
-        size_t e;
-        if (bwdt) {
-            for (int k0 = 0; k0 < K; k0 += 32)
-                acc = mfma_bf16_16x16x32(frag_rows<SwzR8>(sTb, ti * 16, k0 / 8), frag_cols<SXV>(sXV, k0, tj * 16), acc);
-            e = (size_t)(tj * 16 + lr) * C + ti * 16 + 4 * lq;
-        } else {
-            for (int k0 = 0; k0 < K; k0 += 32)
-                acc = mfma_bf16_16x16x32(frag_cols<SXV>(sXV, k0, tj * 16), frag_rows<SwzR8>(sTb, ti * 16, k0 / 8), acc);
-            e = (size_t)(ti * 16 + lr) * DV + tj * 16 + 4 * lq;
-        }
+        for (int k0 = 0; k0 < K; k0 += 32)
+            acc = mfma_bf16_16x16x32(frag_cols<SXV>(sXV, k0, tj * 16), frag_rows<SwzR8>(sTb, ti * 16, k0 / 8), acc);
+        const size_t e = (size_t)(ti * 16 + lr) * DV + tj * 16 + 4 * lq;
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = grd(acc[r], GDN_DIAG_U);
         *reinterpret_cast<float4*>(&Uc[e]) = float4{acc[0], acc[1], acc[2], acc[3]};
@@ -1579,11 +1570,11 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
     // saved states feed the backward's bf16 products and its decay-gradient sums)
     constexpr int PO = BV + 8;
     __shared__ __align__(16) bf16 sSf[2][DK][PO];
-    // the chunk's U^T slice (its BV columns as rows of C floats, padded) and
-    // decay: a lane's four accumulator rows of one column are one 16-byte read
-    constexpr int PU = C + 4;
+    // the chunk's U slice (fp32 rows, padded so the accumulator-layout reads of
+    // four rows 4 apart hit distinct banks) and decay
+    constexpr int PU = BV + 4;
     static_assert(C * BV / 4 == NTHR_S && DK / 4 <= NTHR_S, "one U word and at most one decay word per thread");
-    __shared__ __align__(16) float sU[BV][PU], sGm[DK];
+    __shared__ __align__(16) float sU[C][PU], sGm[DK];
     __shared__ __align__(16) bf16 sDr[2][C][PO], sOr[2][C][PO];
 
     const int x = blockIdx.x;
@@ -1636,7 +1627,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
             else val = reinterpret_cast<const uint4*>(Psb + ch * C * C)[idx - 2 * QW - QK];
             pf[q] = val;
         }
-        upf = load4<float>(Ui + (ch * DV + v0 + tid / (C / 4)) * C + 4 * (tid % (C / 4)));
+        upf = load4<float>(Ui + (ch * C + tid / (BV / 4)) * DV + v0 + 4 * (tid % (BV / 4)));
         gpf = load4<float>(gami + ch * DK + 4 * (tid % (DK / 4)));
     };
     // Registers -> LDS in two halves, each written while the other half's
@@ -1647,7 +1638,7 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
     // they would make it wait for the prefetch.
     auto stash_wq = [&](PFW& pf, UF& upf) {  // W and Qg words, U
         __builtin_amdgcn_sched_barrier(0);
-        st4(&sU[tid / (C / 4)][4 * (tid % (C / 4))], upf);
+        st4(&sU[tid / (BV / 4)][4 * (tid % (BV / 4))], upf);
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
             const int idx = tid + NTHR_S * q;
@@ -1711,10 +1702,9 @@ scan2_kernel(const bf16* __restrict__ Wb, const bf16* __restrict__ Qgb,
 #pragma unroll
             for (int u0 = 0; u0 < DK / 8; u0 += 4)
                 ws = mfma_bf16_16x16x32(frag_rows<SA>(sW, ti * 16, u0), frag_rows<SA>(sSt, tj * 16, u0), ws);
-            const f32x4 uv = *reinterpret_cast<const f32x4*>(&sU[tj * 16 + lr][ti * 16 + 4 * lq]);
             float dv[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dv[r] = uv[r] - ws[r];
+            for (int r = 0; r < 4; ++r) dv[r] = sU[ti * 16 + 4 * lq + r][tj * 16 + lr] - ws[r];
             *reinterpret_cast<uint2*>(swz_at<SC>(sDt, tj * 16 + lr, ti * 16 + 4 * lq)) = pack4_bf16(dv[0], dv[1], dv[2], dv[3]);
             if (SAVE) {  // staged as 32-bit words of column pairs
                 const uint2 wd = acc_colpairs(f32x4{dv[0], dv[1], dv[2], dv[3]});

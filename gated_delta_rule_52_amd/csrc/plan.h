@@ -5,8 +5,7 @@
 // index is ch = (b * H + h) * NC + n.  Workspace arrays are float32 unless noted
 // below, indexed by chunk-head:
 //   W   [ch][C][Dk]   W  = T diag(beta) (K o Gamma)        (WY form of the solve)
-//   U   [ch][C][Dv]   U  = T diag(beta) V  (bf16 inputs at chunk 64 with T kept,
-//                     i.e. for the state-saving scans: U^T [ch][Dv][C])
+//   U   [ch][C][Dv]   U  = T diag(beta) V
 //   Qg  [ch][C][Dk]   Qg = scale * (Q o Gamma)             (query read of the carried state)
 //   Kh  [ch][C][Dk]   Kh = K o exp(G_{C-1} - G)            (key write into the next state)
 //   Ps  [ch][C][C]    Ps = scale * P  (decayed query-key scores, lower incl. diagonal)
