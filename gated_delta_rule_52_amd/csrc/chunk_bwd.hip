@@ -360,7 +360,7 @@ bscanf_kernel(const float* __restrict__ KhTt, const float* __restrict__ Pst,
 
 // ---------------------------------------------------------------------------
 // bscan4: the reverse scan of the state gradient over bf16 chunk tables (bf16
-// inputs, chunk 64), built like scan4: two waves per (b, h, 32-wide Dv slice),
+// inputs, chunk 64): two compute waves per (b, h, 32-wide Dv slice),
 // wave w owning 16 columns of dS for the whole sequence in MFMA accumulators
 // that are the operands of the next products (kperm.h).  Per chunk n, from the
 // last to the first, with dS' the gradient at the chunk's end and the chunk's
@@ -371,8 +371,9 @@ bscanf_kernel(const float* __restrict__ KhTt, const float* __restrict__ Pst,
 //     dS <- gam o dS' + Qg^T dO - W^T dD    (the gradient at the chunk's start)
 // dS' and dD leave as bf16 rows for bchunk1 (transposed by a 0/1 MFMA so a
 // lane stores four consecutive columns).  The dO operand (K along tokens) is
-// gathered from the LDS copy of the slice, eight 2-byte reads per fragment.
-// Two load waves bring the next chunk in and warm the L2, as in scan4.
+// read from the LDS copy of the slice by transposing loads in the same K order.
+// Two load waves bring the next chunk into the other of two LDS buffers by
+// direct loads and touch the lines of the chunk three ahead into the L2.
 // ---------------------------------------------------------------------------
 constexpr int NTHR_B4 = 256;  // waves 0, 1 compute; waves 2, 3 load
 
