@@ -1991,6 +1991,9 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
     const int t0 = n * C;
     const int nvalid = min(C, T - t0);
     const int tid = threadIdx.x, w = tid >> 6;
+    // the wave index as a wave-uniform value: the MFMA tile loops' tile
+    // choice and coordinates then live in scalar registers and branches
+    const int wu = __builtin_amdgcn_readfirstlane(w);
     const size_t tok0 = ((size_t)b * T + t0) * H + h;
     const size_t rsK = (size_t)H * DK;
     const bool cp = tid < NPART * HC;
@@ -2349,7 +2352,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         constexpr int T3 = NB * (HC / 16), M3 = (T3 + NW - 1) / NW;
 #pragma unroll 1  // one tile at a time: its fragments only are live
         for (int m = 0; m < M3; ++m) {
-            const int idx = w + NW * m;
+            const int idx = wu + NW * m;
             if (idx < T3) {
                 const int ti = idx / (HC / 16), tj = idx % (HC / 16);
                 const int tbase = (ti * 16 / (2 * hl)) * (2 * hl);
@@ -2399,15 +2402,28 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                         r2 = mfma_bf16_16x16x32(a2, b2, zero4());
                     }
                 }
+                // results: a lane's four rows acc_row(0) + r of column
+                // acc_col(), at one lane address plus immediate row offsets.
+                // Query rows keep R1 and R2 apart (R2 in sR2, whose rows are
+                // the query halves' rows packed), key rows take R1 + R2.
+                const int lrow = acc_row(0), lcol = acc_col();
+                float* const pR = sR + ridx(ti * 16, tj * 16) + ridx(lrow, lcol);
+                const bool qrows = hl >= 16 ? qt : lrow >= 8;  // the lane's four rows alike
+                if (qrows) {
+                    // first row of this tile's query rows in sR2: the tile's
+                    // first query row i0 maps to (i0 / (2 hl)) hl + i0 % hl, and
+                    // the rows after it follow on
+                    const int i0 = ti * 16 + (hl >= 16 ? 0 : 8);
+                    float* const pR2 = sR2 + ridx((i0 / (2 * hl)) * hl + (i0 % hl), tj * 16) +
+                                       ridx(lrow - (hl >= 16 ? 0 : 8), lcol);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = ti * 16 + acc_row(r), j = tj * 16 + acc_col();
-                    if (hl >= 16 ? qt : (i & 15) >= 8) {
-                        sR[ridx(i, j)] = scale * r1[r];
-                        sR2[ridx((i / (2 * hl)) * hl + (i % hl), j)] = r2[r];
-                    } else {
-                        sR[ridx(i, j)] = scale * r1[r] + r2[r];
+                    for (int r = 0; r < 4; ++r) {
+                        pR[r * PH] = scale * r1[r];
+                        pR2[r * PH] = r2[r];
                     }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pR[r * PH] = scale * r1[r] + r2[r];
                 }
             }
         }
