@@ -2435,17 +2435,18 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                     const int r = p0 + i;
                     const float R1 = sR[ridx(r, cl)], R2 = sR2[ridx((r / (2 * hl)) * hl + (r % hl), cl)];
                     const float bt = sbeta[r];
-                    dq[i] += F[i] * R1;
-                    dk[i] += bt * F[i] * R2;
-                    dG[i] += qv[i] * F[i] * R1 + bt * kv[i] * F[i] * R2;
-                    dbr[i] += kv[i] * F[i] * R2;
+                    const float t1 = F[i] * R1, t2 = F[i] * R2, kt2 = kv[i] * t2;
+                    dq[i] += t1;
+                    dk[i] = fmaf(bt, t2, dk[i]);
+                    dG[i] = fmaf(bt, kt2, fmaf(qv[i], t1, dG[i]));
+                    dbr[i] += kt2;
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < RPP; ++i) {
-                    const float R = sR[ridx(p0 + i, cl)];
-                    dk[i] += F[i] * R;
-                    dG[i] -= kv[i] * F[i] * R;
+                    const float t = F[i] * sR[ridx(p0 + i, cl)];
+                    dk[i] += t;
+                    dG[i] = fmaf(-kv[i], t, dG[i]);
                 }
             }
         }
@@ -2475,15 +2476,15 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                 E *= a[j + 1];
                 const float tP = ext(pu, j) * E;
                 const float tA = ext(au, j) * E;
-                rq += tP * kv[j];
-                ra += tA * kv[j];
-                cs[j] += tP * sqi + tA * bki;
+                rq = fmaf(tP, kv[j], rq);
+                ra = fmaf(tA, kv[j], ra);
+                cs[j] = fmaf(tA, bki, fmaf(tP, sqi, cs[j]));
             }
             rq *= scale;
             dq[i] += rq;
-            dk[i] += bi * ra;
-            dG[i] += qv[i] * rq + bki * ra;
-            dbr[i] += kv[i] * ra;
+            dk[i] = fmaf(bi, ra, dk[i]);
+            dG[i] = fmaf(bki, ra, fmaf(qv[i], rq, dG[i]));
+            dbr[i] = fmaf(kv[i], ra, dbr[i]);
         }
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
