@@ -2350,7 +2350,7 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         }
         __syncthreads();
         constexpr int T3 = NB * (HC / 16), M3 = (T3 + NW - 1) / NW;
-#pragma unroll 1  // one tile at a time: its fragments only are live
+#pragma unroll 2  // two tiles a wave: both in flight (118 VGPRs, no spill)
         for (int m = 0; m < M3; ++m) {
             const int idx = wu + NW * m;
             if (idx < T3) {
