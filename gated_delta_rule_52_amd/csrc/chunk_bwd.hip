@@ -2290,6 +2290,47 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
         }
     }
 
+    // ---- pairs inside one 8-token part (j < i), on VALU: this thread owns
+    // channel c of all 8 rows of its part; E_ij = prod_{s=j+1..i} a_s.  Row
+    // sums rq (of dP E k), ra (of dA E k) and column sums cs (of dP E q +
+    // dA E beta k) give the decay gradient too: d/dG_i E_ij = E_ij = -d/dG_j E_ij.
+    if (cp) {
+        float cs[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) cs[j] = 0.f;
+#pragma unroll
+        for (int i = 1; i < RPP; ++i) {
+            const int r = p0 + i;
+            const float bi = sbeta[r], bki = bi * kv[i], sqi = scale * qv[i];
+            // this row's columns p0 .. p0 + 7: one 16-byte unit of each table
+            const u32x4 pu = __builtin_bit_cast(u32x4, sPv[swz_slot<SwzU8>(r, p0 >> 3)]);
+            const u32x4 au = __builtin_bit_cast(u32x4, sAv[swz_slot<SwzU8>(r, p0 >> 3)]);
+            auto ext = [](const u32x4& u, int j) {
+                return __uint_as_float((j & 1) ? (u[j >> 1] & 0xFFFF0000u) : (u[j >> 1] << 16));
+            };
+            float rq = 0.f, ra = 0.f, E = 1.f;
+#pragma unroll
+            for (int j = i - 1; j >= 0; --j) {
+                E *= a[j + 1];
+                const float tP = ext(pu, j) * E;
+                const float tA = ext(au, j) * E;
+                rq = fmaf(tP, kv[j], rq);
+                ra = fmaf(tA, kv[j], ra);
+                cs[j] = fmaf(tA, bki, fmaf(tP, sqi, cs[j]));
+            }
+            rq *= scale;
+            dq[i] += rq;
+            dk[i] = fmaf(bi, ra, dk[i]);
+            dG[i] = fmaf(bki, ra, fmaf(qv[i], rq, dG[i]));
+            dbr[i] = fmaf(kv[i], ra, dbr[i]);
+        }
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            dk[j] += cs[j];
+            dG[j] -= kv[j] * cs[j];
+        }
+    }
+
     // ---- pairs that span two 8-token parts: levels h = 32, 16, 8 of the
     // block-boundary split.  With F the level factor of each own row (query
     // rows prod_{s=m+1..r} a_s, key rows prod_{s=r+1..m} a_s, m the last token
@@ -2449,47 +2490,6 @@ bchunk2c_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const fl
                     dG[i] = fmaf(-kv[i], t, dG[i]);
                 }
             }
-        }
-    }
-
-    // ---- pairs inside one 8-token part (j < i), on VALU: this thread owns
-    // channel c of all 8 rows of its part; E_ij = prod_{s=j+1..i} a_s.  Row
-    // sums rq (of dP E k), ra (of dA E k) and column sums cs (of dP E q +
-    // dA E beta k) give the decay gradient too: d/dG_i E_ij = E_ij = -d/dG_j E_ij.
-    if (cp) {
-        float cs[RPP];
-#pragma unroll
-        for (int j = 0; j < RPP; ++j) cs[j] = 0.f;
-#pragma unroll
-        for (int i = 1; i < RPP; ++i) {
-            const int r = p0 + i;
-            const float bi = sbeta[r], bki = bi * kv[i], sqi = scale * qv[i];
-            // this row's columns p0 .. p0 + 7: one 16-byte unit of each table
-            const u32x4 pu = __builtin_bit_cast(u32x4, sPv[swz_slot<SwzU8>(r, p0 >> 3)]);
-            const u32x4 au = __builtin_bit_cast(u32x4, sAv[swz_slot<SwzU8>(r, p0 >> 3)]);
-            auto ext = [](const u32x4& u, int j) {
-                return __uint_as_float((j & 1) ? (u[j >> 1] & 0xFFFF0000u) : (u[j >> 1] << 16));
-            };
-            float rq = 0.f, ra = 0.f, E = 1.f;
-#pragma unroll
-            for (int j = i - 1; j >= 0; --j) {
-                E *= a[j + 1];
-                const float tP = ext(pu, j) * E;
-                const float tA = ext(au, j) * E;
-                rq = fmaf(tP, kv[j], rq);
-                ra = fmaf(tA, kv[j], ra);
-                cs[j] = fmaf(tA, bki, fmaf(tP, sqi, cs[j]));
-            }
-            rq *= scale;
-            dq[i] += rq;
-            dk[i] = fmaf(bi, ra, dk[i]);
-            dG[i] = fmaf(bki, ra, fmaf(qv[i], rq, dG[i]));
-            dbr[i] = fmaf(kv[i], ra, dbr[i]);
-        }
-#pragma unroll
-        for (int j = 0; j < RPP; ++j) {
-            dk[j] += cs[j];
-            dG[j] -= kv[j] * cs[j];
         }
     }
 
